@@ -1,0 +1,405 @@
+"""Plain fp64 CPU oracle for the replayed SSM decode path (Mamba-2, Gated DeltaNet).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and the
+CPU-baseline leg of the benchmark may import this module.  It shares no code
+with the GPU library and never imports it.
+
+Pages cited:
+  [DE] "ReplaySSM beschleunigt das Decoding von Hybridmodellen durch Caching der
+       Eingaben statt des Zustands" (German)
+  [ES] its Spanish translation, "ReplaySSM acelera la decodificacion de modelos
+       hibridos ..."
+  [TR] "NVIDIA ve Dao AI Lab, hibrit model cozumlemesini hizlandirmak icin
+       ReplaySSM'i sundu" (Turkish)
+
+Two parts:
+
+* Values.  The replayed path must give the outputs of ordinary token-by-token
+  decoding up to rounding ([TR] "ReplaySSM nasil calisir?").  So the value side
+  of the oracle is ordinary decoding in fp64 (oracle.c), applied to the
+  committed token stream.  Values never depend on when flushes happen.
+
+* Bookkeeping.  A per-sequence integer machine for the buffer pointer (len),
+  the pending draft count (pend) and the flush count (fc), with a buffer of
+  capacity `cap` (16 on the pages, [TR] "ReplaySSM nasil calisir?"):
+    decode      if len+1 > cap: forced flush.  Append at len; len += 1.
+                If len == cap afterwards: flush.  (The flush happens on the
+                step that fills the buffer: [TR] same section; [DE] "Wie es
+                funktioniert".)
+    flush       if len > 0: flush.  Not allowed while drafts are pending.
+    spec(k)     1 <= k <= cap, no drafts pending.  If len+k > cap: forced
+                flush of the committed prefix first.  Drafts occupy
+                [len, len+k); pend = k.  ([TR] "Durum trafigini azaltma ve
+                rollback'in basitlestirilmesi": drafts are appended without
+                verification.)
+    commit(a)   a := clamp(a, 0, pend) (flagged when clamped); len += a;
+                pend = 0.  The accepted prefix advances the pointer.
+    rollback    commit(0): a pointer reset discards the drafts ([DE] "Wie es
+                funktioniert", [ES] "Como funciona").
+  A flush sets fc += 1 and len = 0 and records the checkpoint image (the
+  committed fp64 state at that moment).
+
+The pages leave the following open; the readings taken here are listed with
+the design notes: when the flush happens (on the filling step), whether the
+output includes the current token (yes), the overflow rule for drafts (forced
+flush before appending), and that a load resets len, pend and fc.
+
+Low-precision read copy ([TR] "Kuantizasyon hatasinin sinirlandirilmasi": a
+high-precision checkpoint drives the recurrence, a low-precision copy serves
+reads).  With a read copy, a step that performs no flush produces its output
+from the dequantized copy of the checkpoint followed by the committed tokens
+since the last flush; a step that flushes produces it from the full-precision
+state.  The copy is the quantization of the checkpoint image rounded to fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIBPATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_ubp = ctypes.POINTER(ctypes.c_ubyte)
+
+
+def configure(L):
+    """Declare the C signatures on a loaded oracle library handle."""
+    i, d = ctypes.c_int, ctypes.c_double
+    L.oracle_mamba2_token.argtypes = [i, i, i, i, i, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _ubp]
+    L.oracle_mamba2_token.restype = None
+    L.oracle_gdn_token.argtypes = [i, i, i, i, i, _dp, _dp, _dp, _dp, _dp, _dp, d, _dp, _ubp]
+    L.oracle_gdn_token.restype = None
+    L.oracle_e4m3_decode.argtypes = [i]
+    L.oracle_e4m3_decode.restype = d
+    L.oracle_e4m3_encode.argtypes = [d]
+    L.oracle_e4m3_encode.restype = i
+    L.oracle_e2m1_decode.argtypes = [i]
+    L.oracle_e2m1_decode.restype = d
+    L.oracle_e2m1_encode.argtypes = [d]
+    L.oracle_e2m1_encode.restype = i
+    L.oracle_e8m0_decode.argtypes = [i]
+    L.oracle_e8m0_decode.restype = d
+    L.oracle_mxfp4_quantize_block.argtypes = [_dp, i, _ubp]
+    L.oracle_mxfp4_quantize_block.restype = i
+    L.oracle_e4m3_encode_array.argtypes = [_dp, ctypes.c_long, _ubp]
+    L.oracle_e4m3_encode_array.restype = None
+    L.oracle_e4m3_decode_array.argtypes = [_ubp, ctypes.c_long, _dp]
+    L.oracle_e4m3_decode_array.restype = None
+    L.oracle_mxfp4_quantize_array.argtypes = [_dp, ctypes.c_long, _ubp, _ubp]
+    L.oracle_mxfp4_quantize_array.restype = None
+    L.oracle_mxfp4_dequantize_array.argtypes = [_ubp, _ubp, ctypes.c_long, _dp]
+    L.oracle_mxfp4_dequantize_array.restype = None
+    return L
+
+
+def lib():
+    """Load (building with gcc if absent) the fp64 oracle library."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIBPATH):
+            from oracle import build as _b  # local build on demand
+            _b.build()
+        _lib = configure(ctypes.CDLL(_LIBPATH))
+    return _lib
+
+
+def use_library(handle):
+    """Swap the loaded library (used by the tests that plant mistakes in a copy).
+
+    Returns the previous handle so the caller can restore it."""
+    global _lib
+    prev = _lib
+    _lib = handle
+    return prev
+
+
+def _f64(a):
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    return a, a.ctypes.data_as(_dp)
+
+
+# --------------------------------------------------------------------------
+# Per-token recurrences (thin wrappers over oracle.c)
+# --------------------------------------------------------------------------
+
+def mamba2_token(S, x, Bm, Cm, dt, A, D, active=None):
+    """One ordinary Mamba-2 decode token, in place on S [B,H,P,N] (fp64).
+
+    Returns y [B,H,P] (zeros where the sequence is inactive)."""
+    assert S.dtype == np.float64 and S.flags.c_contiguous
+    Bsz, H, P, N = S.shape
+    G = Bm.shape[1]
+    x, xp = _f64(x)
+    Bm, bp = _f64(Bm)
+    Cm, cp = _f64(Cm)
+    dt, dtp = _f64(dt)
+    A, ap = _f64(A)
+    D, dp = _f64(D)
+    y = np.zeros((Bsz, H, P), np.float64)
+    act = None
+    if active is not None:
+        active = np.ascontiguousarray(active, dtype=np.uint8)
+        act = active.ctypes.data_as(_ubp)
+    lib().oracle_mamba2_token(Bsz, H, G, P, N, S.ctypes.data_as(_dp), xp, bp, cp, dtp, ap, dp,
+                              y.ctypes.data_as(_dp), act)
+    return y
+
+
+def gdn_token(S, q, k, v, alpha, beta, scale=1.0, active=None):
+    """One ordinary Gated DeltaNet decode token, in place on S [B,H,DV,DK] (fp64).
+
+    Returns o [B,H,DV]."""
+    assert S.dtype == np.float64 and S.flags.c_contiguous
+    Bsz, H, DV, DK = S.shape
+    G = k.shape[1]
+    q, qp = _f64(q)
+    k, kp = _f64(k)
+    v, vp = _f64(v)
+    alpha, alp = _f64(alpha)
+    beta, bep = _f64(beta)
+    o = np.zeros((Bsz, H, DV), np.float64)
+    act = None
+    if active is not None:
+        active = np.ascontiguousarray(active, dtype=np.uint8)
+        act = active.ctypes.data_as(_ubp)
+    lib().oracle_gdn_token(Bsz, H, G, DK, DV, S.ctypes.data_as(_dp), qp, kp, vp, alp, bep,
+                           float(scale), o.ctypes.data_as(_dp), act)
+    return o
+
+
+# --------------------------------------------------------------------------
+# Quantizers (OCP MX v1.0 element formats)
+# --------------------------------------------------------------------------
+
+def e4m3_encode(v):
+    v, vp = _f64(np.ravel(v))
+    out = np.empty(v.size, np.uint8)
+    lib().oracle_e4m3_encode_array(vp, v.size, out.ctypes.data_as(_ubp))
+    return out
+
+
+def e4m3_decode(codes):
+    codes = np.ascontiguousarray(np.ravel(codes), dtype=np.uint8)
+    out = np.empty(codes.size, np.float64)
+    lib().oracle_e4m3_decode_array(codes.ctypes.data_as(_ubp), codes.size, out.ctypes.data_as(_dp))
+    return out
+
+
+def mxfp4_quantize(v):
+    """v [..., 32k]: blocks of 32 along the last axis.
+
+    Returns (codes uint8 [..., 32k] one 4-bit code per byte, scales uint8 [..., k])."""
+    v = np.asarray(v, np.float64)
+    assert v.shape[-1] % 32 == 0
+    lead = v.shape[:-1]
+    nb = v.size // 32
+    flat, fp = _f64(v.reshape(nb, 32))
+    codes = np.empty((nb, 32), np.uint8)
+    scales = np.empty(nb, np.uint8)
+    lib().oracle_mxfp4_quantize_array(fp, nb, codes.ctypes.data_as(_ubp), scales.ctypes.data_as(_ubp))
+    return codes.reshape(*lead, v.shape[-1]), scales.reshape(*lead, v.shape[-1] // 32)
+
+
+def mxfp4_dequantize(codes, scales):
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    nb = scales.size
+    out = np.empty(nb * 32, np.float64)
+    lib().oracle_mxfp4_dequantize_array(codes.ctypes.data_as(_ubp), scales.ctypes.data_as(_ubp),
+                                        nb, out.ctypes.data_as(_dp))
+    return out.reshape(codes.shape)
+
+
+def read_copy_values(S_fp64, fmt):
+    """Dequantized read copy of a checkpoint image: round to fp32, quantize, dequantize.
+
+    Blocks (MXFP4) run along the last axis (N for Mamba-2, d_k for GDN)."""
+    s32 = np.asarray(S_fp64, np.float64).astype(np.float32).astype(np.float64)
+    if fmt is None:
+        return s32
+    if fmt == "fp8":
+        return e4m3_decode(e4m3_encode(s32)).reshape(s32.shape)
+    if fmt == "mxfp4":
+        c, s = mxfp4_quantize(s32)
+        return mxfp4_dequantize(c, s)
+    raise ValueError(fmt)
+
+
+# --------------------------------------------------------------------------
+# Op runner: values + bookkeeping
+# --------------------------------------------------------------------------
+
+class PhaseError(RuntimeError):
+    """An operation that the buffer protocol does not allow in the current phase."""
+
+
+class _Session:
+    """Shared bookkeeping for both layer kinds.  Subclasses define _token()."""
+
+    kind = None
+
+    def __init__(self, batch, cap, S0, read_copy=None):
+        if not 1 <= cap <= 16:
+            raise ValueError("buffer capacity must be in [1, 16]")
+        self.B = batch
+        self.cap = cap
+        self.S = np.array(S0, np.float64, copy=True)          # committed state
+        self.ckpt = self.S.copy()                              # image at last flush
+        self.len = np.zeros(batch, np.int32)
+        self.pend = np.zeros(batch, np.int32)
+        self.fc = np.zeros(batch, np.int32)
+        self.err = 0
+        self.read_copy = read_copy
+        self.hist = [[] for _ in range(batch)]                 # committed tokens since flush
+        self._drafts = None                                    # list of per-draft inputs
+        self.flush_events = []                                 # (op index, b) pairs
+        self.nops = 0
+
+    # -- helpers -----------------------------------------------------------
+    def trace(self):
+        return self.len.copy(), self.pend.copy(), self.fc.copy()
+
+    def _flush_rows(self, rows):
+        for b in np.flatnonzero(rows):
+            self.ckpt[b] = self.S[b]
+            self.fc[b] += 1
+            self.len[b] = 0
+            self.hist[b] = []
+            self.flush_events.append((self.nops, int(b)))
+
+    def _slice(self, inp, b):
+        return {k: (v[b:b + 1] if v.ndim >= 1 and v.shape[0] == self.B else v) for k, v in inp.items()}
+
+    def _read_copy_output(self, b, inp):
+        """Output for sequence b from the dequantized checkpoint + history + inp."""
+        S = read_copy_values(self.ckpt[b:b + 1], self.read_copy).copy()
+        for past in self.hist[b]:
+            self._token(S, past)
+        return self._token(S, self._slice(inp, b))[0]
+
+    # -- operations --------------------------------------------------------
+    def load(self, S0):
+        if self.pend.any():
+            raise PhaseError("load while drafts are pending")
+        self.S = np.array(S0, np.float64, copy=True)
+        self.ckpt = self.S.copy()
+        self.len[:] = 0
+        self.pend[:] = 0
+        self.fc[:] = 0
+        self.err = 0
+        self.hist = [[] for _ in range(self.B)]
+        self.nops += 1
+
+    def decode(self, inp):
+        if self.pend.any():
+            raise PhaseError("decode while drafts are pending")
+        forced = self.len + 1 > self.cap
+        self._flush_rows(forced)
+        y = self._token(self.S, inp)
+        self.len += 1
+        full = self.len == self.cap
+        if self.read_copy:
+            no_flush = ~(forced | full)
+            for b in np.flatnonzero(no_flush):
+                y[b] = self._read_copy_output(b, inp)
+        for b in range(self.B):
+            if not full[b]:
+                self.hist[b].append(self._slice(inp, b))
+        self._flush_rows(full)
+        self.nops += 1
+        return y
+
+    def flush(self):
+        if self.pend.any():
+            raise PhaseError("flush while drafts are pending")
+        self._flush_rows(self.len > 0)
+        self.nops += 1
+
+    def spec_append(self, drafts):
+        """drafts: list of k per-token input dicts.  Returns outputs [k] of arrays."""
+        k = len(drafts)
+        if self.pend.any():
+            raise PhaseError("spec_append while drafts are pending")
+        if not 1 <= k <= self.cap:
+            raise ValueError("draft count out of range")
+        pre = self.len + k > self.cap
+        self._flush_rows(pre)
+        S = self.S.copy()
+        outs = []
+        for j, inp in enumerate(drafts):
+            y = self._token(S, inp)
+            if self.read_copy:
+                for b in np.flatnonzero(~pre):
+                    Sq = read_copy_values(self.ckpt[b:b + 1], self.read_copy).copy()
+                    for past in self.hist[b]:
+                        self._token(Sq, past)
+                    for jj in range(j + 1):
+                        yq = self._token(Sq, self._slice(drafts[jj], b))
+                    y[b] = yq[0]
+            outs.append(y)
+        self._drafts = list(drafts)
+        self.pend[:] = k
+        self.nops += 1
+        return outs
+
+    def commit(self, accepted):
+        if self._drafts is None:
+            raise PhaseError("commit or rollback without pending drafts")
+        a = np.asarray(accepted, np.int64)
+        clamped = np.clip(a, 0, self.pend)
+        if (clamped != a).any():
+            self.err |= 1
+        drafts = self._drafts or []
+        for j, inp in enumerate(drafts):
+            act = (clamped > j).astype(np.uint8)
+            if act.any():
+                self._token(self.S, inp, act)
+                for b in np.flatnonzero(act):
+                    self.hist[b].append(self._slice(inp, b))
+        self.len += clamped.astype(np.int32)
+        self.pend[:] = 0
+        self._drafts = None
+        self.nops += 1
+
+    def rollback(self):
+        self.commit(np.zeros(self.B, np.int64))
+
+
+class Mamba2Session(_Session):
+    """Mamba-2 layer: state [B,H,P,N]; per-token inputs x [B,H,P], Bm/Cm [B,G,N], dt [B,H]."""
+
+    kind = "mamba2"
+
+    def __init__(self, A, D, S0, cap=16, read_copy=None):
+        self.A = np.asarray(A, np.float64)
+        self.D = np.asarray(D, np.float64)
+        super().__init__(np.asarray(S0).shape[0], cap, S0, read_copy)
+
+    def _token(self, S, inp, active=None):
+        return mamba2_token(S, inp["x"], inp["Bm"], inp["Cm"], inp["dt"], self.A, self.D, active)
+
+
+class GDNSession(_Session):
+    """Gated DeltaNet layer: state [B,H,DV,DK]; inputs q/k [B,G,DK], v [B,H,DV], alpha/beta [B,H]."""
+
+    kind = "gdn"
+
+    def __init__(self, S0, cap=16, scale=1.0, read_copy=None):
+        self.scale = float(scale)
+        super().__init__(np.asarray(S0).shape[0], cap, S0, read_copy)
+
+    def _token(self, S, inp, active=None):
+        return gdn_token(S, inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], self.scale, active)
+
+
+def normwise_error(got, ref, axis=-1):
+    """max over vectors of ||got - ref||_inf / max(||ref||_inf, 1e-30), vectors along `axis`."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    num = np.max(np.abs(got - ref), axis=axis)
+    den = np.maximum(np.max(np.abs(ref), axis=axis), 1e-30)
+    return float(np.max(num / den)) if num.size else 0.0

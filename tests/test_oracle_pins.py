@@ -1,0 +1,470 @@
+"""Pins of the fp64 CPU oracle against facts that do not come from the oracle itself.
+
+Each test checks the oracle against one of: a brute-force unrolled sum written
+as a closed form (not a loop over the recurrence), a special case with a known
+closed form, a library routine (torch's fp8 cast), the OCP MX format tables, or
+a hand-derived bookkeeping trace.  Together they are chosen so that a dropped
+term, a wrong sign, a wrong index or a transposed operand in the oracle fails
+at least one test (see test_planted_mistakes_are_caught).
+"""
+import os
+
+import numpy as np
+import pytest
+
+from oracle import replay_oracle as ro
+from hybrid_decode_replay_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def f64(d):
+    """fp64 copies of a dict of input arrays (keeps test-side arithmetic in fp64)."""
+    return {k: np.asarray(v, np.float64) for k, v in d.items()}
+
+
+# --------------------------------------------------------------------------
+# Brute-force references (closed forms, numpy only)
+# --------------------------------------------------------------------------
+
+def brute_mamba2(S0, A, D, toks, T):
+    """S_t = (prod_{j<=t} a_j) S0 + sum_{s<=t} (prod_{s<j<=t} a_j) dt_s x_s B_s^T,  y_t = S_t C_t + D x_t."""
+    B, H, P, N = S0.shape
+    G = toks["Bm"].shape[2]
+    hpg = H // G
+    toks = {k: v.astype(np.float64) for k, v in toks.items()}
+    A = np.asarray(A, np.float64)
+    D = np.asarray(D, np.float64)
+    ys = np.zeros((T, B, H, P))
+    S_final = np.zeros_like(S0, dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            g = h // hpg
+            a = np.exp(toks["dt"][:, b, h].astype(np.float64) * A[h])
+            for t in range(T):
+                S = np.prod(a[: t + 1]) * S0[b, h].astype(np.float64)
+                for s in range(t + 1):
+                    w = np.prod(a[s + 1: t + 1]) * toks["dt"][s, b, h]
+                    S = S + w * np.outer(toks["x"][s, b, h], toks["Bm"][s, b, g])
+                ys[t, b, h] = S @ toks["Cm"][t, b, g] + D[h] * toks["x"][t, b, h]
+                if t == T - 1:
+                    S_final[b, h] = S
+    return ys, S_final
+
+
+def brute_gdn(S0, toks, T, scale=1.0):
+    """Dense transition matrices M_j = alpha_j (I - beta_j k_j k_j^T):
+    S_t = S0 M_1..M_t + sum_s beta_s v_s k_s^T M_{s+1}..M_t,  o_t = scale S_t q_t."""
+    B, H, DV, DK = S0.shape
+    G = toks["k"].shape[2]
+    hpg = H // G
+    toks = {k: v.astype(np.float64) for k, v in toks.items()}
+    I = np.eye(DK)
+    ys = np.zeros((T, B, H, DV))
+    S_final = np.zeros_like(S0, dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            g = h // hpg
+            k = toks["k"][:, b, g].astype(np.float64)
+            M = [toks["alpha"][t, b, h] * (I - toks["beta"][t, b, h] * np.outer(k[t], k[t])) for t in range(T)]
+            for t in range(T):
+                prod_all = I.copy()
+                for j in range(t + 1):
+                    prod_all = prod_all @ M[j]
+                S = S0[b, h].astype(np.float64) @ prod_all
+                for s in range(t + 1):
+                    tail = I.copy()
+                    for j in range(s + 1, t + 1):
+                        tail = tail @ M[j]
+                    S = S + toks["beta"][s, b, h] * np.outer(toks["v"][s, b, h], k[s]) @ tail
+                ys[t, b, h] = scale * S @ toks["q"][t, b, g]
+                if t == T - 1:
+                    S_final[b, h] = S
+    return ys, S_final
+
+
+def run_mamba2_oracle(S0, A, D, toks, T):
+    S = S0.astype(np.float64).copy()
+    ys = np.stack([ro.mamba2_token(S, *(toks[k][t] for k in ("x", "Bm", "Cm", "dt")), A, D) for t in range(T)])
+    return ys, S
+
+
+def run_gdn_oracle(S0, toks, T, scale=1.0):
+    S = S0.astype(np.float64).copy()
+    ys = np.stack([ro.gdn_token(S, *(toks[k][t] for k in ("q", "k", "v", "alpha", "beta")), scale) for t in range(T)])
+    return ys, S
+
+
+# --------------------------------------------------------------------------
+# Recurrences vs brute force
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("G", [1, 2])
+def test_mamba2_matches_unrolled_sum(G):
+    B, H, P, N, T = 2, 4, 3, 5, 40
+    A, D = synth.mamba2_params(11, H)
+    toks = synth.mamba2_tokens(11, T, B, H, G, P, N)
+    S0 = synth.checkpoint(11, (B, H, P, N), std=0.5)
+    y_o, S_o = run_mamba2_oracle(S0, A, D, toks, T)
+    y_b, S_b = brute_mamba2(S0, A, D, toks, T)
+    assert np.max(np.abs(y_o - y_b)) <= 1e-12 * max(1.0, np.max(np.abs(y_b)))
+    assert np.max(np.abs(S_o - S_b)) <= 1e-12 * max(1.0, np.max(np.abs(S_b)))
+
+
+@pytest.mark.parametrize("G", [1, 2])
+def test_gdn_matches_transition_products(G):
+    B, H, DK, DV, T = 1, 2, 4, 3, 30
+    toks = synth.gdn_tokens(12, T, B, H, G, DK, DV)
+    S0 = synth.checkpoint(12, (B, H, DV, DK), std=0.5)
+    y_o, S_o = run_gdn_oracle(S0, toks, T, scale=0.7)
+    y_b, S_b = brute_gdn(S0, toks, T, scale=0.7)
+    assert np.max(np.abs(y_o - y_b)) <= 1e-12 * max(1.0, np.max(np.abs(y_b)))
+    assert np.max(np.abs(S_o - S_b)) <= 1e-12 * max(1.0, np.max(np.abs(S_b)))
+
+
+def test_gdn_rectangular_state_orientation():
+    """d_v != d_k: the state is d_v x d_k, o has d_v entries (a transposed state fails)."""
+    B, H, DK, DV, T = 1, 1, 5, 2, 6
+    toks = synth.gdn_tokens(13, T, B, H, H, DK, DV)
+    S0 = synth.checkpoint(13, (B, H, DV, DK), std=0.5)
+    y_o, _ = run_gdn_oracle(S0, toks, T)
+    y_b, _ = brute_gdn(S0, toks, T)
+    assert y_o.shape == (T, B, H, DV)
+    np.testing.assert_allclose(y_o, y_b, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Special cases with closed forms
+# --------------------------------------------------------------------------
+
+def test_mamba2_single_step_from_zero():
+    B, H, G, P, N = 2, 3, 1, 4, 6
+    A, D = (np.asarray(a, np.float64) for a in synth.mamba2_params(1, H))
+    tok = f64(synth.token(synth.mamba2_tokens(1, 1, B, H, G, P, N), 0))
+    S = np.zeros((B, H, P, N))
+    y = ro.mamba2_token(S, tok["x"], tok["Bm"], tok["Cm"], tok["dt"], A, D)
+    for b in range(B):
+        for h in range(H):
+            bc = float(np.dot(tok["Bm"][b, 0].astype(np.float64), tok["Cm"][b, 0]))
+            want = (tok["dt"][b, h] * bc + D[h]) * tok["x"][b, h].astype(np.float64)
+            np.testing.assert_allclose(y[b, h], want, rtol=1e-13, atol=1e-13)
+
+
+def test_mamba2_zero_decay_is_running_sum():
+    B, H, G, P, N, T = 1, 2, 1, 3, 4, 12
+    toks = f64(synth.mamba2_tokens(2, T, B, H, G, P, N))
+    A = np.zeros(H)
+    D = np.zeros(H)
+    S0 = synth.checkpoint(2, (B, H, P, N), std=1.0).astype(np.float64)
+    S = S0.copy()
+    for t in range(T):
+        ro.mamba2_token(S, *(toks[k][t] for k in ("x", "Bm", "Cm", "dt")), A, D)
+    want = S0 + sum(toks["dt"][t][:, :, None, None] * toks["x"][t][:, :, :, None] * toks["Bm"][t][:, :1, None, :]
+                    for t in range(T))
+    np.testing.assert_allclose(S, want, rtol=1e-13, atol=1e-13)
+
+
+def test_mamba2_zero_dt_keeps_state():
+    B, H, G, P, N = 1, 2, 1, 3, 4
+    A, D = (np.asarray(a, np.float64) for a in synth.mamba2_params(3, H))
+    tok = f64(synth.token(synth.mamba2_tokens(3, 1, B, H, G, P, N), 0))
+    tok["dt"] = np.zeros_like(tok["dt"])
+    S0 = synth.checkpoint(3, (B, H, P, N), std=1.0).astype(np.float64)
+    S = S0.copy()
+    y = ro.mamba2_token(S, tok["x"], tok["Bm"], tok["Cm"], tok["dt"], A, D)
+    np.testing.assert_array_equal(S, S0)
+    want = np.einsum("bhpn,bn->bhp", S0, tok["Cm"][:, 0].astype(np.float64)) + D[None, :, None] * tok["x"]
+    np.testing.assert_allclose(y, want, rtol=1e-13, atol=1e-13)
+
+
+def test_mamba2_group_mapping():
+    """Heads h use B/C of group h // (H/G): changing group 1's B alters only heads 2,3."""
+    B, H, G, P, N = 1, 4, 2, 2, 3
+    A, D = synth.mamba2_params(4, H)
+    tok = synth.token(synth.mamba2_tokens(4, 1, B, H, G, P, N), 0)
+    S1 = np.zeros((B, H, P, N))
+    y1 = ro.mamba2_token(S1, tok["x"], tok["Bm"], tok["Cm"], tok["dt"], A, D)
+    Bm2 = tok["Bm"].copy()
+    Bm2[0, 1] += 1.0
+    S2 = np.zeros((B, H, P, N))
+    y2 = ro.mamba2_token(S2, tok["x"], Bm2, tok["Cm"], tok["dt"], A, D)
+    np.testing.assert_array_equal(y1[0, :2], y2[0, :2])
+    assert np.all(y1[0, 2:] != y2[0, 2:])
+
+
+def test_gdn_zero_beta_is_pure_decay():
+    B, H, DK, DV, T = 1, 2, 4, 4, 7
+    toks = f64(synth.gdn_tokens(5, T, B, H, H, DK, DV))
+    toks["beta"] = np.zeros_like(toks["beta"])
+    S0 = synth.checkpoint(5, (B, H, DV, DK), std=1.0).astype(np.float64)
+    S = S0.copy()
+    for t in range(T):
+        o = ro.gdn_token(S, *(toks[k][t] for k in ("q", "k", "v", "alpha", "beta")))
+    decay = np.prod(toks["alpha"].astype(np.float64), axis=0)[0]
+    np.testing.assert_allclose(S[0], decay[:, None, None] * S0[0], rtol=1e-13)
+    np.testing.assert_allclose(o[0], np.einsum("hij,hj->hi", S[0], toks["q"][T - 1, 0]), rtol=1e-13)
+
+
+def test_gdn_unit_beta_overwrites_key_direction():
+    """beta = 1 and |k| = 1: after the update S k = v for any alpha (delta-rule overwrite)."""
+    B, H, DK, DV = 2, 3, 8, 5
+    tok = f64(synth.token(synth.gdn_tokens(6, 1, B, H, H, DK, DV), 0))
+    k = tok["k"].astype(np.float64)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    tok["beta"] = np.ones_like(tok["beta"])
+    S = synth.checkpoint(6, (B, H, DV, DK), std=1.0).astype(np.float64)
+    ro.gdn_token(S, tok["q"], k, tok["v"], tok["alpha"], tok["beta"])
+    Sk = np.einsum("bhij,bhj->bhi", S, k)
+    np.testing.assert_allclose(Sk, tok["v"], rtol=1e-12, atol=1e-12)
+
+
+def test_gdn_single_step_from_zero():
+    B, H, DK, DV = 2, 2, 6, 3
+    tok = f64(synth.token(synth.gdn_tokens(7, 1, B, H, H, DK, DV), 0))
+    S = np.zeros((B, H, DV, DK))
+    o = ro.gdn_token(S, tok["q"], tok["k"], tok["v"], tok["alpha"], tok["beta"], 0.5)
+    kq = np.einsum("bhj,bhj->bh", tok["k"].astype(np.float64), tok["q"])
+    want = 0.5 * (tok["beta"] * kq)[:, :, None] * tok["v"]
+    np.testing.assert_allclose(o, want, rtol=1e-13, atol=1e-14)
+
+
+def test_gdn_orthonormal_keys_projection():
+    """alpha = beta = 1 with orthonormal keys: S_T = S0 (I - K^T K) + V^T K."""
+    DK, DV, T = 6, 3, 4
+    rng = np.random.default_rng(8)
+    Q, _ = np.linalg.qr(rng.standard_normal((DK, DK)))
+    K = Q[:T]                                          # T orthonormal rows
+    V = rng.standard_normal((T, DV))
+    S0 = rng.standard_normal((1, 1, DV, DK))
+    S = S0.copy()
+    for t in range(T):
+        ro.gdn_token(S, K[t][None, None], K[t][None, None], V[t][None, None], np.ones((1, 1)), np.ones((1, 1)))
+    want = S0[0, 0] @ (np.eye(DK) - K.T @ K) + V.T @ K
+    np.testing.assert_allclose(S[0, 0], want, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Quantizers: OCP MX v1.0 tables, a library cast, hand-derived block scales
+# --------------------------------------------------------------------------
+
+def test_e4m3_table_landmarks():
+    """OCP FP8 E4M3: max normal 448 (S.1111.110), min normal 2^-6, max subnormal 7*2^-9,
+    min subnormal 2^-9, S.1111.111 is NaN, sign bit mirrors."""
+    L = ro.lib()
+    assert L.oracle_e4m3_decode(0x7E) == 448.0
+    assert L.oracle_e4m3_decode(0x08) == 2.0 ** -6
+    assert L.oracle_e4m3_decode(0x07) == 7 * 2.0 ** -9
+    assert L.oracle_e4m3_decode(0x01) == 2.0 ** -9
+    assert L.oracle_e4m3_decode(0x38) == 1.0
+    assert L.oracle_e4m3_decode(0x3C) == 1.5
+    assert np.isnan(L.oracle_e4m3_decode(0x7F)) and np.isnan(L.oracle_e4m3_decode(0xFF))
+    assert L.oracle_e4m3_decode(0xBE) == -448.0 or L.oracle_e4m3_decode(0xFE) == -448.0
+    assert L.oracle_e4m3_decode(0xFE) == -448.0
+
+
+def test_e4m3_encode_matches_torch_cast_in_range():
+    torch = pytest.importorskip("torch")
+    # every finite code value, every midpoint between neighbours, and random values
+    vals = np.array([ro.lib().oracle_e4m3_decode(c) for c in range(0x7F)])
+    mids = 0.5 * (vals[1:] + vals[:-1])
+    rng = np.random.default_rng(9)
+    rand = rng.uniform(-448, 448, 20000) * 2.0 ** rng.integers(-12, 1, 20000)
+    x = np.concatenate([vals, -vals, mids, -mids, rand]).astype(np.float32)
+    ours = ro.e4m3_encode(x.astype(np.float64))
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_e4m3_saturates_beyond_max():
+    big = np.array([449.0, 464.0, 480.0, 1e6, np.inf, -500.0, -np.inf])
+    np.testing.assert_array_equal(ro.e4m3_encode(big), [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE])
+    assert ro.e4m3_encode(np.array([np.nan]))[0] == 0x7F
+
+
+def test_e2m1_table_and_ties():
+    L = ro.lib()
+    table = [L.oracle_e2m1_decode(c) for c in range(16)]
+    assert table[:8] == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert table[8:] == [-0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+    # ties go to the even code (mantissa bit 0)
+    ties = {0.25: 0, 0.75: 2, 1.25: 2, 1.75: 4, 2.5: 4, 3.5: 6, 5.0: 6}
+    for v, code in ties.items():
+        assert L.oracle_e2m1_encode(v) == code, v
+        assert L.oracle_e2m1_encode(-v) == code | 8, v
+    assert L.oracle_e2m1_encode(7.0) == 7 and L.oracle_e2m1_encode(1e9) == 7
+    assert L.oracle_e2m1_encode(0.26) == 1 and L.oracle_e2m1_encode(2.6) == 5
+
+
+def test_mxfp4_block_scale_rule():
+    """Shared exponent floor(log2(amax)) - 2 (E2M1's largest exponent), E8M0 bias 127."""
+    cases = [(6.0, 127), (4.0, 127), (7.9, 127), (8.0, 128), (0.3, 123), (1.0, 125), (2.0 ** -140, 0)]
+    for amax, scale_code in cases:
+        v = np.zeros(32)
+        v[5] = amax
+        v[9] = -amax / 3
+        codes, scales = ro.mxfp4_quantize(v)
+        assert scales[0] == scale_code, (amax, scales[0])
+    codes, scales = ro.mxfp4_quantize(np.zeros(32))
+    assert scales[0] == 0 and not codes.any()
+    # hand example: amax 5 -> X = 0; 5 ties between 4 and 6 -> 4; 0.3 -> 0.5; -2.6 -> -3
+    v = np.zeros(32)
+    v[:4] = [5.0, 0.3, -2.6, 1.2]
+    codes, scales = ro.mxfp4_quantize(v)
+    assert scales[0] == 127
+    assert list(codes[:4]) == [6, 1, 8 | 5, 2]
+    deq = ro.mxfp4_dequantize(codes, scales)
+    assert list(deq[:4]) == [4.0, 0.5, -3.0, 1.0]
+    # amax 12 -> X = 1: values are halved before rounding; 12 -> 6 (x2 = 12), 3.1 -> 1.5 (x2 = 3)
+    v[:4] = [12.0, 3.1, -0.2, 0.0]
+    codes, scales = ro.mxfp4_quantize(v)
+    assert scales[0] == 128
+    assert list(ro.mxfp4_dequantize(codes, scales)[:4]) == [12.0, 3.0, -0.0, 0.0]
+
+
+def test_mxfp4_error_bound():
+    """|deq - v| <= half an E2M1 step times the block scale (no clipping under the floor rule
+    beyond amax*(1 - 6/8) ...): checked as the plain nearest-grid property on random blocks."""
+    rng = np.random.default_rng(10)
+    v = rng.standard_normal((200, 32)) * 2.0 ** rng.integers(-20, 20, (200, 1))
+    codes, scales = ro.mxfp4_quantize(v)
+    deq = ro.mxfp4_dequantize(codes, scales)
+    scale = 2.0 ** (scales.astype(np.float64) - 127)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    for i in range(v.shape[0]):
+        r = np.abs(v[i]) / scale[i]
+        best = np.min(np.abs(grid[None, :] - np.minimum(r, 6.0)[:, None]), axis=1)
+        np.testing.assert_allclose(np.abs(np.abs(deq[i]) / scale[i] - np.minimum(r, 6.0)), best, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Bookkeeping: hand-derived golden trace
+# --------------------------------------------------------------------------
+
+def _load_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            tok = line.split()
+            op, arg = tok[0], tok[1]
+            nums = list(map(int, tok[2:]))
+            rows.append((op, arg, nums))
+    return rows
+
+
+def test_bookkeeping_golden_trace_cap4():
+    B, H, G, P, N, cap = 3, 1, 1, 2, 2, 4
+    A, D = synth.mamba2_params(20, H)
+    sess = ro.Mamba2Session(A, D, np.zeros((B, H, P, N)), cap=cap)
+    toks = synth.mamba2_tokens(20, 64, B, H, G, P, N)
+    t = 0
+    for op, arg, want in _load_golden("bookkeeping_cap4.txt"):
+        if op == "decode":
+            sess.decode(synth.token(toks, t)); t += 1
+        elif op == "spec":
+            k = int(arg)
+            sess.spec_append([synth.token(toks, t + j) for j in range(k)]); t += k
+        elif op == "commit":
+            sess.commit([int(a) for a in arg.split(",")])
+        elif op == "rollback":
+            sess.rollback()
+        elif op == "flush":
+            sess.flush()
+        L, Pd, F = sess.trace()
+        got = list(L) + list(Pd) + list(F) + [sess.err]
+        assert got == want, (op, arg, got, want)
+
+
+def test_phase_errors():
+    sess = ro.Mamba2Session(np.zeros(1), np.zeros(1), np.zeros((1, 1, 1, 1)), cap=4)
+    tok = {"x": np.zeros((1, 1, 1)), "Bm": np.zeros((1, 1, 1)), "Cm": np.zeros((1, 1, 1)), "dt": np.zeros((1, 1))}
+    with pytest.raises(ro.PhaseError):
+        sess.rollback()
+    sess.spec_append([tok, tok])
+    for bad in (lambda: sess.decode(tok), sess.flush, lambda: sess.spec_append([tok])):
+        with pytest.raises(ro.PhaseError):
+            bad()
+    with pytest.raises(ValueError):
+        ro.Mamba2Session(np.zeros(1), np.zeros(1), np.zeros((1, 1, 1, 1)), cap=17)
+
+
+def test_decode_flush_cadence_cap16():
+    """With the 16-entry buffer, flushes land on steps 16, 32, 48, 64 and len cycles 1..15,0."""
+    B, H, G, P, N = 2, 1, 1, 2, 2
+    A, D = synth.mamba2_params(21, H)
+    sess = ro.Mamba2Session(A, D, np.zeros((B, H, P, N)))
+    toks = synth.mamba2_tokens(21, 64, B, H, G, P, N)
+    for t in range(64):
+        sess.decode(synth.token(toks, t))
+        L, Pd, F = sess.trace()
+        assert list(L) == [(t + 1) % 16] * B and list(F) == [(t + 1) // 16] * B and not Pd.any()
+    assert [e[0] for e in sess.flush_events[::B]] == [15, 31, 47, 63]
+
+
+# --------------------------------------------------------------------------
+# Op-runner semantics: what the pages fix about flush and rollback
+# --------------------------------------------------------------------------
+
+def _mk(kind, B=2, cap=4, seed=30, read_copy=None):
+    if kind == "mamba2":
+        H, G, P, N = 2, 1, 3, 4
+        A, D = synth.mamba2_params(seed, H)
+        S0 = synth.checkpoint(seed, (B, H, P, N))
+        toks = synth.mamba2_tokens(seed, 80, B, H, G, P, N)
+        return (lambda: ro.Mamba2Session(A, D, S0, cap=cap, read_copy=read_copy)), toks
+    H, DK, DV = 2, 4, 3
+    S0 = synth.checkpoint(seed, (B, H, DV, DK))
+    toks = synth.gdn_tokens(seed, 80, B, H, H, DK, DV)
+    return (lambda: ro.GDNSession(S0, cap=cap, read_copy=read_copy)), toks
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_flush_then_continue_equals_uninterrupted(kind):
+    """Folding the buffer into the checkpoint early changes nothing downstream."""
+    mk, toks = _mk(kind)
+    a, b = mk(), mk()
+    ya, yb = [], []
+    for t in range(23):
+        ya.append(a.decode(synth.token(toks, t)))
+        yb.append(b.decode(synth.token(toks, t)))
+        if t in (2, 9, 10):
+            b.flush()
+    np.testing.assert_array_equal(np.stack(ya), np.stack(yb))
+    np.testing.assert_array_equal(a.S, b.S)
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_rollback_equals_never_appended(kind):
+    mk, toks = _mk(kind)
+    a, b = mk(), mk()
+    for t in range(3):
+        a.decode(synth.token(toks, t)); b.decode(synth.token(toks, t))
+    a.spec_append([synth.token(toks, 50 + j) for j in range(3)])
+    a.rollback()
+    for t in range(3, 12):
+        np.testing.assert_array_equal(a.decode(synth.token(toks, t)), b.decode(synth.token(toks, t)))
+    np.testing.assert_array_equal(a.S, b.S)
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_spec_outputs_and_commit_equal_sequential(kind):
+    mk, toks = _mk(kind, cap=16)
+    a, b = mk(), mk()
+    for t in range(5):
+        a.decode(synth.token(toks, t)); b.decode(synth.token(toks, t))
+    drafts = [synth.token(toks, 5 + j) for j in range(4)]
+    ys = a.spec_append(drafts)
+    seq = [b.decode(d) for d in drafts[:2]]
+    np.testing.assert_array_equal(ys[0], seq[0])
+    np.testing.assert_array_equal(ys[1], seq[1])
+    a.commit([2, 2])
+    np.testing.assert_array_equal(a.S, b.S)
+    assert list(a.len) == list(b.len) == [7, 7]
+
+
+def test_normwise_error_definition():
+    ref = np.array([[1.0, -2.0], [1e-40, 0.0]])
+    got = np.array([[1.0, -2.002], [0.0, 0.0]])
+    assert abs(ro.normwise_error(got, ref) - max(0.002 / 2.0, 1e-40 / 1e-30)) < 1e-15
