@@ -1,0 +1,309 @@
+"""ctypes binding of libreplayssm.so (include/replayssm.h): argument marshalling only.
+
+Every step of the decode path runs in the HIP library; this module turns torch
+tensors into device pointers and the current HIP stream into a handle, and
+turns non-OK status codes into exceptions.  Importing it without the built
+library raises immediately: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBPATH = os.path.join(_HERE, "libreplayssm.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "replayssm.h")
+
+if not os.path.exists(LIBPATH):
+    raise ImportError(f"{LIBPATH} is not built; run __graft_entry__.build() (hipcc, gfx950) first")
+
+_lib = ctypes.CDLL(LIBPATH)
+
+# ---- constants (mirrors of the header's enums) --------------------------
+ABI_VERSION = 1
+MAX_BUF = 16
+OK, ERR_ARG, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_STATE, ERR_CAPACITY, ERR_UNSUPPORTED, ERR_HIP = range(9)
+MAMBA2, GDN = 0, 1
+NONE, F32, F16, BF16, FP8_E4M3, MXFP4 = range(6)
+DEVERR_COMMIT_CLAMPED = 0x1
+FLAG_VALU_FOLD = 0x1
+
+
+class ReplayConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "abi_version", "kind", "batch", "nheads", "ngroups", "head_dim", "state_dim", "buf_cap",
+        "ckpt_dtype", "read_copy", "io_dtype", "flags")] + [("scale", ctypes.c_float)]
+
+
+class ReplayInputs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("x", "B", "C", "dt", "A", "D", "q", "k", "v", "alpha", "beta")]
+
+
+class ReplayLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in (
+        "total_bytes", "ckpt_off", "ckpt_bytes", "rcopy_off", "rcopy_bytes", "rscale_off", "rscale_bytes")] + [
+        ("buf_off", ctypes.c_uint64 * 4), ("buf_bytes", ctypes.c_uint64 * 4)] + [
+        (n, ctypes.c_uint64) for n in ("book_off", "book_bytes", "err_off")]
+
+
+_vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+_CP, _IP, _LP = ctypes.POINTER(ReplayConfig), ctypes.POINTER(ReplayInputs), ctypes.POINTER(ReplayLayout)
+
+_SIGS = {
+    "replay_abi_version": ([], _i32),
+    "replay_status_str": ([_i32], ctypes.c_char_p),
+    "replay_last_error": ([], ctypes.c_char_p),
+    "replay_config_check": ([_CP], _i32),
+    "replay_state_bytes": ([_CP], _sz),
+    "replay_state_alloc": ([_CP, _vp, _sz, _vp, ctypes.POINTER(_vp)], _i32),
+    "replay_state_free": ([_vp], _i32),
+    "replay_state_layout": ([_vp, _LP], _i32),
+    "replay_state_phase": ([_vp], _i32),
+    "replay_load_checkpoint": ([_vp, _vp, _vp], _i32),
+    "replay_read_checkpoint": ([_vp, _vp, _vp], _i32),
+    "replay_read_copy": ([_vp, _vp, _vp, _vp], _i32),
+    "replay_read_book": ([_vp, _vp, _vp, _vp], _i32),
+    "replay_decode_step": ([_vp, _IP, _vp, _vp], _i32),
+    "replay_flush": ([_vp, _IP, _vp], _i32),
+    "replay_spec_append": ([_vp, _i32, _IP, _vp, _vp], _i32),
+    "replay_spec_commit": ([_vp, _vp, _vp], _i32),
+    "replay_spec_rollback": ([_vp, _vp], _i32),
+    "replay_conv_decode_step": ([_CP, _vp, _IP, _vp, _vp], _i32),
+    "replay_conv_spec_step": ([_CP, _vp, _vp, _i32, _IP, _vp, _vp], _i32),
+    "replay_conv_spec_restore": ([_CP, _vp, _vp, _i32, _vp, _vp], _i32),
+    "replay_stream_copy": ([_vp, _vp, _sz, _vp], _i32),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+
+def header_functions(path: str = HEADER):
+    """Names of the functions the public header declares."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(replay_[a-z0-9_]+)\s*\(", text)) - {"replay_state"})
+
+
+class ReplayError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = _lib.replay_last_error().decode() or _lib.replay_status_str(status).decode()
+        super().__init__(f"{where}: {_lib.replay_status_str(status).decode()} ({msg})")
+
+
+def _check(status, where):
+    if status != OK:
+        raise ReplayError(status, where)
+
+
+def lib():
+    return _lib
+
+
+def make_config(kind, batch, nheads, ngroups, head_dim, state_dim, buf_cap=16, io_dtype=F32,
+                read_copy=NONE, ckpt_dtype=F32, flags=0, scale=1.0):
+    return ReplayConfig(ABI_VERSION, kind, batch, nheads, ngroups, head_dim, state_dim, buf_cap,
+                        ckpt_dtype, read_copy, io_dtype, flags, scale)
+
+
+def config_check(cfg: ReplayConfig) -> int:
+    return _lib.replay_config_check(ctypes.byref(cfg))
+
+
+def state_bytes(cfg: ReplayConfig) -> int:
+    return _lib.replay_state_bytes(ctypes.byref(cfg))
+
+
+# ---- torch marshalling -----------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _io_torch_dtype(io):
+    torch = _torch()
+    return torch.bfloat16 if io == BF16 else torch.float32
+
+
+def make_inputs(cfg: ReplayConfig, tensors: dict, params: dict | None = None) -> ReplayInputs:
+    """Pack a dict of device tensors into ReplayInputs.
+
+    Mamba-2 keys: x, Bm, Cm, dt (io dtype) and A, D (fp32, via `params` or `tensors`).
+    GDN keys: q, k, v (io dtype), alpha, beta (fp32)."""
+    torch = _torch()
+    iot = _io_torch_dtype(cfg.io_dtype)
+    p = dict(params or {})
+    p.update(tensors)
+    ri = ReplayInputs()
+    if cfg.kind == MAMBA2:
+        ri.x = _ptr(p.get("x"), iot, "x")
+        ri.B = _ptr(p.get("Bm"), iot, "Bm")
+        ri.C = _ptr(p.get("Cm"), iot, "Cm")
+        ri.dt = _ptr(p.get("dt"), iot, "dt")
+        ri.A = _ptr(p.get("A"), torch.float32, "A")
+        ri.D = _ptr(p.get("D"), torch.float32, "D")
+    else:
+        ri.q = _ptr(p.get("q"), iot, "q")
+        ri.k = _ptr(p.get("k"), iot, "k")
+        ri.v = _ptr(p.get("v"), iot, "v")
+        ri.alpha = _ptr(p.get("alpha"), torch.float32, "alpha")
+        ri.beta = _ptr(p.get("beta"), torch.float32, "beta")
+    return ri
+
+
+class ReplayState:
+    """A replayed SSM layer state (checkpoint + input buffer) in caller-owned device memory."""
+
+    def __init__(self, cfg: ReplayConfig, device="cuda"):
+        torch = _torch()
+        _check(_lib.replay_config_check(ctypes.byref(cfg)), "config")
+        self.cfg = cfg
+        self.device = torch.device(device)
+        n = _lib.replay_state_bytes(ctypes.byref(cfg))
+        self.mem = torch.empty(n + 256, dtype=torch.uint8, device=self.device)
+        base = self.mem.data_ptr()
+        self._off = (-base) % 256
+        h = ctypes.c_void_p()
+        _check(_lib.replay_state_alloc(ctypes.byref(cfg), ctypes.c_void_p(base + self._off), n, _stream(),
+                                       ctypes.byref(h)), "replay_state_alloc")
+        self.h = h
+        self.iot = _io_torch_dtype(cfg.io_dtype)
+
+    def __del__(self):
+        h = getattr(self, "h", None)
+        if h is not None and h.value:
+            _lib.replay_state_free(h)
+            self.h = None
+
+    # -- shapes
+    @property
+    def ckpt_shape(self):
+        c = self.cfg
+        return (c.batch, c.nheads, c.head_dim, c.state_dim)
+
+    def layout(self) -> ReplayLayout:
+        L = ReplayLayout()
+        _check(_lib.replay_state_layout(self.h, ctypes.byref(L)), "replay_state_layout")
+        return L
+
+    def phase(self) -> int:
+        return _lib.replay_state_phase(self.h)
+
+    # -- checkpoint I/O
+    def load_checkpoint(self, S):
+        torch = _torch()
+        S = S.to(device=self.device, dtype=torch.float32).contiguous()
+        assert tuple(S.shape) == self.ckpt_shape
+        _check(_lib.replay_load_checkpoint(self.h, _ptr(S), _stream()), "replay_load_checkpoint")
+        self._keep = S
+
+    def read_checkpoint(self):
+        torch = _torch()
+        out = torch.empty(self.ckpt_shape, dtype=torch.float32, device=self.device)
+        _check(_lib.replay_read_checkpoint(self.h, _ptr(out), _stream()), "replay_read_checkpoint")
+        return out
+
+    def read_copy(self):
+        torch = _torch()
+        c = self.cfg
+        codes = torch.empty(self.ckpt_shape, dtype=torch.uint8, device=self.device)
+        scales = None
+        if c.read_copy == MXFP4:
+            scales = torch.empty((c.batch, c.nheads, c.head_dim, c.state_dim // 32), dtype=torch.uint8,
+                                 device=self.device)
+        _check(_lib.replay_read_copy(self.h, _ptr(codes), _ptr(scales), _stream()), "replay_read_copy")
+        return codes, scales
+
+    def read_book(self):
+        """(len, pend, fc, err) as device tensors."""
+        torch = _torch()
+        book = torch.empty((3, self.cfg.batch), dtype=torch.int32, device=self.device)
+        err = torch.empty((1,), dtype=torch.int32, device=self.device)
+        _check(_lib.replay_read_book(self.h, _ptr(book), _ptr(err), _stream()), "replay_read_book")
+        return book[0], book[1], book[2], err
+
+    # -- the decode path
+    def decode(self, tokens: dict, params: dict | None = None, y=None):
+        torch = _torch()
+        c = self.cfg
+        if y is None:
+            y = torch.empty((1, c.batch, c.nheads, c.head_dim), dtype=self.iot, device=self.device)
+        ri = make_inputs(c, tokens, params)
+        _check(_lib.replay_decode_step(self.h, ctypes.byref(ri), _ptr(y, self.iot, "y"), _stream()),
+               "replay_decode_step")
+        return y
+
+    def flush(self, params: dict | None = None):
+        ri = make_inputs(self.cfg, {}, params)
+        _check(_lib.replay_flush(self.h, ctypes.byref(ri), _stream()), "replay_flush")
+
+    def spec_append(self, k: int, drafts: dict, params: dict | None = None, y=None):
+        torch = _torch()
+        c = self.cfg
+        if y is None:
+            y = torch.empty((k, c.batch, c.nheads, c.head_dim), dtype=self.iot, device=self.device)
+        ri = make_inputs(c, drafts, params)
+        _check(_lib.replay_spec_append(self.h, int(k), ctypes.byref(ri), _ptr(y, self.iot, "y"), _stream()),
+               "replay_spec_append")
+        return y
+
+    def commit(self, accepted):
+        torch = _torch()
+        _check(_lib.replay_spec_commit(self.h, _ptr(accepted, torch.int32, "accepted"), _stream()),
+               "replay_spec_commit")
+
+    def rollback(self):
+        _check(_lib.replay_spec_rollback(self.h, _stream()), "replay_spec_rollback")
+
+
+# ---- conventional baselines -----------------------------------------------------
+def conv_decode_step(cfg: ReplayConfig, S, tokens: dict, params: dict | None = None, y=None):
+    torch = _torch()
+    if y is None:
+        y = torch.empty((1, cfg.batch, cfg.nheads, cfg.head_dim), dtype=_io_torch_dtype(cfg.io_dtype), device=S.device)
+    ri = make_inputs(cfg, tokens, params)
+    _check(_lib.replay_conv_decode_step(ctypes.byref(cfg), _ptr(S, torch.float32, "S"), ctypes.byref(ri),
+                                        _ptr(y), _stream()), "replay_conv_decode_step")
+    return y
+
+
+def conv_spec_step(cfg: ReplayConfig, S, snaps, k: int, drafts: dict, params: dict | None = None, y=None):
+    torch = _torch()
+    if y is None:
+        y = torch.empty((k, cfg.batch, cfg.nheads, cfg.head_dim), dtype=_io_torch_dtype(cfg.io_dtype), device=S.device)
+    ri = make_inputs(cfg, drafts, params)
+    _check(_lib.replay_conv_spec_step(ctypes.byref(cfg), _ptr(S, torch.float32, "S"), _ptr(snaps, torch.float32, "snaps"),
+                                      int(k), ctypes.byref(ri), _ptr(y), _stream()), "replay_conv_spec_step")
+    return y
+
+
+def conv_spec_restore(cfg: ReplayConfig, S, snaps, k: int, accepted):
+    torch = _torch()
+    _check(_lib.replay_conv_spec_restore(ctypes.byref(cfg), _ptr(S, torch.float32, "S"),
+                                         _ptr(snaps, torch.float32, "snaps"), int(k),
+                                         _ptr(accepted, torch.int32, "accepted"), _stream()),
+           "replay_conv_spec_restore")
+
+
+def stream_copy(dst, src, nbytes: int):
+    _check(_lib.replay_stream_copy(_ptr(dst), _ptr(src), int(nbytes), _stream()), "replay_stream_copy")

@@ -1,0 +1,132 @@
+// aux.hip -- bookkeeping, layout conversion and measurement kernels.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace rs {
+
+// ---- bookkeeping ----------------------------------------------------------
+// Book layout: int32 [2 copies][3 fields][B]; field 0 = len, 1 = pend, 2 = fc.
+// Each launch that changes the bookkeeping reads copy `parity` and writes copy
+// `parity ^ 1`, so every workgroup of a launch sees the same pre-launch values.
+
+// Commit (accepted != null) or rollback (accepted == null): the accepted
+// prefix advances the pointer, the rest of the drafts is dropped.
+__global__ void book_commit_kernel(int32_t* book, uint32_t* err, int B, int parity, const int32_t* accepted)
+{
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= B) return;
+    const int32_t* cur = book + (size_t)parity * 3 * B;
+    int32_t* nxt = book + (size_t)(parity ^ 1) * 3 * B;
+    const int pend = cur[B + b];
+    const int a = accepted ? accepted[b] : 0;
+    const int ac = a < 0 ? 0 : (a > pend ? pend : a);
+    if (ac != a) atomicOr(err, REPLAY_COMMIT_CLAMPED_BIT);
+    nxt[b] = cur[b] + ac;
+    nxt[B + b] = 0;
+    nxt[2 * B + b] = cur[2 * B + b];
+}
+
+__global__ void book_reset_kernel(int32_t* book, uint32_t* err, int B, int parity)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < 3 * B) book[(size_t)parity * 3 * B + i] = 0;
+    if (i == 0) *err = 0u;
+}
+
+hipError_t launch_book_commit(int32_t* book, uint32_t* err, int B, int parity, const int32_t* accepted,
+                              hipStream_t s)
+{
+    hipLaunchKernelGGL(book_commit_kernel, dim3((B + 255) / 256), dim3(256), 0, s, book, err, B, parity, accepted);
+    return hipGetLastError();
+}
+
+hipError_t launch_book_reset(int32_t* book, uint32_t* err, int B, int parity, hipStream_t s)
+{
+    hipLaunchKernelGGL(book_reset_kernel, dim3((3 * B + 255) / 256), dim3(256), 0, s, book, err, B, parity);
+    return hipGetLastError();
+}
+
+// ---- zero fill (a kernel, not a memset, so it is safe under graph capture)
+__global__ void fill_zero_kernel(uint4* p, size_t n16, uint8_t* tail, size_t ntail)
+{
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) p[i] = make_uint4(0, 0, 0, 0);
+    if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0;
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s)
+{
+    const size_t n16 = bytes / 16, ntail = bytes % 16;
+    size_t blocks = (n16 + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    if (blocks == 0) blocks = 1;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint4*)p, n16,
+                       (uint8_t*)p + n16 * 16, ntail);
+    return hipGetLastError();
+}
+
+// ---- checkpoint layout conversion -----------------------------------------
+// Logical tile [C][R] row-major (C = output axis, R = reduction axis) <->
+// fragment order (common.hpp).  One thread per float4.
+__device__ __forceinline__ size_t frag_to_logical(size_t q, int C, int R)
+{
+    const int NB = R >> 4;
+    const size_t per_tile = (size_t)C * R / 4;
+    const size_t tile = q / per_tile;
+    size_t rem = q - tile * per_tile;
+    const int lane = (int)(rem & 63);
+    rem >>= 6;
+    const int nb = (int)(rem % NB);
+    const int strip = (int)(rem / NB);
+    const int c = 16 * strip + (lane & 15);
+    const int r = 16 * nb + 4 * (lane >> 4);
+    return tile * (size_t)C * R + (size_t)c * R + r;
+}
+
+__global__ void tiles_to_logical_kernel(const float* ck, float* out, size_t n4, int C, int R)
+{
+    const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= n4) return;
+    st4(out + frag_to_logical(q, C, R), ld4(ck + q * 4));
+}
+
+__global__ void logical_to_tiles_kernel(const float* in, float* ck, size_t n4, int C, int R)
+{
+    const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= n4) return;
+    st4(ck + q * 4, ld4(in + frag_to_logical(q, C, R)));
+}
+
+hipError_t launch_tiles_to_logical(const float* ckpt, float* out, int tiles, int C, int R, hipStream_t s)
+{
+    const size_t n4 = (size_t)tiles * C * R / 4;
+    hipLaunchKernelGGL(tiles_to_logical_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, ckpt, out, n4, C, R);
+    return hipGetLastError();
+}
+
+hipError_t launch_logical_to_tiles(const float* in, float* ckpt, int tiles, int C, int R, hipStream_t s)
+{
+    const size_t n4 = (size_t)tiles * C * R / 4;
+    hipLaunchKernelGGL(logical_to_tiles_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, in, ckpt, n4, C, R);
+    return hipGetLastError();
+}
+
+// ---- streaming copy (bandwidth ceiling and byte-counter reference) --------
+__global__ __launch_bounds__(256) void stream_copy_kernel(const f32x4* src, f32x4* dst, size_t n4)
+{
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+        __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t s)
+{
+    const size_t n4 = bytes / 16;
+    size_t blocks = (n4 + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    if (blocks == 0) blocks = 1;
+    hipLaunchKernelGGL(stream_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const f32x4*)src, (f32x4*)dst, n4);
+    return hipGetLastError();
+}
+
+}  // namespace rs

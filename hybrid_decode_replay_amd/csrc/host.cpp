@@ -1,0 +1,509 @@
+// host.cpp -- the C ABI (include/replayssm.h): validation, state layout,
+// phase tracking, kernel selection and launch.  No call synchronizes.
+#include "../../include/replayssm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "internal.hpp"
+
+struct replay_state {
+    replay_config cfg;
+    uint8_t* mem;
+    size_t bytes;
+    replay_layout lay;
+    int parity;   // bookkeeping copy that holds the current values
+    int phase;    // 0 idle, 1 drafts pending
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+replay_status fail(replay_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+replay_status fail(replay_status s, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+replay_status ok()
+{
+    g_err.clear();
+    return REPLAY_OK;
+}
+
+replay_status hip_check(hipError_t e, const char* what)
+{
+    if (e != hipSuccess) return fail(REPLAY_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+uint64_t align256(uint64_t x) { return (x + 255) & ~(uint64_t)255; }
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int io_bytes(const replay_config* c) { return c->io_dtype == REPLAY_BF16 ? 2 : 4; }
+
+replay_status check_config(const replay_config* c)
+{
+    if (!c) return fail(REPLAY_ERR_ARG, "config is NULL");
+    if (c->abi_version != REPLAY_ABI_VERSION)
+        return fail(REPLAY_ERR_ARG, "abi_version %d, library implements %d", c->abi_version, REPLAY_ABI_VERSION);
+    if (c->kind != REPLAY_MAMBA2 && c->kind != REPLAY_GDN) return fail(REPLAY_ERR_ARG, "unknown kind %d", c->kind);
+    if (c->batch < 1 || c->nheads < 1 || c->ngroups < 1)
+        return fail(REPLAY_ERR_SHAPE, "batch, nheads and ngroups must be >= 1");
+    if (c->nheads % c->ngroups != 0) return fail(REPLAY_ERR_SHAPE, "ngroups %d does not divide nheads %d", c->ngroups, c->nheads);
+    if (c->head_dim < 16 || c->head_dim > 256 || c->head_dim % 16 != 0)
+        return fail(REPLAY_ERR_SHAPE, "head_dim %d must be a multiple of 16 in [16, 256]", c->head_dim);
+    const int R = c->state_dim;
+    if (R != 16 && R != 32 && R != 64 && R != 128 && R != 256)
+        return fail(REPLAY_ERR_SHAPE, "state_dim %d must be 16, 32, 64, 128 or 256", R);
+    if (c->buf_cap < 1 || c->buf_cap > REPLAY_MAX_BUF)
+        return fail(REPLAY_ERR_SHAPE, "buf_cap %d must be in [1, %d]", c->buf_cap, REPLAY_MAX_BUF);
+    if ((long long)c->batch * c->nheads > (1LL << 30)) return fail(REPLAY_ERR_SHAPE, "batch * nheads too large");
+    if (c->io_dtype != REPLAY_F32 && c->io_dtype != REPLAY_BF16)
+        return fail(REPLAY_ERR_DTYPE, "io_dtype must be REPLAY_F32 or REPLAY_BF16");
+    if (c->ckpt_dtype != REPLAY_F32) {
+        if (c->ckpt_dtype == REPLAY_F16) return fail(REPLAY_ERR_UNSUPPORTED, "fp16 recurrence checkpoint not built");
+        return fail(REPLAY_ERR_DTYPE, "ckpt_dtype must be REPLAY_F32");
+    }
+    if (c->read_copy != REPLAY_NONE && c->read_copy != REPLAY_FP8_E4M3 && c->read_copy != REPLAY_MXFP4)
+        return fail(REPLAY_ERR_DTYPE, "read_copy must be NONE, FP8_E4M3 or MXFP4");
+    if (c->read_copy == REPLAY_MXFP4 && R % 32 != 0)
+        return fail(REPLAY_ERR_SHAPE, "MXFP4 read copy needs state_dim divisible by 32");
+    if (c->read_copy != REPLAY_NONE) return fail(REPLAY_ERR_UNSUPPORTED, "read copies not built yet");
+    if (c->kind == REPLAY_GDN) return fail(REPLAY_ERR_UNSUPPORTED, "Gated DeltaNet replay kernel not built yet");
+    if (c->flags & ~REPLAY_FLAG_VALU_FOLD) return fail(REPLAY_ERR_ARG, "unknown flags 0x%x", c->flags);
+    return ok();
+}
+
+void compute_layout(const replay_config* c, replay_layout* L)
+{
+    memset(L, 0, sizeof *L);
+    const uint64_t B = c->batch, H = c->nheads, G = c->ngroups, C = c->head_dim, R = c->state_dim, cap = c->buf_cap;
+    const uint64_t tiles = B * H, io = io_bytes(c);
+    uint64_t off = 0;
+    L->ckpt_off = off;
+    L->ckpt_bytes = tiles * C * R * 4;
+    off = align256(off + L->ckpt_bytes);
+    if (c->read_copy == REPLAY_FP8_E4M3) L->rcopy_bytes = tiles * C * R;
+    if (c->read_copy == REPLAY_MXFP4) {
+        L->rcopy_bytes = tiles * C * R / 2;
+        L->rscale_bytes = tiles * C * (R / 32);
+    }
+    L->rcopy_off = off;
+    off = align256(off + L->rcopy_bytes);
+    L->rscale_off = off;
+    off = align256(off + L->rscale_bytes);
+    L->buf_bytes[0] = 2 * B * H * cap * C * io;   // x (Mamba-2) / v (GDN)
+    L->buf_bytes[1] = 2 * B * G * cap * R * io;   // B (Mamba-2) / k (GDN)
+    L->buf_bytes[2] = 2 * B * H * cap * 4;        // dt (Mamba-2) / alpha (GDN), fp32
+    L->buf_bytes[3] = c->kind == REPLAY_GDN ? 2 * B * H * cap * 4 : 0;  // beta
+    for (int i = 0; i < 4; ++i) {
+        L->buf_off[i] = off;
+        off = align256(off + L->buf_bytes[i]);
+    }
+    L->book_off = off;
+    L->book_bytes = 2 * 3 * B * 4;
+    off = align256(off + L->book_bytes);
+    L->err_off = off;
+    off = align256(off + 4);
+    L->total_bytes = off;
+}
+
+template <class T>
+T* at(const replay_state* st, uint64_t off) { return reinterpret_cast<T*>(st->mem + off); }
+
+replay_status check_ptr(const void* p, const char* name)
+{
+    if (!p) return fail(REPLAY_ERR_ARG, "%s is NULL", name);
+    if (!aligned(p, 16)) return fail(REPLAY_ERR_ALIGN, "%s is not 16-byte aligned", name);
+    return REPLAY_OK;
+}
+
+replay_status check_inputs(const replay_config* c, const replay_inputs* in, bool need_tokens, bool need_D)
+{
+    if (!in) return fail(REPLAY_ERR_ARG, "inputs are NULL");
+    replay_status s;
+    if (c->kind == REPLAY_MAMBA2) {
+        if ((s = check_ptr(in->A, "A")) != REPLAY_OK) return s;
+        if (need_D && (s = check_ptr(in->D, "D")) != REPLAY_OK) return s;
+        if (need_tokens) {
+            if ((s = check_ptr(in->x, "x")) != REPLAY_OK) return s;
+            if ((s = check_ptr(in->B, "B")) != REPLAY_OK) return s;
+            if ((s = check_ptr(in->C, "C")) != REPLAY_OK) return s;
+            if ((s = check_ptr(in->dt, "dt")) != REPLAY_OK) return s;
+        }
+    } else if (need_tokens) {
+        if ((s = check_ptr(in->q, "q")) != REPLAY_OK) return s;
+        if ((s = check_ptr(in->k, "k")) != REPLAY_OK) return s;
+        if ((s = check_ptr(in->v, "v")) != REPLAY_OK) return s;
+        if ((s = check_ptr(in->alpha, "alpha")) != REPLAY_OK) return s;
+        if ((s = check_ptr(in->beta, "beta")) != REPLAY_OK) return s;
+    }
+    return REPLAY_OK;
+}
+
+rs::StepArgs step_args(const replay_state* st, const replay_inputs* in, void* y, int mode, int T)
+{
+    const replay_config* c = &st->cfg;
+    rs::StepArgs a;
+    memset(&a, 0, sizeof a);
+    a.B = c->batch;
+    a.H = c->nheads;
+    a.G = c->ngroups;
+    a.hpg = c->nheads / c->ngroups;
+    a.C = c->head_dim;
+    a.R = c->state_dim;
+    a.cap = c->buf_cap;
+    a.parity = st->parity;
+    a.mode = mode;
+    a.T = T;
+    a.vmax = mode == rs::MODE_DECODE ? c->buf_cap + 1 : (mode == rs::MODE_FLUSH ? c->buf_cap : c->buf_cap + T);
+    a.scale = c->scale;
+    const replay_layout& L = st->lay;
+    a.ckpt = at<float>(st, L.ckpt_off);
+    a.rcopy = L.rcopy_bytes ? at<uint8_t>(st, L.rcopy_off) : nullptr;
+    a.rscale = L.rscale_bytes ? at<uint8_t>(st, L.rscale_off) : nullptr;
+    a.bufc = at<void>(st, L.buf_off[0]);
+    a.bufr = at<void>(st, L.buf_off[1]);
+    a.bufs0 = at<float>(st, L.buf_off[2]);
+    a.bufs1 = L.buf_bytes[3] ? at<float>(st, L.buf_off[3]) : nullptr;
+    const uint64_t B = c->batch, H = c->nheads, G = c->ngroups, cap = c->buf_cap;
+    a.bank_c = B * H * cap * c->head_dim;
+    a.bank_r = B * G * cap * c->state_dim;
+    a.bank_s = B * H * cap;
+    a.book = at<int32_t>(st, L.book_off);
+    a.err = at<uint32_t>(st, L.err_off);
+    if (c->kind == REPLAY_MAMBA2) {
+        a.in_c = in->x;
+        a.in_r = in->B;
+        a.in_q = in->C;
+        a.in_s0 = in->dt;
+        a.A = in->A;
+        a.D = in->D;
+    } else {
+        a.in_c = in->v;
+        a.in_r = in->k;
+        a.in_q = in->q;
+        a.in_s0 = in->alpha;
+        a.in_s1 = in->beta;
+    }
+    a.y = y;
+    return a;
+}
+
+replay_status launch_step(replay_state* st, const replay_inputs* in, void* y, int mode, int T, void* stream)
+{
+    const replay_config* c = &st->cfg;
+    rs::StepArgs a = step_args(st, in, y, mode, T);
+    const int io = c->io_dtype == REPLAY_BF16 ? rs::IO_BF16 : rs::IO_F32;
+    const int rc = c->read_copy == REPLAY_FP8_E4M3 ? rs::RC_FP8 : (c->read_copy == REPLAY_MXFP4 ? rs::RC_MXFP4 : rs::RC_NONE);
+    hipError_t e;
+    if (c->kind == REPLAY_MAMBA2)
+        e = rs::launch_mamba2_step(a, io, rc, (c->flags & REPLAY_FLAG_VALU_FOLD) != 0, (hipStream_t)stream);
+    else
+        e = rs::launch_gdn_step(a, io, rc, (hipStream_t)stream);
+    replay_status s = hip_check(e, "replay step launch");
+    if (s == REPLAY_OK) st->parity ^= 1;
+    return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t replay_abi_version(void) { return REPLAY_ABI_VERSION; }
+
+const char* replay_status_str(int32_t s)
+{
+    switch (s) {
+        case REPLAY_OK: return "ok";
+        case REPLAY_ERR_ARG: return "invalid argument";
+        case REPLAY_ERR_SHAPE: return "unsupported or inconsistent shape";
+        case REPLAY_ERR_DTYPE: return "unsupported dtype";
+        case REPLAY_ERR_ALIGN: return "misaligned pointer or short region";
+        case REPLAY_ERR_STATE: return "operation not allowed in the current phase";
+        case REPLAY_ERR_CAPACITY: return "draft count outside [1, buf_cap]";
+        case REPLAY_ERR_UNSUPPORTED: return "not supported by this build";
+        case REPLAY_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* replay_last_error(void) { return g_err.c_str(); }
+
+replay_status replay_config_check(const replay_config* cfg) { return check_config(cfg); }
+
+size_t replay_state_bytes(const replay_config* cfg)
+{
+    if (check_config(cfg) != REPLAY_OK) return 0;
+    replay_layout L;
+    compute_layout(cfg, &L);
+    return (size_t)L.total_bytes;
+}
+
+replay_status replay_state_alloc(const replay_config* cfg, void* dev_mem, size_t bytes, void* stream,
+                                 replay_state** out)
+{
+    replay_status s = check_config(cfg);
+    if (s != REPLAY_OK) return s;
+    if (!out) return fail(REPLAY_ERR_ARG, "out is NULL");
+    if (!dev_mem) return fail(REPLAY_ERR_ARG, "dev_mem is NULL");
+    if (!aligned(dev_mem, 256)) return fail(REPLAY_ERR_ALIGN, "state region must be 256-byte aligned");
+    replay_layout L;
+    compute_layout(cfg, &L);
+    if (bytes < L.total_bytes)
+        return fail(REPLAY_ERR_ALIGN, "state region has %zu bytes, needs %llu", bytes, (unsigned long long)L.total_bytes);
+    replay_state* st = new replay_state;
+    st->cfg = *cfg;
+    st->mem = static_cast<uint8_t*>(dev_mem);
+    st->bytes = bytes;
+    st->lay = L;
+    st->parity = 0;
+    st->phase = 0;
+    s = hip_check(rs::launch_fill_zero(dev_mem, L.total_bytes, (hipStream_t)stream), "state initialisation");
+    if (s != REPLAY_OK) {
+        delete st;
+        return s;
+    }
+    *out = st;
+    return ok();
+}
+
+replay_status replay_state_free(replay_state* st)
+{
+    if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
+    delete st;
+    return ok();
+}
+
+replay_status replay_state_layout(const replay_state* st, replay_layout* out)
+{
+    if (!st || !out) return fail(REPLAY_ERR_ARG, "NULL argument");
+    *out = st->lay;
+    return ok();
+}
+
+int32_t replay_state_phase(const replay_state* st) { return st ? st->phase : -1; }
+
+replay_status replay_load_checkpoint(replay_state* st, const float* S, void* stream)
+{
+    if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
+    if (st->phase != 0) return fail(REPLAY_ERR_STATE, "load while drafts are pending");
+    replay_status s = check_ptr(S, "S_logical");
+    if (s != REPLAY_OK) return s;
+    const replay_config* c = &st->cfg;
+    const int tiles = c->batch * c->nheads;
+    hipStream_t hs = (hipStream_t)stream;
+    s = hip_check(rs::launch_logical_to_tiles(S, at<float>(st, st->lay.ckpt_off), tiles, c->head_dim, c->state_dim, hs),
+                  "checkpoint load");
+    if (s != REPLAY_OK) return s;
+    return hip_check(rs::launch_book_reset(at<int32_t>(st, st->lay.book_off), at<uint32_t>(st, st->lay.err_off),
+                                           c->batch, st->parity, hs),
+                     "bookkeeping reset");
+}
+
+replay_status replay_read_checkpoint(const replay_state* st, float* out, void* stream)
+{
+    if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
+    replay_status s = check_ptr(out, "S_out");
+    if (s != REPLAY_OK) return s;
+    const replay_config* c = &st->cfg;
+    return hip_check(rs::launch_tiles_to_logical(at<float>(st, st->lay.ckpt_off), out, c->batch * c->nheads,
+                                                 c->head_dim, c->state_dim, (hipStream_t)stream),
+                     "checkpoint read");
+}
+
+replay_status replay_read_copy(const replay_state* st, uint8_t* codes_out, uint8_t* scales_out, void* stream)
+{
+    if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
+    (void)codes_out;
+    (void)scales_out;
+    (void)stream;
+    return fail(REPLAY_ERR_STATE, "state has no read copy");
+}
+
+replay_status replay_read_book(const replay_state* st, int32_t* book_out, uint32_t* err_out, void* stream)
+{
+    if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
+    if (!book_out) return fail(REPLAY_ERR_ARG, "book_out is NULL");
+    const size_t n = (size_t)3 * st->cfg.batch * sizeof(int32_t);
+    hipStream_t hs = (hipStream_t)stream;
+    replay_status s = hip_check(hipMemcpyAsync(book_out, at<int32_t>(st, st->lay.book_off) + (size_t)st->parity * 3 * st->cfg.batch,
+                                               n, hipMemcpyDeviceToDevice, hs),
+                                "bookkeeping copy");
+    if (s != REPLAY_OK || !err_out) return s;
+    return hip_check(hipMemcpyAsync(err_out, at<uint32_t>(st, st->lay.err_off), 4, hipMemcpyDeviceToDevice, hs),
+                     "error word copy");
+}
+
+replay_status replay_decode_step(replay_state* st, const replay_inputs* in, void* y, void* stream)
+{
+    if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
+    if (st->phase != 0) return fail(REPLAY_ERR_STATE, "decode while drafts are pending");
+    replay_status s = check_inputs(&st->cfg, in, true, true);
+    if (s != REPLAY_OK) return s;
+    if ((s = check_ptr(y, "y")) != REPLAY_OK) return s;
+    return launch_step(st, in, y, rs::MODE_DECODE, 1, stream);
+}
+
+replay_status replay_flush(replay_state* st, const replay_inputs* in, void* stream)
+{
+    if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
+    if (st->phase != 0) return fail(REPLAY_ERR_STATE, "flush while drafts are pending");
+    replay_inputs none;
+    memset(&none, 0, sizeof none);
+    if (!in) in = &none;
+    if (st->cfg.kind == REPLAY_MAMBA2) {
+        replay_status s = check_ptr(in->A, "A");
+        if (s != REPLAY_OK) return s;
+    }
+    return launch_step(st, in, nullptr, rs::MODE_FLUSH, 0, stream);
+}
+
+replay_status replay_spec_append(replay_state* st, int32_t k, const replay_inputs* drafts, void* y, void* stream)
+{
+    if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
+    if (st->phase != 0) return fail(REPLAY_ERR_STATE, "spec_append while drafts are pending");
+    if (k < 1 || k > st->cfg.buf_cap) return fail(REPLAY_ERR_CAPACITY, "k = %d outside [1, %d]", k, st->cfg.buf_cap);
+    replay_status s = check_inputs(&st->cfg, drafts, true, true);
+    if (s != REPLAY_OK) return s;
+    if ((s = check_ptr(y, "y")) != REPLAY_OK) return s;
+    s = launch_step(st, drafts, y, rs::MODE_SPEC, k, stream);
+    if (s == REPLAY_OK) st->phase = 1;
+    return s;
+}
+
+static replay_status commit_impl(replay_state* st, const int32_t* accepted, void* stream)
+{
+    if (st->phase != 1) return fail(REPLAY_ERR_STATE, "no drafts pending");
+    replay_status s = hip_check(rs::launch_book_commit(at<int32_t>(st, st->lay.book_off), at<uint32_t>(st, st->lay.err_off),
+                                                       st->cfg.batch, st->parity, accepted, (hipStream_t)stream),
+                                "commit");
+    if (s == REPLAY_OK) {
+        st->parity ^= 1;
+        st->phase = 0;
+    }
+    return s;
+}
+
+replay_status replay_spec_commit(replay_state* st, const int32_t* accepted, void* stream)
+{
+    if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
+    if (!accepted) return fail(REPLAY_ERR_ARG, "accepted is NULL");
+    if (!aligned(accepted, 4)) return fail(REPLAY_ERR_ALIGN, "accepted is not 4-byte aligned");
+    return commit_impl(st, accepted, stream);
+}
+
+replay_status replay_spec_rollback(replay_state* st, void* stream)
+{
+    if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
+    return commit_impl(st, nullptr, stream);
+}
+
+static replay_status conv_common(const replay_config* cfg, rs::ConvArgs* a, const replay_inputs* in, void* y, int T)
+{
+    replay_config c = *cfg;
+    // the baselines have no checkpoint/buffer: read-copy and kind limits of
+    // the replay kernels do not apply
+    c.read_copy = REPLAY_NONE;
+    const int kind = c.kind;
+    c.kind = REPLAY_MAMBA2;
+    replay_status s = check_config(&c);
+    if (s != REPLAY_OK) return s;
+    c.kind = kind;
+    if ((s = check_inputs(&c, in, true, true)) != REPLAY_OK) return s;
+    if ((s = check_ptr(y, "y")) != REPLAY_OK) return s;
+    memset(a, 0, sizeof *a);
+    a->kind = kind == REPLAY_GDN ? 1 : 0;
+    a->B = c.batch;
+    a->H = c.nheads;
+    a->G = c.ngroups;
+    a->hpg = c.nheads / c.ngroups;
+    a->C = c.head_dim;
+    a->R = c.state_dim;
+    a->T = T;
+    a->scale = c.scale;
+    if (kind == REPLAY_MAMBA2) {
+        a->in_c = in->x;
+        a->in_r = in->B;
+        a->in_q = in->C;
+        a->in_s0 = in->dt;
+        a->A = in->A;
+        a->D = in->D;
+    } else {
+        a->in_c = in->v;
+        a->in_r = in->k;
+        a->in_q = in->q;
+        a->in_s0 = in->alpha;
+        a->in_s1 = in->beta;
+    }
+    a->y = y;
+    return REPLAY_OK;
+}
+
+replay_status replay_conv_decode_step(const replay_config* cfg, float* S, const replay_inputs* in, void* y,
+                                      void* stream)
+{
+    rs::ConvArgs a;
+    replay_status s = conv_common(cfg, &a, in, y, 1);
+    if (s != REPLAY_OK) return s;
+    if ((s = check_ptr(S, "S")) != REPLAY_OK) return s;
+    a.S = S;
+    return hip_check(rs::launch_conv_step(a, cfg->io_dtype == REPLAY_BF16 ? rs::IO_BF16 : rs::IO_F32, (hipStream_t)stream),
+                     "conventional decode");
+}
+
+replay_status replay_conv_spec_step(const replay_config* cfg, const float* S, float* snaps, int32_t k,
+                                    const replay_inputs* drafts, void* y, void* stream)
+{
+    rs::ConvArgs a;
+    replay_status s = conv_common(cfg, &a, drafts, y, k);
+    if (s != REPLAY_OK) return s;
+    if (k < 1 || k > REPLAY_MAX_BUF) return fail(REPLAY_ERR_CAPACITY, "k = %d outside [1, %d]", k, REPLAY_MAX_BUF);
+    if ((s = check_ptr(S, "S")) != REPLAY_OK) return s;
+    if ((s = check_ptr(snaps, "snaps")) != REPLAY_OK) return s;
+    a.S_in = S;
+    a.S = const_cast<float*>(S);
+    a.snaps = snaps;
+    return hip_check(rs::launch_conv_step(a, cfg->io_dtype == REPLAY_BF16 ? rs::IO_BF16 : rs::IO_F32, (hipStream_t)stream),
+                     "conventional spec step");
+}
+
+replay_status replay_conv_spec_restore(const replay_config* cfg, float* S, const float* snaps, int32_t k,
+                                       const int32_t* accepted, void* stream)
+{
+    if (!cfg) return fail(REPLAY_ERR_ARG, "config is NULL");
+    replay_status s;
+    if ((s = check_ptr(S, "S")) != REPLAY_OK) return s;
+    if ((s = check_ptr(snaps, "snaps")) != REPLAY_OK) return s;
+    if (!accepted) return fail(REPLAY_ERR_ARG, "accepted is NULL");
+    if (k < 1 || k > REPLAY_MAX_BUF) return fail(REPLAY_ERR_CAPACITY, "k = %d outside [1, %d]", k, REPLAY_MAX_BUF);
+    if (cfg->batch < 1 || cfg->nheads < 1 || cfg->head_dim < 16 || cfg->head_dim % 4 || cfg->state_dim < 4)
+        return fail(REPLAY_ERR_SHAPE, "bad shape");
+    return hip_check(rs::launch_conv_restore(S, snaps, accepted, cfg->batch, cfg->head_dim * cfg->state_dim,
+                                             cfg->nheads, k, (hipStream_t)stream),
+                     "conventional restore");
+}
+
+replay_status replay_stream_copy(void* dst, const void* src, size_t bytes, void* stream)
+{
+    replay_status s;
+    if ((s = check_ptr(dst, "dst")) != REPLAY_OK) return s;
+    if ((s = check_ptr(src, "src")) != REPLAY_OK) return s;
+    if (bytes % 16) return fail(REPLAY_ERR_ALIGN, "bytes must be a multiple of 16");
+    return hip_check(rs::launch_stream_copy(dst, src, bytes, (hipStream_t)stream), "stream copy");
+}
+
+}  // extern "C"

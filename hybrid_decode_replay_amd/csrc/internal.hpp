@@ -1,0 +1,87 @@
+// internal.hpp -- kernel argument blocks and launchers (library-private).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rs {
+
+enum : int { IO_F32 = 0, IO_BF16 = 1 };
+enum : int { RC_NONE = 0, RC_FP8 = 1, RC_MXFP4 = 2 };
+enum : int { MODE_DECODE = 0, MODE_FLUSH = 1, MODE_SPEC = 2 };
+
+// Device error word bits (mirror REPLAY_DEVERR_* of the public header).
+constexpr uint32_t REPLAY_COMMIT_CLAMPED_BIT = 0x1u;
+
+// Arguments of the replay step kernels (decode, explicit flush, spec append).
+// All buffer arrays hold two banks; the bank of a sequence is fc & 1 and a
+// flush moves the sequence to the other bank, so the entries a fold reads are
+// never overwritten by the same launch.
+struct StepArgs {
+    int B, H, G, hpg;        // batch, heads, groups, heads per group
+    int C, R;                // output axis (P or DV), reduction axis (N or DK)
+    int cap;                 // buffer capacity
+    int parity;              // which bookkeeping copy is current
+    int mode;                // MODE_DECODE / MODE_FLUSH / MODE_SPEC
+    int T;                   // new tokens: 1 (decode), k (spec), 0 (flush)
+    int vmax;                // LDS rows reserved for the virtual entry list
+    float scale;             // GDN output scale
+    float* ckpt;             // fragment-ordered fp32 tiles
+    uint8_t* rcopy;          // read-copy codes (or null)
+    uint8_t* rscale;         // MXFP4 scales (or null)
+    // buffer banks (element pointers; bank stride in elements)
+    void* bufc;              // per-head entry vectors: Mamba-2 x [2][B][H][cap][P]; GDN v [2][B][H][cap][DV]
+    void* bufr;              // per-group entry vectors: Mamba-2 B [2][B][G][cap][N]; GDN k [2][B][G][cap][DK]
+    float* bufs0;            // per-head scalar: Mamba-2 dt; GDN alpha   [2][B][H][cap]
+    float* bufs1;            // per-head scalar: GDN beta (null for Mamba-2)
+    size_t bank_c, bank_r, bank_s;
+    int32_t* book;           // [2][3][B]
+    uint32_t* err;
+    // token inputs [T][B][...]
+    const void* in_c;        // Mamba-2 x ; GDN v
+    const void* in_r;        // Mamba-2 B ; GDN k
+    const void* in_q;        // Mamba-2 C ; GDN q
+    const void* in_s0;       // Mamba-2 dt (io dtype) ; GDN alpha (fp32)
+    const float* in_s1;      // GDN beta (fp32)
+    const float* A;          // Mamba-2 A [H]
+    const float* D;          // Mamba-2 D [H]
+    void* y;                 // outputs [T][B][H][C]
+};
+
+hipError_t launch_mamba2_step(const StepArgs& a, int io, int rc, bool valu_fold, hipStream_t s);
+hipError_t launch_gdn_step(const StepArgs& a, int io, int rc, hipStream_t s);
+
+// Bookkeeping, layout conversion and helpers (aux.hip).
+hipError_t launch_book_commit(int32_t* book, uint32_t* err, int B, int parity,
+                              const int32_t* accepted, hipStream_t s);
+hipError_t launch_book_reset(int32_t* book, uint32_t* err, int B, int parity, hipStream_t s);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_tiles_to_logical(const float* ckpt, float* out, int tiles, int C, int R, hipStream_t s);
+hipError_t launch_logical_to_tiles(const float* in, float* ckpt, int tiles, int C, int R, hipStream_t s);
+hipError_t launch_quantize_read_copy(const float* ckpt, uint8_t* codes, uint8_t* scales, int tiles,
+                                     int C, int R, int rc, hipStream_t s);
+hipError_t launch_read_copy_to_logical(const uint8_t* codes, const uint8_t* scales, uint8_t* codes_out,
+                                       uint8_t* scales_out, int tiles, int C, int R, int rc, hipStream_t s);
+hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+
+// Conventional baselines (conv.hip).
+struct ConvArgs {
+    int kind, B, H, G, hpg, C, R, T;
+    float scale;
+    float* S;                // logical [B][H][C][R]
+    const float* S_in;       // spec: read-only source
+    float* snaps;            // spec: [T][B][H][C][R]
+    const void* in_c;
+    const void* in_r;
+    const void* in_q;
+    const void* in_s0;
+    const float* in_s1;
+    const float* A;
+    const float* D;
+    void* y;
+};
+hipError_t launch_conv_step(const ConvArgs& a, int io, hipStream_t s);
+hipError_t launch_conv_restore(float* S, const float* snaps, const int32_t* accepted, int B, int tile_elems,
+                               int H, int k, hipStream_t s);
+
+}  // namespace rs

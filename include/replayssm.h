@@ -1,0 +1,226 @@
+/*
+ * replayssm.h -- C ABI of the MI355X (gfx950) replayed SSM decode library.
+ *
+ * The library keeps each sequence's SSM state as a checkpoint plus a buffer of
+ * the most recent per-token inputs (capacity 1..16; 16 on the pages).  A
+ * decode step that does not fill the buffer appends the token's inputs and
+ * computes the output from the read-only checkpoint plus the buffered inputs,
+ * writing no state; the step whose append fills the buffer folds the buffer
+ * into the checkpoint and writes the checkpoint once.  Speculative drafts are
+ * appended to the buffer, the accepted prefix advances the buffer pointer and
+ * a rollback resets it.  Layers: Mamba-2 and Gated DeltaNet.
+ *
+ * Pages the operations follow:
+ *   [DE] "ReplaySSM beschleunigt das Decoding von Hybridmodellen durch Caching
+ *        der Eingaben statt des Zustands" -- sections "Was passiert ist" and
+ *        "Wie es funktioniert" (checkpoint + input buffer, flush when full,
+ *        pointer reset on rejected drafts).
+ *   [TR] "NVIDIA ve Dao AI Lab, hibrit model cozumlemesini hizlandirmak icin
+ *        ReplaySSM'i sundu" -- sections "ReplaySSM nasil calisir?" (16-entry
+ *        buffer, non-flush and flush steps, outputs equal ordinary decoding up
+ *        to rounding), "Durum trafigini azaltma ve rollback'in
+ *        basitlestirilmesi" (one checkpoint write per window, drafts appended
+ *        unverified, accepted prefix advances the pointer, output-only draft
+ *        evaluation) and "Kuantizasyon hatasinin sinirlandirilmasi"
+ *        (high-precision checkpoint for the recurrence, low-precision copy for
+ *        reads).
+ *
+ * Conventions for every entry point:
+ *   - All data pointers are DEVICE pointers unless stated otherwise.  The
+ *     caller owns all device memory (the state region, inputs, outputs,
+ *     baseline states and snapshots) and all streams; the library owns only
+ *     the host-side handle.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work on `stream`; nothing synchronizes.
+ *   - Host-side validation happens before anything is enqueued.  On a non-OK
+ *     return nothing was enqueued and the state is unchanged; replay_last_error()
+ *     then holds a message (thread-local).
+ *   - REPLAY_ERR_HIP reports a launch error from the HIP runtime.
+ *   - Device-side anomalies never trap: they set sticky bits in the state's
+ *     device error word (replay_read_book).
+ *   - Pointers to inputs, outputs and states must be 16-byte aligned; the
+ *     state region must be 256-byte aligned.  Outputs must not alias inputs.
+ *   - A handle must not be used from two streams without caller ordering.
+ *
+ * Tensor layouts (row-major, logical):
+ *   Mamba-2  x [T][B][H][P], Bm and Cm [T][B][G][N], dt [T][B][H]
+ *            (all in `io_dtype`), A and D [H] fp32, y [T][B][H][P] io_dtype,
+ *            checkpoint (logical) [B][H][P][N] fp32.
+ *   GDN      q and k [T][B][G][DK], v [T][B][H][DV] (io_dtype), alpha and
+ *            beta [T][B][H] fp32, o [T][B][H][DV] io_dtype, checkpoint
+ *            (logical) [B][H][DV][DK] fp32.
+ *   T = 1 for a decode step, T = k for k speculative drafts.
+ *   Head h reads B/C (Mamba-2) or q/k (GDN) of group h / (H / G).
+ */
+#ifndef REPLAYSSM_H
+#define REPLAYSSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define REPLAY_ABI_VERSION 1
+#define REPLAY_MAX_BUF 16
+
+typedef enum {
+    REPLAY_OK = 0,
+    REPLAY_ERR_ARG = 1,         /* NULL pointer or bad scalar argument          */
+    REPLAY_ERR_SHAPE = 2,       /* unsupported or inconsistent dimensions       */
+    REPLAY_ERR_DTYPE = 3,       /* unsupported dtype combination                */
+    REPLAY_ERR_ALIGN = 4,       /* pointer alignment or region size             */
+    REPLAY_ERR_STATE = 5,       /* operation not allowed in the current phase   */
+    REPLAY_ERR_CAPACITY = 6,    /* draft count outside [1, buf_cap]             */
+    REPLAY_ERR_UNSUPPORTED = 7, /* valid request this build does not implement  */
+    REPLAY_ERR_HIP = 8          /* HIP runtime error                            */
+} replay_status;
+
+typedef enum { REPLAY_MAMBA2 = 0, REPLAY_GDN = 1 } replay_kind;
+
+typedef enum {
+    REPLAY_NONE = 0,
+    REPLAY_F32 = 1,
+    REPLAY_F16 = 2,
+    REPLAY_BF16 = 3,
+    REPLAY_FP8_E4M3 = 4,    /* OCP FP8 E4M3 ("fn"), unscaled, RNE, saturating at +-448 */
+    REPLAY_MXFP4 = 5        /* OCP MX FP4 E2M1, one E8M0 scale per 32 elements          */
+} replay_dtype;
+
+/* Device error word bits (sticky; cleared by replay_load_checkpoint). */
+#define REPLAY_DEVERR_COMMIT_CLAMPED 0x1u  /* an accepted count was outside [0, pend] */
+
+/* Configuration flags. */
+#define REPLAY_FLAG_VALU_FOLD 0x1   /* fold with vector FMAs instead of MFMA (cross-check) */
+
+typedef struct {
+    int32_t abi_version;  /* REPLAY_ABI_VERSION                                  */
+    int32_t kind;         /* replay_kind                                         */
+    int32_t batch;        /* B >= 1                                              */
+    int32_t nheads;       /* H >= 1                                              */
+    int32_t ngroups;      /* G >= 1, divides H (Mamba-2 B/C groups; GDN q/k heads)*/
+    int32_t head_dim;     /* Mamba-2 P; GDN DV.  Multiple of 16, <= 256          */
+    int32_t state_dim;    /* Mamba-2 N; GDN DK.  16, 32, 64, 128 or 256          */
+    int32_t buf_cap;      /* buffer capacity, 1..16                              */
+    int32_t ckpt_dtype;   /* REPLAY_F32 (recurrence checkpoint)                  */
+    int32_t read_copy;    /* REPLAY_NONE | REPLAY_FP8_E4M3 | REPLAY_MXFP4        */
+    int32_t io_dtype;     /* REPLAY_F32 | REPLAY_BF16 (token inputs and outputs) */
+    int32_t flags;        /* REPLAY_FLAG_*                                       */
+    float scale;          /* GDN output scale (o = scale * S q); ignored for Mamba-2 */
+} replay_config;
+
+/* Per-call inputs.  Unused fields must be NULL.  A and D (Mamba-2 layer
+ * parameters, fp32 [H]) are needed by every call that computes values;
+ * replay_flush needs only A. */
+typedef struct {
+    const void *x, *B, *C, *dt;     /* Mamba-2 token inputs (io_dtype)  */
+    const float *A, *D;             /* Mamba-2 parameters               */
+    const void *q, *k, *v;          /* GDN token inputs (io_dtype)      */
+    const float *alpha, *beta;      /* GDN gates (fp32)                 */
+} replay_inputs;
+
+/* Byte offsets inside the caller's state region (for inspection/tests). */
+typedef struct {
+    uint64_t total_bytes;
+    uint64_t ckpt_off, ckpt_bytes;     /* checkpoint, fragment-ordered tiles   */
+    uint64_t rcopy_off, rcopy_bytes;   /* read copy element codes              */
+    uint64_t rscale_off, rscale_bytes; /* MXFP4 E8M0 scales                    */
+    uint64_t buf_off[4], buf_bytes[4]; /* buffer arrays, 2 banks each          */
+    uint64_t book_off, book_bytes;     /* int32 [2][3][B]: len, pend, fc       */
+    uint64_t err_off;                  /* uint32 device error word             */
+} replay_layout;
+
+typedef struct replay_state replay_state; /* opaque host handle */
+
+/* ---- library info ------------------------------------------------------ */
+int32_t replay_abi_version(void);
+const char *replay_status_str(int32_t status);
+/* Message for the last non-OK return on this thread ("" if none). */
+const char *replay_last_error(void);
+
+/* ---- state lifetime ----------------------------------------------------- */
+/* Validates a configuration without touching the GPU. */
+replay_status replay_config_check(const replay_config *cfg);
+/* Bytes of device memory a state needs (0 if the configuration is invalid). */
+size_t replay_state_bytes(const replay_config *cfg);
+/* Binds caller-owned device memory (>= replay_state_bytes, 256-byte aligned)
+ * to a new handle and enqueues its initialisation: zero checkpoint, empty
+ * buffer, len = pend = fc = 0, error word 0.  The memory stays owned by the
+ * caller and must outlive the handle. */
+replay_status replay_state_alloc(const replay_config *cfg, void *dev_mem, size_t bytes,
+                                 void *stream, replay_state **out);
+/* Frees the host handle only. */
+replay_status replay_state_free(replay_state *st);
+replay_status replay_state_layout(const replay_state *st, replay_layout *out);
+/* Host-side phase: 0 = idle, 1 = drafts pending. */
+int32_t replay_state_phase(const replay_state *st);
+
+/* ---- checkpoint I/O ----------------------------------------------------- */
+/* Loads an fp32 logical checkpoint (device), refreshes the read copy, empties
+ * the buffer and resets len = pend = fc = 0 and the error word.  Not allowed
+ * while drafts are pending. */
+replay_status replay_load_checkpoint(replay_state *st, const float *S_logical, void *stream);
+/* Writes the current checkpoint (not including buffered tokens) as fp32
+ * logical layout to S_out (device). */
+replay_status replay_read_checkpoint(const replay_state *st, float *S_out, void *stream);
+/* Writes the read copy in logical element order: one byte per element
+ * (FP8 code, or FP4 code in the low nibble) to codes_out [B][H][rows][cols],
+ * and for MXFP4 the E8M0 scales to scales_out [B][H][rows][cols/32]
+ * (may be NULL otherwise).  REPLAY_ERR_STATE if the state has no read copy. */
+replay_status replay_read_copy(const replay_state *st, uint8_t *codes_out, uint8_t *scales_out,
+                               void *stream);
+/* Copies the bookkeeping to book_out (device int32 [3][B]: len, pend, fc) and,
+ * if err_out is not NULL, the device error word to err_out (device uint32). */
+replay_status replay_read_book(const replay_state *st, int32_t *book_out, uint32_t *err_out,
+                               void *stream);
+
+/* ---- the decode path ---------------------------------------------------- */
+/* One decode token for every sequence.  Per sequence: if the buffer is
+ * already full (possible after a commit), the buffer is folded first; the
+ * token's inputs are appended; if that fills the buffer, the buffer is folded
+ * into the checkpoint, which is written once, and the buffer is emptied.
+ * Outputs y [1][B][H][P] (Mamba-2) or [1][B][H][DV] (GDN) in io_dtype.
+ * Not allowed while drafts are pending. */
+replay_status replay_decode_step(replay_state *st, const replay_inputs *in, void *y, void *stream);
+/* Folds every non-empty buffer into its checkpoint (one write per sequence
+ * that had entries); len = 0.  Uses only in->A (Mamba-2).  Not allowed while
+ * drafts are pending. */
+replay_status replay_flush(replay_state *st, const replay_inputs *in, void *stream);
+/* Appends k draft tokens (inputs [k][B][...]) to every sequence's buffer
+ * without verification and writes their outputs y [k][B][H][P or DV]; no
+ * state is written unless a sequence's committed entries plus k exceed the
+ * capacity, in which case its committed prefix is folded first.  Requires
+ * 1 <= k <= buf_cap (else REPLAY_ERR_CAPACITY) and no pending drafts. */
+replay_status replay_spec_append(replay_state *st, int32_t k, const replay_inputs *drafts,
+                                 void *y, void *stream);
+/* accepted: device int32 [B].  len += clamp(accepted[b], 0, pend); pend = 0.
+ * A clamped value sets REPLAY_DEVERR_COMMIT_CLAMPED.  Moves no state bytes.
+ * Requires pending drafts. */
+replay_status replay_spec_commit(replay_state *st, const int32_t *accepted, void *stream);
+/* Drops every pending draft (pointer reset; commit of 0). */
+replay_status replay_spec_rollback(replay_state *st, void *stream);
+
+/* ---- in-run conventional baselines --------------------------------------
+ * Ordinary decoding on a plain fp32 logical state (load, decay and update,
+ * output, store per token), tuned like the replay kernels. */
+replay_status replay_conv_decode_step(const replay_config *cfg, float *S, const replay_inputs *in,
+                                      void *y, void *stream);
+/* k draft steps from S (read once, not written); snapshot j (the state after
+ * draft j) goes to snaps + j * B*H*rows*cols; outputs y [k][B][...]. */
+replay_status replay_conv_spec_step(const replay_config *cfg, const float *S, float *snaps,
+                                    int32_t k, const replay_inputs *drafts, void *y, void *stream);
+/* S[b] = snaps[accepted[b] - 1][b] where 1 <= accepted[b] <= k; unchanged
+ * otherwise.  accepted: device int32 [B]. */
+replay_status replay_conv_spec_restore(const replay_config *cfg, float *S, const float *snaps,
+                                       int32_t k, const int32_t *accepted, void *stream);
+
+/* ---- measurement helpers ------------------------------------------------ */
+/* Streaming copy of `bytes` (multiple of 16) from src to dst: the in-run
+ * bandwidth ceiling and the reference for hardware byte counters. */
+replay_status replay_stream_copy(void *dst, const void *src, size_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* REPLAYSSM_H */

@@ -1,0 +1,121 @@
+"""Drive the HIP library and the fp64 oracle side by side on identical seeded inputs.
+
+Test-side helper.  Inputs come from the seeded generators (synth); the oracle
+never sees a value produced by the HIP path.  Each operation is applied to both
+sides and the outputs, the checkpoint (read back in logical layout) and the
+bookkeeping are compared:
+  outputs      normwise relative error per output vector <= tol
+  checkpoint   normwise relative error per (b, h) matrix <= tol
+  bookkeeping  len, pend, fc and the error word bit-exact
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import replay_oracle as ro
+from hybrid_decode_replay_amd import binding as rb
+
+TOL = {rb.F32: 1e-4, rb.BF16: 2e-2}
+
+
+def dev(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device="cuda", dtype=dtype)
+
+
+class Pair:
+    """A GPU ReplayState and an oracle session fed the same operations."""
+
+    def __init__(self, kind, B, H, G, C, R, cap=16, io=rb.F32, seed=0, S0=None, flags=0, scale=1.0,
+                 read_copy=rb.NONE):
+        self.kind = kind
+        self.cfg = rb.make_config(kind, B, H, G, C, R, cap, io, read_copy=read_copy, flags=flags, scale=scale)
+        self.io = io
+        self.iot = torch.bfloat16 if io == rb.BF16 else torch.float32
+        self.tol = TOL[io]
+        self.B, self.H, self.G, self.C, self.R = B, H, G, C, R
+        if S0 is None:
+            S0 = np.zeros((B, H, C, R), np.float32)
+        self.st = rb.ReplayState(self.cfg)
+        self.st.load_checkpoint(torch.from_numpy(S0).cuda())
+        rc = {rb.NONE: None, rb.FP8_E4M3: "fp8", rb.MXFP4: "mxfp4"}[read_copy]
+        if kind == rb.MAMBA2:
+            from hybrid_decode_replay_amd import synth
+            A, D = synth.mamba2_params(seed, H)
+            self.params = {"A": dev(A, torch.float32), "D": dev(D, torch.float32)}
+            self.orc = ro.Mamba2Session(A, D, S0, cap=cap, read_copy=rc)
+        else:
+            self.params = {}
+            self.orc = ro.GDNSession(S0, cap=cap, scale=scale, read_copy=rc)
+        self.max_err = {"y": 0.0, "ckpt": 0.0}
+
+    # -- conversions
+    def to_dev(self, tok):
+        """np token dict (one token [B,...] or k tokens [k,B,...]) -> device tensors in io dtype."""
+        out = {}
+        for k, v in tok.items():
+            dt = torch.float32 if k in ("alpha", "beta") else self.iot
+            out[k] = dev(v, dt)
+        return out
+
+    # -- comparisons
+    def check_outputs(self, y_gpu, y_orc, what):
+        got = y_gpu.float().cpu().numpy().reshape(np.shape(y_orc))
+        err = ro.normwise_error(got, y_orc)
+        self.max_err["y"] = max(self.max_err["y"], err)
+        assert np.all(np.isfinite(got)), f"{what}: non-finite GPU outputs"
+        assert err <= self.tol, f"{what}: output error {err:.3e} > {self.tol:.1e}"
+
+    def check_state(self, what):
+        torch.cuda.synchronize()
+        ck = self.st.read_checkpoint().cpu().numpy().astype(np.float64)
+        ref = self.orc.ckpt
+        num = np.max(np.abs(ck - ref), axis=(2, 3))
+        den = np.maximum(np.max(np.abs(ref), axis=(2, 3)), 1e-30)
+        err = float(np.max(num / den))
+        # an all-zero reference (e.g. a zero checkpoint never folded) must match exactly
+        zero = np.max(np.abs(ref), axis=(2, 3)) == 0
+        assert np.all(np.max(np.abs(ck), axis=(2, 3))[zero] == 0), f"{what}: nonzero checkpoint where oracle is 0"
+        err = float(np.max(np.where(zero, 0.0, num / den)))
+        self.max_err["ckpt"] = max(self.max_err["ckpt"], err)
+        assert err <= self.tol, f"{what}: checkpoint error {err:.3e} > {self.tol:.1e}"
+        L, P, F, E = self.st.read_book()
+        got = (L.cpu().numpy(), P.cpu().numpy(), F.cpu().numpy(), int(E.cpu().numpy()[0]))
+        oL, oP, oF = self.orc.trace()
+        assert np.array_equal(got[0], oL), f"{what}: len {got[0]} != {oL}"
+        assert np.array_equal(got[1], oP), f"{what}: pend {got[1]} != {oP}"
+        assert np.array_equal(got[2], oF), f"{what}: fc {got[2]} != {oF}"
+        assert got[3] == self.orc.err, f"{what}: error word {got[3]} != {self.orc.err}"
+
+    # -- operations
+    def decode(self, tok, what="decode", check_state=True):
+        y = self.st.decode(self.to_dev(tok), self.params)
+        yo = self.orc.decode(tok)
+        self.check_outputs(y[0], yo, what)
+        if check_state:
+            self.check_state(what)
+        return y
+
+    def flush(self, what="flush"):
+        self.st.flush(self.params)
+        self.orc.flush()
+        self.check_state(what)
+
+    def spec(self, drafts, what="spec"):
+        """drafts: dict of [k, B, ...] arrays."""
+        k = next(iter(drafts.values())).shape[0]
+        y = self.st.spec_append(k, self.to_dev(drafts), self.params)
+        yo = self.orc.spec_append([{n: v[j] for n, v in drafts.items()} for j in range(k)])
+        self.check_outputs(y, np.stack(yo), what)
+        self.check_state(what)
+        return y
+
+    def commit(self, accepted, what="commit"):
+        self.st.commit(torch.tensor(np.asarray(accepted, np.int32), device="cuda"))
+        self.orc.commit(accepted)
+        self.check_state(what)
+
+    def rollback(self, what="rollback"):
+        self.st.rollback()
+        self.orc.rollback()
+        self.check_state(what)
