@@ -73,6 +73,7 @@ _SIGS = {
     "replay_conv_spec_step": ([_CP, _vp, _vp, _i32, _IP, _vp, _vp], _i32),
     "replay_conv_spec_restore": ([_CP, _vp, _vp, _i32, _vp, _vp], _i32),
     "replay_stream_copy": ([_vp, _vp, _sz, _vp], _i32),
+    "replay_stream_read": ([_vp, _sz, _vp, _vp], _i32),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -307,3 +308,7 @@ def conv_spec_restore(cfg: ReplayConfig, S, snaps, k: int, accepted):
 
 def stream_copy(dst, src, nbytes: int):
     _check(_lib.replay_stream_copy(_ptr(dst), _ptr(src), int(nbytes), _stream()), "replay_stream_copy")
+
+
+def stream_read(src, nbytes: int, sum_out):
+    _check(_lib.replay_stream_read(_ptr(src), int(nbytes), _ptr(sum_out), _stream()), "replay_stream_read")

@@ -129,4 +129,33 @@ hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStrea
     return hipGetLastError();
 }
 
+// Read-only stream: the ceiling for checkpoint reads that write nothing back.
+// A fixed grid (8 workgroups per CU) strides over the data with four
+// independent 128-bit loads per thread in flight; one atomic per workgroup.
+__global__ __launch_bounds__(256) void stream_read_kernel(const f32x4* src, size_t n4, float* sum_out)
+{
+    __shared__ float part[4];
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n4; i += 4 * stride) {
+        const f32x4 a0 = __builtin_nontemporal_load(src + i);
+        const f32x4 a1 = __builtin_nontemporal_load(src + i + stride);
+        const f32x4 a2 = __builtin_nontemporal_load(src + i + 2 * stride);
+        const f32x4 a3 = __builtin_nontemporal_load(src + i + 3 * stride);
+        acc += (a0 + a1) + (a2 + a3);
+    }
+    for (; i < n4; i += stride) acc += __builtin_nontemporal_load(src + i);
+    const float v = wave_sum64(acc.x + acc.y + acc.z + acc.w);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) atomicAdd(sum_out, part[0] + part[1] + part[2] + part[3]);
+}
+
+hipError_t launch_stream_read(const void* src, size_t bytes, float* sum_out, hipStream_t s)
+{
+    hipLaunchKernelGGL(stream_read_kernel, dim3(2048), dim3(256), 0, s, (const f32x4*)src, bytes / 16, sum_out);
+    return hipGetLastError();
+}
+
 }  // namespace rs

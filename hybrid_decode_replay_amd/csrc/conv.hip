@@ -26,8 +26,6 @@ __device__ __forceinline__ float row_sum(float v) {
     return v;
 }
 
-__device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
-
 template <int IO>
 __device__ __forceinline__ f32x4 ld4_io(const void* p, size_t i) {
     if constexpr (IO == IO_F32) return ld4(static_cast<const float*>(p) + i);

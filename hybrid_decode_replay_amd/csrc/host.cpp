@@ -506,4 +506,13 @@ replay_status replay_stream_copy(void* dst, const void* src, size_t bytes, void*
     return hip_check(rs::launch_stream_copy(dst, src, bytes, (hipStream_t)stream), "stream copy");
 }
 
+replay_status replay_stream_read(const void* src, size_t bytes, float* sum_out, void* stream)
+{
+    replay_status s;
+    if ((s = check_ptr(src, "src")) != REPLAY_OK) return s;
+    if (!sum_out) return fail(REPLAY_ERR_ARG, "sum_out is NULL");
+    if (bytes % 16) return fail(REPLAY_ERR_ALIGN, "bytes must be a multiple of 16");
+    return hip_check(rs::launch_stream_read(src, bytes, sum_out, (hipStream_t)stream), "stream read");
+}
+
 }  // extern "C"

@@ -63,6 +63,7 @@ hipError_t launch_quantize_read_copy(const float* ckpt, uint8_t* codes, uint8_t*
 hipError_t launch_read_copy_to_logical(const uint8_t* codes, const uint8_t* scales, uint8_t* codes_out,
                                        uint8_t* scales_out, int tiles, int C, int R, int rc, hipStream_t s);
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+hipError_t launch_stream_read(const void* src, size_t bytes, float* sum_out, hipStream_t s);
 
 // Conventional baselines (conv.hip).
 struct ConvArgs {

@@ -219,6 +219,10 @@ replay_status replay_conv_spec_restore(const replay_config *cfg, float *S, const
 /* Streaming copy of `bytes` (multiple of 16) from src to dst: the in-run
  * bandwidth ceiling and the reference for hardware byte counters. */
 replay_status replay_stream_copy(void *dst, const void *src, size_t bytes, void *stream);
+/* Streaming read of `bytes` (multiple of 16) fp32 values from src, adding
+ * their sum to *sum_out (device float, caller-initialised): the read-only
+ * bandwidth ceiling that non-flush steps are measured against. */
+replay_status replay_stream_read(const void *src, size_t bytes, float *sum_out, void *stream);
 
 #ifdef __cplusplus
 }

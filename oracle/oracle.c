@@ -254,3 +254,11 @@ void oracle_mxfp4_dequantize_array(const unsigned char *codes, const unsigned ch
         for (int i = 0; i < 32; ++i) out[b * 32 + i] = oracle_e2m1_decode(codes[b * 32 + i]) * s;
     }
 }
+
+/* Threads the OpenMP loops above use (for reporting the CPU baseline). */
+#ifdef _OPENMP
+#include <omp.h>
+int oracle_threads(void) { return omp_get_max_threads(); }
+#else
+int oracle_threads(void) { return 1; }
+#endif

@@ -93,6 +93,8 @@ def configure(L):
     L.oracle_mxfp4_quantize_array.restype = None
     L.oracle_mxfp4_dequantize_array.argtypes = [_ubp, _ubp, ctypes.c_long, _dp]
     L.oracle_mxfp4_dequantize_array.restype = None
+    L.oracle_threads.argtypes = []
+    L.oracle_threads.restype = ctypes.c_int
     return L
 
 
@@ -115,6 +117,11 @@ def use_library(handle):
     prev = _lib
     _lib = handle
     return prev
+
+
+def threads():
+    """OpenMP threads the oracle's per-token loops run on."""
+    return int(lib().oracle_threads())
 
 
 def _f64(a):
