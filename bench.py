@@ -27,7 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_mamba2_step_b256.txt")
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "mamba2_step_b256_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "hybrid_decode_replay_amd", "csrc", f) for f in ("mamba2.hip", "common.hpp")]
 
 
