@@ -60,6 +60,13 @@ __device__ __forceinline__ float sum_over_row_groups(float v) {
     return v;
 }
 
+// Order LDS accesses made by different lanes of the same wave (no workgroup barrier).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Workgroup -> tile mapping.  Consecutive workgroups are dispatched round-robin
 // over the 8 XCDs; remapping gives each XCD a contiguous range of tiles so that
 // heads sharing group inputs (B/C, q/k) and neighbouring sequences share an L2.

@@ -82,7 +82,6 @@ replay_status check_config(const replay_config* c)
     if (c->read_copy == REPLAY_MXFP4 && R % 32 != 0)
         return fail(REPLAY_ERR_SHAPE, "MXFP4 read copy needs state_dim divisible by 32");
     if (c->read_copy != REPLAY_NONE) return fail(REPLAY_ERR_UNSUPPORTED, "read copies not built yet");
-    if (c->kind == REPLAY_GDN) return fail(REPLAY_ERR_UNSUPPORTED, "Gated DeltaNet replay kernel not built yet");
     if (c->flags & ~REPLAY_FLAG_VALU_FOLD) return fail(REPLAY_ERR_ARG, "unknown flags 0x%x", c->flags);
     return ok();
 }

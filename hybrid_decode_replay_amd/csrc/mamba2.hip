@@ -29,47 +29,18 @@
 // so a non-flush step has no second barrier.
 #include "common.hpp"
 #include "internal.hpp"
+#include "stage.hpp"
 
 namespace rs {
-
-template <int IO>
-__device__ __forceinline__ void chunk_to_lds(float* dst, uint4 v)
-{
-    if constexpr (IO == IO_F32) {
-        st4(dst, __builtin_bit_cast(f32x4, v));
-    } else {
-        st4(dst, f32x4{bf16_bits_to_f32((uint16_t)(v.x & 0xffff)), bf16_bits_to_f32((uint16_t)(v.x >> 16)),
-                       bf16_bits_to_f32((uint16_t)(v.y & 0xffff)), bf16_bits_to_f32((uint16_t)(v.y >> 16))});
-        st4(dst + 4, f32x4{bf16_bits_to_f32((uint16_t)(v.z & 0xffff)), bf16_bits_to_f32((uint16_t)(v.z >> 16)),
-                           bf16_bits_to_f32((uint16_t)(v.w & 0xffff)), bf16_bits_to_f32((uint16_t)(v.w >> 16))});
-    }
-}
-
-template <int IO>
-__device__ __forceinline__ uint4 lds_to_chunk(const float* src)
-{
-    if constexpr (IO == IO_F32) {
-        return __builtin_bit_cast(uint4, ld4(src));
-    } else {
-        const f32x4 a = ld4(src), b = ld4(src + 4);
-        auto pk = [](float lo, float hi) {
-            return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
-        };
-        return uint4{pk(a.x, a.y), pk(a.z, a.w), pk(b.x, b.y), pk(b.z, b.w)};
-    }
-}
 
 template <int NB, int IO, int TMAX, bool MFMA_FOLD>
 __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
 {
     extern __shared__ float lds[];
     constexpr int R = NB * 16;
-    constexpr int ES = IO == IO_BF16 ? 2 : 4;   // bytes per io element
-    constexpr int EPC = 16 / ES;                // elements per 16-byte chunk
-    constexpr int RX = R / EPC;                 // chunks per B or C row
     constexpr int RS = R + 4;                   // padded LDS stride of B rows
     constexpr int PRE = 4;                      // chunks per thread fetched ahead of the checkpoint
-    const int C = a.C, CX = C / EPC;
+    const int C = a.C;
     const int tile = xcd_tile_index();
     const int b = tile / a.H, h = tile - b * a.H;
     const int g = h / a.hpg;
@@ -80,25 +51,9 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
     const size_t sB = (size_t)a.B;
 
     // ---- bookkeeping: identical decision in every workgroup of sequence b
-    const int32_t* bk = a.book + (size_t)a.parity * 3 * sB;
-    const int len = min(max(bk[b], 0), a.cap);   // invariant 0 <= len <= cap; clamped so a
-    const int fc = bk[2 * sB + b];                // corrupted word cannot index out of bounds
-    const int T = a.T;
-    int f;
-    if (a.mode == MODE_DECODE) f = (len + 1 >= a.cap) ? min(len + 1, a.cap) : 0;
-    else if (a.mode == MODE_FLUSH) f = len;
-    else f = (len + T > a.cap) ? len : 0;
-    const int V = len + T;
-    const int bank = fc & 1;
-    const int bank_new = (fc + (f > 0 ? 1 : 0)) & 1;
-
-    if (h == 0 && tid == 0) {
-        int32_t* nbk = a.book + (size_t)(a.parity ^ 1) * 3 * sB;
-        nbk[b] = (a.mode == MODE_DECODE) ? len + 1 - f : (a.mode == MODE_FLUSH ? 0 : len - f);
-        nbk[sB + b] = (a.mode == MODE_SPEC) ? T : 0;
-        nbk[2 * sB + b] = fc + (f > 0 ? 1 : 0);
-    }
-    if (a.mode == MODE_FLUSH && f == 0) return;
+    const StepPlan p = plan_step(a, b, h == 0 && tid == 0);
+    if (a.mode == MODE_FLUSH && p.f == 0) return;
+    const int f = p.f, len = p.len, T = a.T;
 
     // ---- LDS partition (floats)
     const int Tr = T > 0 ? T : 1;
@@ -107,57 +62,20 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
     float* cs = bs + (size_t)a.vmax * RS;         // [Tr][R]    read-out rows C_t
     float* ds = cs + (size_t)Tr * R;              // [vmax]     entry dt
 
+    StageGeom G;
+    G.bufc = a.bufc; G.bufr = a.bufr; G.bufs0 = a.bufs0; G.bufs1 = nullptr;
+    G.in_c = a.in_c; G.in_r = a.in_r; G.in_q = a.in_q; G.in_s0 = a.in_s0; G.in_s1 = nullptr;
+    G.bank_c = a.bank_c; G.bank_r = a.bank_r; G.bank_s = a.bank_s;
+    G.hc = (size_t)b * a.H + h; G.gr = (size_t)b * a.G + g;
+    G.b = b; G.h = h; G.g = g; G.B = a.B; G.H = a.H; G.G = a.G; G.cap = a.cap; G.C = C;
+    G.len = len; G.bank = p.bank; G.V = p.V; G.T = T;
+    G.xc = xs; G.xr = bs; G.xq = cs; G.s0 = ds; G.s1 = nullptr;
+
     // ---- 1. entry and read-out chunks, issued ahead of the checkpoint stream
-    const size_t hc = (size_t)b * a.H + h, gr = (size_t)b * a.G + g;
-    const int nx = V * CX, nbr = V * RX, nch = nx + nbr + T * RX;
-    auto chunk_src = [&](int ch) -> const uint4* {
-        size_t e;
-        const void* base;
-        if (ch < nx) {
-            const int j = ch / CX, o = ch - j * CX;
-            if (j < len) { base = a.bufc; e = (size_t)bank * a.bank_c + (hc * a.cap + j) * C; }
-            else { base = a.in_c; e = (((size_t)(j - len) * sB + b) * a.H + h) * C; }
-            return reinterpret_cast<const uint4*>(static_cast<const char*>(base) + e * ES) + o;
-        }
-        ch -= nx;
-        if (ch < nbr) {
-            const int j = ch / RX, o = ch - j * RX;
-            if (j < len) { base = a.bufr; e = (size_t)bank * a.bank_r + (gr * a.cap + j) * R; }
-            else { base = a.in_r; e = (((size_t)(j - len) * sB + b) * a.G + g) * R; }
-            return reinterpret_cast<const uint4*>(static_cast<const char*>(base) + e * ES) + o;
-        }
-        ch -= nbr;
-        const int t = ch / RX, o = ch - t * RX;
-        e = (((size_t)t * sB + b) * a.G + g) * R;
-        return reinterpret_cast<const uint4*>(static_cast<const char*>(a.in_q) + e * ES) + o;
-    };
-    auto chunk_dst = [&](int ch) -> float* {
-        if (ch < nx) { const int j = ch / CX; return xs + j * C + (ch - j * CX) * EPC; }
-        ch -= nx;
-        if (ch < nbr) { const int j = ch / RX; return bs + j * RS + (ch - j * RX) * EPC; }
-        ch -= nbr;
-        const int t = ch / RX;
-        return cs + t * R + (ch - t * RX) * EPC;
-    };
+    const Stager<IO, R> stg(G);
     uint4 pre[PRE];
-#pragma unroll
-    for (int u = 0; u < PRE; ++u) {
-        const int ch = tid + u * nthr;
-        if (ch < nch) pre[u] = *chunk_src(ch);
-    }
-    // dt stays as raw bits until it is published, so its conversion does not make the
-    // wave wait for the chunk loads before the checkpoint loads are issued
-    uint32_t dtraw = 0, dtshift = 0;
-    if (tid < V) {
-        if (tid < len) {
-            dtraw = reinterpret_cast<const uint32_t*>(a.bufs0)[(size_t)bank * a.bank_s + hc * a.cap + tid];
-        } else if constexpr (IO == IO_F32) {
-            dtraw = static_cast<const uint32_t*>(a.in_s0)[((size_t)(tid - len) * sB + b) * a.H + h];
-        } else {
-            dtraw = static_cast<const uint16_t*>(a.in_s0)[((size_t)(tid - len) * sB + b) * a.H + h];
-            dtshift = 16;
-        }
-    }
+    ScalarRaw sr;
+    stage_issue<IO, R, PRE, true>(stg, tid, nthr, pre, sr);
 
     // ---- 2. checkpoint tile -> registers (one 128-bit load per 16x16 block)
     float* ckw = a.ckpt + (((size_t)tile * (C >> 4) + w) * NB * 64 + lane) * 4;
@@ -166,13 +84,7 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
     for (int nb = 0; nb < NB; ++nb) s[nb] = ld4_stream(ckw + (size_t)nb * 256);
 
     // ---- 3. publish the staged rows
-#pragma unroll
-    for (int u = 0; u < PRE; ++u) {
-        const int ch = tid + u * nthr;
-        if (ch < nch) chunk_to_lds<IO>(chunk_dst(ch), pre[u]);
-    }
-    for (int ch = tid + PRE * nthr; ch < nch; ch += nthr) chunk_to_lds<IO>(chunk_dst(ch), *chunk_src(ch));
-    if (tid < V) ds[tid] = __builtin_bit_cast(float, dtraw << dtshift);
+    stage_publish<IO, R, PRE>(stg, tid, nthr, pre, sr);
     __syncthreads();
 
     const float Ah = a.A[h];
@@ -292,23 +204,7 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
     }
 
     // ---- 7. append the unfolded new tokens to the buffer (slot = position - f)
-    const int j0 = max(f, len);
-    const int nnew = V - j0;
-    if (nnew > 0) {
-        char* bx = static_cast<char*>(a.bufc) + ((size_t)bank_new * a.bank_c + hc * a.cap * C) * ES;
-        for (int i = tid; i < nnew * CX; i += nthr) {
-            const int jj = i / CX, o = i - jj * CX, j = j0 + jj;
-            reinterpret_cast<uint4*>(bx + (size_t)(j - f) * C * ES)[o] = lds_to_chunk<IO>(xs + j * C + o * EPC);
-        }
-        if (tid < nnew) a.bufs0[(size_t)bank_new * a.bank_s + hc * a.cap + (j0 + tid - f)] = ds[j0 + tid];
-        if (h % a.hpg == 0) {
-            char* bb = static_cast<char*>(a.bufr) + ((size_t)bank_new * a.bank_r + gr * a.cap * R) * ES;
-            for (int i = tid; i < nnew * RX; i += nthr) {
-                const int jj = i / RX, o = i - jj * RX, j = j0 + jj;
-                reinterpret_cast<uint4*>(bb + (size_t)(j - f) * R * ES)[o] = lds_to_chunk<IO>(bs + j * RS + o * EPC);
-            }
-        }
-    }
+    stage_append<IO, R>(G, a.bufc, a.bufr, a.bufs0, nullptr, p.bank_new, f, tid, nthr, h % a.hpg == 0);
 }
 
 template <int NB, int IO, int TMAX, bool MF>

@@ -1,0 +1,223 @@
+// stage.hpp -- entry staging shared by the replay step kernels.
+//
+// A launch works on a virtual entry list per sequence: the committed buffer
+// entries 0..len-1 followed by the T new tokens.  Each entry has a per-head
+// vector (Mamba-2 x, GDN v; C wide), a per-group vector (Mamba-2 B, GDN k;
+// R wide) and one or two per-head scalars (Mamba-2 dt; GDN alpha, beta); each
+// new token also has a per-group read-out vector (Mamba-2 C, GDN q).  The rows
+// are fetched as 16-byte chunks.  stage_issue() puts the first PRE chunks of
+// every thread in flight (call it before the checkpoint loads, so that
+// consuming the chunks later waits only for them); stage_publish() converts
+// them to fp32 in LDS.  The caller then needs one workgroup barrier.
+#pragma once
+#include "common.hpp"
+
+namespace rs {
+
+struct StageGeom {
+    const void* bufc;    // per-head vectors, bank-strided
+    const void* bufr;    // per-group vectors
+    const float* bufs0;  // per-head scalar 0 (fp32)
+    const float* bufs1;  // per-head scalar 1 (fp32) or null
+    const void* in_c;
+    const void* in_r;
+    const void* in_q;
+    const void* in_s0;   // io dtype (Mamba-2 dt) or fp32 (GDN alpha)
+    const float* in_s1;
+    size_t bank_c, bank_r, bank_s;
+    size_t hc, gr;       // b*H + h, b*G + g
+    int b, h, g, B, H, G, cap, C, len, bank, V, T;
+    float* xc;           // LDS [vmax][C]
+    float* xr;           // LDS [vmax][R + 4]
+    float* xq;           // LDS [T][R]
+    float* s0;           // LDS [vmax]
+    float* s1;           // LDS [vmax] or null
+};
+
+template <int IO>
+__device__ __forceinline__ void chunk_to_lds(float* dst, uint4 v)
+{
+    if constexpr (IO == IO_F32) {
+        st4(dst, __builtin_bit_cast(f32x4, v));
+    } else {
+        st4(dst, f32x4{bf16_bits_to_f32((uint16_t)(v.x & 0xffff)), bf16_bits_to_f32((uint16_t)(v.x >> 16)),
+                       bf16_bits_to_f32((uint16_t)(v.y & 0xffff)), bf16_bits_to_f32((uint16_t)(v.y >> 16))});
+        st4(dst + 4, f32x4{bf16_bits_to_f32((uint16_t)(v.z & 0xffff)), bf16_bits_to_f32((uint16_t)(v.z >> 16)),
+                           bf16_bits_to_f32((uint16_t)(v.w & 0xffff)), bf16_bits_to_f32((uint16_t)(v.w >> 16))});
+    }
+}
+
+template <int IO>
+__device__ __forceinline__ uint4 lds_to_chunk(const float* src)
+{
+    if constexpr (IO == IO_F32) {
+        return __builtin_bit_cast(uint4, ld4(src));
+    } else {
+        const f32x4 a = ld4(src), b = ld4(src + 4);
+        auto pk = [](float lo, float hi) {
+            return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+        };
+        return uint4{pk(a.x, a.y), pk(a.z, a.w), pk(b.x, b.y), pk(b.z, b.w)};
+    }
+}
+
+template <int IO, int R>
+struct Stager {
+    static constexpr int ES = IO == IO_BF16 ? 2 : 4;
+    static constexpr int EPC = 16 / ES;
+    static constexpr int RX = R / EPC;
+    static constexpr int RS = R + 4;
+
+    const StageGeom& G;
+    int CX, nx, nr, nch;
+
+    __device__ explicit Stager(const StageGeom& g) : G(g) {
+        CX = G.C / EPC;
+        nx = G.V * CX;
+        nr = G.V * RX;
+        nch = nx + nr + G.T * RX;
+    }
+
+    __device__ const uint4* src(int ch) const {
+        size_t e;
+        const void* base;
+        if (ch < nx) {
+            const int j = ch / CX, o = ch - j * CX;
+            if (j < G.len) { base = G.bufc; e = (size_t)G.bank * G.bank_c + (G.hc * G.cap + j) * G.C; }
+            else { base = G.in_c; e = (((size_t)(j - G.len) * G.B + G.b) * G.H + G.h) * G.C; }
+            return reinterpret_cast<const uint4*>(static_cast<const char*>(base) + e * ES) + o;
+        }
+        ch -= nx;
+        if (ch < nr) {
+            const int j = ch / RX, o = ch - j * RX;
+            if (j < G.len) { base = G.bufr; e = (size_t)G.bank * G.bank_r + (G.gr * G.cap + j) * R; }
+            else { base = G.in_r; e = (((size_t)(j - G.len) * G.B + G.b) * G.G + G.g) * R; }
+            return reinterpret_cast<const uint4*>(static_cast<const char*>(base) + e * ES) + o;
+        }
+        ch -= nr;
+        const int t = ch / RX, o = ch - t * RX;
+        e = (((size_t)t * G.B + G.b) * G.G + G.g) * R;
+        return reinterpret_cast<const uint4*>(static_cast<const char*>(G.in_q) + e * ES) + o;
+    }
+
+    __device__ float* dst(int ch) const {
+        if (ch < nx) { const int j = ch / CX; return G.xc + j * G.C + (ch - j * CX) * EPC; }
+        ch -= nx;
+        if (ch < nr) { const int j = ch / RX; return G.xr + j * RS + (ch - j * RX) * EPC; }
+        ch -= nr;
+        const int t = ch / RX;
+        return G.xq + t * R + (ch - t * RX) * EPC;
+    }
+};
+
+// Raw bits of the per-entry scalars of one thread (entry index = tid < V).
+// They stay unconverted until published, so no conversion makes the wave
+// wait for the chunk loads before the checkpoint loads are issued.
+struct ScalarRaw {
+    uint32_t s0 = 0, s0shift = 0, s1 = 0;
+};
+
+template <int IO, int R, int PRE, bool S0_IS_IO>
+__device__ __forceinline__ void stage_issue(const Stager<IO, R>& st, int tid, int nthr, uint4 (&pre)[PRE], ScalarRaw& sr)
+{
+    const StageGeom& G = st.G;
+#pragma unroll
+    for (int u = 0; u < PRE; ++u) {
+        const int ch = tid + u * nthr;
+        if (ch < st.nch) pre[u] = *st.src(ch);
+    }
+    if (tid < G.V) {
+        if (tid < G.len) {
+            sr.s0 = reinterpret_cast<const uint32_t*>(G.bufs0)[(size_t)G.bank * G.bank_s + G.hc * G.cap + tid];
+            if (G.bufs1)
+                sr.s1 = reinterpret_cast<const uint32_t*>(G.bufs1)[(size_t)G.bank * G.bank_s + G.hc * G.cap + tid];
+        } else {
+            const size_t e = ((size_t)(tid - G.len) * G.B + G.b) * G.H + G.h;
+            if constexpr (S0_IS_IO && IO == IO_BF16) {
+                sr.s0 = static_cast<const uint16_t*>(G.in_s0)[e];
+                sr.s0shift = 16;
+            } else {
+                sr.s0 = static_cast<const uint32_t*>(G.in_s0)[e];
+            }
+            if (G.in_s1) sr.s1 = reinterpret_cast<const uint32_t*>(G.in_s1)[e];
+        }
+    }
+}
+
+template <int IO, int R, int PRE>
+__device__ __forceinline__ void stage_publish(const Stager<IO, R>& st, int tid, int nthr, const uint4 (&pre)[PRE],
+                                              const ScalarRaw& sr)
+{
+    const StageGeom& G = st.G;
+#pragma unroll
+    for (int u = 0; u < PRE; ++u) {
+        const int ch = tid + u * nthr;
+        if (ch < st.nch) chunk_to_lds<IO>(st.dst(ch), pre[u]);
+    }
+    for (int ch = tid + PRE * nthr; ch < st.nch; ch += nthr) chunk_to_lds<IO>(st.dst(ch), *st.src(ch));
+    if (tid < G.V) {
+        G.s0[tid] = __builtin_bit_cast(float, sr.s0 << sr.s0shift);
+        if (G.s1) G.s1[tid] = __builtin_bit_cast(float, sr.s1);
+    }
+}
+
+// Append the unfolded new entries [j0, V) to the buffer bank `bank_new` at
+// slot (position - f): per-head vectors and scalars always, per-group vectors
+// only from the first head of the group.
+template <int IO, int R>
+__device__ __forceinline__ void stage_append(const StageGeom& G, void* bufc, void* bufr, float* bufs0, float* bufs1,
+                                             int bank_new, int f, int tid, int nthr, bool group_writer)
+{
+    using S = Stager<IO, R>;
+    const int j0 = max(f, G.len);
+    const int nnew = G.V - j0;
+    if (nnew <= 0) return;
+    const int CX = G.C / S::EPC;
+    char* bx = static_cast<char*>(bufc) + ((size_t)bank_new * G.bank_c + G.hc * G.cap * G.C) * S::ES;
+    for (int i = tid; i < nnew * CX; i += nthr) {
+        const int jj = i / CX, o = i - jj * CX, j = j0 + jj;
+        reinterpret_cast<uint4*>(bx + (size_t)(j - f) * G.C * S::ES)[o] = lds_to_chunk<IO>(G.xc + j * G.C + o * S::EPC);
+    }
+    if (tid < nnew) {
+        bufs0[(size_t)bank_new * G.bank_s + G.hc * G.cap + (j0 + tid - f)] = G.s0[j0 + tid];
+        if (bufs1) bufs1[(size_t)bank_new * G.bank_s + G.hc * G.cap + (j0 + tid - f)] = G.s1[j0 + tid];
+    }
+    if (group_writer) {
+        char* bb = static_cast<char*>(bufr) + ((size_t)bank_new * G.bank_r + G.gr * G.cap * R) * S::ES;
+        for (int i = tid; i < nnew * S::RX; i += nthr) {
+            const int jj = i / S::RX, o = i - jj * S::RX, j = j0 + jj;
+            reinterpret_cast<uint4*>(bb + (size_t)(j - f) * R * S::ES)[o] = lds_to_chunk<IO>(G.xr + j * S::RS + o * S::EPC);
+        }
+    }
+}
+
+// Per-sequence decision shared by every workgroup of sequence b: how many
+// leading entries of the virtual list are folded, and the bookkeeping update
+// (written by one workgroup into the other copy).
+struct StepPlan {
+    int len, fc, f, V, bank, bank_new;
+};
+
+__device__ __forceinline__ StepPlan plan_step(const StepArgs& a, int b, bool writer)
+{
+    const size_t sB = (size_t)a.B;
+    const int32_t* bk = a.book + (size_t)a.parity * 3 * sB;
+    StepPlan p;
+    p.len = min(max(bk[b], 0), a.cap);   // invariant 0 <= len <= cap; clamped so that a
+    p.fc = bk[2 * sB + b];               // corrupted word cannot index out of bounds
+    if (a.mode == MODE_DECODE) p.f = (p.len + 1 >= a.cap) ? min(p.len + 1, a.cap) : 0;
+    else if (a.mode == MODE_FLUSH) p.f = p.len;
+    else p.f = (p.len + a.T > a.cap) ? p.len : 0;
+    p.V = p.len + a.T;
+    p.bank = p.fc & 1;
+    p.bank_new = (p.fc + (p.f > 0 ? 1 : 0)) & 1;
+    if (writer) {
+        int32_t* nbk = a.book + (size_t)(a.parity ^ 1) * 3 * sB;
+        nbk[b] = (a.mode == MODE_DECODE) ? p.len + 1 - p.f : (a.mode == MODE_FLUSH ? 0 : p.len - p.f);
+        nbk[sB + b] = (a.mode == MODE_SPEC) ? a.T : 0;
+        nbk[2 * sB + b] = p.fc + (p.f > 0 ? 1 : 0);
+    }
+    return p;
+}
+
+}  // namespace rs
