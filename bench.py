@@ -1,6 +1,6 @@
 """Benchmark: replayed SSM-layer decode on one MI355X.
 
-Workload (default): the batch-256 hybrid-serving Mamba-2 layer -- B=256
+Headline workload: the batch-256 hybrid-serving Mamba-2 layer -- B=256
 sequences, H=128 heads, P=64, N=128, G=8 groups, fp32 checkpoint (4 MiB per
 sequence), bf16 x/B/C/dt inputs and bf16 outputs, 16-entry buffer, decoding
 from a random N(0, 0.1) checkpoint.  One step = one decode token for every
@@ -8,11 +8,17 @@ sequence of the layer (append, buffer scalars, checkpoint read-out, and on
 every 16th step the fold with its single checkpoint write).  Inputs for every
 timed step are drawn on the device before the timed region.
 
-Printed: one JSON line with tokens/s (sequence-tokens per second for the
-layer), the roofline of the replay kernel (algorithmic bytes / measured
-per-launch time vs the 8 TB/s HBM peak), the in-run conventional fused decode
-kernel on the same workload, a streaming-copy ceiling, and the fp64 CPU
-oracle timed on the host's cores over a bounded sample.
+The JSON line also carries:
+  roofline      the replay kernel: algorithmic bytes per launch / measured
+                per-launch time (HIP events on the launch stream) vs 8 TB/s
+  mamba2        the headline layer in detail, with the in-run conventional
+                fused load-decay-update-store kernel on the same layer
+  gdn           the batch-256 Gated DeltaNet layer (32 heads, d_k = d_v = 128,
+                bf16 q/k/v, fp32 gates), replay and conventional
+  spec          speculative rounds at batch 512 (4 drafts per round, accepted
+                prefix ~ min(Geometric(0.35) - 1, 4), seeded): replay append +
+                commit vs the snapshot-per-draft + restore baseline, both layers
+  cpu_baseline  the fp64 oracle on the host cores over a bounded sample
 """
 from __future__ import annotations
 
@@ -30,23 +36,29 @@ HBM_PEAK_GBS = 8000.0
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "mamba2_step_b256_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "hybrid_decode_replay_amd", "csrc", f) for f in ("mamba2.hip", "common.hpp")]
 
-
-def mamba2_algorithmic_bytes(B, H, G, P, N, cap=16, io_bytes=2):
-    """Bytes the method must move per sequence-token, averaged over a full window of `cap`
-    steps with lockstep flushes: checkpoint read every step, written once per window;
-    current inputs x, B, C, dt; the new entry x, B, dt written; on average (cap-1)/2 prior
-    entries read; output y."""
-    S = H * P * N * 4
-    entry = (H * P + G * N + H) * io_bytes
-    inp = (H * P + 2 * G * N + H) * io_bytes
-    out = H * P * io_bytes
-    return S + S / cap + inp + entry + (cap - 1) / 2 * entry + out
+MAMBA2 = dict(H=128, G=8, C=64, R=128)     # heads, groups, head dim P, state dim N
+GDN = dict(H=32, G=32, C=128, R=128)       # heads, q/k heads, d_v, d_k
 
 
-def conv_algorithmic_bytes(B, H, G, P, N, io_bytes=2):
-    S = H * P * N * 4
-    inp = (H * P + 2 * G * N + H) * io_bytes
-    return 2 * S + inp + H * P * io_bytes
+def algorithmic_bytes(kind, H, G, C, R, cap=16, io_bytes=2):
+    """(replay, conventional) bytes per sequence-token.
+
+    Replay, averaged over a full window of `cap` steps with lockstep flushes: the
+    checkpoint is read every step and written once per window; the current inputs are
+    read; the new entry is written; on average (cap-1)/2 prior entries are read; the
+    output is written.  Conventional: state read and written every token, inputs,
+    output.  Entries: Mamba-2 x, B, dt; GDN k, v and the fp32 gates."""
+    S = H * C * R * 4
+    if kind == "mamba2":
+        entry = (H * C + G * R + H) * io_bytes
+        inp = (H * C + 2 * G * R + H) * io_bytes
+    else:
+        entry = (H * C + G * R) * io_bytes + 2 * H * 4
+        inp = (H * C + 2 * G * R) * io_bytes + 2 * H * 4
+    out = H * C * io_bytes
+    replay = S + S / cap + inp + entry + (cap - 1) / 2 * entry + out
+    conv = 2 * S + inp + out
+    return replay, conv
 
 
 def kernel_source_sha():
@@ -57,7 +69,7 @@ def kernel_source_sha():
     return h.hexdigest()[:16]
 
 
-def read_traffic(units_per_launch):
+def read_traffic():
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
     the current kernel source (else None)."""
     if not os.path.exists(PROFILE_TRAFFIC):
@@ -76,10 +88,10 @@ def read_traffic(units_per_launch):
         return None
 
 
-def cpu_baseline(B, H, G, P, N, budget_s=10.0, max_s=30.0):
+def cpu_baseline(H, G, P, N, budget_s=10.0, max_s=30.0):
     """The fp64 oracle (ordinary decoding, OpenMP over (sequence, head)) on a bounded sample of
-    the same layer shape: 64 sequences (512 MiB of fp64 state, beyond any host cache), steps in
-    chunks of 4 until >= budget_s of CPU time."""
+    the headline layer shape: 64 sequences (512 MiB of fp64 state, beyond any host cache),
+    steps in chunks of 4 until >= budget_s of CPU time."""
     import numpy as np
     from hybrid_decode_replay_amd import synth
     from oracle import replay_oracle as ro
@@ -97,9 +109,176 @@ def cpu_baseline(B, H, G, P, N, budget_s=10.0, max_s=30.0):
         tokens += nseq * chunk
         steps += chunk
         c += 1
-    return {"value": tokens / elapsed, "unit": "tokens/s", "cores": ro.threads(), "kind": "oracle",
-            "sample": f"{nseq} sequences x {steps} decode steps of the same layer shape (fp64 ordinary decoding, "
-                      f"bf16-rounded inputs), {elapsed:.1f} s"}
+    return {"value": round(tokens / elapsed, 1), "unit": "tokens/s", "cores": ro.threads(), "kind": "oracle",
+            "sample": f"{nseq} sequences x {steps} decode steps of the headline layer shape (fp64 ordinary "
+                      f"decoding, bf16-rounded inputs), {elapsed:.1f} s"}
+
+
+class Layer:
+    """Device-side state, parameters and pre-drawn inputs of one synthetic layer."""
+
+    def __init__(self, rb, synth, torch, dev, kind, B, steps, seed, cap=16):
+        self.rb, self.torch, self.dev, self.kind, self.B = rb, torch, dev, kind, B
+        shp = MAMBA2 if kind == "mamba2" else GDN
+        self.H, self.G, self.C, self.R = shp["H"], shp["G"], shp["C"], shp["R"]
+        self.cap = cap
+        self.cfg = rb.make_config(rb.MAMBA2 if kind == "mamba2" else rb.GDN, B, self.H, self.G, self.C, self.R,
+                                  cap, rb.BF16)
+        self.S0 = synth.checkpoint_device(seed, (B, self.H, self.C, self.R), dev)
+        if kind == "mamba2":
+            A, D = synth.mamba2_params(seed, self.H)
+            self.params = {"A": torch.from_numpy(A).to(dev), "D": torch.from_numpy(D).to(dev)}
+            self.toks = synth.mamba2_tokens_device(seed, steps, B, self.H, self.G, self.C, self.R, dev)
+        else:
+            self.params = {}
+            self.toks = synth.gdn_tokens_device(seed, steps, B, self.H, self.G, self.R, self.C, dev)
+
+    def inputs(self, t0, n=1):
+        return self.rb.make_inputs(self.cfg, {k: v[t0:t0 + n] for k, v in self.toks.items()}, self.params)
+
+
+def time_replay_decode(L, K, W, stream):
+    """K timed decode steps after W warm-up steps; per-launch HIP events on the launch stream."""
+    rb, torch = L.rb, L.torch
+    st = rb.ReplayState(L.cfg, device=L.dev)
+    st.load_checkpoint(L.S0)
+    ys = torch.empty((2, 1, L.B, L.H, L.C), dtype=torch.bfloat16, device=L.dev)
+    ins = [L.inputs(t) for t in range(K + W)]
+    lib, sp = rb.lib(), rb.ctypes.c_void_p(stream.cuda_stream)
+    yp = [rb.ctypes.c_void_p(ys[i].data_ptr()) for i in range(2)]
+
+    def step(t):
+        s = lib.replay_decode_step(st.h, rb.ctypes.byref(ins[t]), yp[t & 1], sp)
+        if s != rb.OK:
+            raise rb.ReplayError(s, "replay_decode_step")
+
+    for t in range(W):
+        step(t)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record(stream)
+        step(W + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per = [s.elapsed_time(e) for s, e in ev]
+    total = ev[0][0].elapsed_time(ev[-1][1])
+    flush = [p for i, p in enumerate(per) if (W + i) % L.cap == L.cap - 1]
+    nonflush = [p for i, p in enumerate(per) if (W + i) % L.cap != L.cap - 1]
+    return {"steps": K, "total_ms": total, "avg_launch_ms": sum(per) / K,
+            "flush_ms": sum(flush) / max(1, len(flush)), "nonflush_ms": sum(nonflush) / max(1, len(nonflush))}
+
+
+def time_conv_decode(L, K, stream, t0=0):
+    rb, torch = L.rb, L.torch
+    S = L.S0.clone()
+    y = torch.empty((1, L.B, L.H, L.C), dtype=torch.bfloat16, device=L.dev)
+    ins = [L.inputs(t0 + t) for t in range(K + 4)]
+    lib, sp = rb.lib(), rb.ctypes.c_void_p(stream.cuda_stream)
+    cp, Sp, yp = rb.ctypes.byref(L.cfg), rb.ctypes.c_void_p(S.data_ptr()), rb.ctypes.c_void_p(y.data_ptr())
+    for t in range(4):
+        lib.replay_conv_decode_step(cp, Sp, rb.ctypes.byref(ins[t]), yp, sp)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for t in range(K):
+        s = lib.replay_conv_decode_step(cp, Sp, rb.ctypes.byref(ins[4 + t]), yp, sp)
+        if s != rb.OK:
+            raise rb.ReplayError(s, "replay_conv_decode_step")
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / K
+
+
+def decode_report(L, r, conv_ms):
+    replay_b, conv_b = algorithmic_bytes(L.kind, L.H, L.G, L.C, L.R, L.cap)
+    ms = r["total_ms"] / r["steps"]
+    ach = replay_b * L.B / (r["avg_launch_ms"] / 1e3) / 1e9
+    out = {"batch": L.B, "tokens_per_s": round(L.B / (ms / 1e3), 1), "ms_per_step": round(ms, 5),
+           "avg_launch_ms": round(r["avg_launch_ms"], 5),
+           "flush_step_ms": round(r["flush_ms"], 5), "nonflush_step_ms": round(r["nonflush_ms"], 5),
+           "achieved_gbs": round(ach, 1), "frac_of_peak": round(ach / HBM_PEAK_GBS, 4),
+           "bytes_per_token_algorithmic": int(replay_b)}
+    if conv_ms is not None:
+        out["conventional"] = {"tokens_per_s": round(L.B / (conv_ms / 1e3), 1), "ms_per_step": round(conv_ms, 5),
+                               "achieved_gbs": round(conv_b * L.B / (conv_ms / 1e3) / 1e9, 1),
+                               "bytes_per_token_algorithmic": int(conv_b)}
+        out["speedup_vs_conventional"] = round(conv_ms / ms, 3)
+        out["state_traffic_reduction_algorithmic"] = round(1 - replay_b / conv_b, 4)
+    return out
+
+
+def time_spec(L, rounds, k, stream, seed=3):
+    """Speculative rounds: replay (append k drafts + commit the accepted prefix) and the
+    conventional baseline (k draft steps writing a snapshot each + restore of snapshot a-1)."""
+    import numpy as np
+    rb, torch = L.rb, L.torch
+    rng = np.random.default_rng(seed)
+    acc_np = np.minimum(rng.geometric(0.35, size=(rounds, L.B)) - 1, k).astype(np.int32)
+    acc = torch.from_numpy(acc_np).to(L.dev)
+    lib, sp = rb.lib(), rb.ctypes.c_void_p(stream.cuda_stream)
+    ins = [L.inputs(r * k, k) for r in range(rounds)]
+    y = torch.empty((k, L.B, L.H, L.C), dtype=torch.bfloat16, device=L.dev)
+    yp = rb.ctypes.c_void_p(y.data_ptr())
+    st = rb.ReplayState(L.cfg, device=L.dev)
+    st.load_checkpoint(L.S0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for r in range(rounds):
+        s = lib.replay_spec_append(st.h, k, rb.ctypes.byref(ins[r]), yp, sp)
+        s |= lib.replay_spec_commit(st.h, rb.ctypes.c_void_p(acc[r].data_ptr()), sp)
+        if s != rb.OK:
+            raise rb.ReplayError(s, "replay spec round")
+    e1.record(stream)
+    torch.cuda.synchronize()
+    replay_ms = e0.elapsed_time(e1) / rounds
+    del st
+    S = L.S0.clone()
+    snaps = torch.empty((k,) + tuple(S.shape), dtype=torch.float32, device=L.dev)
+    cp, Sp, npp = rb.ctypes.byref(L.cfg), rb.ctypes.c_void_p(S.data_ptr()), rb.ctypes.c_void_p(snaps.data_ptr())
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for r in range(rounds):
+        s = lib.replay_conv_spec_step(cp, Sp, npp, k, rb.ctypes.byref(ins[r]), yp, sp)
+        s |= lib.replay_conv_spec_restore(cp, Sp, npp, k, rb.ctypes.c_void_p(acc[r].data_ptr()), sp)
+        if s != rb.OK:
+            raise rb.ReplayError(s, "conventional spec round")
+    e1.record(stream)
+    torch.cuda.synchronize()
+    conv_ms = e0.elapsed_time(e1) / rounds
+    del snaps, S
+    accepted = float(acc_np.sum()) / rounds
+    return {"batch": L.B, "drafts": k, "rounds": rounds, "mean_accepted": round(accepted / L.B, 4),
+            "replay_ms_per_round": round(replay_ms, 5), "conventional_ms_per_round": round(conv_ms, 5),
+            "replay_accepted_tokens_per_s": round(accepted / (replay_ms / 1e3), 1),
+            "conventional_accepted_tokens_per_s": round(accepted / (conv_ms / 1e3), 1),
+            "speedup": round(conv_ms / replay_ms, 3)}
+
+
+def ceilings(rb, torch, dev, stream):
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    nb = src.numel() * 4
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        rb.stream_copy(dst, src, nb)
+    e0.record(stream)
+    for _ in range(10):
+        rb.stream_copy(dst, src, nb)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy = 10 * 2 * nb / (e0.elapsed_time(e1) / 1e3) / 1e9
+    acc = torch.zeros(1, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        rb.stream_read(src, nb, acc)
+    e0.record(stream)
+    for _ in range(10):
+        rb.stream_read(src, nb, acc)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    read = 10 * nb / (e0.elapsed_time(e1) / 1e3) / 1e9
+    return round(copy, 1), round(read, 1)
 
 
 def main():
@@ -108,9 +287,10 @@ def main():
     ap.add_argument("--steps", type=int, default=1024)
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--batch", type=int, default=256)
-    ap.add_argument("--conv-steps", type=int, default=256, help="steps of the in-run conventional baseline")
+    ap.add_argument("--conv-steps", type=int, default=256, help="steps of the in-run conventional baselines")
+    ap.add_argument("--spec-rounds", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-conv", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="headline layer only (no GDN, spec, conventional)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the decode path shards by "
@@ -122,129 +302,56 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    B, H, G, P, N, cap = args.batch, 128, 8, 64, 128, 16
-    K, W = args.steps, args.warmup
-    cfg = rb.make_config(rb.MAMBA2, B, H, G, P, N, cap, rb.BF16)
-    st = rb.ReplayState(cfg, device=dev)
-    S0 = synth.checkpoint_device(1, (B, H, P, N), dev)
-    st.load_checkpoint(S0)
-    A, D = synth.mamba2_params(1, H)
-    params = {"A": torch.from_numpy(A).to(dev), "D": torch.from_numpy(D).to(dev)}
-    toks = synth.mamba2_tokens_device(1, K + W, B, H, G, P, N, dev)
-    ys = torch.empty((2, 1, B, H, P), dtype=torch.bfloat16, device=dev)
-    inputs = [rb.make_inputs(cfg, {k: v[t:t + 1] for k, v in toks.items()}, params) for t in range(K + W)]
-    L = rb.lib()
     stream = torch.cuda.current_stream()
-    sp = rb.ctypes.c_void_p(stream.cuda_stream)
-    yptr = [rb.ctypes.c_void_p(ys[i].data_ptr()) for i in range(2)]
+    K, W, B = args.steps, args.warmup, args.batch
 
-    def step(t):
-        s = L.replay_decode_step(st.h, rb.ctypes.byref(inputs[t]), yptr[t & 1], sp)
-        if s != rb.OK:
-            raise rb.ReplayError(s, "replay_decode_step")
-
-    for t in range(W):
-        step(t)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    t0 = time.perf_counter()
-    for i in range(K):
-        ev[i][0].record(stream)
-        step(W + i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = [s.elapsed_time(e) for s, e in ev]                  # ms per launch
-    total_ms = ev[0][0].elapsed_time(ev[-1][1])
-    value = B * K / (total_ms / 1e3)
-    lens_flush = [(W + i) % cap == cap - 1 for i in range(K)]
-    flush_ms = [p for p, f in zip(per, lens_flush) if f]
-    nonflush_ms = [p for p, f in zip(per, lens_flush) if not f]
-    avg_ms = sum(per) / len(per)
-    bytes_unit = mamba2_algorithmic_bytes(B, H, G, P, N, cap)
-    achieved = bytes_unit * B / (avg_ms / 1e3) / 1e9
-    traffic = read_traffic(B)
-    del inputs, toks
+    m2 = Layer(rb, synth, torch, dev, "mamba2", B, K + W + 4, seed=1)
+    r = time_replay_decode(m2, K, W, stream)
+    replay_b, _ = algorithmic_bytes("mamba2", m2.H, m2.G, m2.C, m2.R)
+    achieved = replay_b * B / (r["avg_launch_ms"] / 1e3) / 1e9
+    conv_ms = None if args.no_extras else time_conv_decode(m2, min(args.conv_steps, K), stream)
+    head = decode_report(m2, r, conv_ms)
+    del m2
 
     out = {
         "metric": "SSM-layer decode tokens/s at batch 256; achieved HBM GB/s vs MI355X peak",
-        "value": round(value, 1),
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
-        "ms_per_step": round(total_ms / K, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded, drawn on device; random checkpoint N(0,0.1))",
-        "config": {"workload": "Mamba-2 SSM layer replayed decode", "batch": B, "nheads": H, "head_dim": P,
-                   "state_dim": N, "ngroups": G, "buffer": cap, "checkpoint": "fp32", "io": "bf16"},
+        "config": {"workload": "Mamba-2 SSM layer, replayed decode", "batch": B, "nheads": 128, "head_dim": 64,
+                   "state_dim": 128, "ngroups": 8, "buffer": 16, "checkpoint": "fp32", "io": "bf16"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "mamba2_step_kernel", "algorithmic_bytes_per_launch": int(bytes_unit * B),
-                     "avg_launch_ms": round(avg_ms, 5)},
-        "split": {"flush_step_ms": round(sum(flush_ms) / max(1, len(flush_ms)), 5),
-                  "nonflush_step_ms": round(sum(nonflush_ms) / max(1, len(nonflush_ms)), 5),
-                  "bytes_per_token_algorithmic": int(bytes_unit)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
+                     "kernel": "mamba2_step_kernel", "algorithmic_bytes_per_launch": int(replay_b * B),
+                     "avg_launch_ms": round(r["avg_launch_ms"], 5)},
+        "mamba2": head,
     }
+    out["copy_ceiling_gbs"], out["read_ceiling_gbs"] = ceilings(rb, torch, dev, stream)
 
-    # streaming ceilings: 1 GiB -> 1 GiB copy and 1 GiB read, same stream
-    src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        rb.stream_copy(dst, src, src.numel() * 4)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(10):
-        rb.stream_copy(dst, src, src.numel() * 4)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = 10 * 2 * src.numel() * 4 / (e0.elapsed_time(e1) / 1e3) / 1e9
-    out["copy_ceiling_gbs"] = round(copy_gbs, 1)
-    acc = torch.zeros(1, dtype=torch.float32, device=dev)
-    for _ in range(3):
-        rb.stream_read(src, src.numel() * 4, acc)
-    e0.record(stream)
-    for _ in range(10):
-        rb.stream_read(src, src.numel() * 4, acc)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    out["read_ceiling_gbs"] = round(10 * src.numel() * 4 / (e0.elapsed_time(e1) / 1e3) / 1e9, 1)
-    del src, dst
-
-    if not args.no_conv:
-        # in-run conventional fused decode (load, decay and update, output, store) on the same layer
-        Kc = min(args.conv_steps, K)
-        Sc = S0.clone()
-        ctoks = synth.mamba2_tokens_device(2, Kc + 4, B, H, G, P, N, dev)
-        cin = [rb.make_inputs(cfg, {k: v[t:t + 1] for k, v in ctoks.items()}, params) for t in range(Kc + 4)]
-        cfgp = rb.ctypes.byref(cfg)
-        Sp = rb.ctypes.c_void_p(Sc.data_ptr())
-        for t in range(4):
-            L.replay_conv_decode_step(cfgp, Sp, rb.ctypes.byref(cin[t]), yptr[0], sp)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for t in range(Kc):
-            s = L.replay_conv_decode_step(cfgp, Sp, rb.ctypes.byref(cin[4 + t]), yptr[t & 1], sp)
-            if s != rb.OK:
-                raise rb.ReplayError(s, "replay_conv_decode_step")
-        e1.record(stream)
-        torch.cuda.synchronize()
-        conv_ms = e0.elapsed_time(e1) / Kc
-        conv_bytes = conv_algorithmic_bytes(B, H, G, P, N)
-        out["conventional"] = {"tokens_per_s": round(B / (conv_ms / 1e3), 1), "ms_per_step": round(conv_ms, 5),
-                               "achieved_gbs": round(conv_bytes * B / (conv_ms / 1e3) / 1e9, 1),
-                               "bytes_per_token_algorithmic": int(conv_bytes), "steps": Kc}
-        out["replay_speedup_vs_conventional"] = round(conv_ms / (total_ms / K), 3)
-        out["state_traffic_reduction_algorithmic"] = round(1 - bytes_unit / conv_bytes, 4)
-        del Sc, ctoks, cin
+    if not args.no_extras:
+        gd = Layer(rb, synth, torch, dev, "gdn", B, K + W + 4, seed=2)
+        rg = time_replay_decode(gd, K, W, stream)
+        out["gdn"] = decode_report(gd, rg, time_conv_decode(gd, min(args.conv_steps, K), stream))
+        del gd
+        torch.cuda.empty_cache()
+        spec = {}
+        for kind, seed in (("mamba2", 31), ("gdn", 32)):
+            Ls = Layer(rb, synth, torch, dev, kind, 512, args.spec_rounds * 4, seed=seed)
+            spec[kind] = time_spec(Ls, args.spec_rounds, 4, stream)
+            del Ls
+            torch.cuda.empty_cache()
+        out["spec"] = spec
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(B, H, G, P, N)
-    out["wall_s_timed_region"] = round(wall, 3)
+        out["cpu_baseline"] = cpu_baseline(128, 8, 64, 128)
     print(json.dumps(out), flush=True)
 
 

@@ -53,6 +53,61 @@ __device__ __forceinline__ float wave_sum64(float v) {
     return v;
 }
 
+// ---- DPP (data-parallel primitives) on gfx9: VALU lane permutes without LDS
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, false));
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_MIRROR = 0x140;      // lane i <-> 15-i within a row of 16
+constexpr int DPP_ROW_HALF_MIRROR = 0x141; // lane i <-> 7-i within half a row
+constexpr int DPP_ROW_BCAST15 = 0x142;     // lane 15 of a row -> the next row
+constexpr int DPP_ROW_BCAST31 = 0x143;     // lane 31 -> rows 2 and 3
+
+// Sum over the 4 lanes of each quad; every lane of the quad gets the sum.
+__device__ __forceinline__ float quad_sum(float v) {
+    v += dpp_mov<DPP_QUAD_XOR1>(v);
+    v += dpp_mov<DPP_QUAD_XOR2>(v);
+    return v;
+}
+
+__device__ __forceinline__ float readlane(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Sum over the whole wave, returned to every lane (wave-uniform): quads, half
+// rows, rows by mirrors, then rows into lane 63 by the row broadcasts.
+__device__ __forceinline__ float wave_sum_uniform(float v) {
+    v = quad_sum(v);
+    v += dpp_mov<DPP_ROW_HALF_MIRROR>(v);
+    v += dpp_mov<DPP_ROW_MIRROR>(v);
+    v += dpp_mov<DPP_ROW_BCAST15, 0xa>(v);
+    v += dpp_mov<DPP_ROW_BCAST31, 0xc>(v);
+    return readlane(v, 63);
+}
+
+// Sum over aligned groups of N consecutive lanes (N = 4, 8, 16, 32 or 64),
+// returned to every lane of the group.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group size");
+    v = quad_sum(v);
+    if constexpr (N >= 8) v += dpp_mov<DPP_ROW_HALF_MIRROR>(v);
+    if constexpr (N >= 16) v += dpp_mov<DPP_ROW_MIRROR>(v);
+    if constexpr (N == 32) {
+        v += dpp_mov<DPP_ROW_BCAST15, 0xa>(v);            // rows 1 and 3 hold their pair's sum
+        const float lo = readlane(v, 31), hi = readlane(v, 63);
+        v = (__lane_id() < 32) ? lo : hi;
+    }
+    if constexpr (N == 64) {
+        v += dpp_mov<DPP_ROW_BCAST15, 0xa>(v);
+        v += dpp_mov<DPP_ROW_BCAST31, 0xc>(v);
+        v = readlane(v, 63);
+    }
+    return v;
+}
+
 // Sum over the four lanes that share (lane % 16): lanes l, l^16, l^32, l^48.
 __device__ __forceinline__ float sum_over_row_groups(float v) {
     v += __shfl_xor(v, 16, 64);
@@ -74,6 +129,22 @@ __device__ __forceinline__ int xcd_tile_index() {
     const int n = (int)gridDim.x, i = (int)blockIdx.x;
     if ((n & 7) == 0) return (i & 7) * (n >> 3) + (i >> 3);
     return i;
+}
+
+// A (b, h) tile may be split over `nsplit` workgroups along its output axis;
+// consecutive work items are the splits of one head, then the heads of one
+// sequence.
+struct TileIdx {
+    int b, h, sp;
+};
+
+__device__ __forceinline__ TileIdx tile_of(int item, int H, int nsplit) {
+    TileIdx t;
+    t.sp = item % nsplit;
+    const int bh = item / nsplit;
+    t.b = bh / H;
+    t.h = bh - t.b * H;
+    return t;
 }
 
 __device__ __forceinline__ f32x4 mfma16x16x4(float a, float b, f32x4 c) {

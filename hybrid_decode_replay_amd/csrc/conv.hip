@@ -21,9 +21,7 @@ namespace rs {
 
 template <int N4>
 __device__ __forceinline__ float row_sum(float v) {
-#pragma unroll
-    for (int o = N4 / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    return group_sum<N4>(v);     // the N4 adjacent lanes of a row, by DPP
 }
 
 template <int IO>

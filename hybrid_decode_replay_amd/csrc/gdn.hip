@@ -3,7 +3,10 @@
 // Layer: per head, S (d_v x d_k) evolves as S <- alpha S (I - beta k k^T) + beta v k^T
 // and o = scale S q (gated delta rule).  The checkpoint tile is fragment-
 // ordered (common.hpp) with the reduction axis r = d_k and the output axis
-// c = d_v: wave w owns the 16 value rows v in [16w, 16w+16).
+// c = d_v.  The value rows of a head are split over workgroups of at most
+// four waves (d_v = 128: two workgroups of 64 rows) so that several
+// workgroups share a CU; wave w owns 16 value rows.  Each slice recomputes the
+// small per-head quantities (chains, Gram matrix, inverse) itself.
 //
 // Per launch and sequence the virtual entry list is the committed buffer
 // entries followed by the T new tokens; the first f entries are folded into
@@ -42,24 +45,26 @@ __global__ __launch_bounds__(1024) void gdn_step_kernel(StepArgs a)
     constexpr int PRE = 4;
     constexpr int RPL = (R + 63) / 64;          // chain elements per lane
     const int C = a.C;                          // d_v
-    const int tile = xcd_tile_index();
-    const int b = tile / a.H, h = tile - b * a.H;
+    const TileIdx tix = tile_of(xcd_tile_index(), a.H, a.nsplit);
+    const int b = tix.b, h = tix.h, tile = b * a.H + h;
     const int g = h / a.hpg;
+    const int cw = C / a.nsplit, c0 = tix.sp * cw;   // this workgroup's output columns
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int w = tid >> 6, lane = tid & 63, waves = nthr >> 6;
-    const int col = 16 * w + (lane & 15);
+    const int lc = 16 * w + (lane & 15);             // local output column
+    const int col = c0 + lc;                          // global output column
     const int rq = 4 * (lane >> 4);
     const int l16 = lane & 15, lq = lane >> 4;
     const size_t sB = (size_t)a.B;
 
-    const StepPlan p = plan_step(a, b, h == 0 && tid == 0);
+    const StepPlan p = plan_step(a, b, h == 0 && tix.sp == 0 && tid == 0);
     if (a.mode == MODE_FLUSH && p.f == 0) return;
     const int f = p.f, len = p.len, V = p.V, T = a.T;
     const int Tr = T > 0 ? T : 1, vmax = a.vmax;
 
     // ---- LDS partition (floats)
-    float* vs = lds;                          // [vmax][C]   entry v rows
-    float* ks = vs + (size_t)vmax * C;        // [vmax][RS]  entry k rows
+    float* vs = lds;                          // [vmax][cw]  entry v rows (own columns)
+    float* ks = vs + (size_t)vmax * cw;       // [vmax][RS]  entry k rows
     float* qs = ks + (size_t)vmax * RS;       // [Tr][R]     query rows
     float* rz = qs + (size_t)Tr * R;          // [Tr][R]     chain results r_0
     float* al = rz + (size_t)Tr * R;          // [vmax]      alpha
@@ -73,6 +78,7 @@ __global__ __launch_bounds__(1024) void gdn_step_kernel(StepArgs a)
     G.bank_c = a.bank_c; G.bank_r = a.bank_r; G.bank_s = a.bank_s;
     G.hc = (size_t)b * a.H + h; G.gr = (size_t)b * a.G + g;
     G.b = b; G.h = h; G.g = g; G.B = a.B; G.H = a.H; G.G = a.G; G.cap = a.cap; G.C = C;
+    G.c0 = c0; G.cw = cw;
     G.len = len; G.bank = p.bank; G.V = V; G.T = T;
     G.xc = vs; G.xr = ks; G.xq = qs; G.s0 = al; G.s1 = be;
 
@@ -81,7 +87,7 @@ __global__ __launch_bounds__(1024) void gdn_step_kernel(StepArgs a)
     uint4 pre[PRE];
     ScalarRaw sr;
     stage_issue<IO, R, PRE, false>(stg, tid, nthr, pre, sr);
-    float* ckw = a.ckpt + (((size_t)tile * (C >> 4) + w) * NB * 64 + lane) * 4;
+    float* ckw = a.ckpt + (((size_t)tile * (C >> 4) + (c0 >> 4) + w) * NB * 64 + lane) * 4;
     f32x4 s[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) s[nb] = ld4_stream(ckw + (size_t)nb * 256);
@@ -151,7 +157,7 @@ __global__ __launch_bounds__(1024) void gdn_step_kernel(StepArgs a)
             if (i < f) {
                 float P = 1.f;
                 for (int m = 0; m <= i; ++m) P *= al[m];
-                v = be[i] * (vs[i * C + col] - P * W[r]);
+                v = be[i] * (vs[i * cw + lc] - P * W[r]);
             }
             rhs[r] = v;
         }
@@ -199,7 +205,7 @@ __global__ __launch_bounds__(1024) void gdn_step_kernel(StepArgs a)
                     const int e = lane + 64 * u;
                     if (e < R) part += ks[i * RS + e] * r[u];
                 }
-                const float c = be[i] * wave_sum64(part);
+                const float c = be[i] * wave_sum_uniform(part);
                 const float alpha = al[i];
 #pragma unroll
                 for (int u = 0; u < RPL; ++u) {
@@ -226,7 +232,7 @@ __global__ __launch_bounds__(1024) void gdn_step_kernel(StepArgs a)
                 gacc = sum_over_row_groups(gacc);
                 const int pos = len + t;
                 float rep = 0.f;
-                for (int i = f; i <= pos; ++i) rep += cc[t * vmax + i] * vs[i * C + col];
+                for (int i = f; i <= pos; ++i) rep += cc[t * vmax + i] * vs[i * cw + lc];
                 if (lane < 16) st_io<IO>(a.y, (((size_t)t * sB + b) * a.H + h) * C + col, a.scale * (gacc + rep));
             }
         }
@@ -239,7 +245,8 @@ __global__ __launch_bounds__(1024) void gdn_step_kernel(StepArgs a)
     }
 
     // ---- 7. append the unfolded new tokens
-    stage_append<IO, R>(G, a.bufc, a.bufr, a.bufs0, a.bufs1, p.bank_new, f, tid, nthr, h % a.hpg == 0);
+    stage_append<IO, R>(G, a.bufc, a.bufr, a.bufs0, a.bufs1, p.bank_new, f, tid, nthr, tix.sp == 0,
+                        tix.sp == 0 && h % a.hpg == 0);
 }
 
 template <int NB, int IO, int TMAX>
@@ -247,13 +254,13 @@ static hipError_t launch_nb(const StepArgs& a, hipStream_t s)
 {
     const size_t Tr = a.T > 0 ? a.T : 1;
     const size_t R = NB * 16, vmax = a.vmax;
-    const size_t lds = sizeof(float) * (vmax * (a.C + R + 4) + 2 * Tr * R + 2 * vmax + Tr * vmax + 16 * 17);
+    const size_t lds = sizeof(float) * (vmax * (a.C / a.nsplit + R + 4) + 2 * Tr * R + 2 * vmax + Tr * vmax + 16 * 17);
     auto k = gdn_step_kernel<NB, IO, TMAX>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k, dim3(a.B * a.H), dim3(a.C * 4), lds, s, a);
+    hipLaunchKernelGGL(k, dim3(a.B * a.H * a.nsplit), dim3(a.C / a.nsplit * 4), lds, s, a);
     return hipGetLastError();
 }
 

@@ -170,6 +170,13 @@ rs::StepArgs step_args(const replay_state* st, const replay_inputs* in, void* y,
     a.T = T;
     a.vmax = mode == rs::MODE_DECODE ? c->buf_cap + 1 : (mode == rs::MODE_FLUSH ? c->buf_cap : c->buf_cap + T);
     a.scale = c->scale;
+    // workgroups of at most 4 waves (one 16-column strip each): the largest
+    // divisor of the strip count that is <= 4 sets the waves per workgroup
+    const int strips = c->head_dim / 16;
+    int wpg = 1;
+    for (int d = 4; d >= 1; --d)
+        if (strips % d == 0) { wpg = d; break; }
+    a.nsplit = strips / wpg;
     const replay_layout& L = st->lay;
     a.ckpt = at<float>(st, L.ckpt_off);
     a.rcopy = L.rcopy_bytes ? at<uint8_t>(st, L.rcopy_off) : nullptr;

@@ -25,6 +25,7 @@ struct StepArgs {
     int mode;                // MODE_DECODE / MODE_FLUSH / MODE_SPEC
     int T;                   // new tokens: 1 (decode), k (spec), 0 (flush)
     int vmax;                // LDS rows reserved for the virtual entry list
+    int nsplit;              // workgroups per (b, h) tile, along the output axis
     float scale;             // GDN output scale
     float* ckpt;             // fragment-ordered fp32 tiles
     uint8_t* rcopy;          // read-copy codes (or null)

@@ -1,7 +1,8 @@
 // mamba2.hip -- replayed Mamba-2 decode step for gfx950 (CDNA4).
 //
-// One workgroup per (sequence b, head h); wave w owns the 16 output columns
-// p in [16w, 16w+16) of the head and every state row n (see common.hpp for the
+// One workgroup per (sequence b, head h, column slice): the head's output
+// columns are split over workgroups of at most four waves, and wave w owns 16
+// output columns p and every state row n (see common.hpp for the
 // fragment-ordered tile).  Per launch and sequence the virtual entry list is
 // V = (committed buffer entries 0..len-1) ++ (T new tokens).  The first f
 // entries are folded into the checkpoint (f = 0 on a non-flush step), the
@@ -41,24 +42,26 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
     constexpr int RS = R + 4;                   // padded LDS stride of B rows
     constexpr int PRE = 4;                      // chunks per thread fetched ahead of the checkpoint
     const int C = a.C;
-    const int tile = xcd_tile_index();
-    const int b = tile / a.H, h = tile - b * a.H;
+    const TileIdx tix = tile_of(xcd_tile_index(), a.H, a.nsplit);
+    const int b = tix.b, h = tix.h, tile = b * a.H + h;
     const int g = h / a.hpg;
+    const int cw = C / a.nsplit, c0 = tix.sp * cw;   // this workgroup's output columns
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int w = tid >> 6, lane = tid & 63;
-    const int col = 16 * w + (lane & 15);
+    const int lc = 16 * w + (lane & 15);             // local output column
+    const int col = c0 + lc;                          // global output column
     const int rq = 4 * (lane >> 4);
     const size_t sB = (size_t)a.B;
 
     // ---- bookkeeping: identical decision in every workgroup of sequence b
-    const StepPlan p = plan_step(a, b, h == 0 && tid == 0);
+    const StepPlan p = plan_step(a, b, h == 0 && tix.sp == 0 && tid == 0);
     if (a.mode == MODE_FLUSH && p.f == 0) return;
     const int f = p.f, len = p.len, T = a.T;
 
     // ---- LDS partition (floats)
     const int Tr = T > 0 ? T : 1;
-    float* xs = lds;                              // [vmax][C]  entry x rows
-    float* bs = xs + (size_t)a.vmax * C;          // [vmax][RS] entry B rows
+    float* xs = lds;                              // [vmax][cw] entry x rows (own columns)
+    float* bs = xs + (size_t)a.vmax * cw;         // [vmax][RS] entry B rows
     float* cs = bs + (size_t)a.vmax * RS;         // [Tr][R]    read-out rows C_t
     float* ds = cs + (size_t)Tr * R;              // [vmax]     entry dt
 
@@ -68,6 +71,7 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
     G.bank_c = a.bank_c; G.bank_r = a.bank_r; G.bank_s = a.bank_s;
     G.hc = (size_t)b * a.H + h; G.gr = (size_t)b * a.G + g;
     G.b = b; G.h = h; G.g = g; G.B = a.B; G.H = a.H; G.G = a.G; G.cap = a.cap; G.C = C;
+    G.c0 = c0; G.cw = cw;
     G.len = len; G.bank = p.bank; G.V = p.V; G.T = T;
     G.xc = xs; G.xr = bs; G.xq = cs; G.s0 = ds; G.s1 = nullptr;
 
@@ -78,7 +82,7 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
     stage_issue<IO, R, PRE, true>(stg, tid, nthr, pre, sr);
 
     // ---- 2. checkpoint tile -> registers (one 128-bit load per 16x16 block)
-    float* ckw = a.ckpt + (((size_t)tile * (C >> 4) + w) * NB * 64 + lane) * 4;
+    float* ckw = a.ckpt + (((size_t)tile * (C >> 4) + (c0 >> 4) + w) * NB * 64 + lane) * 4;
     f32x4 s[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) s[nb] = ld4_stream(ckw + (size_t)nb * 256);
@@ -106,7 +110,7 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
                 if (i < f) {
                     float suf = 0.f;
                     for (int j = i + 1; j < f; ++j) suf += ds[j];
-                    v = expf(suf * Ah) * ds[i] * xs[i * C + col];
+                    v = expf(suf * Ah) * ds[i] * xs[i * cw + lc];
                 }
                 bop[kb] = v;
             }
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
                 if (i < f) {
                     float suf = 0.f;
                     for (int j = i + 1; j < f; ++j) suf += ds[j];
-                    v = expf(suf * Ah) * ds[i] * xs[i * C + col];
+                    v = expf(suf * Ah) * ds[i] * xs[i * cw + lc];
                 }
                 wx[i] = v;
             }
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
                 const int pos = len + t;
                 float yv;
                 if (pos < f) {
-                    yv = gacc + Dh * xs[pos * C + col];
+                    yv = gacc + Dh * xs[pos * cw + lc];
                 } else {
                     // replay of entries f..pos: lane quad (jj = l/4) forms B_j . C_t and the
                     // decayed coefficient; output lanes gather the coefficients by shuffle
@@ -176,8 +180,7 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
                             for (int i = 0; i < R / 16; ++i)
                                 dot += dot4(ld4(bs + j * RS + 16 * i + 4 * q), ld4(cs + t * R + 16 * i + 4 * q));
                         }
-                        dot += __shfl_xor(dot, 1, 64);
-                        dot += __shfl_xor(dot, 2, 64);
+                        dot = quad_sum(dot);
                         float coef = 0.f;
                         if (jj < nr) {
                             float suf = 0.f;
@@ -186,11 +189,11 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
                         }
                         const int ne = min(16, nr - jj0);
                         for (int e = 0; e < ne; ++e)
-                            rep += __shfl(coef, 4 * e, 64) * xs[(f + jj0 + e) * C + col];
+                            rep += readlane(coef, 4 * e) * xs[(f + jj0 + e) * cw + lc];
                     }
                     float Lp = 0.f;
                     for (int i = f; i <= pos; ++i) Lp += ds[i];
-                    yv = expf(Lp * Ah) * gacc + rep + Dh * xs[pos * C + col];
+                    yv = expf(Lp * Ah) * gacc + rep + Dh * xs[pos * cw + lc];
                 }
                 if (lane < 16) st_io<IO>(a.y, (((size_t)t * sB + b) * a.H + h) * C + col, yv);
             }
@@ -204,7 +207,8 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
     }
 
     // ---- 7. append the unfolded new tokens to the buffer (slot = position - f)
-    stage_append<IO, R>(G, a.bufc, a.bufr, a.bufs0, nullptr, p.bank_new, f, tid, nthr, h % a.hpg == 0);
+    stage_append<IO, R>(G, a.bufc, a.bufr, a.bufs0, nullptr, p.bank_new, f, tid, nthr, tix.sp == 0,
+                        tix.sp == 0 && h % a.hpg == 0);
 }
 
 template <int NB, int IO, int TMAX, bool MF>
@@ -212,13 +216,13 @@ static hipError_t launch_nb(const StepArgs& a, hipStream_t s)
 {
     const size_t Tr = a.T > 0 ? a.T : 1;
     const size_t R = NB * 16;
-    const size_t lds = sizeof(float) * ((size_t)a.vmax * (a.C + R + 4) + Tr * R + (size_t)a.vmax);
+    const size_t lds = sizeof(float) * ((size_t)a.vmax * (a.C / a.nsplit + R + 4) + Tr * R + (size_t)a.vmax);
     auto k = mamba2_step_kernel<NB, IO, TMAX, MF>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k, dim3(a.B * a.H), dim3(a.C * 4), lds, s, a);
+    hipLaunchKernelGGL(k, dim3(a.B * a.H * a.nsplit), dim3(a.C / a.nsplit * 4), lds, s, a);
     return hipGetLastError();
 }
 

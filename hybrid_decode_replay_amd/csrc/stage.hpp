@@ -27,7 +27,8 @@ struct StageGeom {
     size_t bank_c, bank_r, bank_s;
     size_t hc, gr;       // b*H + h, b*G + g
     int b, h, g, B, H, G, cap, C, len, bank, V, T;
-    float* xc;           // LDS [vmax][C]
+    int c0, cw;          // column slice [c0, c0 + cw) of the per-head vectors this workgroup owns
+    float* xc;           // LDS [vmax][cw]
     float* xr;           // LDS [vmax][R + 4]
     float* xq;           // LDS [T][R]
     float* s0;           // LDS [vmax]
@@ -72,7 +73,7 @@ struct Stager {
     int CX, nx, nr, nch;
 
     __device__ explicit Stager(const StageGeom& g) : G(g) {
-        CX = G.C / EPC;
+        CX = G.cw / EPC;
         nx = G.V * CX;
         nr = G.V * RX;
         nch = nx + nr + G.T * RX;
@@ -83,8 +84,8 @@ struct Stager {
         const void* base;
         if (ch < nx) {
             const int j = ch / CX, o = ch - j * CX;
-            if (j < G.len) { base = G.bufc; e = (size_t)G.bank * G.bank_c + (G.hc * G.cap + j) * G.C; }
-            else { base = G.in_c; e = (((size_t)(j - G.len) * G.B + G.b) * G.H + G.h) * G.C; }
+            if (j < G.len) { base = G.bufc; e = (size_t)G.bank * G.bank_c + (G.hc * G.cap + j) * G.C + G.c0; }
+            else { base = G.in_c; e = (((size_t)(j - G.len) * G.B + G.b) * G.H + G.h) * G.C + G.c0; }
             return reinterpret_cast<const uint4*>(static_cast<const char*>(base) + e * ES) + o;
         }
         ch -= nx;
@@ -101,7 +102,7 @@ struct Stager {
     }
 
     __device__ float* dst(int ch) const {
-        if (ch < nx) { const int j = ch / CX; return G.xc + j * G.C + (ch - j * CX) * EPC; }
+        if (ch < nx) { const int j = ch / CX; return G.xc + j * G.cw + (ch - j * CX) * EPC; }
         ch -= nx;
         if (ch < nr) { const int j = ch / RX; return G.xr + j * RS + (ch - j * RX) * EPC; }
         ch -= nr;
@@ -162,23 +163,25 @@ __device__ __forceinline__ void stage_publish(const Stager<IO, R>& st, int tid, 
 }
 
 // Append the unfolded new entries [j0, V) to the buffer bank `bank_new` at
-// slot (position - f): per-head vectors and scalars always, per-group vectors
-// only from the first head of the group.
+// slot (position - f): each workgroup writes its own column slice of the
+// per-head vectors; scalars come from the first slice, per-group vectors from
+// the first slice of the first head of the group.
 template <int IO, int R>
 __device__ __forceinline__ void stage_append(const StageGeom& G, void* bufc, void* bufr, float* bufs0, float* bufs1,
-                                             int bank_new, int f, int tid, int nthr, bool group_writer)
+                                             int bank_new, int f, int tid, int nthr, bool head_writer,
+                                             bool group_writer)
 {
     using S = Stager<IO, R>;
     const int j0 = max(f, G.len);
     const int nnew = G.V - j0;
     if (nnew <= 0) return;
-    const int CX = G.C / S::EPC;
-    char* bx = static_cast<char*>(bufc) + ((size_t)bank_new * G.bank_c + G.hc * G.cap * G.C) * S::ES;
+    const int CX = G.cw / S::EPC;
+    char* bx = static_cast<char*>(bufc) + ((size_t)bank_new * G.bank_c + G.hc * G.cap * G.C + G.c0) * S::ES;
     for (int i = tid; i < nnew * CX; i += nthr) {
         const int jj = i / CX, o = i - jj * CX, j = j0 + jj;
-        reinterpret_cast<uint4*>(bx + (size_t)(j - f) * G.C * S::ES)[o] = lds_to_chunk<IO>(G.xc + j * G.C + o * S::EPC);
+        reinterpret_cast<uint4*>(bx + (size_t)(j - f) * G.C * S::ES)[o] = lds_to_chunk<IO>(G.xc + j * G.cw + o * S::EPC);
     }
-    if (tid < nnew) {
+    if (head_writer && tid < nnew) {
         bufs0[(size_t)bank_new * G.bank_s + G.hc * G.cap + (j0 + tid - f)] = G.s0[j0 + tid];
         if (bufs1) bufs1[(size_t)bank_new * G.bank_s + G.hc * G.cap + (j0 + tid - f)] = G.s1[j0 + tid];
     }
