@@ -1,6 +1,7 @@
 // aux.hip -- bookkeeping, layout conversion and measurement kernels.
 #include "common.hpp"
 #include "internal.hpp"
+#include "rc.hpp"
 
 namespace rs {
 
@@ -109,6 +110,109 @@ hipError_t launch_logical_to_tiles(const float* in, float* ckpt, int tiles, int 
     const size_t n4 = (size_t)tiles * C * R / 4;
     hipLaunchKernelGGL(logical_to_tiles_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, in, ckpt, n4, C, R);
     return hipGetLastError();
+}
+
+// ---- read copy: quantize the fragment-ordered checkpoint, export codes ---------
+// One wave per (tile, 16-column strip), in the same lane order as the replay
+// kernels, so the quantizer is the one the flush path uses.
+template <int NB, int RC>
+__global__ __launch_bounds__(256) void quantize_rc_kernel(const float* ckpt, uint8_t* codes, uint8_t* scales,
+                                                          size_t nstrips)
+{
+    const size_t strip = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (strip >= nstrips) return;                  // whole waves leave together
+    f32x4 s[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) s[nb] = ld4(ckpt + ((strip * NB + nb) * 64 + lane) * 4);
+    rc_store<NB, RC>(codes, scales, strip, lane, s);
+}
+
+// Raw codes to logical order: codes_out [tiles][C][R] (one code per byte),
+// scales_out [tiles][C][R/32] for MXFP4.
+template <int NB, int RC>
+__global__ __launch_bounds__(256) void rc_to_logical_kernel(const uint8_t* codes, const uint8_t* scales,
+                                                            uint8_t* codes_out, uint8_t* scales_out, size_t nstrips, int C)
+{
+    constexpr int R = NB * 16;
+    const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t strip = gid / 64;
+    const int lane = (int)(gid % 64);
+    if (strip >= nstrips) return;
+    const int strips = C / 16;
+    const size_t tile = strip / strips;
+    const int c = 16 * (int)(strip % strips) + (lane & 15);
+    uint8_t* row = codes_out + (tile * C + c) * R;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            uint32_t code;
+            if constexpr (RC == RC_FP8) {
+                constexpr int BPL = 4 * NB;
+                code = (BPL >= 16) ? codes[rc_offset<BPL>(strip, nb / 4, lane) + (nb % 4) * 4 + r]
+                                   : codes[rc_offset<BPL>(strip, 0, lane) + 4 * nb + r];
+            } else {
+                constexpr int BPL = 2 * NB;
+                const int n = (BPL >= 16 ? (nb % 8) : nb) * 4 + r;
+                const uint8_t byte = codes[rc_offset<BPL>(strip, BPL >= 16 ? nb / 8 : 0, lane) + n / 2];
+                code = (n & 1) ? (byte >> 4) : (byte & 0xfu);
+            }
+            row[16 * nb + 4 * (lane >> 4) + r] = (uint8_t)code;
+        }
+    }
+    if constexpr (RC == RC_MXFP4) {
+        if (lane < 16) {
+            constexpr int NP = NB / 2;
+            for (int p = 0; p < NP; ++p) scales_out[(tile * C + c) * NP + p] = scales[(strip * 16 + lane) * NP + p];
+        }
+    }
+}
+
+template <int RC>
+static hipError_t rc_dispatch(bool quantize, const float* ckpt, const uint8_t* codes_in, const uint8_t* scales_in,
+                              uint8_t* codes, uint8_t* scales, int tiles, int C, int R, hipStream_t s)
+{
+    const size_t nstrips = (size_t)tiles * (C / 16);
+    const dim3 grid((unsigned)((nstrips + 3) / 4)), block(256);
+#define RS_RC_CASE(NBV)                                                                                  \
+    case NBV * 16:                                                                                       \
+        if (quantize) hipLaunchKernelGGL((quantize_rc_kernel<NBV, RC>), grid, block, 0, s, ckpt, codes, scales, nstrips); \
+        else hipLaunchKernelGGL((rc_to_logical_kernel<NBV, RC>), grid, block, 0, s, codes_in, scales_in, codes, scales,    \
+                                nstrips, C);                                                             \
+        return hipGetLastError();
+    switch (R) {
+        case 16:
+            if constexpr (RC == RC_FP8) {
+                if (quantize) hipLaunchKernelGGL((quantize_rc_kernel<1, RC>), grid, block, 0, s, ckpt, codes, scales, nstrips);
+                else hipLaunchKernelGGL((rc_to_logical_kernel<1, RC>), grid, block, 0, s, codes_in, scales_in, codes, scales,
+                                        nstrips, C);
+                return hipGetLastError();
+            }
+            return hipErrorInvalidValue;
+        RS_RC_CASE(2)
+        RS_RC_CASE(4)
+        RS_RC_CASE(8)
+        RS_RC_CASE(16)
+    }
+#undef RS_RC_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_quantize_read_copy(const float* ckpt, uint8_t* codes, uint8_t* scales, int tiles, int C, int R, int rc,
+                                     hipStream_t s)
+{
+    if (rc == RC_FP8) return rc_dispatch<RC_FP8>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, s);
+    if (rc == RC_MXFP4) return rc_dispatch<RC_MXFP4>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_read_copy_to_logical(const uint8_t* codes, const uint8_t* scales, uint8_t* codes_out,
+                                       uint8_t* scales_out, int tiles, int C, int R, int rc, hipStream_t s)
+{
+    if (rc == RC_FP8) return rc_dispatch<RC_FP8>(false, nullptr, codes, scales, codes_out, scales_out, tiles, C, R, s);
+    if (rc == RC_MXFP4) return rc_dispatch<RC_MXFP4>(false, nullptr, codes, scales, codes_out, scales_out, tiles, C, R, s);
+    return hipErrorInvalidValue;
 }
 
 // ---- streaming copy (bandwidth ceiling and byte-counter reference) --------

@@ -32,11 +32,12 @@
 // Decay factors are formed as products of the gates, never as quotients.
 #include "common.hpp"
 #include "internal.hpp"
+#include "rc.hpp"
 #include "stage.hpp"
 
 namespace rs {
 
-template <int NB, int IO, int TMAX>
+template <int NB, int IO, int TMAX, int RC>
 __global__ __launch_bounds__(1024) void gdn_step_kernel(StepArgs a)
 {
     extern __shared__ float lds[];
@@ -87,10 +88,18 @@ __global__ __launch_bounds__(1024) void gdn_step_kernel(StepArgs a)
     uint4 pre[PRE];
     ScalarRaw sr;
     stage_issue<IO, R, PRE, false>(stg, tid, nthr, pre, sr);
-    float* ckw = a.ckpt + (((size_t)tile * (C >> 4) + (c0 >> 4) + w) * NB * 64 + lane) * 4;
+    // a step that folds nothing reads the low-precision copy when there is one
+    const size_t strip_index = (size_t)tile * (C >> 4) + (c0 >> 4) + w;
+    float* ckw = a.ckpt + (strip_index * NB * 64 + lane) * 4;
     f32x4 s[NB];
+    bool from_copy = false;
+    if constexpr (RC != RC_NONE) from_copy = (f == 0);
+    if (from_copy) {
+        if constexpr (RC != RC_NONE) rc_load<NB, RC>(a.rcopy, a.rscale, strip_index, lane, s);
+    } else {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) s[nb] = ld4_stream(ckw + (size_t)nb * 256);
+        for (int nb = 0; nb < NB; ++nb) s[nb] = ld4_stream(ckw + (size_t)nb * 256);
+    }
     stage_publish<IO, R, PRE>(stg, tid, nthr, pre, sr);
     __syncthreads();
 
@@ -242,6 +251,7 @@ __global__ __launch_bounds__(1024) void gdn_step_kernel(StepArgs a)
     if (f > 0) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) st4_stream(ckw + (size_t)nb * 256, s[nb]);
+        if constexpr (RC != RC_NONE) rc_store<NB, RC>(a.rcopy, a.rscale, strip_index, lane, s);
     }
 
     // ---- 7. append the unfolded new tokens
@@ -249,13 +259,13 @@ __global__ __launch_bounds__(1024) void gdn_step_kernel(StepArgs a)
                         tix.sp == 0 && h % a.hpg == 0);
 }
 
-template <int NB, int IO, int TMAX>
+template <int NB, int IO, int TMAX, int RC>
 static hipError_t launch_nb(const StepArgs& a, hipStream_t s)
 {
     const size_t Tr = a.T > 0 ? a.T : 1;
     const size_t R = NB * 16, vmax = a.vmax;
     const size_t lds = sizeof(float) * (vmax * (a.C / a.nsplit + R + 4) + 2 * Tr * R + 2 * vmax + Tr * vmax + 16 * 17);
-    auto k = gdn_step_kernel<NB, IO, TMAX>;
+    auto k = gdn_step_kernel<NB, IO, TMAX, RC>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -264,31 +274,40 @@ static hipError_t launch_nb(const StepArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int IO, int TMAX>
+template <int IO, int TMAX, int RC>
 static hipError_t launch_io(const StepArgs& a, hipStream_t s)
 {
     switch (a.R) {
-        case 16: return launch_nb<1, IO, TMAX>(a, s);
-        case 32: return launch_nb<2, IO, TMAX>(a, s);
-        case 64: return launch_nb<4, IO, TMAX>(a, s);
-        case 128: return launch_nb<8, IO, TMAX>(a, s);
-        case 256: return launch_nb<16, IO, TMAX>(a, s);
+        case 16:
+            if constexpr (RC != RC_MXFP4) return launch_nb<1, IO, TMAX, RC>(a, s);
+            return hipErrorInvalidValue;     // MXFP4 groups need 32 rows
+        case 32: return launch_nb<2, IO, TMAX, RC>(a, s);
+        case 64: return launch_nb<4, IO, TMAX, RC>(a, s);
+        case 128: return launch_nb<8, IO, TMAX, RC>(a, s);
+        case 256: return launch_nb<16, IO, TMAX, RC>(a, s);
     }
     return hipErrorInvalidValue;
 }
 
-template <int TMAX>
+template <int TMAX, int RC>
 static hipError_t launch_t(const StepArgs& a, int io, hipStream_t s)
 {
-    return io == IO_BF16 ? launch_io<IO_BF16, TMAX>(a, s) : launch_io<IO_F32, TMAX>(a, s);
+    return io == IO_BF16 ? launch_io<IO_BF16, TMAX, RC>(a, s) : launch_io<IO_F32, TMAX, RC>(a, s);
+}
+
+template <int TMAX>
+static hipError_t launch_tm(const StepArgs& a, int io, int rc, hipStream_t s)
+{
+    if (rc == RC_FP8) return launch_t<TMAX, RC_FP8>(a, io, s);
+    if (rc == RC_MXFP4) return launch_t<TMAX, RC_MXFP4>(a, io, s);
+    return launch_t<TMAX, RC_NONE>(a, io, s);
 }
 
 hipError_t launch_gdn_step(const StepArgs& a, int io, int rc, hipStream_t s)
 {
-    if (rc != RC_NONE) return hipErrorNotSupported;
-    if (a.T <= 1) return launch_t<1>(a, io, s);
-    if (a.T <= 4) return launch_t<4>(a, io, s);
-    return launch_t<16>(a, io, s);
+    if (a.T <= 1) return launch_tm<1>(a, io, rc, s);
+    if (a.T <= 4) return launch_tm<4>(a, io, rc, s);
+    return launch_tm<16>(a, io, rc, s);
 }
 
 }  // namespace rs

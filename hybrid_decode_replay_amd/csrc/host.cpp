@@ -81,7 +81,6 @@ replay_status check_config(const replay_config* c)
         return fail(REPLAY_ERR_DTYPE, "read_copy must be NONE, FP8_E4M3 or MXFP4");
     if (c->read_copy == REPLAY_MXFP4 && R % 32 != 0)
         return fail(REPLAY_ERR_SHAPE, "MXFP4 read copy needs state_dim divisible by 32");
-    if (c->read_copy != REPLAY_NONE) return fail(REPLAY_ERR_UNSUPPORTED, "read copies not built yet");
     if (c->flags & ~REPLAY_FLAG_VALU_FOLD) return fail(REPLAY_ERR_ARG, "unknown flags 0x%x", c->flags);
     return ok();
 }
@@ -122,6 +121,11 @@ void compute_layout(const replay_config* c, replay_layout* L)
 
 template <class T>
 T* at(const replay_state* st, uint64_t off) { return reinterpret_cast<T*>(st->mem + off); }
+
+int rc_kind(const replay_config* c)
+{
+    return c->read_copy == REPLAY_FP8_E4M3 ? rs::RC_FP8 : (c->read_copy == REPLAY_MXFP4 ? rs::RC_MXFP4 : rs::RC_NONE);
+}
 
 replay_status check_ptr(const void* p, const char* name)
 {
@@ -214,7 +218,7 @@ replay_status launch_step(replay_state* st, const replay_inputs* in, void* y, in
     const replay_config* c = &st->cfg;
     rs::StepArgs a = step_args(st, in, y, mode, T);
     const int io = c->io_dtype == REPLAY_BF16 ? rs::IO_BF16 : rs::IO_F32;
-    const int rc = c->read_copy == REPLAY_FP8_E4M3 ? rs::RC_FP8 : (c->read_copy == REPLAY_MXFP4 ? rs::RC_MXFP4 : rs::RC_NONE);
+    const int rc = rc_kind(c);
     hipError_t e;
     if (c->kind == REPLAY_MAMBA2)
         e = rs::launch_mamba2_step(a, io, rc, (c->flags & REPLAY_FLAG_VALU_FOLD) != 0, (hipStream_t)stream);
@@ -315,6 +319,13 @@ replay_status replay_load_checkpoint(replay_state* st, const float* S, void* str
     s = hip_check(rs::launch_logical_to_tiles(S, at<float>(st, st->lay.ckpt_off), tiles, c->head_dim, c->state_dim, hs),
                   "checkpoint load");
     if (s != REPLAY_OK) return s;
+    if (c->read_copy != REPLAY_NONE) {
+        s = hip_check(rs::launch_quantize_read_copy(at<float>(st, st->lay.ckpt_off), at<uint8_t>(st, st->lay.rcopy_off),
+                                                    st->lay.rscale_bytes ? at<uint8_t>(st, st->lay.rscale_off) : nullptr,
+                                                    tiles, c->head_dim, c->state_dim, rc_kind(c), hs),
+                      "read copy quantize");
+        if (s != REPLAY_OK) return s;
+    }
     return hip_check(rs::launch_book_reset(at<int32_t>(st, st->lay.book_off), at<uint32_t>(st, st->lay.err_off),
                                            c->batch, st->parity, hs),
                      "bookkeeping reset");
@@ -334,10 +345,15 @@ replay_status replay_read_checkpoint(const replay_state* st, float* out, void* s
 replay_status replay_read_copy(const replay_state* st, uint8_t* codes_out, uint8_t* scales_out, void* stream)
 {
     if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
-    (void)codes_out;
-    (void)scales_out;
-    (void)stream;
-    return fail(REPLAY_ERR_STATE, "state has no read copy");
+    const replay_config* c = &st->cfg;
+    if (c->read_copy == REPLAY_NONE) return fail(REPLAY_ERR_STATE, "state has no read copy");
+    if (!codes_out) return fail(REPLAY_ERR_ARG, "codes_out is NULL");
+    if (c->read_copy == REPLAY_MXFP4 && !scales_out) return fail(REPLAY_ERR_ARG, "scales_out is NULL");
+    return hip_check(rs::launch_read_copy_to_logical(at<uint8_t>(st, st->lay.rcopy_off),
+                                                     st->lay.rscale_bytes ? at<uint8_t>(st, st->lay.rscale_off) : nullptr,
+                                                     codes_out, scales_out, c->batch * c->nheads, c->head_dim,
+                                                     c->state_dim, rc_kind(c), (hipStream_t)stream),
+                     "read copy export");
 }
 
 replay_status replay_read_book(const replay_state* st, int32_t* book_out, uint32_t* err_out, void* stream)

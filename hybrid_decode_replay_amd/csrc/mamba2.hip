@@ -30,11 +30,12 @@
 // so a non-flush step has no second barrier.
 #include "common.hpp"
 #include "internal.hpp"
+#include "rc.hpp"
 #include "stage.hpp"
 
 namespace rs {
 
-template <int NB, int IO, int TMAX, bool MFMA_FOLD>
+template <int NB, int IO, int TMAX, bool MFMA_FOLD, int RC>
 __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
 {
     extern __shared__ float lds[];
@@ -82,10 +83,18 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
     stage_issue<IO, R, PRE, true>(stg, tid, nthr, pre, sr);
 
     // ---- 2. checkpoint tile -> registers (one 128-bit load per 16x16 block)
-    float* ckw = a.ckpt + (((size_t)tile * (C >> 4) + (c0 >> 4) + w) * NB * 64 + lane) * 4;
+    // a step that folds nothing reads the low-precision copy when there is one
+    const size_t strip_index = (size_t)tile * (C >> 4) + (c0 >> 4) + w;
+    float* ckw = a.ckpt + (strip_index * NB * 64 + lane) * 4;
     f32x4 s[NB];
+    bool from_copy = false;
+    if constexpr (RC != RC_NONE) from_copy = (f == 0);
+    if (from_copy) {
+        if constexpr (RC != RC_NONE) rc_load<NB, RC>(a.rcopy, a.rscale, strip_index, lane, s);
+    } else {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) s[nb] = ld4_stream(ckw + (size_t)nb * 256);
+        for (int nb = 0; nb < NB; ++nb) s[nb] = ld4_stream(ckw + (size_t)nb * 256);
+    }
 
     // ---- 3. publish the staged rows
     stage_publish<IO, R, PRE>(stg, tid, nthr, pre, sr);
@@ -204,6 +213,7 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
     if (f > 0) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) st4_stream(ckw + (size_t)nb * 256, s[nb]);
+        if constexpr (RC != RC_NONE) rc_store<NB, RC>(a.rcopy, a.rscale, strip_index, lane, s);
     }
 
     // ---- 7. append the unfolded new tokens to the buffer (slot = position - f)
@@ -211,13 +221,13 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
                         tix.sp == 0 && h % a.hpg == 0);
 }
 
-template <int NB, int IO, int TMAX, bool MF>
+template <int NB, int IO, int TMAX, bool MF, int RC>
 static hipError_t launch_nb(const StepArgs& a, hipStream_t s)
 {
     const size_t Tr = a.T > 0 ? a.T : 1;
     const size_t R = NB * 16;
     const size_t lds = sizeof(float) * ((size_t)a.vmax * (a.C / a.nsplit + R + 4) + Tr * R + (size_t)a.vmax);
-    auto k = mamba2_step_kernel<NB, IO, TMAX, MF>;
+    auto k = mamba2_step_kernel<NB, IO, TMAX, MF, RC>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -226,31 +236,40 @@ static hipError_t launch_nb(const StepArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int IO, int TMAX, bool MF>
+template <int IO, int TMAX, bool MF, int RC>
 static hipError_t launch_io(const StepArgs& a, hipStream_t s)
 {
     switch (a.R) {
-        case 16: return launch_nb<1, IO, TMAX, MF>(a, s);
-        case 32: return launch_nb<2, IO, TMAX, MF>(a, s);
-        case 64: return launch_nb<4, IO, TMAX, MF>(a, s);
-        case 128: return launch_nb<8, IO, TMAX, MF>(a, s);
-        case 256: return launch_nb<16, IO, TMAX, MF>(a, s);
+        case 16:
+            if constexpr (RC != RC_MXFP4) return launch_nb<1, IO, TMAX, MF, RC>(a, s);
+            return hipErrorInvalidValue;     // MXFP4 groups need 32 rows
+        case 32: return launch_nb<2, IO, TMAX, MF, RC>(a, s);
+        case 64: return launch_nb<4, IO, TMAX, MF, RC>(a, s);
+        case 128: return launch_nb<8, IO, TMAX, MF, RC>(a, s);
+        case 256: return launch_nb<16, IO, TMAX, MF, RC>(a, s);
     }
     return hipErrorInvalidValue;
 }
 
-template <int TMAX, bool MF>
+template <int TMAX, bool MF, int RC>
 static hipError_t launch_t(const StepArgs& a, int io, hipStream_t s)
 {
-    return io == IO_BF16 ? launch_io<IO_BF16, TMAX, MF>(a, s) : launch_io<IO_F32, TMAX, MF>(a, s);
+    return io == IO_BF16 ? launch_io<IO_BF16, TMAX, MF, RC>(a, s) : launch_io<IO_F32, TMAX, MF, RC>(a, s);
+}
+
+template <int TMAX>
+static hipError_t launch_tm(const StepArgs& a, int io, int rc, bool valu_fold, hipStream_t s)
+{
+    if (rc == RC_FP8) return launch_t<TMAX, true, RC_FP8>(a, io, s);
+    if (rc == RC_MXFP4) return launch_t<TMAX, true, RC_MXFP4>(a, io, s);
+    return valu_fold ? launch_t<TMAX, false, RC_NONE>(a, io, s) : launch_t<TMAX, true, RC_NONE>(a, io, s);
 }
 
 hipError_t launch_mamba2_step(const StepArgs& a, int io, int rc, bool valu_fold, hipStream_t s)
 {
-    if (rc != RC_NONE) return hipErrorNotSupported;
-    if (a.T <= 1) return valu_fold ? launch_t<1, false>(a, io, s) : launch_t<1, true>(a, io, s);
-    if (a.T <= 4) return valu_fold ? launch_t<4, false>(a, io, s) : launch_t<4, true>(a, io, s);
-    return valu_fold ? launch_t<16, false>(a, io, s) : launch_t<16, true>(a, io, s);
+    if (a.T <= 1) return launch_tm<1>(a, io, rc, valu_fold, s);
+    if (a.T <= 4) return launch_tm<4>(a, io, rc, valu_fold, s);
+    return launch_tm<16>(a, io, rc, valu_fold, s);
 }
 
 }  // namespace rs

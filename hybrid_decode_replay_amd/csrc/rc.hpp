@@ -1,0 +1,237 @@
+// rc.hpp -- the low-precision read copy of the checkpoint.
+//
+// The recurrence keeps its fp32 checkpoint; a copy in FP8 E4M3 or MXFP4 (E2M1
+// elements, one E8M0 scale per 32 elements along the reduction axis) serves
+// the reads of non-flush steps, and is refreshed whenever the checkpoint is
+// written.  The fold never reads it, so its rounding error never enters the
+// recurrence ([TR] "NVIDIA ve Dao AI Lab ...", section "Kuantizasyon
+// hatasinin sinirlandirilmasi").  Formats: OCP Microscaling v1.0.
+//
+// Layout, per (tile, 16-column strip), in the lane order of the fp32
+// fragment tiles (common.hpp): lane l holds, per 16x16 block nb, the four
+// values of rows 4*(l/16)..+3 of column l%16.
+//   FP8    4*NB bytes per lane; byte (nb%4)*4 + r of 16-byte chunk nb/4,
+//          chunks stored [chunk][lane][16 B] (narrower tiles: [lane][4*NB B]).
+//   MXFP4  2*NB bytes per lane; nibble (nb%8)*4 + r of 16-byte chunk nb/8,
+//          low nibble first, chunks [chunk][lane][16 B] (narrower: [lane][2*NB B]).
+//          The 32-element groups are block pairs (2s, 2s+1) of one column: the
+//          8 values of each of the four lanes l%16 + 16*q.  Scales: byte
+//          [tile][strip][l%16][s].
+// Quantization rounds to nearest, ties to the even code, and saturates
+// (FP8 at +-448, E2M1 at 6); the shared exponent is floor(log2(amax)) - 2,
+// clamped to [-127, 127], and an all-zero group uses -127.
+#pragma once
+#include "common.hpp"
+
+namespace rs {
+
+// ---- FP8 E4M3 ------------------------------------------------------------
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x)
+{
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t au = u & 0x7fffffffu;
+    if (au > 0x7f800000u) return 0x7fu;                         // NaN
+    const float a = __builtin_bit_cast(float, au);
+    if (a >= 448.f) return sign | 0x7eu;                         // saturate (incl. inf)
+    if (a < 0.015625f) {                                         // below 2^-6: steps of 2^-9
+        return sign | (uint32_t)__builtin_rintf(a * 512.f);      // 8 lands on code 0x08 = 2^-6
+    }
+    int e = (int)(au >> 23) - 127;                               // -6 .. 8
+    uint32_t m = (au >> 20) & 7u;
+    const uint32_t rem = au & 0xfffffu;
+    if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) ++m;   // round to nearest even
+    if (m == 8u) { m = 0; ++e; }
+    return sign | ((uint32_t)(e + 7) << 3) | m;
+}
+
+// ---- FP4 E2M1 and the E8M0 shared exponent --------------------------------
+// Code of v / 2^X (the caller passes the scaled value).
+__device__ __forceinline__ uint32_t f32_to_e2m1(float v)
+{
+    const uint32_t sign = (__builtin_bit_cast(uint32_t, v) >> 28) & 8u;
+    const float a = __builtin_fabsf(v);
+    // nearest of {0, .5, 1, 1.5, 2, 3, 4, 6}; ties go to the even code
+    const uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.f);
+    return sign | c;
+}
+
+// Shared exponent X of a group with largest magnitude amax.
+__device__ __forceinline__ int mx_exponent(float amax)
+{
+    const uint32_t ebits = (__builtin_bit_cast(uint32_t, amax) >> 23) & 0xffu;
+    if (ebits == 0) return -127;                                 // zero or subnormal amax
+    const int X = (int)ebits - 127 - 2;
+    return X < -127 ? -127 : (X > 127 ? 127 : X);
+}
+
+__device__ __forceinline__ float exp2i(int e)                   // 2^e for e in [-126, 127] (normal floats)
+{
+    return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
+}
+
+__device__ __forceinline__ float e8m0_to_f32(uint32_t code)
+{
+    return code == 0 ? __builtin_bit_cast(float, 0x00400000u) : __builtin_bit_cast(float, code << 23);
+}
+
+// ---- tile addressing --------------------------------------------------------
+template <int NB>
+struct RcLayout {
+    static constexpr int FP8_BYTES = 4 * NB;     // per lane per strip
+    static constexpr int FP4_BYTES = 2 * NB;
+};
+
+// byte offset of lane `lane`'s data for chunk q of (tile, strip)
+template <int BYTES_PER_LANE>
+__device__ __forceinline__ size_t rc_offset(size_t strip_index, int q, int lane)
+{
+    if constexpr (BYTES_PER_LANE >= 16)
+        return strip_index * (64 * BYTES_PER_LANE) + (size_t)q * 1024 + (size_t)lane * 16;
+    else
+        return strip_index * (64 * BYTES_PER_LANE) + (size_t)lane * BYTES_PER_LANE;
+}
+
+// ---- FP8: load + dequantize, quantize + store ---------------------------------
+template <int NB>
+__device__ __forceinline__ void rc_fp8_load(const uint8_t* base, size_t strip_index, int lane, f32x4 (&s)[NB])
+{
+    constexpr int BPL = 4 * NB;
+    if constexpr (BPL >= 16) {
+#pragma unroll
+        for (int q = 0; q < NB / 4; ++q) {
+            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + rc_offset<BPL>(strip_index, q, lane)));
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], false);
+                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], true);
+                s[q * 4 + k] = f32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
+        }
+    } else {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(base + rc_offset<BPL>(strip_index, 0, lane) + 4 * nb);
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+            s[nb] = f32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+    }
+}
+
+__device__ __forceinline__ uint32_t pack_e4m3(f32x4 v)
+{
+    return f32_to_e4m3(v.x) | (f32_to_e4m3(v.y) << 8) | (f32_to_e4m3(v.z) << 16) | (f32_to_e4m3(v.w) << 24);
+}
+
+template <int NB>
+__device__ __forceinline__ void rc_fp8_store(uint8_t* base, size_t strip_index, int lane, const f32x4 (&s)[NB])
+{
+    constexpr int BPL = 4 * NB;
+    if constexpr (BPL >= 16) {
+#pragma unroll
+        for (int q = 0; q < NB / 4; ++q) {
+            const u32x4 v = {pack_e4m3(s[q * 4]), pack_e4m3(s[q * 4 + 1]), pack_e4m3(s[q * 4 + 2]), pack_e4m3(s[q * 4 + 3])};
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(base + rc_offset<BPL>(strip_index, q, lane)));
+        }
+    } else {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            *reinterpret_cast<uint32_t*>(base + rc_offset<BPL>(strip_index, 0, lane) + 4 * nb) = pack_e4m3(s[nb]);
+    }
+}
+
+// ---- MXFP4: load + dequantize, quantize + store --------------------------------
+template <int NB>
+__device__ __forceinline__ void rc_fp4_load(const uint8_t* codes, const uint8_t* scales, size_t strip_index, int lane,
+                                            f32x4 (&s)[NB])
+{
+    static_assert(NB % 2 == 0, "MXFP4 groups need block pairs");
+    constexpr int BPL = 2 * NB;
+    constexpr int NP = NB / 2;                       // groups (block pairs) per lane
+    uint32_t w[NP];
+    if constexpr (BPL >= 16) {
+#pragma unroll
+        for (int q = 0; q < NB / 8; ++q) {
+            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + rc_offset<BPL>(strip_index, q, lane)));
+            w[q * 4] = v.x; w[q * 4 + 1] = v.y; w[q * 4 + 2] = v.z; w[q * 4 + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+            w[p] = *reinterpret_cast<const uint32_t*>(codes + rc_offset<BPL>(strip_index, 0, lane) + 4 * p);
+    }
+    const uint8_t* sc = scales + (strip_index * 16 + (lane & 15)) * NP;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const float scale = e8m0_to_f32(sc[p]);
+        const auto b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[p], scale, 0);
+        const auto b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[p], scale, 1);
+        const auto b2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[p], scale, 2);
+        const auto b3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[p], scale, 3);
+        s[2 * p] = f32x4{b0[0], b0[1], b1[0], b1[1]};
+        s[2 * p + 1] = f32x4{b2[0], b2[1], b3[0], b3[1]};
+    }
+}
+
+template <int NB>
+__device__ __forceinline__ void rc_fp4_store(uint8_t* codes, uint8_t* scales, size_t strip_index, int lane,
+                                             const f32x4 (&s)[NB])
+{
+    static_assert(NB % 2 == 0, "MXFP4 groups need block pairs");
+    constexpr int BPL = 2 * NB;
+    constexpr int NP = NB / 2;
+    uint32_t w[NP];
+    uint32_t scw[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const f32x4 a = s[2 * p], b = s[2 * p + 1];
+        float am = fmaxf(fmaxf(fmaxf(__builtin_fabsf(a.x), __builtin_fabsf(a.y)), fmaxf(__builtin_fabsf(a.z), __builtin_fabsf(a.w))),
+                         fmaxf(fmaxf(__builtin_fabsf(b.x), __builtin_fabsf(b.y)), fmaxf(__builtin_fabsf(b.z), __builtin_fabsf(b.w))));
+        am = fmaxf(am, __shfl_xor(am, 16, 64));      // the group spans lanes l%16 + 16*q
+        am = fmaxf(am, __shfl_xor(am, 32, 64));
+        const int X = mx_exponent(am);
+        const float inv = exp2i(-X);                 // X <= 125 for finite amax, so -X >= -125
+        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        uint32_t word = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) word |= f32_to_e2m1(v[k] * inv) << (4 * k);
+        w[p] = word;
+        scw[p] = (uint32_t)(X + 127);
+    }
+    if constexpr (BPL >= 16) {
+#pragma unroll
+        for (int q = 0; q < NB / 8; ++q) {
+            const u32x4 v = {w[q * 4], w[q * 4 + 1], w[q * 4 + 2], w[q * 4 + 3]};
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(codes + rc_offset<BPL>(strip_index, q, lane)));
+        }
+    } else {
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+            *reinterpret_cast<uint32_t*>(codes + rc_offset<BPL>(strip_index, 0, lane) + 4 * p) = w[p];
+    }
+    if (lane < 16) {
+        uint8_t* sc = scales + (strip_index * 16 + lane) * NP;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) sc[p] = (uint8_t)scw[p];
+    }
+}
+
+// Refresh the read copy of one strip from its fp32 registers.
+template <int NB, int RC>
+__device__ __forceinline__ void rc_store(uint8_t* codes, uint8_t* scales, size_t strip_index, int lane, const f32x4 (&s)[NB])
+{
+    if constexpr (RC == RC_FP8) rc_fp8_store<NB>(codes, strip_index, lane, s);
+    else if constexpr (RC == RC_MXFP4) rc_fp4_store<NB>(codes, scales, strip_index, lane, s);
+}
+
+template <int NB, int RC>
+__device__ __forceinline__ void rc_load(const uint8_t* codes, const uint8_t* scales, size_t strip_index, int lane,
+                                        f32x4 (&s)[NB])
+{
+    if constexpr (RC == RC_FP8) rc_fp8_load<NB>(codes, strip_index, lane, s);
+    else if constexpr (RC == RC_MXFP4) rc_fp4_load<NB>(codes, scales, strip_index, lane, s);
+}
+
+}  // namespace rs

@@ -1,0 +1,186 @@
+"""GPU tests of the low-precision read copy (FP8 E4M3 and MXFP4) of the checkpoint.
+
+The pages keep a high-precision checkpoint for the recurrence and serve reads
+from a low-precision copy, so read error never enters the recurrence ([TR]
+"NVIDIA ve Dao AI Lab ...", section "Kuantizasyon hatasinin sinirlandirilmasi").
+Checked here:
+  * quantizer: the copy made from a loaded seeded fp32 checkpoint equals the
+    oracle's OCP quantization of the same values, bit for bit (codes and scales);
+  * read path: outputs of non-flush steps equal the oracle's evaluation of the
+    dequantized copy plus the buffered tokens (1e-4); flush steps are full
+    precision;
+  * invariant after flushes: the copy is the quantization of the new fp32
+    checkpoint (a property of the state, checked on the GPU's own checkpoint);
+  * non-propagation: the fp32 checkpoints are bitwise identical with and
+    without a read copy.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from hybrid_decode_replay_amd import synth  # noqa: E402
+
+FORMATS = ["fp8", "mxfp4"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from hybrid_decode_replay_amd import binding  # noqa: F401
+    yield
+
+
+def rb():
+    from hybrid_decode_replay_amd import binding
+    return binding
+
+
+def rc_code(fmt):
+    b = rb()
+    return {"fp8": b.FP8_E4M3, "mxfp4": b.MXFP4}[fmt]
+
+
+def planted_checkpoint(seed, shape):
+    """N(0, 0.1) values with planted edge cases: FP8 midpoints and saturation, values below
+    the FP8 subnormal step, zeros and negative zeros, an all-zero 32-group, E2M1 ties at a
+    power-of-two group maximum, and a tiny group."""
+    S = synth.checkpoint(seed, shape).copy()
+    flat = S.reshape(-1, shape[-1])
+    rng = np.random.default_rng(seed)
+    rows = rng.choice(flat.shape[0], size=min(8, flat.shape[0]), replace=False)
+    r0 = flat[rows[0]]
+    r0[:8] = [448.0, 464.0, -500.0, 0.5 * (1.0 + 1.125), 2.0 ** -10, -(2.0 ** -10) * 3, 0.0, -0.0]
+    flat[rows[1]][:32] = 0.0                                         # all-zero MX group
+    flat[rows[2]][:32] = [4.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0] * 4   # E2M1 ties, amax 4 -> X = 0
+    flat[rows[3]][:32] = 1e-30 * rng.standard_normal(32)            # tiny group
+    return S.astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("kind,C,R", [("mamba2", 64, 128), ("mamba2", 32, 32), ("gdn", 128, 128), ("gdn", 16, 256),
+                                      ("mamba2", 48, 64)])
+def test_quantizer_bit_exact_at_load(fmt, kind, C, R):
+    from oracle import replay_oracle as ro
+    b = rb()
+    B, H = 3, 2
+    cfg = b.make_config(b.MAMBA2 if kind == "mamba2" else b.GDN, B, H, H, C, R, 16, b.F32, read_copy=rc_code(fmt))
+    st = b.ReplayState(cfg)
+    S0 = planted_checkpoint(40 + C + R, (B, H, C, R))
+    st.load_checkpoint(torch.from_numpy(S0).cuda())
+    codes, scales = st.read_copy()
+    torch.cuda.synchronize()
+    codes = codes.cpu().numpy()
+    if fmt == "fp8":
+        want = ro.e4m3_encode(S0.astype(np.float64)).reshape(S0.shape)
+        np.testing.assert_array_equal(codes, want)
+    else:
+        wc, ws = ro.mxfp4_quantize(S0.astype(np.float64))
+        np.testing.assert_array_equal(codes, wc)
+        np.testing.assert_array_equal(scales.cpu().numpy(), ws)
+
+
+def _pair(kind, fmt, B, H, C, R, cap, seed, io=None):
+    from harness import Pair
+    b = rb()
+    S0 = synth.checkpoint(seed, (B, H, C, R))
+    return Pair(b.MAMBA2 if kind == "mamba2" else b.GDN, B, H, H, C, R, cap=cap, io=io or b.F32, seed=seed, S0=S0,
+                read_copy=rc_code(fmt))
+
+
+def _tokens(kind, seed, T, B, H, C, R, io="f32"):
+    if kind == "mamba2":
+        return synth.mamba2_tokens(seed, T, B, H, H, C, R, dtype=io)
+    return synth.gdn_tokens(seed, T, B, H, H, R, C, dtype=io)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_read_path_outputs_per_window(fmt, kind):
+    """Each window starts from a freshly loaded seeded checkpoint, so both sides quantize the
+    same fp32 values; non-flush outputs come from the copy, the flush step from fp32."""
+    B, H, C, R, cap = 3, 2, 64, 64, 8
+    pair = _pair(kind, fmt, B, H, C, R, cap, seed=50)
+    toks = _tokens(kind, 50, 3 * cap, B, H, C, R)
+    for w in range(3):
+        S = synth.checkpoint(60 + w, (B, H, C, R))
+        pair.st.load_checkpoint(torch.from_numpy(S).cuda())
+        pair.orc.load(S)
+        for t in range(cap):
+            pair.decode(synth.token(toks, w * cap + t), what=f"window {w} step {t}")
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_copy_tracks_checkpoint_and_never_feeds_the_recurrence(fmt, kind):
+    from oracle import replay_oracle as ro
+    b = rb()
+    B, H, C, R, cap, T = 2, 2, 32, 64, 4, 14
+    kk = b.MAMBA2 if kind == "mamba2" else b.GDN
+    S0 = synth.checkpoint(70, (B, H, C, R))
+    states = {}
+    for name, rc in (("plain", b.NONE), ("copy", rc_code(fmt))):
+        st = b.ReplayState(b.make_config(kk, B, H, H, C, R, cap, b.F32, read_copy=rc))
+        st.load_checkpoint(torch.from_numpy(S0).cuda())
+        states[name] = st
+    toks = _tokens(kind, 70, T, B, H, C, R)
+    params = {}
+    if kind == "mamba2":
+        A, D = synth.mamba2_params(70, H)
+        params = {"A": torch.from_numpy(A).cuda(), "D": torch.from_numpy(D).cuda()}
+    for t in range(T):
+        tok = {k: torch.from_numpy(v[t]).cuda() for k, v in toks.items()}
+        for st in states.values():
+            st.decode(tok, params)
+        ck_plain = states["plain"].read_checkpoint()
+        ck_copy = states["copy"].read_checkpoint()
+        torch.cuda.synchronize()
+        assert torch.equal(ck_plain, ck_copy), f"step {t}: the read copy changed the recurrence"
+        codes, scales = states["copy"].read_copy()
+        torch.cuda.synchronize()
+        ck = ck_copy.cpu().numpy().astype(np.float64)
+        if fmt == "fp8":
+            np.testing.assert_array_equal(codes.cpu().numpy(), ro.e4m3_encode(ck).reshape(ck.shape))
+        else:
+            wc, ws = ro.mxfp4_quantize(ck)
+            np.testing.assert_array_equal(codes.cpu().numpy(), wc)
+            np.testing.assert_array_equal(scales.cpu().numpy(), ws)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_spec_with_read_copy(fmt, kind):
+    B, H, C, R, cap = 3, 2, 32, 32, 8
+    pair = _pair(kind, fmt, B, H, C, R, cap, seed=80)
+    toks = _tokens(kind, 80, 40, B, H, C, R)
+    pair.decode(synth.token(toks, 0))
+    pair.decode(synth.token(toks, 1))
+    pair.spec({n: v[2:5] for n, v in toks.items()}, what="spec without pre-flush (copy reads)")
+    pair.commit([3, 1, 0])
+    pair.spec({n: v[5:11] for n, v in toks.items()}, what="spec with pre-flush for some rows")
+
+
+def test_bf16_io_with_mxfp4_copy_full_size_sample():
+    """The batch-128 GDN layer (32 heads, d = 128) with an MXFP4 copy: first window parity on
+    sampled sequences (copy read path, bf16 inputs and outputs)."""
+    from oracle import replay_oracle as ro
+    b = rb()
+    B, H, D, T = 128, 32, 128, 15
+    cfg = b.make_config(b.GDN, B, H, H, D, D, 16, b.BF16, read_copy=b.MXFP4)
+    st = b.ReplayState(cfg)
+    S0 = synth.checkpoint_device(4, (B, H, D, D), "cuda")
+    st.load_checkpoint(S0)
+    toks = synth.gdn_tokens_device(4, T, B, H, H, D, D, "cuda")
+    ys = torch.empty((T, B, H, D), dtype=torch.bfloat16, device="cuda")
+    for t in range(T):
+        st.decode({k: v[t:t + 1] for k, v in toks.items()}, y=ys[t:t + 1])
+    torch.cuda.synchronize()
+    sample = [0, 77]
+    sess = ro.GDNSession(S0[sample].cpu().numpy(), read_copy="mxfp4")
+    host = {k: v[:, sample].float().cpu().numpy() for k, v in toks.items()}
+    yg = ys[:, sample].float().cpu().numpy()
+    for t in range(T):
+        err = ro.normwise_error(yg[t], sess.decode(synth.token(host, t)))
+        assert err <= 2e-2, (t, err)
