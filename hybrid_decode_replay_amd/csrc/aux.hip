@@ -116,8 +116,8 @@ hipError_t launch_logical_to_tiles(const float* in, float* ckpt, int tiles, int 
 // One wave per (tile, 16-column strip), in the same lane order as the replay
 // kernels, so the quantizer is the one the flush path uses.
 template <int NB, int RC>
-__global__ __launch_bounds__(256) void quantize_rc_kernel(const float* ckpt, uint8_t* codes, uint8_t* scales,
-                                                          size_t nstrips)
+__global__ __launch_bounds__(256) void quantize_rc_kernel(float* ckpt, uint8_t* codes, uint8_t* scales,
+                                                          size_t nstrips, int round_ckpt)
 {
     const size_t strip = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -126,6 +126,11 @@ __global__ __launch_bounds__(256) void quantize_rc_kernel(const float* ckpt, uin
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) s[nb] = ld4(ckpt + ((strip * NB + nb) * 64 + lane) * 4);
     rc_store<NB, RC>(codes, scales, strip, lane, s);
+    if (round_ckpt) {                              // checkpoint kept at the copy's precision
+        rc_roundtrip<NB, RC>(s);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) st4(ckpt + ((strip * NB + nb) * 64 + lane) * 4, s[nb]);
+    }
 }
 
 // Raw codes to logical order: codes_out [tiles][C][R] (one code per byte),
@@ -170,21 +175,23 @@ __global__ __launch_bounds__(256) void rc_to_logical_kernel(const uint8_t* codes
 }
 
 template <int RC>
-static hipError_t rc_dispatch(bool quantize, const float* ckpt, const uint8_t* codes_in, const uint8_t* scales_in,
-                              uint8_t* codes, uint8_t* scales, int tiles, int C, int R, hipStream_t s)
+static hipError_t rc_dispatch(bool quantize, float* ckpt, const uint8_t* codes_in, const uint8_t* scales_in,
+                              uint8_t* codes, uint8_t* scales, int tiles, int C, int R, int round_ckpt, hipStream_t s)
 {
     const size_t nstrips = (size_t)tiles * (C / 16);
     const dim3 grid((unsigned)((nstrips + 3) / 4)), block(256);
 #define RS_RC_CASE(NBV)                                                                                  \
     case NBV * 16:                                                                                       \
-        if (quantize) hipLaunchKernelGGL((quantize_rc_kernel<NBV, RC>), grid, block, 0, s, ckpt, codes, scales, nstrips); \
+        if (quantize) hipLaunchKernelGGL((quantize_rc_kernel<NBV, RC>), grid, block, 0, s, ckpt, codes, scales, nstrips, \
+                                         round_ckpt);                                                   \
         else hipLaunchKernelGGL((rc_to_logical_kernel<NBV, RC>), grid, block, 0, s, codes_in, scales_in, codes, scales,    \
                                 nstrips, C);                                                             \
         return hipGetLastError();
     switch (R) {
         case 16:
             if constexpr (RC == RC_FP8) {
-                if (quantize) hipLaunchKernelGGL((quantize_rc_kernel<1, RC>), grid, block, 0, s, ckpt, codes, scales, nstrips);
+                if (quantize) hipLaunchKernelGGL((quantize_rc_kernel<1, RC>), grid, block, 0, s, ckpt, codes, scales, nstrips,
+                                                 round_ckpt);
                 else hipLaunchKernelGGL((rc_to_logical_kernel<1, RC>), grid, block, 0, s, codes_in, scales_in, codes, scales,
                                         nstrips, C);
                 return hipGetLastError();
@@ -199,19 +206,19 @@ static hipError_t rc_dispatch(bool quantize, const float* ckpt, const uint8_t* c
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_quantize_read_copy(const float* ckpt, uint8_t* codes, uint8_t* scales, int tiles, int C, int R, int rc,
-                                     hipStream_t s)
+hipError_t launch_quantize_read_copy(float* ckpt, uint8_t* codes, uint8_t* scales, int tiles, int C, int R, int rc,
+                                     bool round_ckpt, hipStream_t s)
 {
-    if (rc == RC_FP8) return rc_dispatch<RC_FP8>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, s);
-    if (rc == RC_MXFP4) return rc_dispatch<RC_MXFP4>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, s);
+    if (rc == RC_FP8) return rc_dispatch<RC_FP8>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, round_ckpt, s);
+    if (rc == RC_MXFP4) return rc_dispatch<RC_MXFP4>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, round_ckpt, s);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_read_copy_to_logical(const uint8_t* codes, const uint8_t* scales, uint8_t* codes_out,
                                        uint8_t* scales_out, int tiles, int C, int R, int rc, hipStream_t s)
 {
-    if (rc == RC_FP8) return rc_dispatch<RC_FP8>(false, nullptr, codes, scales, codes_out, scales_out, tiles, C, R, s);
-    if (rc == RC_MXFP4) return rc_dispatch<RC_MXFP4>(false, nullptr, codes, scales, codes_out, scales_out, tiles, C, R, s);
+    if (rc == RC_FP8) return rc_dispatch<RC_FP8>(false, nullptr, codes, scales, codes_out, scales_out, tiles, C, R, 0, s);
+    if (rc == RC_MXFP4) return rc_dispatch<RC_MXFP4>(false, nullptr, codes, scales, codes_out, scales_out, tiles, C, R, 0, s);
     return hipErrorInvalidValue;
 }
 

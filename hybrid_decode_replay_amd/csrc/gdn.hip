@@ -197,6 +197,11 @@ __global__ __launch_bounds__(1024) void gdn_step_kernel(StepArgs a)
         }
     }
 
+    // a checkpoint kept at the copy's precision is rounded as soon as it is folded
+    if constexpr (RC != RC_NONE) {
+        if (a.qckpt && f > 0) rc_roundtrip<NB, RC>(s);
+    }
+
     // ---- 4. adjoint chains, one per new token (spread over the waves)
     if (a.mode != MODE_FLUSH) {
         for (int t = w; t < T; t += waves) {

@@ -81,7 +81,10 @@ replay_status check_config(const replay_config* c)
         return fail(REPLAY_ERR_DTYPE, "read_copy must be NONE, FP8_E4M3 or MXFP4");
     if (c->read_copy == REPLAY_MXFP4 && R % 32 != 0)
         return fail(REPLAY_ERR_SHAPE, "MXFP4 read copy needs state_dim divisible by 32");
-    if (c->flags & ~REPLAY_FLAG_VALU_FOLD) return fail(REPLAY_ERR_ARG, "unknown flags 0x%x", c->flags);
+    if (c->flags & ~(REPLAY_FLAG_VALU_FOLD | REPLAY_FLAG_QUANTIZED_CKPT))
+        return fail(REPLAY_ERR_ARG, "unknown flags 0x%x", c->flags);
+    if ((c->flags & REPLAY_FLAG_QUANTIZED_CKPT) && c->read_copy == REPLAY_NONE)
+        return fail(REPLAY_ERR_ARG, "REPLAY_FLAG_QUANTIZED_CKPT needs a read_copy format");
     return ok();
 }
 
@@ -181,6 +184,7 @@ rs::StepArgs step_args(const replay_state* st, const replay_inputs* in, void* y,
     for (int d = 4; d >= 1; --d)
         if (strips % d == 0) { wpg = d; break; }
     a.nsplit = strips / wpg;
+    a.qckpt = (c->flags & REPLAY_FLAG_QUANTIZED_CKPT) ? 1 : 0;
     const replay_layout& L = st->lay;
     a.ckpt = at<float>(st, L.ckpt_off);
     a.rcopy = L.rcopy_bytes ? at<uint8_t>(st, L.rcopy_off) : nullptr;
@@ -322,7 +326,8 @@ replay_status replay_load_checkpoint(replay_state* st, const float* S, void* str
     if (c->read_copy != REPLAY_NONE) {
         s = hip_check(rs::launch_quantize_read_copy(at<float>(st, st->lay.ckpt_off), at<uint8_t>(st, st->lay.rcopy_off),
                                                     st->lay.rscale_bytes ? at<uint8_t>(st, st->lay.rscale_off) : nullptr,
-                                                    tiles, c->head_dim, c->state_dim, rc_kind(c), hs),
+                                                    tiles, c->head_dim, c->state_dim, rc_kind(c),
+                                                    (c->flags & REPLAY_FLAG_QUANTIZED_CKPT) != 0, hs),
                       "read copy quantize");
         if (s != REPLAY_OK) return s;
     }

@@ -26,6 +26,7 @@ struct StepArgs {
     int T;                   // new tokens: 1 (decode), k (spec), 0 (flush)
     int vmax;                // LDS rows reserved for the virtual entry list
     int nsplit;              // workgroups per (b, h) tile, along the output axis
+    int qckpt;               // nonzero: the checkpoint itself is kept at the copy's precision
     float scale;             // GDN output scale
     float* ckpt;             // fragment-ordered fp32 tiles
     uint8_t* rcopy;          // read-copy codes (or null)
@@ -59,8 +60,8 @@ hipError_t launch_book_reset(int32_t* book, uint32_t* err, int B, int parity, hi
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_tiles_to_logical(const float* ckpt, float* out, int tiles, int C, int R, hipStream_t s);
 hipError_t launch_logical_to_tiles(const float* in, float* ckpt, int tiles, int C, int R, hipStream_t s);
-hipError_t launch_quantize_read_copy(const float* ckpt, uint8_t* codes, uint8_t* scales, int tiles,
-                                     int C, int R, int rc, hipStream_t s);
+hipError_t launch_quantize_read_copy(float* ckpt, uint8_t* codes, uint8_t* scales, int tiles,
+                                     int C, int R, int rc, bool round_ckpt, hipStream_t s);
 hipError_t launch_read_copy_to_logical(const uint8_t* codes, const uint8_t* scales, uint8_t* codes_out,
                                        uint8_t* scales_out, int tiles, int C, int R, int rc, hipStream_t s);
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t s);

@@ -160,6 +160,11 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
         }
     }
 
+    // a checkpoint kept at the copy's precision is rounded as soon as it is folded
+    if constexpr (RC != RC_NONE) {
+        if (a.qckpt && f > 0) rc_roundtrip<NB, RC>(s);
+    }
+
     // ---- 5. outputs of the new tokens
     if (a.mode != MODE_FLUSH) {
         const float Dh = a.D[h];

@@ -218,6 +218,54 @@ __device__ __forceinline__ void rc_fp4_store(uint8_t* codes, uint8_t* scales, si
     }
 }
 
+// Round a strip's registers to the copy's grid (quantize, then dequantize),
+// used when the checkpoint itself is kept at the copy's precision.
+template <int NB>
+__device__ __forceinline__ void rc_fp8_roundtrip(f32x4 (&s)[NB])
+{
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const uint32_t w = pack_e4m3(s[nb]);
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+        s[nb] = f32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+}
+
+template <int NB>
+__device__ __forceinline__ void rc_fp4_roundtrip(f32x4 (&s)[NB])
+{
+    static_assert(NB % 2 == 0, "MXFP4 groups need block pairs");
+#pragma unroll
+    for (int p = 0; p < NB / 2; ++p) {
+        const f32x4 a = s[2 * p], b = s[2 * p + 1];
+        float am = fmaxf(fmaxf(fmaxf(__builtin_fabsf(a.x), __builtin_fabsf(a.y)), fmaxf(__builtin_fabsf(a.z), __builtin_fabsf(a.w))),
+                         fmaxf(fmaxf(__builtin_fabsf(b.x), __builtin_fabsf(b.y)), fmaxf(__builtin_fabsf(b.z), __builtin_fabsf(b.w))));
+        am = fmaxf(am, __shfl_xor(am, 16, 64));
+        am = fmaxf(am, __shfl_xor(am, 32, 64));
+        const int X = mx_exponent(am);
+        const float inv = exp2i(-X);
+        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        uint32_t word = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) word |= f32_to_e2m1(v[k] * inv) << (4 * k);
+        const float scale = e8m0_to_f32((uint32_t)(X + 127));
+        const auto b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, scale, 0);
+        const auto b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, scale, 1);
+        const auto b2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, scale, 2);
+        const auto b3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, scale, 3);
+        s[2 * p] = f32x4{b0[0], b0[1], b1[0], b1[1]};
+        s[2 * p + 1] = f32x4{b2[0], b2[1], b3[0], b3[1]};
+    }
+}
+
+template <int NB, int RC>
+__device__ __forceinline__ void rc_roundtrip(f32x4 (&s)[NB])
+{
+    if constexpr (RC == RC_FP8) rc_fp8_roundtrip<NB>(s);
+    else if constexpr (RC == RC_MXFP4) rc_fp4_roundtrip<NB>(s);
+}
+
 // Refresh the read copy of one strip from its fp32 registers.
 template <int NB, int RC>
 __device__ __forceinline__ void rc_store(uint8_t* codes, uint8_t* scales, size_t strip_index, int lane, const f32x4 (&s)[NB])

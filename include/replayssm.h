@@ -93,6 +93,11 @@ typedef enum {
 
 /* Configuration flags. */
 #define REPLAY_FLAG_VALU_FOLD 0x1   /* fold with vector FMAs instead of MFMA (cross-check) */
+/* Keep the checkpoint itself at the read copy's precision (comparison variant:
+ * a low-precision state inside the recurrence).  Needs read_copy != NONE.  The
+ * checkpoint is rounded to the copy's grid at load and right after every fold
+ * (before that step's outputs); the fp32 region then mirrors the copy exactly. */
+#define REPLAY_FLAG_QUANTIZED_CKPT 0x2
 
 typedef struct {
     int32_t abi_version;  /* REPLAY_ABI_VERSION                                  */

@@ -50,6 +50,12 @@ reads).  With a read copy, a step that performs no flush produces its output
 from the dequantized copy of the checkpoint followed by the committed tokens
 since the last flush; a step that flushes produces it from the full-precision
 state.  The copy is the quantization of the checkpoint image rounded to fp32.
+
+Quantized checkpoint (the comparison variant the same section contrasts with:
+a low-precision state inside the recurrence).  The checkpoint is rounded to the
+copy's grid at load and at every flush, and the recurrence continues from the
+rounded state; the output of a step whose own token was folded is read from
+the rounded state.
 """
 from __future__ import annotations
 
@@ -249,18 +255,21 @@ class _Session:
 
     kind = None
 
-    def __init__(self, batch, cap, S0, read_copy=None):
+    def __init__(self, batch, cap, S0, read_copy=None, quantized_ckpt=False):
         if not 1 <= cap <= 16:
             raise ValueError("buffer capacity must be in [1, 16]")
+        if quantized_ckpt and read_copy is None:
+            raise ValueError("a quantized checkpoint needs a format")
         self.B = batch
         self.cap = cap
-        self.S = np.array(S0, np.float64, copy=True)          # committed state
+        self.read_copy = read_copy
+        self.quantized_ckpt = quantized_ckpt
+        self.S = self._round(np.array(S0, np.float64, copy=True))   # committed state
         self.ckpt = self.S.copy()                              # image at last flush
         self.len = np.zeros(batch, np.int32)
         self.pend = np.zeros(batch, np.int32)
         self.fc = np.zeros(batch, np.int32)
         self.err = 0
-        self.read_copy = read_copy
         self.hist = [[] for _ in range(batch)]                 # committed tokens since flush
         self._drafts = None                                    # list of per-draft inputs
         self.flush_events = []                                 # (op index, b) pairs
@@ -270,8 +279,16 @@ class _Session:
     def trace(self):
         return self.len.copy(), self.pend.copy(), self.fc.copy()
 
+    def _round(self, S):
+        """The state as the checkpoint keeps it (rounded to the copy's grid in the
+        quantized-checkpoint variant, unchanged otherwise)."""
+        if not self.quantized_ckpt:
+            return S
+        return read_copy_values(S, self.read_copy).reshape(S.shape)
+
     def _flush_rows(self, rows):
         for b in np.flatnonzero(rows):
+            self.S[b] = self._round(self.S[b:b + 1])[0]
             self.ckpt[b] = self.S[b]
             self.fc[b] += 1
             self.len[b] = 0
@@ -292,7 +309,7 @@ class _Session:
     def load(self, S0):
         if self.pend.any():
             raise PhaseError("load while drafts are pending")
-        self.S = np.array(S0, np.float64, copy=True)
+        self.S = self._round(np.array(S0, np.float64, copy=True))
         self.ckpt = self.S.copy()
         self.len[:] = 0
         self.pend[:] = 0
@@ -317,6 +334,9 @@ class _Session:
             if not full[b]:
                 self.hist[b].append(self._slice(inp, b))
         self._flush_rows(full)
+        if self.quantized_ckpt:
+            for b in np.flatnonzero(full):
+                y[b] = self._readout(self.S[b], self._slice(inp, b))
         self.nops += 1
         return y
 
@@ -381,13 +401,21 @@ class Mamba2Session(_Session):
 
     kind = "mamba2"
 
-    def __init__(self, A, D, S0, cap=16, read_copy=None):
+    def __init__(self, A, D, S0, cap=16, read_copy=None, quantized_ckpt=False):
         self.A = np.asarray(A, np.float64)
         self.D = np.asarray(D, np.float64)
-        super().__init__(np.asarray(S0).shape[0], cap, S0, read_copy)
+        super().__init__(np.asarray(S0).shape[0], cap, S0, read_copy, quantized_ckpt)
 
     def _token(self, S, inp, active=None):
         return mamba2_token(S, inp["x"], inp["Bm"], inp["Cm"], inp["dt"], self.A, self.D, active)
+
+    def _readout(self, S_b, inp_b):
+        """y = S C + D x for one sequence, without a state update."""
+        H = S_b.shape[0]
+        g = np.arange(H) // (H // inp_b["Cm"].shape[1])
+        C = np.asarray(inp_b["Cm"][0], np.float64)[g]                 # [H, N]
+        x = np.asarray(inp_b["x"][0], np.float64)                     # [H, P]
+        return np.einsum("hpn,hn->hp", S_b, C) + self.D[:, None] * x
 
 
 class GDNSession(_Session):
@@ -395,12 +423,19 @@ class GDNSession(_Session):
 
     kind = "gdn"
 
-    def __init__(self, S0, cap=16, scale=1.0, read_copy=None):
+    def __init__(self, S0, cap=16, scale=1.0, read_copy=None, quantized_ckpt=False):
         self.scale = float(scale)
-        super().__init__(np.asarray(S0).shape[0], cap, S0, read_copy)
+        super().__init__(np.asarray(S0).shape[0], cap, S0, read_copy, quantized_ckpt)
 
     def _token(self, S, inp, active=None):
         return gdn_token(S, inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], self.scale, active)
+
+    def _readout(self, S_b, inp_b):
+        """o = scale S q for one sequence, without a state update."""
+        H = S_b.shape[0]
+        g = np.arange(H) // (H // inp_b["q"].shape[1])
+        q = np.asarray(inp_b["q"][0], np.float64)[g]                  # [H, DK]
+        return self.scale * np.einsum("hij,hj->hi", S_b, q)
 
 
 def normwise_error(got, ref, axis=-1):

@@ -1,0 +1,69 @@
+"""Long-decode output error of the low-precision variants against the fp64 recurrence.
+
+Stand-in for the pages' quantization study (Qwen3.5-4B at 128K tokens, GPQA-Diamond;
+[TR] "NVIDIA ve Dao AI Lab ...", section "Kuantizasyon hatasinin sinirlandirilmasi"):
+the batch-128 Gated DeltaNet layer (32 heads, d_k = d_v = 128, bf16 q/k/v, fp32
+gates) decodes 8192 steps from an N(0, 0.1) checkpoint in five variants:
+  R0 fp32 checkpoint only          R1 fp32 checkpoint + FP8 read copy
+  R2 fp32 checkpoint + MXFP4 copy  Q1 FP8 checkpoint only    Q2 MXFP4 checkpoint only
+The normwise output error against the fp64 recurrence is measured on four
+sequences and reported at 1K, 2K, 4K and 8K steps and as the maximum.  The
+claims checked are the ones the pages make: read error stays at the level of one
+quantization of the checkpoint (it does not accumulate: the error late in the run
+is not larger than early on), and a low-precision checkpoint inside the
+recurrence is worse than the same format used only for reads.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+
+
+def test_low_precision_error_over_8192_steps():
+    from hybrid_decode_replay_amd import binding as b, synth
+    from oracle import replay_oracle as ro
+    B, H, D, T, CH = 128, 32, 128, 8192, 512
+    sample = [0, 41, 86, 127]
+    variants = {"R0": (b.NONE, 0), "R1": (b.FP8_E4M3, 0), "R2": (b.MXFP4, 0),
+                "Q1": (b.FP8_E4M3, b.FLAG_QUANTIZED_CKPT), "Q2": (b.MXFP4, b.FLAG_QUANTIZED_CKPT)}
+    S0 = synth.checkpoint_device(4, (B, H, D, D), "cuda")
+    states = {}
+    for name, (rc, fl) in variants.items():
+        st = b.ReplayState(b.make_config(b.GDN, B, H, H, D, D, 16, b.BF16, read_copy=rc, flags=fl))
+        st.load_checkpoint(S0)
+        states[name] = st
+    S = S0[sample].double().cpu().numpy()
+    ys = torch.empty((len(variants), CH, B, H, D), dtype=torch.bfloat16, device="cuda")
+    err = {name: np.zeros(T) for name in variants}
+    print("[lowprec] 5 variants x 8192 steps", flush=True)
+    for c0 in range(0, T, CH):
+        toks = synth.gdn_tokens_device(1000 + c0, CH, B, H, H, D, D, "cuda")
+        for i, st in enumerate(states.values()):
+            for t in range(CH):
+                st.decode({k: v[t:t + 1] for k, v in toks.items()}, y=ys[i, t:t + 1])
+        host = {k: v[:, sample].double().cpu().numpy() for k, v in toks.items()}
+        yg = ys[:, :, sample].double().cpu().numpy()
+        for t in range(CH):
+            yo = ro.gdn_token(S, *(host[k][t] for k in ("q", "k", "v", "alpha", "beta")))
+            for i, name in enumerate(variants):
+                err[name][c0 + t] = ro.normwise_error(yg[i, t], yo)
+    rows = []
+    for name in variants:
+        e = err[name]
+        rows.append((name, *[float(np.max(e[max(0, s - 1024):s])) for s in (1024, 2048, 4096, 8192)], float(e.max())))
+        print(f"[lowprec] {name}: max error over steps ending at 1K/2K/4K/8K = "
+              + " / ".join(f"{v:.3e}" for v in rows[-1][1:5]) + f"; max {rows[-1][5]:.3e}", flush=True)
+    e = {r[0]: r for r in rows}
+    assert e["R0"][5] <= 2e-2                                   # bf16 output rounding only
+    for r in ("R1", "R2"):
+        assert e[r][4] <= 2.0 * e[r][1] + 1e-3, r               # read error does not accumulate
+    assert np.mean(err["Q1"][-1024:]) > np.mean(err["R1"][-1024:])
+    assert np.mean(err["Q2"][-1024:]) > np.mean(err["R2"][-1024:])

@@ -184,3 +184,33 @@ def test_bf16_io_with_mxfp4_copy_full_size_sample():
     for t in range(T):
         err = ro.normwise_error(yg[t], sess.decode(synth.token(host, t)))
         assert err <= 2e-2, (t, err)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_quantized_checkpoint_variant(fmt, kind):
+    """Checkpoint kept at the copy's precision: rounded at load (exactly the oracle's rounding
+    of the same fp32 values), non-flush outputs from it (1e-4), and after every fold the fp32
+    checkpoint lies on the copy's grid (re-quantizing it changes nothing)."""
+    from harness import Pair
+    from oracle import replay_oracle as ro
+    b = rb()
+    B, H, C, R, cap = 2, 2, 32, 64, 6
+    S0 = synth.checkpoint(90, (B, H, C, R))
+    pair = Pair(b.MAMBA2 if kind == "mamba2" else b.GDN, B, H, H, C, R, cap=cap, io=b.F32, seed=90, S0=S0,
+                read_copy=rc_code(fmt), flags=b.FLAG_QUANTIZED_CKPT)
+    # the oracle session of the harness keeps a full-precision checkpoint; use the variant's
+    pair.orc = (ro.Mamba2Session(pair.orc.A, pair.orc.D, S0, cap=cap, read_copy=fmt, quantized_ckpt=True)
+                if kind == "mamba2" else ro.GDNSession(S0, cap=cap, read_copy=fmt, quantized_ckpt=True))
+    torch.cuda.synchronize()
+    ck = pair.st.read_checkpoint().cpu().numpy().astype(np.float64)
+    np.testing.assert_array_equal(ck, pair.orc.S)                      # rounded at load, identically
+    toks = _tokens(kind, 90, 3 * cap, B, H, C, R)
+    for t in range(cap - 1):
+        y = pair.st.decode(pair.to_dev(synth.token(toks, t)), pair.params)
+        pair.check_outputs(y[0], pair.orc.decode(synth.token(toks, t)), f"step {t}")
+    for t in range(cap - 1, 3 * cap):
+        pair.st.decode(pair.to_dev(synth.token(toks, t)), pair.params)
+        torch.cuda.synchronize()
+        ck = pair.st.read_checkpoint().cpu().numpy().astype(np.float64)
+        np.testing.assert_array_equal(ro.read_copy_values(ck, fmt).reshape(ck.shape), ck)

@@ -468,3 +468,59 @@ def test_normwise_error_definition():
     ref = np.array([[1.0, -2.0], [1e-40, 0.0]])
     got = np.array([[1.0, -2.002], [0.0, 0.0]])
     assert abs(ro.normwise_error(got, ref) - max(0.002 / 2.0, 1e-40 / 1e-30)) < 1e-15
+
+
+# --------------------------------------------------------------------------
+# Read-copy and quantized-checkpoint semantics of the op runner
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_readout_equals_identity_token(kind):
+    """The readout used after a rounded fold equals a token whose update is the identity
+    (Mamba-2 dt = 0; GDN alpha = 1, beta = 0)."""
+    mk, toks = _mk(kind)
+    sess = mk()
+    tok = synth.token(toks, 0)
+    S = sess.S.copy()
+    if kind == "mamba2":
+        ident = dict(tok, dt=np.zeros_like(tok["dt"]))
+    else:
+        ident = dict(tok, alpha=np.ones_like(tok["alpha"]), beta=np.zeros_like(tok["beta"]))
+    y_id = sess._token(S, ident)
+    np.testing.assert_array_equal(S, sess.S)
+    for b in range(sess.B):
+        np.testing.assert_allclose(sess._readout(sess.S[b], sess._slice(tok, b)), y_id[b], rtol=1e-14, atol=1e-15)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_read_copy_is_identity_on_grid_values(fmt):
+    """A checkpoint already on the copy's grid reads back exactly, so read-copy outputs equal
+    full-precision outputs; and rounding is idempotent."""
+    B, H, G, P, N = 2, 2, 1, 4, 32
+    A, D = synth.mamba2_params(60, H)
+    S0 = ro.read_copy_values(synth.checkpoint(60, (B, H, P, N)), fmt).reshape(B, H, P, N)
+    np.testing.assert_array_equal(ro.read_copy_values(S0, fmt).reshape(S0.shape), S0)
+    toks = synth.mamba2_tokens(60, 5, B, H, G, P, N)
+    plain = ro.Mamba2Session(A, D, S0, cap=8)
+    rc = ro.Mamba2Session(A, D, S0, cap=8, read_copy=fmt)
+    for t in range(5):
+        np.testing.assert_allclose(rc.decode(synth.token(toks, t)), plain.decode(synth.token(toks, t)),
+                                   rtol=1e-13, atol=1e-13)
+
+
+def test_quantized_checkpoint_rounds_at_every_flush():
+    B, H, G, P, N, cap = 2, 2, 1, 4, 32, 3
+    A, D = synth.mamba2_params(61, H)
+    S0 = synth.checkpoint(61, (B, H, P, N))
+    sess = ro.Mamba2Session(A, D, S0, cap=cap, read_copy="fp8", quantized_ckpt=True)
+    plain = ro.Mamba2Session(A, D, S0, cap=cap)
+    toks = synth.mamba2_tokens(61, 10, B, H, G, P, N)
+    assert not np.array_equal(sess.S, plain.S)
+    for t in range(10):
+        sess.decode(synth.token(toks, t))
+        plain.decode(synth.token(toks, t))
+        if (t + 1) % cap == 0:
+            np.testing.assert_array_equal(ro.read_copy_values(sess.ckpt, "fp8").reshape(sess.ckpt.shape), sess.ckpt)
+    assert np.max(np.abs(sess.S - plain.S)) > 0
+    with pytest.raises(ValueError):
+        ro.Mamba2Session(A, D, S0, quantized_ckpt=True)
