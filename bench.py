@@ -18,7 +18,12 @@ The JSON line also carries:
   spec          speculative rounds at batch 512 (4 drafts per round, accepted
                 prefix ~ min(Geometric(0.35) - 1, 4), seeded): replay append +
                 commit vs the snapshot-per-draft + restore baseline, both layers
+  gdn_read_copy_b128
+                the batch-128 GDN layer with an fp32 checkpoint and no copy,
+                an FP8 E4M3 read copy, and an MXFP4 read copy
   cpu_baseline  the fp64 oracle on the host cores over a bounded sample
+With --sweep FILE, both layers are also timed at batch 1..512 (replay and
+conventional), one JSON line per point in FILE.
 """
 from __future__ import annotations
 
@@ -33,20 +38,23 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "mamba2_step_b256_traffic.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "hybrid_decode_replay_amd", "csrc", f) for f in ("mamba2.hip", "common.hpp")]
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "mamba2_step_b256_traffic.txt")  # written by profsum
+KERNEL_SOURCES = [os.path.join(ROOT, "hybrid_decode_replay_amd", "csrc", f)
+                  for f in ("mamba2.hip", "common.hpp", "stage.hpp", "rc.hpp")]
 
 MAMBA2 = dict(H=128, G=8, C=64, R=128)     # heads, groups, head dim P, state dim N
 GDN = dict(H=32, G=32, C=128, R=128)       # heads, q/k heads, d_v, d_k
 
 
-def algorithmic_bytes(kind, H, G, C, R, cap=16, io_bytes=2):
+def algorithmic_bytes(kind, H, G, C, R, cap=16, io_bytes=2, read_copy=None):
     """(replay, conventional) bytes per sequence-token.
 
     Replay, averaged over a full window of `cap` steps with lockstep flushes: the
     checkpoint is read every step and written once per window; the current inputs are
     read; the new entry is written; on average (cap-1)/2 prior entries are read; the
-    output is written.  Conventional: state read and written every token, inputs,
+    output is written.  With a read copy, the cap-1 non-flush steps read the copy and
+    the flush step reads and writes fp32 and writes the copy: per token copy + S/8 in
+    place of S + S/cap.  Conventional: state read and written every token, inputs,
     output.  Entries: Mamba-2 x, B, dt; GDN k, v and the fp32 gates."""
     S = H * C * R * 4
     if kind == "mamba2":
@@ -56,7 +64,12 @@ def algorithmic_bytes(kind, H, G, C, R, cap=16, io_bytes=2):
         entry = (H * C + G * R) * io_bytes + 2 * H * 4
         inp = (H * C + 2 * G * R) * io_bytes + 2 * H * 4
     out = H * C * io_bytes
-    replay = S + S / cap + inp + entry + (cap - 1) / 2 * entry + out
+    state = S + S / cap
+    if read_copy is not None:
+        n = H * C * R
+        copy = n if read_copy == "fp8" else n / 2 + n / 32
+        state = (cap - 1) / cap * copy + 2 * S / cap + copy / cap
+    replay = state + inp + entry + (cap - 1) / 2 * entry + out
     conv = 2 * S + inp + out
     return replay, conv
 
@@ -117,13 +130,15 @@ def cpu_baseline(H, G, P, N, budget_s=10.0, max_s=30.0):
 class Layer:
     """Device-side state, parameters and pre-drawn inputs of one synthetic layer."""
 
-    def __init__(self, rb, synth, torch, dev, kind, B, steps, seed, cap=16):
+    def __init__(self, rb, synth, torch, dev, kind, B, steps, seed, cap=16, read_copy=None):
         self.rb, self.torch, self.dev, self.kind, self.B = rb, torch, dev, kind, B
         shp = MAMBA2 if kind == "mamba2" else GDN
         self.H, self.G, self.C, self.R = shp["H"], shp["G"], shp["C"], shp["R"]
         self.cap = cap
+        self.read_copy = read_copy
+        rc = {None: rb.NONE, "fp8": rb.FP8_E4M3, "mxfp4": rb.MXFP4}[read_copy]
         self.cfg = rb.make_config(rb.MAMBA2 if kind == "mamba2" else rb.GDN, B, self.H, self.G, self.C, self.R,
-                                  cap, rb.BF16)
+                                  cap, rb.BF16, read_copy=rc)
         self.S0 = synth.checkpoint_device(seed, (B, self.H, self.C, self.R), dev)
         if kind == "mamba2":
             A, D = synth.mamba2_params(seed, self.H)
@@ -191,7 +206,7 @@ def time_conv_decode(L, K, stream, t0=0):
 
 
 def decode_report(L, r, conv_ms):
-    replay_b, conv_b = algorithmic_bytes(L.kind, L.H, L.G, L.C, L.R, L.cap)
+    replay_b, conv_b = algorithmic_bytes(L.kind, L.H, L.G, L.C, L.R, L.cap, read_copy=L.read_copy)
     ms = r["total_ms"] / r["steps"]
     ach = replay_b * L.B / (r["avg_launch_ms"] / 1e3) / 1e9
     out = {"batch": L.B, "tokens_per_s": round(L.B / (ms / 1e3), 1), "ms_per_step": round(ms, 5),
@@ -291,6 +306,7 @@ def main():
     ap.add_argument("--spec-rounds", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="headline layer only (no GDN, spec, conventional)")
+    ap.add_argument("--sweep", metavar="FILE", help="also sweep batch 1..512 for both layers, JSON lines to FILE")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the decode path shards by "
@@ -349,6 +365,31 @@ def main():
             del Ls
             torch.cuda.empty_cache()
         out["spec"] = spec
+        # low-precision reads on the batch-128 GDN layer: fp32, FP8 and MXFP4 read copies
+        lp = {}
+        for rc in (None, "fp8", "mxfp4"):
+            Lr = Layer(rb, synth, torch, dev, "gdn", 128, 256 + 32 + 4, seed=4, read_copy=rc)
+            rr = time_replay_decode(Lr, 256, 32, stream)
+            lp[rc or "fp32"] = decode_report(Lr, rr, None)
+            del Lr
+            torch.cuda.empty_cache()
+        out["gdn_read_copy_b128"] = lp
+
+    if args.sweep:
+        with open(args.sweep, "w") as f:
+            for kind in ("mamba2", "gdn"):
+                for bsz in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512):
+                    Lw = Layer(rb, synth, torch, dev, kind, bsz, 64 + 16 + 4, seed=5)
+                    rw = time_replay_decode(Lw, 64, 16, stream)
+                    rep = decode_report(Lw, rw, time_conv_decode(Lw, 32, stream))
+                    rep["kind"] = kind
+                    f.write(json.dumps(rep) + "\n")
+                    f.flush()
+                    print(f"[sweep] {kind} B={bsz}: replay {rep['ms_per_step']:.4f} ms, conventional "
+                          f"{rep['conventional']['ms_per_step']:.4f} ms, speedup {rep['speedup_vs_conventional']}",
+                          file=sys.stderr, flush=True)
+                    del Lw
+                    torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(128, 8, 64, 128)

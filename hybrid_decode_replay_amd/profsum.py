@@ -1,16 +1,16 @@
 """Summarise rocprofv3 CSV output into the short text files kept under profiles/.
 
-Usage (after the rocprofv3 runs named in the summary headers):
-    python -m hybrid_decode_replay_amd.profsum KT_DIR FETCH_DIR WRITE_DIR OUT_PREFIX \
-        "KERNEL-TRACE COMMAND" "FETCH_SIZE COMMAND" "WRITE_SIZE COMMAND"
+Usage (after the rocprofv3 runs whose commands are passed in, for the record):
+    python -m hybrid_decode_replay_amd.profsum trace KT_DIR OUT.md "COMMAND"
+    python -m hybrid_decode_replay_amd.profsum traffic FETCH_DIR WRITE_DIR OUT.txt KERNEL GRID \\
+        "FETCH_SIZE COMMAND" "WRITE_SIZE COMMAND"
 
-* KT_DIR holds *_kernel_stats.csv from `rocprofv3 --kernel-trace --stats`.
-* FETCH_DIR / WRITE_DIR hold *_counter_collection.csv from `--pmc FETCH_SIZE` and
-  `--pmc WRITE_SIZE` runs of the same program.
-The counters are calibrated on the streaming-copy kernel of the same run, whose
-bytes are known (it reads and writes 1 GiB): scale = known bytes / counter bytes.
-The traffic per launch of the replay kernel is the mean over its dispatches of
-FETCH*scale_fetch + WRITE*scale_write.
+trace    per (kernel, grid size) call counts and durations from *_kernel_trace.csv of a
+         `rocprofv3 --kernel-trace` run (one row per workload of the program).
+traffic  HBM bytes per launch of KERNEL dispatches with grid size GRID (threads), from
+         *_counter_collection.csv of a `--pmc FETCH_SIZE` and a `--pmc WRITE_SIZE` run.
+         Both counters are calibrated on the streaming-copy kernel of the same runs,
+         which reads and writes 1 GiB: scale = known bytes / counter bytes.
 """
 from __future__ import annotations
 
@@ -22,6 +22,11 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 COPY_BYTES = 1 << 30
+SOURCES = {
+    "mamba2_step_kernel": ("mamba2.hip", "common.hpp", "stage.hpp", "rc.hpp"),
+    "gdn_step_kernel": ("gdn.hip", "common.hpp", "stage.hpp", "rc.hpp"),
+    "conv_step_kernel": ("conv.hip", "common.hpp"),
+}
 
 
 def _one(pattern):
@@ -31,12 +36,39 @@ def _one(pattern):
     return files[0]
 
 
-def kernel_key(name: str) -> str:
-    for key in ("mamba2_step_kernel", "gdn_step_kernel", "conv_step_kernel", "stream_copy_kernel",
-                "stream_read_kernel", "book_commit_kernel", "conv_restore_kernel"):
-        if key in name:
-            return key
-    return name.split("(")[0][:60]
+def short(name: str) -> str:
+    base = name.split("(")[0]
+    return base.replace("void ", "").replace("rs::", "")
+
+
+def source_sha(kernel):
+    h = hashlib.sha256()
+    for f in SOURCES[kernel]:
+        with open(os.path.join(ROOT, "hybrid_decode_replay_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def trace(kt_dir, out, command):
+    rows = list(csv.DictReader(open(_one(os.path.join(kt_dir, "**", "*kernel_trace.csv")))))
+    groups = {}
+    for r in rows:
+        key = (short(r["Kernel_Name"]), int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    total = sum(sum(v) for v in groups.values())
+    lines = [f"# rocprofv3 kernel trace: {os.path.basename(out)[:-3]}", "",
+             "Command (from the repository root; run under `cd /tmp && export TMPDIR=/tmp`):", "",
+             f"    {command}", "",
+             "Per (kernel, grid) -- one row per workload of the run; durations in microseconds.", "",
+             "| kernel | workgroups x threads | calls | avg us | min us | max us | share |",
+             "|---|---|---|---|---|---|---|"]
+    for (name, grid, wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        if not name.startswith(("mamba2", "gdn", "conv", "stream", "book", "quantize", "logical", "tiles", "rc_")):
+            continue
+        lines.append(f"| `{name}` | {grid // wg} x {wg} | {len(d)} | {sum(d) / len(d):.1f} | {min(d):.1f} | "
+                     f"{max(d):.1f} | {100 * sum(d) / total:.1f}% |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 def counters(path, cname):
@@ -44,70 +76,53 @@ def counters(path, cname):
     for r in csv.DictReader(open(path)):
         if r["Counter_Name"] != cname:
             continue
-        out.setdefault(kernel_key(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        key = (short(r["Kernel_Name"]).split("<")[0], int(r["Grid_Size"]))
+        out.setdefault(key, []).append(float(r["Counter_Value"]))
     return out
 
 
-def source_sha(files):
-    h = hashlib.sha256()
-    for p in files:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
-def main(kt_dir, fetch_dir, write_dir, prefix, command, fetch_cmd, write_cmd, kernel="mamba2_step_kernel",
-         sources=("hybrid_decode_replay_amd/csrc/mamba2.hip", "hybrid_decode_replay_amd/csrc/common.hpp")):
-    stats = list(csv.DictReader(open(_one(os.path.join(kt_dir, "**", "*kernel_stats.csv")))))
+def traffic(fetch_dir, write_dir, out, kernel, grid, fetch_cmd, write_cmd):
+    grid = int(grid)
     fetch = counters(_one(os.path.join(fetch_dir, "**", "*counter_collection.csv")), "FETCH_SIZE")
     write = counters(_one(os.path.join(write_dir, "**", "*counter_collection.csv")), "WRITE_SIZE")
-    cf = sum(fetch["stream_copy_kernel"]) / len(fetch["stream_copy_kernel"])
-    cw = sum(write["stream_copy_kernel"]) / len(write["stream_copy_kernel"])
-    s_fetch = COPY_BYTES / (cf * 1024)
-    s_write = COPY_BYTES / (cw * 1024)
-    kf, kw = fetch[kernel], write[kernel]
+
+    def pick(d, name, g=None):
+        vals = [v for (k, gg), vs in d.items() if k == name and (g is None or gg == g) for v in vs]
+        if not vals:
+            raise KeyError((name, g))
+        return vals
+
+    cf, cw = pick(fetch, "stream_copy_kernel"), pick(write, "stream_copy_kernel")
+    s_fetch = COPY_BYTES / (sum(cf) / len(cf) * 1024)
+    s_write = COPY_BYTES / (sum(cw) / len(cw) * 1024)
+    kf, kw = pick(fetch, kernel, grid), pick(write, kernel, grid)
     n = min(len(kf), len(kw))
     per = [kf[i] * 1024 * s_fetch + kw[i] * 1024 * s_write for i in range(n)]
-    traffic = sum(per) / n
-
-    lines = [f"# rocprofv3 kernel trace: {os.path.basename(prefix)}", "",
-             "Command (from the repository root; run under `cd /tmp && export TMPDIR=/tmp`):", "",
-             f"    {command}", "",
-             "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
-    for r in stats[:12]:
-        lines.append(f"| {kernel_key(r['Name'])} `{r['Name'][:70]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
-                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
-    with open(prefix + "_kernel_trace.md", "w") as f:
+    lines = [f"# HBM traffic of {kernel} (grid {grid} threads) from rocprofv3 --pmc runs",
+             f"# FETCH_SIZE run: {fetch_cmd}",
+             f"# WRITE_SIZE run: {write_cmd}",
+             "# calibration: stream_copy_kernel reads and writes 1 GiB per dispatch",
+             f"kernel = {kernel}",
+             f"grid_threads = {grid}",
+             f"kernel_source_sha = {source_sha(kernel)}",
+             f"dispatches = {n}",
+             f"fetch_scale = {s_fetch:.4f}",
+             f"write_scale = {s_write:.4f}",
+             f"fetch_kib_per_dispatch_mean = {sum(kf[:n]) / n:.1f}",
+             f"write_kib_per_dispatch_mean = {sum(kw[:n]) / n:.1f}",
+             f"fetch_kib_per_dispatch_min_max = {min(kf[:n]):.1f} {max(kf[:n]):.1f}",
+             f"write_kib_per_dispatch_min_max = {min(kw[:n]):.1f} {max(kw[:n]):.1f}",
+             f"traffic_bytes_per_launch = {sum(per) / n:.0f}"]
+    with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
-
-    sha = source_sha(sources)
-    txt = [f"# HBM traffic of {kernel} from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (separate runs)",
-           f"# FETCH_SIZE run: {fetch_cmd}",
-           f"# WRITE_SIZE run: {write_cmd}",
-           "# calibration: stream_copy_kernel reads and writes 1 GiB per dispatch",
-           f"kernel = {kernel}",
-           f"kernel_source_sha = {sha}",
-           f"dispatches = {n}",
-           f"copy_fetch_kib = {cf:.1f}",
-           f"copy_write_kib = {cw:.1f}",
-           f"fetch_scale = {s_fetch:.4f}",
-           f"write_scale = {s_write:.4f}",
-           f"fetch_kib_per_dispatch_mean = {sum(kf[:n]) / n:.1f}",
-           f"write_kib_per_dispatch_mean = {sum(kw[:n]) / n:.1f}",
-           f"fetch_kib_per_dispatch_min_max = {min(kf):.1f} {max(kf):.1f}",
-           f"write_kib_per_dispatch_min_max = {min(kw):.1f} {max(kw):.1f}",
-           f"traffic_bytes_per_launch = {traffic:.0f}"]
-    for k in sorted(set(fetch) & set(write)):
-        if k in (kernel, "stream_copy_kernel") or "at::" in k or k.startswith("void at"):
-            continue
-        fk, wk = fetch[k], write[k]
-        m = min(len(fk), len(wk))
-        t = sum(fk[i] * 1024 * s_fetch + wk[i] * 1024 * s_write for i in range(m)) / m
-        txt.append(f"other.{k}.traffic_bytes_per_launch = {t:.0f}")
-    with open(prefix + "_traffic.txt", "w") as f:
-        f.write("\n".join(txt) + "\n")
-    print(prefix, "traffic/launch", traffic)
+    print(out, "traffic per launch", sum(per) / n)
 
 
 if __name__ == "__main__":
-    main(*sys.argv[1:8])
+    mode, args = sys.argv[1], sys.argv[2:]
+    if mode == "trace":
+        trace(*args)
+    elif mode == "traffic":
+        traffic(*args)
+    else:
+        raise SystemExit(__doc__)
