@@ -205,6 +205,56 @@ def time_conv_decode(L, K, stream, t0=0):
     return e0.elapsed_time(e1) / K
 
 
+def time_graph(L, conventional, n=64, reps=8):
+    """Per-step GPU time of n back-to-back decode steps captured in one HIP graph (no host
+    launch overhead and no events between steps), averaged over `reps` replays.  n is a
+    multiple of the buffer capacity, so every replay covers whole windows and ends at the
+    parity it began with."""
+    rb, torch = L.rb, L.torch
+    lib = rb.lib()
+    ins = [L.inputs(t) for t in range(n)]
+    y = torch.empty((1, L.B, L.H, L.C), dtype=torch.bfloat16, device=L.dev)
+    yp = rb.ctypes.c_void_p(y.data_ptr())
+    if conventional:
+        S = L.S0.clone()
+        cp, Sp = rb.ctypes.byref(L.cfg), rb.ctypes.c_void_p(S.data_ptr())
+
+        def step(t, sp):
+            return lib.replay_conv_decode_step(cp, Sp, rb.ctypes.byref(ins[t]), yp, sp)
+    else:
+        st = rb.ReplayState(L.cfg, device=L.dev)
+        st.load_checkpoint(L.S0)
+
+        def step(t, sp):
+            return lib.replay_decode_step(st.h, rb.ctypes.byref(ins[t]), yp, sp)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                       # eager warm-up: one full pass
+        for t in range(n):
+            status = step(t, rb.ctypes.c_void_p(side.cuda_stream))
+            if status != rb.OK:
+                raise rb.ReplayError(status, "graph warm-up")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        sp = rb.ctypes.c_void_p(side.cuda_stream)
+        for t in range(n):
+            status = step(t, sp)
+            if status != rb.OK:
+                raise rb.ReplayError(status, "graph capture")
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * n)
+    del g
+    return ms
+
+
 def decode_report(L, r, conv_ms):
     replay_b, conv_b = algorithmic_bytes(L.kind, L.H, L.G, L.C, L.R, L.cap, read_copy=L.read_copy)
     ms = r["total_ms"] / r["steps"]
@@ -383,11 +433,14 @@ def main():
                     rw = time_replay_decode(Lw, 64, 16, stream)
                     rep = decode_report(Lw, rw, time_conv_decode(Lw, 32, stream))
                     rep["kind"] = kind
+                    g_rep, g_conv = time_graph(Lw, False), time_graph(Lw, True)
+                    rep["graph"] = {"replay_ms_per_step": round(g_rep, 5), "conventional_ms_per_step": round(g_conv, 5),
+                                    "speedup_vs_conventional": round(g_conv / g_rep, 3)}
                     f.write(json.dumps(rep) + "\n")
                     f.flush()
                     print(f"[sweep] {kind} B={bsz}: replay {rep['ms_per_step']:.4f} ms, conventional "
-                          f"{rep['conventional']['ms_per_step']:.4f} ms, speedup {rep['speedup_vs_conventional']}",
-                          file=sys.stderr, flush=True)
+                          f"{rep['conventional']['ms_per_step']:.4f} ms, speedup {rep['speedup_vs_conventional']}; "
+                          f"graph {g_rep:.4f} / {g_conv:.4f} ms", file=sys.stderr, flush=True)
                     del Lw
                     torch.cuda.empty_cache()
 

@@ -66,6 +66,22 @@ constexpr int DPP_ROW_HALF_MIRROR = 0x141; // lane i <-> 7-i within half a row
 constexpr int DPP_ROW_BCAST15 = 0x142;     // lane 15 of a row -> the next row
 constexpr int DPP_ROW_BCAST31 = 0x143;     // lane 31 -> rows 2 and 3
 
+constexpr int DPP_ROW_SHR1 = 0x111;        // lane i <- lane i-1 within a row (0 at the row start)
+constexpr int DPP_ROW_SHR2 = 0x112;
+constexpr int DPP_ROW_SHR4 = 0x114;
+constexpr int DPP_ROW_SHR8 = 0x118;
+
+// Inclusive prefix sum over lanes 0..31 (Hillis-Steele within each row of 16,
+// then row 0's total carried into row 1).  Lanes 32..63 hold partial values.
+__device__ __forceinline__ float scan32_inclusive(float v) {
+    v += dpp_mov<DPP_ROW_SHR1>(v);
+    v += dpp_mov<DPP_ROW_SHR2>(v);
+    v += dpp_mov<DPP_ROW_SHR4>(v);
+    v += dpp_mov<DPP_ROW_SHR8>(v);
+    v += dpp_mov<0x142, 0xa>(v);            // row_bcast:15 into rows 1 and 3
+    return v;
+}
+
 // Sum over the 4 lanes of each quad; every lane of the quad gets the sum.
 __device__ __forceinline__ float quad_sum(float v) {
     v += dpp_mov<DPP_QUAD_XOR1>(v);

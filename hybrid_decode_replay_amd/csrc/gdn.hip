@@ -81,7 +81,7 @@ __global__ __launch_bounds__(1024) void gdn_step_kernel(StepArgs a)
     G.b = b; G.h = h; G.g = g; G.B = a.B; G.H = a.H; G.G = a.G; G.cap = a.cap; G.C = C;
     G.c0 = c0; G.cw = cw;
     G.len = len; G.bank = p.bank; G.V = V; G.T = T;
-    G.xc = vs; G.xr = ks; G.xq = qs; G.s0 = al; G.s1 = be;
+    G.xc = vs; G.xr = ks; G.xq = qs; G.s0 = al; G.s1 = be; G.p0 = nullptr;
 
     // ---- 1. entry chunks ahead of the checkpoint stream, 2. checkpoint tile
     const Stager<IO, R> stg(G);

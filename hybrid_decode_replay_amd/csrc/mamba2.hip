@@ -20,7 +20,9 @@
 //           (if the token itself was folded, pos < f: y_t = S' C_t + D_h x_t)
 //
 // Non-flush steps read the checkpoint once and write no state; the flush step
-// writes it once.  Only exponentials of sums of l (all <= 0) are taken.
+// writes it once.  Only exponentials of sums of l (all <= 0) are taken; a sum
+// over an entry range is a difference of inclusive prefix sums of dt, formed
+// once per launch by a wave scan while the entries are published.
 //
 // Memory schedule per workgroup: the entry rows (x, B), the read-out rows C
 // and dt are fetched as 16-byte chunks issued before the checkpoint stream,
@@ -42,6 +44,7 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
     constexpr int R = NB * 16;
     constexpr int RS = R + 4;                   // padded LDS stride of B rows
     constexpr int PRE = 4;                      // chunks per thread fetched ahead of the checkpoint
+    constexpr int VM = (16 + TMAX + 3) & ~3;    // bound on the entry count cap + T, padded to 4
     const int C = a.C;
     const TileIdx tix = tile_of(xcd_tile_index(), a.H, a.nsplit);
     const int b = tix.b, h = tix.h, tile = b * a.H + h;
@@ -61,10 +64,11 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
 
     // ---- LDS partition (floats)
     const int Tr = T > 0 ? T : 1;
-    float* xs = lds;                              // [vmax][cw] entry x rows (own columns)
+    float* ds = lds;                              // [VM]       entry dt (vmax <= VM)
+    float* ps = ds + VM;                          // [VM]       inclusive prefix sums of dt
+    float* xs = ps + VM;                          // [vmax][cw] entry x rows (own columns)
     float* bs = xs + (size_t)a.vmax * cw;         // [vmax][RS] entry B rows
     float* cs = bs + (size_t)a.vmax * RS;         // [Tr][R]    read-out rows C_t
-    float* ds = cs + (size_t)Tr * R;              // [vmax]     entry dt
 
     StageGeom G;
     G.bufc = a.bufc; G.bufr = a.bufr; G.bufs0 = a.bufs0; G.bufs1 = nullptr;
@@ -74,7 +78,7 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
     G.b = b; G.h = h; G.g = g; G.B = a.B; G.H = a.H; G.G = a.G; G.cap = a.cap; G.C = C;
     G.c0 = c0; G.cw = cw;
     G.len = len; G.bank = p.bank; G.V = p.V; G.T = T;
-    G.xc = xs; G.xr = bs; G.xq = cs; G.s0 = ds; G.s1 = nullptr;
+    G.xc = xs; G.xr = bs; G.xq = cs; G.s0 = ds; G.s1 = nullptr; G.p0 = ps;
 
     // ---- 1. entry and read-out chunks, issued ahead of the checkpoint stream
     const Stager<IO, R> stg(G);
@@ -103,10 +107,11 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
     const float Ah = a.A[h];
 
     // ---- 4. fold the first f entries into the checkpoint registers
+    // sums of dt over an entry range come from the prefix sums: sum_{lo<=i<hi} = ps[hi-1] - ps[lo-1]
+    // (with dt >= 0 and A_h <= 0 every exponent is <= 0 up to the rounding of that difference)
     if (f > 0) {
-        float Lf = 0.f;
-        for (int i = 0; i < f; ++i) Lf += ds[i];
-        const float decay = expf(Lf * Ah);
+        const float pf = ps[f - 1];
+        const float decay = expf(pf * Ah);
         if constexpr (MFMA_FOLD) {
             // D[n][p] += sum_i A[n][i] B[i][p] with A = B_i[n] (lane: n = l%16,
             // i = l/16) and B = e^{..} dt_i x_i[p] (lane: i = l/16, p = l%16).
@@ -115,13 +120,7 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 const int i = kb * 4 + iq;
-                float v = 0.f;
-                if (i < f) {
-                    float suf = 0.f;
-                    for (int j = i + 1; j < f; ++j) suf += ds[j];
-                    v = expf(suf * Ah) * ds[i] * xs[i * cw + lc];
-                }
-                bop[kb] = v;
+                bop[kb] = (i < f) ? expf((pf - ps[i]) * Ah) * ds[i] * xs[i * cw + lc] : 0.f;
             }
             const int nkb = (f + 3) >> 2;
 #pragma unroll
@@ -140,15 +139,8 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
         } else {
             float wx[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float v = 0.f;
-                if (i < f) {
-                    float suf = 0.f;
-                    for (int j = i + 1; j < f; ++j) suf += ds[j];
-                    v = expf(suf * Ah) * ds[i] * xs[i * cw + lc];
-                }
-                wx[i] = v;
-            }
+            for (int i = 0; i < 16; ++i)
+                wx[i] = (i < f) ? expf((pf - ps[i]) * Ah) * ds[i] * xs[i * cw + lc] : 0.f;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -171,21 +163,15 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
 #pragma unroll
         for (int t = 0; t < TMAX; ++t) {
             if (t < T) {
-                // checkpoint read-out (S' C_t)[col], reduced over the four row groups
-                float gacc = 0.f;
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) gacc += dot4(s[nb], ld4(cs + t * R + nb * 16 + rq));
-                gacc = sum_over_row_groups(gacc);
                 const int pos = len + t;
-                float yv;
-                if (pos < f) {
-                    yv = gacc + Dh * xs[pos * cw + lc];
-                } else {
-                    // replay of entries f..pos: lane quad (jj = l/4) forms B_j . C_t and the
-                    // decayed coefficient; output lanes gather the coefficients by shuffle
+                const float xt = xs[pos * cw + lc];
+                // replay of entries f..pos (formed first: it needs only LDS, so it runs while
+                // the checkpoint loads are in flight).  Lane quad jj = l/4 forms B_j . C_t and
+                // the decayed coefficient; output lanes gather the coefficients by readlane.
+                float rep = 0.f, gdec = 1.f;
+                if (pos >= f) {
                     const int nr = pos - f + 1;
                     const int q = lane & 3;
-                    float rep = 0.f;
                     for (int jj0 = 0; jj0 < nr; jj0 += 16) {
                         const int jj = jj0 + (lane >> 2), j = f + jj;
                         float dot = 0.f;
@@ -195,20 +181,21 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
                                 dot += dot4(ld4(bs + j * RS + 16 * i + 4 * q), ld4(cs + t * R + 16 * i + 4 * q));
                         }
                         dot = quad_sum(dot);
-                        float coef = 0.f;
-                        if (jj < nr) {
-                            float suf = 0.f;
-                            for (int i = j + 1; i <= pos; ++i) suf += ds[i];
-                            coef = expf(suf * Ah) * ds[j] * dot;
-                        }
-                        const int ne = min(16, nr - jj0);
-                        for (int e = 0; e < ne; ++e)
-                            rep += readlane(coef, 4 * e) * xs[(f + jj0 + e) * cw + lc];
+                        const float coef = (jj < nr) ? expf((ps[pos] - ps[j]) * Ah) * ds[j] * dot : 0.f;
+                        // entries past pos carry a zero coefficient; their index is clamped to a
+                        // staged row so the product stays finite
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            rep += readlane(coef, 4 * e) * xs[min(f + jj0 + e, pos) * cw + lc];
                     }
-                    float Lp = 0.f;
-                    for (int i = f; i <= pos; ++i) Lp += ds[i];
-                    yv = expf(Lp * Ah) * gacc + rep + Dh * xs[pos * cw + lc];
+                    gdec = expf((ps[pos] - (f > 0 ? ps[f - 1] : 0.f)) * Ah);
                 }
+                // checkpoint read-out (S' C_t)[col], reduced over the four row groups
+                float gacc = 0.f;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) gacc += dot4(s[nb], ld4(cs + t * R + nb * 16 + rq));
+                gacc = sum_over_row_groups(gacc);
+                const float yv = (pos >= f) ? gdec * gacc + rep + Dh * xt : gacc + Dh * xt;
                 if (lane < 16) st_io<IO>(a.y, (((size_t)t * sB + b) * a.H + h) * C + col, yv);
             }
         }
@@ -231,7 +218,8 @@ static hipError_t launch_nb(const StepArgs& a, hipStream_t s)
 {
     const size_t Tr = a.T > 0 ? a.T : 1;
     const size_t R = NB * 16;
-    const size_t lds = sizeof(float) * ((size_t)a.vmax * (a.C / a.nsplit + R + 4) + Tr * R + (size_t)a.vmax);
+    const size_t VM = (16 + TMAX + 3) & ~3;
+    const size_t lds = sizeof(float) * ((size_t)a.vmax * (a.C / a.nsplit + R + 4) + Tr * R + 2 * VM);
     auto k = mamba2_step_kernel<NB, IO, TMAX, MF, RC>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -33,6 +33,7 @@ struct StageGeom {
     float* xq;           // LDS [T][R]
     float* s0;           // LDS [vmax]
     float* s1;           // LDS [vmax] or null
+    float* p0;           // LDS [vmax]: inclusive prefix sums of scalar 0, or null
 };
 
 template <int IO>
@@ -159,6 +160,12 @@ __device__ __forceinline__ void stage_publish(const Stager<IO, R>& st, int tid, 
     if (tid < G.V) {
         G.s0[tid] = __builtin_bit_cast(float, sr.s0 << sr.s0shift);
         if (G.s1) G.s1[tid] = __builtin_bit_cast(float, sr.s1);
+    }
+    // entries are at most 32 (cap + T), all in wave 0: prefix sums by a wave scan
+    if (G.p0 && tid < 64) {
+        const float v = tid < G.V ? __builtin_bit_cast(float, sr.s0 << sr.s0shift) : 0.f;
+        const float ps = scan32_inclusive(v);
+        if (tid < G.V) G.p0[tid] = ps;
     }
 }
 
