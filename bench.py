@@ -21,9 +21,16 @@ The JSON line also carries:
   gdn_read_copy_b128
                 the batch-128 GDN layer with an fp32 checkpoint and no copy,
                 an FP8 E4M3 read copy, and an MXFP4 read copy
+  fp16_checkpoint
+                both batch-256 layers with an fp16 recurrence checkpoint, and
+                the conventional kernel on an fp16 state
   cpu_baseline  the fp64 oracle on the host cores over a bounded sample
 With --sweep FILE, both layers are also timed at batch 1..512 (replay and
-conventional), one JSON line per point in FILE.
+conventional, eagerly and as HIP-graph replays), one JSON line per point in FILE.
+
+Timing: `value` and `ms_per_step` come from K steps launched back to back
+between two events; the per-launch durations behind `roofline` come from a
+second pass of K steps with an event pair around every launch.
 """
 from __future__ import annotations
 
@@ -40,23 +47,24 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "mamba2_step_b256_traffic.txt")  # written by profsum
 KERNEL_SOURCES = [os.path.join(ROOT, "hybrid_decode_replay_amd", "csrc", f)
-                  for f in ("mamba2.hip", "common.hpp", "stage.hpp", "rc.hpp")]
+                  for f in ("mamba2_kernel.hpp", "mamba2.hip", "ckpt.hpp", "common.hpp", "stage.hpp", "rc.hpp")]
 
 MAMBA2 = dict(H=128, G=8, C=64, R=128)     # heads, groups, head dim P, state dim N
 GDN = dict(H=32, G=32, C=128, R=128)       # heads, q/k heads, d_v, d_k
 
 
-def algorithmic_bytes(kind, H, G, C, R, cap=16, io_bytes=2, read_copy=None):
+def algorithmic_bytes(kind, H, G, C, R, cap=16, io_bytes=2, read_copy=None, ckpt_bytes=4):
     """(replay, conventional) bytes per sequence-token.
 
     Replay, averaged over a full window of `cap` steps with lockstep flushes: the
     checkpoint is read every step and written once per window; the current inputs are
     read; the new entry is written; on average (cap-1)/2 prior entries are read; the
     output is written.  With a read copy, the cap-1 non-flush steps read the copy and
-    the flush step reads and writes fp32 and writes the copy: per token copy + S/8 in
-    place of S + S/cap.  Conventional: state read and written every token, inputs,
-    output.  Entries: Mamba-2 x, B, dt; GDN k, v and the fp32 gates."""
-    S = H * C * R * 4
+    the flush step reads and writes the checkpoint and writes the copy: per token copy +
+    S/8 in place of S + S/cap.  Conventional: state read and written every token,
+    inputs, output.  Entries: Mamba-2 x, B, dt; GDN k, v and the fp32 gates.  S is the
+    checkpoint (and conventional state) at ckpt_bytes per element."""
+    S = H * C * R * ckpt_bytes
     if kind == "mamba2":
         entry = (H * C + G * R + H) * io_bytes
         inp = (H * C + 2 * G * R + H) * io_bytes
@@ -130,16 +138,17 @@ def cpu_baseline(H, G, P, N, budget_s=10.0, max_s=30.0):
 class Layer:
     """Device-side state, parameters and pre-drawn inputs of one synthetic layer."""
 
-    def __init__(self, rb, synth, torch, dev, kind, B, steps, seed, cap=16, read_copy=None):
+    def __init__(self, rb, synth, torch, dev, kind, B, steps, seed, cap=16, read_copy=None, ckpt="f32"):
         self.rb, self.torch, self.dev, self.kind, self.B = rb, torch, dev, kind, B
         shp = MAMBA2 if kind == "mamba2" else GDN
         self.H, self.G, self.C, self.R = shp["H"], shp["G"], shp["C"], shp["R"]
         self.cap = cap
         self.read_copy = read_copy
+        self.ckpt = ckpt
         rc = {None: rb.NONE, "fp8": rb.FP8_E4M3, "mxfp4": rb.MXFP4}[read_copy]
         self.cfg = rb.make_config(rb.MAMBA2 if kind == "mamba2" else rb.GDN, B, self.H, self.G, self.C, self.R,
-                                  cap, rb.BF16, read_copy=rc)
-        self.S0 = synth.checkpoint_device(seed, (B, self.H, self.C, self.R), dev)
+                                  cap, rb.BF16, read_copy=rc, ckpt_dtype=rb.F16 if ckpt == "f16" else rb.F32)
+        self.S0 = synth.checkpoint_device(seed, (B, self.H, self.C, self.R), dev).to(rb.ckpt_torch_dtype(self.cfg))
         if kind == "mamba2":
             A, D = synth.mamba2_params(seed, self.H)
             self.params = {"A": torch.from_numpy(A).to(dev), "D": torch.from_numpy(D).to(dev)}
@@ -153,7 +162,9 @@ class Layer:
 
 
 def time_replay_decode(L, K, W, stream):
-    """K timed decode steps after W warm-up steps; per-launch HIP events on the launch stream."""
+    """W warm-up steps, then K timed steps back to back (the throughput), then K more steps
+    with a HIP event pair around every launch on the launch stream (per-launch durations,
+    split into flush and non-flush steps).  The second pass reuses the same inputs."""
     rb, torch = L.rb, L.torch
     st = rb.ReplayState(L.cfg, device=L.dev)
     st.load_checkpoint(L.S0)
@@ -161,25 +172,34 @@ def time_replay_decode(L, K, W, stream):
     ins = [L.inputs(t) for t in range(K + W)]
     lib, sp = rb.lib(), rb.ctypes.c_void_p(stream.cuda_stream)
     yp = [rb.ctypes.c_void_p(ys[i].data_ptr()) for i in range(2)]
+    n = [0]                                   # steps issued so far (the flush cadence)
 
     def step(t):
         s = lib.replay_decode_step(st.h, rb.ctypes.byref(ins[t]), yp[t & 1], sp)
         if s != rb.OK:
             raise rb.ReplayError(s, "replay_decode_step")
+        n[0] += 1
 
     for t in range(W):
         step(t)
     torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(K):
+        step(W + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    total = e0.elapsed_time(e1)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    first = n[0]
     for i in range(K):
         ev[i][0].record(stream)
         step(W + i)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     per = [s.elapsed_time(e) for s, e in ev]
-    total = ev[0][0].elapsed_time(ev[-1][1])
-    flush = [p for i, p in enumerate(per) if (W + i) % L.cap == L.cap - 1]
-    nonflush = [p for i, p in enumerate(per) if (W + i) % L.cap != L.cap - 1]
+    flush = [p for i, p in enumerate(per) if (first + i) % L.cap == L.cap - 1]
+    nonflush = [p for i, p in enumerate(per) if (first + i) % L.cap != L.cap - 1]
     return {"steps": K, "total_ms": total, "avg_launch_ms": sum(per) / K,
             "flush_ms": sum(flush) / max(1, len(flush)), "nonflush_ms": sum(nonflush) / max(1, len(nonflush))}
 
@@ -256,7 +276,8 @@ def time_graph(L, conventional, n=64, reps=8):
 
 
 def decode_report(L, r, conv_ms):
-    replay_b, conv_b = algorithmic_bytes(L.kind, L.H, L.G, L.C, L.R, L.cap, read_copy=L.read_copy)
+    replay_b, conv_b = algorithmic_bytes(L.kind, L.H, L.G, L.C, L.R, L.cap, read_copy=L.read_copy,
+                                         ckpt_bytes=2 if L.ckpt == "f16" else 4)
     ms = r["total_ms"] / r["steps"]
     ach = replay_b * L.B / (r["avg_launch_ms"] / 1e3) / 1e9
     out = {"batch": L.B, "tokens_per_s": round(L.B / (ms / 1e3), 1), "ms_per_step": round(ms, 5),
@@ -424,6 +445,15 @@ def main():
             del Lr
             torch.cuda.empty_cache()
         out["gdn_read_copy_b128"] = lp
+        # fp16 recurrence checkpoint at batch 256 (the conventional baseline on an fp16 state)
+        f16 = {}
+        for kind, seed in (("mamba2", 6), ("gdn", 7)):
+            Lh = Layer(rb, synth, torch, dev, kind, B, 256 + 32 + 4, seed=seed, ckpt="f16")
+            rh = time_replay_decode(Lh, 256, 32, stream)
+            f16[kind] = decode_report(Lh, rh, time_conv_decode(Lh, 64, stream))
+            del Lh
+            torch.cuda.empty_cache()
+        out["fp16_checkpoint"] = f16
 
     if args.sweep:
         with open(args.sweep, "w") as f:

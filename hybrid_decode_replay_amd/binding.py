@@ -147,6 +147,12 @@ def _io_torch_dtype(io):
     return torch.bfloat16 if io == BF16 else torch.float32
 
 
+def ckpt_torch_dtype(cfg: ReplayConfig):
+    """torch dtype of logical checkpoints and conventional-baseline states for `cfg`."""
+    torch = _torch()
+    return torch.float16 if cfg.ckpt_dtype == F16 else torch.float32
+
+
 def make_inputs(cfg: ReplayConfig, tensors: dict, params: dict | None = None) -> ReplayInputs:
     """Pack a dict of device tensors into ReplayInputs.
 
@@ -190,6 +196,7 @@ class ReplayState:
                                        ctypes.byref(h)), "replay_state_alloc")
         self.h = h
         self.iot = _io_torch_dtype(cfg.io_dtype)
+        self.ckt = ckpt_torch_dtype(cfg)
 
     def __del__(self):
         h = getattr(self, "h", None)
@@ -213,15 +220,15 @@ class ReplayState:
 
     # -- checkpoint I/O
     def load_checkpoint(self, S):
-        torch = _torch()
-        S = S.to(device=self.device, dtype=torch.float32).contiguous()
+        """S: logical [B][H][rows][cols]; converted to the checkpoint dtype (torch's RNE cast) if needed."""
+        S = S.to(device=self.device, dtype=self.ckt).contiguous()
         assert tuple(S.shape) == self.ckpt_shape
         _check(_lib.replay_load_checkpoint(self.h, _ptr(S), _stream()), "replay_load_checkpoint")
         self._keep = S
 
     def read_checkpoint(self):
         torch = _torch()
-        out = torch.empty(self.ckpt_shape, dtype=torch.float32, device=self.device)
+        out = torch.empty(self.ckpt_shape, dtype=self.ckt, device=self.device)
         _check(_lib.replay_read_checkpoint(self.h, _ptr(out), _stream()), "replay_read_checkpoint")
         return out
 
@@ -284,7 +291,7 @@ def conv_decode_step(cfg: ReplayConfig, S, tokens: dict, params: dict | None = N
     if y is None:
         y = torch.empty((1, cfg.batch, cfg.nheads, cfg.head_dim), dtype=_io_torch_dtype(cfg.io_dtype), device=S.device)
     ri = make_inputs(cfg, tokens, params)
-    _check(_lib.replay_conv_decode_step(ctypes.byref(cfg), _ptr(S, torch.float32, "S"), ctypes.byref(ri),
+    _check(_lib.replay_conv_decode_step(ctypes.byref(cfg), _ptr(S, ckpt_torch_dtype(cfg), "S"), ctypes.byref(ri),
                                         _ptr(y), _stream()), "replay_conv_decode_step")
     return y
 
@@ -294,15 +301,17 @@ def conv_spec_step(cfg: ReplayConfig, S, snaps, k: int, drafts: dict, params: di
     if y is None:
         y = torch.empty((k, cfg.batch, cfg.nheads, cfg.head_dim), dtype=_io_torch_dtype(cfg.io_dtype), device=S.device)
     ri = make_inputs(cfg, drafts, params)
-    _check(_lib.replay_conv_spec_step(ctypes.byref(cfg), _ptr(S, torch.float32, "S"), _ptr(snaps, torch.float32, "snaps"),
+    ckt = ckpt_torch_dtype(cfg)
+    _check(_lib.replay_conv_spec_step(ctypes.byref(cfg), _ptr(S, ckt, "S"), _ptr(snaps, ckt, "snaps"),
                                       int(k), ctypes.byref(ri), _ptr(y), _stream()), "replay_conv_spec_step")
     return y
 
 
 def conv_spec_restore(cfg: ReplayConfig, S, snaps, k: int, accepted):
     torch = _torch()
-    _check(_lib.replay_conv_spec_restore(ctypes.byref(cfg), _ptr(S, torch.float32, "S"),
-                                         _ptr(snaps, torch.float32, "snaps"), int(k),
+    ckt = ckpt_torch_dtype(cfg)
+    _check(_lib.replay_conv_spec_restore(ctypes.byref(cfg), _ptr(S, ckt, "S"),
+                                         _ptr(snaps, ckt, "snaps"), int(k),
                                          _ptr(accepted, torch.int32, "accepted"), _stream()),
            "replay_conv_spec_restore")
 

@@ -1,5 +1,6 @@
 // aux.hip -- bookkeeping, layout conversion and measurement kernels.
 #include "common.hpp"
+#include "ckpt.hpp"
 #include "internal.hpp"
 #include "rc.hpp"
 
@@ -84,52 +85,72 @@ __device__ __forceinline__ size_t frag_to_logical(size_t q, int C, int R)
     return tile * (size_t)C * R + (size_t)c * R + r;
 }
 
-__global__ void tiles_to_logical_kernel(const float* ck, float* out, size_t n4, int C, int R)
+// One thread per lane-block q (4 consecutive values of a logical row); T is
+// the storage type (float or a 16-bit word).
+template <int CK, class T>
+__global__ void tiles_to_logical_kernel(const T* ck, T* out, size_t n4, int C, int R)
 {
     const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (q >= n4) return;
-    st4(out + frag_to_logical(q, C, R), ld4(ck + q * 4));
+    const T* src = ck + ckpt_elem_offset<CK>(q, R >> 4);
+    T* dst = out + frag_to_logical(q, C, R);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = src[i];
 }
 
-__global__ void logical_to_tiles_kernel(const float* in, float* ck, size_t n4, int C, int R)
+template <int CK, class T>
+__global__ void logical_to_tiles_kernel(const T* in, T* ck, size_t n4, int C, int R)
 {
     const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (q >= n4) return;
-    st4(ck + q * 4, ld4(in + frag_to_logical(q, C, R)));
+    const T* src = in + frag_to_logical(q, C, R);
+    T* dst = ck + ckpt_elem_offset<CK>(q, R >> 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = src[i];
 }
 
-hipError_t launch_tiles_to_logical(const float* ckpt, float* out, int tiles, int C, int R, hipStream_t s)
+hipError_t launch_tiles_to_logical(const void* ckpt, void* out, int tiles, int C, int R, int ck, hipStream_t s)
 {
     const size_t n4 = (size_t)tiles * C * R / 4;
-    hipLaunchKernelGGL(tiles_to_logical_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, ckpt, out, n4, C, R);
+    const dim3 grid((unsigned)((n4 + 255) / 256)), block(256);
+    if (ck == CK_F16)
+        hipLaunchKernelGGL((tiles_to_logical_kernel<CK_F16, uint16_t>), grid, block, 0, s,
+                           static_cast<const uint16_t*>(ckpt), static_cast<uint16_t*>(out), n4, C, R);
+    else
+        hipLaunchKernelGGL((tiles_to_logical_kernel<CK_F32, float>), grid, block, 0, s,
+                           static_cast<const float*>(ckpt), static_cast<float*>(out), n4, C, R);
     return hipGetLastError();
 }
 
-hipError_t launch_logical_to_tiles(const float* in, float* ckpt, int tiles, int C, int R, hipStream_t s)
+hipError_t launch_logical_to_tiles(const void* in, void* ckpt, int tiles, int C, int R, int ck, hipStream_t s)
 {
     const size_t n4 = (size_t)tiles * C * R / 4;
-    hipLaunchKernelGGL(logical_to_tiles_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, in, ckpt, n4, C, R);
+    const dim3 grid((unsigned)((n4 + 255) / 256)), block(256);
+    if (ck == CK_F16)
+        hipLaunchKernelGGL((logical_to_tiles_kernel<CK_F16, uint16_t>), grid, block, 0, s,
+                           static_cast<const uint16_t*>(in), static_cast<uint16_t*>(ckpt), n4, C, R);
+    else
+        hipLaunchKernelGGL((logical_to_tiles_kernel<CK_F32, float>), grid, block, 0, s,
+                           static_cast<const float*>(in), static_cast<float*>(ckpt), n4, C, R);
     return hipGetLastError();
 }
 
 // ---- read copy: quantize the fragment-ordered checkpoint, export codes ---------
 // One wave per (tile, 16-column strip), in the same lane order as the replay
 // kernels, so the quantizer is the one the flush path uses.
-template <int NB, int RC>
-__global__ __launch_bounds__(256) void quantize_rc_kernel(float* ckpt, uint8_t* codes, uint8_t* scales,
+template <int NB, int RC, int CK>
+__global__ __launch_bounds__(256) void quantize_rc_kernel(void* ckpt, uint8_t* codes, uint8_t* scales,
                                                           size_t nstrips, int round_ckpt)
 {
     const size_t strip = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (strip >= nstrips) return;                  // whole waves leave together
     f32x4 s[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) s[nb] = ld4(ckpt + ((strip * NB + nb) * 64 + lane) * 4);
+    ckpt_load<NB, CK>(ckpt, strip, lane, s);
     rc_store<NB, RC>(codes, scales, strip, lane, s);
     if (round_ckpt) {                              // checkpoint kept at the copy's precision
         rc_roundtrip<NB, RC>(s);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) st4(ckpt + ((strip * NB + nb) * 64 + lane) * 4, s[nb]);
+        ckpt_store<NB, CK>(ckpt, strip, lane, s);
     }
 }
 
@@ -174,24 +195,24 @@ __global__ __launch_bounds__(256) void rc_to_logical_kernel(const uint8_t* codes
     }
 }
 
-template <int RC>
-static hipError_t rc_dispatch(bool quantize, float* ckpt, const uint8_t* codes_in, const uint8_t* scales_in,
+template <int RC, int CK>
+static hipError_t rc_dispatch(bool quantize, void* ckpt, const uint8_t* codes_in, const uint8_t* scales_in,
                               uint8_t* codes, uint8_t* scales, int tiles, int C, int R, int round_ckpt, hipStream_t s)
 {
     const size_t nstrips = (size_t)tiles * (C / 16);
     const dim3 grid((unsigned)((nstrips + 3) / 4)), block(256);
 #define RS_RC_CASE(NBV)                                                                                  \
     case NBV * 16:                                                                                       \
-        if (quantize) hipLaunchKernelGGL((quantize_rc_kernel<NBV, RC>), grid, block, 0, s, ckpt, codes, scales, nstrips, \
-                                         round_ckpt);                                                   \
+        if (quantize) hipLaunchKernelGGL((quantize_rc_kernel<NBV, RC, CK>), grid, block, 0, s, ckpt, codes, scales,   \
+                                         nstrips, round_ckpt);                                          \
         else hipLaunchKernelGGL((rc_to_logical_kernel<NBV, RC>), grid, block, 0, s, codes_in, scales_in, codes, scales,    \
                                 nstrips, C);                                                             \
         return hipGetLastError();
     switch (R) {
         case 16:
             if constexpr (RC == RC_FP8) {
-                if (quantize) hipLaunchKernelGGL((quantize_rc_kernel<1, RC>), grid, block, 0, s, ckpt, codes, scales, nstrips,
-                                                 round_ckpt);
+                if (quantize) hipLaunchKernelGGL((quantize_rc_kernel<1, RC, CK>), grid, block, 0, s, ckpt, codes, scales,
+                                                 nstrips, round_ckpt);
                 else hipLaunchKernelGGL((rc_to_logical_kernel<1, RC>), grid, block, 0, s, codes_in, scales_in, codes, scales,
                                         nstrips, C);
                 return hipGetLastError();
@@ -206,19 +227,27 @@ static hipError_t rc_dispatch(bool quantize, float* ckpt, const uint8_t* codes_i
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_quantize_read_copy(float* ckpt, uint8_t* codes, uint8_t* scales, int tiles, int C, int R, int rc,
-                                     bool round_ckpt, hipStream_t s)
+hipError_t launch_quantize_read_copy(void* ckpt, uint8_t* codes, uint8_t* scales, int tiles, int C, int R, int rc,
+                                     int ck, bool round_ckpt, hipStream_t s)
 {
-    if (rc == RC_FP8) return rc_dispatch<RC_FP8>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, round_ckpt, s);
-    if (rc == RC_MXFP4) return rc_dispatch<RC_MXFP4>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, round_ckpt, s);
+    if (ck == CK_F16) {
+        if (round_ckpt) return hipErrorInvalidValue;     // the quantized-checkpoint variant keeps fp32 storage
+        if (rc == RC_FP8) return rc_dispatch<RC_FP8, CK_F16>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, 0, s);
+        if (rc == RC_MXFP4) return rc_dispatch<RC_MXFP4, CK_F16>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, 0, s);
+        return hipErrorInvalidValue;
+    }
+    if (rc == RC_FP8)
+        return rc_dispatch<RC_FP8, CK_F32>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, round_ckpt, s);
+    if (rc == RC_MXFP4)
+        return rc_dispatch<RC_MXFP4, CK_F32>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, round_ckpt, s);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_read_copy_to_logical(const uint8_t* codes, const uint8_t* scales, uint8_t* codes_out,
                                        uint8_t* scales_out, int tiles, int C, int R, int rc, hipStream_t s)
 {
-    if (rc == RC_FP8) return rc_dispatch<RC_FP8>(false, nullptr, codes, scales, codes_out, scales_out, tiles, C, R, 0, s);
-    if (rc == RC_MXFP4) return rc_dispatch<RC_MXFP4>(false, nullptr, codes, scales, codes_out, scales_out, tiles, C, R, 0, s);
+    if (rc == RC_FP8) return rc_dispatch<RC_FP8, CK_F32>(false, nullptr, codes, scales, codes_out, scales_out, tiles, C, R, 0, s);
+    if (rc == RC_MXFP4) return rc_dispatch<RC_MXFP4, CK_F32>(false, nullptr, codes, scales, codes_out, scales_out, tiles, C, R, 0, s);
     return hipErrorInvalidValue;
 }
 

@@ -1,0 +1,94 @@
+// ckpt.hpp -- fragment-ordered checkpoint strips in fp32 or fp16 storage.
+//
+// A strip is the 16-column slice of a (b, h) tile that one wave owns: NB
+// 16x16 blocks along the reduction axis, lane l holding rows 4(l/16)..+3 of
+// column l%16 of every block (the v_mfma_f32_16x16x4_f32 accumulator layout,
+// common.hpp).  Storage:
+//   fp32  one 16-byte word per block and lane at float4 index
+//         (strip*NB + nb)*64 + lane;
+//   fp16  blocks 2p and 2p+1 share one 16-byte word per lane (4 halves each)
+//         at 16-byte index (strip*NB/2 + p)*64 + lane; a one-block strip
+//         (NB = 1) uses an 8-byte word per lane at index strip*64 + lane.
+// Either way a wave moves a strip as contiguous 1 KiB rows of 128-bit words
+// (512 B rows for NB = 1 in fp16).  Values are fp32 in registers; an fp16
+// store rounds to nearest even.
+#pragma once
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace rs {
+
+typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 h4_to_f32(u32x2 u) {
+    return __builtin_convertvector(__builtin_bit_cast(h16x4, u), f32x4);
+}
+__device__ __forceinline__ u32x2 f32_to_h4(f32x4 v) {
+    return __builtin_bit_cast(u32x2, __builtin_convertvector(v, h16x4));
+}
+
+template <int NB, int CK>
+__device__ __forceinline__ void ckpt_load(const void* ck, size_t strip, int lane, f32x4 (&s)[NB])
+{
+    if constexpr (CK == CK_F32) {
+        const float* p = static_cast<const float*>(ck) + (strip * NB * 64 + lane) * 4;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) s[nb] = ld4_stream(p + (size_t)nb * 256);
+    } else if constexpr (NB == 1) {
+        const u32x2* p = static_cast<const u32x2*>(ck) + strip * 64 + lane;
+        s[0] = h4_to_f32(__builtin_nontemporal_load(p));
+    } else {
+        const u32x4* p = static_cast<const u32x4*>(ck) + strip * (NB / 2) * 64 + lane;
+#pragma unroll
+        for (int q = 0; q < NB / 2; ++q) {
+            const u32x4 w = __builtin_nontemporal_load(p + q * 64);
+            s[2 * q] = h4_to_f32(u32x2{w.x, w.y});
+            s[2 * q + 1] = h4_to_f32(u32x2{w.z, w.w});
+        }
+    }
+}
+
+template <int NB, int CK>
+__device__ __forceinline__ void ckpt_store(void* ck, size_t strip, int lane, const f32x4 (&s)[NB])
+{
+    if constexpr (CK == CK_F32) {
+        float* p = static_cast<float*>(ck) + (strip * NB * 64 + lane) * 4;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) st4_stream(p + (size_t)nb * 256, s[nb]);
+    } else if constexpr (NB == 1) {
+        u32x2* p = static_cast<u32x2*>(ck) + strip * 64 + lane;
+        __builtin_nontemporal_store(f32_to_h4(s[0]), p);
+    } else {
+        u32x4* p = static_cast<u32x4*>(ck) + strip * (NB / 2) * 64 + lane;
+#pragma unroll
+        for (int q = 0; q < NB / 2; ++q) {
+            const u32x2 lo = f32_to_h4(s[2 * q]), hi = f32_to_h4(s[2 * q + 1]);
+            __builtin_nontemporal_store(u32x4{lo.x, lo.y, hi.x, hi.y}, p + q * 64);
+        }
+    }
+}
+
+// Registers -> the values the store will keep (identity for fp32).
+template <int NB, int CK>
+__device__ __forceinline__ void ckpt_round(f32x4 (&s)[NB])
+{
+    if constexpr (CK == CK_F16) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) s[nb] = h4_to_f32(f32_to_h4(s[nb]));
+    }
+}
+
+// Element offset of the first of the 4 values of lane-block q, q = (strip*NB +
+// nb)*64 + lane (the fp32 float4 index), in the storage of checkpoint dtype CK.
+template <int CK>
+__device__ __forceinline__ size_t ckpt_elem_offset(size_t q, int NB)
+{
+    if (CK == CK_F32 || NB == 1) return q * 4;
+    const size_t lane = q & 63, sb = q >> 6;       // sb = strip*NB + nb
+    const size_t strip = sb / NB;
+    const int nb = (int)(sb - strip * NB);
+    return ((strip * (NB / 2) + nb / 2) * 64 + lane) * 8 + (nb & 1) * 4;
+}
+
+}  // namespace rs

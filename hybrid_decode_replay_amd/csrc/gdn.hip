@@ -1,318 +1,11 @@
-// gdn.hip -- replayed Gated DeltaNet decode step for gfx950 (CDNA4).
-//
-// Layer: per head, S (d_v x d_k) evolves as S <- alpha S (I - beta k k^T) + beta v k^T
-// and o = scale S q (gated delta rule).  The checkpoint tile is fragment-
-// ordered (common.hpp) with the reduction axis r = d_k and the output axis
-// c = d_v.  The value rows of a head are split over workgroups of at most
-// four waves (d_v = 128: two workgroups of 64 rows) so that several
-// workgroups share a CU; wave w owns 16 value rows.  Each slice recomputes the
-// small per-head quantities (chains, Gram matrix, inverse) itself.
-//
-// Per launch and sequence the virtual entry list is the committed buffer
-// entries followed by the T new tokens; the first f entries are folded into
-// the checkpoint (the filling step, [TR] "NVIDIA ve Dao AI Lab ...", section
-// "ReplaySSM nasil calisir?"), the rest are replayed on top of it for the
-// outputs ([DE] "ReplaySSM beschleunigt das Decoding ...", section "Wie es
-// funktioniert": output from the checkpoint plus the buffered inputs).
-//
-// Output of a token at position pos, by the adjoint chain: r = q; for
-// i = pos down to f: c_i = beta_i (k_i . r), r <- alpha_i (r - c_i k_i); then
-//     o = scale (S' r + sum_i c_i v_i).
-// One checkpoint product per token; the chain needs only the buffered k, alpha,
-// beta and costs O(d_k) per entry.  The drafts of a speculative append get one
-// chain each from the same checkpoint read (output-only evaluation, [TR]
-// section "Durum trafigini azaltma ve rollback'in basitlestirilmesi").
-//
-// Fold of entries 0..f-1 in WY form (the intermediate state from small matrix
-// products, same section), with P_i = alpha_0 ... alpha_i:
-//     W   = K S0^T                       (f x d_v; MFMA, S0 straight from registers)
-//     A_ij = beta_i (alpha_{j+1} ... alpha_i) (k_i . k_j)   for j < i
-//     U   = (I + A)^{-1} diag(beta) (V - diag(P) W)      (16 x 16 inverse, then MFMA)
-//     S'  = P_{f-1} S0 + sum_i (alpha_{i+1} ... alpha_{f-1}) u_i k_i^T   (MFMA)
-// Decay factors are formed as products of the gates, never as quotients.
-#include "common.hpp"
-#include "internal.hpp"
-#include "rc.hpp"
-#include "stage.hpp"
+// gdn.hip -- Gated DeltaNet replay step kernels with an fp32 checkpoint.
+#include "gdn_kernel.hpp"
 
 namespace rs {
 
-template <int NB, int IO, int TMAX, int RC>
-__global__ __launch_bounds__(1024) void gdn_step_kernel(StepArgs a)
+hipError_t launch_gdn_step_f32(const StepArgs& a, int io, int rc, hipStream_t s)
 {
-    extern __shared__ float lds[];
-    constexpr int R = NB * 16;                  // d_k
-    constexpr int RS = R + 4;
-    constexpr int PRE = 4;
-    constexpr int RPL = (R + 63) / 64;          // chain elements per lane
-    const int C = a.C;                          // d_v
-    const TileIdx tix = tile_of(xcd_tile_index(), a.H, a.nsplit);
-    const int b = tix.b, h = tix.h, tile = b * a.H + h;
-    const int g = h / a.hpg;
-    const int cw = C / a.nsplit, c0 = tix.sp * cw;   // this workgroup's output columns
-    const int tid = threadIdx.x, nthr = blockDim.x;
-    const int w = tid >> 6, lane = tid & 63, waves = nthr >> 6;
-    const int lc = 16 * w + (lane & 15);             // local output column
-    const int col = c0 + lc;                          // global output column
-    const int rq = 4 * (lane >> 4);
-    const int l16 = lane & 15, lq = lane >> 4;
-    const size_t sB = (size_t)a.B;
-
-    const StepPlan p = plan_step(a, b, h == 0 && tix.sp == 0 && tid == 0);
-    if (a.mode == MODE_FLUSH && p.f == 0) return;
-    const int f = p.f, len = p.len, V = p.V, T = a.T;
-    const int Tr = T > 0 ? T : 1, vmax = a.vmax;
-
-    // ---- LDS partition (floats)
-    float* vs = lds;                          // [vmax][cw]  entry v rows (own columns)
-    float* ks = vs + (size_t)vmax * cw;       // [vmax][RS]  entry k rows
-    float* qs = ks + (size_t)vmax * RS;       // [Tr][R]     query rows
-    float* rz = qs + (size_t)Tr * R;          // [Tr][R]     chain results r_0
-    float* al = rz + (size_t)Tr * R;          // [vmax]      alpha
-    float* be = al + vmax;                    // [vmax]      beta
-    float* cc = be + vmax;                    // [Tr][vmax]  chain coefficients c_i
-    float* ti = cc + (size_t)Tr * vmax;       // [16][17]    (I + A)^{-1}
-
-    StageGeom G;
-    G.bufc = a.bufc; G.bufr = a.bufr; G.bufs0 = a.bufs0; G.bufs1 = a.bufs1;
-    G.in_c = a.in_c; G.in_r = a.in_r; G.in_q = a.in_q; G.in_s0 = a.in_s0; G.in_s1 = a.in_s1;
-    G.bank_c = a.bank_c; G.bank_r = a.bank_r; G.bank_s = a.bank_s;
-    G.hc = (size_t)b * a.H + h; G.gr = (size_t)b * a.G + g;
-    G.b = b; G.h = h; G.g = g; G.B = a.B; G.H = a.H; G.G = a.G; G.cap = a.cap; G.C = C;
-    G.c0 = c0; G.cw = cw;
-    G.len = len; G.bank = p.bank; G.V = V; G.T = T;
-    G.xc = vs; G.xr = ks; G.xq = qs; G.s0 = al; G.s1 = be; G.p0 = nullptr;
-
-    // ---- 1. entry chunks ahead of the checkpoint stream, 2. checkpoint tile
-    const Stager<IO, R> stg(G);
-    uint4 pre[PRE];
-    ScalarRaw sr;
-    stage_issue<IO, R, PRE, false>(stg, tid, nthr, pre, sr);
-    // a step that folds nothing reads the low-precision copy when there is one
-    const size_t strip_index = (size_t)tile * (C >> 4) + (c0 >> 4) + w;
-    float* ckw = a.ckpt + (strip_index * NB * 64 + lane) * 4;
-    f32x4 s[NB];
-    bool from_copy = false;
-    if constexpr (RC != RC_NONE) from_copy = (f == 0);
-    if (from_copy) {
-        if constexpr (RC != RC_NONE) rc_load<NB, RC>(a.rcopy, a.rscale, strip_index, lane, s);
-    } else {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) s[nb] = ld4_stream(ckw + (size_t)nb * 256);
-    }
-    stage_publish<IO, R, PRE>(stg, tid, nthr, pre, sr);
-    __syncthreads();
-
-    // ---- 3. fold the first f entries (WY form on MFMA)
-    if (f > 0) {
-        // W[i][v] = (S0 k_i)[v]; lane result rows i = lq*4 + r, column col
-        f32x4 W = {0.f, 0.f, 0.f, 0.f};
-        const bool arow = l16 < f;
-#pragma unroll
-        for (int jb = 0; jb < NB; ++jb) {
-            const f32x4 kv = arow ? ld4(ks + l16 * RS + jb * 16 + rq) : f32x4{0.f, 0.f, 0.f, 0.f};
-            W = mfma16x16x4(kv.x, s[jb].x, W);
-            W = mfma16x16x4(kv.y, s[jb].y, W);
-            W = mfma16x16x4(kv.z, s[jb].z, W);
-            W = mfma16x16x4(kv.w, s[jb].w, W);
-        }
-        if (w == 0) {
-            // Gram k_i . k_j on MFMA (lane result rows i = lq*4 + r, column j = l16)
-            f32x4 gm = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int d = 0; d < R / 4; ++d) {
-                const float kv = arow ? ks[l16 * RS + 4 * d + lq] : 0.f;
-                gm = mfma16x16x4(kv, kv, gm);
-            }
-            // strictly lower triangle of A, written to ti as a scratch matrix
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = lq * 4 + r, j = l16;
-                float v = 0.f;
-                if (j < i && i < f) {
-                    float dec = 1.f;
-                    for (int m = j + 1; m <= i; ++m) dec *= al[m];
-                    v = be[i] * dec * gm[r];
-                }
-                ti[i * 17 + j] = v;
-            }
-            wave_lds_sync();
-            // column c of (I + A)^{-1} by forward substitution (lanes 0..15)
-            float tc[16];
-            if (lane < 16) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float acc = (i == lane) ? 1.f : 0.f;
-#pragma unroll
-                    for (int j = 0; j < i; ++j) acc -= ti[i * 17 + j] * tc[j];
-                    tc[i] = acc;
-                }
-            }
-            // all reads of the scratch matrix are done before it is overwritten
-            wave_lds_sync();
-            if (lane < 16) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) ti[i * 17 + lane] = tc[i];
-            }
-        }
-        __syncthreads();
-
-        // rhs[i][v] = beta_i (v_i[v] - P_i W[i][v]) for i < f
-        f32x4 rhs;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = lq * 4 + r;
-            float v = 0.f;
-            if (i < f) {
-                float P = 1.f;
-                for (int m = 0; m <= i; ++m) P *= al[m];
-                v = be[i] * (vs[i * cw + lc] - P * W[r]);
-            }
-            rhs[r] = v;
-        }
-        // U = (I + A)^{-1} rhs, then scaled by the decay from entry i to the end of the fold
-        f32x4 U = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) U = mfma16x16x4(ti[l16 * 17 + lq * 4 + r], rhs[r], U);
-        float decay = 1.f;
-        for (int m = 0; m < f; ++m) decay *= al[m];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = lq * 4 + r;
-            float sfx = 1.f;
-            for (int m = i + 1; m < f; ++m) sfx *= al[m];
-            U[r] = (i < f) ? sfx * U[r] : 0.f;
-        }
-        // S'^T[j][v] = decay S0^T[j][v] + sum_i K[i][j] U~[i][v]
-#pragma unroll
-        for (int jb = 0; jb < NB; ++jb) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = lq * 4 + r;
-                const float kv = (i < f) ? ks[i * RS + jb * 16 + l16] : 0.f;
-                acc = mfma16x16x4(kv, U[r], acc);
-            }
-            s[jb] = decay * s[jb] + acc;
-        }
-    }
-
-    // a checkpoint kept at the copy's precision is rounded as soon as it is folded
-    if constexpr (RC != RC_NONE) {
-        if (a.qckpt && f > 0) rc_roundtrip<NB, RC>(s);
-    }
-
-    // ---- 4. adjoint chains, one per new token (spread over the waves)
-    if (a.mode != MODE_FLUSH) {
-        for (int t = w; t < T; t += waves) {
-            const int pos = len + t;
-            float r[RPL];
-#pragma unroll
-            for (int u = 0; u < RPL; ++u) {
-                const int e = lane + 64 * u;
-                r[u] = e < R ? qs[t * R + e] : 0.f;
-            }
-            for (int i = pos; i >= f; --i) {
-                float part = 0.f;
-#pragma unroll
-                for (int u = 0; u < RPL; ++u) {
-                    const int e = lane + 64 * u;
-                    if (e < R) part += ks[i * RS + e] * r[u];
-                }
-                const float c = be[i] * wave_sum_uniform(part);
-                const float alpha = al[i];
-#pragma unroll
-                for (int u = 0; u < RPL; ++u) {
-                    const int e = lane + 64 * u;
-                    if (e < R) r[u] = alpha * (r[u] - c * ks[i * RS + e]);
-                }
-                if (lane == 0) cc[t * vmax + i] = c;
-            }
-#pragma unroll
-            for (int u = 0; u < RPL; ++u) {
-                const int e = lane + 64 * u;
-                if (e < R) rz[t * R + e] = r[u];
-            }
-        }
-        __syncthreads();
-
-        // ---- 5. o_t = scale (S' r_0 + sum_i c_i v_i)
-#pragma unroll
-        for (int t = 0; t < TMAX; ++t) {
-            if (t < T) {
-                float gacc = 0.f;
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) gacc += dot4(s[nb], ld4(rz + t * R + nb * 16 + rq));
-                gacc = sum_over_row_groups(gacc);
-                const int pos = len + t;
-                float rep = 0.f;
-                for (int i = f; i <= pos; ++i) rep += cc[t * vmax + i] * vs[i * cw + lc];
-                if (lane < 16) st_io<IO>(a.y, (((size_t)t * sB + b) * a.H + h) * C + col, a.scale * (gacc + rep));
-            }
-        }
-    }
-
-    // ---- 6. single checkpoint write on a folding step
-    if (f > 0) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) st4_stream(ckw + (size_t)nb * 256, s[nb]);
-        if constexpr (RC != RC_NONE) rc_store<NB, RC>(a.rcopy, a.rscale, strip_index, lane, s);
-    }
-
-    // ---- 7. append the unfolded new tokens
-    stage_append<IO, R>(G, a.bufc, a.bufr, a.bufs0, a.bufs1, p.bank_new, f, tid, nthr, tix.sp == 0,
-                        tix.sp == 0 && h % a.hpg == 0);
-}
-
-template <int NB, int IO, int TMAX, int RC>
-static hipError_t launch_nb(const StepArgs& a, hipStream_t s)
-{
-    const size_t Tr = a.T > 0 ? a.T : 1;
-    const size_t R = NB * 16, vmax = a.vmax;
-    const size_t lds = sizeof(float) * (vmax * (a.C / a.nsplit + R + 4) + 2 * Tr * R + 2 * vmax + Tr * vmax + 16 * 17);
-    auto k = gdn_step_kernel<NB, IO, TMAX, RC>;
-    if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(k, dim3(a.B * a.H * a.nsplit), dim3(a.C / a.nsplit * 4), lds, s, a);
-    return hipGetLastError();
-}
-
-template <int IO, int TMAX, int RC>
-static hipError_t launch_io(const StepArgs& a, hipStream_t s)
-{
-    switch (a.R) {
-        case 16:
-            if constexpr (RC != RC_MXFP4) return launch_nb<1, IO, TMAX, RC>(a, s);
-            return hipErrorInvalidValue;     // MXFP4 groups need 32 rows
-        case 32: return launch_nb<2, IO, TMAX, RC>(a, s);
-        case 64: return launch_nb<4, IO, TMAX, RC>(a, s);
-        case 128: return launch_nb<8, IO, TMAX, RC>(a, s);
-        case 256: return launch_nb<16, IO, TMAX, RC>(a, s);
-    }
-    return hipErrorInvalidValue;
-}
-
-template <int TMAX, int RC>
-static hipError_t launch_t(const StepArgs& a, int io, hipStream_t s)
-{
-    return io == IO_BF16 ? launch_io<IO_BF16, TMAX, RC>(a, s) : launch_io<IO_F32, TMAX, RC>(a, s);
-}
-
-template <int TMAX>
-static hipError_t launch_tm(const StepArgs& a, int io, int rc, hipStream_t s)
-{
-    if (rc == RC_FP8) return launch_t<TMAX, RC_FP8>(a, io, s);
-    if (rc == RC_MXFP4) return launch_t<TMAX, RC_MXFP4>(a, io, s);
-    return launch_t<TMAX, RC_NONE>(a, io, s);
-}
-
-hipError_t launch_gdn_step(const StepArgs& a, int io, int rc, hipStream_t s)
-{
-    if (a.T <= 1) return launch_tm<1>(a, io, rc, s);
-    if (a.T <= 4) return launch_tm<4>(a, io, rc, s);
-    return launch_tm<16>(a, io, rc, s);
+    return gdn_launch<CK_F32>(a, io, rc, s);
 }
 
 }  // namespace rs

@@ -53,6 +53,8 @@ uint64_t align256(uint64_t x) { return (x + 255) & ~(uint64_t)255; }
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 int io_bytes(const replay_config* c) { return c->io_dtype == REPLAY_BF16 ? 2 : 4; }
+int ckpt_bytes(const replay_config* c) { return c->ckpt_dtype == REPLAY_F16 ? 2 : 4; }
+int ck_kind(const replay_config* c) { return c->ckpt_dtype == REPLAY_F16 ? rs::CK_F16 : rs::CK_F32; }
 
 replay_status check_config(const replay_config* c)
 {
@@ -73,10 +75,8 @@ replay_status check_config(const replay_config* c)
     if ((long long)c->batch * c->nheads > (1LL << 30)) return fail(REPLAY_ERR_SHAPE, "batch * nheads too large");
     if (c->io_dtype != REPLAY_F32 && c->io_dtype != REPLAY_BF16)
         return fail(REPLAY_ERR_DTYPE, "io_dtype must be REPLAY_F32 or REPLAY_BF16");
-    if (c->ckpt_dtype != REPLAY_F32) {
-        if (c->ckpt_dtype == REPLAY_F16) return fail(REPLAY_ERR_UNSUPPORTED, "fp16 recurrence checkpoint not built");
-        return fail(REPLAY_ERR_DTYPE, "ckpt_dtype must be REPLAY_F32");
-    }
+    if (c->ckpt_dtype != REPLAY_F32 && c->ckpt_dtype != REPLAY_F16)
+        return fail(REPLAY_ERR_DTYPE, "ckpt_dtype must be REPLAY_F32 or REPLAY_F16");
     if (c->read_copy != REPLAY_NONE && c->read_copy != REPLAY_FP8_E4M3 && c->read_copy != REPLAY_MXFP4)
         return fail(REPLAY_ERR_DTYPE, "read_copy must be NONE, FP8_E4M3 or MXFP4");
     if (c->read_copy == REPLAY_MXFP4 && R % 32 != 0)
@@ -85,6 +85,10 @@ replay_status check_config(const replay_config* c)
         return fail(REPLAY_ERR_ARG, "unknown flags 0x%x", c->flags);
     if ((c->flags & REPLAY_FLAG_QUANTIZED_CKPT) && c->read_copy == REPLAY_NONE)
         return fail(REPLAY_ERR_ARG, "REPLAY_FLAG_QUANTIZED_CKPT needs a read_copy format");
+    if ((c->flags & REPLAY_FLAG_QUANTIZED_CKPT) && c->ckpt_dtype != REPLAY_F32)
+        return fail(REPLAY_ERR_UNSUPPORTED, "REPLAY_FLAG_QUANTIZED_CKPT keeps an fp32 checkpoint");
+    if ((c->flags & REPLAY_FLAG_VALU_FOLD) && (c->kind != REPLAY_MAMBA2 || c->ckpt_dtype != REPLAY_F32))
+        return fail(REPLAY_ERR_UNSUPPORTED, "REPLAY_FLAG_VALU_FOLD is a Mamba-2 fp32-checkpoint cross-check");
     return ok();
 }
 
@@ -95,7 +99,7 @@ void compute_layout(const replay_config* c, replay_layout* L)
     const uint64_t tiles = B * H, io = io_bytes(c);
     uint64_t off = 0;
     L->ckpt_off = off;
-    L->ckpt_bytes = tiles * C * R * 4;
+    L->ckpt_bytes = tiles * C * R * ckpt_bytes(c);
     off = align256(off + L->ckpt_bytes);
     if (c->read_copy == REPLAY_FP8_E4M3) L->rcopy_bytes = tiles * C * R;
     if (c->read_copy == REPLAY_MXFP4) {
@@ -186,7 +190,7 @@ rs::StepArgs step_args(const replay_state* st, const replay_inputs* in, void* y,
     a.nsplit = strips / wpg;
     a.qckpt = (c->flags & REPLAY_FLAG_QUANTIZED_CKPT) ? 1 : 0;
     const replay_layout& L = st->lay;
-    a.ckpt = at<float>(st, L.ckpt_off);
+    a.ckpt = at<void>(st, L.ckpt_off);
     a.rcopy = L.rcopy_bytes ? at<uint8_t>(st, L.rcopy_off) : nullptr;
     a.rscale = L.rscale_bytes ? at<uint8_t>(st, L.rscale_off) : nullptr;
     a.bufc = at<void>(st, L.buf_off[0]);
@@ -224,10 +228,12 @@ replay_status launch_step(replay_state* st, const replay_inputs* in, void* y, in
     const int io = c->io_dtype == REPLAY_BF16 ? rs::IO_BF16 : rs::IO_F32;
     const int rc = rc_kind(c);
     hipError_t e;
+    const bool f16 = c->ckpt_dtype == REPLAY_F16;
     if (c->kind == REPLAY_MAMBA2)
-        e = rs::launch_mamba2_step(a, io, rc, (c->flags & REPLAY_FLAG_VALU_FOLD) != 0, (hipStream_t)stream);
+        e = f16 ? rs::launch_mamba2_step_f16(a, io, rc, (hipStream_t)stream)
+                : rs::launch_mamba2_step_f32(a, io, rc, (c->flags & REPLAY_FLAG_VALU_FOLD) != 0, (hipStream_t)stream);
     else
-        e = rs::launch_gdn_step(a, io, rc, (hipStream_t)stream);
+        e = f16 ? rs::launch_gdn_step_f16(a, io, rc, (hipStream_t)stream) : rs::launch_gdn_step_f32(a, io, rc, (hipStream_t)stream);
     replay_status s = hip_check(e, "replay step launch");
     if (s == REPLAY_OK) st->parity ^= 1;
     return s;
@@ -311,7 +317,7 @@ replay_status replay_state_layout(const replay_state* st, replay_layout* out)
 
 int32_t replay_state_phase(const replay_state* st) { return st ? st->phase : -1; }
 
-replay_status replay_load_checkpoint(replay_state* st, const float* S, void* stream)
+replay_status replay_load_checkpoint(replay_state* st, const void* S, void* stream)
 {
     if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
     if (st->phase != 0) return fail(REPLAY_ERR_STATE, "load while drafts are pending");
@@ -320,13 +326,14 @@ replay_status replay_load_checkpoint(replay_state* st, const float* S, void* str
     const replay_config* c = &st->cfg;
     const int tiles = c->batch * c->nheads;
     hipStream_t hs = (hipStream_t)stream;
-    s = hip_check(rs::launch_logical_to_tiles(S, at<float>(st, st->lay.ckpt_off), tiles, c->head_dim, c->state_dim, hs),
+    s = hip_check(rs::launch_logical_to_tiles(S, at<void>(st, st->lay.ckpt_off), tiles, c->head_dim, c->state_dim,
+                                              ck_kind(c), hs),
                   "checkpoint load");
     if (s != REPLAY_OK) return s;
     if (c->read_copy != REPLAY_NONE) {
-        s = hip_check(rs::launch_quantize_read_copy(at<float>(st, st->lay.ckpt_off), at<uint8_t>(st, st->lay.rcopy_off),
+        s = hip_check(rs::launch_quantize_read_copy(at<void>(st, st->lay.ckpt_off), at<uint8_t>(st, st->lay.rcopy_off),
                                                     st->lay.rscale_bytes ? at<uint8_t>(st, st->lay.rscale_off) : nullptr,
-                                                    tiles, c->head_dim, c->state_dim, rc_kind(c),
+                                                    tiles, c->head_dim, c->state_dim, rc_kind(c), ck_kind(c),
                                                     (c->flags & REPLAY_FLAG_QUANTIZED_CKPT) != 0, hs),
                       "read copy quantize");
         if (s != REPLAY_OK) return s;
@@ -336,14 +343,14 @@ replay_status replay_load_checkpoint(replay_state* st, const float* S, void* str
                      "bookkeeping reset");
 }
 
-replay_status replay_read_checkpoint(const replay_state* st, float* out, void* stream)
+replay_status replay_read_checkpoint(const replay_state* st, void* out, void* stream)
 {
     if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
     replay_status s = check_ptr(out, "S_out");
     if (s != REPLAY_OK) return s;
     const replay_config* c = &st->cfg;
-    return hip_check(rs::launch_tiles_to_logical(at<float>(st, st->lay.ckpt_off), out, c->batch * c->nheads,
-                                                 c->head_dim, c->state_dim, (hipStream_t)stream),
+    return hip_check(rs::launch_tiles_to_logical(at<void>(st, st->lay.ckpt_off), out, c->batch * c->nheads,
+                                                 c->head_dim, c->state_dim, ck_kind(c), (hipStream_t)stream),
                      "checkpoint read");
 }
 
@@ -442,9 +449,10 @@ replay_status replay_spec_rollback(replay_state* st, void* stream)
 static replay_status conv_common(const replay_config* cfg, rs::ConvArgs* a, const replay_inputs* in, void* y, int T)
 {
     replay_config c = *cfg;
-    // the baselines have no checkpoint/buffer: read-copy and kind limits of
-    // the replay kernels do not apply
+    // the baselines have no checkpoint/buffer: read-copy, flag and kind limits
+    // of the replay kernels do not apply
     c.read_copy = REPLAY_NONE;
+    c.flags = 0;
     const int kind = c.kind;
     c.kind = REPLAY_MAMBA2;
     replay_status s = check_config(&c);
@@ -480,7 +488,7 @@ static replay_status conv_common(const replay_config* cfg, rs::ConvArgs* a, cons
     return REPLAY_OK;
 }
 
-replay_status replay_conv_decode_step(const replay_config* cfg, float* S, const replay_inputs* in, void* y,
+replay_status replay_conv_decode_step(const replay_config* cfg, void* S, const replay_inputs* in, void* y,
                                       void* stream)
 {
     rs::ConvArgs a;
@@ -488,11 +496,12 @@ replay_status replay_conv_decode_step(const replay_config* cfg, float* S, const 
     if (s != REPLAY_OK) return s;
     if ((s = check_ptr(S, "S")) != REPLAY_OK) return s;
     a.S = S;
-    return hip_check(rs::launch_conv_step(a, cfg->io_dtype == REPLAY_BF16 ? rs::IO_BF16 : rs::IO_F32, (hipStream_t)stream),
+    return hip_check(rs::launch_conv_step(a, cfg->io_dtype == REPLAY_BF16 ? rs::IO_BF16 : rs::IO_F32, ck_kind(cfg),
+                                          (hipStream_t)stream),
                      "conventional decode");
 }
 
-replay_status replay_conv_spec_step(const replay_config* cfg, const float* S, float* snaps, int32_t k,
+replay_status replay_conv_spec_step(const replay_config* cfg, const void* S, void* snaps, int32_t k,
                                     const replay_inputs* drafts, void* y, void* stream)
 {
     rs::ConvArgs a;
@@ -502,13 +511,14 @@ replay_status replay_conv_spec_step(const replay_config* cfg, const float* S, fl
     if ((s = check_ptr(S, "S")) != REPLAY_OK) return s;
     if ((s = check_ptr(snaps, "snaps")) != REPLAY_OK) return s;
     a.S_in = S;
-    a.S = const_cast<float*>(S);
+    a.S = const_cast<void*>(S);
     a.snaps = snaps;
-    return hip_check(rs::launch_conv_step(a, cfg->io_dtype == REPLAY_BF16 ? rs::IO_BF16 : rs::IO_F32, (hipStream_t)stream),
+    return hip_check(rs::launch_conv_step(a, cfg->io_dtype == REPLAY_BF16 ? rs::IO_BF16 : rs::IO_F32, ck_kind(cfg),
+                                          (hipStream_t)stream),
                      "conventional spec step");
 }
 
-replay_status replay_conv_spec_restore(const replay_config* cfg, float* S, const float* snaps, int32_t k,
+replay_status replay_conv_spec_restore(const replay_config* cfg, void* S, const void* snaps, int32_t k,
                                        const int32_t* accepted, void* stream)
 {
     if (!cfg) return fail(REPLAY_ERR_ARG, "config is NULL");
@@ -517,10 +527,14 @@ replay_status replay_conv_spec_restore(const replay_config* cfg, float* S, const
     if ((s = check_ptr(snaps, "snaps")) != REPLAY_OK) return s;
     if (!accepted) return fail(REPLAY_ERR_ARG, "accepted is NULL");
     if (k < 1 || k > REPLAY_MAX_BUF) return fail(REPLAY_ERR_CAPACITY, "k = %d outside [1, %d]", k, REPLAY_MAX_BUF);
-    if (cfg->batch < 1 || cfg->nheads < 1 || cfg->head_dim < 16 || cfg->head_dim % 4 || cfg->state_dim < 4)
-        return fail(REPLAY_ERR_SHAPE, "bad shape");
-    return hip_check(rs::launch_conv_restore(S, snaps, accepted, cfg->batch, cfg->head_dim * cfg->state_dim,
-                                             cfg->nheads, k, (hipStream_t)stream),
+    replay_config c = *cfg;
+    c.kind = REPLAY_MAMBA2;
+    c.read_copy = REPLAY_NONE;
+    c.flags = 0;
+    if ((s = check_config(&c)) != REPLAY_OK) return s;
+    const size_t tile_bytes = (size_t)cfg->head_dim * cfg->state_dim * ckpt_bytes(cfg);
+    return hip_check(rs::launch_conv_restore(S, snaps, accepted, cfg->batch, tile_bytes, cfg->nheads, k,
+                                             (hipStream_t)stream),
                      "conventional restore");
 }
 

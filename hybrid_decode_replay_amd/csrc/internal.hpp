@@ -9,6 +9,7 @@ namespace rs {
 enum : int { IO_F32 = 0, IO_BF16 = 1 };
 enum : int { RC_NONE = 0, RC_FP8 = 1, RC_MXFP4 = 2 };
 enum : int { MODE_DECODE = 0, MODE_FLUSH = 1, MODE_SPEC = 2 };
+enum : int { CK_F32 = 0, CK_F16 = 1 };     // recurrence checkpoint storage
 
 // Device error word bits (mirror REPLAY_DEVERR_* of the public header).
 constexpr uint32_t REPLAY_COMMIT_CLAMPED_BIT = 0x1u;
@@ -28,7 +29,7 @@ struct StepArgs {
     int nsplit;              // workgroups per (b, h) tile, along the output axis
     int qckpt;               // nonzero: the checkpoint itself is kept at the copy's precision
     float scale;             // GDN output scale
-    float* ckpt;             // fragment-ordered fp32 tiles
+    void* ckpt;              // fragment-ordered tiles (fp32 or fp16, ckpt.hpp)
     uint8_t* rcopy;          // read-copy codes (or null)
     uint8_t* rscale;         // MXFP4 scales (or null)
     // buffer banks (element pointers; bank stride in elements)
@@ -50,18 +51,21 @@ struct StepArgs {
     void* y;                 // outputs [T][B][H][C]
 };
 
-hipError_t launch_mamba2_step(const StepArgs& a, int io, int rc, bool valu_fold, hipStream_t s);
-hipError_t launch_gdn_step(const StepArgs& a, int io, int rc, hipStream_t s);
+// One translation unit per checkpoint dtype (mamba2.hip / mamba2_f16.hip, ...).
+hipError_t launch_mamba2_step_f32(const StepArgs& a, int io, int rc, bool valu_fold, hipStream_t s);
+hipError_t launch_mamba2_step_f16(const StepArgs& a, int io, int rc, hipStream_t s);
+hipError_t launch_gdn_step_f32(const StepArgs& a, int io, int rc, hipStream_t s);
+hipError_t launch_gdn_step_f16(const StepArgs& a, int io, int rc, hipStream_t s);
 
 // Bookkeeping, layout conversion and helpers (aux.hip).
 hipError_t launch_book_commit(int32_t* book, uint32_t* err, int B, int parity,
                               const int32_t* accepted, hipStream_t s);
 hipError_t launch_book_reset(int32_t* book, uint32_t* err, int B, int parity, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
-hipError_t launch_tiles_to_logical(const float* ckpt, float* out, int tiles, int C, int R, hipStream_t s);
-hipError_t launch_logical_to_tiles(const float* in, float* ckpt, int tiles, int C, int R, hipStream_t s);
-hipError_t launch_quantize_read_copy(float* ckpt, uint8_t* codes, uint8_t* scales, int tiles,
-                                     int C, int R, int rc, bool round_ckpt, hipStream_t s);
+hipError_t launch_tiles_to_logical(const void* ckpt, void* out, int tiles, int C, int R, int ck, hipStream_t s);
+hipError_t launch_logical_to_tiles(const void* in, void* ckpt, int tiles, int C, int R, int ck, hipStream_t s);
+hipError_t launch_quantize_read_copy(void* ckpt, uint8_t* codes, uint8_t* scales, int tiles,
+                                     int C, int R, int rc, int ck, bool round_ckpt, hipStream_t s);
 hipError_t launch_read_copy_to_logical(const uint8_t* codes, const uint8_t* scales, uint8_t* codes_out,
                                        uint8_t* scales_out, int tiles, int C, int R, int rc, hipStream_t s);
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
@@ -71,9 +75,9 @@ hipError_t launch_stream_read(const void* src, size_t bytes, float* sum_out, hip
 struct ConvArgs {
     int kind, B, H, G, hpg, C, R, T;
     float scale;
-    float* S;                // logical [B][H][C][R]
-    const float* S_in;       // spec: read-only source
-    float* snaps;            // spec: [T][B][H][C][R]
+    void* S;                 // logical [B][H][C][R] (fp32 or fp16)
+    const void* S_in;        // spec: read-only source
+    void* snaps;             // spec: [T][B][H][C][R]
     const void* in_c;
     const void* in_r;
     const void* in_q;
@@ -83,8 +87,8 @@ struct ConvArgs {
     const float* D;
     void* y;
 };
-hipError_t launch_conv_step(const ConvArgs& a, int io, hipStream_t s);
-hipError_t launch_conv_restore(float* S, const float* snaps, const int32_t* accepted, int B, int tile_elems,
+hipError_t launch_conv_step(const ConvArgs& a, int io, int ck, hipStream_t s);
+hipError_t launch_conv_restore(void* S, const void* snaps, const int32_t* accepted, int B, size_t tile_bytes,
                                int H, int k, hipStream_t s);
 
 }  // namespace rs

@@ -1,0 +1,277 @@
+// mamba2_kernel.hpp -- replayed Mamba-2 decode step for gfx950 (CDNA4).
+// Included by one translation unit per checkpoint storage dtype.
+//
+// One workgroup per (sequence b, head h, column slice): the head's output
+// columns are split over workgroups of at most four waves, and wave w owns 16
+// output columns p and every state row n (see common.hpp for the
+// fragment-ordered tile).  Per launch and sequence the virtual entry list is
+// V = (committed buffer entries 0..len-1) ++ (T new tokens).  The first f
+// entries are folded into the checkpoint (f = 0 on a non-flush step), the
+// rest stay in the buffer and are replayed on top of the checkpoint for the
+// outputs.  With l_i = dt_i A_h (pages: the checkpoint plus buffered inputs
+// give the output and the recurrence is unrolled over the buffered window --
+// [DE] "ReplaySSM beschleunigt das Decoding ...", section "Wie es
+// funktioniert"; the filling step folds and writes the checkpoint once --
+// [TR] "NVIDIA ve Dao AI Lab ...", section "ReplaySSM nasil calisir?"):
+//
+//   fold    S' = e^{sum_{i<f} l_i} S0 + sum_{i<f} e^{sum_{i<j<f} l_j} dt_i x_i B_i^T
+//           a [P x f] . [f x N] contraction per head, on MFMA (f <= 16)
+//   output  y_t = e^{L'} (S' C_t) + sum_{f<=j<=pos} e^{sum_{j<i<=pos} l_i} dt_j (B_j . C_t) x_j
+//                 + D_h x_t,     L' = sum_{f<=i<=pos} l_i,  pos = len + t
+//           (if the token itself was folded, pos < f: y_t = S' C_t + D_h x_t)
+//
+// Non-flush steps read the checkpoint once and write no state; the flush step
+// writes it once.  Only exponentials of sums of l (all <= 0) are taken; a sum
+// over an entry range is a difference of inclusive prefix sums of dt, formed
+// once per launch by a wave scan while the entries are published.
+//
+// Memory schedule per workgroup: the entry rows (x, B), the read-out rows C
+// and dt are fetched as 16-byte chunks issued before the checkpoint stream,
+// so they land while the 128-bit checkpoint loads are still in flight; one
+// workgroup barrier publishes them in LDS.  Every wave then computes the
+// replay coefficients it needs itself (lane-parallel dots and suffix sums),
+// so a non-flush step has no second barrier.
+#pragma once
+#include "common.hpp"
+#include "internal.hpp"
+#include "ckpt.hpp"
+#include "rc.hpp"
+#include "stage.hpp"
+
+namespace rs {
+
+template <int NB, int IO, int TMAX, bool MFMA_FOLD, int RC, int CK>
+__global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
+{
+    extern __shared__ float lds[];
+    constexpr int R = NB * 16;
+    constexpr int RS = R + 4;                   // padded LDS stride of B rows
+    constexpr int PRE = 4;                      // chunks per thread fetched ahead of the checkpoint
+    constexpr int VM = (16 + TMAX + 3) & ~3;    // bound on the entry count cap + T, padded to 4
+    const int C = a.C;
+    const TileIdx tix = tile_of(xcd_tile_index(), a.H, a.nsplit);
+    const int b = tix.b, h = tix.h, tile = b * a.H + h;
+    const int g = h / a.hpg;
+    const int cw = C / a.nsplit, c0 = tix.sp * cw;   // this workgroup's output columns
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int w = tid >> 6, lane = tid & 63;
+    const int lc = 16 * w + (lane & 15);             // local output column
+    const int col = c0 + lc;                          // global output column
+    const int rq = 4 * (lane >> 4);
+    const size_t sB = (size_t)a.B;
+
+    // ---- bookkeeping: identical decision in every workgroup of sequence b
+    const StepPlan p = plan_step(a, b, h == 0 && tix.sp == 0 && tid == 0);
+    if (a.mode == MODE_FLUSH && p.f == 0) return;
+    const int f = p.f, len = p.len, T = a.T;
+
+    // ---- LDS partition (floats; the launch sizes cs for max(T, 1) rows)
+    float* ds = lds;                              // [VM]       entry dt (vmax <= VM)
+    float* ps = ds + VM;                          // [VM]       inclusive prefix sums of dt
+    float* xs = ps + VM;                          // [vmax][cw] entry x rows (own columns)
+    float* bs = xs + (size_t)a.vmax * cw;         // [vmax][RS] entry B rows
+    float* cs = bs + (size_t)a.vmax * RS;         // [Tr][R]    read-out rows C_t
+
+    StageGeom G;
+    G.bufc = a.bufc; G.bufr = a.bufr; G.bufs0 = a.bufs0; G.bufs1 = nullptr;
+    G.in_c = a.in_c; G.in_r = a.in_r; G.in_q = a.in_q; G.in_s0 = a.in_s0; G.in_s1 = nullptr;
+    G.bank_c = a.bank_c; G.bank_r = a.bank_r; G.bank_s = a.bank_s;
+    G.hc = (size_t)b * a.H + h; G.gr = (size_t)b * a.G + g;
+    G.b = b; G.h = h; G.g = g; G.B = a.B; G.H = a.H; G.G = a.G; G.cap = a.cap; G.C = C;
+    G.c0 = c0; G.cw = cw;
+    G.len = len; G.bank = p.bank; G.V = p.V; G.T = T;
+    G.xc = xs; G.xr = bs; G.xq = cs; G.s0 = ds; G.s1 = nullptr; G.p0 = ps;
+
+    // ---- 1. entry and read-out chunks, issued ahead of the checkpoint stream
+    const Stager<IO, R> stg(G);
+    uint4 pre[PRE];
+    ScalarRaw sr;
+    stage_issue<IO, R, PRE, true>(stg, tid, nthr, pre, sr);
+
+    // ---- 2. checkpoint strip -> registers (128-bit loads, ckpt.hpp)
+    // a step that folds nothing reads the low-precision copy when there is one
+    const size_t strip_index = (size_t)tile * (C >> 4) + (c0 >> 4) + w;
+    f32x4 s[NB];
+    bool from_copy = false;
+    if constexpr (RC != RC_NONE) from_copy = (f == 0);
+    if (from_copy) {
+        if constexpr (RC != RC_NONE) rc_load<NB, RC>(a.rcopy, a.rscale, strip_index, lane, s);
+    } else {
+        ckpt_load<NB, CK>(a.ckpt, strip_index, lane, s);
+    }
+
+    // ---- 3. publish the staged rows
+    stage_publish<IO, R, PRE>(stg, tid, nthr, pre, sr);
+    __syncthreads();
+
+    const float Ah = a.A[h];
+
+    // ---- 4. fold the first f entries into the checkpoint registers
+    // sums of dt over an entry range come from the prefix sums: sum_{lo<=i<hi} = ps[hi-1] - ps[lo-1]
+    // (with dt >= 0 and A_h <= 0 every exponent is <= 0 up to the rounding of that difference)
+    if (f > 0) {
+        const float pf = ps[f - 1];
+        const float decay = expf(pf * Ah);
+        if constexpr (MFMA_FOLD) {
+            // D[n][p] += sum_i A[n][i] B[i][p] with A = B_i[n] (lane: n = l%16,
+            // i = l/16) and B = e^{..} dt_i x_i[p] (lane: i = l/16, p = l%16).
+            const int iq = lane >> 4;
+            float bop[4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const int i = kb * 4 + iq;
+                bop[kb] = (i < f) ? expf((pf - ps[i]) * Ah) * ds[i] * xs[i * cw + lc] : 0.f;
+            }
+            const int nkb = (f + 3) >> 2;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    if (kb < nkb) {
+                        const int i = kb * 4 + iq;
+                        const float av = (i < f) ? bs[i * RS + nb * 16 + (lane & 15)] : 0.f;
+                        acc = mfma16x16x4(av, bop[kb], acc);
+                    }
+                }
+                s[nb] = decay * s[nb] + acc;
+            }
+        } else {
+            float wx[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                wx[i] = (i < f) ? expf((pf - ps[i]) * Ah) * ds[i] * xs[i * cw + lc] : 0.f;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (i < f) acc += wx[i] * ld4(bs + i * RS + nb * 16 + rq);
+                s[nb] = decay * s[nb] + acc;
+            }
+        }
+    }
+
+    // the folded state takes the checkpoint's storage precision at once (fp16:
+    // RNE), so this step's outputs and the read copy see the stored values
+    if (f > 0) ckpt_round<NB, CK>(s);
+    // a checkpoint kept at the copy's precision is rounded as soon as it is folded
+    if constexpr (RC != RC_NONE) {
+        if (a.qckpt && f > 0) rc_roundtrip<NB, RC>(s);
+    }
+
+    // ---- 5. outputs of the new tokens
+    if (a.mode != MODE_FLUSH) {
+        const float Dh = a.D[h];
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) {
+            if (t < T) {
+                const int pos = len + t;
+                const float xt = xs[pos * cw + lc];
+                // replay of entries f..pos (formed first: it needs only LDS, so it runs while
+                // the checkpoint loads are in flight).  Lane quad jj = l/4 forms B_j . C_t and
+                // the decayed coefficient; output lanes gather the coefficients by readlane.
+                float rep = 0.f, gdec = 1.f;
+                if (pos >= f) {
+                    const int nr = pos - f + 1;
+                    const int q = lane & 3;
+                    for (int jj0 = 0; jj0 < nr; jj0 += 16) {
+                        const int jj = jj0 + (lane >> 2), j = f + jj;
+                        float dot = 0.f;
+                        if (jj < nr) {
+#pragma unroll
+                            for (int i = 0; i < R / 16; ++i)
+                                dot += dot4(ld4(bs + j * RS + 16 * i + 4 * q), ld4(cs + t * R + 16 * i + 4 * q));
+                        }
+                        dot = quad_sum(dot);
+                        const float coef = (jj < nr) ? expf((ps[pos] - ps[j]) * Ah) * ds[j] * dot : 0.f;
+                        // entries past pos carry a zero coefficient; their index is clamped to a
+                        // staged row so the product stays finite
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            rep += readlane(coef, 4 * e) * xs[min(f + jj0 + e, pos) * cw + lc];
+                    }
+                    gdec = expf((ps[pos] - (f > 0 ? ps[f - 1] : 0.f)) * Ah);
+                }
+                // checkpoint read-out (S' C_t)[col], reduced over the four row groups
+                float gacc = 0.f;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) gacc += dot4(s[nb], ld4(cs + t * R + nb * 16 + rq));
+                gacc = sum_over_row_groups(gacc);
+                const float yv = (pos >= f) ? gdec * gacc + rep + Dh * xt : gacc + Dh * xt;
+                if (lane < 16) st_io<IO>(a.y, (((size_t)t * sB + b) * a.H + h) * C + col, yv);
+            }
+        }
+    }
+
+    // ---- 6. single checkpoint write on a folding step
+    if (f > 0) {
+        ckpt_store<NB, CK>(a.ckpt, strip_index, lane, s);
+        if constexpr (RC != RC_NONE) rc_store<NB, RC>(a.rcopy, a.rscale, strip_index, lane, s);
+    }
+
+    // ---- 7. append the unfolded new tokens to the buffer (slot = position - f)
+    stage_append<IO, R>(G, a.bufc, a.bufr, a.bufs0, nullptr, p.bank_new, f, tid, nthr, tix.sp == 0,
+                        tix.sp == 0 && h % a.hpg == 0);
+}
+
+template <int NB, int IO, int TMAX, bool MF, int RC, int CK>
+static hipError_t mamba2_launch_nb(const StepArgs& a, hipStream_t s)
+{
+    const size_t Tr = a.T > 0 ? a.T : 1;
+    const size_t R = NB * 16;
+    const size_t VM = (16 + TMAX + 3) & ~3;
+    const size_t lds = sizeof(float) * ((size_t)a.vmax * (a.C / a.nsplit + R + 4) + Tr * R + 2 * VM);
+    auto k = mamba2_step_kernel<NB, IO, TMAX, MF, RC, CK>;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k, dim3(a.B * a.H * a.nsplit), dim3(a.C / a.nsplit * 4), lds, s, a);
+    return hipGetLastError();
+}
+
+template <int IO, int TMAX, bool MF, int RC, int CK>
+static hipError_t mamba2_launch_io(const StepArgs& a, hipStream_t s)
+{
+    switch (a.R) {
+        case 16:
+            if constexpr (RC != RC_MXFP4) return mamba2_launch_nb<1, IO, TMAX, MF, RC, CK>(a, s);
+            return hipErrorInvalidValue;     // MXFP4 groups need 32 rows
+        case 32: return mamba2_launch_nb<2, IO, TMAX, MF, RC, CK>(a, s);
+        case 64: return mamba2_launch_nb<4, IO, TMAX, MF, RC, CK>(a, s);
+        case 128: return mamba2_launch_nb<8, IO, TMAX, MF, RC, CK>(a, s);
+        case 256: return mamba2_launch_nb<16, IO, TMAX, MF, RC, CK>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int TMAX, bool MF, int RC, int CK>
+static hipError_t mamba2_launch_t(const StepArgs& a, int io, hipStream_t s)
+{
+    return io == IO_BF16 ? mamba2_launch_io<IO_BF16, TMAX, MF, RC, CK>(a, s) : mamba2_launch_io<IO_F32, TMAX, MF, RC, CK>(a, s);
+}
+
+// Dispatch over the draft count (TMAX = 1, 4, 16), read copy and fold flavour
+// for checkpoint storage CK; the MFMA fold is the product path, the vector
+// fold a cross-check kept for fp32 checkpoints.
+template <int TMAX, int CK>
+static hipError_t mamba2_launch_tm(const StepArgs& a, int io, int rc, bool valu_fold, hipStream_t s)
+{
+    if (rc == RC_FP8) return mamba2_launch_t<TMAX, true, RC_FP8, CK>(a, io, s);
+    if (rc == RC_MXFP4) return mamba2_launch_t<TMAX, true, RC_MXFP4, CK>(a, io, s);
+    if constexpr (CK == CK_F32) {
+        if (valu_fold) return mamba2_launch_t<TMAX, false, RC_NONE, CK>(a, io, s);
+    }
+    return mamba2_launch_t<TMAX, true, RC_NONE, CK>(a, io, s);
+}
+
+template <int CK>
+static hipError_t mamba2_launch(const StepArgs& a, int io, int rc, bool valu_fold, hipStream_t s)
+{
+    if (a.T <= 1) return mamba2_launch_tm<1, CK>(a, io, rc, valu_fold, s);
+    if (a.T <= 4) return mamba2_launch_tm<4, CK>(a, io, rc, valu_fold, s);
+    return mamba2_launch_tm<16, CK>(a, io, rc, valu_fold, s);
+}
+
+}  // namespace rs

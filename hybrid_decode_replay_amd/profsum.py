@@ -23,9 +23,9 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 COPY_BYTES = 1 << 30
 SOURCES = {
-    "mamba2_step_kernel": ("mamba2.hip", "common.hpp", "stage.hpp", "rc.hpp"),
-    "gdn_step_kernel": ("gdn.hip", "common.hpp", "stage.hpp", "rc.hpp"),
-    "conv_step_kernel": ("conv.hip", "common.hpp"),
+    "mamba2_step_kernel": ("mamba2_kernel.hpp", "mamba2.hip", "ckpt.hpp", "common.hpp", "stage.hpp", "rc.hpp"),
+    "gdn_step_kernel": ("gdn_kernel.hpp", "gdn.hip", "ckpt.hpp", "common.hpp", "stage.hpp", "rc.hpp"),
+    "conv_step_kernel": ("conv.hip", "ckpt.hpp", "common.hpp"),
 }
 
 

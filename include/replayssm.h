@@ -45,10 +45,10 @@
  * Tensor layouts (row-major, logical):
  *   Mamba-2  x [T][B][H][P], Bm and Cm [T][B][G][N], dt [T][B][H]
  *            (all in `io_dtype`), A and D [H] fp32, y [T][B][H][P] io_dtype,
- *            checkpoint (logical) [B][H][P][N] fp32.
+ *            checkpoint (logical) [B][H][P][N] in `ckpt_dtype`.
  *   GDN      q and k [T][B][G][DK], v [T][B][H][DV] (io_dtype), alpha and
  *            beta [T][B][H] fp32, o [T][B][H][DV] io_dtype, checkpoint
- *            (logical) [B][H][DV][DK] fp32.
+ *            (logical) [B][H][DV][DK] in `ckpt_dtype`.
  *   T = 1 for a decode step, T = k for k speculative drafts.
  *   Head h reads B/C (Mamba-2) or q/k (GDN) of group h / (H / G).
  */
@@ -88,13 +88,22 @@ typedef enum {
     REPLAY_MXFP4 = 5        /* OCP MX FP4 E2M1, one E8M0 scale per 32 elements          */
 } replay_dtype;
 
+/* Recurrence checkpoint dtype.  REPLAY_F32, or REPLAY_F16 (IEEE binary16; the
+ * [TR] page, section "Kuantizasyon hatasinin sinirlandirilmasi", pairs
+ * low-precision reads with an FP16 or FP8 recurrence): a fold decodes the
+ * fp16 checkpoint to fp32, folds in fp32, rounds the result to fp16 (RNE)
+ * right away -- that step's outputs and the read copy see the rounded values --
+ * and writes it once.  Non-flush steps read half the bytes of fp32. */
+
 /* Device error word bits (sticky; cleared by replay_load_checkpoint). */
 #define REPLAY_DEVERR_COMMIT_CLAMPED 0x1u  /* an accepted count was outside [0, pend] */
 
 /* Configuration flags. */
-#define REPLAY_FLAG_VALU_FOLD 0x1   /* fold with vector FMAs instead of MFMA (cross-check) */
+#define REPLAY_FLAG_VALU_FOLD 0x1   /* Mamba-2, fp32 checkpoint: fold with vector FMAs instead
+                                       of MFMA (cross-check) */
 /* Keep the checkpoint itself at the read copy's precision (comparison variant:
- * a low-precision state inside the recurrence).  Needs read_copy != NONE.  The
+ * a low-precision state inside the recurrence).  Needs read_copy != NONE and an
+ * fp32 checkpoint.  The
  * checkpoint is rounded to the copy's grid at load and right after every fold
  * (before that step's outputs); the fp32 region then mirrors the copy exactly. */
 #define REPLAY_FLAG_QUANTIZED_CKPT 0x2
@@ -108,7 +117,7 @@ typedef struct {
     int32_t head_dim;     /* Mamba-2 P; GDN DV.  Multiple of 16, <= 256          */
     int32_t state_dim;    /* Mamba-2 N; GDN DK.  16, 32, 64, 128 or 256          */
     int32_t buf_cap;      /* buffer capacity, 1..16                              */
-    int32_t ckpt_dtype;   /* REPLAY_F32 (recurrence checkpoint)                  */
+    int32_t ckpt_dtype;   /* REPLAY_F32 | REPLAY_F16 (recurrence checkpoint)     */
     int32_t read_copy;    /* REPLAY_NONE | REPLAY_FP8_E4M3 | REPLAY_MXFP4        */
     int32_t io_dtype;     /* REPLAY_F32 | REPLAY_BF16 (token inputs and outputs) */
     int32_t flags;        /* REPLAY_FLAG_*                                       */
@@ -162,13 +171,15 @@ replay_status replay_state_layout(const replay_state *st, replay_layout *out);
 int32_t replay_state_phase(const replay_state *st);
 
 /* ---- checkpoint I/O ----------------------------------------------------- */
-/* Loads an fp32 logical checkpoint (device), refreshes the read copy, empties
- * the buffer and resets len = pend = fc = 0 and the error word.  Not allowed
+/* Logical checkpoints at the boundary are [B][H][rows][cols] arrays in the
+ * state's ckpt_dtype (float or IEEE binary16), rows = P or DV, cols = N or DK.
+ * Loads a logical checkpoint (device), refreshes the read copy, empties the
+ * buffer and resets len = pend = fc = 0 and the error word.  Not allowed
  * while drafts are pending. */
-replay_status replay_load_checkpoint(replay_state *st, const float *S_logical, void *stream);
-/* Writes the current checkpoint (not including buffered tokens) as fp32
- * logical layout to S_out (device). */
-replay_status replay_read_checkpoint(const replay_state *st, float *S_out, void *stream);
+replay_status replay_load_checkpoint(replay_state *st, const void *S_logical, void *stream);
+/* Writes the current checkpoint (not including buffered tokens) in logical
+ * layout and ckpt_dtype to S_out (device). */
+replay_status replay_read_checkpoint(const replay_state *st, void *S_out, void *stream);
 /* Writes the read copy in logical element order: one byte per element
  * (FP8 code, or FP4 code in the low nibble) to codes_out [B][H][rows][cols],
  * and for MXFP4 the E8M0 scales to scales_out [B][H][rows][cols/32]
@@ -207,17 +218,20 @@ replay_status replay_spec_commit(replay_state *st, const int32_t *accepted, void
 replay_status replay_spec_rollback(replay_state *st, void *stream);
 
 /* ---- in-run conventional baselines --------------------------------------
- * Ordinary decoding on a plain fp32 logical state (load, decay and update,
- * output, store per token), tuned like the replay kernels. */
-replay_status replay_conv_decode_step(const replay_config *cfg, float *S, const replay_inputs *in,
+ * Ordinary decoding on a plain logical state [B][H][rows][cols] in the
+ * config's ckpt_dtype (load, decay and update, output, store per token; an
+ * fp16 state is updated in fp32, the output is read from that update and the
+ * state is stored RNE), tuned like the replay kernels.  read_copy and flags
+ * are ignored. */
+replay_status replay_conv_decode_step(const replay_config *cfg, void *S, const replay_inputs *in,
                                       void *y, void *stream);
 /* k draft steps from S (read once, not written); snapshot j (the state after
- * draft j) goes to snaps + j * B*H*rows*cols; outputs y [k][B][...]. */
-replay_status replay_conv_spec_step(const replay_config *cfg, const float *S, float *snaps,
+ * draft j) goes to snaps + j * B*H*rows*cols elements; outputs y [k][B][...]. */
+replay_status replay_conv_spec_step(const replay_config *cfg, const void *S, void *snaps,
                                     int32_t k, const replay_inputs *drafts, void *y, void *stream);
 /* S[b] = snaps[accepted[b] - 1][b] where 1 <= accepted[b] <= k; unchanged
  * otherwise.  accepted: device int32 [B]. */
-replay_status replay_conv_spec_restore(const replay_config *cfg, float *S, const float *snaps,
+replay_status replay_conv_spec_restore(const replay_config *cfg, void *S, const void *snaps,
                                        int32_t k, const int32_t *accepted, void *stream);
 
 /* ---- measurement helpers ------------------------------------------------ */

@@ -56,6 +56,12 @@ a low-precision state inside the recurrence).  The checkpoint is rounded to the
 copy's grid at load and at every flush, and the recurrence continues from the
 rounded state; the output of a step whose own token was folded is read from
 the rounded state.
+
+FP16 recurrence checkpoint (the same section pairs low-precision reads with an
+FP16 or FP8 recurrence).  The checkpoint is stored as IEEE binary16: rounded to
+nearest even at load and at every flush (numpy's float64 -> float16 cast), and
+the recurrence and outputs continue from the stored values exactly as in the
+quantized-checkpoint case.  The pages give no tolerance for it.
 """
 from __future__ import annotations
 
@@ -255,15 +261,21 @@ class _Session:
 
     kind = None
 
-    def __init__(self, batch, cap, S0, read_copy=None, quantized_ckpt=False):
+    def __init__(self, batch, cap, S0, read_copy=None, quantized_ckpt=False, ckpt_dtype="f32"):
         if not 1 <= cap <= 16:
             raise ValueError("buffer capacity must be in [1, 16]")
         if quantized_ckpt and read_copy is None:
             raise ValueError("a quantized checkpoint needs a format")
+        if ckpt_dtype not in ("f32", "f16"):
+            raise ValueError("checkpoint dtype must be 'f32' or 'f16'")
+        if quantized_ckpt and ckpt_dtype != "f32":
+            raise ValueError("the quantized-checkpoint variant keeps an fp32 checkpoint")
         self.B = batch
         self.cap = cap
         self.read_copy = read_copy
         self.quantized_ckpt = quantized_ckpt
+        self.ckpt_dtype = ckpt_dtype
+        self.rounds = quantized_ckpt or ckpt_dtype == "f16"    # folds land on a coarser grid
         self.S = self._round(np.array(S0, np.float64, copy=True))   # committed state
         self.ckpt = self.S.copy()                              # image at last flush
         self.len = np.zeros(batch, np.int32)
@@ -280,8 +292,11 @@ class _Session:
         return self.len.copy(), self.pend.copy(), self.fc.copy()
 
     def _round(self, S):
-        """The state as the checkpoint keeps it (rounded to the copy's grid in the
-        quantized-checkpoint variant, unchanged otherwise)."""
+        """The state as the checkpoint keeps it: rounded to binary16 for an fp16
+        checkpoint, to the copy's grid in the quantized-checkpoint variant, unchanged
+        otherwise."""
+        if self.ckpt_dtype == "f16":
+            return np.asarray(S, np.float64).astype(np.float16).astype(np.float64)
         if not self.quantized_ckpt:
             return S
         return read_copy_values(S, self.read_copy).reshape(S.shape)
@@ -334,7 +349,7 @@ class _Session:
             if not full[b]:
                 self.hist[b].append(self._slice(inp, b))
         self._flush_rows(full)
-        if self.quantized_ckpt:
+        if self.rounds:
             for b in np.flatnonzero(full):
                 y[b] = self._readout(self.S[b], self._slice(inp, b))
         self.nops += 1
@@ -401,10 +416,10 @@ class Mamba2Session(_Session):
 
     kind = "mamba2"
 
-    def __init__(self, A, D, S0, cap=16, read_copy=None, quantized_ckpt=False):
+    def __init__(self, A, D, S0, cap=16, read_copy=None, quantized_ckpt=False, ckpt_dtype="f32"):
         self.A = np.asarray(A, np.float64)
         self.D = np.asarray(D, np.float64)
-        super().__init__(np.asarray(S0).shape[0], cap, S0, read_copy, quantized_ckpt)
+        super().__init__(np.asarray(S0).shape[0], cap, S0, read_copy, quantized_ckpt, ckpt_dtype)
 
     def _token(self, S, inp, active=None):
         return mamba2_token(S, inp["x"], inp["Bm"], inp["Cm"], inp["dt"], self.A, self.D, active)
@@ -423,9 +438,9 @@ class GDNSession(_Session):
 
     kind = "gdn"
 
-    def __init__(self, S0, cap=16, scale=1.0, read_copy=None, quantized_ckpt=False):
+    def __init__(self, S0, cap=16, scale=1.0, read_copy=None, quantized_ckpt=False, ckpt_dtype="f32"):
         self.scale = float(scale)
-        super().__init__(np.asarray(S0).shape[0], cap, S0, read_copy, quantized_ckpt)
+        super().__init__(np.asarray(S0).shape[0], cap, S0, read_copy, quantized_ckpt, ckpt_dtype)
 
     def _token(self, S, inp, active=None):
         return gdn_token(S, inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], self.scale, active)

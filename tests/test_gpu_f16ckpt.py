@@ -1,0 +1,181 @@
+"""GPU parity of the fp16 recurrence checkpoint (Mamba-2 and Gated DeltaNet) through the C ABI.
+
+The checkpoint is stored as IEEE binary16: a fold decodes it, folds in fp32 and
+rounds the result to nearest even at once.  The oracle rounds its fp64 state the
+same way at load and at every flush ([TR] "NVIDIA ve Dao AI Lab ...", section
+"Kuantizasyon hatasinin sinirlandirilmasi", pairs low-precision reads with an
+FP16 recurrence).  Checked here:
+  * load / read of the checkpoint: bit-exact round trip of binary16 values in
+    every strip layout (one block, block pairs);
+  * decode, flush and spec paths against the oracle within TOL_F16 (derived in
+    tests/harness.py from the binary16 rounding of both sides), bookkeeping
+    bit-exact;
+  * after every flush the stored checkpoint is on the binary16 grid and the
+    read copy is the quantization of exactly those values (bit-exact);
+  * the conventional baseline with an fp16 state against ordinary decoding
+    that rounds the state to binary16 after every token.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from hybrid_decode_replay_amd import synth  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from hybrid_decode_replay_amd import binding  # noqa: F401  (fails loudly if not built)
+    yield
+
+
+def rb():
+    from hybrid_decode_replay_amd import binding
+    return binding
+
+
+def _kind(name):
+    b = rb()
+    return b.MAMBA2 if name == "mamba2" else b.GDN
+
+
+def _tokens(kind, seed, T, B, H, G, C, R, io="f32"):
+    if kind == "mamba2":
+        return synth.mamba2_tokens(seed, T, B, H, G, C, R, dtype=io)
+    return synth.gdn_tokens(seed, T, B, H, G, R, C, dtype=io)
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+@pytest.mark.parametrize("C,R", [(16, 16), (48, 32), (64, 128), (32, 256)])
+def test_checkpoint_round_trip_bit_exact(kind, C, R):
+    b = rb()
+    B, H = 3, 2
+    st = b.ReplayState(b.make_config(_kind(kind), B, H, H, C, R, 16, b.F32, ckpt_dtype=b.F16))
+    S = torch.from_numpy(synth.checkpoint(7 + C + R, (B, H, C, R)).astype(np.float16)).cuda()
+    st.load_checkpoint(S)
+    back = st.read_checkpoint()
+    torch.cuda.synchronize()
+    assert back.dtype == torch.float16
+    assert torch.equal(back.view(torch.int16), S.view(torch.int16))
+    L = st.layout()
+    assert L.ckpt_bytes == B * H * C * R * 2
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+@pytest.mark.parametrize("B,H,G,C,R,cap,io", [
+    (3, 4, 2, 64, 128, 16, "f32"),
+    (2, 2, 1, 32, 16, 5, "bf16"),      # one-block strips (8-byte words)
+    (5, 3, 3, 48, 64, 7, "f32"),       # ragged windows, three waves
+    (2, 2, 2, 128, 256, 4, "bf16"),
+])
+def test_decode_windows(kind, B, H, G, C, R, cap, io):
+    from harness import Pair
+    b = rb()
+    if kind == "gdn":
+        G = H
+    S0 = synth.checkpoint(11, (B, H, C, R))
+    pair = Pair(_kind(kind), B, H, G, C, R, cap=cap, io=b.BF16 if io == "bf16" else b.F32, seed=11, S0=S0,
+                ckpt=b.F16)
+    T = 3 * cap + 2
+    toks = _tokens(kind, 11, T, B, H, G, C, R, io)
+    print(f"[f16 decode] {kind} B={B} H={H} C={C} R={R} cap={cap} io={io}", flush=True)
+    for t in range(T):
+        pair.decode(synth.token(toks, t), what=f"step {t}")
+        if (t + 1) % cap == 0:
+            ck = pair.st.read_checkpoint()
+            torch.cuda.synchronize()
+            assert ck.dtype == torch.float16
+    print("max errors", pair.max_err)
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_spec_commit_rollback_and_flush(kind):
+    from harness import Pair
+    b = rb()
+    B, H, C, R, cap = 4, 2, 32, 64, 8
+    pair = Pair(_kind(kind), B, H, H, C, R, cap=cap, io=b.F32, seed=21, S0=synth.checkpoint(21, (B, H, C, R)),
+                ckpt=b.F16)
+    toks = _tokens(kind, 21, 40, B, H, H, C, R)
+    for t in range(3):
+        pair.decode(synth.token(toks, t))
+    pair.spec({n: v[3:7] for n, v in toks.items()}, what="spec 4")
+    pair.commit([4, 2, 0, 1])
+    pair.spec({n: v[7:13] for n, v in toks.items()}, what="spec 6 with pre-flush rows")
+    pair.rollback()
+    pair.decode(synth.token(toks, 13))
+    pair.flush()
+    pair.spec({n: v[14:22] for n, v in toks.items()}, what="spec 8 from an empty buffer")
+    pair.commit([8, 8, 3, 0])
+    for t in range(22, 30):
+        pair.decode(synth.token(toks, t))
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_read_copy_of_fp16_checkpoint(kind, fmt):
+    from harness import Pair
+    from oracle import replay_oracle as ro
+    b = rb()
+    B, H, C, R, cap = 2, 2, 32, 64, 4
+    rc = {"fp8": b.FP8_E4M3, "mxfp4": b.MXFP4}[fmt]
+    pair = Pair(_kind(kind), B, H, H, C, R, cap=cap, io=b.F32, seed=31, S0=synth.checkpoint(31, (B, H, C, R)),
+                ckpt=b.F16, read_copy=rc)
+    toks = _tokens(kind, 31, 3 * cap, B, H, H, C, R)
+    for t in range(3 * cap):
+        pair.decode(synth.token(toks, t), what=f"step {t}")
+        ck = pair.st.read_checkpoint()
+        codes, scales = pair.st.read_copy()
+        torch.cuda.synchronize()
+        ck64 = ck.float().cpu().numpy().astype(np.float64)
+        if fmt == "fp8":
+            np.testing.assert_array_equal(codes.cpu().numpy(), ro.e4m3_encode(ck64).reshape(ck64.shape))
+        else:
+            wc, ws = ro.mxfp4_quantize(ck64)
+            np.testing.assert_array_equal(codes.cpu().numpy(), wc)
+            np.testing.assert_array_equal(scales.cpu().numpy(), ws)
+
+
+def test_fp16_flags_rejected():
+    b = rb()
+    cfg = b.make_config(b.MAMBA2, 2, 2, 1, 32, 32, 8, b.F32, ckpt_dtype=b.F16, read_copy=b.FP8_E4M3,
+                        flags=b.FLAG_QUANTIZED_CKPT)
+    assert b.config_check(cfg) == b.ERR_UNSUPPORTED
+    cfg = b.make_config(b.MAMBA2, 2, 2, 1, 32, 32, 8, b.F32, ckpt_dtype=b.F16, flags=b.FLAG_VALU_FOLD)
+    assert b.config_check(cfg) == b.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_conventional_fp16_state(kind):
+    """Conventional decoding on an fp16 state vs the oracle's per-token step on an fp64 state
+    that is rounded to binary16 after every token (outputs from the unrounded update on both
+    sides; the state rounded after every token on both sides)."""
+    from harness import TOL_F16
+    from oracle import replay_oracle as ro
+    b = rb()
+    B, H, C, R, T = 3, 2, 32, 64, 6
+    cfg = b.make_config(_kind(kind), B, H, H, C, R, 16, b.F32, ckpt_dtype=b.F16)
+    S0 = synth.checkpoint(41, (B, H, C, R)).astype(np.float16)
+    S = torch.from_numpy(S0).cuda()
+    toks = _tokens(kind, 41, T, B, H, H, C, R)
+    Sref = S0.astype(np.float64)
+    params, A, D = {}, None, None
+    if kind == "mamba2":
+        A, D = synth.mamba2_params(41, H)
+        params = {"A": torch.from_numpy(A).cuda(), "D": torch.from_numpy(D).cuda()}
+    for t in range(T):
+        tok = synth.token(toks, t)
+        y = b.conv_decode_step(cfg, S, {k: torch.from_numpy(v).cuda() for k, v in tok.items()}, params)
+        if kind == "mamba2":
+            yr = ro.mamba2_token(Sref, tok["x"], tok["Bm"], tok["Cm"], tok["dt"], A, D)
+        else:
+            yr = ro.gdn_token(Sref, tok["q"], tok["k"], tok["v"], tok["alpha"], tok["beta"])
+        Sref[...] = Sref.astype(np.float16).astype(np.float64)
+        torch.cuda.synchronize()
+        err = ro.normwise_error(y[0].float().cpu().numpy(), yr)
+        assert err <= TOL_F16, (t, err)
+        Sg = S.float().cpu().numpy().astype(np.float64)
+        cerr = float(np.max(np.abs(Sg - Sref)) / np.max(np.abs(Sref)))
+        assert cerr <= TOL_F16, (t, cerr)

@@ -524,3 +524,75 @@ def test_quantized_checkpoint_rounds_at_every_flush():
     assert np.max(np.abs(sess.S - plain.S)) > 0
     with pytest.raises(ValueError):
         ro.Mamba2Session(A, D, S0, quantized_ckpt=True)
+
+
+# --------------------------------------------------------------------------
+# FP16 recurrence checkpoint
+# --------------------------------------------------------------------------
+
+def test_binary16_rounding_landmarks():
+    """IEEE binary16 (1 sign, 5 exponent bits with bias 15, 10 fraction bits) rounded to
+    nearest even, written out from the format: the oracle's fp16 checkpoint rounding."""
+    sess = ro.Mamba2Session(np.zeros(1), np.zeros(1), np.zeros((1, 1, 1, 4)), ckpt_dtype="f16")
+    u = 2.0 ** -10                           # spacing of binary16 in [1, 2)
+    cases = [
+        (1.0 + u / 2, 1.0),                  # tie, the even neighbour is 1
+        (1.0 + 3 * u / 2, 1.0 + 2 * u),      # tie, the even neighbour is above
+        (1.0 + u / 2 + 2.0 ** -30, 1.0 + u), # just above the tie
+        (65504.0, 65504.0),                  # largest finite
+        (65519.99, 65504.0),                 # below the overflow threshold 65520
+        (2.0 ** -24, 2.0 ** -24),            # smallest subnormal
+        (2.0 ** -25, 0.0),                   # tie between 0 and 2^-24: even is 0
+        (3 * 2.0 ** -26, 2.0 ** -24),        # above that tie
+        (2.0 ** -14 - 2.0 ** -24, 2.0 ** -14 - 2.0 ** -24),   # largest subnormal
+        (-(1.0 + 3 * u / 2), -(1.0 + 2 * u)),
+    ]
+    S = np.array([[[[v for v, _ in cases]]]], np.float64).reshape(1, 1, 1, -1)
+    got = sess._round(S).ravel()
+    np.testing.assert_array_equal(got, [w for _, w in cases])
+    with np.errstate(over="ignore"):
+        assert np.isinf(sess._round(np.array([65520.0]))[0])   # the overflow threshold rounds up
+
+
+def test_f16_checkpoint_rounds_at_load_and_every_flush():
+    """The fp16 session equals the fp32 session until a flush; at a flush its checkpoint is
+    the binary16 rounding of the state the fp32 recurrence reaches from the same start."""
+    B, H, G, P, N, cap = 2, 2, 1, 4, 32, 3
+    A, D = synth.mamba2_params(62, H)
+    S0 = synth.checkpoint(62, (B, H, P, N)).astype(np.float16).astype(np.float64)
+    toks = synth.mamba2_tokens(62, 7, B, H, G, P, N)
+    f16 = ro.Mamba2Session(A, D, S0, cap=cap, ckpt_dtype="f16")
+    f32 = ro.Mamba2Session(A, D, S0, cap=cap)
+    np.testing.assert_array_equal(f16.S, S0)
+    for t in range(cap - 1):
+        np.testing.assert_array_equal(f16.decode(synth.token(toks, t)), f32.decode(synth.token(toks, t)))
+    f16.decode(synth.token(toks, cap - 1))
+    f32.decode(synth.token(toks, cap - 1))
+    np.testing.assert_array_equal(f16.ckpt, f32.ckpt.astype(np.float16).astype(np.float64))
+    assert np.max(np.abs(f16.ckpt - f32.ckpt)) > 0
+    with pytest.raises(ValueError):
+        ro.Mamba2Session(A, D, S0, ckpt_dtype="bf16")
+    with pytest.raises(ValueError):
+        ro.Mamba2Session(A, D, S0, read_copy="fp8", quantized_ckpt=True, ckpt_dtype="f16")
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_f16_checkpoint_exact_on_dyadic_inputs(kind):
+    """With inputs whose recurrence stays on the binary16 grid (A = 0 and dt a power of two
+    for Mamba-2; alpha = 1, beta = 0 for GDN, so the state only decays by exactly 1 or
+    accumulates exactly), the fp16 and fp32 sessions agree bit for bit through flushes."""
+    B, H, G, P, N, cap = 1, 2, 1, 4, 16, 2
+    S0 = (np.arange(B * H * P * N).reshape(B, H, P, N) % 7 - 3) * 0.25
+    if kind == "mamba2":
+        A, D = np.zeros(H), np.ones(H)
+        toks = {"x": np.full((6, B, H, P), 0.5), "Bm": np.full((6, B, G, N), 0.25),
+                "Cm": np.full((6, B, G, N), 1.0), "dt": np.full((6, B, H), 0.125)}
+        a, b = (ro.Mamba2Session(A, D, S0, cap=cap, ckpt_dtype=c) for c in ("f16", "f32"))
+    else:
+        toks = {"q": np.full((6, B, G, N), 0.5), "k": np.full((6, B, G, N), 0.25),
+                "v": np.full((6, B, H, P), 1.0), "alpha": np.ones((6, B, H)), "beta": np.zeros((6, B, H))}
+        a, b = (ro.GDNSession(S0, cap=cap, ckpt_dtype=c) for c in ("f16", "f32"))
+    for t in range(6):
+        np.testing.assert_array_equal(a.decode(synth.token(toks, t)), b.decode(synth.token(toks, t)))
+        np.testing.assert_array_equal(a.ckpt, b.ckpt)
+    assert a.fc[0] == 3
