@@ -174,6 +174,32 @@ __device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return a.x * b.x + a.y
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
 
+// EL consecutive floats of LDS to registers and back (16-byte accesses when EL
+// is a multiple of 4; p then 16-byte aligned).
+template <int EL>
+__device__ __forceinline__ void lds_row_load(const float* p, float (&v)[EL]) {
+    if constexpr (EL % 4 == 0) {
+#pragma unroll
+        for (int m = 0; m < EL; m += 4) {
+            const f32x4 t = ld4(p + m);
+            v[m] = t.x; v[m + 1] = t.y; v[m + 2] = t.z; v[m + 3] = t.w;
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < EL; ++m) v[m] = p[m];
+    }
+}
+template <int EL>
+__device__ __forceinline__ void lds_row_store(float* p, const float (&v)[EL]) {
+    if constexpr (EL % 4 == 0) {
+#pragma unroll
+        for (int m = 0; m < EL; m += 4) st4(p + m, f32x4{v[m], v[m + 1], v[m + 2], v[m + 3]});
+    } else {
+#pragma unroll
+        for (int m = 0; m < EL; ++m) p[m] = v[m];
+    }
+}
+
 // Nontemporal 128-bit global load/store for the checkpoint stream.
 __device__ __forceinline__ f32x4 ld4_stream(const float* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));

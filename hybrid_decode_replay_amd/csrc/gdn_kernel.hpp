@@ -20,9 +20,13 @@
 // i = pos down to f: c_i = beta_i (k_i . r), r <- alpha_i (r - c_i k_i); then
 //     o = scale (S' r + sum_i c_i v_i).
 // One checkpoint product per token; the chain needs only the buffered k, alpha,
-// beta and costs O(d_k) per entry.  The drafts of a speculative append get one
-// chain each from the same checkpoint read (output-only evaluation, [TR]
-// section "Durum trafigini azaltma ve rollback'in basitlestirilmesi").
+// beta and costs O(d_k) per entry.  A chain runs on a row of 16 lanes (the
+// dot k_i . r reduces inside the row), so it never waits on the checkpoint
+// loads.  A single decode token runs its chain in every row of every wave,
+// with no workgroup barrier; the drafts of a speculative append get one chain
+// each, on separate rows, from the same checkpoint read (output-only
+// evaluation, [TR] section "Durum trafigini azaltma ve rollback'in
+// basitlestirilmesi").
 //
 // Fold of entries 0..f-1 in WY form (the intermediate state from small matrix
 // products, same section), with P_i = alpha_0 ... alpha_i:
@@ -47,7 +51,7 @@ __global__ __launch_bounds__(1024) void gdn_step_kernel(StepArgs a)
     constexpr int R = NB * 16;                  // d_k
     constexpr int RS = R + 4;
     constexpr int PRE = 4;
-    constexpr int RPL = (R + 63) / 64;          // chain elements per lane
+    constexpr int EL = R / 16;                  // chain elements per lane (one row of 16 lanes per chain)
     const int C = a.C;                          // d_v
     const TileIdx tix = tile_of(xcd_tile_index(), a.H, a.nsplit);
     const int b = tix.b, h = tix.h, tile = b * a.H + h;
@@ -70,11 +74,12 @@ __global__ __launch_bounds__(1024) void gdn_step_kernel(StepArgs a)
     float* vs = lds;                          // [vmax][cw]  entry v rows (own columns)
     float* ks = vs + (size_t)vmax * cw;       // [vmax][RS]  entry k rows
     float* qs = ks + (size_t)vmax * RS;       // [Tr][R]     query rows
-    float* rz = qs + (size_t)Tr * R;          // [Tr][R]     chain results r_0
-    float* al = rz + (size_t)Tr * R;          // [vmax]      alpha
+    float* rz = qs + (size_t)Tr * R;          // [max(Tr,4)][R] chain results r_0 (per token, or per wave)
+    float* al = rz + (size_t)(Tr > 4 ? Tr : 4) * R;   // [vmax] alpha
     float* be = al + vmax;                    // [vmax]      beta
     float* cc = be + vmax;                    // [Tr][vmax]  chain coefficients c_i
     float* ti = cc + (size_t)Tr * vmax;       // [16][17]    (I + A)^{-1}
+    float* tt = ti + 16 * 17;                 // [16][17]    gate products over entry ranges
 
     StageGeom G;
     G.bufc = a.bufc; G.bufr = a.bufr; G.bufs0 = a.bufs0; G.bufs1 = a.bufs1;
@@ -118,6 +123,16 @@ __global__ __launch_bounds__(1024) void gdn_step_kernel(StepArgs a)
             W = mfma16x16x4(kv.w, s[jb].w, W);
         }
         if (w == 0) {
+            // gate products tt[j][i] = alpha_{j+1} ... alpha_i (1 for i <= j), i, j < f:
+            // lane j multiplies along i, every product formed as a product
+            if (lane < 16) {
+                float p = 1.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    if (i > lane && i < f) p *= al[i];
+                    tt[lane * 17 + i] = p;
+                }
+            }
             // Gram k_i . k_j on MFMA (lane result rows i = lq*4 + r, column j = l16)
             f32x4 gm = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -125,16 +140,12 @@ __global__ __launch_bounds__(1024) void gdn_step_kernel(StepArgs a)
                 const float kv = arow ? ks[l16 * RS + 4 * d + lq] : 0.f;
                 gm = mfma16x16x4(kv, kv, gm);
             }
+            wave_lds_sync();
             // strictly lower triangle of A, written to ti as a scratch matrix
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = lq * 4 + r, j = l16;
-                float v = 0.f;
-                if (j < i && i < f) {
-                    float dec = 1.f;
-                    for (int m = j + 1; m <= i; ++m) dec *= al[m];
-                    v = be[i] * dec * gm[r];
-                }
+                const float v = (j < i && i < f) ? be[i] * tt[j * 17 + i] * gm[r] : 0.f;
                 ti[i * 17 + j] = v;
             }
             wave_lds_sync();
@@ -164,25 +175,18 @@ __global__ __launch_bounds__(1024) void gdn_step_kernel(StepArgs a)
         for (int r = 0; r < 4; ++r) {
             const int i = lq * 4 + r;
             float v = 0.f;
-            if (i < f) {
-                float P = 1.f;
-                for (int m = 0; m <= i; ++m) P *= al[m];
-                v = be[i] * (vs[i * cw + lc] - P * W[r]);
-            }
+            if (i < f) v = be[i] * (vs[i * cw + lc] - (al[0] * tt[i]) * W[r]);   // P_i = alpha_0 tt[0][i]
             rhs[r] = v;
         }
         // U = (I + A)^{-1} rhs, then scaled by the decay from entry i to the end of the fold
         f32x4 U = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < 4; ++r) U = mfma16x16x4(ti[l16 * 17 + lq * 4 + r], rhs[r], U);
-        float decay = 1.f;
-        for (int m = 0; m < f; ++m) decay *= al[m];
+        const float decay = al[0] * tt[f - 1];                       // P_{f-1}
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = lq * 4 + r;
-            float sfx = 1.f;
-            for (int m = i + 1; m < f; ++m) sfx *= al[m];
-            U[r] = (i < f) ? sfx * U[r] : 0.f;
+            U[r] = (i < f) ? tt[i * 17 + f - 1] * U[r] : 0.f;         // alpha_{i+1} ... alpha_{f-1}
         }
         // S'^T[j][v] = decay S0^T[j][v] + sum_i K[i][j] U~[i][v]
 #pragma unroll
@@ -206,52 +210,83 @@ __global__ __launch_bounds__(1024) void gdn_step_kernel(StepArgs a)
         if (a.qckpt && f > 0) rc_roundtrip<NB, RC>(s);
     }
 
-    // ---- 4. adjoint chains, one per new token (spread over the waves)
+    // ---- 4./5. adjoint chains and outputs.  A chain runs on one row of 16 lanes:
+    // lane j of the row holds elements EL*j .. EL*j+EL-1 of r (EL = d_k / 16), so
+    // k_i . r reduces inside the row by DPP, with no cross-row step or readlane.
+    // The gates are kept out of the vector update: with r = sig * rr and sig the
+    // product of the gates of the entries already passed, c_i = sig beta_i (k_i . rr)
+    // and rr <- rr - beta_i (k_i . rr) k_i, then sig <- alpha_i sig; r_0 = sig rr.
     if (a.mode != MODE_FLUSH) {
-        for (int t = w; t < T; t += waves) {
-            const int pos = len + t;
-            float r[RPL];
-#pragma unroll
-            for (int u = 0; u < RPL; ++u) {
-                const int e = lane + 64 * u;
-                r[u] = e < R ? qs[t * R + e] : 0.f;
-            }
-            for (int i = pos; i >= f; --i) {
+        const int rho = lane >> 4, j16 = lane & 15;
+        if constexpr (TMAX == 1) {
+            // one token: every row of every wave runs the chain itself (no workgroup
+            // barrier) and keeps the replay sum sum_i c_i v_i of its lane's column
+            float r[EL];
+            lds_row_load<EL>(qs + EL * j16, r);
+            float rep = 0.f, sig = 1.f;
+            for (int i = len; i >= f; --i) {
+                float kv[EL];
+                lds_row_load<EL>(ks + i * RS + EL * j16, kv);
                 float part = 0.f;
 #pragma unroll
-                for (int u = 0; u < RPL; ++u) {
-                    const int e = lane + 64 * u;
-                    if (e < R) part += ks[i * RS + e] * r[u];
-                }
-                const float c = be[i] * wave_sum_uniform(part);
-                const float alpha = al[i];
+                for (int m = 0; m < EL; ++m) part += kv[m] * r[m];
+                const float bd = be[i] * group_sum<16>(part);
+                rep += (sig * bd) * vs[i * cw + lc];
 #pragma unroll
-                for (int u = 0; u < RPL; ++u) {
-                    const int e = lane + 64 * u;
-                    if (e < R) r[u] = alpha * (r[u] - c * ks[i * RS + e]);
-                }
-                if (lane == 0) cc[t * vmax + i] = c;
+                for (int m = 0; m < EL; ++m) r[m] -= bd * kv[m];
+                sig *= al[i];
             }
 #pragma unroll
-            for (int u = 0; u < RPL; ++u) {
-                const int e = lane + 64 * u;
-                if (e < R) rz[t * R + e] = r[u];
-            }
-        }
-        __syncthreads();
-
-        // ---- 5. o_t = scale (S' r_0 + sum_i c_i v_i)
+            for (int m = 0; m < EL; ++m) r[m] *= sig;
+            // r_0 of this wave (every row holds the same values) -> wave-private LDS row
+            float* rw = rz + (size_t)w * R;
+            if (rho == 0) lds_row_store<EL>(rw + EL * j16, r);
+            wave_lds_sync();
+            float gacc = 0.f;
 #pragma unroll
-        for (int t = 0; t < TMAX; ++t) {
-            if (t < T) {
-                float gacc = 0.f;
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) gacc += dot4(s[nb], ld4(rz + t * R + nb * 16 + rq));
-                gacc = sum_over_row_groups(gacc);
+            for (int nb = 0; nb < NB; ++nb) gacc += dot4(s[nb], ld4(rw + nb * 16 + rq));
+            gacc = sum_over_row_groups(gacc);
+            if (lane < 16) st_io<IO>(a.y, ((size_t)b * a.H + h) * C + col, a.scale * (gacc + rep));
+        } else {
+            // several tokens: one chain per (wave, row) pair; coefficients and r_0 go
+            // through LDS to the output lanes
+            for (int t = w * 4 + rho; t < T; t += waves * 4) {
                 const int pos = len + t;
-                float rep = 0.f;
-                for (int i = f; i <= pos; ++i) rep += cc[t * vmax + i] * vs[i * cw + lc];
-                if (lane < 16) st_io<IO>(a.y, (((size_t)t * sB + b) * a.H + h) * C + col, a.scale * (gacc + rep));
+                float r[EL];
+                lds_row_load<EL>(qs + t * R + EL * j16, r);
+                float sig = 1.f;
+                for (int i = pos; i >= f; --i) {
+                    float kv[EL];
+                    lds_row_load<EL>(ks + i * RS + EL * j16, kv);
+                    float part = 0.f;
+#pragma unroll
+                    for (int m = 0; m < EL; ++m) part += kv[m] * r[m];
+                    const float bd = be[i] * group_sum<16>(part);
+#pragma unroll
+                    for (int m = 0; m < EL; ++m) r[m] -= bd * kv[m];
+                    if (j16 == 0) cc[t * vmax + i] = sig * bd;
+                    sig *= al[i];
+                }
+#pragma unroll
+                for (int m = 0; m < EL; ++m) r[m] *= sig;
+                lds_row_store<EL>(rz + t * R + EL * j16, r);
+            }
+            __syncthreads();
+
+            // o_t = scale (S' r_0 + sum_i c_i v_i)
+#pragma unroll
+            for (int t = 0; t < TMAX; ++t) {
+                if (t < T) {
+                    float gacc = 0.f;
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) gacc += dot4(s[nb], ld4(rz + t * R + nb * 16 + rq));
+                    gacc = sum_over_row_groups(gacc);
+                    const int pos = len + t;
+                    float rep = 0.f;
+                    for (int i = f; i <= pos; ++i) rep += cc[t * vmax + i] * vs[i * cw + lc];
+                    if (lane < 16)
+                        st_io<IO>(a.y, (((size_t)t * sB + b) * a.H + h) * C + col, a.scale * (gacc + rep));
+                }
             }
         }
     }
@@ -272,7 +307,8 @@ static hipError_t gdn_launch_nb(const StepArgs& a, hipStream_t s)
 {
     const size_t Tr = a.T > 0 ? a.T : 1;
     const size_t R = NB * 16, vmax = a.vmax;
-    const size_t lds = sizeof(float) * (vmax * (a.C / a.nsplit + R + 4) + 2 * Tr * R + 2 * vmax + Tr * vmax + 16 * 17);
+    const size_t lds = sizeof(float) * (vmax * (a.C / a.nsplit + R + 4) + Tr * R + (Tr > 4 ? Tr : 4) * R + 2 * vmax +
+                                        Tr * vmax + 2 * 16 * 17);
     auto k = gdn_step_kernel<NB, IO, TMAX, RC, CK>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
