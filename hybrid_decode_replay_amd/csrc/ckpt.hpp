@@ -28,6 +28,47 @@ __device__ __forceinline__ u32x2 f32_to_h4(f32x4 v) {
     return __builtin_bit_cast(u32x2, __builtin_convertvector(v, h16x4));
 }
 
+// Issuing a strip's loads and decoding them are separate steps, so the wave
+// keeps working (on LDS data) while the loads are in flight and waits only
+// where the values are first needed.  The loaded words land in the state
+// registers themselves (fp16: the word of blocks 2q and 2q+1 in s[2q]) and
+// are decoded in place, so a step that may take either of two sources (the
+// checkpoint or its read copy) holds one set of registers.
+template <int NB, int CK>
+__device__ __forceinline__ void ckpt_issue(const void* ck, size_t strip, int lane, f32x4 (&s)[NB])
+{
+    if constexpr (CK == CK_F32) {
+        const float* p = static_cast<const float*>(ck) + (strip * NB * 64 + lane) * 4;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) s[nb] = ld4_stream(p + (size_t)nb * 256);
+    } else if constexpr (NB == 1) {
+        const u32x2 v = __builtin_nontemporal_load(static_cast<const u32x2*>(ck) + strip * 64 + lane);
+        s[0] = __builtin_bit_cast(f32x4, u32x4{v.x, v.y, 0u, 0u});
+    } else {
+        const u32x4* p = static_cast<const u32x4*>(ck) + strip * (NB / 2) * 64 + lane;
+#pragma unroll
+        for (int q = 0; q < NB / 2; ++q) s[2 * q] = __builtin_bit_cast(f32x4, __builtin_nontemporal_load(p + q * 64));
+    }
+}
+
+template <int NB, int CK>
+__device__ __forceinline__ void ckpt_decode(f32x4 (&s)[NB])
+{
+    if constexpr (CK == CK_F16) {
+        if constexpr (NB == 1) {
+            const u32x4 w = __builtin_bit_cast(u32x4, s[0]);
+            s[0] = h4_to_f32(u32x2{w.x, w.y});
+        } else {
+#pragma unroll
+            for (int q = 0; q < NB / 2; ++q) {
+                const u32x4 w = __builtin_bit_cast(u32x4, s[2 * q]);
+                s[2 * q] = h4_to_f32(u32x2{w.x, w.y});
+                s[2 * q + 1] = h4_to_f32(u32x2{w.z, w.w});
+            }
+        }
+    }
+}
+
 template <int NB, int CK>
 __device__ __forceinline__ void ckpt_load(const void* ck, size_t strip, int lane, f32x4 (&s)[NB])
 {

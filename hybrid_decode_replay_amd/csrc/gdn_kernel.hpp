@@ -97,20 +97,22 @@ __global__ __launch_bounds__(1024) void gdn_step_kernel(StepArgs a)
     ScalarRaw sr;
     stage_issue<IO, R, PRE, false>(stg, tid, nthr, pre, sr);
     // a step that folds nothing reads the low-precision copy when there is one
+    // (loads issued now, decoded where the values are first used)
     const size_t strip_index = (size_t)tile * (C >> 4) + (c0 >> 4) + w;
     f32x4 s[NB];
     bool from_copy = false;
     if constexpr (RC != RC_NONE) from_copy = (f == 0);
     if (from_copy) {
-        if constexpr (RC != RC_NONE) rc_load<NB, RC>(a.rcopy, a.rscale, strip_index, lane, s);
+        if constexpr (RC != RC_NONE) rc_issue<NB, RC>(a.rcopy, a.rscale, strip_index, lane, s);
     } else {
-        ckpt_load<NB, CK>(a.ckpt, strip_index, lane, s);
+        ckpt_issue<NB, CK>(a.ckpt, strip_index, lane, s);
     }
     stage_publish<IO, R, PRE>(stg, tid, nthr, pre, sr);
     __syncthreads();
 
     // ---- 3. fold the first f entries (WY form on MFMA)
     if (f > 0) {
+        ckpt_decode<NB, CK>(s);
         // W[i][v] = (S0 k_i)[v]; lane result rows i = lq*4 + r, column col
         f32x4 W = {0.f, 0.f, 0.f, 0.f};
         const bool arow = l16 < f;
@@ -242,6 +244,10 @@ __global__ __launch_bounds__(1024) void gdn_step_kernel(StepArgs a)
             float* rw = rz + (size_t)w * R;
             if (rho == 0) lds_row_store<EL>(rw + EL * j16, r);
             wave_lds_sync();
+            if (f == 0) {
+                if (from_copy) rc_decode<NB, RC>(s);
+                else ckpt_decode<NB, CK>(s);
+            }
             float gacc = 0.f;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) gacc += dot4(s[nb], ld4(rw + nb * 16 + rq));
@@ -272,6 +278,10 @@ __global__ __launch_bounds__(1024) void gdn_step_kernel(StepArgs a)
                 lds_row_store<EL>(rz + t * R + EL * j16, r);
             }
             __syncthreads();
+            if (f == 0) {
+                if (from_copy) rc_decode<NB, RC>(s);
+                else ckpt_decode<NB, CK>(s);
+            }
 
             // o_t = scale (S' r_0 + sum_i c_i v_i)
 #pragma unroll

@@ -88,21 +88,26 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
     ScalarRaw sr;
     stage_issue<IO, R, PRE, true>(stg, tid, nthr, pre, sr);
 
-    // ---- 2. checkpoint strip -> registers (128-bit loads, ckpt.hpp)
+    // ---- 2. checkpoint strip loads (128-bit, ckpt.hpp), decoded where first used
     // a step that folds nothing reads the low-precision copy when there is one
     const size_t strip_index = (size_t)tile * (C >> 4) + (c0 >> 4) + w;
     f32x4 s[NB];
     bool from_copy = false;
     if constexpr (RC != RC_NONE) from_copy = (f == 0);
     if (from_copy) {
-        if constexpr (RC != RC_NONE) rc_load<NB, RC>(a.rcopy, a.rscale, strip_index, lane, s);
+        if constexpr (RC != RC_NONE) rc_issue<NB, RC>(a.rcopy, a.rscale, strip_index, lane, s);
     } else {
-        ckpt_load<NB, CK>(a.ckpt, strip_index, lane, s);
+        ckpt_issue<NB, CK>(a.ckpt, strip_index, lane, s);
     }
 
     // ---- 3. publish the staged rows
     stage_publish<IO, R, PRE>(stg, tid, nthr, pre, sr);
     __syncthreads();
+    // An fp16 checkpoint without a copy is decoded here: the shorter register
+    // life of the raw words keeps the kernel at six waves per SIMD, which beats
+    // overlapping the replay terms with the loads.
+    constexpr bool EARLY_DECODE = CK == CK_F16 && RC == RC_NONE;
+    if constexpr (EARLY_DECODE) ckpt_decode<NB, CK>(s);
 
     const float Ah = a.A[h];
 
@@ -110,6 +115,7 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
     // sums of dt over an entry range come from the prefix sums: sum_{lo<=i<hi} = ps[hi-1] - ps[lo-1]
     // (with dt >= 0 and A_h <= 0 every exponent is <= 0 up to the rounding of that difference)
     if (f > 0) {
+        if constexpr (!EARLY_DECODE) ckpt_decode<NB, CK>(s);
         const float pf = ps[f - 1];
         const float decay = expf(pf * Ah);
         if constexpr (MFMA_FOLD) {
@@ -192,6 +198,11 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
                             rep += readlane(coef, 4 * e) * xs[min(f + jj0 + e, pos) * cw + lc];
                     }
                     gdec = expf((ps[pos] - (f > 0 ? ps[f - 1] : 0.f)) * Ah);
+                }
+                // the checkpoint values are needed from here on
+                if (!EARLY_DECODE && t == 0 && f == 0) {
+                    if (from_copy) rc_decode<NB, RC>(s);
+                    else ckpt_decode<NB, CK>(s);
                 }
                 // checkpoint read-out (S' C_t)[col], reduced over the four row groups
                 float gacc = 0.f;

@@ -93,30 +93,33 @@ __device__ __forceinline__ size_t rc_offset(size_t strip_index, int q, int lane)
 }
 
 // ---- FP8: load + dequantize, quantize + store ---------------------------------
+// Loads are issued into raw words and decoded where the values are needed, so
+// the wave can work on other data while they are in flight.
 template <int NB>
-__device__ __forceinline__ void rc_fp8_load(const uint8_t* base, size_t strip_index, int lane, f32x4 (&s)[NB])
+__device__ __forceinline__ void rc_fp8_issue(const uint8_t* base, size_t strip_index, int lane, uint32_t (&w)[NB])
 {
     constexpr int BPL = 4 * NB;
     if constexpr (BPL >= 16) {
 #pragma unroll
         for (int q = 0; q < NB / 4; ++q) {
             const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + rc_offset<BPL>(strip_index, q, lane)));
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], false);
-                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[k], true);
-                s[q * 4 + k] = f32x4{lo[0], lo[1], hi[0], hi[1]};
-            }
+            w[q * 4] = v.x; w[q * 4 + 1] = v.y; w[q * 4 + 2] = v.z; w[q * 4 + 3] = v.w;
         }
     } else {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(base + rc_offset<BPL>(strip_index, 0, lane) + 4 * nb);
-            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-            s[nb] = f32x4{lo[0], lo[1], hi[0], hi[1]};
-        }
+        for (int nb = 0; nb < NB; ++nb)
+            w[nb] = *reinterpret_cast<const uint32_t*>(base + rc_offset<BPL>(strip_index, 0, lane) + 4 * nb);
+    }
+}
+
+template <int NB>
+__device__ __forceinline__ void rc_fp8_decode(const uint32_t (&w)[NB], f32x4 (&s)[NB])
+{
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[nb], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[nb], true);
+        s[nb] = f32x4{lo[0], lo[1], hi[0], hi[1]};
     }
 }
 
@@ -144,13 +147,12 @@ __device__ __forceinline__ void rc_fp8_store(uint8_t* base, size_t strip_index, 
 
 // ---- MXFP4: load + dequantize, quantize + store --------------------------------
 template <int NB>
-__device__ __forceinline__ void rc_fp4_load(const uint8_t* codes, const uint8_t* scales, size_t strip_index, int lane,
-                                            f32x4 (&s)[NB])
+__device__ __forceinline__ void rc_fp4_issue(const uint8_t* codes, const uint8_t* scales, size_t strip_index, int lane,
+                                             uint32_t (&w)[NB / 2], uint32_t (&sc)[NB / 2])
 {
     static_assert(NB % 2 == 0, "MXFP4 groups need block pairs");
     constexpr int BPL = 2 * NB;
     constexpr int NP = NB / 2;                       // groups (block pairs) per lane
-    uint32_t w[NP];
     if constexpr (BPL >= 16) {
 #pragma unroll
         for (int q = 0; q < NB / 8; ++q) {
@@ -162,9 +164,16 @@ __device__ __forceinline__ void rc_fp4_load(const uint8_t* codes, const uint8_t*
         for (int p = 0; p < NP; ++p)
             w[p] = *reinterpret_cast<const uint32_t*>(codes + rc_offset<BPL>(strip_index, 0, lane) + 4 * p);
     }
-    const uint8_t* sc = scales + (strip_index * 16 + (lane & 15)) * NP;
+    const uint8_t* scp = scales + (strip_index * 16 + (lane & 15)) * NP;
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
+    for (int p = 0; p < NP; ++p) sc[p] = scp[p];
+}
+
+template <int NB>
+__device__ __forceinline__ void rc_fp4_decode(const uint32_t (&w)[NB / 2], const uint32_t (&sc)[NB / 2], f32x4 (&s)[NB])
+{
+#pragma unroll
+    for (int p = 0; p < NB / 2; ++p) {
         const float scale = e8m0_to_f32(sc[p]);
         const auto b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[p], scale, 0);
         const auto b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[p], scale, 1);
@@ -274,12 +283,50 @@ __device__ __forceinline__ void rc_store(uint8_t* codes, uint8_t* scales, size_t
     else if constexpr (RC == RC_MXFP4) rc_fp4_store<NB>(codes, scales, strip_index, lane, s);
 }
 
+// Read-copy words of a strip, issued into the state registers (fp8: the word
+// of block nb in s[nb].x; MXFP4: the codes of group p in s[2p].x and its
+// scale in s[2p].y) and decoded in place where first needed.
 template <int NB, int RC>
-__device__ __forceinline__ void rc_load(const uint8_t* codes, const uint8_t* scales, size_t strip_index, int lane,
-                                        f32x4 (&s)[NB])
+__device__ __forceinline__ void rc_issue(const uint8_t* codes, const uint8_t* scales, size_t strip_index, int lane,
+                                         f32x4 (&s)[NB])
 {
-    if constexpr (RC == RC_FP8) rc_fp8_load<NB>(codes, strip_index, lane, s);
-    else if constexpr (RC == RC_MXFP4) rc_fp4_load<NB>(codes, scales, strip_index, lane, s);
+    if constexpr (RC == RC_FP8) {
+        uint32_t w[NB];
+        rc_fp8_issue<NB>(codes, strip_index, lane, w);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) s[nb].x = __builtin_bit_cast(float, w[nb]);
+    } else if constexpr (RC == RC_MXFP4) {
+        uint32_t w[NB / 2], sc[NB / 2];
+        rc_fp4_issue<NB>(codes, scales, strip_index, lane, w, sc);
+#pragma unroll
+        for (int p = 0; p < NB / 2; ++p) {
+            s[2 * p].x = __builtin_bit_cast(float, w[p]);
+            s[2 * p].y = __builtin_bit_cast(float, sc[p]);
+        }
+    }
+}
+
+template <int NB, int RC>
+__device__ __forceinline__ void rc_decode(f32x4 (&s)[NB])
+{
+    if constexpr (RC == RC_FP8) {
+        uint32_t w[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const float x = s[nb].x;                 // bit_cast of a vector component goes through a scalar
+            w[nb] = __builtin_bit_cast(uint32_t, x);
+        }
+        rc_fp8_decode<NB>(w, s);
+    } else if constexpr (RC == RC_MXFP4) {
+        uint32_t w[NB / 2], sc[NB / 2];
+#pragma unroll
+        for (int p = 0; p < NB / 2; ++p) {
+            const float x = s[2 * p].x, y = s[2 * p].y;   // via scalars (see above)
+            w[p] = __builtin_bit_cast(uint32_t, x);
+            sc[p] = __builtin_bit_cast(uint32_t, y);
+        }
+        rc_fp4_decode<NB>(w, sc, s);
+    }
 }
 
 }  // namespace rs
