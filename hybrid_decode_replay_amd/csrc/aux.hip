@@ -85,28 +85,22 @@ __device__ __forceinline__ size_t frag_to_logical(size_t q, int C, int R)
     return tile * (size_t)C * R + (size_t)c * R + r;
 }
 
-// One thread per lane-block q (4 consecutive values of a logical row); T is
-// the storage type (float or a 16-bit word).
-template <int CK, class T>
-__global__ void tiles_to_logical_kernel(const T* ck, T* out, size_t n4, int C, int R)
+// One thread per lane-block q (4 consecutive values of a logical row), moved
+// as one word W (16 bytes of fp32 or 8 bytes of fp16).
+template <int CK, class W>
+__global__ void tiles_to_logical_kernel(const W* ck, W* out, size_t n4, int C, int R)
 {
     const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (q >= n4) return;
-    const T* src = ck + ckpt_elem_offset<CK>(q, R >> 4);
-    T* dst = out + frag_to_logical(q, C, R);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = src[i];
+    out[frag_to_logical(q, C, R) / 4] = ck[ckpt_elem_offset<CK>(q, R >> 4) / 4];
 }
 
-template <int CK, class T>
-__global__ void logical_to_tiles_kernel(const T* in, T* ck, size_t n4, int C, int R)
+template <int CK, class W>
+__global__ void logical_to_tiles_kernel(const W* in, W* ck, size_t n4, int C, int R)
 {
     const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (q >= n4) return;
-    const T* src = in + frag_to_logical(q, C, R);
-    T* dst = ck + ckpt_elem_offset<CK>(q, R >> 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = src[i];
+    ck[ckpt_elem_offset<CK>(q, R >> 4) / 4] = in[frag_to_logical(q, C, R) / 4];
 }
 
 hipError_t launch_tiles_to_logical(const void* ckpt, void* out, int tiles, int C, int R, int ck, hipStream_t s)
@@ -114,11 +108,11 @@ hipError_t launch_tiles_to_logical(const void* ckpt, void* out, int tiles, int C
     const size_t n4 = (size_t)tiles * C * R / 4;
     const dim3 grid((unsigned)((n4 + 255) / 256)), block(256);
     if (ck == CK_F16)
-        hipLaunchKernelGGL((tiles_to_logical_kernel<CK_F16, uint16_t>), grid, block, 0, s,
-                           static_cast<const uint16_t*>(ckpt), static_cast<uint16_t*>(out), n4, C, R);
+        hipLaunchKernelGGL((tiles_to_logical_kernel<CK_F16, u32x2>), grid, block, 0, s,
+                           static_cast<const u32x2*>(ckpt), static_cast<u32x2*>(out), n4, C, R);
     else
-        hipLaunchKernelGGL((tiles_to_logical_kernel<CK_F32, float>), grid, block, 0, s,
-                           static_cast<const float*>(ckpt), static_cast<float*>(out), n4, C, R);
+        hipLaunchKernelGGL((tiles_to_logical_kernel<CK_F32, u32x4>), grid, block, 0, s,
+                           static_cast<const u32x4*>(ckpt), static_cast<u32x4*>(out), n4, C, R);
     return hipGetLastError();
 }
 
@@ -127,11 +121,11 @@ hipError_t launch_logical_to_tiles(const void* in, void* ckpt, int tiles, int C,
     const size_t n4 = (size_t)tiles * C * R / 4;
     const dim3 grid((unsigned)((n4 + 255) / 256)), block(256);
     if (ck == CK_F16)
-        hipLaunchKernelGGL((logical_to_tiles_kernel<CK_F16, uint16_t>), grid, block, 0, s,
-                           static_cast<const uint16_t*>(in), static_cast<uint16_t*>(ckpt), n4, C, R);
+        hipLaunchKernelGGL((logical_to_tiles_kernel<CK_F16, u32x2>), grid, block, 0, s,
+                           static_cast<const u32x2*>(in), static_cast<u32x2*>(ckpt), n4, C, R);
     else
-        hipLaunchKernelGGL((logical_to_tiles_kernel<CK_F32, float>), grid, block, 0, s,
-                           static_cast<const float*>(in), static_cast<float*>(ckpt), n4, C, R);
+        hipLaunchKernelGGL((logical_to_tiles_kernel<CK_F32, u32x4>), grid, block, 0, s,
+                           static_cast<const u32x4*>(in), static_cast<u32x4*>(ckpt), n4, C, R);
     return hipGetLastError();
 }
 

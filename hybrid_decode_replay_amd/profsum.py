@@ -4,6 +4,8 @@ Usage (after the rocprofv3 runs whose commands are passed in, for the record):
     python -m hybrid_decode_replay_amd.profsum trace KT_DIR OUT.md "COMMAND"
     python -m hybrid_decode_replay_amd.profsum traffic FETCH_DIR WRITE_DIR OUT.txt KERNEL GRID \\
         "FETCH_SIZE COMMAND" "WRITE_SIZE COMMAND"
+KERNEL is a name with template arguments as rocprofv3 prints them (one instantiation,
+e.g. "mamba2_step_kernel<8, 1, 1, true, 0, 0>") or a bare name (all instantiations).
 
 trace    per (kernel, grid size) call counts and durations from *_kernel_trace.csv of a
          `rocprofv3 --kernel-trace` run (one row per workload of the program).
@@ -76,9 +78,15 @@ def counters(path, cname):
     for r in csv.DictReader(open(path)):
         if r["Counter_Name"] != cname:
             continue
-        key = (short(r["Kernel_Name"]).split("<")[0], int(r["Grid_Size"]))
+        key = (short(r["Kernel_Name"]), int(r["Grid_Size"]))
         out.setdefault(key, []).append(float(r["Counter_Value"]))
     return out
+
+
+def _matches(name, want):
+    """A kernel given with template arguments matches exactly; a bare name matches every
+    instantiation."""
+    return name == want if "<" in want else name.split("<")[0] == want
 
 
 def traffic(fetch_dir, write_dir, out, kernel, grid, fetch_cmd, write_cmd):
@@ -87,7 +95,7 @@ def traffic(fetch_dir, write_dir, out, kernel, grid, fetch_cmd, write_cmd):
     write = counters(_one(os.path.join(write_dir, "**", "*counter_collection.csv")), "WRITE_SIZE")
 
     def pick(d, name, g=None):
-        vals = [v for (k, gg), vs in d.items() if k == name and (g is None or gg == g) for v in vs]
+        vals = [v for (k, gg), vs in d.items() if _matches(k, name) and (g is None or gg == g) for v in vs]
         if not vals:
             raise KeyError((name, g))
         return vals
@@ -104,7 +112,7 @@ def traffic(fetch_dir, write_dir, out, kernel, grid, fetch_cmd, write_cmd):
              "# calibration: stream_copy_kernel reads and writes 1 GiB per dispatch",
              f"kernel = {kernel}",
              f"grid_threads = {grid}",
-             f"kernel_source_sha = {source_sha(kernel)}",
+             f"kernel_source_sha = {source_sha(kernel.split('<')[0])}",
              f"dispatches = {n}",
              f"fetch_scale = {s_fetch:.4f}",
              f"write_scale = {s_write:.4f}",

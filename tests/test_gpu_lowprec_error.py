@@ -3,15 +3,19 @@
 Stand-in for the pages' quantization study (Qwen3.5-4B at 128K tokens, GPQA-Diamond;
 [TR] "NVIDIA ve Dao AI Lab ...", section "Kuantizasyon hatasinin sinirlandirilmasi"):
 the batch-128 Gated DeltaNet layer (32 heads, d_k = d_v = 128, bf16 q/k/v, fp32
-gates) decodes 8192 steps from an N(0, 0.1) checkpoint in five variants:
+gates) decodes 8192 steps from an N(0, 0.1) checkpoint in seven variants:
   R0 fp32 checkpoint only          R1 fp32 checkpoint + FP8 read copy
   R2 fp32 checkpoint + MXFP4 copy  Q1 FP8 checkpoint only    Q2 MXFP4 checkpoint only
+  H0 fp16 checkpoint only          H2 fp16 checkpoint + MXFP4 copy
 The normwise output error against the fp64 recurrence is measured on four
-sequences and reported at 1K, 2K, 4K and 8K steps and as the maximum.  The
-claims checked are the ones the pages make: read error stays at the level of one
+sequences and reported as the maximum over the windows ending at 1K, 2K, 4K and
+8K steps, the overall maximum and the mean over the last 1K steps.  The claims
+checked are the ones the pages make: read error stays at the level of one
 quantization of the checkpoint (it does not accumulate: the error late in the run
-is not larger than early on), and a low-precision checkpoint inside the
-recurrence is worse than the same format used only for reads.
+is not larger than early on), a low-precision checkpoint inside the recurrence is
+worse than the same format used only for reads, and an fp16 recurrence stays
+close to fp32 (the pages give no tolerance for it; the bound below is the bf16
+output rounding plus a few binary16 units).
 """
 import numpy as np
 import pytest
@@ -32,18 +36,21 @@ def test_low_precision_error_over_8192_steps():
     from oracle import replay_oracle as ro
     B, H, D, T, CH = 128, 32, 128, 8192, 512
     sample = [0, 41, 86, 127]
-    variants = {"R0": (b.NONE, 0), "R1": (b.FP8_E4M3, 0), "R2": (b.MXFP4, 0),
-                "Q1": (b.FP8_E4M3, b.FLAG_QUANTIZED_CKPT), "Q2": (b.MXFP4, b.FLAG_QUANTIZED_CKPT)}
-    S0 = synth.checkpoint_device(4, (B, H, D, D), "cuda")
+    variants = {"R0": (b.NONE, 0, b.F32), "R1": (b.FP8_E4M3, 0, b.F32), "R2": (b.MXFP4, 0, b.F32),
+                "Q1": (b.FP8_E4M3, b.FLAG_QUANTIZED_CKPT, b.F32), "Q2": (b.MXFP4, b.FLAG_QUANTIZED_CKPT, b.F32),
+                "H0": (b.NONE, 0, b.F16), "H2": (b.MXFP4, 0, b.F16)}
+    # one starting checkpoint for every variant: N(0, 0.1) rounded to binary16, so the fp16
+    # variants start from the same values as the others
+    S0 = synth.checkpoint_device(4, (B, H, D, D), "cuda").half().float()
     states = {}
-    for name, (rc, fl) in variants.items():
-        st = b.ReplayState(b.make_config(b.GDN, B, H, H, D, D, 16, b.BF16, read_copy=rc, flags=fl))
+    for name, (rc, fl, ck) in variants.items():
+        st = b.ReplayState(b.make_config(b.GDN, B, H, H, D, D, 16, b.BF16, read_copy=rc, flags=fl, ckpt_dtype=ck))
         st.load_checkpoint(S0)
         states[name] = st
     S = S0[sample].double().cpu().numpy()
     ys = torch.empty((len(variants), CH, B, H, D), dtype=torch.bfloat16, device="cuda")
     err = {name: np.zeros(T) for name in variants}
-    print("[lowprec] 5 variants x 8192 steps", flush=True)
+    print(f"[lowprec] {len(variants)} variants x {T} steps", flush=True)
     for c0 in range(0, T, CH):
         toks = synth.gdn_tokens_device(1000 + c0, CH, B, H, H, D, D, "cuda")
         for i, st in enumerate(states.values()):
@@ -58,12 +65,15 @@ def test_low_precision_error_over_8192_steps():
     rows = []
     for name in variants:
         e = err[name]
-        rows.append((name, *[float(np.max(e[max(0, s - 1024):s])) for s in (1024, 2048, 4096, 8192)], float(e.max())))
+        rows.append((name, *[float(np.max(e[max(0, s - 1024):s])) for s in (1024, 2048, 4096, 8192)], float(e.max()),
+                     float(np.mean(e[-1024:]))))
         print(f"[lowprec] {name}: max error over steps ending at 1K/2K/4K/8K = "
-              + " / ".join(f"{v:.3e}" for v in rows[-1][1:5]) + f"; max {rows[-1][5]:.3e}", flush=True)
+              + " / ".join(f"{v:.3e}" for v in rows[-1][1:5]) + f"; max {rows[-1][5]:.3e}"
+              + f"; mean over the last 1K {rows[-1][6]:.3e}", flush=True)
     e = {r[0]: r for r in rows}
     assert e["R0"][5] <= 2e-2                                   # bf16 output rounding only
-    for r in ("R1", "R2"):
+    assert e["H0"][5] <= 2e-2 and e["H0"][6] <= e["R0"][6] + 8 * 2.0 ** -11
+    for r in ("R1", "R2", "H2"):
         assert e[r][4] <= 2.0 * e[r][1] + 1e-3, r               # read error does not accumulate
-    assert np.mean(err["Q1"][-1024:]) > np.mean(err["R1"][-1024:])
-    assert np.mean(err["Q2"][-1024:]) > np.mean(err["R2"][-1024:])
+    assert e["Q1"][6] > e["R1"][6]
+    assert e["Q2"][6] > e["R2"][6]
