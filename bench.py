@@ -24,6 +24,9 @@ The JSON line also carries:
   fp16_checkpoint
                 both batch-256 layers with an fp16 recurrence checkpoint, and
                 the conventional kernel on an fp16 state
+  flush_schedule_mamba2_b256
+                per-step launch time (p50, p99, max) with lockstep folds and
+                with staggered flush phases
   cpu_baseline  the fp64 oracle on the host cores over a bounded sample
 With --sweep FILE, both layers are also timed at batch 1..512 (replay and
 conventional, eagerly and as HIP-graph replays), one JSON line per point in FILE.
@@ -138,7 +141,7 @@ def cpu_baseline(H, G, P, N, budget_s=10.0, max_s=30.0):
 class Layer:
     """Device-side state, parameters and pre-drawn inputs of one synthetic layer."""
 
-    def __init__(self, rb, synth, torch, dev, kind, B, steps, seed, cap=16, read_copy=None, ckpt="f32"):
+    def __init__(self, rb, synth, torch, dev, kind, B, steps, seed, cap=16, read_copy=None, ckpt="f32", flags=0):
         self.rb, self.torch, self.dev, self.kind, self.B = rb, torch, dev, kind, B
         shp = MAMBA2 if kind == "mamba2" else GDN
         self.H, self.G, self.C, self.R = shp["H"], shp["G"], shp["C"], shp["R"]
@@ -147,7 +150,8 @@ class Layer:
         self.ckpt = ckpt
         rc = {None: rb.NONE, "fp8": rb.FP8_E4M3, "mxfp4": rb.MXFP4}[read_copy]
         self.cfg = rb.make_config(rb.MAMBA2 if kind == "mamba2" else rb.GDN, B, self.H, self.G, self.C, self.R,
-                                  cap, rb.BF16, read_copy=rc, ckpt_dtype=rb.F16 if ckpt == "f16" else rb.F32)
+                                  cap, rb.BF16, read_copy=rc, ckpt_dtype=rb.F16 if ckpt == "f16" else rb.F32,
+                                  flags=flags)
         self.S0 = synth.checkpoint_device(seed, (B, self.H, self.C, self.R), dev).to(rb.ckpt_torch_dtype(self.cfg))
         if kind == "mamba2":
             A, D = synth.mamba2_params(seed, self.H)
@@ -200,8 +204,11 @@ def time_replay_decode(L, K, W, stream):
     per = [s.elapsed_time(e) for s, e in ev]
     flush = [p for i, p in enumerate(per) if (first + i) % L.cap == L.cap - 1]
     nonflush = [p for i, p in enumerate(per) if (first + i) % L.cap != L.cap - 1]
+    srt = sorted(per)
     return {"steps": K, "total_ms": total, "avg_launch_ms": sum(per) / K,
-            "flush_ms": sum(flush) / max(1, len(flush)), "nonflush_ms": sum(nonflush) / max(1, len(nonflush))}
+            "flush_ms": sum(flush) / max(1, len(flush)), "nonflush_ms": sum(nonflush) / max(1, len(nonflush)),
+            "max_launch_ms": srt[-1], "p99_launch_ms": srt[min(K - 1, int(0.99 * K))],
+            "p50_launch_ms": srt[K // 2]}
 
 
 def time_conv_decode(L, K, stream, t0=0):
@@ -454,6 +461,18 @@ def main():
             del Lh
             torch.cuda.empty_cache()
         out["fp16_checkpoint"] = f16
+        # flush schedule at batch 256: lockstep folds (every 16th step folds every sequence)
+        # against staggered phases (about 1/16 of the sequences fold on each step)
+        sched = {}
+        for name, fl in (("lockstep", 0), ("staggered", rb.FLAG_STAGGER_FLUSH)):
+            Lg = Layer(rb, synth, torch, dev, "mamba2", B, 256 + 32 + 4, seed=8, flags=fl)
+            rg = time_replay_decode(Lg, 256, 32, stream)
+            sched[name] = {"ms_per_step": round(rg["total_ms"] / rg["steps"], 5),
+                           "launch_ms_p50": round(rg["p50_launch_ms"], 5), "launch_ms_p99": round(rg["p99_launch_ms"], 5),
+                           "launch_ms_max": round(rg["max_launch_ms"], 5)}
+            del Lg
+            torch.cuda.empty_cache()
+        out["flush_schedule_mamba2_b256"] = sched
 
     if args.sweep:
         with open(args.sweep, "w") as f:

@@ -29,6 +29,7 @@ NONE, F32, F16, BF16, FP8_E4M3, MXFP4 = range(6)
 DEVERR_COMMIT_CLAMPED = 0x1
 FLAG_VALU_FOLD = 0x1
 FLAG_QUANTIZED_CKPT = 0x2
+FLAG_STAGGER_FLUSH = 0x4
 
 
 class ReplayConfig(ctypes.Structure):

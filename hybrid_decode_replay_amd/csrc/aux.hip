@@ -7,9 +7,10 @@
 namespace rs {
 
 // ---- bookkeeping ----------------------------------------------------------
-// Book layout: int32 [2 copies][3 fields][B]; field 0 = len, 1 = pend, 2 = fc.
-// Each launch that changes the bookkeeping reads copy `parity` and writes copy
-// `parity ^ 1`, so every workgroup of a launch sees the same pre-launch values.
+// Book layout: int32 [2 copies][4 fields][B]; field 0 = len, 1 = pend, 2 = fc,
+// 3 = lim (length of the current window).  Each launch that changes the
+// bookkeeping reads copy `parity` and writes copy `parity ^ 1`, so every
+// workgroup of a launch sees the same pre-launch values.
 
 // Commit (accepted != null) or rollback (accepted == null): the accepted
 // prefix advances the pointer, the rest of the drafts is dropped.
@@ -17,8 +18,8 @@ __global__ void book_commit_kernel(int32_t* book, uint32_t* err, int B, int pari
 {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= B) return;
-    const int32_t* cur = book + (size_t)parity * 3 * B;
-    int32_t* nxt = book + (size_t)(parity ^ 1) * 3 * B;
+    const int32_t* cur = book + (size_t)parity * 4 * B;
+    int32_t* nxt = book + (size_t)(parity ^ 1) * 4 * B;
     const int pend = cur[B + b];
     const int a = accepted ? accepted[b] : 0;
     const int ac = a < 0 ? 0 : (a > pend ? pend : a);
@@ -26,13 +27,21 @@ __global__ void book_commit_kernel(int32_t* book, uint32_t* err, int B, int pari
     nxt[b] = cur[b] + ac;
     nxt[B + b] = 0;
     nxt[2 * B + b] = cur[2 * B + b];
+    nxt[3 * B + b] = cur[3 * B + b];
 }
 
-__global__ void book_reset_kernel(int32_t* book, uint32_t* err, int B, int parity)
+// len = pend = fc = 0; lim = cap, or 1 + (b mod cap) for staggered flushes.
+__global__ void book_reset_kernel(int32_t* book, uint32_t* err, int B, int parity, int cap, int stagger)
 {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < 3 * B) book[(size_t)parity * 3 * B + i] = 0;
-    if (i == 0) *err = 0u;
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < B) {
+        int32_t* cur = book + (size_t)parity * 4 * B;
+        cur[b] = 0;
+        cur[B + b] = 0;
+        cur[2 * B + b] = 0;
+        cur[3 * B + b] = stagger ? 1 + b % cap : cap;
+    }
+    if (b == 0) *err = 0u;
 }
 
 hipError_t launch_book_commit(int32_t* book, uint32_t* err, int B, int parity, const int32_t* accepted,
@@ -42,9 +51,10 @@ hipError_t launch_book_commit(int32_t* book, uint32_t* err, int B, int parity, c
     return hipGetLastError();
 }
 
-hipError_t launch_book_reset(int32_t* book, uint32_t* err, int B, int parity, hipStream_t s)
+hipError_t launch_book_reset(int32_t* book, uint32_t* err, int B, int parity, int cap, bool stagger, hipStream_t s)
 {
-    hipLaunchKernelGGL(book_reset_kernel, dim3((3 * B + 255) / 256), dim3(256), 0, s, book, err, B, parity);
+    hipLaunchKernelGGL(book_reset_kernel, dim3((B + 255) / 256), dim3(256), 0, s, book, err, B, parity, cap,
+                       stagger ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -81,7 +81,7 @@ replay_status check_config(const replay_config* c)
         return fail(REPLAY_ERR_DTYPE, "read_copy must be NONE, FP8_E4M3 or MXFP4");
     if (c->read_copy == REPLAY_MXFP4 && R % 32 != 0)
         return fail(REPLAY_ERR_SHAPE, "MXFP4 read copy needs state_dim divisible by 32");
-    if (c->flags & ~(REPLAY_FLAG_VALU_FOLD | REPLAY_FLAG_QUANTIZED_CKPT))
+    if (c->flags & ~(REPLAY_FLAG_VALU_FOLD | REPLAY_FLAG_QUANTIZED_CKPT | REPLAY_FLAG_STAGGER_FLUSH))
         return fail(REPLAY_ERR_ARG, "unknown flags 0x%x", c->flags);
     if ((c->flags & REPLAY_FLAG_QUANTIZED_CKPT) && c->read_copy == REPLAY_NONE)
         return fail(REPLAY_ERR_ARG, "REPLAY_FLAG_QUANTIZED_CKPT needs a read_copy format");
@@ -119,7 +119,7 @@ void compute_layout(const replay_config* c, replay_layout* L)
         off = align256(off + L->buf_bytes[i]);
     }
     L->book_off = off;
-    L->book_bytes = 2 * 3 * B * 4;
+    L->book_bytes = 2 * 4 * B * 4;
     off = align256(off + L->book_bytes);
     L->err_off = off;
     off = align256(off + 4);
@@ -293,6 +293,11 @@ replay_status replay_state_alloc(const replay_config* cfg, void* dev_mem, size_t
     st->parity = 0;
     st->phase = 0;
     s = hip_check(rs::launch_fill_zero(dev_mem, L.total_bytes, (hipStream_t)stream), "state initialisation");
+    if (s == REPLAY_OK)
+        s = hip_check(rs::launch_book_reset(at<int32_t>(st, L.book_off), at<uint32_t>(st, L.err_off), cfg->batch, 0,
+                                            cfg->buf_cap, (cfg->flags & REPLAY_FLAG_STAGGER_FLUSH) != 0,
+                                            (hipStream_t)stream),
+                      "bookkeeping initialisation");
     if (s != REPLAY_OK) {
         delete st;
         return s;
@@ -339,7 +344,8 @@ replay_status replay_load_checkpoint(replay_state* st, const void* S, void* stre
         if (s != REPLAY_OK) return s;
     }
     return hip_check(rs::launch_book_reset(at<int32_t>(st, st->lay.book_off), at<uint32_t>(st, st->lay.err_off),
-                                           c->batch, st->parity, hs),
+                                           c->batch, st->parity, c->buf_cap,
+                                           (c->flags & REPLAY_FLAG_STAGGER_FLUSH) != 0, hs),
                      "bookkeeping reset");
 }
 
@@ -374,7 +380,7 @@ replay_status replay_read_book(const replay_state* st, int32_t* book_out, uint32
     if (!book_out) return fail(REPLAY_ERR_ARG, "book_out is NULL");
     const size_t n = (size_t)3 * st->cfg.batch * sizeof(int32_t);
     hipStream_t hs = (hipStream_t)stream;
-    replay_status s = hip_check(hipMemcpyAsync(book_out, at<int32_t>(st, st->lay.book_off) + (size_t)st->parity * 3 * st->cfg.batch,
+    replay_status s = hip_check(hipMemcpyAsync(book_out, at<int32_t>(st, st->lay.book_off) + (size_t)st->parity * 4 * st->cfg.batch,
                                                n, hipMemcpyDeviceToDevice, hs),
                                 "bookkeeping copy");
     if (s != REPLAY_OK || !err_out) return s;

@@ -38,7 +38,7 @@ struct StepArgs {
     float* bufs0;            // per-head scalar: Mamba-2 dt; GDN alpha   [2][B][H][cap]
     float* bufs1;            // per-head scalar: GDN beta (null for Mamba-2)
     size_t bank_c, bank_r, bank_s;
-    int32_t* book;           // [2][3][B]
+    int32_t* book;           // [2][4][B]: len, pend, fc, lim (length of the current window)
     uint32_t* err;
     // token inputs [T][B][...]
     const void* in_c;        // Mamba-2 x ; GDN v
@@ -60,7 +60,7 @@ hipError_t launch_gdn_step_f16(const StepArgs& a, int io, int rc, hipStream_t s)
 // Bookkeeping, layout conversion and helpers (aux.hip).
 hipError_t launch_book_commit(int32_t* book, uint32_t* err, int B, int parity,
                               const int32_t* accepted, hipStream_t s);
-hipError_t launch_book_reset(int32_t* book, uint32_t* err, int B, int parity, hipStream_t s);
+hipError_t launch_book_reset(int32_t* book, uint32_t* err, int B, int parity, int cap, bool stagger, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_tiles_to_logical(const void* ckpt, void* out, int tiles, int C, int R, int ck, hipStream_t s);
 hipError_t launch_logical_to_tiles(const void* in, void* ckpt, int tiles, int C, int R, int ck, hipStream_t s);

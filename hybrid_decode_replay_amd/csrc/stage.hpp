@@ -203,7 +203,14 @@ __device__ __forceinline__ void stage_append(const StageGeom& G, void* bufc, voi
 
 // Per-sequence decision shared by every workgroup of sequence b: how many
 // leading entries of the virtual list are folded, and the bookkeeping update
-// (written by one workgroup into the other copy).
+// (written by one workgroup into the other copy).  A window holds lim entries
+// (cap, or a shorter first window under staggered flushes):
+//   decode  len == cap: forced fold of the committed entries first; then the
+//           token is appended and a window that reaches lim folds.  With
+//           cap == 1 both happen on one step (two folds, fc += 2).
+//   flush   fold the len committed entries.
+//   spec    len + T > cap: fold the committed prefix before the drafts.
+// After a fold the window limit is cap.
 struct StepPlan {
     int len, fc, f, V, bank, bank_new;
 };
@@ -211,21 +218,36 @@ struct StepPlan {
 __device__ __forceinline__ StepPlan plan_step(const StepArgs& a, int b, bool writer)
 {
     const size_t sB = (size_t)a.B;
-    const int32_t* bk = a.book + (size_t)a.parity * 3 * sB;
+    const int32_t* bk = a.book + (size_t)a.parity * 4 * sB;
     StepPlan p;
     p.len = min(max(bk[b], 0), a.cap);   // invariant 0 <= len <= cap; clamped so that a
     p.fc = bk[2 * sB + b];               // corrupted word cannot index out of bounds
-    if (a.mode == MODE_DECODE) p.f = (p.len + 1 >= a.cap) ? min(p.len + 1, a.cap) : 0;
-    else if (a.mode == MODE_FLUSH) p.f = p.len;
-    else p.f = (p.len + a.T > a.cap) ? p.len : 0;
+    const int lim = min(max(bk[3 * sB + b], 1), a.cap);
+    int folds;
+    if (a.mode == MODE_DECODE) {
+        if (p.len + 1 > a.cap) {          // forced: the buffer is full
+            folds = a.cap == 1 ? 2 : 1;
+            p.f = a.cap == 1 ? p.len + 1 : p.len;
+        } else {
+            folds = p.len + 1 >= lim ? 1 : 0;
+            p.f = folds ? p.len + 1 : 0;
+        }
+    } else if (a.mode == MODE_FLUSH) {
+        folds = p.len > 0 ? 1 : 0;
+        p.f = p.len;
+    } else {
+        folds = p.len + a.T > a.cap ? 1 : 0;
+        p.f = folds ? p.len : 0;
+    }
     p.V = p.len + a.T;
     p.bank = p.fc & 1;
-    p.bank_new = (p.fc + (p.f > 0 ? 1 : 0)) & 1;
+    p.bank_new = (p.fc + folds) & 1;
     if (writer) {
-        int32_t* nbk = a.book + (size_t)(a.parity ^ 1) * 3 * sB;
-        nbk[b] = (a.mode == MODE_DECODE) ? p.len + 1 - p.f : (a.mode == MODE_FLUSH ? 0 : p.len - p.f);
+        int32_t* nbk = a.book + (size_t)(a.parity ^ 1) * 4 * sB;
+        nbk[b] = (a.mode == MODE_SPEC) ? p.len - p.f : p.len + (a.mode == MODE_DECODE ? 1 : 0) - p.f;
         nbk[sB + b] = (a.mode == MODE_SPEC) ? a.T : 0;
-        nbk[2 * sB + b] = p.fc + (p.f > 0 ? 1 : 0);
+        nbk[2 * sB + b] = p.fc + folds;
+        nbk[3 * sB + b] = folds ? a.cap : lim;
     }
     return p;
 }

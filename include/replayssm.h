@@ -107,6 +107,13 @@ typedef enum {
  * checkpoint is rounded to the copy's grid at load and right after every fold
  * (before that step's outputs); the fp32 region then mirrors the copy exactly. */
 #define REPLAY_FLAG_QUANTIZED_CKPT 0x2
+/* Staggered flush phases: after a load, sequence b's first window ends after
+ * 1 + (b mod buf_cap) decode tokens instead of buf_cap, so that in lockstep
+ * decoding only about batch/buf_cap sequences fold on any one step and every
+ * step costs about the same; later windows have buf_cap tokens.  An explicit
+ * replay_flush ends the stagger for the sequences it folds.  Values do not
+ * depend on when folds happen (up to rounding); only the flush schedule does. */
+#define REPLAY_FLAG_STAGGER_FLUSH 0x4
 
 typedef struct {
     int32_t abi_version;  /* REPLAY_ABI_VERSION                                  */
@@ -141,7 +148,7 @@ typedef struct {
     uint64_t rcopy_off, rcopy_bytes;   /* read copy element codes              */
     uint64_t rscale_off, rscale_bytes; /* MXFP4 E8M0 scales                    */
     uint64_t buf_off[4], buf_bytes[4]; /* buffer arrays, 2 banks each          */
-    uint64_t book_off, book_bytes;     /* int32 [2][3][B]: len, pend, fc       */
+    uint64_t book_off, book_bytes;     /* int32 [2][4][B]: len, pend, fc, window limit */
     uint64_t err_off;                  /* uint32 device error word             */
 } replay_layout;
 

@@ -39,6 +39,11 @@ Two parts:
   A flush sets fc += 1 and len = 0 and records the checkpoint image (the
   committed fp64 state at that moment).
 
+  Staggered flush phases (an option; the pages leave the flush schedule to the
+  implementation, and values do not depend on it): a window holds lim entries;
+  after a load lim = 1 + (b mod cap) for sequence b, after any flush lim = cap,
+  and the decode rule "if len == cap afterwards" reads "if len >= lim".
+
 The pages leave the following open; the readings taken here are listed with
 the design notes: when the flush happens (on the filling step), whether the
 output includes the current token (yes), the overflow rule for drafts (forced
@@ -261,7 +266,7 @@ class _Session:
 
     kind = None
 
-    def __init__(self, batch, cap, S0, read_copy=None, quantized_ckpt=False, ckpt_dtype="f32"):
+    def __init__(self, batch, cap, S0, read_copy=None, quantized_ckpt=False, ckpt_dtype="f32", stagger=False):
         if not 1 <= cap <= 16:
             raise ValueError("buffer capacity must be in [1, 16]")
         if quantized_ckpt and read_copy is None:
@@ -276,11 +281,13 @@ class _Session:
         self.quantized_ckpt = quantized_ckpt
         self.ckpt_dtype = ckpt_dtype
         self.rounds = quantized_ckpt or ckpt_dtype == "f16"    # folds land on a coarser grid
+        self.stagger = stagger
         self.S = self._round(np.array(S0, np.float64, copy=True))   # committed state
         self.ckpt = self.S.copy()                              # image at last flush
         self.len = np.zeros(batch, np.int32)
         self.pend = np.zeros(batch, np.int32)
         self.fc = np.zeros(batch, np.int32)
+        self.lim = self._first_limits()
         self.err = 0
         self.hist = [[] for _ in range(batch)]                 # committed tokens since flush
         self._drafts = None                                    # list of per-draft inputs
@@ -288,6 +295,11 @@ class _Session:
         self.nops = 0
 
     # -- helpers -----------------------------------------------------------
+    def _first_limits(self):
+        if self.stagger:
+            return (1 + np.arange(self.B) % self.cap).astype(np.int32)
+        return np.full(self.B, self.cap, np.int32)
+
     def trace(self):
         return self.len.copy(), self.pend.copy(), self.fc.copy()
 
@@ -307,6 +319,7 @@ class _Session:
             self.ckpt[b] = self.S[b]
             self.fc[b] += 1
             self.len[b] = 0
+            self.lim[b] = self.cap
             self.hist[b] = []
             self.flush_events.append((self.nops, int(b)))
 
@@ -329,6 +342,7 @@ class _Session:
         self.len[:] = 0
         self.pend[:] = 0
         self.fc[:] = 0
+        self.lim = self._first_limits()
         self.err = 0
         self.hist = [[] for _ in range(self.B)]
         self.nops += 1
@@ -340,7 +354,7 @@ class _Session:
         self._flush_rows(forced)
         y = self._token(self.S, inp)
         self.len += 1
-        full = self.len == self.cap
+        full = self.len >= self.lim
         if self.read_copy:
             no_flush = ~(forced | full)
             for b in np.flatnonzero(no_flush):
@@ -416,10 +430,10 @@ class Mamba2Session(_Session):
 
     kind = "mamba2"
 
-    def __init__(self, A, D, S0, cap=16, read_copy=None, quantized_ckpt=False, ckpt_dtype="f32"):
+    def __init__(self, A, D, S0, cap=16, read_copy=None, quantized_ckpt=False, ckpt_dtype="f32", stagger=False):
         self.A = np.asarray(A, np.float64)
         self.D = np.asarray(D, np.float64)
-        super().__init__(np.asarray(S0).shape[0], cap, S0, read_copy, quantized_ckpt, ckpt_dtype)
+        super().__init__(np.asarray(S0).shape[0], cap, S0, read_copy, quantized_ckpt, ckpt_dtype, stagger)
 
     def _token(self, S, inp, active=None):
         return mamba2_token(S, inp["x"], inp["Bm"], inp["Cm"], inp["dt"], self.A, self.D, active)
@@ -438,9 +452,9 @@ class GDNSession(_Session):
 
     kind = "gdn"
 
-    def __init__(self, S0, cap=16, scale=1.0, read_copy=None, quantized_ckpt=False, ckpt_dtype="f32"):
+    def __init__(self, S0, cap=16, scale=1.0, read_copy=None, quantized_ckpt=False, ckpt_dtype="f32", stagger=False):
         self.scale = float(scale)
-        super().__init__(np.asarray(S0).shape[0], cap, S0, read_copy, quantized_ckpt, ckpt_dtype)
+        super().__init__(np.asarray(S0).shape[0], cap, S0, read_copy, quantized_ckpt, ckpt_dtype, stagger)
 
     def _token(self, S, inp, active=None):
         return gdn_token(S, inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], self.scale, active)

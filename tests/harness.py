@@ -52,14 +52,15 @@ class Pair:
         self.st.load_checkpoint(torch.from_numpy(np.ascontiguousarray(S0)).cuda())
         rc = {rb.NONE: None, rb.FP8_E4M3: "fp8", rb.MXFP4: "mxfp4"}[read_copy]
         cd = "f16" if ckpt == rb.F16 else "f32"
+        stagger = bool(flags & rb.FLAG_STAGGER_FLUSH)
         if kind == rb.MAMBA2:
             from hybrid_decode_replay_amd import synth
             A, D = synth.mamba2_params(seed, H)
             self.params = {"A": dev(A, torch.float32), "D": dev(D, torch.float32)}
-            self.orc = ro.Mamba2Session(A, D, S0, cap=cap, read_copy=rc, ckpt_dtype=cd)
+            self.orc = ro.Mamba2Session(A, D, S0, cap=cap, read_copy=rc, ckpt_dtype=cd, stagger=stagger)
         else:
             self.params = {}
-            self.orc = ro.GDNSession(S0, cap=cap, scale=scale, read_copy=rc, ckpt_dtype=cd)
+            self.orc = ro.GDNSession(S0, cap=cap, scale=scale, read_copy=rc, ckpt_dtype=cd, stagger=stagger)
         self.max_err = {"y": 0.0, "ckpt": 0.0}
 
     # -- conversions

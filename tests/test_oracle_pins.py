@@ -408,16 +408,17 @@ def test_decode_flush_cadence_cap16():
 # --------------------------------------------------------------------------
 
 def _mk(kind, B=2, cap=4, seed=30, read_copy=None):
+    """A session factory (keyword `stagger` passed through) and the tokens of a tiny layer."""
     if kind == "mamba2":
         H, G, P, N = 2, 1, 3, 4
         A, D = synth.mamba2_params(seed, H)
         S0 = synth.checkpoint(seed, (B, H, P, N))
         toks = synth.mamba2_tokens(seed, 80, B, H, G, P, N)
-        return (lambda: ro.Mamba2Session(A, D, S0, cap=cap, read_copy=read_copy)), toks
+        return (lambda stagger=False: ro.Mamba2Session(A, D, S0, cap=cap, read_copy=read_copy, stagger=stagger)), toks
     H, DK, DV = 2, 4, 3
     S0 = synth.checkpoint(seed, (B, H, DV, DK))
     toks = synth.gdn_tokens(seed, 80, B, H, H, DK, DV)
-    return (lambda: ro.GDNSession(S0, cap=cap, read_copy=read_copy)), toks
+    return (lambda stagger=False: ro.GDNSession(S0, cap=cap, read_copy=read_copy, stagger=stagger)), toks
 
 
 @pytest.mark.parametrize("kind", ["mamba2", "gdn"])
@@ -596,3 +597,48 @@ def test_f16_checkpoint_exact_on_dyadic_inputs(kind):
         np.testing.assert_array_equal(a.decode(synth.token(toks, t)), b.decode(synth.token(toks, t)))
         np.testing.assert_array_equal(a.ckpt, b.ckpt)
     assert a.fc[0] == 3
+
+
+# --------------------------------------------------------------------------
+# Staggered flush phases and the full-buffer decode at capacity 1
+# --------------------------------------------------------------------------
+
+def test_stagger_schedule_closed_form():
+    """Sequence b folds after 1 + (b mod cap) tokens, then every cap tokens."""
+    B, H, G, P, N, cap, T = 5, 1, 1, 4, 8, 3, 11
+    A, D = synth.mamba2_params(63, H)
+    sess = ro.Mamba2Session(A, D, synth.checkpoint(63, (B, H, P, N)), cap=cap, stagger=True)
+    toks = synth.mamba2_tokens(63, T, B, H, G, P, N)
+    for t in range(T):
+        sess.decode(synth.token(toks, t))
+    got = sorted((op, b) for op, b in sess.flush_events)
+    want = sorted((s, b) for b in range(B) for s in range(T)
+                  if s + 1 >= 1 + b % cap and (s + 1 - (1 + b % cap)) % cap == 0)
+    assert got == want
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_stagger_leaves_values_unchanged(kind):
+    """The flush schedule changes only where the state is cut, not the values (fp64)."""
+    mk, toks = _mk(kind, B=4)
+    plain, stag = mk(), mk(stagger=True)
+    for t in range(30):
+        np.testing.assert_allclose(stag.decode(synth.token(toks, t)), plain.decode(synth.token(toks, t)),
+                                   rtol=1e-12, atol=1e-12)
+    assert stag.flush_events != plain.flush_events
+    np.testing.assert_array_equal(plain.lim, 4)
+
+
+def test_full_buffer_decode_at_capacity_one():
+    """cap = 1, len = 1 after a commit: the decode folds the committed entry, appends the
+    token, and the one-entry window is full again -- two flushes on one step."""
+    B, H, G, P, N = 2, 1, 1, 4, 8
+    A, D = synth.mamba2_params(64, H)
+    sess = ro.Mamba2Session(A, D, synth.checkpoint(64, (B, H, P, N)), cap=1)
+    toks = synth.mamba2_tokens(64, 3, B, H, G, P, N)
+    sess.spec_append([synth.token(toks, 0)])
+    sess.commit([1, 0])
+    fc0 = sess.fc.copy()
+    sess.decode(synth.token(toks, 1))
+    np.testing.assert_array_equal(sess.len, [0, 0])
+    np.testing.assert_array_equal(sess.fc - fc0, [2, 1])
