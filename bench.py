@@ -24,6 +24,10 @@ The JSON line also carries:
   fp16_checkpoint
                 both batch-256 layers with an fp16 recurrence checkpoint, and
                 the conventional kernel on an fp16 state
+  fp8_checkpoint
+                both batch-256 layers with an FP8 E4M3 recurrence checkpoint,
+                with no copy (the conventional kernel on an FP8 state beside
+                it) and with an MXFP4 read copy
   flush_schedule_mamba2_b256
                 per-step launch time (p50, p99, max) with lockstep folds and
                 with staggered flush phases
@@ -150,7 +154,7 @@ class Layer:
         self.ckpt = ckpt
         rc = {None: rb.NONE, "fp8": rb.FP8_E4M3, "mxfp4": rb.MXFP4}[read_copy]
         self.cfg = rb.make_config(rb.MAMBA2 if kind == "mamba2" else rb.GDN, B, self.H, self.G, self.C, self.R,
-                                  cap, rb.BF16, read_copy=rc, ckpt_dtype=rb.F16 if ckpt == "f16" else rb.F32,
+                                  cap, rb.BF16, read_copy=rc, ckpt_dtype={"f16": rb.F16, "fp8": rb.FP8_E4M3}.get(ckpt, rb.F32),
                                   flags=flags)
         self.S0 = synth.checkpoint_device(seed, (B, self.H, self.C, self.R), dev).to(rb.ckpt_torch_dtype(self.cfg))
         if kind == "mamba2":
@@ -284,7 +288,7 @@ def time_graph(L, conventional, n=64, reps=8):
 
 def decode_report(L, r, conv_ms):
     replay_b, conv_b = algorithmic_bytes(L.kind, L.H, L.G, L.C, L.R, L.cap, read_copy=L.read_copy,
-                                         ckpt_bytes=2 if L.ckpt == "f16" else 4)
+                                         ckpt_bytes={"f16": 2, "fp8": 1}.get(L.ckpt, 4))
     ms = r["total_ms"] / r["steps"]
     ach = replay_b * L.B / (r["avg_launch_ms"] / 1e3) / 1e9
     out = {"batch": L.B, "tokens_per_s": round(L.B / (ms / 1e3), 1), "ms_per_step": round(ms, 5),
@@ -461,6 +465,18 @@ def main():
             del Lh
             torch.cuda.empty_cache()
         out["fp16_checkpoint"] = f16
+        # FP8 recurrence checkpoint at batch 256: alone (beside the conventional kernel on an
+        # FP8 state) and with an MXFP4 read copy
+        f8 = {}
+        for kind, seed in (("mamba2", 9), ("gdn", 10)):
+            for rc in (None, "mxfp4"):
+                Lq = Layer(rb, synth, torch, dev, kind, B, 256 + 32 + 4, seed=seed, ckpt="fp8", read_copy=rc)
+                rq = time_replay_decode(Lq, 256, 32, stream)
+                f8[kind + ("_mxfp4_copy" if rc else "")] = decode_report(
+                    Lq, rq, None if rc else time_conv_decode(Lq, 64, stream))
+                del Lq
+                torch.cuda.empty_cache()
+        out["fp8_checkpoint"] = f8
         # flush schedule at batch 256: lockstep folds (every 16th step folds every sequence)
         # against staggered phases (about 1/16 of the sequences fold on each step)
         sched = {}

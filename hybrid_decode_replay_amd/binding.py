@@ -151,7 +151,7 @@ def _io_torch_dtype(io):
 def ckpt_torch_dtype(cfg: ReplayConfig):
     """torch dtype of logical checkpoints and conventional-baseline states for `cfg`."""
     torch = _torch()
-    return torch.float16 if cfg.ckpt_dtype == F16 else torch.float32
+    return {F16: torch.float16, FP8_E4M3: torch.float8_e4m3fn}.get(cfg.ckpt_dtype, torch.float32)
 
 
 def make_inputs(cfg: ReplayConfig, tensors: dict, params: dict | None = None) -> ReplayInputs:

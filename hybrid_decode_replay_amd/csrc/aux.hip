@@ -117,7 +117,10 @@ hipError_t launch_tiles_to_logical(const void* ckpt, void* out, int tiles, int C
 {
     const size_t n4 = (size_t)tiles * C * R / 4;
     const dim3 grid((unsigned)((n4 + 255) / 256)), block(256);
-    if (ck == CK_F16)
+    if (ck == CK_FP8)
+        hipLaunchKernelGGL((tiles_to_logical_kernel<CK_FP8, uint32_t>), grid, block, 0, s,
+                           static_cast<const uint32_t*>(ckpt), static_cast<uint32_t*>(out), n4, C, R);
+    else if (ck == CK_F16)
         hipLaunchKernelGGL((tiles_to_logical_kernel<CK_F16, u32x2>), grid, block, 0, s,
                            static_cast<const u32x2*>(ckpt), static_cast<u32x2*>(out), n4, C, R);
     else
@@ -130,7 +133,10 @@ hipError_t launch_logical_to_tiles(const void* in, void* ckpt, int tiles, int C,
 {
     const size_t n4 = (size_t)tiles * C * R / 4;
     const dim3 grid((unsigned)((n4 + 255) / 256)), block(256);
-    if (ck == CK_F16)
+    if (ck == CK_FP8)
+        hipLaunchKernelGGL((logical_to_tiles_kernel<CK_FP8, uint32_t>), grid, block, 0, s,
+                           static_cast<const uint32_t*>(in), static_cast<uint32_t*>(ckpt), n4, C, R);
+    else if (ck == CK_F16)
         hipLaunchKernelGGL((logical_to_tiles_kernel<CK_F16, u32x2>), grid, block, 0, s,
                            static_cast<const u32x2*>(in), static_cast<u32x2*>(ckpt), n4, C, R);
     else
@@ -234,6 +240,10 @@ static hipError_t rc_dispatch(bool quantize, void* ckpt, const uint8_t* codes_in
 hipError_t launch_quantize_read_copy(void* ckpt, uint8_t* codes, uint8_t* scales, int tiles, int C, int R, int rc,
                                      int ck, bool round_ckpt, hipStream_t s)
 {
+    if (ck == CK_FP8) {
+        if (round_ckpt || rc != RC_MXFP4) return hipErrorInvalidValue;   // only an MXFP4 copy of an FP8 checkpoint
+        return rc_dispatch<RC_MXFP4, CK_FP8>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, 0, s);
+    }
     if (ck == CK_F16) {
         if (round_ckpt) return hipErrorInvalidValue;     // the quantized-checkpoint variant keeps fp32 storage
         if (rc == RC_FP8) return rc_dispatch<RC_FP8, CK_F16>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, 0, s);

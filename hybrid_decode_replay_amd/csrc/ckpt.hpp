@@ -15,6 +15,7 @@
 #pragma once
 #include "common.hpp"
 #include "internal.hpp"
+#include "rc.hpp"
 
 namespace rs {
 
@@ -37,7 +38,12 @@ __device__ __forceinline__ u32x2 f32_to_h4(f32x4 v) {
 template <int NB, int CK>
 __device__ __forceinline__ void ckpt_issue(const void* ck, size_t strip, int lane, f32x4 (&s)[NB])
 {
-    if constexpr (CK == CK_F32) {
+    if constexpr (CK == CK_FP8) {
+        uint32_t w[NB];
+        rc_fp8_issue<NB>(static_cast<const uint8_t*>(ck), strip, lane, w);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) s[nb].x = __builtin_bit_cast(float, w[nb]);
+    } else if constexpr (CK == CK_F32) {
         const float* p = static_cast<const float*>(ck) + (strip * NB * 64 + lane) * 4;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) s[nb] = ld4_stream(p + (size_t)nb * 256);
@@ -54,7 +60,15 @@ __device__ __forceinline__ void ckpt_issue(const void* ck, size_t strip, int lan
 template <int NB, int CK>
 __device__ __forceinline__ void ckpt_decode(f32x4 (&s)[NB])
 {
-    if constexpr (CK == CK_F16) {
+    if constexpr (CK == CK_FP8) {
+        uint32_t w[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const float x = s[nb].x;                 // a vector component is bit-cast through a scalar
+            w[nb] = __builtin_bit_cast(uint32_t, x);
+        }
+        rc_fp8_decode<NB>(w, s);
+    } else if constexpr (CK == CK_F16) {
         if constexpr (NB == 1) {
             const u32x4 w = __builtin_bit_cast(u32x4, s[0]);
             s[0] = h4_to_f32(u32x2{w.x, w.y});
@@ -72,7 +86,10 @@ __device__ __forceinline__ void ckpt_decode(f32x4 (&s)[NB])
 template <int NB, int CK>
 __device__ __forceinline__ void ckpt_load(const void* ck, size_t strip, int lane, f32x4 (&s)[NB])
 {
-    if constexpr (CK == CK_F32) {
+    if constexpr (CK == CK_FP8) {
+        ckpt_issue<NB, CK>(ck, strip, lane, s);
+        ckpt_decode<NB, CK>(s);
+    } else if constexpr (CK == CK_F32) {
         const float* p = static_cast<const float*>(ck) + (strip * NB * 64 + lane) * 4;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) s[nb] = ld4_stream(p + (size_t)nb * 256);
@@ -93,7 +110,9 @@ __device__ __forceinline__ void ckpt_load(const void* ck, size_t strip, int lane
 template <int NB, int CK>
 __device__ __forceinline__ void ckpt_store(void* ck, size_t strip, int lane, const f32x4 (&s)[NB])
 {
-    if constexpr (CK == CK_F32) {
+    if constexpr (CK == CK_FP8) {
+        rc_fp8_store<NB>(static_cast<uint8_t*>(ck), strip, lane, s);
+    } else if constexpr (CK == CK_F32) {
         float* p = static_cast<float*>(ck) + (strip * NB * 64 + lane) * 4;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) st4_stream(p + (size_t)nb * 256, s[nb]);
@@ -114,7 +133,9 @@ __device__ __forceinline__ void ckpt_store(void* ck, size_t strip, int lane, con
 template <int NB, int CK>
 __device__ __forceinline__ void ckpt_round(f32x4 (&s)[NB])
 {
-    if constexpr (CK == CK_F16) {
+    if constexpr (CK == CK_FP8) {
+        rc_fp8_roundtrip<NB>(s);
+    } else if constexpr (CK == CK_F16) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) s[nb] = h4_to_f32(f32_to_h4(s[nb]));
     }
@@ -125,6 +146,14 @@ __device__ __forceinline__ void ckpt_round(f32x4 (&s)[NB])
 template <int CK>
 __device__ __forceinline__ size_t ckpt_elem_offset(size_t q, int NB)
 {
+    if (CK == CK_FP8) {                             // bytes, in the FP8 read-copy layout
+        const size_t lane = q & 63, sb = q >> 6;
+        const size_t strip = sb / NB;
+        const int nb = (int)(sb - strip * NB);
+        const size_t bpl = 4 * (size_t)NB;
+        if (bpl >= 16) return strip * 64 * bpl + (size_t)(nb / 4) * 1024 + lane * 16 + (nb % 4) * 4;
+        return strip * 64 * bpl + lane * bpl + (size_t)nb * 4;
+    }
     if (CK == CK_F32 || NB == 1) return q * 4;
     const size_t lane = q & 63, sb = q >> 6;       // sb = strip*NB + nb
     const size_t strip = sb / NB;

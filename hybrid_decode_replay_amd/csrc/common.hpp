@@ -104,11 +104,12 @@ __device__ __forceinline__ float wave_sum_uniform(float v) {
     return readlane(v, 63);
 }
 
-// Sum over aligned groups of N consecutive lanes (N = 2, 4, 8, 16, 32 or 64),
+// Sum over aligned groups of N consecutive lanes (N = 1, 2, 4, 8, 16, 32 or 64),
 // returned to every lane of the group.
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
-    static_assert(N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group size");
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group size");
+    if constexpr (N == 1) return v;
     if constexpr (N == 2) return v + dpp_mov<DPP_QUAD_XOR1>(v);
     v = quad_sum(v);
     if constexpr (N >= 8) v += dpp_mov<DPP_ROW_HALF_MIRROR>(v);

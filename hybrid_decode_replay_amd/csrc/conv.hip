@@ -4,11 +4,11 @@
 // it, read out the output, store the state ([DE] "ReplaySSM beschleunigt das
 // Decoding ...", section "Wie es funktioniert" describes this step and why
 // it is memory-bound).  The state is the plain logical tile [C][R] (Mamba-2
-// [P][N], GDN [DV][DK]) in fp32 or fp16; an fp16 state is updated in fp32, the
+// [P][N], GDN [DV][DK]) in fp32, fp16 or FP8 E4M3; a low-precision state is updated in fp32, the
 // output is read from the fp32 update, and the state is rounded (RNE) after
 // every token, as storing and reloading it would.  Every row evolves
 // independently given the token, so a thread owns one 16-byte word of a row
-// (4 fp32 or 8 fp16 values): the lanes of a row are adjacent, loads and stores
+// (4 fp32, 8 fp16 or 16 FP8 values): the lanes of a row are adjacent, loads and stores
 // are 128-bit and contiguous across the row, and row dot products reduce with
 // DPP.  UNR = 8 words per thread are loaded before any arithmetic.
 //
@@ -36,29 +36,49 @@ __device__ __forceinline__ f32x4 ld4_io(const void* p, size_t i) {
 // 16-byte word of storage (fp32: VW = 1; fp16: VW = 2).
 template <int CK>
 struct StateWord {
-    static constexpr int VW = CK == CK_F16 ? 2 : 1;
+    static constexpr int VW = CK == CK_FP8 ? 4 : (CK == CK_F16 ? 2 : 1);
     static __device__ __forceinline__ void load(const void* base, size_t e, f32x4 (&v)[VW]) {
         if constexpr (CK == CK_F32) {
             v[0] = ld4_stream(static_cast<const float*>(base) + e);
-        } else {
+        } else if constexpr (CK == CK_F16) {
             const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + e));
             v[0] = h4_to_f32(u32x2{w.x, w.y});
             v[1] = h4_to_f32(u32x2{w.z, w.w});
+        } else {
+            const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(base) + e));
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(ww[i], false);
+                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(ww[i], true);
+                v[i] = f32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
         }
     }
     static __device__ __forceinline__ void store(void* base, size_t e, const f32x4 (&v)[VW]) {
         if constexpr (CK == CK_F32) {
             st4_stream(static_cast<float*>(base) + e, v[0]);
-        } else {
+        } else if constexpr (CK == CK_F16) {
             const u32x2 lo = f32_to_h4(v[0]), hi = f32_to_h4(v[1]);
             __builtin_nontemporal_store(u32x4{lo.x, lo.y, hi.x, hi.y},
                                         reinterpret_cast<u32x4*>(static_cast<uint16_t*>(base) + e));
+        } else {
+            __builtin_nontemporal_store(u32x4{pack_e4m3(v[0]), pack_e4m3(v[1]), pack_e4m3(v[2]), pack_e4m3(v[3])},
+                                        reinterpret_cast<u32x4*>(static_cast<uint8_t*>(base) + e));
         }
     }
     static __device__ __forceinline__ void round(f32x4 (&v)[VW]) {
         if constexpr (CK == CK_F16) {
 #pragma unroll
             for (int i = 0; i < VW; ++i) v[i] = h4_to_f32(f32_to_h4(v[i]));
+        } else if constexpr (CK == CK_FP8) {
+#pragma unroll
+            for (int i = 0; i < VW; ++i) {
+                const uint32_t w = pack_e4m3(v[i]);
+                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+                v[i] = f32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
         }
     }
 };
@@ -196,6 +216,7 @@ static hipError_t conv_launch_io(const ConvArgs& a, hipStream_t s)
 
 hipError_t launch_conv_step(const ConvArgs& a, int io, int ck, hipStream_t s)
 {
+    if (ck == CK_FP8) return io == IO_BF16 ? conv_launch_io<IO_BF16, CK_FP8>(a, s) : conv_launch_io<IO_F32, CK_FP8>(a, s);
     if (ck == CK_F16) return io == IO_BF16 ? conv_launch_io<IO_BF16, CK_F16>(a, s) : conv_launch_io<IO_F32, CK_F16>(a, s);
     return io == IO_BF16 ? conv_launch_io<IO_BF16, CK_F32>(a, s) : conv_launch_io<IO_F32, CK_F32>(a, s);
 }

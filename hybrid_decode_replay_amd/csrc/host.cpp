@@ -53,8 +53,14 @@ uint64_t align256(uint64_t x) { return (x + 255) & ~(uint64_t)255; }
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 int io_bytes(const replay_config* c) { return c->io_dtype == REPLAY_BF16 ? 2 : 4; }
-int ckpt_bytes(const replay_config* c) { return c->ckpt_dtype == REPLAY_F16 ? 2 : 4; }
-int ck_kind(const replay_config* c) { return c->ckpt_dtype == REPLAY_F16 ? rs::CK_F16 : rs::CK_F32; }
+int ckpt_bytes(const replay_config* c)
+{
+    return c->ckpt_dtype == REPLAY_F16 ? 2 : (c->ckpt_dtype == REPLAY_FP8_E4M3 ? 1 : 4);
+}
+int ck_kind(const replay_config* c)
+{
+    return c->ckpt_dtype == REPLAY_F16 ? rs::CK_F16 : (c->ckpt_dtype == REPLAY_FP8_E4M3 ? rs::CK_FP8 : rs::CK_F32);
+}
 
 replay_status check_config(const replay_config* c)
 {
@@ -75,8 +81,10 @@ replay_status check_config(const replay_config* c)
     if ((long long)c->batch * c->nheads > (1LL << 30)) return fail(REPLAY_ERR_SHAPE, "batch * nheads too large");
     if (c->io_dtype != REPLAY_F32 && c->io_dtype != REPLAY_BF16)
         return fail(REPLAY_ERR_DTYPE, "io_dtype must be REPLAY_F32 or REPLAY_BF16");
-    if (c->ckpt_dtype != REPLAY_F32 && c->ckpt_dtype != REPLAY_F16)
-        return fail(REPLAY_ERR_DTYPE, "ckpt_dtype must be REPLAY_F32 or REPLAY_F16");
+    if (c->ckpt_dtype != REPLAY_F32 && c->ckpt_dtype != REPLAY_F16 && c->ckpt_dtype != REPLAY_FP8_E4M3)
+        return fail(REPLAY_ERR_DTYPE, "ckpt_dtype must be REPLAY_F32, REPLAY_F16 or REPLAY_FP8_E4M3");
+    if (c->ckpt_dtype == REPLAY_FP8_E4M3 && c->read_copy == REPLAY_FP8_E4M3)
+        return fail(REPLAY_ERR_UNSUPPORTED, "an FP8 checkpoint takes no FP8 read copy (it is one)");
     if (c->read_copy != REPLAY_NONE && c->read_copy != REPLAY_FP8_E4M3 && c->read_copy != REPLAY_MXFP4)
         return fail(REPLAY_ERR_DTYPE, "read_copy must be NONE, FP8_E4M3 or MXFP4");
     if (c->read_copy == REPLAY_MXFP4 && R % 32 != 0)
@@ -228,12 +236,16 @@ replay_status launch_step(replay_state* st, const replay_inputs* in, void* y, in
     const int io = c->io_dtype == REPLAY_BF16 ? rs::IO_BF16 : rs::IO_F32;
     const int rc = rc_kind(c);
     hipError_t e;
-    const bool f16 = c->ckpt_dtype == REPLAY_F16;
+    const hipStream_t hs = (hipStream_t)stream;
+    const int ck = ck_kind(c);
     if (c->kind == REPLAY_MAMBA2)
-        e = f16 ? rs::launch_mamba2_step_f16(a, io, rc, (hipStream_t)stream)
-                : rs::launch_mamba2_step_f32(a, io, rc, (c->flags & REPLAY_FLAG_VALU_FOLD) != 0, (hipStream_t)stream);
+        e = ck == rs::CK_F16   ? rs::launch_mamba2_step_f16(a, io, rc, hs)
+            : ck == rs::CK_FP8 ? rs::launch_mamba2_step_fp8(a, io, rc, hs)
+                               : rs::launch_mamba2_step_f32(a, io, rc, (c->flags & REPLAY_FLAG_VALU_FOLD) != 0, hs);
     else
-        e = f16 ? rs::launch_gdn_step_f16(a, io, rc, (hipStream_t)stream) : rs::launch_gdn_step_f32(a, io, rc, (hipStream_t)stream);
+        e = ck == rs::CK_F16   ? rs::launch_gdn_step_f16(a, io, rc, hs)
+            : ck == rs::CK_FP8 ? rs::launch_gdn_step_fp8(a, io, rc, hs)
+                               : rs::launch_gdn_step_f32(a, io, rc, hs);
     replay_status s = hip_check(e, "replay step launch");
     if (s == REPLAY_OK) st->parity ^= 1;
     return s;

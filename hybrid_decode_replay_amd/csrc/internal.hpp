@@ -9,7 +9,7 @@ namespace rs {
 enum : int { IO_F32 = 0, IO_BF16 = 1 };
 enum : int { RC_NONE = 0, RC_FP8 = 1, RC_MXFP4 = 2 };
 enum : int { MODE_DECODE = 0, MODE_FLUSH = 1, MODE_SPEC = 2 };
-enum : int { CK_F32 = 0, CK_F16 = 1 };     // recurrence checkpoint storage
+enum : int { CK_F32 = 0, CK_F16 = 1, CK_FP8 = 2 };   // recurrence checkpoint storage
 
 // Device error word bits (mirror REPLAY_DEVERR_* of the public header).
 constexpr uint32_t REPLAY_COMMIT_CLAMPED_BIT = 0x1u;
@@ -56,6 +56,8 @@ hipError_t launch_mamba2_step_f32(const StepArgs& a, int io, int rc, bool valu_f
 hipError_t launch_mamba2_step_f16(const StepArgs& a, int io, int rc, hipStream_t s);
 hipError_t launch_gdn_step_f32(const StepArgs& a, int io, int rc, hipStream_t s);
 hipError_t launch_gdn_step_f16(const StepArgs& a, int io, int rc, hipStream_t s);
+hipError_t launch_mamba2_step_fp8(const StepArgs& a, int io, int rc, hipStream_t s);
+hipError_t launch_gdn_step_fp8(const StepArgs& a, int io, int rc, hipStream_t s);
 
 // Bookkeeping, layout conversion and helpers (aux.hip).
 hipError_t launch_book_commit(int32_t* book, uint32_t* err, int B, int parity,

@@ -88,12 +88,16 @@ typedef enum {
     REPLAY_MXFP4 = 5        /* OCP MX FP4 E2M1, one E8M0 scale per 32 elements          */
 } replay_dtype;
 
-/* Recurrence checkpoint dtype.  REPLAY_F32, or REPLAY_F16 (IEEE binary16; the
- * [TR] page, section "Kuantizasyon hatasinin sinirlandirilmasi", pairs
- * low-precision reads with an FP16 or FP8 recurrence): a fold decodes the
- * fp16 checkpoint to fp32, folds in fp32, rounds the result to fp16 (RNE)
- * right away -- that step's outputs and the read copy see the rounded values --
- * and writes it once.  Non-flush steps read half the bytes of fp32. */
+/* Recurrence checkpoint dtype.  REPLAY_F32, REPLAY_F16 (IEEE binary16) or
+ * REPLAY_FP8_E4M3 (OCP E4M3, unscaled, RNE, saturating at +-448; the [TR]
+ * page, section "Kuantizasyon hatasinin sinirlandirilmasi", pairs
+ * low-precision reads with an FP16 or FP8 recurrence).  A fold decodes the
+ * low-precision checkpoint to fp32, folds in fp32, rounds the result to the
+ * checkpoint dtype (RNE) right away -- that step's outputs and the read copy
+ * see the rounded values -- and writes it once.  Non-flush steps read half
+ * (fp16) or a quarter (FP8) of the bytes of fp32.  An FP8 checkpoint takes no
+ * read copy or an MXFP4 one (an FP8 copy would repeat the checkpoint:
+ * REPLAY_ERR_UNSUPPORTED).  FP8 tiles use the read copy's strip layout. */
 
 /* Device error word bits (sticky; cleared by replay_load_checkpoint). */
 #define REPLAY_DEVERR_COMMIT_CLAMPED 0x1u  /* an accepted count was outside [0, pend] */
@@ -124,7 +128,7 @@ typedef struct {
     int32_t head_dim;     /* Mamba-2 P; GDN DV.  Multiple of 16, <= 256          */
     int32_t state_dim;    /* Mamba-2 N; GDN DK.  16, 32, 64, 128 or 256          */
     int32_t buf_cap;      /* buffer capacity, 1..16                              */
-    int32_t ckpt_dtype;   /* REPLAY_F32 | REPLAY_F16 (recurrence checkpoint)     */
+    int32_t ckpt_dtype;   /* REPLAY_F32 | REPLAY_F16 | REPLAY_FP8_E4M3 (recurrence checkpoint) */
     int32_t read_copy;    /* REPLAY_NONE | REPLAY_FP8_E4M3 | REPLAY_MXFP4        */
     int32_t io_dtype;     /* REPLAY_F32 | REPLAY_BF16 (token inputs and outputs) */
     int32_t flags;        /* REPLAY_FLAG_*                                       */
@@ -179,7 +183,8 @@ int32_t replay_state_phase(const replay_state *st);
 
 /* ---- checkpoint I/O ----------------------------------------------------- */
 /* Logical checkpoints at the boundary are [B][H][rows][cols] arrays in the
- * state's ckpt_dtype (float or IEEE binary16), rows = P or DV, cols = N or DK.
+ * state's ckpt_dtype (float, IEEE binary16 or E4M3 bytes), rows = P or DV,
+ * cols = N or DK.
  * Loads a logical checkpoint (device), refreshes the read copy, empties the
  * buffer and resets len = pend = fc = 0 and the error word.  Not allowed
  * while drafts are pending. */
@@ -226,9 +231,9 @@ replay_status replay_spec_rollback(replay_state *st, void *stream);
 
 /* ---- in-run conventional baselines --------------------------------------
  * Ordinary decoding on a plain logical state [B][H][rows][cols] in the
- * config's ckpt_dtype (load, decay and update, output, store per token; an
- * fp16 state is updated in fp32, the output is read from that update and the
- * state is stored RNE), tuned like the replay kernels.  read_copy and flags
+ * config's ckpt_dtype (load, decay and update, output, store per token; a
+ * low-precision state is updated in fp32, the output is read from that update
+ * and the state is stored RNE), tuned like the replay kernels.  read_copy and flags
  * are ignored. */
 replay_status replay_conv_decode_step(const replay_config *cfg, void *S, const replay_inputs *in,
                                       void *y, void *stream);

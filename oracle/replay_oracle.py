@@ -67,6 +67,10 @@ FP16 or FP8 recurrence).  The checkpoint is stored as IEEE binary16: rounded to
 nearest even at load and at every flush (numpy's float64 -> float16 cast), and
 the recurrence and outputs continue from the stored values exactly as in the
 quantized-checkpoint case.  The pages give no tolerance for it.
+
+FP8 recurrence checkpoint (same section).  As the FP16 case, with the state
+rounded at load and at every flush to the nearest OCP E4M3 value (ties to even,
+saturating at +-448, e4m3_encode below) straight from the fp64 fold.
 """
 from __future__ import annotations
 
@@ -271,8 +275,10 @@ class _Session:
             raise ValueError("buffer capacity must be in [1, 16]")
         if quantized_ckpt and read_copy is None:
             raise ValueError("a quantized checkpoint needs a format")
-        if ckpt_dtype not in ("f32", "f16"):
-            raise ValueError("checkpoint dtype must be 'f32' or 'f16'")
+        if ckpt_dtype not in ("f32", "f16", "fp8"):
+            raise ValueError("checkpoint dtype must be 'f32', 'f16' or 'fp8'")
+        if ckpt_dtype == "fp8" and read_copy == "fp8":
+            raise ValueError("an FP8 copy of an FP8 checkpoint repeats it")
         if quantized_ckpt and ckpt_dtype != "f32":
             raise ValueError("the quantized-checkpoint variant keeps an fp32 checkpoint")
         self.B = batch
@@ -280,7 +286,7 @@ class _Session:
         self.read_copy = read_copy
         self.quantized_ckpt = quantized_ckpt
         self.ckpt_dtype = ckpt_dtype
-        self.rounds = quantized_ckpt or ckpt_dtype == "f16"    # folds land on a coarser grid
+        self.rounds = quantized_ckpt or ckpt_dtype != "f32"    # folds land on a coarser grid
         self.stagger = stagger
         self.S = self._round(np.array(S0, np.float64, copy=True))   # committed state
         self.ckpt = self.S.copy()                              # image at last flush
@@ -304,11 +310,13 @@ class _Session:
         return self.len.copy(), self.pend.copy(), self.fc.copy()
 
     def _round(self, S):
-        """The state as the checkpoint keeps it: rounded to binary16 for an fp16
-        checkpoint, to the copy's grid in the quantized-checkpoint variant, unchanged
-        otherwise."""
+        """The state as the checkpoint keeps it: rounded to binary16 or E4M3 for an
+        fp16 or FP8 checkpoint, to the copy's grid in the quantized-checkpoint variant,
+        unchanged otherwise."""
         if self.ckpt_dtype == "f16":
             return np.asarray(S, np.float64).astype(np.float16).astype(np.float64)
+        if self.ckpt_dtype == "fp8":
+            return e4m3_decode(e4m3_encode(S)).reshape(np.shape(S))
         if not self.quantized_ckpt:
             return S
         return read_copy_values(S, self.read_copy).reshape(S.shape)

@@ -642,3 +642,94 @@ def test_full_buffer_decode_at_capacity_one():
     sess.decode(synth.token(toks, 1))
     np.testing.assert_array_equal(sess.len, [0, 0])
     np.testing.assert_array_equal(sess.fc - fc0, [2, 1])
+
+
+# --------------------------------------------------------------------------
+# FP8 (E4M3) recurrence checkpoint
+# --------------------------------------------------------------------------
+
+def test_fp8_checkpoint_fold_rounds_by_hand():
+    """One Mamba-2 token folded at cap = 1 (A = 0, dt = x = 1, so the fold adds B to the
+    state).  Each element's E4M3 rounding worked by hand from the format (1.m x 2^(e-7),
+    3 mantissa bits, subnormal step 2^-9, largest finite 448):
+      1 + 1/16     -> 1        tie between 1 and 1.125, even mantissa wins
+      1 + 3/32     -> 1.125    nearest
+      1.125 + 1/16 -> 1.25     tie between 1.125 and 1.25, even mantissa wins
+      416 + 64     -> 448      saturates (step 32 in [256, 448])
+      0 + 0.001    -> 2^-9     nearest subnormal (half step is 2^-10 < 0.001)
+      0 - 0.3      -> -0.3125  step 2^-5 in [0.25, 0.5)
+    The step's output is read from the rounded state: y = S' . C (D = 0)."""
+    S0 = np.array([1.0, 1.0, 1.125, 416.0, 0.0, 0.0]).reshape(1, 1, 1, 6)
+    Bv = np.array([1 / 16, 3 / 32, 1 / 16, 64.0, 0.001, -0.3])
+    C = np.array([1.0, 1.0, 1.0, 2.0 ** -7, 512.0, 1.0])
+    sess = ro.Mamba2Session(np.zeros(1), np.zeros(1), S0, cap=1, ckpt_dtype="fp8")
+    np.testing.assert_array_equal(sess.S, S0)         # already on the grid: load keeps it
+    tok = {"x": np.ones((1, 1, 1)), "Bm": Bv.reshape(1, 1, 6), "Cm": C.reshape(1, 1, 6), "dt": np.ones((1, 1))}
+    y = sess.decode(tok)
+    want = np.array([1.0, 1.125, 1.25, 448.0, 2.0 ** -9, -0.3125])
+    np.testing.assert_array_equal(sess.ckpt.ravel(), want)
+    assert y.ravel()[0] == 1.0 + 1.125 + 1.25 + 3.5 + 1.0 - 0.3125
+    assert sess.fc[0] == 1
+
+
+def test_fp8_checkpoint_gdn_column_replaced_by_hand():
+    """GDN with alpha = beta = 1 and k = e_0 replaces column 0 of the state with v; the FP8
+    checkpoint then holds v rounded to E4M3 and leaves the other columns as loaded."""
+    S0 = np.full((1, 1, 3, 4), 0.5)
+    tok = {"q": np.array([[[1.0, 0, 0, 0]]]), "k": np.array([[[1.0, 0, 0, 0]]]),
+           "v": np.array([[[1.0625, 0.3, -17.0]]]), "alpha": np.ones((1, 1)), "beta": np.ones((1, 1))}
+    sess = ro.GDNSession(S0, cap=1, ckpt_dtype="fp8")
+    o = sess.decode(tok)
+    want = S0.copy()
+    want[0, 0, :, 0] = [1.0, 0.3125, -16.0]           # tie to even; nearest; step 2 in [16, 32)
+    np.testing.assert_array_equal(sess.ckpt, want)
+    np.testing.assert_array_equal(o.ravel(), [1.0, 0.3125, -16.0])    # o = S' q, q = e_0
+
+
+def test_fp8_checkpoint_rounds_at_load_and_every_flush():
+    """The FP8 session equals the fp32 session until a flush; at a flush its checkpoint is
+    the E4M3 rounding of the state the fp32 recurrence reaches from the same start."""
+    B, H, G, P, N, cap = 2, 2, 1, 4, 32, 3
+    A, D = synth.mamba2_params(65, H)
+    S0 = synth.checkpoint(65, (B, H, P, N), std=1.0)
+    fp8 = ro.Mamba2Session(A, D, S0, cap=cap, ckpt_dtype="fp8")
+    grid = ro.e4m3_decode(ro.e4m3_encode(S0)).reshape(S0.shape)
+    np.testing.assert_array_equal(fp8.S, grid)
+    assert np.max(np.abs(grid - S0)) > 0
+    f32 = ro.Mamba2Session(A, D, grid, cap=cap)
+    toks = synth.mamba2_tokens(65, 7, B, H, G, P, N)
+    for t in range(cap - 1):
+        np.testing.assert_array_equal(fp8.decode(synth.token(toks, t)), f32.decode(synth.token(toks, t)))
+    fp8.decode(synth.token(toks, cap - 1))
+    f32.decode(synth.token(toks, cap - 1))
+    np.testing.assert_array_equal(fp8.ckpt, ro.e4m3_decode(ro.e4m3_encode(f32.ckpt)).reshape(S0.shape))
+    # E4M3 keeps 3 mantissa bits: the rounding moves the state by at most 2^-4 relative
+    # per normal element, and by at most half the subnormal step 2^-10 below 2^-6
+    bound = np.maximum(np.abs(f32.ckpt) * 2.0 ** -4, 2.0 ** -10)
+    assert np.all(np.abs(fp8.ckpt - f32.ckpt) <= bound * (1 + 1e-12))
+    with pytest.raises(ValueError):
+        ro.Mamba2Session(A, D, S0, read_copy="fp8", ckpt_dtype="fp8")
+    with pytest.raises(ValueError):
+        ro.Mamba2Session(A, D, S0, read_copy="mxfp4", quantized_ckpt=True, ckpt_dtype="fp8")
+    ro.Mamba2Session(A, D, S0, read_copy="mxfp4", ckpt_dtype="fp8")     # allowed
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_fp8_checkpoint_exact_on_grid_inputs(kind):
+    """Inputs whose folds land on the E4M3 grid (increments of 1/4 on states below 4 in
+    magnitude): the FP8 and fp32 sessions agree bit for bit through flushes."""
+    B, H, G, P, N, cap = 1, 2, 1, 4, 16, 2
+    S0 = (np.arange(B * H * P * N).reshape(B, H, P, N) % 7 - 3) * 0.25
+    if kind == "mamba2":
+        A, D = np.zeros(H), np.ones(H)
+        toks = {"x": np.full((6, B, H, P), 0.5), "Bm": np.full((6, B, G, N), 0.25),
+                "Cm": np.full((6, B, G, N), 1.0), "dt": np.full((6, B, H), 1.0)}
+        a, b = (ro.Mamba2Session(A, D, S0, cap=cap, ckpt_dtype=c) for c in ("fp8", "f32"))
+    else:
+        toks = {"q": np.full((6, B, G, N), 0.5), "k": np.full((6, B, G, N), 0.25),
+                "v": np.full((6, B, H, P), 1.0), "alpha": np.ones((6, B, H)), "beta": np.zeros((6, B, H))}
+        a, b = (ro.GDNSession(S0, cap=cap, ckpt_dtype=c) for c in ("fp8", "f32"))
+    for t in range(6):
+        np.testing.assert_array_equal(a.decode(synth.token(toks, t)), b.decode(synth.token(toks, t)))
+        np.testing.assert_array_equal(a.ckpt, b.ckpt)
+    assert a.fc[0] == 3
