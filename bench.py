@@ -31,6 +31,11 @@ The JSON line also carries:
   flush_schedule_mamba2_b256
                 per-step launch time (p50, p99, max) with lockstep folds and
                 with staggered flush phases
+  hybrid_stack_b256
+                a model step over four SSM layers (Mamba-2, GDN, Mamba-2, GDN
+                at the shapes above, batch 256) through one layer stack, with
+                lockstep and staggered flush phases, against the conventional
+                kernel per layer
   cpu_baseline  the fp64 oracle on the host cores over a bounded sample
 With --sweep FILE, both layers are also timed at batch 1..512 (replay and
 conventional, eagerly and as HIP-graph replays), one JSON line per point in FILE.
@@ -234,6 +239,71 @@ def time_conv_decode(L, K, stream, t0=0):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / K
+
+
+def time_stack(layers, K, W, stream):
+    """One model step = every layer's decode step in layer order through one ReplayStack
+    (one bookkeeping set).  W warm-up model steps, then K timed back to back, then K more
+    with an event pair around every model step (p50 / p99).  The conventional baseline
+    runs one conventional decode step per layer on plain states, K model steps."""
+    rb, torch = layers[0].rb, layers[0].torch
+    lib, sp = rb.lib(), rb.ctypes.c_void_p(stream.cuda_stream)
+    states = [rb.ReplayState(L.cfg, device=L.dev) for L in layers]
+    stk = rb.ReplayStack(states)
+    stk.load([L.S0 for L in layers])
+    ys = [torch.empty((1, L.B, L.H, L.C), dtype=torch.bfloat16, device=L.dev) for L in layers]
+    yp = [rb.ctypes.c_void_p(y.data_ptr()) for y in ys]
+    ins = [[L.inputs(t) for t in range(K + W)] for L in layers]
+
+    def model_step(t):
+        for i in range(len(layers)):
+            s = lib.replay_stack_decode_layer(stk.h, i, rb.ctypes.byref(ins[i][t]), yp[i], sp)
+            if s != rb.OK:
+                raise rb.ReplayError(s, "replay_stack_decode_layer")
+
+    for t in range(W):
+        model_step(t)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(K):
+        model_step(W + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    replay_ms = e0.elapsed_time(e1) / K
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record(stream)
+        model_step(W + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    del stk, states
+    conv_S = [L.S0.clone() for L in layers]
+    cps = [rb.ctypes.byref(L.cfg) for L in layers]
+    Sps = [rb.ctypes.c_void_p(S.data_ptr()) for S in conv_S]
+
+    def conv_step(t):
+        for i in range(len(layers)):
+            s = lib.replay_conv_decode_step(cps[i], Sps[i], rb.ctypes.byref(ins[i][t]), yp[i], sp)
+            if s != rb.OK:
+                raise rb.ReplayError(s, "replay_conv_decode_step")
+
+    for t in range(min(W, 4)):
+        conv_step(t)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(K):
+        conv_step(W + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    conv_ms = e0.elapsed_time(e1) / K
+    B = layers[0].B
+    return {"layers": [L.kind for L in layers], "batch": B, "replay_ms_per_model_step": round(replay_ms, 5),
+            "replay_tokens_per_s": round(B / (replay_ms / 1e3), 1),
+            "model_step_ms_p50": round(per[K // 2], 5), "model_step_ms_p99": round(per[min(K - 1, int(0.99 * K))], 5),
+            "conventional_ms_per_model_step": round(conv_ms, 5),
+            "speedup_vs_conventional": round(conv_ms / replay_ms, 3)}
 
 
 def time_graph(L, conventional, n=64, reps=8):
@@ -489,6 +559,16 @@ def main():
             del Lg
             torch.cuda.empty_cache()
         out["flush_schedule_mamba2_b256"] = sched
+        # a hybrid model's SSM layers decoded as one stack (one bookkeeping set), lockstep
+        # and staggered flush phases, against the conventional kernel per layer
+        stack = {}
+        for name, fl in (("lockstep", 0), ("staggered", rb.FLAG_STAGGER_FLUSH)):
+            Ls = [Layer(rb, synth, torch, dev, kind, B, 128 + 16, seed=40 + i, flags=fl)
+                  for i, kind in enumerate(("mamba2", "gdn", "mamba2", "gdn"))]
+            stack[name] = time_stack(Ls, 128, 16, stream)
+            del Ls
+            torch.cuda.empty_cache()
+        out["hybrid_stack_b256"] = stack
 
     if args.sweep:
         with open(args.sweep, "w") as f:

@@ -74,6 +74,18 @@ _SIGS = {
     "replay_conv_decode_step": ([_CP, _vp, _IP, _vp, _vp], _i32),
     "replay_conv_spec_step": ([_CP, _vp, _vp, _i32, _IP, _vp, _vp], _i32),
     "replay_conv_spec_restore": ([_CP, _vp, _vp, _i32, _vp, _vp], _i32),
+    "replay_stack_create": ([ctypes.POINTER(_vp), _i32, _vp, ctypes.POINTER(_vp)], _i32),
+    "replay_stack_free": ([_vp], _i32),
+    "replay_stack_load": ([_vp, ctypes.POINTER(_vp), _vp], _i32),
+    "replay_stack_decode_layer": ([_vp, _i32, _IP, _vp, _vp], _i32),
+    "replay_stack_spec_layer": ([_vp, _i32, _i32, _IP, _vp, _vp], _i32),
+    "replay_stack_flush": ([_vp, ctypes.POINTER(_IP), _vp], _i32),
+    "replay_stack_commit": ([_vp, _vp, _vp], _i32),
+    "replay_stack_rollback": ([_vp, _vp], _i32),
+    "replay_stack_read_book": ([_vp, _vp, _vp, _vp], _i32),
+    "replay_stack_layers": ([_vp], _i32),
+    "replay_stack_next_layer": ([_vp], _i32),
+    "replay_stack_phase": ([_vp], _i32),
     "replay_stream_copy": ([_vp, _vp, _sz, _vp], _i32),
     "replay_stream_read": ([_vp, _sz, _vp, _vp], _i32),
 }
@@ -284,6 +296,92 @@ class ReplayState:
 
     def rollback(self):
         _check(_lib.replay_spec_rollback(self.h, _stream()), "replay_spec_rollback")
+
+
+class ReplayStack:
+    """The SSM layers of one model with one shared bookkeeping set (replay_stack_* in the
+    C ABI).  `layers` are ReplayState objects with equal batch and buf_cap; they stay
+    referenced here, so they outlive the stack handle."""
+
+    def __init__(self, layers):
+        self.layers = list(layers)
+        arr = (_vp * len(self.layers))(*[st.h.value for st in self.layers])
+        h = _vp()
+        _check(_lib.replay_stack_create(arr, len(self.layers), _stream(), ctypes.byref(h)), "replay_stack_create")
+        self.h = h
+
+    def __del__(self):
+        h = getattr(self, "h", None)
+        if h is not None and h.value:
+            _lib.replay_stack_free(h)
+            self.h = None
+
+    def free(self):
+        """Unbind the layers now (each must then be loaded before it steps on its own)."""
+        self.__del__()
+
+    def next_layer(self) -> int:
+        return _lib.replay_stack_next_layer(self.h)
+
+    def phase(self) -> int:
+        return _lib.replay_stack_phase(self.h)
+
+    def load(self, checkpoints):
+        """checkpoints[l]: layer l's logical checkpoint (converted to its checkpoint dtype)."""
+        keep = []
+        for st, S in zip(self.layers, checkpoints, strict=True):
+            S = S.to(device=st.device, dtype=st.ckt).contiguous()
+            assert tuple(S.shape) == st.ckpt_shape
+            keep.append(S)
+        arr = (_vp * len(keep))(*[S.data_ptr() for S in keep])
+        _check(_lib.replay_stack_load(self.h, arr, _stream()), "replay_stack_load")
+        self._keep = keep
+
+    def decode_layer(self, layer: int, tokens: dict, params: dict | None = None, y=None):
+        torch = _torch()
+        st = self.layers[layer]
+        c = st.cfg
+        if y is None:
+            y = torch.empty((1, c.batch, c.nheads, c.head_dim), dtype=st.iot, device=st.device)
+        ri = make_inputs(c, tokens, params)
+        _check(_lib.replay_stack_decode_layer(self.h, int(layer), ctypes.byref(ri), _ptr(y, st.iot, "y"), _stream()),
+               "replay_stack_decode_layer")
+        return y
+
+    def spec_layer(self, layer: int, k: int, drafts: dict, params: dict | None = None, y=None):
+        torch = _torch()
+        st = self.layers[layer]
+        c = st.cfg
+        if y is None:
+            y = torch.empty((k, c.batch, c.nheads, c.head_dim), dtype=st.iot, device=st.device)
+        ri = make_inputs(c, drafts, params)
+        _check(_lib.replay_stack_spec_layer(self.h, int(layer), int(k), ctypes.byref(ri), _ptr(y, st.iot, "y"),
+                                            _stream()), "replay_stack_spec_layer")
+        return y
+
+    def flush(self, params=None):
+        """params[l]: layer l's parameter dict (Mamba-2 needs A) or None."""
+        params = params or [None] * len(self.layers)
+        ris = [make_inputs(st.cfg, {}, p) for st, p in zip(self.layers, params, strict=True)]
+        arr = (_IP * len(ris))(*[ctypes.pointer(ri) for ri in ris])
+        _check(_lib.replay_stack_flush(self.h, arr, _stream()), "replay_stack_flush")
+
+    def commit(self, accepted):
+        torch = _torch()
+        _check(_lib.replay_stack_commit(self.h, _ptr(accepted, torch.int32, "accepted"), _stream()),
+               "replay_stack_commit")
+
+    def rollback(self):
+        _check(_lib.replay_stack_rollback(self.h, _stream()), "replay_stack_rollback")
+
+    def read_book(self):
+        """(len, pend, fc, err) of the shared bookkeeping, as device tensors."""
+        torch = _torch()
+        B = self.layers[0].cfg.batch
+        book = torch.empty((3, B), dtype=torch.int32, device=self.layers[0].device)
+        err = torch.empty((1,), dtype=torch.int32, device=self.layers[0].device)
+        _check(_lib.replay_stack_read_book(self.h, _ptr(book), _ptr(err), _stream()), "replay_stack_read_book")
+        return book[0], book[1], book[2], err
 
 
 # ---- conventional baselines -----------------------------------------------------

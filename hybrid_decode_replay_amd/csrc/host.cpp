@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "internal.hpp"
 
@@ -18,6 +19,21 @@ struct replay_state {
     replay_layout lay;
     int parity;   // bookkeeping copy that holds the current values
     int phase;    // 0 idle, 1 drafts pending
+    replay_stack* stack = nullptr;   // set while bound to a stack (which then owns the bookkeeping)
+    bool needs_load = false;         // a former stack member: its own bookkeeping is stale
+};
+
+// Layers of one model share one bookkeeping set (layer 0's region).  A model
+// step runs every layer once, in order; `next` is the layer it expects.
+struct replay_stack {
+    std::vector<replay_state*> layers;
+    int32_t* book;
+    uint32_t* err;
+    int parity = 0;
+    int phase = 0;    // 0 idle, 1 drafts pending
+    int next = 0;     // next layer of the current step (0 between steps)
+    int step_mode = -1;
+    int step_k = 0;
 };
 
 namespace {
@@ -211,6 +227,11 @@ rs::StepArgs step_args(const replay_state* st, const replay_inputs* in, void* y,
     a.bank_s = B * H * cap;
     a.book = at<int32_t>(st, L.book_off);
     a.err = at<uint32_t>(st, L.err_off);
+    if (st->stack) {                      // every member follows the stack's one bookkeeping set
+        a.book = st->stack->book;
+        a.err = st->stack->err;
+        a.parity = st->stack->parity;
+    }
     if (c->kind == REPLAY_MAMBA2) {
         a.in_c = in->x;
         a.in_r = in->B;
@@ -247,7 +268,7 @@ replay_status launch_step(replay_state* st, const replay_inputs* in, void* y, in
             : ck == rs::CK_FP8 ? rs::launch_gdn_step_fp8(a, io, rc, hs)
                                : rs::launch_gdn_step_f32(a, io, rc, hs);
     replay_status s = hip_check(e, "replay step launch");
-    if (s == REPLAY_OK) st->parity ^= 1;
+    if (s == REPLAY_OK && !st->stack) st->parity ^= 1;
     return s;
 }
 
@@ -334,10 +355,22 @@ replay_status replay_state_layout(const replay_state* st, replay_layout* out)
 
 int32_t replay_state_phase(const replay_state* st) { return st ? st->phase : -1; }
 
+static replay_status load_impl(replay_state* st, const void* S, void* stream);
+
 replay_status replay_load_checkpoint(replay_state* st, const void* S, void* stream)
 {
     if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
+    if (st->stack) return fail(REPLAY_ERR_STATE, "the state is a stack member: load through the stack");
     if (st->phase != 0) return fail(REPLAY_ERR_STATE, "load while drafts are pending");
+    replay_status s = load_impl(st, S, stream);
+    if (s == REPLAY_OK) st->needs_load = false;
+    return s;
+}
+
+// Checkpoint tiles and read copy of one state, then its bookkeeping (the
+// stack's, for a member).
+static replay_status load_impl(replay_state* st, const void* S, void* stream)
+{
     replay_status s = check_ptr(S, "S_logical");
     if (s != REPLAY_OK) return s;
     const replay_config* c = &st->cfg;
@@ -355,6 +388,7 @@ replay_status replay_load_checkpoint(replay_state* st, const void* S, void* stre
                       "read copy quantize");
         if (s != REPLAY_OK) return s;
     }
+    if (st->stack) return REPLAY_OK;
     return hip_check(rs::launch_book_reset(at<int32_t>(st, st->lay.book_off), at<uint32_t>(st, st->lay.err_off),
                                            c->batch, st->parity, c->buf_cap,
                                            (c->flags & REPLAY_FLAG_STAGGER_FLUSH) != 0, hs),
@@ -386,23 +420,31 @@ replay_status replay_read_copy(const replay_state* st, uint8_t* codes_out, uint8
                      "read copy export");
 }
 
+static replay_status read_book_impl(const int32_t* book, const uint32_t* err, int B, int parity, int32_t* book_out,
+                                    uint32_t* err_out, void* stream)
+{
+    if (!book_out) return fail(REPLAY_ERR_ARG, "book_out is NULL");
+    const size_t n = (size_t)3 * B * sizeof(int32_t);
+    hipStream_t hs = (hipStream_t)stream;
+    replay_status s = hip_check(hipMemcpyAsync(book_out, book + (size_t)parity * 4 * B, n, hipMemcpyDeviceToDevice, hs),
+                                "bookkeeping copy");
+    if (s != REPLAY_OK || !err_out) return s;
+    return hip_check(hipMemcpyAsync(err_out, err, 4, hipMemcpyDeviceToDevice, hs), "error word copy");
+}
+
 replay_status replay_read_book(const replay_state* st, int32_t* book_out, uint32_t* err_out, void* stream)
 {
     if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
-    if (!book_out) return fail(REPLAY_ERR_ARG, "book_out is NULL");
-    const size_t n = (size_t)3 * st->cfg.batch * sizeof(int32_t);
-    hipStream_t hs = (hipStream_t)stream;
-    replay_status s = hip_check(hipMemcpyAsync(book_out, at<int32_t>(st, st->lay.book_off) + (size_t)st->parity * 4 * st->cfg.batch,
-                                               n, hipMemcpyDeviceToDevice, hs),
-                                "bookkeeping copy");
-    if (s != REPLAY_OK || !err_out) return s;
-    return hip_check(hipMemcpyAsync(err_out, at<uint32_t>(st, st->lay.err_off), 4, hipMemcpyDeviceToDevice, hs),
-                     "error word copy");
+    if (st->stack) return fail(REPLAY_ERR_STATE, "the state is a stack member: read the stack's bookkeeping");
+    return read_book_impl(at<int32_t>(st, st->lay.book_off), at<uint32_t>(st, st->lay.err_off), st->cfg.batch,
+                          st->parity, book_out, err_out, stream);
 }
 
 replay_status replay_decode_step(replay_state* st, const replay_inputs* in, void* y, void* stream)
 {
     if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
+    if (st->stack) return fail(REPLAY_ERR_STATE, "the state is a stack member: step it through the stack");
+    if (st->needs_load) return fail(REPLAY_ERR_STATE, "a former stack member must be loaded first");
     if (st->phase != 0) return fail(REPLAY_ERR_STATE, "decode while drafts are pending");
     replay_status s = check_inputs(&st->cfg, in, true, true);
     if (s != REPLAY_OK) return s;
@@ -413,6 +455,8 @@ replay_status replay_decode_step(replay_state* st, const replay_inputs* in, void
 replay_status replay_flush(replay_state* st, const replay_inputs* in, void* stream)
 {
     if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
+    if (st->stack) return fail(REPLAY_ERR_STATE, "the state is a stack member: step it through the stack");
+    if (st->needs_load) return fail(REPLAY_ERR_STATE, "a former stack member must be loaded first");
     if (st->phase != 0) return fail(REPLAY_ERR_STATE, "flush while drafts are pending");
     replay_inputs none;
     memset(&none, 0, sizeof none);
@@ -427,6 +471,8 @@ replay_status replay_flush(replay_state* st, const replay_inputs* in, void* stre
 replay_status replay_spec_append(replay_state* st, int32_t k, const replay_inputs* drafts, void* y, void* stream)
 {
     if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
+    if (st->stack) return fail(REPLAY_ERR_STATE, "the state is a stack member: step it through the stack");
+    if (st->needs_load) return fail(REPLAY_ERR_STATE, "a former stack member must be loaded first");
     if (st->phase != 0) return fail(REPLAY_ERR_STATE, "spec_append while drafts are pending");
     if (k < 1 || k > st->cfg.buf_cap) return fail(REPLAY_ERR_CAPACITY, "k = %d outside [1, %d]", k, st->cfg.buf_cap);
     replay_status s = check_inputs(&st->cfg, drafts, true, true);
@@ -453,6 +499,8 @@ static replay_status commit_impl(replay_state* st, const int32_t* accepted, void
 replay_status replay_spec_commit(replay_state* st, const int32_t* accepted, void* stream)
 {
     if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
+    if (st->stack) return fail(REPLAY_ERR_STATE, "the state is a stack member: step it through the stack");
+    if (st->needs_load) return fail(REPLAY_ERR_STATE, "a former stack member must be loaded first");
     if (!accepted) return fail(REPLAY_ERR_ARG, "accepted is NULL");
     if (!aligned(accepted, 4)) return fail(REPLAY_ERR_ALIGN, "accepted is not 4-byte aligned");
     return commit_impl(st, accepted, stream);
@@ -461,8 +509,193 @@ replay_status replay_spec_commit(replay_state* st, const int32_t* accepted, void
 replay_status replay_spec_rollback(replay_state* st, void* stream)
 {
     if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
+    if (st->stack) return fail(REPLAY_ERR_STATE, "the state is a stack member: step it through the stack");
+    if (st->needs_load) return fail(REPLAY_ERR_STATE, "a former stack member must be loaded first");
     return commit_impl(st, nullptr, stream);
 }
+
+// ---- layer stacks: one bookkeeping set for every SSM layer of a model --------
+
+static replay_status stack_check_step(const replay_stack* stk, int32_t layer, int mode, int k)
+{
+    if (!stk) return fail(REPLAY_ERR_ARG, "stack is NULL");
+    const int n = (int)stk->layers.size();
+    if (layer < 0 || layer >= n) return fail(REPLAY_ERR_ARG, "layer %d outside [0, %d)", layer, n);
+    if (layer != stk->next)
+        return fail(REPLAY_ERR_STATE, "layer %d stepped out of order: the step expects layer %d", layer, stk->next);
+    if (stk->next == 0 && stk->phase != 0) return fail(REPLAY_ERR_STATE, "drafts are pending");
+    if (stk->next > 0 && (mode != stk->step_mode || k != stk->step_k))
+        return fail(REPLAY_ERR_STATE, "every layer of a step runs the same operation with the same draft count");
+    return REPLAY_OK;
+}
+
+// A layer of the step ran: after the last one the shared bookkeeping copy
+// written by the step becomes the current one.
+static void stack_advance(replay_stack* stk, int mode, int k)
+{
+    if (stk->next == 0) {
+        stk->step_mode = mode;
+        stk->step_k = k;
+    }
+    if (++stk->next == (int)stk->layers.size()) {
+        stk->next = 0;
+        stk->parity ^= 1;
+        stk->step_mode = -1;
+        if (mode == rs::MODE_SPEC) stk->phase = 1;
+    }
+}
+
+static replay_status stack_idle(const replay_stack* stk, const char* what)
+{
+    if (!stk) return fail(REPLAY_ERR_ARG, "stack is NULL");
+    if (stk->next != 0) return fail(REPLAY_ERR_STATE, "%s in the middle of a step (layer %d is next)", what, stk->next);
+    return REPLAY_OK;
+}
+
+static replay_status stack_reset_book(replay_stack* stk, void* stream)
+{
+    const replay_config* c = &stk->layers[0]->cfg;
+    return hip_check(rs::launch_book_reset(stk->book, stk->err, c->batch, stk->parity, c->buf_cap,
+                                           (c->flags & REPLAY_FLAG_STAGGER_FLUSH) != 0, (hipStream_t)stream),
+                     "bookkeeping reset");
+}
+
+replay_status replay_stack_create(replay_state* const* layers, int32_t nlayers, void* stream, replay_stack** out)
+{
+    if (!out) return fail(REPLAY_ERR_ARG, "out is NULL");
+    if (!layers || nlayers < 1) return fail(REPLAY_ERR_ARG, "a stack needs at least one layer");
+    const replay_config* c0 = layers[0] ? &layers[0]->cfg : nullptr;
+    for (int l = 0; l < nlayers; ++l) {
+        const replay_state* st = layers[l];
+        if (!st) return fail(REPLAY_ERR_ARG, "layer %d is NULL", l);
+        for (int m = 0; m < l; ++m)
+            if (layers[m] == st) return fail(REPLAY_ERR_ARG, "layer %d repeats layer %d", l, m);
+        if (st->stack) return fail(REPLAY_ERR_STATE, "layer %d already belongs to a stack", l);
+        if (st->phase != 0) return fail(REPLAY_ERR_STATE, "layer %d has pending drafts", l);
+        const replay_config* c = &st->cfg;
+        if (c->batch != c0->batch || c->buf_cap != c0->buf_cap)
+            return fail(REPLAY_ERR_SHAPE, "layer %d: batch and buf_cap must match layer 0", l);
+        if ((c->flags & REPLAY_FLAG_STAGGER_FLUSH) != (c0->flags & REPLAY_FLAG_STAGGER_FLUSH))
+            return fail(REPLAY_ERR_ARG, "layer %d: REPLAY_FLAG_STAGGER_FLUSH must match layer 0", l);
+    }
+    replay_stack* stk = new replay_stack;
+    stk->layers.assign(layers, layers + nlayers);
+    stk->book = at<int32_t>(layers[0], layers[0]->lay.book_off);
+    stk->err = at<uint32_t>(layers[0], layers[0]->lay.err_off);
+    replay_status s = stack_reset_book(stk, stream);
+    if (s != REPLAY_OK) {
+        delete stk;
+        return s;
+    }
+    for (replay_state* st : stk->layers) st->stack = stk;
+    *out = stk;
+    return ok();
+}
+
+replay_status replay_stack_free(replay_stack* stk)
+{
+    if (!stk) return fail(REPLAY_ERR_ARG, "stack is NULL");
+    for (replay_state* st : stk->layers) {
+        st->stack = nullptr;
+        st->needs_load = true;
+        st->phase = 0;
+    }
+    delete stk;
+    return ok();
+}
+
+replay_status replay_stack_load(replay_stack* stk, const void* const* S, void* stream)
+{
+    replay_status s = stack_idle(stk, "load");
+    if (s != REPLAY_OK) return s;
+    if (stk->phase != 0) return fail(REPLAY_ERR_STATE, "load while drafts are pending");
+    if (!S) return fail(REPLAY_ERR_ARG, "S_logical is NULL");
+    for (size_t l = 0; l < stk->layers.size(); ++l)
+        if ((s = check_ptr(S[l], "S_logical[layer]")) != REPLAY_OK) return s;
+    for (size_t l = 0; l < stk->layers.size(); ++l)
+        if ((s = load_impl(stk->layers[l], S[l], stream)) != REPLAY_OK) return s;
+    return stack_reset_book(stk, stream);
+}
+
+replay_status replay_stack_decode_layer(replay_stack* stk, int32_t layer, const replay_inputs* in, void* y,
+                                        void* stream)
+{
+    replay_status s = stack_check_step(stk, layer, rs::MODE_DECODE, 1);
+    if (s != REPLAY_OK) return s;
+    replay_state* st = stk->layers[layer];
+    if ((s = check_inputs(&st->cfg, in, true, true)) != REPLAY_OK) return s;
+    if ((s = check_ptr(y, "y")) != REPLAY_OK) return s;
+    if ((s = launch_step(st, in, y, rs::MODE_DECODE, 1, stream)) != REPLAY_OK) return s;
+    stack_advance(stk, rs::MODE_DECODE, 1);
+    return ok();
+}
+
+replay_status replay_stack_spec_layer(replay_stack* stk, int32_t layer, int32_t k, const replay_inputs* drafts,
+                                      void* y, void* stream)
+{
+    replay_status s = stack_check_step(stk, layer, rs::MODE_SPEC, k);
+    if (s != REPLAY_OK) return s;
+    replay_state* st = stk->layers[layer];
+    if (k < 1 || k > st->cfg.buf_cap) return fail(REPLAY_ERR_CAPACITY, "k = %d outside [1, %d]", k, st->cfg.buf_cap);
+    if ((s = check_inputs(&st->cfg, drafts, true, true)) != REPLAY_OK) return s;
+    if ((s = check_ptr(y, "y")) != REPLAY_OK) return s;
+    if ((s = launch_step(st, drafts, y, rs::MODE_SPEC, k, stream)) != REPLAY_OK) return s;
+    stack_advance(stk, rs::MODE_SPEC, k);
+    return ok();
+}
+
+replay_status replay_stack_flush(replay_stack* stk, const replay_inputs* const* in, void* stream)
+{
+    replay_status s = stack_idle(stk, "flush");
+    if (s != REPLAY_OK) return s;
+    if (stk->phase != 0) return fail(REPLAY_ERR_STATE, "flush while drafts are pending");
+    replay_inputs none;
+    memset(&none, 0, sizeof none);
+    for (size_t l = 0; l < stk->layers.size(); ++l) {
+        const replay_inputs* il = (in && in[l]) ? in[l] : &none;
+        if (stk->layers[l]->cfg.kind == REPLAY_MAMBA2 && (s = check_ptr(il->A, "A")) != REPLAY_OK) return s;
+    }
+    for (size_t l = 0; l < stk->layers.size(); ++l) {
+        const replay_inputs* il = (in && in[l]) ? in[l] : &none;
+        if ((s = launch_step(stk->layers[l], il, nullptr, rs::MODE_FLUSH, 0, stream)) != REPLAY_OK) return s;
+    }
+    stk->parity ^= 1;
+    return ok();
+}
+
+static replay_status stack_commit_impl(replay_stack* stk, const int32_t* accepted, void* stream)
+{
+    replay_status s = stack_idle(stk, "commit");
+    if (s != REPLAY_OK) return s;
+    if (stk->phase != 1) return fail(REPLAY_ERR_STATE, "no drafts pending");
+    s = hip_check(rs::launch_book_commit(stk->book, stk->err, stk->layers[0]->cfg.batch, stk->parity, accepted,
+                                         (hipStream_t)stream),
+                  "commit");
+    if (s == REPLAY_OK) {
+        stk->parity ^= 1;
+        stk->phase = 0;
+    }
+    return s;
+}
+
+replay_status replay_stack_commit(replay_stack* stk, const int32_t* accepted, void* stream)
+{
+    if (!accepted) return fail(REPLAY_ERR_ARG, "accepted is NULL");
+    if (!aligned(accepted, 4)) return fail(REPLAY_ERR_ALIGN, "accepted is not 4-byte aligned");
+    return stack_commit_impl(stk, accepted, stream);
+}
+
+replay_status replay_stack_rollback(replay_stack* stk, void* stream) { return stack_commit_impl(stk, nullptr, stream); }
+
+replay_status replay_stack_read_book(const replay_stack* stk, int32_t* book_out, uint32_t* err_out, void* stream)
+{
+    if (!stk) return fail(REPLAY_ERR_ARG, "stack is NULL");
+    return read_book_impl(stk->book, stk->err, stk->layers[0]->cfg.batch, stk->parity, book_out, err_out, stream);
+}
+
+int32_t replay_stack_layers(const replay_stack* stk) { return stk ? (int32_t)stk->layers.size() : -1; }
+int32_t replay_stack_next_layer(const replay_stack* stk) { return stk ? stk->next : -1; }
+int32_t replay_stack_phase(const replay_stack* stk) { return stk ? stk->phase : -1; }
 
 static replay_status conv_common(const replay_config* cfg, rs::ConvArgs* a, const replay_inputs* in, void* y, int T)
 {

@@ -229,6 +229,66 @@ replay_status replay_spec_commit(replay_state *st, const int32_t *accepted, void
 /* Drops every pending draft (pointer reset; commit of 0). */
 replay_status replay_spec_rollback(replay_state *st, void *stream);
 
+/* ---- layer stacks --------------------------------------------------------
+ * A hybrid model interleaves several SSM layers with a few attention layers
+ * ([TR] "NVIDIA ve Dao AI Lab ...", section "ReplaySSM nasil calisir?"; the
+ * decode-step speedups of section "Durum trafigini azaltma ve rollback'in
+ * basitlestirilmesi" are measured on such models).  Every SSM layer of the model decodes the same
+ * token positions of the same sequences, so the buffer bookkeeping (len, pend,
+ * fc and the window limit per sequence) is one set for the whole model: a
+ * stack keeps it once, every layer's step follows it, and a speculative commit
+ * or rollback is one pointer update for all layers.
+ *
+ * Members are ordinary states (Mamba-2 and GDN may be mixed) with equal batch
+ * and buf_cap and the same REPLAY_FLAG_STAGGER_FLUSH setting.  While bound to
+ * a stack a member refuses its own load, decode, flush, spec, commit and
+ * rollback calls (REPLAY_ERR_STATE); replay_read_checkpoint / replay_read_copy
+ * still work on it.  A model step calls the layer entry points once per layer
+ * in layer order (the caller computes layer l+1's inputs from layer l's
+ * outputs in between); after the last layer the shared bookkeeping advances.
+ * A call out of order, or a spec step whose k differs from the step's first
+ * layer, returns REPLAY_ERR_STATE and launches nothing.
+ */
+typedef struct replay_stack replay_stack; /* opaque host handle */
+
+/* Binds nlayers (>= 1) states into a stack, in layer order, and resets the
+ * shared bookkeeping (len = pend = fc = 0, error word 0) on `stream`.  The
+ * states must be idle and in no other stack.  The stack keeps the pointers; it
+ * owns no device memory of its own (layer 0's bookkeeping region is the shared
+ * one). */
+replay_status replay_stack_create(replay_state *const *layers, int32_t nlayers, void *stream,
+                                  replay_stack **out);
+/* Unbinds the members and frees the handle.  A former member must be loaded
+ * (replay_load_checkpoint) before it steps on its own again. */
+replay_status replay_stack_free(replay_stack *stk);
+/* Loads every layer's logical checkpoint (S_logical[l], device, in that
+ * layer's ckpt_dtype), refreshes read copies and resets the shared
+ * bookkeeping.  Not allowed mid-step or while drafts are pending. */
+replay_status replay_stack_load(replay_stack *stk, const void *const *S_logical, void *stream);
+/* Layer `layer`'s decode step (as replay_decode_step).  Must be the next
+ * layer of the current step. */
+replay_status replay_stack_decode_layer(replay_stack *stk, int32_t layer, const replay_inputs *in,
+                                        void *y, void *stream);
+/* Layer `layer`'s spec append of k drafts (as replay_spec_append).  Every
+ * layer of the step appends the same k; after the last layer the drafts are
+ * pending for the whole stack. */
+replay_status replay_stack_spec_layer(replay_stack *stk, int32_t layer, int32_t k,
+                                      const replay_inputs *drafts, void *y, void *stream);
+/* Folds every non-empty buffer of every layer (in[l] as for replay_flush;
+ * in may be NULL for an all-GDN stack). */
+replay_status replay_stack_flush(replay_stack *stk, const replay_inputs *const *in, void *stream);
+/* One commit (accepted: device int32 [B]) or rollback for every layer. */
+replay_status replay_stack_commit(replay_stack *stk, const int32_t *accepted, void *stream);
+replay_status replay_stack_rollback(replay_stack *stk, void *stream);
+/* The shared bookkeeping, as replay_read_book. */
+replay_status replay_stack_read_book(const replay_stack *stk, int32_t *book_out, uint32_t *err_out,
+                                     void *stream);
+/* Number of layers; the layer the current step expects next (0 between
+ * steps); 0 idle or 1 drafts pending.  -1 for a NULL handle. */
+int32_t replay_stack_layers(const replay_stack *stk);
+int32_t replay_stack_next_layer(const replay_stack *stk);
+int32_t replay_stack_phase(const replay_stack *stk);
+
 /* ---- in-run conventional baselines --------------------------------------
  * Ordinary decoding on a plain logical state [B][H][rows][cols] in the
  * config's ckpt_dtype (load, decay and update, output, store per token; a

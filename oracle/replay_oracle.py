@@ -475,6 +475,91 @@ class GDNSession(_Session):
         return self.scale * np.einsum("hij,hj->hi", S_b, q)
 
 
+class StackSession:
+    """The SSM layers of one model, each its own session, stepped as one stack.
+
+    Every layer of a hybrid model decodes the same token positions of the same
+    sequences ([TR] "NVIDIA ve Dao AI Lab ...", section "ReplaySSM nasil calisir?"),
+    so the layers' bookkeeping moves in lockstep and one set describes them all.
+    The protocol: a model step runs each layer once, in layer order, all with the
+    same operation and draft count; a commit or rollback applies to every layer;
+    loads and flushes act on all layers between steps.  Each layer keeps its own
+    session here, so the lockstep claim is checked, not assumed: trace() asserts
+    that every layer's bookkeeping is the same."""
+
+    def __init__(self, sessions):
+        self.layers = list(sessions)
+        if not self.layers:
+            raise ValueError("a stack needs at least one layer")
+        if len({(s.B, s.cap, s.stagger) for s in self.layers}) != 1:
+            raise ValueError("layers of a stack share batch, capacity and the stagger setting")
+        self.next = 0
+        self.step_op = None          # (operation, draft count) of the step in progress
+
+    def _enter(self, layer, op):
+        if layer != self.next:
+            raise PhaseError(f"layer {layer} stepped out of order (layer {self.next} is next)")
+        if self.next > 0 and op != self.step_op:
+            raise PhaseError("every layer of a step runs the same operation and draft count")
+        self.step_op = op
+
+    def _leave(self):
+        self.next += 1
+        if self.next == len(self.layers):
+            self.next = 0
+            self.step_op = None
+
+    def _idle(self, what):
+        if self.next:
+            raise PhaseError(f"{what} in the middle of a step")
+
+    def decode_layer(self, layer, inp):
+        self._enter(layer, ("decode", 1))
+        y = self.layers[layer].decode(inp)
+        self._leave()
+        return y
+
+    def spec_layer(self, layer, drafts):
+        self._enter(layer, ("spec", len(drafts)))
+        ys = self.layers[layer].spec_append(drafts)
+        self._leave()
+        return ys
+
+    def flush(self):
+        self._idle("flush")
+        for s in self.layers:
+            s.flush()
+
+    def commit(self, accepted):
+        self._idle("commit")
+        for s in self.layers:
+            s.commit(accepted)
+
+    def rollback(self):
+        self._idle("rollback")
+        for s in self.layers:
+            s.rollback()
+
+    def load(self, checkpoints):
+        self._idle("load")
+        for s, S0 in zip(self.layers, checkpoints, strict=True):
+            s.load(S0)
+
+    @property
+    def err(self):
+        errs = {s.err for s in self.layers}
+        assert len(errs) == 1, "layers disagree on the error word"
+        return errs.pop()
+
+    def trace(self):
+        self._idle("trace")
+        traces = [s.trace() for s in self.layers]
+        for t in traces[1:]:
+            for a, b in zip(t, traces[0]):
+                assert np.array_equal(a, b), "layers of a stack left lockstep"
+        return traces[0]
+
+
 def normwise_error(got, ref, axis=-1):
     """max over vectors of ||got - ref||_inf / max(||ref||_inf, 1e-30), vectors along `axis`."""
     got = np.asarray(got, np.float64)

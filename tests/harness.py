@@ -140,10 +140,15 @@ class Pair:
         self.marked |= diff.any(axis=(2, 3))
 
     def check_state(self, what):
+        self.check_ckpt(what)
+        self._check_book(what)
+
+    def check_ckpt(self, what):
+        """The checkpoint against the oracle's (the bookkeeping is not read: a stack member's
+        lives in the stack)."""
         torch.cuda.synchronize()
         if self.fp8:
             self._check_fp8_state(what)
-            self._check_book(what)
             return
         ck = self.st.read_checkpoint().cpu().numpy().astype(np.float64)
         ref = self.orc.ckpt
@@ -156,16 +161,10 @@ class Pair:
         err = float(np.max(np.where(zero, 0.0, num / den)))
         self.max_err["ckpt"] = max(self.max_err["ckpt"], err)
         assert err <= self.tol, f"{what}: checkpoint error {err:.3e} > {self.tol:.1e}"
-        self._check_book(what)
 
     def _check_book(self, what):
-        L, P, F, E = self.st.read_book()
-        got = (L.cpu().numpy(), P.cpu().numpy(), F.cpu().numpy(), int(E.cpu().numpy()[0]))
-        oL, oP, oF = self.orc.trace()
-        assert np.array_equal(got[0], oL), f"{what}: len {got[0]} != {oL}"
-        assert np.array_equal(got[1], oP), f"{what}: pend {got[1]} != {oP}"
-        assert np.array_equal(got[2], oF), f"{what}: fc {got[2]} != {oF}"
-        assert got[3] == self.orc.err, f"{what}: error word {got[3]} != {self.orc.err}"
+        check_book(self.st.read_book(), self.orc, what)
+
 
     # -- operations
     def decode(self, tok, what="decode", check_state=True):
@@ -204,3 +203,15 @@ class Pair:
         self.st.rollback()
         self.orc.rollback()
         self.check_state(what)
+
+
+def check_book(book, orc, what):
+    """GPU bookkeeping (len, pend, fc, err device tensors) against an oracle session or stack:
+    bit-exact."""
+    L, P, F, E = book
+    got = (L.cpu().numpy(), P.cpu().numpy(), F.cpu().numpy(), int(E.cpu().numpy()[0]))
+    oL, oP, oF = orc.trace()
+    assert np.array_equal(got[0], oL), f"{what}: len {got[0]} != {oL}"
+    assert np.array_equal(got[1], oP), f"{what}: pend {got[1]} != {oP}"
+    assert np.array_equal(got[2], oF), f"{what}: fc {got[2]} != {oF}"
+    assert got[3] == orc.err, f"{what}: error word {got[3]} != {orc.err}"

@@ -1,0 +1,192 @@
+"""GPU parity of layer stacks: the SSM layers of one model with one bookkeeping set.
+
+A hybrid model's SSM layers all decode the same token positions ([TR] "NVIDIA ve
+Dao AI Lab ...", section "ReplaySSM nasil calisir?"), so a stack keeps the
+buffer pointers once and a speculative commit or rollback is one pointer update
+for every layer.  Checked here, through the C ABI, against the oracle's
+StackSession (one oracle session per layer, whose bookkeeping must stay in
+lockstep):
+  * a mixed stack -- Mamba-2 and GDN layers, fp32 / fp16 / FP8 checkpoints, with
+    and without read copies -- through decode steps, spec append with one
+    commit for all layers, rollback and flush: every layer's outputs and
+    checkpoint within its tolerance, the shared bookkeeping bit-exact; also with
+    staggered flush phases;
+  * the protocol: layer order, one operation and draft count per step, members
+    refusing their own step calls, and a former member stepping alone again
+    after a load.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from hybrid_decode_replay_amd import synth  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from hybrid_decode_replay_amd import binding  # noqa: F401  (fails loudly if not built)
+    yield
+
+
+def rb():
+    from hybrid_decode_replay_amd import binding
+    return binding
+
+
+B, CAP = 4, 5
+# (kind, H, G, C, R, checkpoint dtype, read copy)
+LAYERS = [("mamba2", 4, 2, 64, 128, "f32", None),
+          ("gdn", 2, 2, 32, 64, "f32", "mxfp4"),
+          ("mamba2", 2, 1, 32, 64, "f16", "fp8"),
+          ("gdn", 2, 2, 64, 32, "fp8", None)]
+
+
+def _pairs(flags=0):
+    from harness import Pair
+    b = rb()
+    pairs, toks = [], []
+    for i, (kind, H, G, C, R, ck, rc) in enumerate(LAYERS):
+        seed = 90 + i
+        p = Pair(b.MAMBA2 if kind == "mamba2" else b.GDN, B, H, G, C, R, cap=CAP, io=b.F32, seed=seed,
+                 S0=synth.checkpoint(seed, (B, H, C, R), std=0.5), flags=flags,
+                 ckpt={"f32": b.F32, "f16": b.F16, "fp8": b.FP8_E4M3}[ck],
+                 read_copy={None: b.NONE, "fp8": b.FP8_E4M3, "mxfp4": b.MXFP4}[rc])
+        pairs.append(p)
+        if kind == "mamba2":
+            toks.append(synth.mamba2_tokens(seed, 40, B, H, G, C, R))
+        else:
+            toks.append(synth.gdn_tokens(seed, 40, B, H, G, R, C))
+    return pairs, toks
+
+
+class StackPair:
+    """A GPU ReplayStack and the oracle's StackSession over the same layers."""
+
+    def __init__(self, pairs):
+        from oracle import replay_oracle as ro
+        self.pairs = pairs
+        self.g = rb().ReplayStack([p.st for p in pairs])
+        self.o = ro.StackSession([p.orc for p in pairs])
+
+    def check(self, what):
+        from harness import check_book
+        for l, p in enumerate(self.pairs):
+            p.check_ckpt(f"{what}, layer {l}")
+        check_book(self.g.read_book(), self.o, what)
+
+    def decode(self, toks, t, what):
+        for l, p in enumerate(self.pairs):
+            tok = synth.token(toks[l], t)
+            y = self.g.decode_layer(l, p.to_dev(tok), p.params)
+            yo = self.o.decode_layer(l, tok)
+            if p.fp8:
+                p.check_ckpt(f"{what}, layer {l}")
+            p.check_outputs(y[0], yo, f"{what}, layer {l}")
+        self.check(what)
+
+    def spec(self, toks, a, z, what):
+        for l, p in enumerate(self.pairs):
+            drafts = {n: v[a:z] for n, v in toks[l].items()}
+            y = self.g.spec_layer(l, z - a, p.to_dev(drafts), p.params)
+            yo = self.o.spec_layer(l, [synth.token(toks[l], t) for t in range(a, z)])
+            if p.fp8:
+                p.check_ckpt(f"{what}, layer {l}")
+            p.check_outputs(y, np.stack(yo), f"{what}, layer {l}")
+        self.check(what)
+
+
+@pytest.mark.parametrize("stagger", [False, True])
+def test_mixed_stack_parity(stagger):
+    b = rb()
+    pairs, toks = _pairs(b.FLAG_STAGGER_FLUSH if stagger else 0)
+    sp = StackPair(pairs)
+    print(f"[stack] {len(pairs)} layers, stagger={stagger}", flush=True)
+    assert sp.g.next_layer() == 0 and sp.g.phase() == 0
+    for t in range(7):
+        sp.decode(toks, t, f"decode {t}")
+    sp.spec(toks, 7, 10, "spec 3")
+    assert sp.g.phase() == 1
+    accepted = [3, 1, 0, 2]
+    sp.g.commit(torch.tensor(accepted, dtype=torch.int32, device="cuda"))
+    sp.o.commit(accepted)
+    sp.check("commit")
+    for t in range(10, 14):
+        sp.decode(toks, t, f"decode {t}")
+    sp.spec(toks, 14, 18, "spec 4")
+    sp.g.rollback()
+    sp.o.rollback()
+    sp.check("rollback")
+    sp.decode(toks, 18, "decode 18")
+    sp.g.flush([p.params for p in pairs])
+    sp.o.flush()
+    sp.check("flush")
+    for t in range(19, 26):
+        sp.decode(toks, t, f"decode {t}")
+    # reload every layer through the stack: buffers empty, pointers reset
+    S = [synth.checkpoint(99 + l, p.st.ckpt_shape, std=0.5) for l, p in enumerate(pairs)]
+    from oracle import replay_oracle as ro
+    Sl = []
+    for p, s in zip(pairs, S):
+        if p.fp8:
+            s = ro.e4m3_decode(ro.e4m3_encode(s)).reshape(s.shape).astype(np.float32)
+        elif p.st.ckt == torch.float16:
+            s = s.astype(np.float16)
+        Sl.append(s)
+    sp.g.load([torch.from_numpy(np.ascontiguousarray(s)).cuda() for s in Sl])
+    sp.o.load([np.asarray(s, np.float64) for s in Sl])
+    sp.check("load")
+    for t in range(26, 30):
+        sp.decode(toks, t, f"decode {t}")
+    for l, p in enumerate(pairs):
+        print(f"[stack] layer {l} max errors {p.max_err}", flush=True)
+
+
+def test_stack_protocol():
+    b = rb()
+    pairs, toks = _pairs()
+    sp = StackPair(pairs)
+    p0, p1 = pairs[0], pairs[1]
+    tok0 = p0.to_dev(synth.token(toks[0], 0))
+    tok1 = p1.to_dev(synth.token(toks[1], 0))
+
+    def status(fn):
+        with pytest.raises(b.ReplayError) as ei:
+            fn()
+        return ei.value.status
+
+    assert status(lambda: sp.g.decode_layer(1, tok1, p1.params)) == b.ERR_STATE        # layer 0 first
+    assert status(lambda: p0.st.decode(tok0, p0.params)) == b.ERR_STATE                # member alone
+    assert status(lambda: p0.st.read_book()) == b.ERR_STATE
+    assert status(lambda: p0.st.load_checkpoint(p0.st.read_checkpoint())) == b.ERR_STATE
+    sp.g.decode_layer(0, tok0, p0.params)
+    assert sp.g.next_layer() == 1
+    assert status(lambda: sp.g.spec_layer(1, 1, {k: v[None, 0] for k, v in tok1.items()}, p1.params)) == b.ERR_STATE
+    assert status(lambda: sp.g.flush([p.params for p in pairs])) == b.ERR_STATE     # mid-step
+    assert status(lambda: sp.g.rollback()) == b.ERR_STATE
+    for l in range(1, len(pairs)):
+        sp.g.decode_layer(l, pairs[l].to_dev(synth.token(toks[l], 0)), pairs[l].params)
+    assert sp.g.next_layer() == 0
+    assert status(lambda: sp.g.commit(torch.zeros(B, dtype=torch.int32, device="cuda"))) == b.ERR_STATE
+    drafts = {n: v[1:3] for n, v in toks[0].items()}
+    sp.g.spec_layer(0, 2, p0.to_dev(drafts), p0.params)
+    d1 = p1.to_dev({n: v[1:4] for n, v in toks[1].items()})
+    assert status(lambda: sp.g.spec_layer(1, 3, d1, p1.params)) == b.ERR_STATE        # k = 3 after k = 2
+    assert status(lambda: sp.g.spec_layer(1, 2 * CAP, d1, p1.params)) == b.ERR_STATE
+    # a second stack over a bound layer, and mismatched batches, are refused
+    assert status(lambda: b.ReplayStack([p0.st])) == b.ERR_STATE
+    other = b.ReplayState(b.make_config(b.GDN, B + 1, 2, 2, 32, 32, CAP, b.F32))
+    alone = b.ReplayState(b.make_config(b.GDN, B, 2, 2, 32, 32, CAP, b.F32))
+    assert status(lambda: b.ReplayStack([alone, other])) == b.ERR_SHAPE
+    # after the stack is freed a former member must be loaded before it steps alone
+    sp.g.free()
+    assert status(lambda: p0.st.decode(tok0, p0.params)) == b.ERR_STATE
+    S = torch.from_numpy(synth.checkpoint(5, p0.st.ckpt_shape)).cuda()
+    p0.st.load_checkpoint(S)
+    p0.st.decode(tok0, p0.params)
+    L, P, F, E = p0.st.read_book()
+    torch.cuda.synchronize()
+    assert L.cpu().tolist() == [1] * B and int(E.cpu()[0]) == 0
