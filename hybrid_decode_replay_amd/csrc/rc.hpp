@@ -26,36 +26,26 @@
 namespace rs {
 
 // ---- FP8 E4M3 ------------------------------------------------------------
-__device__ __forceinline__ uint32_t f32_to_e4m3(float x)
+// gfx950's v_cvt_pk_fp8_f32 rounds to the nearest OCP E4M3 value (ties to
+// even, subnormals included) but does not saturate here, so magnitudes of 448
+// and above (infinities too) are clamped to 448 first.  It writes NaN as 0xff;
+// the byte fix-up below makes every NaN the code 0x7f.
+__device__ __forceinline__ float e4m3_sat(float x)
 {
-    const uint32_t u = __builtin_bit_cast(uint32_t, x);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t au = u & 0x7fffffffu;
-    if (au > 0x7f800000u) return 0x7fu;                         // NaN
-    const float a = __builtin_bit_cast(float, au);
-    if (a >= 448.f) return sign | 0x7eu;                         // saturate (incl. inf)
-    if (a < 0.015625f) {                                         // below 2^-6: steps of 2^-9
-        return sign | (uint32_t)__builtin_rintf(a * 512.f);      // 8 lands on code 0x08 = 2^-6
-    }
-    int e = (int)(au >> 23) - 127;                               // -6 .. 8
-    uint32_t m = (au >> 20) & 7u;
-    const uint32_t rem = au & 0xfffffu;
-    if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) ++m;   // round to nearest even
-    if (m == 8u) { m = 0; ++e; }
-    return sign | ((uint32_t)(e + 7) << 3) | m;
+    return __builtin_fabsf(x) >= 448.f ? __builtin_copysignf(448.f, x) : x;
+}
+
+__device__ __forceinline__ uint32_t pack_e4m3(f32x4 v)
+{
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_sat(v.x), e4m3_sat(v.y), 0, false);      // bytes 0, 1
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_sat(v.z), e4m3_sat(v.w), w, true);           // bytes 2, 3
+    // bytes whose low seven bits are all ones are NaN: clear their sign bit (no carry
+    // crosses a byte: each masked byte is at most 0x7f before the +1)
+    const uint32_t t = (uint32_t)w & 0x7f7f7f7fu;
+    return (uint32_t)w & ~((t + 0x01010101u) & 0x80808080u);
 }
 
 // ---- FP4 E2M1 and the E8M0 shared exponent --------------------------------
-// Code of v / 2^X (the caller passes the scaled value).
-__device__ __forceinline__ uint32_t f32_to_e2m1(float v)
-{
-    const uint32_t sign = (__builtin_bit_cast(uint32_t, v) >> 28) & 8u;
-    const float a = __builtin_fabsf(v);
-    // nearest of {0, .5, 1, 1.5, 2, 3, 4, 6}; ties go to the even code
-    const uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.f);
-    return sign | c;
-}
-
 // Shared exponent X of a group with largest magnitude amax.
 __device__ __forceinline__ int mx_exponent(float amax)
 {
@@ -65,14 +55,24 @@ __device__ __forceinline__ int mx_exponent(float amax)
     return X < -127 ? -127 : (X > 127 ? 127 : X);
 }
 
-__device__ __forceinline__ float exp2i(int e)                   // 2^e for e in [-126, 127] (normal floats)
-{
-    return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
-}
-
 __device__ __forceinline__ float e8m0_to_f32(uint32_t code)
 {
     return code == 0 ? __builtin_bit_cast(float, 0x00400000u) : __builtin_bit_cast(float, code << 23);
+}
+
+// Eight E2M1 codes of v[k] / 2^X, v[0] in the low nibble.  gfx950's scaled
+// conversion divides by the scale it is given, rounds to the nearest E2M1
+// value with ties to even and saturates at 6; the scale is passed as the
+// group's E8M0 value 2^X (2^-127 as the subnormal float for X = -127).
+__device__ __forceinline__ uint32_t pack_e2m1(const float (&v)[8], int X)
+{
+    const float scale = e8m0_to_f32((uint32_t)(X + 127));
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], scale, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], scale, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], scale, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], scale, 3);
+    return w;
 }
 
 // ---- tile addressing --------------------------------------------------------
@@ -121,11 +121,6 @@ __device__ __forceinline__ void rc_fp8_decode(const uint32_t (&w)[NB], f32x4 (&s
         const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[nb], true);
         s[nb] = f32x4{lo[0], lo[1], hi[0], hi[1]};
     }
-}
-
-__device__ __forceinline__ uint32_t pack_e4m3(f32x4 v)
-{
-    return f32_to_e4m3(v.x) | (f32_to_e4m3(v.y) << 8) | (f32_to_e4m3(v.z) << 16) | (f32_to_e4m3(v.w) << 24);
 }
 
 template <int NB>
@@ -201,12 +196,8 @@ __device__ __forceinline__ void rc_fp4_store(uint8_t* codes, uint8_t* scales, si
         am = fmaxf(am, __shfl_xor(am, 16, 64));      // the group spans lanes l%16 + 16*q
         am = fmaxf(am, __shfl_xor(am, 32, 64));
         const int X = mx_exponent(am);
-        const float inv = exp2i(-X);                 // X <= 125 for finite amax, so -X >= -125
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        uint32_t word = 0;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) word |= f32_to_e2m1(v[k] * inv) << (4 * k);
-        w[p] = word;
+        w[p] = pack_e2m1(v, X);
         scw[p] = (uint32_t)(X + 127);
     }
     if constexpr (BPL >= 16) {
@@ -253,11 +244,8 @@ __device__ __forceinline__ void rc_fp4_roundtrip(f32x4 (&s)[NB])
         am = fmaxf(am, __shfl_xor(am, 16, 64));
         am = fmaxf(am, __shfl_xor(am, 32, 64));
         const int X = mx_exponent(am);
-        const float inv = exp2i(-X);
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        uint32_t word = 0;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) word |= f32_to_e2m1(v[k] * inv) << (4 * k);
+        const uint32_t word = pack_e2m1(v, X);
         const float scale = e8m0_to_f32((uint32_t)(X + 127));
         const auto b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, scale, 0);
         const auto b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, scale, 1);

@@ -82,6 +82,97 @@ def test_quantizer_bit_exact_at_load(fmt, kind, C, R):
         np.testing.assert_array_equal(scales.cpu().numpy(), ws)
 
 
+def e4m3_sweep(seed):
+    """Every finite E4M3 magnitude, every midpoint between neighbouring magnitudes (the
+    ties), one fp32 ulp either side of each midpoint, values at and past the saturation
+    threshold (448, the 464 midpoint, infinity), values below half the smallest
+    subnormal, both signs, a positive NaN, and log-uniform values from 2^-12 to 2^10.
+    Magnitudes come from the format's definition: 2^(e-7)(1 + m/8), subnormals 2^-6 m/8."""
+    mags = [2.0 ** -6 * m / 8 for m in range(8)] + [2.0 ** (e - 7) * (1 + m / 8) for e in range(1, 16)
+                                                    for m in range(8) if (e, m) != (15, 7)]
+    mags = np.array(mags, np.float64)
+    mids = ((mags[:-1] + mags[1:]) / 2).astype(np.float32)       # exact in fp32
+    up, dn = np.nextafter(mids, np.float32(np.inf)), np.nextafter(mids, np.float32(0))
+    extra = np.array([449.0, 463.99997, 464.0, 464.00003, 1e6, 3e38, np.inf, 2.0 ** -11, 1e-30, 1e-40],
+                     np.float32)
+    pos = np.concatenate([mags.astype(np.float32), mids, up, dn, extra])
+    rng = np.random.default_rng(seed)
+    rnd = (np.exp2(rng.uniform(-12, 10, 4000)) * rng.choice([-1.0, 1.0], 4000)).astype(np.float32)
+    return np.concatenate([pos, -pos, rnd, np.array([np.nan], np.float32)])
+
+
+@pytest.mark.parametrize("kind,C,R", [("mamba2", 64, 128), ("gdn", 128, 128)])
+def test_fp8_encoder_every_code_and_midpoint(kind, C, R):
+    """The kernels' E4M3 encoder against the oracle's nearest-value search on the sweep
+    above, placed at the head of an N(0, 0.1) checkpoint (codes compared bit for bit)."""
+    from oracle import replay_oracle as ro
+    b = rb()
+    B, H = 2, 2
+    cfg = b.make_config(b.MAMBA2 if kind == "mamba2" else b.GDN, B, H, H, C, R, 16, b.F32, read_copy=b.FP8_E4M3)
+    st = b.ReplayState(cfg)
+    S0 = synth.checkpoint(70 + C, (B, H, C, R)).astype(np.float32)
+    sweep = e4m3_sweep(71)
+    assert sweep.size <= S0.size
+    S0.reshape(-1)[:sweep.size] = sweep
+    st.load_checkpoint(torch.from_numpy(S0).cuda())
+    codes, _ = st.read_copy()
+    torch.cuda.synchronize()
+    codes = codes.cpu().numpy().reshape(-1)
+    want = ro.e4m3_encode(S0.astype(np.float64)).reshape(-1)
+    bad = np.nonzero(codes != want)[0]
+    assert bad.size == 0, [(float(S0.reshape(-1)[i]), int(codes[i]), int(want[i])) for i in bad[:10]]
+
+
+def mxfp4_sweep_groups(seed):
+    """32-element groups whose largest magnitude is 7.9 * 2^X (shared exponent X), the
+    other elements walking -7 .. 7 times 2^X in steps of 1/8 (every E2M1 value, every tie
+    between neighbours, values past saturation), each group also with every element one
+    fp32 ulp up and one down; X from -126 to 100; a group with a subnormal maximum, an
+    all-zero group and scaled N(0, 1) groups."""
+    rng = np.random.default_rng(seed)
+    grid = np.arange(-56, 57) / 8.0
+    groups = []
+    for X in (-126, -20, -3, 0, 2, 7, 100):
+        for st in range(0, grid.size, 31):
+            g = np.zeros(32)
+            chunk = grid[st:st + 31]
+            g[:chunk.size] = chunk
+            g[31] = 7.9
+            g = (g * 2.0 ** X).astype(np.float32)
+            for d in (None, np.inf, -np.inf):
+                h = g.copy() if d is None else np.nextafter(g, np.float32(d))
+                h[31] = g[31]
+                groups.append(h)
+    groups.append((np.arange(32) * 2.0 ** -140).astype(np.float32))      # subnormal maximum
+    groups.append(np.zeros(32, np.float32))
+    for _ in range(64):
+        groups.append((rng.standard_normal(32) * np.exp2(rng.uniform(-10, 10))).astype(np.float32))
+    return np.stack(groups)
+
+
+@pytest.mark.parametrize("kind,C,R", [("mamba2", 64, 128), ("gdn", 128, 128)])
+def test_mxfp4_encoder_every_tie(kind, C, R):
+    """The kernels' MXFP4 encoder (shared exponent and element codes) against the
+    oracle's on the groups above, placed along the reduction axis of an N(0, 0.1)
+    checkpoint (codes and scales compared bit for bit)."""
+    from oracle import replay_oracle as ro
+    b = rb()
+    B, H = 2, 2
+    cfg = b.make_config(b.MAMBA2 if kind == "mamba2" else b.GDN, B, H, H, C, R, 16, b.F32, read_copy=b.MXFP4)
+    st = b.ReplayState(cfg)
+    S0 = synth.checkpoint(80 + C, (B, H, C, R)).astype(np.float32)
+    groups = mxfp4_sweep_groups(81)
+    flat = S0.reshape(-1, 32)                    # groups of 32 along the last axis
+    assert groups.shape[0] <= flat.shape[0]
+    flat[:groups.shape[0]] = groups
+    st.load_checkpoint(torch.from_numpy(S0).cuda())
+    codes, scales = st.read_copy()
+    torch.cuda.synchronize()
+    wc, ws = ro.mxfp4_quantize(S0.astype(np.float64))
+    np.testing.assert_array_equal(scales.cpu().numpy(), ws)
+    np.testing.assert_array_equal(codes.cpu().numpy(), wc)
+
+
 def _pair(kind, fmt, B, H, C, R, cap, seed, io=None):
     from harness import Pair
     b = rb()
