@@ -36,6 +36,9 @@ The JSON line also carries:
                 at the shapes above, batch 256) through one layer stack, with
                 lockstep and staggered flush phases, against the conventional
                 kernel per layer
+  flush_mfma    (in each layer report) the fold's MFMA flops per flush step and
+                their rate over the measured flush-step time, against the
+                fp32 MFMA peak (157.3 TFLOP/s)
   cpu_baseline  the fp64 oracle on the host cores over a bounded sample
 With --sweep FILE, both layers are also timed at batch 1..512 (replay and
 conventional, eagerly and as HIP-graph replays), one JSON line per point in FILE.
@@ -356,6 +359,20 @@ def time_graph(L, conventional, n=64, reps=8):
     return ms
 
 
+MFMA_F32_PEAK_TFLOPS = 157.3
+
+
+def fold_flops(kind, H, G, C, R, cap=16):
+    """MFMA flops of one full fold (cap entries) per sequence, as the kernels issue them.
+
+    Mamba-2: S^T[N x P] += B^T [N x cap] . (decayed dt x)[cap x P] per head: 2 cap C R.
+    GDN (WY form): W = K S0^T (2 cap R C), Gram K K^T (2 cap cap R), U = T . rhs
+    (2 cap cap C) and S'^T += K^T U (2 R cap C) per head."""
+    if kind == "mamba2":
+        return H * 2 * cap * C * R
+    return H * (2 * cap * R * C + 2 * cap * cap * R + 2 * cap * cap * C + 2 * R * cap * C)
+
+
 def decode_report(L, r, conv_ms):
     replay_b, conv_b = algorithmic_bytes(L.kind, L.H, L.G, L.C, L.R, L.cap, read_copy=L.read_copy,
                                          ckpt_bytes={"f16": 2, "fp8": 1}.get(L.ckpt, 4))
@@ -366,6 +383,10 @@ def decode_report(L, r, conv_ms):
            "flush_step_ms": round(r["flush_ms"], 5), "nonflush_step_ms": round(r["nonflush_ms"], 5),
            "achieved_gbs": round(ach, 1), "frac_of_peak": round(ach / HBM_PEAK_GBS, 4),
            "bytes_per_token_algorithmic": int(replay_b)}
+    ff = fold_flops(L.kind, L.H, L.G, L.C, L.R, L.cap) * L.B
+    tf = ff / (r["flush_ms"] / 1e3) / 1e12
+    out["flush_mfma"] = {"flops_per_flush_step": ff, "tflops": round(tf, 2),
+                         "frac_of_fp32_mfma_peak": round(tf / MFMA_F32_PEAK_TFLOPS, 4)}
     if conv_ms is not None:
         out["conventional"] = {"tokens_per_s": round(L.B / (conv_ms / 1e3), 1), "ms_per_step": round(conv_ms, 5),
                                "achieved_gbs": round(conv_b * L.B / (conv_ms / 1e3) / 1e9, 1),

@@ -9,6 +9,9 @@ e.g. "mamba2_step_kernel<8, 1, 1, true, 0, 0>") or a bare name (all instantiatio
 
 trace    per (kernel, grid size) call counts and durations from *_kernel_trace.csv of a
          `rocprofv3 --kernel-trace` run (one row per workload of the program).
+mfma     flush-step MFMA use (MfmaUtil, MfmaFlopsF32) per (kernel, grid) from a
+         `--pmc MfmaUtil MfmaFlopsF32 GRBM_GUI_ACTIVE` run:
+             python -m hybrid_decode_replay_amd.profsum mfma PMC_DIR OUT.md "COMMAND"
 traffic  HBM bytes per launch of KERNEL dispatches with grid size GRID (threads), from
          *_counter_collection.csv of a `--pmc FETCH_SIZE` and a `--pmc WRITE_SIZE` run.
          Both counters are calibrated on the streaming-copy kernel of the same runs,
@@ -126,11 +129,58 @@ def traffic(fetch_dir, write_dir, out, kernel, grid, fetch_cmd, write_cmd):
     print(out, "traffic per launch", sum(per) / n)
 
 
+def mfma(pmc_dir, out, command):
+    """Flush-step MFMA use per (kernel, grid) from a `--pmc MfmaUtil MfmaFlopsF32
+    GRBM_GUI_ACTIVE` run.  A replay step issues MFMA only when it folds, so the
+    dispatches with MfmaFlopsF32 > 0 are the flush steps.  MfmaUtil is rocprofv3's own
+    derived counter: MFMA busy cycles summed over SIMDs / (GUI-active cycles x SIMDs)."""
+    per = {}
+    for r in csv.DictReader(open(_one(os.path.join(pmc_dir, "**", "*counter_collection.csv")))):
+        d = per.setdefault(int(r["Dispatch_Id"]), {"name": short(r["Kernel_Name"]), "grid": int(r["Grid_Size"]),
+                                                  "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    groups = {}
+    for d in per.values():
+        if d.get("MfmaFlopsF32", 0.0) > 0 and d["name"].startswith(("mamba2", "gdn")):
+            groups.setdefault((d["name"], d["grid"]), []).append(d)
+    # full folds (every sequence of the batch folds: the most flops seen for the kernel and
+    # grid) apart from partial ones (staggered flush phases, forced flushes of some sequences)
+    split = {}
+    for (name, grid), ds in groups.items():
+        top = max(d["MfmaFlopsF32"] for d in ds)
+        full = [d for d in ds if d["MfmaFlopsF32"] >= 0.999 * top]
+        part = [d for d in ds if d["MfmaFlopsF32"] < 0.999 * top]
+        split[(name, grid, "full")] = full
+        if part:
+            split[(name, grid, "partial")] = part
+    lines = [f"# MFMA use on fold (flush) dispatches: {os.path.basename(out)[:-3]}", "",
+             "Command (from the repository root; run under `cd /tmp && export TMPDIR=/tmp`):", "",
+             f"    {command}", "",
+             "Dispatches with MfmaFlopsF32 > 0 (replay steps issue MFMA only when they fold).",
+             "MfmaUtil: rocprofv3's derived counter, MFMA busy cycles summed over SIMDs / (GUI-active cycles x SIMDs).",
+             "TFLOP/s: MfmaFlopsF32 / the profiled dispatch duration (counter runs serialise dispatches).", "",
+             "Full: every sequence folds (the largest MfmaFlopsF32 of the kernel and grid); partial: some do.", "",
+             "| kernel | grid (threads) | folds | dispatches | MfmaFlopsF32 per dispatch | MfmaUtil % | profiled us "
+             "| TFLOP/s |",
+             "|---|---|---|---|---|---|---|---|"]
+    for (name, grid, kind), ds in sorted(split.items(), key=lambda kv: (kv[0][2], -kv[0][1], kv[0][0])):
+        n = len(ds)
+        fl = sum(d["MfmaFlopsF32"] for d in ds) / n
+        ut = sum(d.get("MfmaUtil", 0.0) for d in ds) / n
+        us = sum(d["ns"] for d in ds) / n / 1e3
+        lines.append(f"| `{name}` | {grid} | {kind} | {n} | {fl:.4g} | {ut:.2f} | {us:.1f} | {fl / us / 1e6:.2f} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out, len(split), "rows")
+
+
 if __name__ == "__main__":
     mode, args = sys.argv[1], sys.argv[2:]
     if mode == "trace":
         trace(*args)
     elif mode == "traffic":
         traffic(*args)
+    elif mode == "mfma":
+        mfma(*args)
     else:
         raise SystemExit(__doc__)
