@@ -166,6 +166,17 @@ __device__ __forceinline__ TileIdx tile_of(int item, int H, int nsplit) {
     return t;
 }
 
+// An offset every lane of the wave holds the same value of, moved to scalar
+// registers: a load or store at base + this offset + a per-lane offset then
+// takes the scalar-base form (one VGPR for the lane's 32-bit offset) instead
+// of a 64-bit VGPR address per access.
+__device__ __forceinline__ size_t wave_uniform(size_t x)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+    return ((size_t)hi << 32) | lo;
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }

@@ -41,7 +41,7 @@
 namespace rs {
 
 template <int NB, int IO, int TMAX, bool MFMA_FOLD, int RC, int CK>
-__global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
+__global__ __launch_bounds__(256, NB <= 8 ? 6 : 4) void mamba2_step_kernel(StepArgs a)
 {
     extern __shared__ float lds[];
     constexpr int R = NB * 16;
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(1024) void mamba2_step_kernel(StepArgs a)
     const int g = h / a.hpg;
     const int cw = C / a.nsplit, c0 = tix.sp * cw;   // this workgroup's output columns
     const int tid = threadIdx.x, nthr = blockDim.x;
-    const int w = tid >> 6, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lc = 16 * w + (lane & 15);             // local output column
     const int col = c0 + lc;                          // global output column
     const int rq = 4 * (lane >> 4);
