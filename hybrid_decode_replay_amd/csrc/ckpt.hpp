@@ -35,16 +35,6 @@ __device__ __forceinline__ u32x2 f32_to_h4(f32x4 v) {
 // registers themselves (fp16: the word of blocks 2q and 2q+1 in s[2q]) and
 // are decoded in place, so a step that may take either of two sources (the
 // checkpoint or its read copy) holds one set of registers.
-// Lane `lane`'s 16 bytes of 1 KiB block `blk` of a strip whose first block
-// starts at element `first` of `ck` (elements of type T, E per block).  Each run
-// of four blocks gets its own wave-uniform base, so every access is a scalar
-// base + the lane's 32-bit offset + an immediate below 4 KiB.
-template <int E, class T>
-__device__ __forceinline__ T* strip_block(T* ck, size_t first, int blk, int lane)
-{
-    return ck + wave_uniform(first + (size_t)(blk >> 2) * 4 * E) + (blk & 3) * E + lane * (E / 64);
-}
-
 template <int NB, int CK>
 __device__ __forceinline__ void ckpt_issue(const void* ck, size_t strip, int lane, f32x4 (&s)[NB])
 {
@@ -125,17 +115,19 @@ __device__ __forceinline__ void ckpt_store(void* ck, size_t strip, int lane, con
         rc_fp8_store<NB>(static_cast<uint8_t*>(ck), strip, lane, s);
     } else if constexpr (CK == CK_F32) {
         float* p = static_cast<float*>(ck);
+        const int ln = lane_id();
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) st4_stream(strip_block<256>(p, strip * NB * 256, nb, lane), s[nb]);
+        for (int nb = 0; nb < NB; ++nb) st4_stream(strip_block<256>(p, strip * NB * 256, nb, ln), s[nb]);
     } else if constexpr (NB == 1) {
         u32x2* p = static_cast<u32x2*>(ck) + strip * 64 + lane;
         __builtin_nontemporal_store(f32_to_h4(s[0]), p);
     } else {
         u32x4* p = static_cast<u32x4*>(ck);
+        const int ln = lane_id();
 #pragma unroll
         for (int q = 0; q < NB / 2; ++q) {
             const u32x2 lo = f32_to_h4(s[2 * q]), hi = f32_to_h4(s[2 * q + 1]);
-            __builtin_nontemporal_store(u32x4{lo.x, lo.y, hi.x, hi.y}, strip_block<64>(p, strip * (NB / 2) * 64, q, lane));
+            __builtin_nontemporal_store(u32x4{lo.x, lo.y, hi.x, hi.y}, strip_block<64>(p, strip * (NB / 2) * 64, q, ln));
         }
     }
 }

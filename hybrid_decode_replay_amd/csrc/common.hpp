@@ -170,11 +170,28 @@ __device__ __forceinline__ TileIdx tile_of(int item, int H, int nsplit) {
 // registers: a load or store at base + this offset + a per-lane offset then
 // takes the scalar-base form (one VGPR for the lane's 32-bit offset) instead
 // of a 64-bit VGPR address per access.
+// This lane's index in its wave, computed afresh: a value the compiler cannot
+// merge with an earlier threadIdx-based copy, so that copy need not stay live.
+__device__ __forceinline__ int lane_id()
+{
+    return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
 __device__ __forceinline__ size_t wave_uniform(size_t x)
 {
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
     return ((size_t)hi << 32) | lo;
+}
+
+// Lane `lane`'s 16 bytes of 1 KiB block `blk` of a strip whose first block
+// starts at element `first` of `ck` (elements of type T, E per block).  Each run
+// of four blocks gets its own wave-uniform base, so every access is a scalar
+// base + the lane's 32-bit offset + an immediate below 4 KiB.
+template <int E, class T>
+__device__ __forceinline__ T* strip_block(T* ck, size_t first, int blk, int lane)
+{
+    return ck + wave_uniform(first + (size_t)(blk >> 2) * 4 * E) + (blk & 3) * E + lane * (E / 64);
 }
 
 __device__ __forceinline__ f32x4 mfma16x16x4(float a, float b, f32x4 c) {

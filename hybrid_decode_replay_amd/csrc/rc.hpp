@@ -102,7 +102,7 @@ __device__ __forceinline__ void rc_fp8_issue(const uint8_t* base, size_t strip_i
     if constexpr (BPL >= 16) {
 #pragma unroll
         for (int q = 0; q < NB / 4; ++q) {
-            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + rc_offset<BPL>(strip_index, q, lane)));
+            const u32x4 v = __builtin_nontemporal_load(strip_block<64>(reinterpret_cast<const u32x4*>(base), strip_index * 4 * BPL, q, lane));
             w[q * 4] = v.x; w[q * 4 + 1] = v.y; w[q * 4 + 2] = v.z; w[q * 4 + 3] = v.w;
         }
     } else {
@@ -131,7 +131,7 @@ __device__ __forceinline__ void rc_fp8_store(uint8_t* base, size_t strip_index, 
 #pragma unroll
         for (int q = 0; q < NB / 4; ++q) {
             const u32x4 v = {pack_e4m3(s[q * 4]), pack_e4m3(s[q * 4 + 1]), pack_e4m3(s[q * 4 + 2]), pack_e4m3(s[q * 4 + 3])};
-            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(base + rc_offset<BPL>(strip_index, q, lane)));
+            __builtin_nontemporal_store(v, strip_block<64>(reinterpret_cast<u32x4*>(base), strip_index * 4 * BPL, q, lane_id()));
         }
     } else {
 #pragma unroll
@@ -151,7 +151,7 @@ __device__ __forceinline__ void rc_fp4_issue(const uint8_t* codes, const uint8_t
     if constexpr (BPL >= 16) {
 #pragma unroll
         for (int q = 0; q < NB / 8; ++q) {
-            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes + rc_offset<BPL>(strip_index, q, lane)));
+            const u32x4 v = __builtin_nontemporal_load(strip_block<64>(reinterpret_cast<const u32x4*>(codes), strip_index * 4 * BPL, q, lane));
             w[q * 4] = v.x; w[q * 4 + 1] = v.y; w[q * 4 + 2] = v.z; w[q * 4 + 3] = v.w;
         }
     } else {
@@ -204,7 +204,7 @@ __device__ __forceinline__ void rc_fp4_store(uint8_t* codes, uint8_t* scales, si
 #pragma unroll
         for (int q = 0; q < NB / 8; ++q) {
             const u32x4 v = {w[q * 4], w[q * 4 + 1], w[q * 4 + 2], w[q * 4 + 3]};
-            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(codes + rc_offset<BPL>(strip_index, q, lane)));
+            __builtin_nontemporal_store(v, strip_block<64>(reinterpret_cast<u32x4*>(codes), strip_index * 4 * BPL, q, lane_id()));
         }
     } else {
 #pragma unroll
