@@ -128,20 +128,31 @@ __device__ __forceinline__ void stage_issue(const Stager<IO, R>& st, int tid, in
         const int ch = tid + u * nthr;
         if (ch < st.nch) pre[u] = *st.src(ch);
     }
+    // Entry scalars: lanes below len read the buffer, the rest the current inputs
+    // (present whenever tokens are appended; with none, V == len).  One load per
+    // lane through a selected address: a branch per source would leave a register
+    // written on one path and loaded on the other, and the wait that orders the two
+    // would hold back the checkpoint loads behind every chunk issued above.
     if (tid < G.V) {
-        if (tid < G.len) {
-            sr.s0 = reinterpret_cast<const uint32_t*>(G.bufs0)[(size_t)G.bank * G.bank_s + G.hc * G.cap + tid];
-            if (G.bufs1)
-                sr.s1 = reinterpret_cast<const uint32_t*>(G.bufs1)[(size_t)G.bank * G.bank_s + G.hc * G.cap + tid];
+        const bool buffered = tid < G.len;
+        const size_t eb = (size_t)G.bank * G.bank_s + G.hc * G.cap + tid;
+        const size_t ei = ((size_t)max(tid - G.len, 0) * G.B + G.b) * G.H + G.h;
+        if constexpr (S0_IS_IO && IO == IO_BF16) {
+            // with bf16 io every buffered value is a bf16 widened to fp32 (low half
+            // zero), so its upper half is the bf16 code itself
+            const uint16_t* p = buffered ? reinterpret_cast<const uint16_t*>(G.bufs0) + 2 * eb + 1
+                                         : static_cast<const uint16_t*>(G.in_s0) + ei;
+            sr.s0 = *p;
+            sr.s0shift = 16;
         } else {
-            const size_t e = ((size_t)(tid - G.len) * G.B + G.b) * G.H + G.h;
-            if constexpr (S0_IS_IO && IO == IO_BF16) {
-                sr.s0 = static_cast<const uint16_t*>(G.in_s0)[e];
-                sr.s0shift = 16;
-            } else {
-                sr.s0 = static_cast<const uint32_t*>(G.in_s0)[e];
-            }
-            if (G.in_s1) sr.s1 = reinterpret_cast<const uint32_t*>(G.in_s1)[e];
+            const uint32_t* p = buffered ? reinterpret_cast<const uint32_t*>(G.bufs0) + eb
+                                         : static_cast<const uint32_t*>(G.in_s0) + ei;
+            sr.s0 = *p;
+        }
+        if (G.bufs1) {
+            const uint32_t* p = buffered ? reinterpret_cast<const uint32_t*>(G.bufs1) + eb
+                                         : reinterpret_cast<const uint32_t*>(G.in_s1) + ei;
+            sr.s1 = *p;
         }
     }
 }
