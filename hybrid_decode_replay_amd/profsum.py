@@ -12,6 +12,8 @@ trace    per (kernel, grid size) call counts and durations from *_kernel_trace.c
 mfma     flush-step MFMA use (MfmaUtil, MfmaFlopsF32) per (kernel, grid) from a
          `--pmc MfmaUtil MfmaFlopsF32 GRBM_GUI_ACTIVE` run:
              python -m hybrid_decode_replay_amd.profsum mfma PMC_DIR OUT.md "COMMAND"
+sweep    the batch 1..512 table from `bench.py --sweep FILE`:
+             python -m hybrid_decode_replay_amd.profsum sweep FILE OUT.md "COMMAND"
 traffic  HBM bytes per launch of KERNEL dispatches with grid size GRID (threads), from
          *_counter_collection.csv of a `--pmc FETCH_SIZE` and a `--pmc WRITE_SIZE` run.
          Both counters are calibrated on the streaming-copy kernel of the same runs,
@@ -174,6 +176,33 @@ def mfma(pmc_dir, out, command):
     print(out, len(split), "rows")
 
 
+def sweep(jsonl, out, command):
+    """Batch-sweep table from the JSON lines `bench.py --sweep FILE` writes (one per layer
+    and batch size)."""
+    import json
+    rows = [json.loads(line) for line in open(jsonl) if line.strip()]
+    lines = ["# Batch sweep: replay vs conventional fused decode, per decode step (MI355X, one GPU)", "",
+             f"Command: `{command}`",
+             "(per point: 64 timed steps after 16 warm-up steps; bf16 io, fp32 checkpoint, 16-entry buffer;",
+             "Mamba-2 H=128 P=64 N=128 G=8; GDN 32 heads d=128).", "",
+             "Two timings per point:", "",
+             "* **graph** -- 64 back-to-back steps captured in one HIP graph, replayed 8 times (GPU time per step,",
+             "  no host launch overhead); the same for the conventional kernel.",
+             "* **eager** -- 64 steps launched one by one from Python, back to back between two events (both",
+             "  kernels); the non-flush and flush columns come from a second pass with an event pair per launch.", "",
+             "| layer | batch | graph replay ms | graph conv ms | graph speedup | eager replay ms | eager conv ms "
+             "| replay non-flush ms | replay flush ms | replay GB/s (algorithmic, per launch) |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        g = r["graph"]
+        lines.append(f"| {r['kind']} | {r['batch']} | {g['replay_ms_per_step']:.4f} | {g['conventional_ms_per_step']:.4f} "
+                     f"| {g['speedup_vs_conventional']:.3f} | {r['ms_per_step']:.4f} | {r['conventional']['ms_per_step']:.4f} "
+                     f"| {r['nonflush_step_ms']:.4f} | {r['flush_step_ms']:.4f} | {r['achieved_gbs']:.0f} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out, len(rows), "points")
+
+
 if __name__ == "__main__":
     mode, args = sys.argv[1], sys.argv[2:]
     if mode == "trace":
@@ -182,5 +211,7 @@ if __name__ == "__main__":
         traffic(*args)
     elif mode == "mfma":
         mfma(*args)
+    elif mode == "sweep":
+        sweep(*args)
     else:
         raise SystemExit(__doc__)
