@@ -84,13 +84,18 @@ struct StateWord {
 };
 
 constexpr int CONV_THREADS = 256;
-constexpr int CONV_UNR = 8;
+// Row passes a thread holds at once: every storage width keeps 32 fp32 state
+// values per thread in registers (fp32: 8 words of 4, fp16: 4 of 8, FP8: 2 of
+// 16), which leaves room for seven waves per SIMD.
+template <int CK>
+constexpr int conv_unroll() { return CK == CK_FP8 ? 2 : (CK == CK_F16 ? 4 : 8); }
 
 template <int R, int IO, int KIND, bool SPEC, int CK>
 __global__ __launch_bounds__(CONV_THREADS) void conv_step_kernel(ConvArgs a)
 {
     using SW = StateWord<CK>;
     constexpr int VW = SW::VW;
+    constexpr int CONV_UNR = conv_unroll<CK>();
     constexpr int EPT = 4 * VW;              // state values per thread and row
     constexpr int NL = R / EPT;              // lanes per row (adjacent)
     constexpr int RP = CONV_THREADS / NL;    // rows per pass
