@@ -148,14 +148,15 @@ def test_fp16_flags_rejected():
 
 
 @pytest.mark.parametrize("kind", ["mamba2", "gdn"])
-def test_conventional_fp16_state(kind):
+@pytest.mark.parametrize("C,R", [(32, 64), (160, 64), (160, 128)])   # 1 row pass; 3-5 with a ragged last
+def test_conventional_fp16_state(kind, C, R):
     """Conventional decoding on an fp16 state vs the oracle's per-token step on an fp64 state
     that is rounded to binary16 after every token (outputs from the unrounded update on both
     sides; the state rounded after every token on both sides)."""
     from harness import TOL_F16
     from oracle import replay_oracle as ro
     b = rb()
-    B, H, C, R, T = 3, 2, 32, 64, 6
+    B, H, T = 3, 2, 6
     cfg = b.make_config(_kind(kind), B, H, H, C, R, 16, b.F32, ckpt_dtype=b.F16)
     S0 = synth.checkpoint(41, (B, H, C, R)).astype(np.float16)
     S = torch.from_numpy(S0).cuda()

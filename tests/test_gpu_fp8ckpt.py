@@ -195,16 +195,21 @@ def test_fp8_flags_rejected():
 
 
 @pytest.mark.parametrize("kind", ["mamba2", "gdn"])
-def test_conventional_fp8_state(kind):
+@pytest.mark.parametrize("C,R", [(32, 64), (160, 64), (160, 128)])   # 1 row pass; 3-5 with a ragged last
+def test_conventional_fp8_state(kind, C, R):
     """Conventional decoding on an FP8 state vs the oracle's per-token step on an fp64 state
     rounded to E4M3 after every token (outputs from the unrounded update on both sides).
-    The first token starts from identical values: outputs within 1e-4; after it, the states
-    stay within one E4M3 step, rarely apart, and outputs of matrices that never differed
-    stay within 1e-4."""
-    from harness import e4m3_grid_index
+    The first token starts from identical values: outputs within 1e-4.  An element first
+    differs by one E4M3 step (the two updates straddle a rounding midpoint), rarely; a
+    (b, h) matrix that ever differed is marked and carries its own history from then on
+    (a one-step difference decayed into a finer binade spans two steps there; in GDN the
+    row's k.s couples its elements), so it is held to one coarse step normwise
+    (FP8_TOL_MARKED, as for the replay path); outputs of unmarked matrices stay within
+    1e-4."""
+    from harness import FP8_TOL_MARKED, e4m3_grid_index
     from oracle import replay_oracle as ro
     b = rb()
-    B, H, C, R, T = 3, 2, 32, 64, 6
+    B, H, T = 3, 2, 6
     cfg = b.make_config(_kind(kind), B, H, H, C, R, 16, b.F32, ckpt_dtype=b.FP8_E4M3)
     S0 = synth.checkpoint(42, (B, H, C, R), std=0.5)
     Sref = ro.e4m3_decode(ro.e4m3_encode(S0)).reshape(S0.shape)
@@ -229,7 +234,11 @@ def test_conventional_fp8_state(kind):
         assert np.max(err[~marked], initial=0.0) <= 1e-4, (t, err)
         Sg = ro.e4m3_decode(S.view(torch.uint8).cpu().numpy()).reshape(Sref.shape)
         diff = Sg != Sref
-        if diff.any():
-            assert np.all(np.abs(e4m3_grid_index(Sg[diff]) - e4m3_grid_index(Sref[diff])) == 1), t
+        fresh = diff & ~marked[:, :, None, None]
+        if fresh.any():
+            assert np.all(np.abs(e4m3_grid_index(Sg[fresh]) - e4m3_grid_index(Sref[fresh])) == 1), t
+        if marked.any():
+            dm = np.max(np.abs(Sg - Sref), axis=(2, 3)) / np.maximum(np.max(np.abs(Sref), axis=(2, 3)), 1e-30)
+            assert np.max(dm[marked]) <= FP8_TOL_MARKED, (t, np.max(dm[marked]))
         assert diff.mean() <= 1e-3, (t, diff.mean())
         marked |= diff.any(axis=(2, 3))
