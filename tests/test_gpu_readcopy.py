@@ -253,28 +253,38 @@ def test_spec_with_read_copy(fmt, kind):
     pair.spec({n: v[5:11] for n, v in toks.items()}, what="spec with pre-flush for some rows")
 
 
-def test_bf16_io_with_mxfp4_copy_full_size_sample():
-    """The batch-128 GDN layer (32 heads, d = 128) with an MXFP4 copy: first window parity on
-    sampled sequences (copy read path, bf16 inputs and outputs)."""
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_bf16_io_read_copy_full_size_sample(fmt):
+    """The batch-128 GDN layer (32 heads, d = 128, bf16 io) with an FP8 or MXFP4 copy, 48
+    steps (three folds, each re-making the copy from the stored checkpoint): outputs of
+    sampled sequences against the oracle's read-copy semantics (non-flush steps read the
+    dequantized copy, folding steps the fp32 checkpoint), the fp32 checkpoint within 1e-4,
+    bookkeeping bit-exact."""
     from oracle import replay_oracle as ro
     b = rb()
-    B, H, D, T = 128, 32, 128, 15
-    cfg = b.make_config(b.GDN, B, H, H, D, D, 16, b.BF16, read_copy=b.MXFP4)
+    B, H, D, T = 128, 32, 128, 48
+    cfg = b.make_config(b.GDN, B, H, H, D, D, 16, b.BF16, read_copy=rc_code(fmt))
     st = b.ReplayState(cfg)
     S0 = synth.checkpoint_device(4, (B, H, D, D), "cuda")
     st.load_checkpoint(S0)
     toks = synth.gdn_tokens_device(4, T, B, H, H, D, D, "cuda")
     ys = torch.empty((T, B, H, D), dtype=torch.bfloat16, device="cuda")
+    print(f"[full-size gdn {fmt} copy] launching", flush=True)
     for t in range(T):
         st.decode({k: v[t:t + 1] for k, v in toks.items()}, y=ys[t:t + 1])
+    ck = st.read_checkpoint()
+    L, Pd, F, E = st.read_book()
     torch.cuda.synchronize()
-    sample = [0, 77]
-    sess = ro.GDNSession(S0[sample].cpu().numpy(), read_copy="mxfp4")
+    assert torch.all(L == 0) and torch.all(F == 3) and torch.all(Pd == 0) and int(E[0]) == 0
+    sample = [0, 77, 127]
+    sess = ro.GDNSession(S0[sample].cpu().numpy(), read_copy=fmt)
     host = {k: v[:, sample].float().cpu().numpy() for k, v in toks.items()}
     yg = ys[:, sample].float().cpu().numpy()
     for t in range(T):
         err = ro.normwise_error(yg[t], sess.decode(synth.token(host, t)))
         assert err <= 2e-2, (t, err)
+    err_ck = ro.normwise_error(ck[sample].cpu().numpy(), sess.ckpt, axis=(2, 3))
+    assert err_ck <= 1e-4, err_ck
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
