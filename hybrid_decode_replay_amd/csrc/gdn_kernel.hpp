@@ -44,6 +44,16 @@
 
 namespace rs {
 
+// The lane index recomputed where it is used: the asm is opaque, so the compiler
+// can neither merge it with another copy nor keep one copy live across the kernel
+// (a value that cheap is better recomputed than held in a register or spilled).
+__device__ __forceinline__ int lane_id_here()
+{
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 template <int NB, int IO, int TMAX, int RC, int CK>
 __global__ __launch_bounds__(256, NB <= 8 ? 6 : 4) void gdn_step_kernel(StepArgs a)
 {
@@ -177,7 +187,7 @@ __global__ __launch_bounds__(256, NB <= 8 ? 6 : 4) void gdn_step_kernel(StepArgs
         for (int r = 0; r < 4; ++r) {
             const int i = lq * 4 + r;
             float v = 0.f;
-            if (i < f) v = be[i] * (vs[i * cw + lc] - (al[0] * tt[i]) * W[r]);   // P_i = alpha_0 tt[0][i]
+            if (i < f) v = be[i] * (vs[i * cw + 16 * w + (lane_id_here() & 15)] - (al[0] * tt[i]) * W[r]);   // P_i = alpha_0 tt[0][i]
             rhs[r] = v;
         }
         // U = (I + A)^{-1} rhs, then scaled by the decay from entry i to the end of the fold
@@ -233,7 +243,7 @@ __global__ __launch_bounds__(256, NB <= 8 ? 6 : 4) void gdn_step_kernel(StepArgs
 #pragma unroll
                 for (int m = 0; m < EL; ++m) part += kv[m] * r[m];
                 const float bd = be[i] * group_sum<16>(part);
-                rep += (sig * bd) * vs[i * cw + lc];
+                rep += (sig * bd) * vs[i * cw + 16 * w + (lane_id_here() & 15)];
 #pragma unroll
                 for (int m = 0; m < EL; ++m) r[m] -= bd * kv[m];
                 sig *= al[i];
@@ -293,7 +303,7 @@ __global__ __launch_bounds__(256, NB <= 8 ? 6 : 4) void gdn_step_kernel(StepArgs
                     gacc = sum_over_row_groups(gacc);
                     const int pos = len + t;
                     float rep = 0.f;
-                    for (int i = f; i <= pos; ++i) rep += cc[t * vmax + i] * vs[i * cw + lc];
+                    for (int i = f; i <= pos; ++i) rep += cc[t * vmax + i] * vs[i * cw + 16 * w + (lane_id_here() & 15)];
                     if (lane < 16)
                         st_io<IO>(a.y, (((size_t)t * sB + b) * a.H + h) * C + col, a.scale * (gacc + rep));
                 }
