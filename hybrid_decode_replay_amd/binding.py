@@ -16,7 +16,7 @@ LIBPATH = os.path.join(_HERE, "libreplayssm.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "replayssm.h")
 
 if not os.path.exists(LIBPATH):
-    raise ImportError(f"{LIBPATH} is not built; run __graft_entry__.build() (hipcc, gfx950) first")
+    raise ImportError(f"{LIBPATH} is not built; build it first: python -m hybrid_decode_replay_amd.build (hipcc, gfx950)")
 
 _lib = ctypes.CDLL(LIBPATH)
 
