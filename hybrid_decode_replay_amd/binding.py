@@ -63,6 +63,14 @@ _SIGS = {
     "replay_state_layout": ([_vp, _LP], _i32),
     "replay_state_phase": ([_vp], _i32),
     "replay_load_checkpoint": ([_vp, _vp, _vp], _i32),
+    "replay_load_checkpoint_f32": ([_vp, _vp, _vp], _i32),
+    "replay_load_slots": ([_vp, _i32, ctypes.POINTER(_i32), _vp, _vp], _i32),
+    "replay_decode_step_masked": ([_vp, _IP, _vp, _vp, _vp], _i32),
+    "replay_spec_append_masked": ([_vp, _i32, _IP, _vp, _vp, _vp], _i32),
+    "replay_stack_load_f32": ([_vp, ctypes.POINTER(_vp), _vp], _i32),
+    "replay_stack_load_slots": ([_vp, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_vp), _vp], _i32),
+    "replay_stack_decode_layer_masked": ([_vp, _i32, _IP, _vp, _vp, _vp], _i32),
+    "replay_stack_spec_layer_masked": ([_vp, _i32, _i32, _IP, _vp, _vp, _vp], _i32),
     "replay_read_checkpoint": ([_vp, _vp, _vp], _i32),
     "replay_read_copy": ([_vp, _vp, _vp, _vp], _i32),
     "replay_read_book": ([_vp, _vp, _vp, _vp], _i32),
@@ -192,6 +200,34 @@ def make_inputs(cfg: ReplayConfig, tensors: dict, params: dict | None = None) ->
     return ri
 
 
+def _load_call(st, S, what):
+    """Load a whole-state checkpoint: fp32 through the library's own rounding, or already in
+    the checkpoint dtype.  No dtype conversion happens here."""
+    torch = _torch()
+    if tuple(S.shape) != st.ckpt_shape:
+        raise ValueError(f"checkpoint shape {tuple(S.shape)}, expected {st.ckpt_shape}")
+    if S.dtype == torch.float32:
+        _check(_lib.replay_load_checkpoint_f32(st.h, _ptr(S, name="S"), _stream()), what + "_f32")
+    elif S.dtype == st.ckt:
+        _check(_lib.replay_load_checkpoint(st.h, _ptr(S, name="S"), _stream()), what)
+    else:
+        raise TypeError(f"checkpoint dtype {S.dtype}: pass fp32 or {st.ckt}")
+    st._keep = S
+
+
+def _slot_array(slots, B):
+    """Host int32 array of slot indices (the library validates range and distinctness)."""
+    vals = [int(b) for b in slots]
+    return (_i32 * len(vals))(*vals)
+
+
+def _mask_ptr(active, B):
+    torch = _torch()
+    if tuple(active.shape) != (B,):
+        raise ValueError(f"active mask has shape {tuple(active.shape)}, expected ({B},)")
+    return _ptr(active, torch.uint8, "active")
+
+
 class ReplayState:
     """A replayed SSM layer state (checkpoint + input buffer) in caller-owned device memory."""
 
@@ -233,10 +269,20 @@ class ReplayState:
 
     # -- checkpoint I/O
     def load_checkpoint(self, S):
-        """S: logical [B][H][rows][cols]; converted to the checkpoint dtype (torch's RNE cast) if needed."""
-        S = S.to(device=self.device, dtype=self.ckt).contiguous()
-        assert tuple(S.shape) == self.ckpt_shape
-        _check(_lib.replay_load_checkpoint(self.h, _ptr(S), _stream()), "replay_load_checkpoint")
+        """S: logical [B][H][rows][cols] device tensor, either fp32 (the library rounds it to
+        the checkpoint dtype: replay_load_checkpoint_f32) or already in the checkpoint dtype."""
+        _load_call(self, S, "replay_load_checkpoint")
+
+    def load_slots(self, slots, S):
+        """Per-sequence arrival: sequences `slots` (ints) take the fp32 checkpoints S [n][H][rows][cols]
+        (device); every other sequence keeps its state (replay_load_slots)."""
+        torch = _torch()
+        arr = _slot_array(slots, self.cfg.batch)
+        c = self.cfg
+        if tuple(S.shape) != (len(arr), c.nheads, c.head_dim, c.state_dim):
+            raise ValueError(f"S has shape {tuple(S.shape)}, expected {(len(arr), c.nheads, c.head_dim, c.state_dim)}")
+        _check(_lib.replay_load_slots(self.h, len(arr), arr, _ptr(S, torch.float32, "S"), _stream()),
+               "replay_load_slots")
         self._keep = S
 
     def read_checkpoint(self):
@@ -265,28 +311,38 @@ class ReplayState:
         return book[0], book[1], book[2], err
 
     # -- the decode path
-    def decode(self, tokens: dict, params: dict | None = None, y=None):
+    def decode(self, tokens: dict, params: dict | None = None, y=None, active=None):
+        """One decode token; with `active` (device uint8 [B]) only the sequences it marks step
+        (replay_decode_step_masked), and the rows of y of the others are left as they were."""
         torch = _torch()
         c = self.cfg
         if y is None:
-            y = torch.empty((1, c.batch, c.nheads, c.head_dim), dtype=self.iot, device=self.device)
+            y = torch.zeros((1, c.batch, c.nheads, c.head_dim), dtype=self.iot, device=self.device)
         ri = make_inputs(c, tokens, params)
-        _check(_lib.replay_decode_step(self.h, ctypes.byref(ri), _ptr(y, self.iot, "y"), _stream()),
-               "replay_decode_step")
+        if active is None:
+            _check(_lib.replay_decode_step(self.h, ctypes.byref(ri), _ptr(y, self.iot, "y"), _stream()),
+                   "replay_decode_step")
+        else:
+            _check(_lib.replay_decode_step_masked(self.h, ctypes.byref(ri), _mask_ptr(active, c.batch),
+                                                  _ptr(y, self.iot, "y"), _stream()), "replay_decode_step_masked")
         return y
 
     def flush(self, params: dict | None = None):
         ri = make_inputs(self.cfg, {}, params)
         _check(_lib.replay_flush(self.h, ctypes.byref(ri), _stream()), "replay_flush")
 
-    def spec_append(self, k: int, drafts: dict, params: dict | None = None, y=None):
+    def spec_append(self, k: int, drafts: dict, params: dict | None = None, y=None, active=None):
         torch = _torch()
         c = self.cfg
         if y is None:
-            y = torch.empty((k, c.batch, c.nheads, c.head_dim), dtype=self.iot, device=self.device)
+            y = torch.zeros((k, c.batch, c.nheads, c.head_dim), dtype=self.iot, device=self.device)
         ri = make_inputs(c, drafts, params)
-        _check(_lib.replay_spec_append(self.h, int(k), ctypes.byref(ri), _ptr(y, self.iot, "y"), _stream()),
-               "replay_spec_append")
+        if active is None:
+            _check(_lib.replay_spec_append(self.h, int(k), ctypes.byref(ri), _ptr(y, self.iot, "y"), _stream()),
+                   "replay_spec_append")
+        else:
+            _check(_lib.replay_spec_append_masked(self.h, int(k), ctypes.byref(ri), _mask_ptr(active, c.batch),
+                                                  _ptr(y, self.iot, "y"), _stream()), "replay_spec_append_masked")
         return y
 
     def commit(self, accepted):
@@ -327,36 +383,64 @@ class ReplayStack:
         return _lib.replay_stack_phase(self.h)
 
     def load(self, checkpoints):
-        """checkpoints[l]: layer l's logical checkpoint (converted to its checkpoint dtype)."""
-        keep = []
+        """checkpoints[l]: layer l's logical checkpoint, all fp32 (rounded by the library to each
+        layer's checkpoint dtype: replay_stack_load_f32) or all in the layers' checkpoint dtypes."""
+        torch = _torch()
         for st, S in zip(self.layers, checkpoints, strict=True):
-            S = S.to(device=st.device, dtype=st.ckt).contiguous()
-            assert tuple(S.shape) == st.ckpt_shape
-            keep.append(S)
-        arr = (_vp * len(keep))(*[S.data_ptr() for S in keep])
-        _check(_lib.replay_stack_load(self.h, arr, _stream()), "replay_stack_load")
-        self._keep = keep
+            if tuple(S.shape) != st.ckpt_shape:
+                raise ValueError(f"checkpoint shape {tuple(S.shape)}, expected {st.ckpt_shape}")
+        f32 = all(S.dtype == torch.float32 for S in checkpoints)
+        if not f32 and any(S.dtype != st.ckt for st, S in zip(self.layers, checkpoints)):
+            raise TypeError("stack checkpoints must all be fp32 or all in their layers' checkpoint dtypes")
+        arr = (_vp * len(checkpoints))(*[_ptr(S, name="S").value for S in checkpoints])
+        if f32:
+            _check(_lib.replay_stack_load_f32(self.h, arr, _stream()), "replay_stack_load_f32")
+        else:
+            _check(_lib.replay_stack_load(self.h, arr, _stream()), "replay_stack_load")
+        self._keep = list(checkpoints)
 
-    def decode_layer(self, layer: int, tokens: dict, params: dict | None = None, y=None):
+    def load_slots(self, slots, checkpoints):
+        """Per-sequence arrival in every layer: checkpoints[l] is layer l's fp32 [n][H][rows][cols]."""
+        torch = _torch()
+        arr = _slot_array(slots, self.layers[0].cfg.batch)
+        for st, S in zip(self.layers, checkpoints, strict=True):
+            c = st.cfg
+            if tuple(S.shape) != (len(arr), c.nheads, c.head_dim, c.state_dim):
+                raise ValueError("slot checkpoint shape mismatch")
+        ptrs = (_vp * len(checkpoints))(*[_ptr(S, torch.float32, "S").value for S in checkpoints])
+        _check(_lib.replay_stack_load_slots(self.h, len(arr), arr, ptrs, _stream()), "replay_stack_load_slots")
+        self._keep = list(checkpoints)
+
+    def decode_layer(self, layer: int, tokens: dict, params: dict | None = None, y=None, active=None):
         torch = _torch()
         st = self.layers[layer]
         c = st.cfg
         if y is None:
-            y = torch.empty((1, c.batch, c.nheads, c.head_dim), dtype=st.iot, device=st.device)
+            y = torch.zeros((1, c.batch, c.nheads, c.head_dim), dtype=st.iot, device=st.device)
         ri = make_inputs(c, tokens, params)
-        _check(_lib.replay_stack_decode_layer(self.h, int(layer), ctypes.byref(ri), _ptr(y, st.iot, "y"), _stream()),
-               "replay_stack_decode_layer")
+        if active is None:
+            _check(_lib.replay_stack_decode_layer(self.h, int(layer), ctypes.byref(ri), _ptr(y, st.iot, "y"),
+                                                  _stream()), "replay_stack_decode_layer")
+        else:
+            _check(_lib.replay_stack_decode_layer_masked(self.h, int(layer), ctypes.byref(ri),
+                                                         _mask_ptr(active, c.batch), _ptr(y, st.iot, "y"),
+                                                         _stream()), "replay_stack_decode_layer_masked")
         return y
 
-    def spec_layer(self, layer: int, k: int, drafts: dict, params: dict | None = None, y=None):
+    def spec_layer(self, layer: int, k: int, drafts: dict, params: dict | None = None, y=None, active=None):
         torch = _torch()
         st = self.layers[layer]
         c = st.cfg
         if y is None:
-            y = torch.empty((k, c.batch, c.nheads, c.head_dim), dtype=st.iot, device=st.device)
+            y = torch.zeros((k, c.batch, c.nheads, c.head_dim), dtype=st.iot, device=st.device)
         ri = make_inputs(c, drafts, params)
-        _check(_lib.replay_stack_spec_layer(self.h, int(layer), int(k), ctypes.byref(ri), _ptr(y, st.iot, "y"),
-                                            _stream()), "replay_stack_spec_layer")
+        if active is None:
+            _check(_lib.replay_stack_spec_layer(self.h, int(layer), int(k), ctypes.byref(ri), _ptr(y, st.iot, "y"),
+                                                _stream()), "replay_stack_spec_layer")
+        else:
+            _check(_lib.replay_stack_spec_layer_masked(self.h, int(layer), int(k), ctypes.byref(ri),
+                                                       _mask_ptr(active, c.batch), _ptr(y, st.iot, "y"),
+                                                       _stream()), "replay_stack_spec_layer_masked")
         return y
 
     def flush(self, params=None):

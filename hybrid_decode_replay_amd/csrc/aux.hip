@@ -58,6 +58,27 @@ hipError_t launch_book_reset(int32_t* book, uint32_t* err, int B, int parity, in
     return hipGetLastError();
 }
 
+// A sequence that (re)joins the batch: empty buffer, no drafts, a fresh window
+// of cap entries.  Written into the current copy; the other copy is rewritten
+// in full by the next launch that changes the bookkeeping.
+__global__ void book_reset_slots_kernel(int32_t* book, int B, int parity, int cap, SlotMap m)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= m.n) return;
+    const int b = m.slot[i];
+    int32_t* cur = book + (size_t)parity * 4 * B;
+    cur[b] = 0;
+    cur[B + b] = 0;
+    cur[2 * B + b] = 0;
+    cur[3 * B + b] = cap;
+}
+
+hipError_t launch_book_reset_slots(int32_t* book, int B, int parity, int cap, const SlotMap& m, hipStream_t s)
+{
+    hipLaunchKernelGGL(book_reset_slots_kernel, dim3(1), dim3(SLOT_CHUNK), 0, s, book, B, parity, cap, m);
+    return hipGetLastError();
+}
+
 // ---- zero fill (a kernel, not a memset, so it is safe under graph capture)
 __global__ void fill_zero_kernel(uint4* p, size_t n16, uint8_t* tail, size_t ntail)
 {
@@ -105,12 +126,40 @@ __global__ void tiles_to_logical_kernel(const W* ck, W* out, size_t n4, int C, i
     out[frag_to_logical(q, C, R) / 4] = ck[ckpt_elem_offset<CK>(q, R >> 4) / 4];
 }
 
+// Lane-block q of the source tiles -> the same lane-block of the tile the slot
+// map names.
+__device__ __forceinline__ size_t map_block(size_t q, size_t per_tile, const SlotMap& m)
+{
+    if (m.n == 0) return q;
+    const size_t ts = q / per_tile;
+    const size_t i = ts / (size_t)m.H;
+    const size_t td = (size_t)m.slot[i] * m.H + (ts - i * m.H);
+    return td * per_tile + (q - ts * per_tile);
+}
+
+// One word W (4 values in the checkpoint dtype) per thread, same dtype on both sides.
 template <int CK, class W>
-__global__ void logical_to_tiles_kernel(const W* in, W* ck, size_t n4, int C, int R)
+__global__ void logical_to_tiles_kernel(const W* in, W* ck, size_t n4, int C, int R, SlotMap m)
 {
     const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (q >= n4) return;
-    ck[ckpt_elem_offset<CK>(q, R >> 4) / 4] = in[frag_to_logical(q, C, R) / 4];
+    const size_t qd = map_block(q, (size_t)C * R / 4, m);
+    ck[ckpt_elem_offset<CK>(qd, R >> 4) / 4] = in[frag_to_logical(q, C, R) / 4];
+}
+
+// Four fp32 values per thread, rounded to the checkpoint dtype by the same
+// conversions the fold's store uses (binary16 RNE; E4M3 RNE saturating at +-448,
+// NaN to 0x7f).
+template <int CK>
+__global__ void logical_f32_to_tiles_kernel(const f32x4* in, void* ck, size_t n4, int C, int R, SlotMap m)
+{
+    const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= n4) return;
+    const f32x4 v = in[frag_to_logical(q, C, R) / 4];
+    const size_t e = ckpt_elem_offset<CK>(map_block(q, (size_t)C * R / 4, m), R >> 4);
+    if constexpr (CK == CK_F32) static_cast<f32x4*>(ck)[e / 4] = v;
+    else if constexpr (CK == CK_F16) static_cast<u32x2*>(ck)[e / 4] = f32_to_h4(v);
+    else static_cast<uint32_t*>(ck)[e / 4] = pack_e4m3(v);
 }
 
 hipError_t launch_tiles_to_logical(const void* ckpt, void* out, int tiles, int C, int R, int ck, hipStream_t s)
@@ -129,19 +178,27 @@ hipError_t launch_tiles_to_logical(const void* ckpt, void* out, int tiles, int C
     return hipGetLastError();
 }
 
-hipError_t launch_logical_to_tiles(const void* in, void* ckpt, int tiles, int C, int R, int ck, hipStream_t s)
+hipError_t launch_logical_to_tiles(const void* in, void* ckpt, int tiles, int C, int R, int ck, bool src_f32,
+                                   const SlotMap& m, hipStream_t s)
 {
     const size_t n4 = (size_t)tiles * C * R / 4;
     const dim3 grid((unsigned)((n4 + 255) / 256)), block(256);
-    if (ck == CK_FP8)
+    if (src_f32 && ck != CK_F32) {
+        const f32x4* src = static_cast<const f32x4*>(in);
+        if (ck == CK_FP8)
+            hipLaunchKernelGGL((logical_f32_to_tiles_kernel<CK_FP8>), grid, block, 0, s, src, ckpt, n4, C, R, m);
+        else
+            hipLaunchKernelGGL((logical_f32_to_tiles_kernel<CK_F16>), grid, block, 0, s, src, ckpt, n4, C, R, m);
+    } else if (ck == CK_FP8) {
         hipLaunchKernelGGL((logical_to_tiles_kernel<CK_FP8, uint32_t>), grid, block, 0, s,
-                           static_cast<const uint32_t*>(in), static_cast<uint32_t*>(ckpt), n4, C, R);
-    else if (ck == CK_F16)
+                           static_cast<const uint32_t*>(in), static_cast<uint32_t*>(ckpt), n4, C, R, m);
+    } else if (ck == CK_F16) {
         hipLaunchKernelGGL((logical_to_tiles_kernel<CK_F16, u32x2>), grid, block, 0, s,
-                           static_cast<const u32x2*>(in), static_cast<u32x2*>(ckpt), n4, C, R);
-    else
+                           static_cast<const u32x2*>(in), static_cast<u32x2*>(ckpt), n4, C, R, m);
+    } else {
         hipLaunchKernelGGL((logical_to_tiles_kernel<CK_F32, u32x4>), grid, block, 0, s,
-                           static_cast<const u32x4*>(in), static_cast<u32x4*>(ckpt), n4, C, R);
+                           static_cast<const u32x4*>(in), static_cast<u32x4*>(ckpt), n4, C, R, m);
+    }
     return hipGetLastError();
 }
 
@@ -150,11 +207,12 @@ hipError_t launch_logical_to_tiles(const void* in, void* ckpt, int tiles, int C,
 // kernels, so the quantizer is the one the flush path uses.
 template <int NB, int RC, int CK>
 __global__ __launch_bounds__(256) void quantize_rc_kernel(void* ckpt, uint8_t* codes, uint8_t* scales,
-                                                          size_t nstrips, int round_ckpt)
+                                                          size_t nstrips, int round_ckpt, int strips_per_tile, SlotMap m)
 {
-    const size_t strip = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const size_t src_strip = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    if (strip >= nstrips) return;                  // whole waves leave together
+    if (src_strip >= nstrips) return;              // whole waves leave together
+    const size_t strip = map_block(src_strip, (size_t)strips_per_tile, m);
     f32x4 s[NB];
     ckpt_load<NB, CK>(ckpt, strip, lane, s);
     rc_store<NB, RC>(codes, scales, strip, lane, s);
@@ -207,14 +265,16 @@ __global__ __launch_bounds__(256) void rc_to_logical_kernel(const uint8_t* codes
 
 template <int RC, int CK>
 static hipError_t rc_dispatch(bool quantize, void* ckpt, const uint8_t* codes_in, const uint8_t* scales_in,
-                              uint8_t* codes, uint8_t* scales, int tiles, int C, int R, int round_ckpt, hipStream_t s)
+                              uint8_t* codes, uint8_t* scales, int tiles, int C, int R, int round_ckpt,
+                              const SlotMap& m, hipStream_t s)
 {
     const size_t nstrips = (size_t)tiles * (C / 16);
+    const int spt = C / 16;
     const dim3 grid((unsigned)((nstrips + 3) / 4)), block(256);
 #define RS_RC_CASE(NBV)                                                                                  \
     case NBV * 16:                                                                                       \
         if (quantize) hipLaunchKernelGGL((quantize_rc_kernel<NBV, RC, CK>), grid, block, 0, s, ckpt, codes, scales,   \
-                                         nstrips, round_ckpt);                                          \
+                                         nstrips, round_ckpt, spt, m);                                  \
         else hipLaunchKernelGGL((rc_to_logical_kernel<NBV, RC>), grid, block, 0, s, codes_in, scales_in, codes, scales,    \
                                 nstrips, C);                                                             \
         return hipGetLastError();
@@ -222,7 +282,7 @@ static hipError_t rc_dispatch(bool quantize, void* ckpt, const uint8_t* codes_in
         case 16:
             if constexpr (RC == RC_FP8) {
                 if (quantize) hipLaunchKernelGGL((quantize_rc_kernel<1, RC, CK>), grid, block, 0, s, ckpt, codes, scales,
-                                                 nstrips, round_ckpt);
+                                                 nstrips, round_ckpt, spt, m);
                 else hipLaunchKernelGGL((rc_to_logical_kernel<1, RC>), grid, block, 0, s, codes_in, scales_in, codes, scales,
                                         nstrips, C);
                 return hipGetLastError();
@@ -238,30 +298,33 @@ static hipError_t rc_dispatch(bool quantize, void* ckpt, const uint8_t* codes_in
 }
 
 hipError_t launch_quantize_read_copy(void* ckpt, uint8_t* codes, uint8_t* scales, int tiles, int C, int R, int rc,
-                                     int ck, bool round_ckpt, hipStream_t s)
+                                     int ck, bool round_ckpt, const SlotMap& m, hipStream_t s)
 {
     if (ck == CK_FP8) {
         if (round_ckpt || rc != RC_MXFP4) return hipErrorInvalidValue;   // only an MXFP4 copy of an FP8 checkpoint
-        return rc_dispatch<RC_MXFP4, CK_FP8>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, 0, s);
+        return rc_dispatch<RC_MXFP4, CK_FP8>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, 0, m, s);
     }
     if (ck == CK_F16) {
         if (round_ckpt) return hipErrorInvalidValue;     // the quantized-checkpoint variant keeps fp32 storage
-        if (rc == RC_FP8) return rc_dispatch<RC_FP8, CK_F16>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, 0, s);
-        if (rc == RC_MXFP4) return rc_dispatch<RC_MXFP4, CK_F16>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, 0, s);
+        if (rc == RC_FP8) return rc_dispatch<RC_FP8, CK_F16>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, 0, m, s);
+        if (rc == RC_MXFP4) return rc_dispatch<RC_MXFP4, CK_F16>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, 0, m, s);
         return hipErrorInvalidValue;
     }
     if (rc == RC_FP8)
-        return rc_dispatch<RC_FP8, CK_F32>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, round_ckpt, s);
+        return rc_dispatch<RC_FP8, CK_F32>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, round_ckpt, m, s);
     if (rc == RC_MXFP4)
-        return rc_dispatch<RC_MXFP4, CK_F32>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, round_ckpt, s);
+        return rc_dispatch<RC_MXFP4, CK_F32>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, round_ckpt, m, s);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_read_copy_to_logical(const uint8_t* codes, const uint8_t* scales, uint8_t* codes_out,
                                        uint8_t* scales_out, int tiles, int C, int R, int rc, hipStream_t s)
 {
-    if (rc == RC_FP8) return rc_dispatch<RC_FP8, CK_F32>(false, nullptr, codes, scales, codes_out, scales_out, tiles, C, R, 0, s);
-    if (rc == RC_MXFP4) return rc_dispatch<RC_MXFP4, CK_F32>(false, nullptr, codes, scales, codes_out, scales_out, tiles, C, R, 0, s);
+    SlotMap all;
+    all.n = 0;
+    all.H = 1;
+    if (rc == RC_FP8) return rc_dispatch<RC_FP8, CK_F32>(false, nullptr, codes, scales, codes_out, scales_out, tiles, C, R, 0, all, s);
+    if (rc == RC_MXFP4) return rc_dispatch<RC_MXFP4, CK_F32>(false, nullptr, codes, scales, codes_out, scales_out, tiles, C, R, 0, all, s);
     return hipErrorInvalidValue;
 }
 

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256, NB <= 8 ? 6 : 4) void gdn_step_kernel(StepArgs
     const size_t sB = (size_t)a.B;
 
     const StepPlan p = plan_step(a, b, h == 0 && tix.sp == 0 && tid == 0);
-    if (a.mode == MODE_FLUSH && p.f == 0) return;
+    if (p.skip || (a.mode == MODE_FLUSH && p.f == 0)) return;
     const int f = p.f, len = p.len, V = p.V, T = a.T;
     const int Tr = T > 0 ? T : 1, vmax = a.vmax;
 

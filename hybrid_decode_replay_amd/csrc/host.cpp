@@ -34,6 +34,7 @@ struct replay_stack {
     int next = 0;     // next layer of the current step (0 between steps)
     int step_mode = -1;
     int step_k = 0;
+    const uint8_t* step_active = nullptr;   // the active mask every layer of the step uses
 };
 
 namespace {
@@ -62,6 +63,22 @@ replay_status hip_check(hipError_t e, const char* what)
 {
     if (e != hipSuccess) return fail(REPLAY_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
     return ok();
+}
+
+// Clears an error an earlier, unrelated HIP call may have left behind, so that
+// the hipGetLastError a launcher returns reports its own launch only.
+hipError_t fresh() { return hipGetLastError(); }
+
+// hip_check of a launch expression, after clearing any stale error (the comma
+// operator sequences the clearing before the launch).
+#define LAUNCH(expr, what) hip_check(((void)fresh(), (expr)), what)
+
+rs::SlotMap all_tiles(int H)
+{
+    rs::SlotMap m;
+    m.n = 0;
+    m.H = H;
+    return m;
 }
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~(uint64_t)255; }
@@ -188,7 +205,8 @@ replay_status check_inputs(const replay_config* c, const replay_inputs* in, bool
     return REPLAY_OK;
 }
 
-rs::StepArgs step_args(const replay_state* st, const replay_inputs* in, void* y, int mode, int T)
+rs::StepArgs step_args(const replay_state* st, const replay_inputs* in, void* y, int mode, int T,
+                       const uint8_t* active)
 {
     const replay_config* c = &st->cfg;
     rs::StepArgs a;
@@ -247,13 +265,16 @@ rs::StepArgs step_args(const replay_state* st, const replay_inputs* in, void* y,
         a.in_s1 = in->beta;
     }
     a.y = y;
+    a.active = active;
     return a;
 }
 
-replay_status launch_step(replay_state* st, const replay_inputs* in, void* y, int mode, int T, void* stream)
+replay_status launch_step(replay_state* st, const replay_inputs* in, void* y, int mode, int T, void* stream,
+                          const uint8_t* active = nullptr)
 {
     const replay_config* c = &st->cfg;
-    rs::StepArgs a = step_args(st, in, y, mode, T);
+    rs::StepArgs a = step_args(st, in, y, mode, T, active);
+    (void)fresh();
     const int io = c->io_dtype == REPLAY_BF16 ? rs::IO_BF16 : rs::IO_F32;
     const int rc = rc_kind(c);
     hipError_t e;
@@ -325,9 +346,9 @@ replay_status replay_state_alloc(const replay_config* cfg, void* dev_mem, size_t
     st->lay = L;
     st->parity = 0;
     st->phase = 0;
-    s = hip_check(rs::launch_fill_zero(dev_mem, L.total_bytes, (hipStream_t)stream), "state initialisation");
+    s = LAUNCH(rs::launch_fill_zero(dev_mem, L.total_bytes, (hipStream_t)stream), "state initialisation");
     if (s == REPLAY_OK)
-        s = hip_check(rs::launch_book_reset(at<int32_t>(st, L.book_off), at<uint32_t>(st, L.err_off), cfg->batch, 0,
+        s = LAUNCH(rs::launch_book_reset(at<int32_t>(st, L.book_off), at<uint32_t>(st, L.err_off), cfg->batch, 0,
                                             cfg->buf_cap, (cfg->flags & REPLAY_FLAG_STAGGER_FLUSH) != 0,
                                             (hipStream_t)stream),
                       "bookkeeping initialisation");
@@ -342,6 +363,7 @@ replay_status replay_state_alloc(const replay_config* cfg, void* dev_mem, size_t
 replay_status replay_state_free(replay_state* st)
 {
     if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
+    if (st->stack) return fail(REPLAY_ERR_STATE, "the state is bound to a stack: free the stack first");
     delete st;
     return ok();
 }
@@ -355,44 +377,112 @@ replay_status replay_state_layout(const replay_state* st, replay_layout* out)
 
 int32_t replay_state_phase(const replay_state* st) { return st ? st->phase : -1; }
 
-static replay_status load_impl(replay_state* st, const void* S, void* stream);
+static replay_status load_impl(replay_state* st, const void* S, bool src_f32, void* stream);
 
 replay_status replay_load_checkpoint(replay_state* st, const void* S, void* stream)
 {
     if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
     if (st->stack) return fail(REPLAY_ERR_STATE, "the state is a stack member: load through the stack");
     if (st->phase != 0) return fail(REPLAY_ERR_STATE, "load while drafts are pending");
-    replay_status s = load_impl(st, S, stream);
+    replay_status s = load_impl(st, S, false, stream);
     if (s == REPLAY_OK) st->needs_load = false;
     return s;
 }
 
+replay_status replay_load_checkpoint_f32(replay_state* st, const float* S, void* stream)
+{
+    if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
+    if (st->stack) return fail(REPLAY_ERR_STATE, "the state is a stack member: load through the stack");
+    if (st->phase != 0) return fail(REPLAY_ERR_STATE, "load while drafts are pending");
+    replay_status s = load_impl(st, S, true, stream);
+    if (s == REPLAY_OK) st->needs_load = false;
+    return s;
+}
+
+// Checkpoint tiles and read copy of the tiles `m` names (all of them for a
+// whole-state load), from `ntiles` source tiles.
+static replay_status load_tiles(replay_state* st, const void* S, bool src_f32, int ntiles, const rs::SlotMap& m,
+                                hipStream_t hs)
+{
+    const replay_config* c = &st->cfg;
+    replay_status s = LAUNCH(rs::launch_logical_to_tiles(S, at<void>(st, st->lay.ckpt_off), ntiles, c->head_dim,
+                                                         c->state_dim, ck_kind(c), src_f32, m, hs),
+                             "checkpoint load");
+    if (s != REPLAY_OK || c->read_copy == REPLAY_NONE) return s;
+    return LAUNCH(rs::launch_quantize_read_copy(at<void>(st, st->lay.ckpt_off), at<uint8_t>(st, st->lay.rcopy_off),
+                                                st->lay.rscale_bytes ? at<uint8_t>(st, st->lay.rscale_off) : nullptr,
+                                                ntiles, c->head_dim, c->state_dim, rc_kind(c), ck_kind(c),
+                                                (c->flags & REPLAY_FLAG_QUANTIZED_CKPT) != 0, m, hs),
+                  "read copy quantize");
+}
+
 // Checkpoint tiles and read copy of one state, then its bookkeeping (the
 // stack's, for a member).
-static replay_status load_impl(replay_state* st, const void* S, void* stream)
+static replay_status load_impl(replay_state* st, const void* S, bool src_f32, void* stream)
 {
     replay_status s = check_ptr(S, "S_logical");
     if (s != REPLAY_OK) return s;
     const replay_config* c = &st->cfg;
-    const int tiles = c->batch * c->nheads;
     hipStream_t hs = (hipStream_t)stream;
-    s = hip_check(rs::launch_logical_to_tiles(S, at<void>(st, st->lay.ckpt_off), tiles, c->head_dim, c->state_dim,
-                                              ck_kind(c), hs),
-                  "checkpoint load");
-    if (s != REPLAY_OK) return s;
-    if (c->read_copy != REPLAY_NONE) {
-        s = hip_check(rs::launch_quantize_read_copy(at<void>(st, st->lay.ckpt_off), at<uint8_t>(st, st->lay.rcopy_off),
-                                                    st->lay.rscale_bytes ? at<uint8_t>(st, st->lay.rscale_off) : nullptr,
-                                                    tiles, c->head_dim, c->state_dim, rc_kind(c), ck_kind(c),
-                                                    (c->flags & REPLAY_FLAG_QUANTIZED_CKPT) != 0, hs),
-                      "read copy quantize");
-        if (s != REPLAY_OK) return s;
+    s = load_tiles(st, S, src_f32, c->batch * c->nheads, all_tiles(c->nheads), hs);
+    if (s != REPLAY_OK || st->stack) return s;
+    return LAUNCH(rs::launch_book_reset(at<int32_t>(st, st->lay.book_off), at<uint32_t>(st, st->lay.err_off),
+                                        c->batch, st->parity, c->buf_cap,
+                                        (c->flags & REPLAY_FLAG_STAGGER_FLUSH) != 0, hs),
+                  "bookkeeping reset");
+}
+
+// Host-side checks of a per-slot load's sequence list: 1 <= n <= B, every slot
+// in [0, B), no slot twice.
+static replay_status check_slots(int32_t n, const int32_t* slots, int B)
+{
+    if (n < 1 || n > B) return fail(REPLAY_ERR_ARG, "slot count %d outside [1, %d]", n, B);
+    if (!slots) return fail(REPLAY_ERR_ARG, "slots is NULL");
+    std::vector<char> seen((size_t)B, 0);
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t b = slots[i];
+        if (b < 0 || b >= B) return fail(REPLAY_ERR_ARG, "slot %d outside [0, %d)", b, B);
+        if (seen[(size_t)b]) return fail(REPLAY_ERR_ARG, "slot %d listed twice", b);
+        seen[(size_t)b] = 1;
     }
-    if (st->stack) return REPLAY_OK;
-    return hip_check(rs::launch_book_reset(at<int32_t>(st, st->lay.book_off), at<uint32_t>(st, st->lay.err_off),
-                                           c->batch, st->parity, c->buf_cap,
-                                           (c->flags & REPLAY_FLAG_STAGGER_FLUSH) != 0, hs),
-                     "bookkeeping reset");
+    return REPLAY_OK;
+}
+
+// The listed sequences' checkpoints (fp32 source [n][H][rows][cols]) and read
+// copies, in chunks of SLOT_CHUNK sequences per launch; then, unless the state
+// is a stack member, their bookkeeping.
+static replay_status load_slots_impl(replay_state* st, int32_t n, const int32_t* slots, const float* S, hipStream_t hs)
+{
+    const replay_config* c = &st->cfg;
+    const size_t seq_floats = (size_t)c->nheads * c->head_dim * c->state_dim;
+    for (int32_t i0 = 0; i0 < n; i0 += rs::SLOT_CHUNK) {
+        rs::SlotMap m;
+        m.n = n - i0 < rs::SLOT_CHUNK ? n - i0 : rs::SLOT_CHUNK;
+        m.H = c->nheads;
+        for (int i = 0; i < m.n; ++i) m.slot[i] = slots[i0 + i];
+        replay_status s = load_tiles(st, S + (size_t)i0 * seq_floats, true, m.n * c->nheads, m, hs);
+        if (s != REPLAY_OK) return s;
+        if (!st->stack) {
+            s = LAUNCH(rs::launch_book_reset_slots(at<int32_t>(st, st->lay.book_off), c->batch, st->parity,
+                                                   c->buf_cap, m, hs),
+                       "slot bookkeeping reset");
+            if (s != REPLAY_OK) return s;
+        }
+    }
+    return REPLAY_OK;
+}
+
+replay_status replay_load_slots(replay_state* st, int32_t n, const int32_t* slots, const float* S, void* stream)
+{
+    if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
+    if (st->stack) return fail(REPLAY_ERR_STATE, "the state is a stack member: load through the stack");
+    if (st->needs_load) return fail(REPLAY_ERR_STATE, "a former stack member must be loaded first");
+    if (st->phase != 0) return fail(REPLAY_ERR_STATE, "load while drafts are pending");
+    replay_status s = check_slots(n, slots, st->cfg.batch);
+    if (s != REPLAY_OK) return s;
+    if ((s = check_ptr(S, "S_logical")) != REPLAY_OK) return s;
+    if ((s = load_slots_impl(st, n, slots, S, (hipStream_t)stream)) != REPLAY_OK) return s;
+    return ok();
 }
 
 replay_status replay_read_checkpoint(const replay_state* st, void* out, void* stream)
@@ -401,7 +491,7 @@ replay_status replay_read_checkpoint(const replay_state* st, void* out, void* st
     replay_status s = check_ptr(out, "S_out");
     if (s != REPLAY_OK) return s;
     const replay_config* c = &st->cfg;
-    return hip_check(rs::launch_tiles_to_logical(at<void>(st, st->lay.ckpt_off), out, c->batch * c->nheads,
+    return LAUNCH(rs::launch_tiles_to_logical(at<void>(st, st->lay.ckpt_off), out, c->batch * c->nheads,
                                                  c->head_dim, c->state_dim, ck_kind(c), (hipStream_t)stream),
                      "checkpoint read");
 }
@@ -413,7 +503,7 @@ replay_status replay_read_copy(const replay_state* st, uint8_t* codes_out, uint8
     if (c->read_copy == REPLAY_NONE) return fail(REPLAY_ERR_STATE, "state has no read copy");
     if (!codes_out) return fail(REPLAY_ERR_ARG, "codes_out is NULL");
     if (c->read_copy == REPLAY_MXFP4 && !scales_out) return fail(REPLAY_ERR_ARG, "scales_out is NULL");
-    return hip_check(rs::launch_read_copy_to_logical(at<uint8_t>(st, st->lay.rcopy_off),
+    return LAUNCH(rs::launch_read_copy_to_logical(at<uint8_t>(st, st->lay.rcopy_off),
                                                      st->lay.rscale_bytes ? at<uint8_t>(st, st->lay.rscale_off) : nullptr,
                                                      codes_out, scales_out, c->batch * c->nheads, c->head_dim,
                                                      c->state_dim, rc_kind(c), (hipStream_t)stream),
@@ -426,10 +516,10 @@ static replay_status read_book_impl(const int32_t* book, const uint32_t* err, in
     if (!book_out) return fail(REPLAY_ERR_ARG, "book_out is NULL");
     const size_t n = (size_t)3 * B * sizeof(int32_t);
     hipStream_t hs = (hipStream_t)stream;
-    replay_status s = hip_check(hipMemcpyAsync(book_out, book + (size_t)parity * 4 * B, n, hipMemcpyDeviceToDevice, hs),
+    replay_status s = LAUNCH(hipMemcpyAsync(book_out, book + (size_t)parity * 4 * B, n, hipMemcpyDeviceToDevice, hs),
                                 "bookkeeping copy");
     if (s != REPLAY_OK || !err_out) return s;
-    return hip_check(hipMemcpyAsync(err_out, err, 4, hipMemcpyDeviceToDevice, hs), "error word copy");
+    return LAUNCH(hipMemcpyAsync(err_out, err, 4, hipMemcpyDeviceToDevice, hs), "error word copy");
 }
 
 replay_status replay_read_book(const replay_state* st, int32_t* book_out, uint32_t* err_out, void* stream)
@@ -440,7 +530,8 @@ replay_status replay_read_book(const replay_state* st, int32_t* book_out, uint32
                           st->parity, book_out, err_out, stream);
 }
 
-replay_status replay_decode_step(replay_state* st, const replay_inputs* in, void* y, void* stream)
+static replay_status decode_impl(replay_state* st, const replay_inputs* in, const uint8_t* active, void* y,
+                                 void* stream)
 {
     if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
     if (st->stack) return fail(REPLAY_ERR_STATE, "the state is a stack member: step it through the stack");
@@ -449,7 +540,19 @@ replay_status replay_decode_step(replay_state* st, const replay_inputs* in, void
     replay_status s = check_inputs(&st->cfg, in, true, true);
     if (s != REPLAY_OK) return s;
     if ((s = check_ptr(y, "y")) != REPLAY_OK) return s;
-    return launch_step(st, in, y, rs::MODE_DECODE, 1, stream);
+    return launch_step(st, in, y, rs::MODE_DECODE, 1, stream, active);
+}
+
+replay_status replay_decode_step(replay_state* st, const replay_inputs* in, void* y, void* stream)
+{
+    return decode_impl(st, in, nullptr, y, stream);
+}
+
+replay_status replay_decode_step_masked(replay_state* st, const replay_inputs* in, const uint8_t* active, void* y,
+                                        void* stream)
+{
+    if (!active) return fail(REPLAY_ERR_ARG, "active is NULL");
+    return decode_impl(st, in, active, y, stream);
 }
 
 replay_status replay_flush(replay_state* st, const replay_inputs* in, void* stream)
@@ -468,7 +571,8 @@ replay_status replay_flush(replay_state* st, const replay_inputs* in, void* stre
     return launch_step(st, in, nullptr, rs::MODE_FLUSH, 0, stream);
 }
 
-replay_status replay_spec_append(replay_state* st, int32_t k, const replay_inputs* drafts, void* y, void* stream)
+static replay_status spec_impl(replay_state* st, int32_t k, const replay_inputs* drafts, const uint8_t* active,
+                               void* y, void* stream)
 {
     if (!st) return fail(REPLAY_ERR_ARG, "state is NULL");
     if (st->stack) return fail(REPLAY_ERR_STATE, "the state is a stack member: step it through the stack");
@@ -478,15 +582,27 @@ replay_status replay_spec_append(replay_state* st, int32_t k, const replay_input
     replay_status s = check_inputs(&st->cfg, drafts, true, true);
     if (s != REPLAY_OK) return s;
     if ((s = check_ptr(y, "y")) != REPLAY_OK) return s;
-    s = launch_step(st, drafts, y, rs::MODE_SPEC, k, stream);
+    s = launch_step(st, drafts, y, rs::MODE_SPEC, k, stream, active);
     if (s == REPLAY_OK) st->phase = 1;
     return s;
+}
+
+replay_status replay_spec_append(replay_state* st, int32_t k, const replay_inputs* drafts, void* y, void* stream)
+{
+    return spec_impl(st, k, drafts, nullptr, y, stream);
+}
+
+replay_status replay_spec_append_masked(replay_state* st, int32_t k, const replay_inputs* drafts,
+                                        const uint8_t* active, void* y, void* stream)
+{
+    if (!active) return fail(REPLAY_ERR_ARG, "active is NULL");
+    return spec_impl(st, k, drafts, active, y, stream);
 }
 
 static replay_status commit_impl(replay_state* st, const int32_t* accepted, void* stream)
 {
     if (st->phase != 1) return fail(REPLAY_ERR_STATE, "no drafts pending");
-    replay_status s = hip_check(rs::launch_book_commit(at<int32_t>(st, st->lay.book_off), at<uint32_t>(st, st->lay.err_off),
+    replay_status s = LAUNCH(rs::launch_book_commit(at<int32_t>(st, st->lay.book_off), at<uint32_t>(st, st->lay.err_off),
                                                        st->cfg.batch, st->parity, accepted, (hipStream_t)stream),
                                 "commit");
     if (s == REPLAY_OK) {
@@ -516,7 +632,7 @@ replay_status replay_spec_rollback(replay_state* st, void* stream)
 
 // ---- layer stacks: one bookkeeping set for every SSM layer of a model --------
 
-static replay_status stack_check_step(const replay_stack* stk, int32_t layer, int mode, int k)
+static replay_status stack_check_step(const replay_stack* stk, int32_t layer, int mode, int k, const uint8_t* active)
 {
     if (!stk) return fail(REPLAY_ERR_ARG, "stack is NULL");
     const int n = (int)stk->layers.size();
@@ -526,16 +642,19 @@ static replay_status stack_check_step(const replay_stack* stk, int32_t layer, in
     if (stk->next == 0 && stk->phase != 0) return fail(REPLAY_ERR_STATE, "drafts are pending");
     if (stk->next > 0 && (mode != stk->step_mode || k != stk->step_k))
         return fail(REPLAY_ERR_STATE, "every layer of a step runs the same operation with the same draft count");
+    if (stk->next > 0 && active != stk->step_active)
+        return fail(REPLAY_ERR_STATE, "every layer of a step uses the same active mask");
     return REPLAY_OK;
 }
 
 // A layer of the step ran: after the last one the shared bookkeeping copy
 // written by the step becomes the current one.
-static void stack_advance(replay_stack* stk, int mode, int k)
+static void stack_advance(replay_stack* stk, int mode, int k, const uint8_t* active)
 {
     if (stk->next == 0) {
         stk->step_mode = mode;
         stk->step_k = k;
+        stk->step_active = active;
     }
     if (++stk->next == (int)stk->layers.size()) {
         stk->next = 0;
@@ -555,7 +674,7 @@ static replay_status stack_idle(const replay_stack* stk, const char* what)
 static replay_status stack_reset_book(replay_stack* stk, void* stream)
 {
     const replay_config* c = &stk->layers[0]->cfg;
-    return hip_check(rs::launch_book_reset(stk->book, stk->err, c->batch, stk->parity, c->buf_cap,
+    return LAUNCH(rs::launch_book_reset(stk->book, stk->err, c->batch, stk->parity, c->buf_cap,
                                            (c->flags & REPLAY_FLAG_STAGGER_FLUSH) != 0, (hipStream_t)stream),
                      "bookkeeping reset");
 }
@@ -604,7 +723,7 @@ replay_status replay_stack_free(replay_stack* stk)
     return ok();
 }
 
-replay_status replay_stack_load(replay_stack* stk, const void* const* S, void* stream)
+static replay_status stack_load_impl(replay_stack* stk, const void* const* S, bool src_f32, void* stream)
 {
     replay_status s = stack_idle(stk, "load");
     if (s != REPLAY_OK) return s;
@@ -613,35 +732,97 @@ replay_status replay_stack_load(replay_stack* stk, const void* const* S, void* s
     for (size_t l = 0; l < stk->layers.size(); ++l)
         if ((s = check_ptr(S[l], "S_logical[layer]")) != REPLAY_OK) return s;
     for (size_t l = 0; l < stk->layers.size(); ++l)
-        if ((s = load_impl(stk->layers[l], S[l], stream)) != REPLAY_OK) return s;
+        if ((s = load_impl(stk->layers[l], S[l], src_f32, stream)) != REPLAY_OK) return s;
     return stack_reset_book(stk, stream);
+}
+
+replay_status replay_stack_load(replay_stack* stk, const void* const* S, void* stream)
+{
+    return stack_load_impl(stk, S, false, stream);
+}
+
+replay_status replay_stack_load_f32(replay_stack* stk, const float* const* S, void* stream)
+{
+    return stack_load_impl(stk, reinterpret_cast<const void* const*>(S), true, stream);
+}
+
+replay_status replay_stack_load_slots(replay_stack* stk, int32_t n, const int32_t* slots, const float* const* S,
+                                      void* stream)
+{
+    replay_status s = stack_idle(stk, "load");
+    if (s != REPLAY_OK) return s;
+    if (stk->phase != 0) return fail(REPLAY_ERR_STATE, "load while drafts are pending");
+    const replay_config* c0 = &stk->layers[0]->cfg;
+    if ((s = check_slots(n, slots, c0->batch)) != REPLAY_OK) return s;
+    if (!S) return fail(REPLAY_ERR_ARG, "S_logical is NULL");
+    for (size_t l = 0; l < stk->layers.size(); ++l)
+        if ((s = check_ptr(S[l], "S_logical[layer]")) != REPLAY_OK) return s;
+    hipStream_t hs = (hipStream_t)stream;
+    for (size_t l = 0; l < stk->layers.size(); ++l)
+        if ((s = load_slots_impl(stk->layers[l], n, slots, S[l], hs)) != REPLAY_OK) return s;
+    for (int32_t i0 = 0; i0 < n; i0 += rs::SLOT_CHUNK) {
+        rs::SlotMap m;
+        m.n = n - i0 < rs::SLOT_CHUNK ? n - i0 : rs::SLOT_CHUNK;
+        m.H = 1;
+        for (int i = 0; i < m.n; ++i) m.slot[i] = slots[i0 + i];
+        s = LAUNCH(rs::launch_book_reset_slots(stk->book, c0->batch, stk->parity, c0->buf_cap, m, hs),
+                   "slot bookkeeping reset");
+        if (s != REPLAY_OK) return s;
+    }
+    return ok();
+}
+
+static replay_status stack_decode_impl(replay_stack* stk, int32_t layer, const replay_inputs* in,
+                                       const uint8_t* active, void* y, void* stream)
+{
+    replay_status s = stack_check_step(stk, layer, rs::MODE_DECODE, 1, active);
+    if (s != REPLAY_OK) return s;
+    replay_state* st = stk->layers[layer];
+    if ((s = check_inputs(&st->cfg, in, true, true)) != REPLAY_OK) return s;
+    if ((s = check_ptr(y, "y")) != REPLAY_OK) return s;
+    if ((s = launch_step(st, in, y, rs::MODE_DECODE, 1, stream, active)) != REPLAY_OK) return s;
+    stack_advance(stk, rs::MODE_DECODE, 1, active);
+    return ok();
 }
 
 replay_status replay_stack_decode_layer(replay_stack* stk, int32_t layer, const replay_inputs* in, void* y,
                                         void* stream)
 {
-    replay_status s = stack_check_step(stk, layer, rs::MODE_DECODE, 1);
+    return stack_decode_impl(stk, layer, in, nullptr, y, stream);
+}
+
+replay_status replay_stack_decode_layer_masked(replay_stack* stk, int32_t layer, const replay_inputs* in,
+                                               const uint8_t* active, void* y, void* stream)
+{
+    if (!active) return fail(REPLAY_ERR_ARG, "active is NULL");
+    return stack_decode_impl(stk, layer, in, active, y, stream);
+}
+
+static replay_status stack_spec_impl(replay_stack* stk, int32_t layer, int32_t k, const replay_inputs* drafts,
+                                     const uint8_t* active, void* y, void* stream)
+{
+    replay_status s = stack_check_step(stk, layer, rs::MODE_SPEC, k, active);
     if (s != REPLAY_OK) return s;
     replay_state* st = stk->layers[layer];
-    if ((s = check_inputs(&st->cfg, in, true, true)) != REPLAY_OK) return s;
+    if (k < 1 || k > st->cfg.buf_cap) return fail(REPLAY_ERR_CAPACITY, "k = %d outside [1, %d]", k, st->cfg.buf_cap);
+    if ((s = check_inputs(&st->cfg, drafts, true, true)) != REPLAY_OK) return s;
     if ((s = check_ptr(y, "y")) != REPLAY_OK) return s;
-    if ((s = launch_step(st, in, y, rs::MODE_DECODE, 1, stream)) != REPLAY_OK) return s;
-    stack_advance(stk, rs::MODE_DECODE, 1);
+    if ((s = launch_step(st, drafts, y, rs::MODE_SPEC, k, stream, active)) != REPLAY_OK) return s;
+    stack_advance(stk, rs::MODE_SPEC, k, active);
     return ok();
 }
 
 replay_status replay_stack_spec_layer(replay_stack* stk, int32_t layer, int32_t k, const replay_inputs* drafts,
                                       void* y, void* stream)
 {
-    replay_status s = stack_check_step(stk, layer, rs::MODE_SPEC, k);
-    if (s != REPLAY_OK) return s;
-    replay_state* st = stk->layers[layer];
-    if (k < 1 || k > st->cfg.buf_cap) return fail(REPLAY_ERR_CAPACITY, "k = %d outside [1, %d]", k, st->cfg.buf_cap);
-    if ((s = check_inputs(&st->cfg, drafts, true, true)) != REPLAY_OK) return s;
-    if ((s = check_ptr(y, "y")) != REPLAY_OK) return s;
-    if ((s = launch_step(st, drafts, y, rs::MODE_SPEC, k, stream)) != REPLAY_OK) return s;
-    stack_advance(stk, rs::MODE_SPEC, k);
-    return ok();
+    return stack_spec_impl(stk, layer, k, drafts, nullptr, y, stream);
+}
+
+replay_status replay_stack_spec_layer_masked(replay_stack* stk, int32_t layer, int32_t k, const replay_inputs* drafts,
+                                             const uint8_t* active, void* y, void* stream)
+{
+    if (!active) return fail(REPLAY_ERR_ARG, "active is NULL");
+    return stack_spec_impl(stk, layer, k, drafts, active, y, stream);
 }
 
 replay_status replay_stack_flush(replay_stack* stk, const replay_inputs* const* in, void* stream)
@@ -668,7 +849,7 @@ static replay_status stack_commit_impl(replay_stack* stk, const int32_t* accepte
     replay_status s = stack_idle(stk, "commit");
     if (s != REPLAY_OK) return s;
     if (stk->phase != 1) return fail(REPLAY_ERR_STATE, "no drafts pending");
-    s = hip_check(rs::launch_book_commit(stk->book, stk->err, stk->layers[0]->cfg.batch, stk->parity, accepted,
+    s = LAUNCH(rs::launch_book_commit(stk->book, stk->err, stk->layers[0]->cfg.batch, stk->parity, accepted,
                                          (hipStream_t)stream),
                   "commit");
     if (s == REPLAY_OK) {
@@ -747,7 +928,7 @@ replay_status replay_conv_decode_step(const replay_config* cfg, void* S, const r
     if (s != REPLAY_OK) return s;
     if ((s = check_ptr(S, "S")) != REPLAY_OK) return s;
     a.S = S;
-    return hip_check(rs::launch_conv_step(a, cfg->io_dtype == REPLAY_BF16 ? rs::IO_BF16 : rs::IO_F32, ck_kind(cfg),
+    return LAUNCH(rs::launch_conv_step(a, cfg->io_dtype == REPLAY_BF16 ? rs::IO_BF16 : rs::IO_F32, ck_kind(cfg),
                                           (hipStream_t)stream),
                      "conventional decode");
 }
@@ -764,7 +945,7 @@ replay_status replay_conv_spec_step(const replay_config* cfg, const void* S, voi
     a.S_in = S;
     a.S = const_cast<void*>(S);
     a.snaps = snaps;
-    return hip_check(rs::launch_conv_step(a, cfg->io_dtype == REPLAY_BF16 ? rs::IO_BF16 : rs::IO_F32, ck_kind(cfg),
+    return LAUNCH(rs::launch_conv_step(a, cfg->io_dtype == REPLAY_BF16 ? rs::IO_BF16 : rs::IO_F32, ck_kind(cfg),
                                           (hipStream_t)stream),
                      "conventional spec step");
 }
@@ -784,7 +965,7 @@ replay_status replay_conv_spec_restore(const replay_config* cfg, void* S, const 
     c.flags = 0;
     if ((s = check_config(&c)) != REPLAY_OK) return s;
     const size_t tile_bytes = (size_t)cfg->head_dim * cfg->state_dim * ckpt_bytes(cfg);
-    return hip_check(rs::launch_conv_restore(S, snaps, accepted, cfg->batch, tile_bytes, cfg->nheads, k,
+    return LAUNCH(rs::launch_conv_restore(S, snaps, accepted, cfg->batch, tile_bytes, cfg->nheads, k,
                                              (hipStream_t)stream),
                      "conventional restore");
 }
@@ -795,7 +976,7 @@ replay_status replay_stream_copy(void* dst, const void* src, size_t bytes, void*
     if ((s = check_ptr(dst, "dst")) != REPLAY_OK) return s;
     if ((s = check_ptr(src, "src")) != REPLAY_OK) return s;
     if (bytes % 16) return fail(REPLAY_ERR_ALIGN, "bytes must be a multiple of 16");
-    return hip_check(rs::launch_stream_copy(dst, src, bytes, (hipStream_t)stream), "stream copy");
+    return LAUNCH(rs::launch_stream_copy(dst, src, bytes, (hipStream_t)stream), "stream copy");
 }
 
 replay_status replay_stream_read(const void* src, size_t bytes, float* sum_out, void* stream)
@@ -804,7 +985,7 @@ replay_status replay_stream_read(const void* src, size_t bytes, float* sum_out, 
     if ((s = check_ptr(src, "src")) != REPLAY_OK) return s;
     if (!sum_out) return fail(REPLAY_ERR_ARG, "sum_out is NULL");
     if (bytes % 16) return fail(REPLAY_ERR_ALIGN, "bytes must be a multiple of 16");
-    return hip_check(rs::launch_stream_read(src, bytes, sum_out, (hipStream_t)stream), "stream read");
+    return LAUNCH(rs::launch_stream_read(src, bytes, sum_out, (hipStream_t)stream), "stream read");
 }
 
 }  // extern "C"

@@ -14,6 +14,17 @@ enum : int { CK_F32 = 0, CK_F16 = 1, CK_FP8 = 2 };   // recurrence checkpoint st
 // Device error word bits (mirror REPLAY_DEVERR_* of the public header).
 constexpr uint32_t REPLAY_COMMIT_CLAMPED_BIT = 0x1u;
 
+// The sequences a per-slot load writes, passed by value (kernel arguments), so
+// the list a kernel sees is exactly the one the host validated: distinct slots
+// in [0, B).  n == 0 means every tile in order (a whole-state load).  Source
+// tile i*H + h (i-th listed sequence, head h) lands in tile slot[i]*H + h.
+constexpr int SLOT_CHUNK = 256;
+struct SlotMap {
+    int n;
+    int H;
+    int32_t slot[SLOT_CHUNK];
+};
+
 // Arguments of the replay step kernels (decode, explicit flush, spec append).
 // All buffer arrays hold two banks; the bank of a sequence is fc & 1 and a
 // flush moves the sequence to the other bank, so the entries a fold reads are
@@ -49,6 +60,7 @@ struct StepArgs {
     const float* A;          // Mamba-2 A [H]
     const float* D;          // Mamba-2 D [H]
     void* y;                 // outputs [T][B][H][C]
+    const uint8_t* active;   // [B] nonzero = the sequence takes part in the step (null = all)
 };
 
 // One translation unit per checkpoint dtype (mamba2.hip / mamba2_f16.hip, ...).
@@ -63,11 +75,18 @@ hipError_t launch_gdn_step_fp8(const StepArgs& a, int io, int rc, hipStream_t s)
 hipError_t launch_book_commit(int32_t* book, uint32_t* err, int B, int parity,
                               const int32_t* accepted, hipStream_t s);
 hipError_t launch_book_reset(int32_t* book, uint32_t* err, int B, int parity, int cap, bool stagger, hipStream_t s);
+// len = pend = fc = 0 and lim = cap for the listed sequences only (error word untouched).
+hipError_t launch_book_reset_slots(int32_t* book, int B, int parity, int cap, const SlotMap& m, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_tiles_to_logical(const void* ckpt, void* out, int tiles, int C, int R, int ck, hipStream_t s);
-hipError_t launch_logical_to_tiles(const void* in, void* ckpt, int tiles, int C, int R, int ck, hipStream_t s);
+// Logical source tiles (`tiles` of them, in the checkpoint dtype, or fp32 when
+// src_f32 -- then rounded on the device to the checkpoint dtype: binary16 RNE,
+// or E4M3 RNE saturating at +-448) into the fragment-ordered checkpoint, at the
+// tiles `m` names.
+hipError_t launch_logical_to_tiles(const void* in, void* ckpt, int tiles, int C, int R, int ck, bool src_f32,
+                                   const SlotMap& m, hipStream_t s);
 hipError_t launch_quantize_read_copy(void* ckpt, uint8_t* codes, uint8_t* scales, int tiles,
-                                     int C, int R, int rc, int ck, bool round_ckpt, hipStream_t s);
+                                     int C, int R, int rc, int ck, bool round_ckpt, const SlotMap& m, hipStream_t s);
 hipError_t launch_read_copy_to_logical(const uint8_t* codes, const uint8_t* scales, uint8_t* codes_out,
                                        uint8_t* scales_out, int tiles, int C, int R, int rc, hipStream_t s);
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t s);

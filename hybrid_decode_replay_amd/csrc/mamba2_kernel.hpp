@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256, NB <= 8 ? 6 : 4) void mamba2_step_kernel(StepA
 
     // ---- bookkeeping: identical decision in every workgroup of sequence b
     const StepPlan p = plan_step(a, b, h == 0 && tix.sp == 0 && tid == 0);
-    if (a.mode == MODE_FLUSH && p.f == 0) return;
+    if (p.skip || (a.mode == MODE_FLUSH && p.f == 0)) return;
     const int f = p.f, len = p.len, T = a.T;
 
     // ---- LDS partition (floats; the launch sizes cs for max(T, 1) rows)

@@ -222,8 +222,12 @@ __device__ __forceinline__ void stage_append(const StageGeom& G, void* bufc, voi
 //   flush   fold the len committed entries.
 //   spec    len + T > cap: fold the committed prefix before the drafts.
 // After a fold the window limit is cap.
+// A sequence the step's active mask leaves out (decode and spec only) takes no
+// part: nothing is appended, folded or written for it, and its bookkeeping is
+// carried into the other copy unchanged (skip; the workgroup then returns).
 struct StepPlan {
     int len, fc, f, V, bank, bank_new;
+    bool skip;
 };
 
 __device__ __forceinline__ StepPlan plan_step(const StepArgs& a, int b, bool writer)
@@ -234,6 +238,20 @@ __device__ __forceinline__ StepPlan plan_step(const StepArgs& a, int b, bool wri
     p.len = min(max(bk[b], 0), a.cap);   // invariant 0 <= len <= cap; clamped so that a
     p.fc = bk[2 * sB + b];               // corrupted word cannot index out of bounds
     const int lim = min(max(bk[3 * sB + b], 1), a.cap);
+    p.skip = a.active != nullptr && a.mode != MODE_FLUSH && a.active[b] == 0;
+    if (p.skip) {
+        if (writer) {
+            int32_t* nbk = a.book + (size_t)(a.parity ^ 1) * 4 * sB;
+            nbk[b] = p.len;
+            nbk[sB + b] = 0;
+            nbk[2 * sB + b] = p.fc;
+            nbk[3 * sB + b] = lim;
+        }
+        p.f = 0;
+        p.V = p.len;
+        p.bank = p.bank_new = p.fc & 1;
+        return p;
+    }
     int folds;
     if (a.mode == MODE_DECODE) {
         if (p.len + 1 > a.cap) {          // forced: the buffer is full

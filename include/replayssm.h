@@ -175,7 +175,8 @@ size_t replay_state_bytes(const replay_config *cfg);
  * caller and must outlive the handle. */
 replay_status replay_state_alloc(const replay_config *cfg, void *dev_mem, size_t bytes,
                                  void *stream, replay_state **out);
-/* Frees the host handle only. */
+/* Frees the host handle only.  REPLAY_ERR_STATE while the state is bound to a
+ * stack (free the stack first). */
 replay_status replay_state_free(replay_state *st);
 replay_status replay_state_layout(const replay_state *st, replay_layout *out);
 /* Host-side phase: 0 = idle, 1 = drafts pending. */
@@ -189,6 +190,28 @@ int32_t replay_state_phase(const replay_state *st);
  * buffer and resets len = pend = fc = 0 and the error word.  Not allowed
  * while drafts are pending. */
 replay_status replay_load_checkpoint(replay_state *st, const void *S_logical, void *stream);
+/* As replay_load_checkpoint, from an fp32 logical checkpoint [B][H][rows][cols]
+ * (device) whatever the state's ckpt_dtype: the library rounds each value on
+ * the device with the encoder its folds use -- IEEE binary16 round to nearest
+ * even (overflow to +-inf) for REPLAY_F16; OCP E4M3 round to nearest even,
+ * finite and infinite magnitudes beyond 448 saturated to +-448, NaN to 0x7f
+ * for REPLAY_FP8_E4M3 ([TR] "Kuantizasyon hatasinin sinirlandirilmasi": FP16
+ * or FP8 recurrence).  For an fp32 checkpoint it equals replay_load_checkpoint. */
+replay_status replay_load_checkpoint_f32(replay_state *st, const float *S_logical, void *stream);
+/* Per-sequence arrival: a prefill hands over the state of n sequences, which
+ * (re)occupy batch slots slots[0..n-1] (HOST int32 array; distinct, each in
+ * [0, B), 1 <= n <= B, else REPLAY_ERR_ARG).  S_logical (device fp32
+ * [n][H][rows][cols], slot i's checkpoint at index i) is rounded to the
+ * ckpt_dtype as in replay_load_checkpoint_f32 and becomes those sequences'
+ * checkpoint; their read copy is refreshed, their buffer emptied and their
+ * len = pend = fc = 0 with a full window of buf_cap entries (also under
+ * REPLAY_FLAG_STAGGER_FLUSH: an arrival's window already starts at its own
+ * time).  Every other sequence keeps its checkpoint, buffer and bookkeeping;
+ * the error word is kept.  Not allowed while drafts are pending ([DE] "Warum
+ * es wichtig ist": the gain comes from many concurrent sequences; [TR]
+ * "ReplaySSM nasil calisir?": every sequence flushes its own buffer). */
+replay_status replay_load_slots(replay_state *st, int32_t n, const int32_t *slots, const float *S_logical,
+                                void *stream);
 /* Writes the current checkpoint (not including buffered tokens) in logical
  * layout and ckpt_dtype to S_out (device). */
 replay_status replay_read_checkpoint(const replay_state *st, void *S_out, void *stream);
@@ -211,6 +234,14 @@ replay_status replay_read_book(const replay_state *st, int32_t *book_out, uint32
  * Outputs y [1][B][H][P] (Mamba-2) or [1][B][H][DV] (GDN) in io_dtype.
  * Not allowed while drafts are pending. */
 replay_status replay_decode_step(replay_state *st, const replay_inputs *in, void *y, void *stream);
+/* replay_decode_step for the sequences whose active[b] (device uint8 [B]) is
+ * nonzero.  A sequence with active[b] == 0 sits the step out: nothing is
+ * appended to its buffer, nothing is folded or written for it, its rows of y
+ * are left as they were and its len, fc and window are unchanged (departed or
+ * idle slots of a serving batch).  The mask is read by the step's kernel on
+ * `stream`. */
+replay_status replay_decode_step_masked(replay_state *st, const replay_inputs *in, const uint8_t *active, void *y,
+                                        void *stream);
 /* Folds every non-empty buffer into its checkpoint (one write per sequence
  * that had entries); len = 0.  Uses only in->A (Mamba-2).  Not allowed while
  * drafts are pending. */
@@ -222,6 +253,12 @@ replay_status replay_flush(replay_state *st, const replay_inputs *in, void *stre
  * 1 <= k <= buf_cap (else REPLAY_ERR_CAPACITY) and no pending drafts. */
 replay_status replay_spec_append(replay_state *st, int32_t k, const replay_inputs *drafts,
                                  void *y, void *stream);
+/* replay_spec_append for the sequences whose active[b] is nonzero (device
+ * uint8 [B]); the others append no drafts (pend stays 0, so their accepted
+ * count must be 0 at the commit), write no outputs and keep their buffer and
+ * bookkeeping.  The drafts are pending for the whole state afterwards. */
+replay_status replay_spec_append_masked(replay_state *st, int32_t k, const replay_inputs *drafts,
+                                        const uint8_t *active, void *y, void *stream);
 /* accepted: device int32 [B].  len += clamp(accepted[b], 0, pend); pend = 0.
  * A clamped value sets REPLAY_DEVERR_COMMIT_CLAMPED.  Moves no state bytes.
  * Requires pending drafts. */
@@ -265,6 +302,15 @@ replay_status replay_stack_free(replay_stack *stk);
  * layer's ckpt_dtype), refreshes read copies and resets the shared
  * bookkeeping.  Not allowed mid-step or while drafts are pending. */
 replay_status replay_stack_load(replay_stack *stk, const void *const *S_logical, void *stream);
+/* As replay_stack_load from fp32 logical checkpoints, rounded by the library
+ * (replay_load_checkpoint_f32). */
+replay_status replay_stack_load_f32(replay_stack *stk, const float *const *S_logical, void *stream);
+/* Per-sequence arrival for every layer (replay_load_slots): S_logical[l] is
+ * layer l's device fp32 [n][H_l][rows_l][cols_l]; the shared bookkeeping of the
+ * listed slots is reset once.  Not allowed mid-step or while drafts are
+ * pending. */
+replay_status replay_stack_load_slots(replay_stack *stk, int32_t n, const int32_t *slots,
+                                      const float *const *S_logical, void *stream);
 /* Layer `layer`'s decode step (as replay_decode_step).  Must be the next
  * layer of the current step. */
 replay_status replay_stack_decode_layer(replay_stack *stk, int32_t layer, const replay_inputs *in,
@@ -274,6 +320,14 @@ replay_status replay_stack_decode_layer(replay_stack *stk, int32_t layer, const 
  * pending for the whole stack. */
 replay_status replay_stack_spec_layer(replay_stack *stk, int32_t layer, int32_t k,
                                       const replay_inputs *drafts, void *y, void *stream);
+/* Masked variants (replay_decode_step_masked, replay_spec_append_masked):
+ * every layer of one step must pass the same `active` pointer (else
+ * REPLAY_ERR_STATE), and its contents must not change during the step. */
+replay_status replay_stack_decode_layer_masked(replay_stack *stk, int32_t layer, const replay_inputs *in,
+                                               const uint8_t *active, void *y, void *stream);
+replay_status replay_stack_spec_layer_masked(replay_stack *stk, int32_t layer, int32_t k,
+                                             const replay_inputs *drafts, const uint8_t *active, void *y,
+                                             void *stream);
 /* Folds every non-empty buffer of every layer (in[l] as for replay_flush;
  * in may be NULL for an all-GDN stack). */
 replay_status replay_stack_flush(replay_stack *stk, const replay_inputs *const *in, void *stream);

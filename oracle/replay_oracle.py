@@ -44,6 +44,19 @@ Two parts:
   after a load lim = 1 + (b mod cap) for sequence b, after any flush lim = cap,
   and the decode rule "if len == cap afterwards" reads "if len >= lim".
 
+  Ragged serving batches (the pages' gain comes from many concurrent
+  sequences, [DE] "Warum es wichtig ist", and every sequence flushes its own
+  buffer, [TR] "ReplaySSM nasil calisir?"; the operations below are the
+  plainest reading of sequences joining and leaving a batch):
+    decode / spec with an active mask
+                only the marked sequences take the operation; the others keep
+                their state, buffer and (len, fc, lim), and take no drafts
+                (pend stays 0).
+    load_slots(slots, S)
+                the listed sequences take new checkpoints (rounded as a load
+                rounds them), with an empty buffer, len = pend = fc = 0 and a
+                full window lim = cap; the others keep everything.
+
 The pages leave the following open; the readings taken here are listed with
 the design notes: when the flush happens (on the filling step), whether the
 output includes the current token (yes), the overflow rule for drafts (forced
@@ -270,7 +283,8 @@ class _Session:
 
     kind = None
 
-    def __init__(self, batch, cap, S0, read_copy=None, quantized_ckpt=False, ckpt_dtype="f32", stagger=False):
+    def __init__(self, batch, cap, S0, read_copy=None, quantized_ckpt=False, ckpt_dtype="f32", stagger=False,
+                 seq_ids=None):
         if not 1 <= cap <= 16:
             raise ValueError("buffer capacity must be in [1, 16]")
         if quantized_ckpt and read_copy is None:
@@ -288,6 +302,11 @@ class _Session:
         self.ckpt_dtype = ckpt_dtype
         self.rounds = quantized_ckpt or ckpt_dtype != "f32"    # folds land on a coarser grid
         self.stagger = stagger
+        # batch index of each sequence held here (a session may hold a sample of a batch);
+        # the staggered first window depends on it
+        self.seq_ids = np.arange(batch) if seq_ids is None else np.asarray(seq_ids, np.int64)
+        if self.seq_ids.shape != (batch,):
+            raise ValueError("one batch index per sequence")
         self.S = self._round(np.array(S0, np.float64, copy=True))   # committed state
         self.ckpt = self.S.copy()                              # image at last flush
         self.len = np.zeros(batch, np.int32)
@@ -303,7 +322,7 @@ class _Session:
     # -- helpers -----------------------------------------------------------
     def _first_limits(self):
         if self.stagger:
-            return (1 + np.arange(self.B) % self.cap).astype(np.int32)
+            return (1 + self.seq_ids % self.cap).astype(np.int32)
         return np.full(self.B, self.cap, np.int32)
 
     def trace(self):
@@ -343,7 +362,7 @@ class _Session:
 
     # -- operations --------------------------------------------------------
     def load(self, S0):
-        if self.pend.any():
+        if self._drafts is not None:
             raise PhaseError("load while drafts are pending")
         self.S = self._round(np.array(S0, np.float64, copy=True))
         self.ckpt = self.S.copy()
@@ -355,21 +374,31 @@ class _Session:
         self.hist = [[] for _ in range(self.B)]
         self.nops += 1
 
-    def decode(self, inp):
-        if self.pend.any():
+    def _mask(self, active):
+        if active is None:
+            return np.ones(self.B, bool)
+        active = np.asarray(active, bool)
+        if active.shape != (self.B,):
+            raise ValueError("the active mask has one entry per sequence")
+        return active
+
+    def decode(self, inp, active=None):
+        """One decode token for the sequences `active` marks (all by default).  Outputs of
+        the others are zero here (the GPU leaves their rows untouched)."""
+        if self._drafts is not None:
             raise PhaseError("decode while drafts are pending")
-        forced = self.len + 1 > self.cap
+        act = self._mask(active)
+        forced = act & (self.len + 1 > self.cap)
         self._flush_rows(forced)
-        y = self._token(self.S, inp)
-        self.len += 1
-        full = self.len >= self.lim
+        y = self._token(self.S, inp, act.astype(np.uint8))
+        self.len += act.astype(np.int32)
+        full = act & (self.len >= self.lim)
         if self.read_copy:
-            no_flush = ~(forced | full)
+            no_flush = act & ~(forced | full)
             for b in np.flatnonzero(no_flush):
                 y[b] = self._read_copy_output(b, inp)
-        for b in range(self.B):
-            if not full[b]:
-                self.hist[b].append(self._slice(inp, b))
+        for b in np.flatnonzero(act & ~full):
+            self.hist[b].append(self._slice(inp, b))
         self._flush_rows(full)
         if self.rounds:
             for b in np.flatnonzero(full):
@@ -378,26 +407,30 @@ class _Session:
         return y
 
     def flush(self):
-        if self.pend.any():
+        if self._drafts is not None:
             raise PhaseError("flush while drafts are pending")
         self._flush_rows(self.len > 0)
         self.nops += 1
 
-    def spec_append(self, drafts):
-        """drafts: list of k per-token input dicts.  Returns outputs [k] of arrays."""
+    def spec_append(self, drafts, active=None):
+        """drafts: list of k per-token input dicts.  Returns outputs [k] of arrays (zero for
+        sequences `active` leaves out; they take no drafts)."""
         k = len(drafts)
-        if self.pend.any():
+        if self._drafts is not None:
             raise PhaseError("spec_append while drafts are pending")
         if not 1 <= k <= self.cap:
             raise ValueError("draft count out of range")
-        pre = self.len + k > self.cap
+        act = self._mask(active)
+        pre = act & (self.len + k > self.cap)
         self._flush_rows(pre)
         S = self.S.copy()
         outs = []
         for j, inp in enumerate(drafts):
-            y = self._token(S, inp)
+            y = self._token(S, inp, act.astype(np.uint8))
             if self.read_copy:
-                for b in np.flatnonzero(~pre):
+                # a sequence whose committed prefix was not folded reads the copy of its
+                # checkpoint, replays its committed history, then drafts 0..j
+                for b in np.flatnonzero(act & ~pre):
                     Sq = read_copy_values(self.ckpt[b:b + 1], self.read_copy).copy()
                     for past in self.hist[b]:
                         self._token(Sq, past)
@@ -406,9 +439,28 @@ class _Session:
                     y[b] = yq[0]
             outs.append(y)
         self._drafts = list(drafts)
-        self.pend[:] = k
+        self.pend[:] = np.where(act, k, 0)
         self.nops += 1
         return outs
+
+    def load_slots(self, slots, S_new):
+        """Sequences `slots` take the checkpoints S_new [n, ...] (rounded as a load rounds them),
+        with an empty buffer, len = pend = fc = 0 and a full window; the others keep theirs."""
+        if self._drafts is not None:
+            raise PhaseError("load while drafts are pending")
+        slots = [int(b) for b in slots]
+        if len(set(slots)) != len(slots) or any(not 0 <= b < self.B for b in slots):
+            raise ValueError("slots must be distinct sequence indices")
+        S_new = np.asarray(S_new, np.float64)
+        for i, b in enumerate(slots):
+            self.S[b] = self._round(S_new[i:i + 1].copy())[0]
+            self.ckpt[b] = self.S[b]
+            self.len[b] = 0
+            self.pend[b] = 0
+            self.fc[b] = 0
+            self.lim[b] = self.cap
+            self.hist[b] = []
+        self.nops += 1
 
     def commit(self, accepted):
         if self._drafts is None:
@@ -438,10 +490,11 @@ class Mamba2Session(_Session):
 
     kind = "mamba2"
 
-    def __init__(self, A, D, S0, cap=16, read_copy=None, quantized_ckpt=False, ckpt_dtype="f32", stagger=False):
+    def __init__(self, A, D, S0, cap=16, read_copy=None, quantized_ckpt=False, ckpt_dtype="f32", stagger=False,
+                 seq_ids=None):
         self.A = np.asarray(A, np.float64)
         self.D = np.asarray(D, np.float64)
-        super().__init__(np.asarray(S0).shape[0], cap, S0, read_copy, quantized_ckpt, ckpt_dtype, stagger)
+        super().__init__(np.asarray(S0).shape[0], cap, S0, read_copy, quantized_ckpt, ckpt_dtype, stagger, seq_ids)
 
     def _token(self, S, inp, active=None):
         return mamba2_token(S, inp["x"], inp["Bm"], inp["Cm"], inp["dt"], self.A, self.D, active)
@@ -460,9 +513,10 @@ class GDNSession(_Session):
 
     kind = "gdn"
 
-    def __init__(self, S0, cap=16, scale=1.0, read_copy=None, quantized_ckpt=False, ckpt_dtype="f32", stagger=False):
+    def __init__(self, S0, cap=16, scale=1.0, read_copy=None, quantized_ckpt=False, ckpt_dtype="f32", stagger=False,
+                 seq_ids=None):
         self.scale = float(scale)
-        super().__init__(np.asarray(S0).shape[0], cap, S0, read_copy, quantized_ckpt, ckpt_dtype, stagger)
+        super().__init__(np.asarray(S0).shape[0], cap, S0, read_copy, quantized_ckpt, ckpt_dtype, stagger, seq_ids)
 
     def _token(self, S, inp, active=None):
         return gdn_token(S, inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], self.scale, active)
@@ -513,17 +567,26 @@ class StackSession:
         if self.next:
             raise PhaseError(f"{what} in the middle of a step")
 
-    def decode_layer(self, layer, inp):
-        self._enter(layer, ("decode", 1))
-        y = self.layers[layer].decode(inp)
+    @staticmethod
+    def _mask_key(active):
+        return None if active is None else np.asarray(active, bool).tobytes()
+
+    def decode_layer(self, layer, inp, active=None):
+        self._enter(layer, ("decode", 1, self._mask_key(active)))
+        y = self.layers[layer].decode(inp, active)
         self._leave()
         return y
 
-    def spec_layer(self, layer, drafts):
-        self._enter(layer, ("spec", len(drafts)))
-        ys = self.layers[layer].spec_append(drafts)
+    def spec_layer(self, layer, drafts, active=None):
+        self._enter(layer, ("spec", len(drafts), self._mask_key(active)))
+        ys = self.layers[layer].spec_append(drafts, active)
         self._leave()
         return ys
+
+    def load_slots(self, slots, checkpoints):
+        self._idle("load")
+        for s, S in zip(self.layers, checkpoints, strict=True):
+            s.load_slots(slots, S)
 
     def flush(self):
         self._idle("flush")

@@ -13,9 +13,10 @@ every flush.  Checked here:
   * the first fold: every code equal to the oracle's, except where the oracle's
     exact fold result lies within fp32 rounding of an E4M3 midpoint -- there the
     two codes are neighbours;
-  * longer runs with spec, commit, rollback and flush: checkpoints one E4M3
-    step at most from the oracle's, rarely (tests/harness.py), outputs within
-    tolerance wherever the checkpoint matched; bookkeeping bit-exact;
+  * longer runs with spec, commit, rollback and flush: checkpoints within the
+    element-wise bound derived in tests/harness.py (Fp8Bound) and rarely
+    different at all, outputs within the io tolerance plus the read-out of the
+    measured checkpoint difference; bookkeeping bit-exact;
   * an MXFP4 copy is the quantization of exactly the stored FP8 values;
   * the conventional baseline with an FP8 state.
 Bit-exact agreement on inputs that make all arithmetic exact is in
@@ -199,27 +200,33 @@ def test_fp8_flags_rejected():
 def test_conventional_fp8_state(kind, C, R):
     """Conventional decoding on an FP8 state vs the oracle's per-token step on an fp64 state
     rounded to E4M3 after every token (outputs from the unrounded update on both sides).
-    The first token starts from identical values: outputs within 1e-4.  An element first
-    differs by one E4M3 step (the two updates straddle a rounding midpoint), rarely; a
-    (b, h) matrix that ever differed is marked and carries its own history from then on
-    (a one-step difference decayed into a finer binade spans two steps there; in GDN the
-    row's k.s couples its elements), so it is held to one coarse step normwise
-    (FP8_TOL_MARKED, as for the replay path); outputs of unmarked matrices stay within
-    1e-4."""
-    from harness import FP8_TOL_MARKED, e4m3_grid_index
+    Both start from the same E4M3 values.  Every token rounds the state on both sides, so the
+    element-wise bound of tests/harness.py (Fp8Bound) is advanced once per token: a
+    difference is carried by the update (Mamba-2 decay <= 1 per element; GDN a product of
+    factors of 2-norm <= 1 per row) and each rounding may add about one E4M3 step.  The
+    outputs, read from the unrounded update, may differ by the read-out of the previous
+    state difference (readout_bound) beyond 1e-4 of the vector's norm; at most 1e-3 of the
+    codes may differ."""
+    from harness import Fp8Bound, readout_bound
     from oracle import replay_oracle as ro
     b = rb()
     B, H, T = 3, 2, 6
     cfg = b.make_config(_kind(kind), B, H, H, C, R, 16, b.F32, ckpt_dtype=b.FP8_E4M3)
     S0 = synth.checkpoint(42, (B, H, C, R), std=0.5)
     Sref = ro.e4m3_decode(ro.e4m3_encode(S0)).reshape(S0.shape)
-    S = torch.from_numpy(Sref.astype(np.float32)).to(torch.float8_e4m3fn).cuda()
+    # the conventional state in the checkpoint dtype, made by the library's own load rounding
+    st = b.ReplayState(b.make_config(_kind(kind), B, H, H, C, R, 16, b.F32, ckpt_dtype=b.FP8_E4M3))
+    st.load_checkpoint(torch.from_numpy(S0).cuda())
+    S = st.read_checkpoint()
+    torch.cuda.synchronize()
+    assert np.array_equal(ro.e4m3_decode(S.view(torch.uint8).cpu().numpy()).reshape(S0.shape), Sref)
     toks = _tokens(kind, 42, T, B, H, H, C, R)
     params, A, D = {}, None, None
     if kind == "mamba2":
         A, D = synth.mamba2_params(42, H)
         params = {"A": torch.from_numpy(A).cuda(), "D": torch.from_numpy(D).cuda()}
-    marked = np.zeros((B, H), bool)
+    bound = Fp8Bound(kind, (B, H, C, R))
+    dS = np.zeros((B, H, C, R))
     for t in range(T):
         tok = synth.token(toks, t)
         y = b.conv_decode_step(cfg, S, {k: torch.from_numpy(v).cuda() for k, v in tok.items()}, params)
@@ -230,15 +237,9 @@ def test_conventional_fp8_state(kind, C, R):
         Sref[...] = ro.e4m3_decode(ro.e4m3_encode(Sref)).reshape(Sref.shape)
         torch.cuda.synchronize()
         yg = y[0].float().cpu().numpy().astype(np.float64)
-        err = np.max(np.abs(yg - yr), axis=-1) / np.maximum(np.max(np.abs(yr), axis=-1), 1e-30)
-        assert np.max(err[~marked], initial=0.0) <= 1e-4, (t, err)
+        allow = 1e-4 * np.max(np.abs(yr), axis=-1, keepdims=True) + readout_bound(kind, dS, [tok])[0]
+        over = np.abs(yg - yr) > allow
+        assert not over.any(), (t, int(over.sum()))
+        bound.advance(np.ones(B, bool), Sref)
         Sg = ro.e4m3_decode(S.view(torch.uint8).cpu().numpy()).reshape(Sref.shape)
-        diff = Sg != Sref
-        fresh = diff & ~marked[:, :, None, None]
-        if fresh.any():
-            assert np.all(np.abs(e4m3_grid_index(Sg[fresh]) - e4m3_grid_index(Sref[fresh])) == 1), t
-        if marked.any():
-            dm = np.max(np.abs(Sg - Sref), axis=(2, 3)) / np.maximum(np.max(np.abs(Sref), axis=(2, 3)), 1e-30)
-            assert np.max(dm[marked]) <= FP8_TOL_MARKED, (t, np.max(dm[marked]))
-        assert diff.mean() <= 1e-3, (t, diff.mean())
-        marked |= diff.any(axis=(2, 3))
+        dS, _ = bound.check(Sg, Sref, f"token {t}")

@@ -132,7 +132,7 @@ def test_phase_rules_and_capacity():
     st.spec_append(1, tok, params)
     assert st.phase() == 1
     for fn in (lambda: st.decode(tok, params), lambda: st.flush(params), lambda: st.spec_append(1, tok, params),
-               lambda: st.load_checkpoint(torch.zeros(st.ckpt_shape))):
+               lambda: st.load_checkpoint(torch.zeros(st.ckpt_shape, device="cuda"))):
         with pytest.raises(b.ReplayError) as e:
             fn()
         assert e.value.status == b.ERR_STATE
