@@ -43,14 +43,29 @@ The JSON line also carries:
 With --sweep FILE, both layers are also timed at batch 1..512 (replay and
 conventional, eagerly and as HIP-graph replays), one JSON line per point in FILE.
 
-Timing: `value` and `ms_per_step` come from K steps launched back to back
-between two events; the per-launch durations behind `roofline` come from a
-second pass of K steps with an event pair around every launch.
+Timing.  Every decode timing starts with the W warm-up steps, then untimed
+steps up to the next 16-step window boundary and two more full windows (so the
+timed region starts warm and at a window boundary; the count is in the line as
+`untimed_steps_before_timed_region`).  `value` and `ms_per_step` come from
+exactly K steps launched back to back between two events on the launch stream.
+`roofline.achieved` comes from a separate back-to-back pass over four whole
+windows (64 steps: 60 non-fold and 4 fold steps), so its per-launch time has
+the fold fraction the per-window algorithmic bytes assume, whatever K is; no
+event sits between those launches.  A third pass with an event pair around each
+launch gives the fold / non-fold split and the launch-time percentiles.
+
+Working sets below 512 MiB per step (the batch sweep's small batches, the
+batch-128 read copies) are decoded round-robin over several copies of the layer
+state (`rotate`), so that a launch never finds its checkpoint or copy in the
+256 MiB Infinity Cache left there by the previous launch.
+
+Measured traffic comes from the committed rocprofv3 byte-counter summaries in
+profiles/ (FETCH_SIZE + WRITE_SIZE, calibrated on a streaming copy of known
+size), used only while the kernel sources still hash to the profiled version.
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -60,26 +75,28 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "mamba2_step_b256_traffic.txt")  # written by profsum
-KERNEL_SOURCES = [os.path.join(ROOT, "hybrid_decode_replay_amd", "csrc", f)
-                  for f in ("mamba2_kernel.hpp", "mamba2.hip", "ckpt.hpp", "common.hpp", "stage.hpp", "rc.hpp")]
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC = {("mamba2", "replay"): "mamba2_step_b256_traffic.txt", ("mamba2", "conv"): "conv_step_mamba2_b256_traffic.txt",
+           ("gdn", "replay"): "gdn_step_b256_traffic.txt", ("gdn", "conv"): "conv_step_gdn_b256_traffic.txt"}
 
 MAMBA2 = dict(H=128, G=8, C=64, R=128)     # heads, groups, head dim P, state dim N
 GDN = dict(H=32, G=32, C=128, R=128)       # heads, q/k heads, d_v, d_k
+ROTATE_MIN_BYTES = 512 << 20
 
 
-def algorithmic_bytes(kind, H, G, C, R, cap=16, io_bytes=2, read_copy=None, ckpt_bytes=4):
-    """(replay, conventional) bytes per sequence-token.
+def traffic_model(kind, H, G, C, R, cap=16, io_bytes=2, read_copy=None, ckpt_bytes=4):
+    """Algorithmic bytes per sequence-token, by part: (replay, conventional) dicts.
 
-    Replay, averaged over a full window of `cap` steps with lockstep flushes: the
-    checkpoint is read every step and written once per window; the current inputs are
-    read; the new entry is written; on average (cap-1)/2 prior entries are read; the
-    output is written.  With a read copy, the cap-1 non-flush steps read the copy and
-    the flush step reads and writes the checkpoint and writes the copy: per token copy +
-    S/8 in place of S + S/cap.  Conventional: state read and written every token,
-    inputs, output.  Entries: Mamba-2 x, B, dt; GDN k, v and the fp32 gates.  S is the
-    checkpoint (and conventional state) at ckpt_bytes per element."""
-    S = H * C * R * ckpt_bytes
+    Replay, averaged over a full window of `cap` steps with lockstep flushes: the checkpoint
+    is read every step and written once per window ("ckpt"); the new entry is written and on
+    average (cap-1)/2 prior entries are read ("buffer"); the current inputs are read and the
+    output written ("io").  With a read copy the cap-1 non-flush steps read the copy and the
+    flush step reads and writes the checkpoint and writes the copy.  Conventional: the state
+    is read and written every token ("state"), plus the same io.  Entries: Mamba-2 x, B, dt;
+    GDN k, v and the fp32 gates.  S is the checkpoint (and conventional state) at
+    ckpt_bytes per element."""
+    n = H * C * R
+    S = n * ckpt_bytes
     if kind == "mamba2":
         entry = (H * C + G * R + H) * io_bytes
         inp = (H * C + 2 * G * R + H) * io_bytes
@@ -87,71 +104,141 @@ def algorithmic_bytes(kind, H, G, C, R, cap=16, io_bytes=2, read_copy=None, ckpt
         entry = (H * C + G * R) * io_bytes + 2 * H * 4
         inp = (H * C + 2 * G * R) * io_bytes + 2 * H * 4
     out = H * C * io_bytes
-    state = S + S / cap
+    ckpt = S + S / cap
     if read_copy is not None:
-        n = H * C * R
         copy = n if read_copy == "fp8" else n / 2 + n / 32
-        state = (cap - 1) / cap * copy + 2 * S / cap + copy / cap
-    replay = state + inp + entry + (cap - 1) / 2 * entry + out
-    conv = 2 * S + inp + out
+        ckpt = (cap - 1) / cap * copy + 2 * S / cap + copy / cap
+    replay = {"ckpt": ckpt, "buffer": entry + (cap - 1) / 2 * entry, "io": inp + out}
+    conv = {"state": 2 * S, "io": inp + out}
     return replay, conv
 
 
-def kernel_source_sha():
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+def algorithmic_bytes(kind, H, G, C, R, cap=16, io_bytes=2, read_copy=None, ckpt_bytes=4):
+    """(replay, conventional) bytes per sequence-token (the sums of traffic_model)."""
+    rep, conv = traffic_model(kind, H, G, C, R, cap, io_bytes, read_copy, ckpt_bytes)
+    return sum(rep.values()), sum(conv.values())
 
 
-def read_traffic():
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
-    the current kernel source (else None)."""
-    if not os.path.exists(PROFILE_TRAFFIC):
+def reductions(rep, conv):
+    """Replay-vs-conventional traffic reduction under three accountings (1 - replay/conv):
+    all bytes; state + buffer bytes (io excluded on both sides); checkpoint only (the
+    buffer also excluded on the replay side)."""
+    return {"all_bytes": round(1 - (rep["ckpt"] + rep["buffer"] + rep["io"]) / (conv["state"] + conv["io"]), 4),
+            "state_and_buffer": round(1 - (rep["ckpt"] + rep["buffer"]) / conv["state"], 4),
+            "checkpoint_only": round(1 - rep["ckpt"] / conv["state"], 4)}
+
+
+def read_traffic(name):
+    """Window bytes per launch from a committed rocprofv3 counter summary in profiles/, if it
+    was taken on the current kernel source (else None)."""
+    from hybrid_decode_replay_amd import profsum
+    path = os.path.join(PROFILES, name)
+    if not os.path.exists(path):
         return None
     kv = {}
-    with open(PROFILE_TRAFFIC) as f:
+    with open(path) as f:
         for line in f:
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha") != kernel_source_sha():
-        return None
     try:
-        return float(kv["traffic_bytes_per_launch"])
-    except (KeyError, ValueError):
+        if kv.get("kernel_source_sha") != profsum.source_sha(kv["kernel"].split("<")[0]):
+            return None
+        return float(kv.get("window_traffic_bytes_per_launch", kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError, OSError):
         return None
 
 
-def cpu_baseline(H, G, P, N, budget_s=10.0, max_s=30.0):
-    """The fp64 oracle (ordinary decoding, OpenMP over (sequence, head)) on a bounded sample of
-    the headline layer shape: 64 sequences (512 MiB of fp64 state, beyond any host cache),
-    steps in chunks of 4 until >= budget_s of CPU time."""
+def measured_reduction(kind, B, rep_model, conv_model):
+    """The replay-vs-conventional reduction from the measured counter bytes of both kernels
+    (batch-256 layers), with the same three accountings; the io and buffer parts removed for
+    the narrower ones are the algorithmic ones (the counters see only totals)."""
+    r, c = read_traffic(TRAFFIC[(kind, "replay")]), read_traffic(TRAFFIC[(kind, "conv")])
+    if r is None or c is None:
+        return None
+    r, c = r / B, c / B
+    io, buf = rep_model["io"], rep_model["buffer"]
+    return {"replay_bytes_per_token": round(r), "conventional_bytes_per_token": round(c),
+            "all_bytes": round(1 - r / c, 4),
+            "state_and_buffer": round(1 - (r - io) / (c - conv_model["io"]), 4),
+            "checkpoint_only": round(1 - (r - io - buf) / (c - conv_model["io"]), 4),
+            "source": f"profiles/{TRAFFIC[(kind, 'replay')]}, profiles/{TRAFFIC[(kind, 'conv')]} "
+                      "(FETCH_SIZE + WRITE_SIZE per launch, 15:1 non-fold:fold window; io and buffer parts "
+                      "algorithmic)"}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rate(kind, nseq, budget_s, seed):
+    """Tokens/s of the fp64 oracle (ordinary decoding) on nseq sequences of a layer shape."""
     import numpy as np
     from hybrid_decode_replay_amd import synth
     from oracle import replay_oracle as ro
-    nseq, chunk = 64, 4
-    A, D = synth.mamba2_params(1, H)
-    S = synth.checkpoint(1, (nseq, H, P, N)).astype(np.float64)
-    elapsed, tokens, steps, c = 0.0, 0, 0, 0
-    while elapsed < budget_s and elapsed < max_s:
-        toks = synth.mamba2_tokens(100 + c, chunk, nseq, H, G, P, N, dtype="bf16")
+    shp = MAMBA2 if kind == "mamba2" else GDN
+    H, G, C, R = shp["H"], shp["G"], shp["C"], shp["R"]
+    chunk = 4
+    S = synth.checkpoint(seed, (nseq, H, C, R)).astype(np.float64)
+    A, D = synth.mamba2_params(seed, H)
+    elapsed, steps, c = 0.0, 0, 0
+    while elapsed < budget_s:
+        if kind == "mamba2":
+            toks = synth.mamba2_tokens(100 + c, chunk, nseq, H, G, C, R, dtype="bf16")
+        else:
+            toks = synth.gdn_tokens(100 + c, chunk, nseq, H, G, R, C, dtype="bf16")
         toks = {k: v.astype(np.float64) for k, v in toks.items()}
         t0 = time.perf_counter()
         for t in range(chunk):
-            ro.mamba2_token(S, toks["x"][t], toks["Bm"][t], toks["Cm"][t], toks["dt"][t], A, D)
+            if kind == "mamba2":
+                ro.mamba2_token(S, toks["x"][t], toks["Bm"][t], toks["Cm"][t], toks["dt"][t], A, D)
+            else:
+                ro.gdn_token(S, toks["q"][t], toks["k"][t], toks["v"][t], toks["alpha"][t], toks["beta"][t])
         elapsed += time.perf_counter() - t0
-        tokens += nseq * chunk
         steps += chunk
         c += 1
-    return {"value": round(tokens / elapsed, 1), "unit": "tokens/s", "cores": ro.threads(), "kind": "oracle",
-            "sample": f"{nseq} sequences x {steps} decode steps of the headline layer shape (fp64 ordinary "
-                      f"decoding, bf16-rounded inputs), {elapsed:.1f} s"}
+    return nseq * steps / elapsed, steps, elapsed
+
+
+def cpu_baseline(budget_s=8.0):
+    """The fp64 oracle (ordinary decoding, OpenMP over (sequence, head)) on the host cores, on
+    bounded samples: the headline Mamba-2 layer shape with 64 sequences (512 MiB of fp64 state,
+    beyond any host cache) on every thread and on one, and the GDN layer shape on every thread;
+    steps in chunks of 4 until about budget_s of wall time per leg."""
+    from oracle import replay_oracle as ro
+    threads = ro.threads()
+    m2, m2_steps, m2_s = _oracle_rate("mamba2", 64, budget_s, 1)
+    gd, gd_steps, gd_s = _oracle_rate("gdn", 64, 0.75 * budget_s, 2)
+    ro.set_threads(1)
+    try:
+        one, one_steps, one_s = _oracle_rate("mamba2", 4, 0.5 * budget_s, 3)
+    finally:
+        ro.set_threads(threads)
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    return {"value": round(m2, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"64 sequences x {m2_steps} decode steps of the batch-256 Mamba-2 layer shape (fp64 ordinary "
+                      f"decoding, bf16-rounded inputs), {m2_s:.1f} s on {threads} threads",
+            "nproc": os.cpu_count(), "affinity_cpus": affinity, "cpu_model": _cpu_model(),
+            "one_thread_tokens_per_s": round(one, 1),
+            "one_thread_sample": f"4 sequences x {one_steps} steps, {one_s:.1f} s",
+            "gdn_tokens_per_s": round(gd, 1),
+            "gdn_sample": f"64 sequences x {gd_steps} steps of the batch-256 GDN layer shape, {gd_s:.1f} s "
+                          f"on {threads} threads"}
 
 
 class Layer:
-    """Device-side state, parameters and pre-drawn inputs of one synthetic layer."""
+    """Device-side state parameters and pre-drawn inputs of one synthetic layer.  The initial
+    checkpoint is fp32; the library rounds it to the checkpoint dtype at load."""
 
     def __init__(self, rb, synth, torch, dev, kind, B, steps, seed, cap=16, read_copy=None, ckpt="f32", flags=0):
         self.rb, self.torch, self.dev, self.kind, self.B = rb, torch, dev, kind, B
@@ -164,7 +251,7 @@ class Layer:
         self.cfg = rb.make_config(rb.MAMBA2 if kind == "mamba2" else rb.GDN, B, self.H, self.G, self.C, self.R,
                                   cap, rb.BF16, read_copy=rc, ckpt_dtype={"f16": rb.F16, "fp8": rb.FP8_E4M3}.get(ckpt, rb.F32),
                                   flags=flags)
-        self.S0 = synth.checkpoint_device(seed, (B, self.H, self.C, self.R), dev).to(rb.ckpt_torch_dtype(self.cfg))
+        self.S0 = synth.checkpoint_device(seed, (B, self.H, self.C, self.R), dev)
         if kind == "mamba2":
             A, D = synth.mamba2_params(seed, self.H)
             self.params = {"A": torch.from_numpy(A).to(dev), "D": torch.from_numpy(D).to(dev)}
@@ -172,73 +259,147 @@ class Layer:
         else:
             self.params = {}
             self.toks = synth.gdn_tokens_device(seed, steps, B, self.H, self.G, self.R, self.C, dev)
+        self.ntok = steps
 
     def inputs(self, t0, n=1):
         return self.rb.make_inputs(self.cfg, {k: v[t0:t0 + n] for k, v in self.toks.items()}, self.params)
 
+    def state_bytes_per_step(self):
+        """Bytes a non-fold step streams from the checkpoint or its read copy."""
+        n = self.B * self.H * self.C * self.R
+        if self.read_copy == "fp8":
+            return n
+        if self.read_copy == "mxfp4":
+            return n // 2 + n // 32
+        return n * {"f16": 2, "fp8": 1}.get(self.ckpt, 4)
 
-def time_replay_decode(L, K, W, stream):
-    """W warm-up steps, then K timed steps back to back (the throughput), then K more steps
-    with a HIP event pair around every launch on the launch stream (per-launch durations,
-    split into flush and non-flush steps).  The second pass reuses the same inputs."""
-    rb, torch = L.rb, L.torch
-    st = rb.ReplayState(L.cfg, device=L.dev)
-    st.load_checkpoint(L.S0)
-    ys = torch.empty((2, 1, L.B, L.H, L.C), dtype=torch.bfloat16, device=L.dev)
-    ins = [L.inputs(t) for t in range(K + W)]
-    lib, sp = rb.lib(), rb.ctypes.c_void_p(stream.cuda_stream)
-    yp = [rb.ctypes.c_void_p(ys[i].data_ptr()) for i in range(2)]
-    n = [0]                                   # steps issued so far (the flush cadence)
+    def conventional_state(self):
+        """The plain logical state for the conventional kernel, in the checkpoint dtype, made by
+        the library's own load rounding (a replay state loaded from S0, read back)."""
+        st = self.rb.ReplayState(self.cfg, device=self.dev)
+        st.load_checkpoint(self.S0)
+        S = st.read_checkpoint()
+        self.torch.cuda.synchronize()
+        return S
 
-    def step(t):
-        s = lib.replay_decode_step(st.h, rb.ctypes.byref(ins[t]), yp[t & 1], sp)
+
+def auto_rotate(L, cap_states=64):
+    """Copies of the layer state a timing cycles through so that consecutive launches stream
+    at least 512 MiB of distinct checkpoint (or read-copy) bytes."""
+    return max(1, min(cap_states, -(-ROTATE_MIN_BYTES // L.state_bytes_per_step())))
+
+
+class Stepper:
+    """Decode steps of one layer issued back to back, round-robin over `rotate` states that
+    all start from the layer's checkpoint.  Step n runs on state n % rotate with input n mod
+    the number of drawn tokens; it is a fold step when that state's own step count
+    n // rotate is the last of a window."""
+
+    def __init__(self, L, stream, rotate=1):
+        rb, torch = L.rb, L.torch
+        self.L, self.rotate, self.cap = L, rotate, L.cap
+        self.states = []
+        for _ in range(rotate):
+            st = rb.ReplayState(L.cfg, device=L.dev)
+            st.load_checkpoint(L.S0)
+            self.states.append(st)
+        self.ys = torch.empty((2, 1, L.B, L.H, L.C), dtype=torch.bfloat16, device=L.dev)
+        self.ins = [L.inputs(t) for t in range(L.ntok)]
+        self.lib, self.sp = rb.lib(), rb.ctypes.c_void_p(stream.cuda_stream)
+        self.yp = [rb.ctypes.c_void_p(self.ys[i].data_ptr()) for i in range(2)]
+        self.n = 0
+
+    def step(self):
+        rb = self.L.rb
+        st = self.states[self.n % self.rotate]
+        s = self.lib.replay_decode_step(st.h, rb.ctypes.byref(self.ins[self.n % len(self.ins)]), self.yp[self.n & 1],
+                                        self.sp)
         if s != rb.OK:
             raise rb.ReplayError(s, "replay_decode_step")
-        n[0] += 1
+        self.n += 1
 
-    for t in range(W):
+    def is_fold(self, n):
+        return (n // self.rotate) % self.cap == self.cap - 1
+
+    def align(self):
+        """Untimed steps up to the next point where every state starts a window."""
+        while self.n % (self.cap * self.rotate):
+            self.step()
+
+
+def time_replay_decode(L, K, W, stream, rotate=1, windows=4):
+    """W warm-up steps, untimed steps to the next window boundary plus two full windows per
+    state, then K timed steps back to back (the throughput); then, from a window boundary,
+    `windows` whole windows per state back to back (the roofline's per-launch time), and two
+    whole windows with an event pair around every launch (fold / non-fold split, percentiles)."""
+    torch = L.torch
+    sp = Stepper(L, stream, rotate)
+    for _ in range(W):
+        sp.step()
+    sp.align()
+    for _ in range(2 * sp.cap * rotate):
+        sp.step()
+    untimed = sp.n
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(K):
+        sp.step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    total = e0.elapsed_time(e1)
+    sp.align()
+    nw = windows * sp.cap * rotate
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(nw):
+        sp.step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    window_ms = e0.elapsed_time(e1) / nw
+    ne = 2 * sp.cap * rotate
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(ne)]
+    first = sp.n
+    for i in range(ne):
+        ev[i][0].record(stream)
+        sp.step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in ev]
+    flush = [p for i, p in enumerate(per) if sp.is_fold(first + i)]
+    nonflush = [p for i, p in enumerate(per) if not sp.is_fold(first + i)]
+    srt = sorted(per)
+    del sp
+    return {"steps": K, "total_ms": total, "untimed_before": untimed, "window_ms_per_step": window_ms,
+            "window_steps": nw, "rotate": rotate,
+            "flush_ms": sum(flush) / max(1, len(flush)), "nonflush_ms": sum(nonflush) / max(1, len(nonflush)),
+            "max_launch_ms": srt[-1], "p99_launch_ms": srt[min(ne - 1, int(0.99 * ne))], "p50_launch_ms": srt[ne // 2]}
+
+
+def time_conv_decode(L, K, stream, t0=0, rotate=1):
+    """K conventional decode steps back to back after 4 warm-up steps, round-robin over
+    `rotate` copies of the state."""
+    rb, torch = L.rb, L.torch
+    Ss = [L.conventional_state() for _ in range(rotate)]
+    y = torch.empty((1, L.B, L.H, L.C), dtype=torch.bfloat16, device=L.dev)
+    nin = min(L.ntok - t0, K + 4)
+    ins = [L.inputs(t0 + t) for t in range(nin)]
+    lib, sp = rb.lib(), rb.ctypes.c_void_p(stream.cuda_stream)
+    cp, yp = rb.ctypes.byref(L.cfg), rb.ctypes.c_void_p(y.data_ptr())
+    Sps = [rb.ctypes.c_void_p(S.data_ptr()) for S in Ss]
+
+    def step(t):
+        s = lib.replay_conv_decode_step(cp, Sps[t % rotate], rb.ctypes.byref(ins[t % nin]), yp, sp)
+        if s != rb.OK:
+            raise rb.ReplayError(s, "replay_conv_decode_step")
+
+    for t in range(4 * rotate):
         step(t)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for i in range(K):
-        step(W + i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    total = e0.elapsed_time(e1)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    first = n[0]
-    for i in range(K):
-        ev[i][0].record(stream)
-        step(W + i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    per = [s.elapsed_time(e) for s, e in ev]
-    flush = [p for i, p in enumerate(per) if (first + i) % L.cap == L.cap - 1]
-    nonflush = [p for i, p in enumerate(per) if (first + i) % L.cap != L.cap - 1]
-    srt = sorted(per)
-    return {"steps": K, "total_ms": total, "avg_launch_ms": sum(per) / K,
-            "flush_ms": sum(flush) / max(1, len(flush)), "nonflush_ms": sum(nonflush) / max(1, len(nonflush)),
-            "max_launch_ms": srt[-1], "p99_launch_ms": srt[min(K - 1, int(0.99 * K))],
-            "p50_launch_ms": srt[K // 2]}
-
-
-def time_conv_decode(L, K, stream, t0=0):
-    rb, torch = L.rb, L.torch
-    S = L.S0.clone()
-    y = torch.empty((1, L.B, L.H, L.C), dtype=torch.bfloat16, device=L.dev)
-    ins = [L.inputs(t0 + t) for t in range(K + 4)]
-    lib, sp = rb.lib(), rb.ctypes.c_void_p(stream.cuda_stream)
-    cp, Sp, yp = rb.ctypes.byref(L.cfg), rb.ctypes.c_void_p(S.data_ptr()), rb.ctypes.c_void_p(y.data_ptr())
-    for t in range(4):
-        lib.replay_conv_decode_step(cp, Sp, rb.ctypes.byref(ins[t]), yp, sp)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
     for t in range(K):
-        s = lib.replay_conv_decode_step(cp, Sp, rb.ctypes.byref(ins[4 + t]), yp, sp)
-        if s != rb.OK:
-            raise rb.ReplayError(s, "replay_conv_decode_step")
+        step(4 * rotate + t)
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / K
@@ -374,15 +535,23 @@ def fold_flops(kind, H, G, C, R, cap=16):
 
 
 def decode_report(L, r, conv_ms):
-    replay_b, conv_b = algorithmic_bytes(L.kind, L.H, L.G, L.C, L.R, L.cap, read_copy=L.read_copy,
-                                         ckpt_bytes={"f16": 2, "fp8": 1}.get(L.ckpt, 4))
+    """One layer's report: throughput over the K timed steps; achieved bandwidth from the
+    whole-window pass (algorithmic bytes of a window / its back-to-back time); fold split and
+    percentiles from the event-pair pass; bytes per token and the replay-vs-conventional
+    reduction, algorithmic and (for the batch-256 fp32 layers) measured."""
+    ckb = {"f16": 2, "fp8": 1}.get(L.ckpt, 4)
+    rep_m, conv_m = traffic_model(L.kind, L.H, L.G, L.C, L.R, L.cap, read_copy=L.read_copy, ckpt_bytes=ckb)
+    replay_b, conv_b = sum(rep_m.values()), sum(conv_m.values())
     ms = r["total_ms"] / r["steps"]
-    ach = replay_b * L.B / (r["avg_launch_ms"] / 1e3) / 1e9
+    wms = r["window_ms_per_step"]
+    ach = replay_b * L.B / (wms / 1e3) / 1e9
     out = {"batch": L.B, "tokens_per_s": round(L.B / (ms / 1e3), 1), "ms_per_step": round(ms, 5),
-           "avg_launch_ms": round(r["avg_launch_ms"], 5),
+           "window_ms_per_step": round(wms, 5), "window_tokens_per_s": round(L.B / (wms / 1e3), 1),
            "flush_step_ms": round(r["flush_ms"], 5), "nonflush_step_ms": round(r["nonflush_ms"], 5),
            "achieved_gbs": round(ach, 1), "frac_of_peak": round(ach / HBM_PEAK_GBS, 4),
-           "bytes_per_token_algorithmic": int(replay_b)}
+           "bytes_per_token_algorithmic": int(replay_b),
+           "bytes_per_token_algorithmic_parts": {k: int(v) for k, v in rep_m.items()},
+           "rotate": r["rotate"], "untimed_steps_before_timed_region": r["untimed_before"]}
     ff = fold_flops(L.kind, L.H, L.G, L.C, L.R, L.cap) * L.B
     tf = ff / (r["flush_ms"] / 1e3) / 1e12
     out["flush_mfma"] = {"flops_per_flush_step": ff, "tflops": round(tf, 2),
@@ -392,7 +561,10 @@ def decode_report(L, r, conv_ms):
                                "achieved_gbs": round(conv_b * L.B / (conv_ms / 1e3) / 1e9, 1),
                                "bytes_per_token_algorithmic": int(conv_b)}
         out["speedup_vs_conventional"] = round(conv_ms / ms, 3)
-        out["state_traffic_reduction_algorithmic"] = round(1 - replay_b / conv_b, 4)
+        out["speedup_vs_conventional_window"] = round(conv_ms / wms, 3)
+        out["state_traffic_reduction_algorithmic"] = reductions(rep_m, conv_m)
+        if L.B == 256 and L.ckpt == "f32" and L.read_copy is None:
+            out["state_traffic_reduction_measured"] = measured_reduction(L.kind, L.B, rep_m, conv_m)
     return out
 
 
@@ -445,6 +617,9 @@ def time_spec(L, rounds, k, stream, seed=3):
 
 
 def ceilings(rb, torch, dev, stream):
+    """In-run streaming ceilings with the replay kernels' access pattern (32 KiB tiles per
+    workgroup, eight 128-bit loads in flight per lane): a 1 GiB copy (read + write) and a
+    1 GiB read, each 10 launches back to back after 3 warm-up launches."""
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     nb = src.numel() * 4
@@ -466,7 +641,12 @@ def ceilings(rb, torch, dev, stream):
     e1.record(stream)
     torch.cuda.synchronize()
     read = 10 * nb / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src, dst
     return round(copy, 1), round(read, 1)
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def main():
@@ -493,14 +673,19 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
     K, W, B = args.steps, args.warmup, args.batch
+    ntok = min(K + W + 4, 320)
 
-    m2 = Layer(rb, synth, torch, dev, "mamba2", B, K + W + 4, seed=1)
+    log(f"headline: Mamba-2 layer, batch {B}, {K} timed steps")
+    m2 = Layer(rb, synth, torch, dev, "mamba2", B, ntok, seed=1)
     r = time_replay_decode(m2, K, W, stream)
-    replay_b, _ = algorithmic_bytes("mamba2", m2.H, m2.G, m2.C, m2.R)
-    achieved = replay_b * B / (r["avg_launch_ms"] / 1e3) / 1e9
+    rep_m, _ = traffic_model("mamba2", m2.H, m2.G, m2.C, m2.R)
+    replay_b = sum(rep_m.values())
+    achieved = replay_b * B / (r["window_ms_per_step"] / 1e3) / 1e9
     conv_ms = None if args.no_extras else time_conv_decode(m2, min(args.conv_steps, K), stream)
     head = decode_report(m2, r, conv_ms)
     del m2
+    torch.cuda.empty_cache()
+    traffic = read_traffic(TRAFFIC[("mamba2", "replay")]) if B == 256 else None
 
     out = {
         "metric": "SSM-layer decode tokens/s at batch 256; achieved HBM GB/s vs MI355X peak",
@@ -518,19 +703,30 @@ def main():
         "config": {"workload": "Mamba-2 SSM layer, replayed decode", "batch": B, "nheads": 128, "head_dim": 64,
                    "state_dim": 128, "ngroups": 8, "buffer": 16, "checkpoint": "fp32", "io": "bf16"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "mamba2_step_kernel", "algorithmic_bytes_per_launch": int(replay_b * B),
-                     "avg_launch_ms": round(r["avg_launch_ms"], 5)},
+                     "launch_ms": round(r["window_ms_per_step"], 5),
+                     "launch_ms_source": f"{r['window_steps']} steps (4 whole 16-step windows) back to back between "
+                                         "two events on the launch stream",
+                     "traffic_source": "profiles/mamba2_step_b256_traffic.txt (window bytes per launch; null when "
+                                       "the kernel sources changed since it was taken)"},
+        "timing": {"untimed_steps_before_timed_region": r["untimed_before"],
+                   "note": "W warm-up steps, then untimed steps to a window boundary and two full windows"},
         "mamba2": head,
     }
+    log("ceilings")
     out["copy_ceiling_gbs"], out["read_ceiling_gbs"] = ceilings(rb, torch, dev, stream)
+    out["mamba2"]["frac_of_read_ceiling"] = round(head["achieved_gbs"] / out["read_ceiling_gbs"], 4)
 
     if not args.no_extras:
-        gd = Layer(rb, synth, torch, dev, "gdn", B, K + W + 4, seed=2)
+        log("GDN layer")
+        gd = Layer(rb, synth, torch, dev, "gdn", B, ntok, seed=2)
         rg = time_replay_decode(gd, K, W, stream)
         out["gdn"] = decode_report(gd, rg, time_conv_decode(gd, min(args.conv_steps, K), stream))
+        out["gdn"]["frac_of_read_ceiling"] = round(out["gdn"]["achieved_gbs"] / out["read_ceiling_gbs"], 4)
         del gd
         torch.cuda.empty_cache()
+        log("speculative rounds")
         spec = {}
         for kind, seed in (("mamba2", 31), ("gdn", 32)):
             Ls = Layer(rb, synth, torch, dev, kind, 512, args.spec_rounds * 4, seed=seed)
@@ -538,43 +734,51 @@ def main():
             del Ls
             torch.cuda.empty_cache()
         out["spec"] = spec
-        # low-precision reads on the batch-128 GDN layer: fp32, FP8 and MXFP4 read copies
+        # low-precision reads on the batch-128 GDN layer: fp32, FP8 and MXFP4 read copies,
+        # rotated over enough states that no launch finds its copy in the Infinity Cache
+        log("read copies")
         lp = {}
         for rc in (None, "fp8", "mxfp4"):
-            Lr = Layer(rb, synth, torch, dev, "gdn", 128, 256 + 32 + 4, seed=4, read_copy=rc)
-            rr = time_replay_decode(Lr, 256, 32, stream)
+            Lr = Layer(rb, synth, torch, dev, "gdn", 128, 160, seed=4, read_copy=rc)
+            rr = time_replay_decode(Lr, 256, 32, stream, rotate=auto_rotate(Lr))
             lp[rc or "fp32"] = decode_report(Lr, rr, None)
             del Lr
             torch.cuda.empty_cache()
         out["gdn_read_copy_b128"] = lp
         # fp16 recurrence checkpoint at batch 256 (the conventional baseline on an fp16 state)
+        log("fp16 checkpoints")
         f16 = {}
         for kind, seed in (("mamba2", 6), ("gdn", 7)):
-            Lh = Layer(rb, synth, torch, dev, kind, B, 256 + 32 + 4, seed=seed, ckpt="f16")
-            rh = time_replay_decode(Lh, 256, 32, stream)
-            f16[kind] = decode_report(Lh, rh, time_conv_decode(Lh, 64, stream))
+            Lh = Layer(rb, synth, torch, dev, kind, B, 160, seed=seed, ckpt="f16")
+            rot = auto_rotate(Lh)
+            rh = time_replay_decode(Lh, 256, 32, stream, rotate=rot)
+            f16[kind] = decode_report(Lh, rh, time_conv_decode(Lh, 64, stream, rotate=rot))
             del Lh
             torch.cuda.empty_cache()
         out["fp16_checkpoint"] = f16
         # FP8 recurrence checkpoint at batch 256: alone (beside the conventional kernel on an
         # FP8 state) and with an MXFP4 read copy
+        log("FP8 checkpoints")
         f8 = {}
         for kind, seed in (("mamba2", 9), ("gdn", 10)):
             for rc in (None, "mxfp4"):
-                Lq = Layer(rb, synth, torch, dev, kind, B, 256 + 32 + 4, seed=seed, ckpt="fp8", read_copy=rc)
-                rq = time_replay_decode(Lq, 256, 32, stream)
+                Lq = Layer(rb, synth, torch, dev, kind, B, 160, seed=seed, ckpt="fp8", read_copy=rc)
+                rot = auto_rotate(Lq)
+                rq = time_replay_decode(Lq, 256, 32, stream, rotate=rot)
                 f8[kind + ("_mxfp4_copy" if rc else "")] = decode_report(
-                    Lq, rq, None if rc else time_conv_decode(Lq, 64, stream))
+                    Lq, rq, None if rc else time_conv_decode(Lq, 64, stream, rotate=rot))
                 del Lq
                 torch.cuda.empty_cache()
         out["fp8_checkpoint"] = f8
         # flush schedule at batch 256: lockstep folds (every 16th step folds every sequence)
         # against staggered phases (about 1/16 of the sequences fold on each step)
+        log("flush schedules")
         sched = {}
         for name, fl in (("lockstep", 0), ("staggered", rb.FLAG_STAGGER_FLUSH)):
-            Lg = Layer(rb, synth, torch, dev, "mamba2", B, 256 + 32 + 4, seed=8, flags=fl)
+            Lg = Layer(rb, synth, torch, dev, "mamba2", B, 160, seed=8, flags=fl)
             rg = time_replay_decode(Lg, 256, 32, stream)
             sched[name] = {"ms_per_step": round(rg["total_ms"] / rg["steps"], 5),
+                           "window_ms_per_step": round(rg["window_ms_per_step"], 5),
                            "launch_ms_p50": round(rg["p50_launch_ms"], 5), "launch_ms_p99": round(rg["p99_launch_ms"], 5),
                            "launch_ms_max": round(rg["max_launch_ms"], 5)}
             del Lg
@@ -582,6 +786,7 @@ def main():
         out["flush_schedule_mamba2_b256"] = sched
         # a hybrid model's SSM layers decoded as one stack (one bookkeeping set), lockstep
         # and staggered flush phases, against the conventional kernel per layer
+        log("hybrid stack")
         stack = {}
         for name, fl in (("lockstep", 0), ("staggered", rb.FLAG_STAGGER_FLUSH)):
             Ls = [Layer(rb, synth, torch, dev, kind, B, 128 + 16, seed=40 + i, flags=fl)
@@ -596,22 +801,24 @@ def main():
             for kind in ("mamba2", "gdn"):
                 for bsz in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512):
                     Lw = Layer(rb, synth, torch, dev, kind, bsz, 64 + 16 + 4, seed=5)
-                    rw = time_replay_decode(Lw, 64, 16, stream)
-                    rep = decode_report(Lw, rw, time_conv_decode(Lw, 32, stream))
+                    rot = auto_rotate(Lw)
+                    rw = time_replay_decode(Lw, 64, 16, stream, rotate=rot)
+                    rep = decode_report(Lw, rw, time_conv_decode(Lw, 64, stream, rotate=rot))
                     rep["kind"] = kind
                     g_rep, g_conv = time_graph(Lw, False), time_graph(Lw, True)
                     rep["graph"] = {"replay_ms_per_step": round(g_rep, 5), "conventional_ms_per_step": round(g_conv, 5),
-                                    "speedup_vs_conventional": round(g_conv / g_rep, 3)}
+                                    "speedup_vs_conventional": round(g_conv / g_rep, 3), "rotate": 1}
                     f.write(json.dumps(rep) + "\n")
                     f.flush()
-                    print(f"[sweep] {kind} B={bsz}: replay {rep['ms_per_step']:.4f} ms, conventional "
+                    print(f"[sweep] {kind} B={bsz} rotate={rot}: replay {rep['ms_per_step']:.4f} ms, conventional "
                           f"{rep['conventional']['ms_per_step']:.4f} ms, speedup {rep['speedup_vs_conventional']}; "
                           f"graph {g_rep:.4f} / {g_conv:.4f} ms", file=sys.stderr, flush=True)
                     del Lw
                     torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(128, 8, 64, 128)
+        log("CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
 
 

@@ -94,6 +94,9 @@ _SIGS = {
     "replay_stack_layers": ([_vp], _i32),
     "replay_stack_next_layer": ([_vp], _i32),
     "replay_stack_phase": ([_vp], _i32),
+    "replay_standin_linear": ([_vp, _vp, _vp, _i32, _i32, _i32, _vp], _i32),
+    "replay_standin_attention": ([_vp, ctypes.c_int64, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_float,
+                                  _vp], _i32),
     "replay_stream_copy": ([_vp, _vp, _sz, _vp], _i32),
     "replay_stream_read": ([_vp, _sz, _vp, _vp], _i32),
 }
@@ -497,6 +500,41 @@ def conv_spec_restore(cfg: ReplayConfig, S, snaps, k: int, accepted):
                                          _ptr(snaps, ckt, "snaps"), int(k),
                                          _ptr(accepted, torch.int32, "accepted"), _stream()),
            "replay_conv_spec_restore")
+
+
+# ---- stand-in non-SSM layers of a model step ---------------------------------------
+def standin_linear(X, W, Y=None):
+    """Y = X W^T in bf16 (X [M][K], W [N][K]) by replay_standin_linear."""
+    torch = _torch()
+    M, K = X.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("W must be [N][K]")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    bf = torch.bfloat16
+    _check(_lib.replay_standin_linear(_ptr(X, bf, "X"), _ptr(W, bf, "W"), _ptr(Y, bf, "Y"), M, K, N, _stream()),
+           "replay_standin_linear")
+    return Y
+
+
+def standin_attention(q, K, V, scale, o=None):
+    """Decode attention (replay_standin_attention): q [B][Hq*D] rows (any row stride), K and V
+    [B][Hkv][L][D]; returns o [B][Hq][D]."""
+    torch = _torch()
+    B, Hkv, L, D = K.shape
+    if q.dim() != 2 or q.stride(1) != 1:
+        raise ValueError("q must be [B][row] with contiguous rows")
+    Hq = q.shape[1] // D
+    if o is None:
+        o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=K.device)
+    bf = torch.bfloat16
+    if q.dtype != bf or not q.is_cuda:
+        raise ValueError("q must be a bf16 device tensor")
+    _check(_lib.replay_standin_attention(ctypes.c_void_p(q.data_ptr()), q.stride(0), _ptr(K, bf, "K"),
+                                         _ptr(V, bf, "V"), _ptr(o, bf, "o"), B, Hq, Hkv, D, L, float(scale),
+                                         _stream()), "replay_standin_attention")
+    return o
 
 
 def stream_copy(dst, src, nbytes: int):

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libreplayssm.so")
 SOURCES = ["host.cpp", "mamba2.hip", "mamba2_f16.hip", "mamba2_fp8.hip", "gdn.hip", "gdn_f16.hip", "gdn_fp8.hip",
-           "aux.hip", "conv.hip"]
+           "aux.hip", "conv.hip", "standin.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -328,41 +328,72 @@ hipError_t launch_read_copy_to_logical(const uint8_t* codes, const uint8_t* scal
     return hipErrorInvalidValue;
 }
 
-// ---- streaming copy (bandwidth ceiling and byte-counter reference) --------
+// ---- streaming copy / read: bandwidth ceilings and byte-counter reference ----
+// Same access pattern as the replay step kernels' checkpoint stream: one
+// workgroup of four waves per 32 KiB tile, workgroups remapped so each XCD
+// takes a contiguous range of tiles, every lane with eight 128-bit nontemporal
+// loads in flight (each wave moves eight contiguous 1 KiB rows), issued before
+// any of them is consumed.  A ragged tail (bytes not a multiple of 32 KiB) is
+// handled by the last workgroup, 16 bytes per thread.
+constexpr int STREAM_TILE_F4 = 2048;              // 32 KiB per workgroup
+
 __global__ __launch_bounds__(256) void stream_copy_kernel(const f32x4* src, f32x4* dst, size_t n4)
 {
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+    const size_t tile = (size_t)xcd_tile_index();
+    const size_t base = tile * STREAM_TILE_F4 + (threadIdx.x >> 6) * 512 + (threadIdx.x & 63);
+    if (base + 7 * 64 < n4 && (tile + 1) * STREAM_TILE_F4 <= n4) {
+        f32x4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = __builtin_nontemporal_load(src + base + i * 64);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) __builtin_nontemporal_store(v[i], dst + base + i * 64);
+        return;
+    }
+    for (size_t i = tile * STREAM_TILE_F4 + threadIdx.x; i < n4 && i < (tile + 1) * STREAM_TILE_F4; i += blockDim.x)
         __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t s)
 {
     const size_t n4 = bytes / 16;
-    size_t blocks = (n4 + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
+    size_t blocks = (n4 + STREAM_TILE_F4 - 1) / STREAM_TILE_F4;
     if (blocks == 0) blocks = 1;
     hipLaunchKernelGGL(stream_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const f32x4*)src, (f32x4*)dst, n4);
     return hipGetLastError();
 }
 
 // Read-only stream: the ceiling for checkpoint reads that write nothing back.
-// A fixed grid (8 workgroups per CU) strides over the data with four
-// independent 128-bit loads per thread in flight; one atomic per workgroup.
+// A fixed grid of 8 workgroups per CU walks the 32 KiB tiles (two per
+// iteration: sixteen 128-bit loads in flight per lane); the loaded values are
+// summed, so no load is dead, and one atomic per workgroup adds its sum.
+constexpr int STREAM_READ_GRID = 2048;
+
 __global__ __launch_bounds__(256) void stream_read_kernel(const f32x4* src, size_t n4, float* sum_out)
 {
     __shared__ float part[4];
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    const size_t ntiles = n4 / STREAM_TILE_F4;
+    const size_t off = (threadIdx.x >> 6) * 512 + (threadIdx.x & 63);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (; i + 3 * stride < n4; i += 4 * stride) {
-        const f32x4 a0 = __builtin_nontemporal_load(src + i);
-        const f32x4 a1 = __builtin_nontemporal_load(src + i + stride);
-        const f32x4 a2 = __builtin_nontemporal_load(src + i + 2 * stride);
-        const f32x4 a3 = __builtin_nontemporal_load(src + i + 3 * stride);
-        acc += (a0 + a1) + (a2 + a3);
+    size_t t = (size_t)xcd_tile_index();
+    for (; t + gridDim.x < ntiles; t += 2 * (size_t)gridDim.x) {
+        const f32x4* p0 = src + t * STREAM_TILE_F4 + off;
+        const f32x4* p1 = src + (t + gridDim.x) * STREAM_TILE_F4 + off;
+        f32x4 v[16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = __builtin_nontemporal_load(p0 + i * 64);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[8 + i] = __builtin_nontemporal_load(p1 + i * 64);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc += v[i];
     }
-    for (; i < n4; i += stride) acc += __builtin_nontemporal_load(src + i);
+    if (t < ntiles) {
+        const f32x4* p0 = src + t * STREAM_TILE_F4 + off;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc += __builtin_nontemporal_load(p0 + i * 64);
+    }
+    if (blockIdx.x == 0)                           // the ragged tail past the last whole tile
+        for (size_t i = ntiles * STREAM_TILE_F4 + threadIdx.x; i < n4; i += blockDim.x)
+            acc += __builtin_nontemporal_load(src + i);
     const float v = wave_sum64(acc.x + acc.y + acc.z + acc.w);
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
     __syncthreads();
@@ -371,7 +402,8 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const f32x4* src, size
 
 hipError_t launch_stream_read(const void* src, size_t bytes, float* sum_out, hipStream_t s)
 {
-    hipLaunchKernelGGL(stream_read_kernel, dim3(2048), dim3(256), 0, s, (const f32x4*)src, bytes / 16, sum_out);
+    hipLaunchKernelGGL(stream_read_kernel, dim3(STREAM_READ_GRID), dim3(256), 0, s, (const f32x4*)src, bytes / 16,
+                       sum_out);
     return hipGetLastError();
 }
 

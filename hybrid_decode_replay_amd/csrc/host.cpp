@@ -970,6 +970,43 @@ replay_status replay_conv_spec_restore(const replay_config* cfg, void* S, const 
                      "conventional restore");
 }
 
+replay_status replay_standin_linear(const void* X, const void* W, void* Y, int32_t M, int32_t K, int32_t N,
+                                    void* stream)
+{
+    replay_status s;
+    if ((s = check_ptr(X, "X")) != REPLAY_OK) return s;
+    if ((s = check_ptr(W, "W")) != REPLAY_OK) return s;
+    if ((s = check_ptr(Y, "Y")) != REPLAY_OK) return s;
+    if (M < 1 || K < 128 || K % 128 != 0 || N < 32 || N % 32 != 0)
+        return fail(REPLAY_ERR_SHAPE, "linear needs M >= 1, K a multiple of 128 and N a multiple of 32 (M %d, K %d, N %d)",
+                    M, K, N);
+    if ((long long)(M + 255) / 256 > 65535) return fail(REPLAY_ERR_SHAPE, "M %d too large", M);
+    return LAUNCH(rs::launch_standin_linear(X, W, Y, M, K, N, (hipStream_t)stream), "stand-in linear");
+}
+
+replay_status replay_standin_attention(const void* q, int64_t q_stride, const void* K, const void* V, void* o,
+                                       int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t L, float scale,
+                                       void* stream)
+{
+    replay_status s;
+    if ((s = check_ptr(q, "q")) != REPLAY_OK) return s;
+    if ((s = check_ptr(K, "K")) != REPLAY_OK) return s;
+    if ((s = check_ptr(V, "V")) != REPLAY_OK) return s;
+    if ((s = check_ptr(o, "o")) != REPLAY_OK) return s;
+    if (B < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0 || L < 1)
+        return fail(REPLAY_ERR_SHAPE, "attention needs B, Hkv, L >= 1 and Hkv dividing Hq");
+    const int qpk = Hq / Hkv;
+    if (qpk != 1 && qpk != 2 && qpk != 4 && qpk != 8)
+        return fail(REPLAY_ERR_UNSUPPORTED, "query heads per key/value head must be 1, 2, 4 or 8 (is %d)", qpk);
+    if (D != 128) return fail(REPLAY_ERR_UNSUPPORTED, "head dimension %d (128 is built)", D);
+    if (q_stride < (int64_t)Hq * D || q_stride % 8 != 0)
+        return fail(REPLAY_ERR_ARG, "q_stride %lld must be >= Hq * D and a multiple of 8", (long long)q_stride);
+    if ((long long)B * Hkv > (1LL << 31) - 1) return fail(REPLAY_ERR_SHAPE, "B * Hkv too large");
+    return LAUNCH(rs::launch_standin_attention(q, K, V, o, B, Hq, Hkv, D, L, (size_t)q_stride, scale,
+                                               (hipStream_t)stream),
+                  "stand-in attention");
+}
+
 replay_status replay_stream_copy(void* dst, const void* src, size_t bytes, void* stream)
 {
     replay_status s;

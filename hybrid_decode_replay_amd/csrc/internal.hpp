@@ -109,6 +109,10 @@ struct ConvArgs {
     void* y;
 };
 hipError_t launch_conv_step(const ConvArgs& a, int io, int ck, hipStream_t s);
+// Stand-in non-SSM layers of a model step (standin.hip).
+hipError_t launch_standin_linear(const void* X, const void* W, void* Y, int M, int K, int N, hipStream_t s);
+hipError_t launch_standin_attention(const void* q, const void* Kc, const void* Vc, void* o, int B, int Hq, int Hkv,
+                                    int D, int L, size_t q_stride, float scale, hipStream_t s);
 hipError_t launch_conv_restore(void* S, const void* snaps, const int32_t* accepted, int B, size_t tile_bytes,
                                int H, int k, hipStream_t s);
 

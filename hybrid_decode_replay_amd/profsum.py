@@ -17,7 +17,13 @@ sweep    the batch 1..512 table from `bench.py --sweep FILE`:
 traffic  HBM bytes per launch of KERNEL dispatches with grid size GRID (threads), from
          *_counter_collection.csv of a `--pmc FETCH_SIZE` and a `--pmc WRITE_SIZE` run.
          Both counters are calibrated on the streaming-copy kernel of the same runs,
-         which reads and writes 1 GiB: scale = known bytes / counter bytes.
+         which reads and writes 1 GiB: scale = known bytes / counter bytes.  Fold and
+         non-fold dispatches are told apart by their write bytes, and the bytes of a
+         16-step window (15 non-fold + 1 fold, per launch) are reported.
+dram     the same kernel's L2-to-memory requests from TCC_EA0_RDREQ*/WRREQ* runs, scaled by
+         the copy kernel's, against its algorithmic bytes per launch:
+             python -m hybrid_decode_replay_amd.profsum dram RD_DIR WR_DIR OUT.txt KERNEL GRID \\
+                 "READ COMMAND" "WRITE COMMAND" ALGORITHMIC_BYTES
 """
 from __future__ import annotations
 
@@ -111,6 +117,15 @@ def traffic(fetch_dir, write_dir, out, kernel, grid, fetch_cmd, write_cmd):
     kf, kw = pick(fetch, kernel, grid), pick(write, kernel, grid)
     n = min(len(kf), len(kw))
     per = [kf[i] * 1024 * s_fetch + kw[i] * 1024 * s_write for i in range(n)]
+    # fold dispatches write the checkpoint; the rest write only entries and outputs.  The two
+    # runs dispatch in the same order, so dispatch i of one is dispatch i of the other.
+    # Dispatches that fold only some sequences (staggered flush phases) write in between;
+    # they are counted but left out of both classes.
+    wmax, wmin = max(kw[:n]), min(kw[:n])
+    split = wmax > 4 * max(wmin, 1e-9)
+    fold = [per[i] for i in range(n) if split and kw[i] > 0.5 * wmax]
+    rest = [per[i] for i in range(n) if not split or kw[i] < 2 * wmin]
+    partial = n - len(fold) - len(rest)
     lines = [f"# HBM traffic of {kernel} (grid {grid} threads) from rocprofv3 --pmc runs",
              f"# FETCH_SIZE run: {fetch_cmd}",
              f"# WRITE_SIZE run: {write_cmd}",
@@ -126,9 +141,87 @@ def traffic(fetch_dir, write_dir, out, kernel, grid, fetch_cmd, write_cmd):
              f"fetch_kib_per_dispatch_min_max = {min(kf[:n]):.1f} {max(kf[:n]):.1f}",
              f"write_kib_per_dispatch_min_max = {min(kw[:n]):.1f} {max(kw[:n]):.1f}",
              f"traffic_bytes_per_launch = {sum(per) / n:.0f}"]
+    if fold and rest:
+        nf, f = sum(rest) / len(rest), sum(fold) / len(fold)
+        lines += [f"fold_dispatches = {len(fold)}",
+                  f"partial_fold_dispatches = {partial}",
+                  f"fold_bytes_per_launch = {f:.0f}",
+                  f"nonfold_bytes_per_launch = {nf:.0f}",
+                  "# a 16-step window: 15 non-fold steps and one fold step",
+                  f"window_traffic_bytes_per_launch = {(15 * nf + f) / 16:.0f}"]
+    else:
+        lines.append(f"window_traffic_bytes_per_launch = {sum(per) / n:.0f}")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(out, "traffic per launch", sum(per) / n)
+
+
+def dram(rd_dir, wr_dir, out, kernel, grid, rd_cmd, wr_cmd, algorithmic_bytes):
+    """Cross-check of the FETCH_SIZE / WRITE_SIZE scale on the replay kernel itself, from a run
+    with --pmc TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_DRAM_sum and one with
+    --pmc TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_64B_sum TCC_EA0_WRREQ_DRAM_sum.  Request bytes are
+    counted from the request sizes (32 or 64 bytes) without the bubble term; the same count is
+    taken on the streaming copy kernel, which moves a known 1 GiB each way, and the ratio
+    (known / counted) is applied to the kernel's counts.  The DRAM columns give the share of
+    requests the L2 sends to memory (MC) rather than elsewhere."""
+    grid = int(grid)
+    rd_csv = _one(os.path.join(rd_dir, "**", "*counter_collection.csv"))
+    wr_csv = _one(os.path.join(wr_dir, "**", "*counter_collection.csv"))
+
+    def per_dispatch(path, names):
+        d = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] in names:
+                e = d.setdefault(int(r["Dispatch_Id"]), {"name": short(r["Kernel_Name"]), "grid": int(r["Grid_Size"])})
+                e[r["Counter_Name"]] = float(r["Counter_Value"])
+        return d
+
+    rd = per_dispatch(rd_csv, ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_DRAM_sum"))
+    wr = per_dispatch(wr_csv, ("TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum", "TCC_EA0_WRREQ_DRAM_sum"))
+
+    def rbytes(e):
+        return (e["TCC_EA0_RDREQ_sum"] - e["TCC_EA0_RDREQ_32B_sum"]) * 64 + e["TCC_EA0_RDREQ_32B_sum"] * 32
+
+    def wbytes(e):
+        return (e["TCC_EA0_WRREQ_sum"] - e["TCC_EA0_WRREQ_64B_sum"]) * 32 + e["TCC_EA0_WRREQ_64B_sum"] * 64
+
+    def sel(d, name, g=None):
+        return [e for e in d.values() if _matches(e["name"], name) and (g is None or e["grid"] == g)]
+
+    crd, cwr = sel(rd, "stream_copy_kernel"), sel(wr, "stream_copy_kernel")
+    s_rd = COPY_BYTES / (sum(map(rbytes, crd)) / len(crd))
+    s_wr = COPY_BYTES / (sum(map(wbytes, cwr)) / len(cwr))
+    krd, kwr = sel(rd, kernel, grid), sel(wr, kernel, grid)
+    n = min(len(krd), len(kwr))
+    rb_, wb_ = [rbytes(e) * s_rd for e in krd[:n]], [wbytes(e) * s_wr for e in kwr[:n]]
+    wmax = max(wb_)
+    split = wmax > 4 * max(min(wb_), 1e-9)
+    fold = [i for i in range(n) if split and wb_[i] > 0.5 * wmax]
+    rest = [i for i in range(n) if not split or wb_[i] < 2 * min(wb_)]
+    tot = [rb_[i] + wb_[i] for i in range(n)]
+    win = (15 * sum(tot[i] for i in rest) / len(rest) + sum(tot[i] for i in fold) / len(fold)) / 16 \
+        if fold and rest else sum(tot) / n
+    dram_rd = sum(e["TCC_EA0_RDREQ_DRAM_sum"] for e in krd[:n]) / max(sum(e["TCC_EA0_RDREQ_sum"] for e in krd[:n]), 1)
+    dram_wr = sum(e["TCC_EA0_WRREQ_DRAM_sum"] for e in kwr[:n]) / max(sum(e["TCC_EA0_WRREQ_sum"] for e in kwr[:n]), 1)
+    alg = float(algorithmic_bytes)
+    lines = [f"# L2-to-memory request cross-check of {kernel} (grid {grid} threads), rocprofv3 --pmc runs",
+             f"# read-request run: {rd_cmd}",
+             f"# write-request run: {wr_cmd}",
+             "# request bytes = 64 x 64-byte requests + 32 x 32-byte requests, scaled by the copy kernel's known 1 GiB",
+             f"kernel = {kernel}",
+             f"grid_threads = {grid}",
+             f"kernel_source_sha = {source_sha(kernel.split('<')[0])}",
+             f"dispatches = {n}",
+             f"read_scale_from_copy = {s_rd:.4f}",
+             f"write_scale_from_copy = {s_wr:.4f}",
+             f"dram_share_of_read_requests = {dram_rd:.4f}",
+             f"dram_share_of_write_requests = {dram_wr:.4f}",
+             f"window_request_bytes_per_launch = {win:.0f}",
+             f"algorithmic_bytes_per_launch = {alg:.0f}",
+             f"request_over_algorithmic = {win / alg:.4f}"]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out, "request bytes / algorithmic", win / alg)
 
 
 def mfma(pmc_dir, out, command):
@@ -211,6 +304,8 @@ if __name__ == "__main__":
         traffic(*args)
     elif mode == "mfma":
         mfma(*args)
+    elif mode == "dram":
+        dram(*args)
     elif mode == "sweep":
         sweep(*args)
     else:

@@ -360,6 +360,32 @@ replay_status replay_conv_spec_step(const replay_config *cfg, const void *S, voi
 replay_status replay_conv_spec_restore(const replay_config *cfg, void *S, const void *snaps,
                                        int32_t k, const int32_t *accepted, void *stream);
 
+/* ---- stand-in non-SSM layers ----------------------------------------------
+ * A hybrid model's decode step also runs its mixers' dense projections and a
+ * few attention layers ([TR] "NVIDIA ve Dao AI Lab ...", section "ReplaySSM
+ * nasil calisir?": SSM layers interleaved with attention layers); the pages'
+ * decode-step speedups are the SSM gain diluted by them (section "Durum
+ * trafigini azaltma ve rollback'in basitlestirilmesi").  These two calls are
+ * that rest of a step, with caller-provided random weights and caches, so a
+ * model step can be timed with replayed and with conventional SSM layers.
+ * Both are plain definitions (no buffer or checkpoint): */
+/* Y[m][n] = sum_k X[m][k] W[n][k]: X [M][K], W [N][K] (one output feature's
+ * weights contiguous), Y [M][N]; all bf16, row-major, fp32 accumulation, Y
+ * rounded to nearest even.  Needs K a multiple of 128 and N a multiple of 32
+ * (else REPLAY_ERR_SHAPE). */
+replay_status replay_standin_linear(const void *X, const void *W, void *Y, int32_t M, int32_t K, int32_t N,
+                                    void *stream);
+/* Decode attention of one query token per sequence: for sequence b and query
+ * head h (key/value head g = h / (Hq / Hkv)),
+ *   o[b][h] = sum_t softmax_t(scale * q[b][h] . K[b][g][t]) V[b][g][t]
+ * over the L cached tokens.  q row b starts at q + b * q_stride elements (its
+ * Hq heads of D values contiguous), K and V are [B][Hkv][L][D], o is
+ * [B][Hq][D]; all bf16, fp32 softmax and accumulation.  D must be 128 and
+ * Hq / Hkv one of 1, 2, 4, 8 (else REPLAY_ERR_UNSUPPORTED). */
+replay_status replay_standin_attention(const void *q, int64_t q_stride, const void *K, const void *V, void *o,
+                                       int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t L, float scale,
+                                       void *stream);
+
 /* ---- measurement helpers ------------------------------------------------ */
 /* Streaming copy of `bytes` (multiple of 16) from src to dst: the in-run
  * bandwidth ceiling and the reference for hardware byte counters. */

@@ -259,6 +259,10 @@ void oracle_mxfp4_dequantize_array(const unsigned char *codes, const unsigned ch
 #ifdef _OPENMP
 #include <omp.h>
 int oracle_threads(void) { return omp_get_max_threads(); }
+/* Threads for the loops above from now on (n >= 1); used to time the oracle on
+ * one core beside all of them. */
+void oracle_set_threads(int n) { omp_set_num_threads(n < 1 ? 1 : n); }
 #else
 int oracle_threads(void) { return 1; }
+void oracle_set_threads(int n) { (void)n; }
 #endif

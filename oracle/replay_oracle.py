@@ -129,6 +129,8 @@ def configure(L):
     L.oracle_mxfp4_dequantize_array.restype = None
     L.oracle_threads.argtypes = []
     L.oracle_threads.restype = ctypes.c_int
+    L.oracle_set_threads.argtypes = [ctypes.c_int]
+    L.oracle_set_threads.restype = None
     return L
 
 
@@ -156,6 +158,11 @@ def use_library(handle):
 def threads():
     """OpenMP threads the oracle's per-token loops run on."""
     return int(lib().oracle_threads())
+
+
+def set_threads(n):
+    """Run the oracle's per-token loops on n threads from now on."""
+    lib().oracle_set_threads(int(n))
 
 
 def _f64(a):
