@@ -520,6 +520,164 @@ def time_graph(L, conventional, n=64, reps=8):
     return ms
 
 
+D_MODEL = 4096
+STANDIN_ATTN = dict(Hq=32, Hkv=8, D=128)
+
+
+def standin_shapes(kind):
+    """(in, out) projection widths of a mixer at d_model 4096: Mamba-2 in_proj to x, z, B, C, dt
+    (2 H P + 2 G N + H) and out_proj from H P; GDN in_proj to q, k, v, an output gate and the two
+    gates (4 H d + 2 H) and out_proj from H d_v; attention to q, k, v (Hq + 2 Hkv) D and o_proj
+    from Hq D."""
+    if kind == "mamba2":
+        return 2 * MAMBA2["H"] * MAMBA2["C"] + 2 * MAMBA2["G"] * MAMBA2["R"] + MAMBA2["H"], MAMBA2["H"] * MAMBA2["C"]
+    if kind == "gdn":
+        return 4 * GDN["H"] * GDN["C"] + 2 * GDN["H"], GDN["H"] * GDN["C"]
+    a = STANDIN_ATTN
+    return (a["Hq"] + 2 * a["Hkv"]) * a["D"], a["Hq"] * a["D"]
+
+
+def time_model_step(rb, synth, torch, dev, stream, B, context, mlp, K=32, W=8, d_ff=8192):
+    """A synthetic hybrid decode step at batch B: mixers Mamba-2, GDN, attention, Mamba-2, GDN
+    (the SSM layers at the shapes above, one layer stack), every mixer with its input and
+    output projection (replay_standin_linear, bf16 random weights, d_model 4096), the attention
+    layer reading a cache of `context` tokens per sequence (replay_standin_attention, 32 query
+    and 8 key/value heads of 128), and with mlp=True a dense MLP after every mixer (d_model ->
+    2 d_ff -> d_model as two products; the elementwise gate between them, under 1% of the
+    bytes, is not run).  The SSM layers' inputs are drawn separately rather than sliced from
+    the projection outputs: bytes and launches are those of a step, values are synthetic.
+    Timed three ways over K model steps after W warm-up steps: with replayed SSM layers, with
+    the conventional kernel in their place, and the stand-ins alone."""
+    g = torch.Generator(device=dev).manual_seed(77 + context + (1 if mlp else 0))
+
+    def weight(n_out, n_in):
+        return (torch.randn((n_out, n_in), generator=g, device=dev) * n_in ** -0.5).to(torch.bfloat16)
+
+    pattern = ["mamba2", "gdn", "attn", "mamba2", "gdn"]
+    ssm = [Layer(rb, synth, torch, dev, k, B, K + W, seed=60 + i) for i, k in enumerate(p for p in pattern if p != "attn")]
+    Wt = []
+    for kind in pattern:
+        n_in, n_out = standin_shapes(kind)
+        Wt.append((weight(n_in, D_MODEL), weight(D_MODEL, n_out)))
+    Wm = [(weight(2 * d_ff, D_MODEL), weight(D_MODEL, d_ff)) for _ in pattern] if mlp else None
+    a = STANDIN_ATTN
+    Kc = torch.randn((B, a["Hkv"], context, a["D"]), generator=g, device=dev).to(torch.bfloat16)
+    Vc = torch.randn((B, a["Hkv"], context, a["D"]), generator=g, device=dev).to(torch.bfloat16)
+    X = torch.randn((B, D_MODEL), generator=g, device=dev).to(torch.bfloat16)
+    proj = {kind: torch.empty((B, standin_shapes(kind)[0]), dtype=torch.bfloat16, device=dev) for kind in set(pattern)}
+    att_o = torch.empty((B, a["Hq"], a["D"]), dtype=torch.bfloat16, device=dev)
+    X2 = torch.empty_like(X)
+    up = torch.empty((B, 2 * d_ff), dtype=torch.bfloat16, device=dev) if mlp else None
+    act = torch.empty((B, d_ff), dtype=torch.bfloat16, device=dev) if mlp else None   # gated activation
+    ys = [torch.empty((1, L.B, L.H, L.C), dtype=torch.bfloat16, device=dev) for L in ssm]
+    lib, sp = rb.lib(), rb.ctypes.c_void_p(stream.cuda_stream)
+    states = [rb.ReplayState(L.cfg, device=dev) for L in ssm]
+    stk = rb.ReplayStack(states)
+    stk.load([L.S0 for L in ssm])
+    conv_S = [L.conventional_state() for L in ssm]
+    ins = [[L.inputs(t) for t in range(K + W)] for L in ssm]
+    ptr = rb.ctypes.c_void_p
+
+    def lin(x, w, y):
+        st = lib.replay_standin_linear(ptr(x.data_ptr()), ptr(w.data_ptr()), ptr(y.data_ptr()), x.shape[0],
+                                       w.shape[1], w.shape[0], sp)
+        if st != rb.OK:
+            raise rb.ReplayError(st, "replay_standin_linear")
+
+    def step(t, mode):
+        li = 0
+        for pos, kind in enumerate(pattern):
+            w_in, w_out = Wt[pos]
+            lin(X, w_in, proj[kind])
+            if kind == "attn":
+                st = lib.replay_standin_attention(ptr(proj["attn"].data_ptr()), proj["attn"].shape[1],
+                                                  ptr(Kc.data_ptr()), ptr(Vc.data_ptr()), ptr(att_o.data_ptr()), B,
+                                                  a["Hq"], a["Hkv"], a["D"], context, float(a["D"] ** -0.5), sp)
+                if st != rb.OK:
+                    raise rb.ReplayError(st, "replay_standin_attention")
+                lin(att_o.view(B, -1), w_out, X2)
+            else:
+                if mode == "replay":
+                    st = lib.replay_stack_decode_layer(stk.h, li, rb.ctypes.byref(ins[li][t]), ptr(ys[li].data_ptr()), sp)
+                elif mode == "conv":
+                    st = lib.replay_conv_decode_step(rb.ctypes.byref(ssm[li].cfg), ptr(conv_S[li].data_ptr()),
+                                                     rb.ctypes.byref(ins[li][t]), ptr(ys[li].data_ptr()), sp)
+                else:
+                    st = rb.OK
+                if st != rb.OK:
+                    raise rb.ReplayError(st, "SSM layer")
+                lin(ys[li].view(B, -1), w_out, X2)
+                li += 1
+            if mlp:
+                w_up, w_down = Wm[pos]
+                lin(X2, w_up, up)
+                lin(act, w_down, X)
+
+    def timed(mode):
+        for t in range(W):
+            step(t, mode)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for t in range(K):
+            step(W + t, mode)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    rep, conv, rest = timed("replay"), timed("conv"), timed("standins")
+    del stk, states
+    return {"pattern": pattern, "batch": B, "attention_context": context, "mlp_d_ff": d_ff if mlp else None,
+            "replay_ms_per_model_step": round(rep, 4), "conventional_ms_per_model_step": round(conv, 4),
+            "standins_alone_ms": round(rest, 4), "speedup_vs_conventional": round(conv / rep, 3),
+            "standin_share_of_replay_step": round(rest / rep, 3),
+            "ssm_speedup_implied": round((conv - rest) / max(rep - rest, 1e-9), 3),
+            "replay_tokens_per_s": round(B / (rep / 1e3), 1)}
+
+
+def time_standins(rb, torch, dev, stream, B=256, reps=20):
+    """Per-launch time and algorithmic bandwidth of the stand-in kernels at the model step's
+    shapes: weights (and activations) for the projections, the cache for attention."""
+    g = torch.Generator(device=dev).manual_seed(91)
+    out = {}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def run(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    for name, (n_in, n_out) in (("mamba2_in_proj", (D_MODEL, standin_shapes("mamba2")[0])),
+                                ("mamba2_out_proj", (standin_shapes("mamba2")[1], D_MODEL)),
+                                ("attn_o_proj", (STANDIN_ATTN["Hq"] * STANDIN_ATTN["D"], D_MODEL))):
+        X = torch.randn((B, n_in), generator=g, device=dev).to(torch.bfloat16)
+        Wt = torch.randn((n_out, n_in), generator=g, device=dev).to(torch.bfloat16)
+        Y = torch.empty((B, n_out), dtype=torch.bfloat16, device=dev)
+        ms = run(lambda: rb.standin_linear(X, Wt, Y))
+        nbytes = 2 * (n_out * n_in + B * n_in + B * n_out)
+        out[name] = {"M": B, "K": n_in, "N": n_out, "ms": round(ms, 5), "gbs": round(nbytes / (ms / 1e3) / 1e9, 1),
+                     "tflops": round(2 * B * n_in * n_out / (ms / 1e3) / 1e12, 1)}
+        del X, Wt, Y
+    a = STANDIN_ATTN
+    for L in (1024, 4096):
+        q = torch.randn((B, a["Hq"] * a["D"]), generator=g, device=dev).to(torch.bfloat16)
+        Kc = torch.randn((B, a["Hkv"], L, a["D"]), generator=g, device=dev).to(torch.bfloat16)
+        Vc = torch.randn_like(Kc)
+        o = torch.empty((B, a["Hq"], a["D"]), dtype=torch.bfloat16, device=dev)
+        ms = run(lambda: rb.standin_attention(q, Kc, Vc, a["D"] ** -0.5, o))
+        nbytes = 2 * Kc.numel() * 2
+        out[f"attention_L{L}"] = {"ms": round(ms, 5), "gbs": round(nbytes / (ms / 1e3) / 1e9, 1)}
+        del q, Kc, Vc, o
+    torch.cuda.empty_cache()
+    return out
+
+
 MFMA_F32_PEAK_TFLOPS = 157.3
 
 
@@ -795,6 +953,17 @@ def main():
             del Ls
             torch.cuda.empty_cache()
         out["hybrid_stack_b256"] = stack
+        # the SSM layers inside a whole synthetic hybrid decode step (stand-in projections,
+        # attention and MLPs identical in both runs): the step-level, diluted gain
+        log("hybrid model step with stand-in layers")
+        out["standin_kernels_b256"] = time_standins(rb, torch, dev, stream)
+        model = {}
+        for context in (1024, 4096):
+            for mlp in (False, True):
+                model[f"context{context}_{'mlp' if mlp else 'nomlp'}"] = time_model_step(
+                    rb, synth, torch, dev, stream, B, context, mlp)
+                torch.cuda.empty_cache()
+        out["hybrid_model_step_b256"] = model
 
     if args.sweep:
         with open(args.sweep, "w") as f:

@@ -28,20 +28,50 @@ __device__ __forceinline__ f32x4 mfma16x16x32bf16(bf16x8 a, bf16x8 b, f32x4 c)
 }
 
 // ---- linear ------------------------------------------------------------------
-// Workgroup: four waves, output tile of 256 rows x 32 columns; wave w owns rows
-// 64w..64w+63 as four 16-row blocks and both 16-column blocks.  Operand layout of
-// the 16x16x32 MFMA: A lane l holds row l%16, k = 8(l/16)..+7; B lane l holds
-// column l%16, the same k; the 16x16 result has rows 4(l/16)..+3 of column l%16.
-// Each k step of 32 takes one 16-byte load per operand block per lane; KU steps
-// are loaded before any is multiplied.  Rows past M read row M-1 and are not
-// stored.
-constexpr int LIN_KU = 4;
+// Workgroup: four waves and an output tile of 64 rows x 32 columns (four 16-row
+// by two 16-column MFMA blocks).  The waves split K: wave w takes the 128-wide
+// k chunks w, w+4, w+8, ..., so every weight is read by one wave only, and the
+// four partial tiles are summed through LDS at the end.  Operand layout of the
+// 16x16x32 MFMA: A lane l holds row l%16, k = 8(l/16)..+7; B lane l holds column
+// l%16, the same k; the 16x16 result has rows 4(l/16)..+3 of column l%16.  A
+// chunk takes four 16-byte loads per operand block per lane; the next chunk's
+// loads are issued before the current one is multiplied (two register sets).
+// Rows past M read row M-1 and are not stored.
+struct LinChunk {
+    bf16x8 a[4][4], b[4][2];
+};
+
+__device__ __forceinline__ void lin_load(LinChunk& c, const uint16_t* const (&xrow)[4], const uint16_t* const (&wrow)[2],
+                                         int k0)
+{
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            c.b[u][j] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(
+                                                       reinterpret_cast<const u32x4*>(wrow[j] + k0 + 32 * u)));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            c.a[u][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xrow[i] + k0 + 32 * u));
+    }
+}
+
+__device__ __forceinline__ void lin_mma(const LinChunk& c, f32x4 (&acc)[4][2])
+{
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = mfma16x16x32bf16(c.a[u][i], c.b[u][j], acc[i][j]);
+}
 
 __global__ __launch_bounds__(256) void standin_linear_kernel(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M,
                                                              int K, int N)
 {
+    __shared__ f32x4 red[3][4][2][64];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int n0 = blockIdx.x * 32, m0 = blockIdx.y * 256 + w * 64;
+    const int n0 = blockIdx.x * 32, m0 = blockIdx.y * 64;
     const int lr = lane & 15, kq = 8 * (lane >> 4);
     const uint16_t* xrow[4];
 #pragma unroll
@@ -54,39 +84,43 @@ __global__ __launch_bounds__(256) void standin_linear_kernel(const uint16_t* X, 
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < K; k0 += 32 * LIN_KU) {
-        bf16x8 a[LIN_KU][4], b[LIN_KU][2];
-#pragma unroll
-        for (int u = 0; u < LIN_KU; ++u) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                b[u][j] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(
-                                                         reinterpret_cast<const u32x4*>(wrow[j] + k0 + 32 * u)));
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a[u][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xrow[i] + k0 + 32 * u));
-        }
-#pragma unroll
-        for (int u = 0; u < LIN_KU; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = mfma16x16x32bf16(a[u][i], b[u][j], acc[i][j]);
+    const int nch = K / 128;
+    LinChunk c0, c1;
+    int c = w;
+    if (c < nch) lin_load(c0, xrow, wrow, 128 * c);
+    while (c < nch) {
+        if (c + 4 < nch) lin_load(c1, xrow, wrow, 128 * (c + 4));
+        lin_mma(c0, acc);
+        c += 4;
+        if (c >= nch) break;
+        if (c + 4 < nch) lin_load(c0, xrow, wrow, 128 * (c + 4));
+        lin_mma(c1, acc);
+        c += 4;
     }
+    if (w > 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) red[w - 1][i][j][lane] = acc[i][j];
+    }
+    __syncthreads();
+    if (w != 0) return;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j) {
+            const f32x4 v = acc[i][j] + red[0][i][j][lane] + red[1][i][j][lane] + red[2][i][j][lane];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = m0 + 16 * i + 4 * (lane >> 4) + r;
-                if (row < M) Y[(size_t)row * N + n0 + 16 * j + lr] = f32_to_bf16_bits(acc[i][j][r]);
+                if (row < M) Y[(size_t)row * N + n0 + 16 * j + lr] = f32_to_bf16_bits(v[r]);
             }
+        }
 }
 
 hipError_t launch_standin_linear(const void* X, const void* W, void* Y, int M, int K, int N, hipStream_t s)
 {
-    hipLaunchKernelGGL(standin_linear_kernel, dim3(N / 32, (M + 255) / 256), dim3(256), 0, s,
+    hipLaunchKernelGGL(standin_linear_kernel, dim3(N / 32, (M + 63) / 64), dim3(256), 0, s,
                        static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(W), static_cast<uint16_t*>(Y), M,
                        K, N);
     return hipGetLastError();
@@ -137,26 +171,36 @@ __global__ __launch_bounds__(256) void standin_attention_kernel(const uint16_t* 
     }
     for (int c0 = 64 * w; c0 < L; c0 += 256) {
         const int nt = min(64, L - c0);
-        // scores of the chunk's tokens, 4 per step; lanes of a row hold the row's sum
+        // the chunk's keys and values, 4 tokens per load instruction, all issued up front
+        u32x4 kw[16], vw[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int t = min(4 * u + tg, nt - 1);      // past the cache end: a valid row, never used
+            kw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + (size_t)(c0 + t) * D + ch));
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int t = min(4 * u + tg, nt - 1);
+            vw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + (size_t)(c0 + t) * D + ch));
+        }
+        // scores; the 16 lanes of a row hold the row's sum
+#pragma unroll
         for (int u = 0; u < 16; ++u) {
             const int t = 4 * u + tg;
             float part[QPK];
 #pragma unroll
             for (int h = 0; h < QPK; ++h) part[h] = 0.f;
-            if (t < nt) {
-                const u32x4 kw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + (size_t)(c0 + t) * D + ch));
-                const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w};
+            const uint32_t kk[4] = {kw[u].x, kw[u].y, kw[u].z, kw[u].w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float k0 = bf16_bits_to_f32((uint16_t)(kk[e] & 0xffff));
-                    const float k1 = bf16_bits_to_f32((uint16_t)(kk[e] >> 16));
+            for (int e = 0; e < 4; ++e) {
+                const float k0 = bf16_bits_to_f32((uint16_t)(kk[e] & 0xffff));
+                const float k1 = bf16_bits_to_f32((uint16_t)(kk[e] >> 16));
 #pragma unroll
-                    for (int h = 0; h < QPK; ++h) part[h] += qv[h][2 * e] * k0 + qv[h][2 * e + 1] * k1;
-                }
+                for (int h = 0; h < QPK; ++h) part[h] += qv[h][2 * e] * k0 + qv[h][2 * e + 1] * k1;
             }
 #pragma unroll
             for (int h = 0; h < QPK; ++h) part[h] = group_sum<16>(part[h]);
-            if ((lane & 15) == 0 && t < 64) {
+            if ((lane & 15) == 0) {
 #pragma unroll
                 for (int h = 0; h < QPK; ++h) ps[w][t][h] = t < nt ? part[h] : -INFINITY;
             }
@@ -182,20 +226,18 @@ __global__ __launch_bounds__(256) void standin_attention_kernel(const uint16_t* 
         for (int h = 0; h < QPK; ++h)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[h][e] *= corr[h];
-        // outputs: lane (token group tg, channels ch..ch+7) accumulates p * v
+        // outputs: lane (token group tg, channels ch..ch+7) accumulates p * v (p = 0 past the end)
+#pragma unroll
         for (int u = 0; u < 16; ++u) {
             const int t = 4 * u + tg;
-            if (t < nt) {
-                const u32x4 vw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + (size_t)(c0 + t) * D + ch));
-                const uint32_t vv[4] = {vw.x, vw.y, vw.z, vw.w};
+            const uint32_t vv[4] = {vw[u].x, vw[u].y, vw[u].z, vw[u].w};
 #pragma unroll
-                for (int h = 0; h < QPK; ++h) {
-                    const float p = ps[w][t][h];
+            for (int h = 0; h < QPK; ++h) {
+                const float p = ps[w][t][h];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        acc[h][2 * e] += p * bf16_bits_to_f32((uint16_t)(vv[e] & 0xffff));
-                        acc[h][2 * e + 1] += p * bf16_bits_to_f32((uint16_t)(vv[e] >> 16));
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    acc[h][2 * e] += p * bf16_bits_to_f32((uint16_t)(vv[e] & 0xffff));
+                    acc[h][2 * e + 1] += p * bf16_bits_to_f32((uint16_t)(vv[e] >> 16));
                 }
             }
         }
