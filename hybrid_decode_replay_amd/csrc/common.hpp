@@ -27,13 +27,21 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t v) {
     return __builtin_bit_cast(float, (uint32_t)v << 16);
 }
 
-// fp32 -> bf16, round to nearest even (NaN kept quiet).
+// fp32 -> bf16, round to nearest even (NaN kept quiet): gfx950's v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
+
+// e^x for the decay factors (x <= 0 in use): v_exp_f32 on x log2(e).  The
+// product's rounding changes the result by a relative 2^-24 |x log2 e|, about
+// 1e-6 for the decays of one window.
+__device__ __forceinline__ float fexp(float x) {
+    return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+// A value every lane of the wave holds the same copy of, moved to a scalar
+// register (index arithmetic on it then runs on the scalar unit).
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 template <int IO>
 __device__ __forceinline__ float ld_io(const void* p, size_t i) {

@@ -98,6 +98,7 @@ __global__ __launch_bounds__(256, NB <= 8 ? 6 : 4) void gdn_step_kernel(StepArgs
     G.hc = (size_t)b * a.H + h; G.gr = (size_t)b * a.G + g;
     G.b = b; G.h = h; G.g = g; G.B = a.B; G.H = a.H; G.G = a.G; G.cap = a.cap; G.C = C;
     G.c0 = c0; G.cw = cw;
+    G.ht = 1; G.xc_stride = 0; G.sc_stride = 0;
     G.len = len; G.bank = p.bank; G.V = V; G.T = T;
     G.xc = vs; G.xr = ks; G.xq = qs; G.s0 = al; G.s1 = be; G.p0 = nullptr;
 

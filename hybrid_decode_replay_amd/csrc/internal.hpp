@@ -61,6 +61,7 @@ struct StepArgs {
     const float* D;          // Mamba-2 D [H]
     void* y;                 // outputs [T][B][H][C]
     const uint8_t* active;   // [B] nonzero = the sequence takes part in the step (null = all)
+    int ht;                  // heads per workgroup (Mamba-2: 1, 2 or 4; a divisor of hpg)
 };
 
 // One translation unit per checkpoint dtype (mamba2.hip / mamba2_f16.hip, ...).

@@ -40,8 +40,13 @@
 
 namespace rs {
 
-template <int NB, int IO, int TMAX, bool MFMA_FOLD, int RC, int CK>
-__global__ __launch_bounds__(256, NB <= 8 ? 6 : 4) void mamba2_step_kernel(StepArgs a)
+// HT heads of one group per workgroup (HT = 1, 2 or 4; HT > 1 only with four
+// waves).  The sequence's bookkeeping, the group's B and C rows and the entry
+// staging are done once for the HT heads; the heads are then processed in turn,
+// and head hh+1's checkpoint (or read-copy) loads are issued before head hh's
+// arithmetic, so one head's stream overlaps the previous head's work.
+template <int NB, int IO, int TMAX, bool MFMA_FOLD, int RC, int CK, int HT>
+__global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2)) void mamba2_step_kernel(StepArgs a)
 {
     extern __shared__ float lds[];
     constexpr int R = NB * 16;
@@ -49,9 +54,9 @@ __global__ __launch_bounds__(256, NB <= 8 ? 6 : 4) void mamba2_step_kernel(StepA
     constexpr int PRE = 4;                      // chunks per thread fetched ahead of the checkpoint
     constexpr int VM = (16 + TMAX + 3) & ~3;    // bound on the entry count cap + T, padded to 4
     const int C = a.C;
-    const TileIdx tix = tile_of(xcd_tile_index(), a.H, a.nsplit);
-    const int b = tix.b, h = tix.h, tile = b * a.H + h;
-    const int g = h / a.hpg;
+    const TileIdx tix = tile_of(xcd_tile_index(), a.H / HT, a.nsplit);
+    const int b = tix.b, h0 = tix.h * HT;
+    const int g = h0 / a.hpg;
     const int cw = C / a.nsplit, c0 = tix.sp * cw;   // this workgroup's output columns
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -61,24 +66,25 @@ __global__ __launch_bounds__(256, NB <= 8 ? 6 : 4) void mamba2_step_kernel(StepA
     const size_t sB = (size_t)a.B;
 
     // ---- bookkeeping: identical decision in every workgroup of sequence b
-    const StepPlan p = plan_step(a, b, h == 0 && tix.sp == 0 && tid == 0);
+    const StepPlan p = plan_step(a, b, h0 == 0 && tix.sp == 0 && tid == 0);
     if (p.skip || (a.mode == MODE_FLUSH && p.f == 0)) return;
     const int f = p.f, len = p.len, T = a.T;
 
     // ---- LDS partition (floats; the launch sizes cs for max(T, 1) rows)
-    float* ds = lds;                              // [VM]       entry dt (vmax <= VM)
-    float* ps = ds + VM;                          // [VM]       inclusive prefix sums of dt
-    float* xs = ps + VM;                          // [vmax][cw] entry x rows (own columns)
-    float* bs = xs + (size_t)a.vmax * cw;         // [vmax][RS] entry B rows
-    float* cs = bs + (size_t)a.vmax * RS;         // [Tr][R]    read-out rows C_t
+    float* ds = lds;                              // [HT][VM]       entry dt (vmax <= VM)
+    float* ps = ds + HT * VM;                     // [HT][VM]       inclusive prefix sums of dt
+    float* xs = ps + HT * VM;                     // [HT][vmax][cw] entry x rows (own columns)
+    float* bs = xs + (size_t)HT * a.vmax * cw;    // [vmax][RS]     entry B rows
+    float* cs = bs + (size_t)a.vmax * RS;         // [Tr][R]        read-out rows C_t
 
     StageGeom G;
     G.bufc = a.bufc; G.bufr = a.bufr; G.bufs0 = a.bufs0; G.bufs1 = nullptr;
     G.in_c = a.in_c; G.in_r = a.in_r; G.in_q = a.in_q; G.in_s0 = a.in_s0; G.in_s1 = nullptr;
     G.bank_c = a.bank_c; G.bank_r = a.bank_r; G.bank_s = a.bank_s;
-    G.hc = (size_t)b * a.H + h; G.gr = (size_t)b * a.G + g;
-    G.b = b; G.h = h; G.g = g; G.B = a.B; G.H = a.H; G.G = a.G; G.cap = a.cap; G.C = C;
+    G.hc = (size_t)b * a.H + h0; G.gr = (size_t)b * a.G + g;
+    G.b = b; G.h = h0; G.g = g; G.B = a.B; G.H = a.H; G.G = a.G; G.cap = a.cap; G.C = C;
     G.c0 = c0; G.cw = cw;
+    G.ht = HT; G.xc_stride = a.vmax * cw; G.sc_stride = VM;
     G.len = len; G.bank = p.bank; G.V = p.V; G.T = T;
     G.xc = xs; G.xr = bs; G.xq = cs; G.s0 = ds; G.s1 = nullptr; G.p0 = ps;
 
@@ -88,158 +94,215 @@ __global__ __launch_bounds__(256, NB <= 8 ? 6 : 4) void mamba2_step_kernel(StepA
     ScalarRaw sr;
     stage_issue<IO, R, PRE, true>(stg, tid, nthr, pre, sr);
 
-    // ---- 2. checkpoint strip loads (128-bit, ckpt.hpp), decoded where first used
+    // ---- 2. checkpoint strip loads (128-bit, ckpt.hpp), decoded where first used;
     // a step that folds nothing reads the low-precision copy when there is one
-    const size_t strip_index = (size_t)tile * (C >> 4) + (c0 >> 4) + w;
-    f32x4 s[NB];
     bool from_copy = false;
     if constexpr (RC != RC_NONE) from_copy = (f == 0);
-    if (from_copy) {
-        if constexpr (RC != RC_NONE) rc_issue<NB, RC>(a.rcopy, a.rscale, strip_index, lane, s);
-    } else {
-        ckpt_issue<NB, CK>(a.ckpt, strip_index, lane, s);
-    }
+    auto issue = [&](int hh, f32x4 (&dst)[NB]) {
+        const size_t strip = (size_t)(b * a.H + h0 + hh) * (C >> 4) + (c0 >> 4) + w;
+        if (from_copy) {
+            if constexpr (RC != RC_NONE) rc_issue<NB, RC>(a.rcopy, a.rscale, strip, lane, dst);
+        } else {
+            ckpt_issue<NB, CK>(a.ckpt, strip, lane, dst);
+        }
+    };
+    f32x4 sbuf[HT > 1 ? 2 : 1][NB];
+    issue(0, sbuf[0]);
 
     // ---- 3. publish the staged rows
     stage_publish<IO, R, PRE>(stg, tid, nthr, pre, sr);
     __syncthreads();
-    // An fp16 checkpoint without a copy is decoded here: the shorter register
-    // life of the raw words keeps the kernel at six waves per SIMD, which beats
-    // overlapping the replay terms with the loads.
+    // An fp16 checkpoint without a copy is decoded as soon as it is needed at all:
+    // the shorter register life of the raw words keeps the kernel at more waves per
+    // SIMD, which beats overlapping the replay terms with the loads.
     constexpr bool EARLY_DECODE = CK == CK_F16 && RC == RC_NONE;
-    if constexpr (EARLY_DECODE) ckpt_decode<NB, CK>(s);
 
-    const float Ah = a.A[h];
-
-    // ---- 4. fold the first f entries into the checkpoint registers
-    // sums of dt over an entry range come from the prefix sums: sum_{lo<=i<hi} = ps[hi-1] - ps[lo-1]
-    // (with dt >= 0 and A_h <= 0 every exponent is <= 0 up to the rounding of that difference)
-    if (f > 0) {
-        if constexpr (!EARLY_DECODE) ckpt_decode<NB, CK>(s);
-        const float pf = ps[f - 1];
-        const float decay = expf(pf * Ah);
-        if constexpr (MFMA_FOLD) {
-            // D[n][p] += sum_i A[n][i] B[i][p] with A = B_i[n] (lane: n = l%16,
-            // i = l/16) and B = e^{..} dt_i x_i[p] (lane: i = l/16, p = l%16).
-            const int iq = lane >> 4;
-            float bop[4];
+    // B_j . C for the decode token: per group, so formed once for every head of the
+    // workgroup (lane quad jj holds entry f + jj; one token has at most 16 unfolded
+    // entries).  Several tokens form theirs per head below.
+    float dot1 = 0.f;
+    if constexpr (TMAX == 1) {
+        const int nr = len - f + 1;
+        if (a.mode != MODE_FLUSH && nr > 0) {
+            const int jj = lane >> 2, j = f + jj, q = lane & 3;
+            if (jj < nr) {
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const int i = kb * 4 + iq;
-                bop[kb] = (i < f) ? expf((pf - ps[i]) * Ah) * ds[i] * xs[i * cw + lc] : 0.f;
+                for (int i = 0; i < R / 16; ++i)
+                    dot1 += dot4(ld4(bs + j * RS + 16 * i + 4 * q), ld4(cs + 16 * i + 4 * q));
             }
-            const int nkb = (f + 3) >> 2;
+            dot1 = quad_sum(dot1);
+        }
+    }
+
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int hh = 0; hh < HT; ++hh) {
+        f32x4 (&s)[NB] = sbuf[hh & (HT > 1 ? 1 : 0)];
+        if constexpr (HT > 1) {
+            if (hh + 1 < HT) issue(hh + 1, sbuf[(hh + 1) & 1]);
+        }
+        const int h = h0 + hh;
+        const size_t strip_index = (size_t)(b * a.H + h) * (C >> 4) + (c0 >> 4) + w;
+        const float* dsh = ds + hh * VM;
+        const float* psh = ps + hh * VM;
+        const float* xsh = xs + (size_t)hh * a.vmax * cw;
+        if constexpr (EARLY_DECODE) ckpt_decode<NB, CK>(s);
+
+        const float Ah = a.A[h];
+
+        // ---- 4. fold the first f entries into the checkpoint registers
+        // sums of dt over an entry range come from the prefix sums: sum_{lo<=i<hi} = ps[hi-1] - ps[lo-1]
+        // (with dt >= 0 and A_h <= 0 every exponent is <= 0 up to the rounding of that difference)
+        if (f > 0) {
+            if constexpr (!EARLY_DECODE) ckpt_decode<NB, CK>(s);
+            const float pf = psh[f - 1];
+            const float decay = fexp(pf * Ah);
+            if constexpr (MFMA_FOLD) {
+                // D[n][p] += sum_i A[n][i] B[i][p] with A = B_i[n] (lane: n = l%16,
+                // i = l/16) and B = e^{..} dt_i x_i[p] (lane: i = l/16, p = l%16).
+                const int iq = lane >> 4;
+                float bop[4];
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
-                    if (kb < nkb) {
-                        const int i = kb * 4 + iq;
-                        const float av = (i < f) ? bs[i * RS + nb * 16 + (lane & 15)] : 0.f;
-                        acc = mfma16x16x4(av, bop[kb], acc);
-                    }
+                    const int i = kb * 4 + iq;
+                    bop[kb] = (i < f) ? fexp((pf - psh[i]) * Ah) * dsh[i] * xsh[i * cw + lc] : 0.f;
                 }
-                s[nb] = decay * s[nb] + acc;
-            }
-        } else {
-            float wx[16];
+                const int nkb = (f + 3) >> 2;
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                wx[i] = (i < f) ? expf((pf - ps[i]) * Ah) * ds[i] * xs[i * cw + lc] : 0.f;
+                for (int nb = 0; nb < NB; ++nb) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    for (int kb = 0; kb < 4; ++kb) {
+                        if (kb < nkb) {
+                            const int i = kb * 4 + iq;
+                            const float av = (i < f) ? bs[i * RS + nb * 16 + (lane & 15)] : 0.f;
+                            acc = mfma16x16x4(av, bop[kb], acc);
+                        }
+                    }
+                    s[nb] = decay * s[nb] + acc;
+                }
+            } else {
+                float wx[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    if (i < f) acc += wx[i] * ld4(bs + i * RS + nb * 16 + rq);
-                s[nb] = decay * s[nb] + acc;
+                    wx[i] = (i < f) ? fexp((pf - psh[i]) * Ah) * dsh[i] * xsh[i * cw + lc] : 0.f;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if (i < f) acc += wx[i] * ld4(bs + i * RS + nb * 16 + rq);
+                    s[nb] = decay * s[nb] + acc;
+                }
             }
         }
-    }
 
-    // the folded state takes the checkpoint's storage precision at once (fp16:
-    // RNE), so this step's outputs and the read copy see the stored values
-    if (f > 0) ckpt_round<NB, CK>(s);
-    // a checkpoint kept at the copy's precision is rounded as soon as it is folded
-    if constexpr (RC != RC_NONE) {
-        if (a.qckpt && f > 0) rc_roundtrip<NB, RC>(s);
-    }
+        // the folded state takes the checkpoint's storage precision at once (fp16:
+        // RNE), so this step's outputs and the read copy see the stored values
+        if (f > 0) ckpt_round<NB, CK>(s);
+        // a checkpoint kept at the copy's precision is rounded as soon as it is folded
+        if constexpr (RC != RC_NONE) {
+            if (a.qckpt && f > 0) rc_roundtrip<NB, RC>(s);
+        }
 
-    // ---- 5. outputs of the new tokens
-    if (a.mode != MODE_FLUSH) {
-        const float Dh = a.D[h];
+        // ---- 5. outputs of the new tokens
+        if (a.mode != MODE_FLUSH) {
+            const float Dh = a.D[h];
 #pragma unroll
-        for (int t = 0; t < TMAX; ++t) {
-            if (t < T) {
-                const int pos = len + t;
-                const float xt = xs[pos * cw + lc];
-                // replay of entries f..pos (formed first: it needs only LDS, so it runs while
-                // the checkpoint loads are in flight).  Lane quad jj = l/4 forms B_j . C_t and
-                // the decayed coefficient; output lanes gather the coefficients by readlane.
-                float rep = 0.f, gdec = 1.f;
-                if (pos >= f) {
-                    const int nr = pos - f + 1;
-                    const int q = lane & 3;
-                    for (int jj0 = 0; jj0 < nr; jj0 += 16) {
-                        const int jj = jj0 + (lane >> 2), j = f + jj;
-                        float dot = 0.f;
-                        if (jj < nr) {
+            for (int t = 0; t < TMAX; ++t) {
+                if (t < T) {
+                    const int pos = len + t;
+                    const float xt = xsh[pos * cw + lc];
+                    // replay of entries f..pos (formed first: it needs only LDS, so it runs while
+                    // the checkpoint loads are in flight).  Lane quad jj = l/4 forms B_j . C_t and
+                    // the decayed coefficient; output lanes gather the coefficients by readlane.
+                    float rep = 0.f, gdec = 1.f;
+                    if (pos >= f) {
+                        const int nr = pos - f + 1;
+                        const int q = lane & 3;
+                        const float* xcol = xsh + lc;
+                        const int pos_u = uni(pos), cw_u = uni(cw), f_u = uni(f);
+                        for (int jj0 = 0; jj0 < nr; jj0 += 16) {
+                            const int jj = jj0 + (lane >> 2), j = f + jj;
+                            float dot = dot1;
+                            if constexpr (TMAX > 1) {
+                                if (jj < nr) {
 #pragma unroll
-                            for (int i = 0; i < R / 16; ++i)
-                                dot += dot4(ld4(bs + j * RS + 16 * i + 4 * q), ld4(cs + t * R + 16 * i + 4 * q));
+                                    for (int i = 0; i < R / 16; ++i)
+                                        dot += dot4(ld4(bs + j * RS + 16 * i + 4 * q), ld4(cs + t * R + 16 * i + 4 * q));
+                                }
+                                dot = quad_sum(dot);
+                            }
+                            const float coef = (jj < nr) ? fexp((psh[pos] - psh[j]) * Ah) * dsh[j] * dot : 0.f;
+                            // entries past pos carry a zero coefficient; their row is clamped to a
+                            // staged one so the product stays finite (row offsets are scalar)
+                            // four entries per pass, passes while entries remain (nr is uniform)
+                            const int ne = uni(min(nr - jj0, 16));
+#pragma unroll
+                            for (int e4 = 0; e4 < 16; e4 += 4) {
+                                if (e4 < ne) {
+#pragma unroll
+                                    for (int e = e4; e < e4 + 4; ++e)
+                                        rep += readlane(coef, 4 * e) * xcol[uni(min(f_u + jj0 + e, pos_u) * cw_u)];
+                                }
+                            }
                         }
-                        dot = quad_sum(dot);
-                        const float coef = (jj < nr) ? expf((ps[pos] - ps[j]) * Ah) * ds[j] * dot : 0.f;
-                        // entries past pos carry a zero coefficient; their index is clamped to a
-                        // staged row so the product stays finite
-#pragma unroll
-                        for (int e = 0; e < 16; ++e)
-                            rep += readlane(coef, 4 * e) * xs[min(f + jj0 + e, pos) * cw + lc];
+                        gdec = fexp((psh[pos] - (f > 0 ? psh[f - 1] : 0.f)) * Ah);
                     }
-                    gdec = expf((ps[pos] - (f > 0 ? ps[f - 1] : 0.f)) * Ah);
-                }
-                // the checkpoint values are needed from here on
-                if (!EARLY_DECODE && t == 0 && f == 0) {
-                    if (from_copy) rc_decode<NB, RC>(s);
-                    else ckpt_decode<NB, CK>(s);
-                }
-                // checkpoint read-out (S' C_t)[col], reduced over the four row groups
-                float gacc = 0.f;
+                    // the checkpoint values are needed from here on
+                    if (!EARLY_DECODE && t == 0 && f == 0) {
+                        if (from_copy) rc_decode<NB, RC>(s);
+                        else ckpt_decode<NB, CK>(s);
+                    }
+                    // checkpoint read-out (S' C_t)[col], reduced over the four row groups
+                    float gacc = 0.f;
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) gacc += dot4(s[nb], ld4(cs + t * R + nb * 16 + rq));
-                gacc = sum_over_row_groups(gacc);
-                const float yv = (pos >= f) ? gdec * gacc + rep + Dh * xt : gacc + Dh * xt;
-                if (lane < 16) st_io<IO>(a.y, (((size_t)t * sB + b) * a.H + h) * C + col, yv);
+                    for (int nb = 0; nb < NB; ++nb) gacc += dot4(s[nb], ld4(cs + t * R + nb * 16 + rq));
+                    gacc = sum_over_row_groups(gacc);
+                    const float yv = (pos >= f) ? gdec * gacc + rep + Dh * xt : gacc + Dh * xt;
+                    if (lane < 16) st_io<IO>(a.y, (((size_t)t * sB + b) * a.H + h) * C + col, yv);
+                }
             }
         }
-    }
 
-    // ---- 6. single checkpoint write on a folding step
-    if (f > 0) {
-        ckpt_store<NB, CK>(a.ckpt, strip_index, lane, s);
-        if constexpr (RC != RC_NONE) rc_store<NB, RC>(a.rcopy, a.rscale, strip_index, lane, s);
+        // ---- 6. single checkpoint write on a folding step
+        if (f > 0) {
+            ckpt_store<NB, CK>(a.ckpt, strip_index, lane, s);
+            if constexpr (RC != RC_NONE) rc_store<NB, RC>(a.rcopy, a.rscale, strip_index, lane, s);
+        }
     }
 
     // ---- 7. append the unfolded new tokens to the buffer (slot = position - f)
     stage_append<IO, R>(G, a.bufc, a.bufr, a.bufs0, nullptr, p.bank_new, f, tid, nthr, tix.sp == 0,
-                        tix.sp == 0 && h % a.hpg == 0);
+                        tix.sp == 0 && h0 % a.hpg == 0);
 }
 
-template <int NB, int IO, int TMAX, bool MF, int RC, int CK>
-static hipError_t mamba2_launch_nb(const StepArgs& a, hipStream_t s)
+template <int NB, int IO, int TMAX, bool MF, int RC, int CK, int HT>
+static hipError_t mamba2_launch_ht(const StepArgs& a, hipStream_t s)
 {
     const size_t Tr = a.T > 0 ? a.T : 1;
     const size_t R = NB * 16;
     const size_t VM = (16 + TMAX + 3) & ~3;
-    const size_t lds = sizeof(float) * ((size_t)a.vmax * (a.C / a.nsplit + R + 4) + Tr * R + 2 * VM);
-    auto k = mamba2_step_kernel<NB, IO, TMAX, MF, RC, CK>;
+    const size_t lds = sizeof(float) * (HT * (size_t)a.vmax * (a.C / a.nsplit) + (size_t)a.vmax * (R + 4) + Tr * R +
+                                        2 * HT * VM);
+    auto k = mamba2_step_kernel<NB, IO, TMAX, MF, RC, CK, HT>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k, dim3(a.B * a.H * a.nsplit), dim3(a.C / a.nsplit * 4), lds, s, a);
+    hipLaunchKernelGGL(k, dim3(a.B * (a.H / HT) * a.nsplit), dim3(a.C / a.nsplit * 4), lds, s, a);
     return hipGetLastError();
+}
+
+// Heads per workgroup: a.ht (set by the host: 4 when four heads share a group and
+// the workgroup has four waves, else 1).  The four-head form is built for state
+// dimensions 64 and 128 and up to 4 new tokens per step; other launches use one head.
+template <int NB, int IO, int TMAX, bool MF, int RC, int CK>
+static hipError_t mamba2_launch_nb(const StepArgs& a, hipStream_t s)
+{
+    if constexpr ((NB == 4 || NB == 8) && TMAX <= 4 && MF) {
+        if (a.ht == 4) return mamba2_launch_ht<NB, IO, TMAX, MF, RC, CK, 4>(a, s);
+    }
+    return mamba2_launch_ht<NB, IO, TMAX, MF, RC, CK, 1>(a, s);
 }
 
 template <int IO, int TMAX, bool MF, int RC, int CK>

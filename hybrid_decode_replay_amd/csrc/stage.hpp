@@ -9,6 +9,10 @@
 // every thread in flight (call it before the checkpoint loads, so that
 // consuming the chunks later waits only for them); stage_publish() converts
 // them to fp32 in LDS.  The caller then needs one workgroup barrier.
+//
+// A workgroup may serve ht consecutive heads h..h+ht-1 of one group: their
+// per-head rows and scalars are staged side by side (xc_stride, sc_stride
+// floats apart), the group's rows once.
 #pragma once
 #include "common.hpp"
 
@@ -25,15 +29,18 @@ struct StageGeom {
     const void* in_s0;   // io dtype (Mamba-2 dt) or fp32 (GDN alpha)
     const float* in_s1;
     size_t bank_c, bank_r, bank_s;
-    size_t hc, gr;       // b*H + h, b*G + g
+    size_t hc, gr;       // b*H + h (first head), b*G + g
     int b, h, g, B, H, G, cap, C, len, bank, V, T;
     int c0, cw;          // column slice [c0, c0 + cw) of the per-head vectors this workgroup owns
-    float* xc;           // LDS [vmax][cw]
+    int ht;              // heads staged (h .. h + ht - 1, one group)
+    int xc_stride;       // floats between consecutive heads' xc rows
+    int sc_stride;       // floats between consecutive heads' scalars (s0, s1, p0)
+    float* xc;           // LDS [ht][vmax][cw]
     float* xr;           // LDS [vmax][R + 4]
     float* xq;           // LDS [T][R]
-    float* s0;           // LDS [vmax]
-    float* s1;           // LDS [vmax] or null
-    float* p0;           // LDS [vmax]: inclusive prefix sums of scalar 0, or null
+    float* s0;           // LDS [ht][sc_stride]
+    float* s1;           // LDS [ht][sc_stride] or null
+    float* p0;           // LDS [ht][sc_stride]: inclusive prefix sums of scalar 0, or null
 };
 
 template <int IO>
@@ -71,11 +78,12 @@ struct Stager {
     static constexpr int RS = R + 4;
 
     const StageGeom& G;
-    int CX, nx, nr, nch;
+    int CX, nxh, nx, nr, nch;
 
     __device__ explicit Stager(const StageGeom& g) : G(g) {
         CX = G.cw / EPC;
-        nx = G.V * CX;
+        nxh = G.V * CX;
+        nx = G.ht * nxh;
         nr = G.V * RX;
         nch = nx + nr + G.T * RX;
     }
@@ -84,9 +92,11 @@ struct Stager {
         size_t e;
         const void* base;
         if (ch < nx) {
-            const int j = ch / CX, o = ch - j * CX;
-            if (j < G.len) { base = G.bufc; e = (size_t)G.bank * G.bank_c + (G.hc * G.cap + j) * G.C + G.c0; }
-            else { base = G.in_c; e = (((size_t)(j - G.len) * G.B + G.b) * G.H + G.h) * G.C + G.c0; }
+            const int hh = G.ht == 1 ? 0 : ch / nxh;
+            const int r = ch - hh * nxh;
+            const int j = r / CX, o = r - j * CX;
+            if (j < G.len) { base = G.bufc; e = (size_t)G.bank * G.bank_c + ((G.hc + hh) * G.cap + j) * G.C + G.c0; }
+            else { base = G.in_c; e = (((size_t)(j - G.len) * G.B + G.b) * G.H + G.h + hh) * G.C + G.c0; }
             return reinterpret_cast<const uint4*>(static_cast<const char*>(base) + e * ES) + o;
         }
         ch -= nx;
@@ -103,7 +113,12 @@ struct Stager {
     }
 
     __device__ float* dst(int ch) const {
-        if (ch < nx) { const int j = ch / CX; return G.xc + j * G.cw + (ch - j * CX) * EPC; }
+        if (ch < nx) {
+            const int hh = G.ht == 1 ? 0 : ch / nxh;
+            const int r = ch - hh * nxh;
+            const int j = r / CX;
+            return G.xc + hh * G.xc_stride + j * G.cw + (r - j * CX) * EPC;
+        }
         ch -= nx;
         if (ch < nr) { const int j = ch / RX; return G.xr + j * RS + (ch - j * RX) * EPC; }
         ch -= nr;
@@ -112,9 +127,9 @@ struct Stager {
     }
 };
 
-// Raw bits of the per-entry scalars of one thread (entry index = tid < V).
-// They stay unconverted until published, so no conversion makes the wave
-// wait for the chunk loads before the checkpoint loads are issued.
+// Raw bits of the per-entry scalars of one thread: head tid / 32, entry tid % 32
+// (V <= 32).  They stay unconverted until published, so no conversion makes the
+// wave wait for the chunk loads before the checkpoint loads are issued.
 struct ScalarRaw {
     uint32_t s0 = 0, s0shift = 0, s1 = 0;
 };
@@ -133,10 +148,11 @@ __device__ __forceinline__ void stage_issue(const Stager<IO, R>& st, int tid, in
     // lane through a selected address: a branch per source would leave a register
     // written on one path and loaded on the other, and the wait that orders the two
     // would hold back the checkpoint loads behind every chunk issued above.
-    if (tid < G.V) {
-        const bool buffered = tid < G.len;
-        const size_t eb = (size_t)G.bank * G.bank_s + G.hc * G.cap + tid;
-        const size_t ei = ((size_t)max(tid - G.len, 0) * G.B + G.b) * G.H + G.h;
+    const int sh = tid >> 5, sj = tid & 31;
+    if (sh < G.ht && sj < G.V) {
+        const bool buffered = sj < G.len;
+        const size_t eb = (size_t)G.bank * G.bank_s + (G.hc + sh) * G.cap + sj;
+        const size_t ei = ((size_t)max(sj - G.len, 0) * G.B + G.b) * G.H + G.h + sh;
         if constexpr (S0_IS_IO && IO == IO_BF16) {
             // with bf16 io every buffered value is a bf16 widened to fp32 (low half
             // zero), so its upper half is the bf16 code itself
@@ -168,15 +184,18 @@ __device__ __forceinline__ void stage_publish(const Stager<IO, R>& st, int tid, 
         if (ch < st.nch) chunk_to_lds<IO>(st.dst(ch), pre[u]);
     }
     for (int ch = tid + PRE * nthr; ch < st.nch; ch += nthr) chunk_to_lds<IO>(st.dst(ch), *st.src(ch));
-    if (tid < G.V) {
-        G.s0[tid] = __builtin_bit_cast(float, sr.s0 << sr.s0shift);
-        if (G.s1) G.s1[tid] = __builtin_bit_cast(float, sr.s1);
+    const int sh = tid >> 5, sj = tid & 31;
+    const bool mine = sh < G.ht && sj < G.V;
+    if (mine) {
+        G.s0[sh * G.sc_stride + sj] = __builtin_bit_cast(float, sr.s0 << sr.s0shift);
+        if (G.s1) G.s1[sh * G.sc_stride + sj] = __builtin_bit_cast(float, sr.s1);
     }
-    // entries are at most 32 (cap + T), all in wave 0: prefix sums by a wave scan
-    if (G.p0 && tid < 64) {
-        const float v = tid < G.V ? __builtin_bit_cast(float, sr.s0 << sr.s0shift) : 0.f;
+    // entries are at most 32 (cap + T): one head's prefix sums per half wave (a
+    // 32-lane scan runs in lanes 0..31 and, independently, in lanes 32..63)
+    if (G.p0 && tid < 64 * ((G.ht + 1) >> 1)) {
+        const float v = mine ? __builtin_bit_cast(float, sr.s0 << sr.s0shift) : 0.f;
         const float ps = scan32_inclusive(v);
-        if (tid < G.V) G.p0[tid] = ps;
+        if (mine) G.p0[sh * G.sc_stride + sj] = ps;
     }
 }
 
@@ -194,14 +213,20 @@ __device__ __forceinline__ void stage_append(const StageGeom& G, void* bufc, voi
     const int nnew = G.V - j0;
     if (nnew <= 0) return;
     const int CX = G.cw / S::EPC;
-    char* bx = static_cast<char*>(bufc) + ((size_t)bank_new * G.bank_c + G.hc * G.cap * G.C + G.c0) * S::ES;
-    for (int i = tid; i < nnew * CX; i += nthr) {
-        const int jj = i / CX, o = i - jj * CX, j = j0 + jj;
-        reinterpret_cast<uint4*>(bx + (size_t)(j - f) * G.C * S::ES)[o] = lds_to_chunk<IO>(G.xc + j * G.cw + o * S::EPC);
+    for (int i = tid; i < G.ht * nnew * CX; i += nthr) {
+        const int hh = i / (nnew * CX), r = i - hh * nnew * CX;
+        const int jj = r / CX, o = r - jj * CX, j = j0 + jj;
+        char* bx = static_cast<char*>(bufc) + ((size_t)bank_new * G.bank_c + (G.hc + hh) * G.cap * G.C + G.c0) * S::ES;
+        reinterpret_cast<uint4*>(bx + (size_t)(j - f) * G.C * S::ES)[o] =
+            lds_to_chunk<IO>(G.xc + hh * G.xc_stride + j * G.cw + o * S::EPC);
     }
-    if (head_writer && tid < nnew) {
-        bufs0[(size_t)bank_new * G.bank_s + G.hc * G.cap + (j0 + tid - f)] = G.s0[j0 + tid];
-        if (bufs1) bufs1[(size_t)bank_new * G.bank_s + G.hc * G.cap + (j0 + tid - f)] = G.s1[j0 + tid];
+    if (head_writer) {
+        for (int i = tid; i < G.ht * nnew; i += nthr) {
+            const int hh = i / nnew, jj = i - hh * nnew;
+            const size_t slot = (size_t)bank_new * G.bank_s + (G.hc + hh) * G.cap + (j0 + jj - f);
+            bufs0[slot] = G.s0[hh * G.sc_stride + j0 + jj];
+            if (bufs1) bufs1[slot] = G.s1[hh * G.sc_stride + j0 + jj];
+        }
     }
     if (group_writer) {
         char* bb = static_cast<char*>(bufr) + ((size_t)bank_new * G.bank_r + G.gr * G.cap * R) * S::ES;
