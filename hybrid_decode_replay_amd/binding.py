@@ -30,6 +30,7 @@ DEVERR_COMMIT_CLAMPED = 0x1
 FLAG_VALU_FOLD = 0x1
 FLAG_QUANTIZED_CKPT = 0x2
 FLAG_STAGGER_FLUSH = 0x4
+FLAG_MX_SCALE_CEIL = 0x8
 
 
 class ReplayConfig(ctypes.Structure):

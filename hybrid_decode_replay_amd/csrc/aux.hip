@@ -207,7 +207,7 @@ hipError_t launch_logical_to_tiles(const void* in, void* ckpt, int tiles, int C,
 // kernels, so the quantizer is the one the flush path uses.
 template <int NB, int RC, int CK>
 __global__ __launch_bounds__(256) void quantize_rc_kernel(void* ckpt, uint8_t* codes, uint8_t* scales,
-                                                          size_t nstrips, int round_ckpt, int strips_per_tile, SlotMap m)
+                                                          size_t nstrips, int mode, int strips_per_tile, SlotMap m)
 {
     const size_t src_strip = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -215,9 +215,10 @@ __global__ __launch_bounds__(256) void quantize_rc_kernel(void* ckpt, uint8_t* c
     const size_t strip = map_block(src_strip, (size_t)strips_per_tile, m);
     f32x4 s[NB];
     ckpt_load<NB, CK>(ckpt, strip, lane, s);
-    rc_store<NB, RC>(codes, scales, strip, lane, s);
-    if (round_ckpt) {                              // checkpoint kept at the copy's precision
-        rc_roundtrip<NB, RC>(s);
+    const bool mx_ceil = (mode & QMODE_MX_CEIL) != 0;
+    rc_store<NB, RC>(codes, scales, strip, lane, s, mx_ceil);
+    if (mode & QMODE_ROUND_CKPT) {                 // checkpoint kept at the copy's precision
+        rc_roundtrip<NB, RC>(s, mx_ceil);
         ckpt_store<NB, CK>(ckpt, strip, lane, s);
     }
 }
@@ -265,7 +266,7 @@ __global__ __launch_bounds__(256) void rc_to_logical_kernel(const uint8_t* codes
 
 template <int RC, int CK>
 static hipError_t rc_dispatch(bool quantize, void* ckpt, const uint8_t* codes_in, const uint8_t* scales_in,
-                              uint8_t* codes, uint8_t* scales, int tiles, int C, int R, int round_ckpt,
+                              uint8_t* codes, uint8_t* scales, int tiles, int C, int R, int mode,
                               const SlotMap& m, hipStream_t s)
 {
     const size_t nstrips = (size_t)tiles * (C / 16);
@@ -274,7 +275,7 @@ static hipError_t rc_dispatch(bool quantize, void* ckpt, const uint8_t* codes_in
 #define RS_RC_CASE(NBV)                                                                                  \
     case NBV * 16:                                                                                       \
         if (quantize) hipLaunchKernelGGL((quantize_rc_kernel<NBV, RC, CK>), grid, block, 0, s, ckpt, codes, scales,   \
-                                         nstrips, round_ckpt, spt, m);                                  \
+                                         nstrips, mode, spt, m);                                  \
         else hipLaunchKernelGGL((rc_to_logical_kernel<NBV, RC>), grid, block, 0, s, codes_in, scales_in, codes, scales,    \
                                 nstrips, C);                                                             \
         return hipGetLastError();
@@ -282,7 +283,7 @@ static hipError_t rc_dispatch(bool quantize, void* ckpt, const uint8_t* codes_in
         case 16:
             if constexpr (RC == RC_FP8) {
                 if (quantize) hipLaunchKernelGGL((quantize_rc_kernel<1, RC, CK>), grid, block, 0, s, ckpt, codes, scales,
-                                                 nstrips, round_ckpt, spt, m);
+                                                 nstrips, mode, spt, m);
                 else hipLaunchKernelGGL((rc_to_logical_kernel<1, RC>), grid, block, 0, s, codes_in, scales_in, codes, scales,
                                         nstrips, C);
                 return hipGetLastError();
@@ -298,22 +299,25 @@ static hipError_t rc_dispatch(bool quantize, void* ckpt, const uint8_t* codes_in
 }
 
 hipError_t launch_quantize_read_copy(void* ckpt, uint8_t* codes, uint8_t* scales, int tiles, int C, int R, int rc,
-                                     int ck, bool round_ckpt, const SlotMap& m, hipStream_t s)
+                                     int ck, bool round_ckpt, bool mx_ceil, const SlotMap& m, hipStream_t s)
 {
+    const int ceil_bit = (mx_ceil && rc == RC_MXFP4) ? QMODE_MX_CEIL : 0;
+    const int mode = (round_ckpt ? QMODE_ROUND_CKPT : 0) | ceil_bit;
     if (ck == CK_FP8) {
         if (round_ckpt || rc != RC_MXFP4) return hipErrorInvalidValue;   // only an MXFP4 copy of an FP8 checkpoint
-        return rc_dispatch<RC_MXFP4, CK_FP8>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, 0, m, s);
+        return rc_dispatch<RC_MXFP4, CK_FP8>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, ceil_bit, m, s);
     }
     if (ck == CK_F16) {
         if (round_ckpt) return hipErrorInvalidValue;     // the quantized-checkpoint variant keeps fp32 storage
         if (rc == RC_FP8) return rc_dispatch<RC_FP8, CK_F16>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, 0, m, s);
-        if (rc == RC_MXFP4) return rc_dispatch<RC_MXFP4, CK_F16>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, 0, m, s);
+        if (rc == RC_MXFP4)
+            return rc_dispatch<RC_MXFP4, CK_F16>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, ceil_bit, m, s);
         return hipErrorInvalidValue;
     }
     if (rc == RC_FP8)
-        return rc_dispatch<RC_FP8, CK_F32>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, round_ckpt, m, s);
+        return rc_dispatch<RC_FP8, CK_F32>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, mode, m, s);
     if (rc == RC_MXFP4)
-        return rc_dispatch<RC_MXFP4, CK_F32>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, round_ckpt, m, s);
+        return rc_dispatch<RC_MXFP4, CK_F32>(true, ckpt, nullptr, nullptr, codes, scales, tiles, C, R, mode, m, s);
     return hipErrorInvalidValue;
 }
 

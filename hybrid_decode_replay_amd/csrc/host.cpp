@@ -122,8 +122,11 @@ replay_status check_config(const replay_config* c)
         return fail(REPLAY_ERR_DTYPE, "read_copy must be NONE, FP8_E4M3 or MXFP4");
     if (c->read_copy == REPLAY_MXFP4 && R % 32 != 0)
         return fail(REPLAY_ERR_SHAPE, "MXFP4 read copy needs state_dim divisible by 32");
-    if (c->flags & ~(REPLAY_FLAG_VALU_FOLD | REPLAY_FLAG_QUANTIZED_CKPT | REPLAY_FLAG_STAGGER_FLUSH))
+    if (c->flags & ~(REPLAY_FLAG_VALU_FOLD | REPLAY_FLAG_QUANTIZED_CKPT | REPLAY_FLAG_STAGGER_FLUSH |
+                     REPLAY_FLAG_MX_SCALE_CEIL))
         return fail(REPLAY_ERR_ARG, "unknown flags 0x%x", c->flags);
+    if ((c->flags & REPLAY_FLAG_MX_SCALE_CEIL) && c->read_copy != REPLAY_MXFP4)
+        return fail(REPLAY_ERR_ARG, "REPLAY_FLAG_MX_SCALE_CEIL applies to an MXFP4 read copy only");
     if ((c->flags & REPLAY_FLAG_QUANTIZED_CKPT) && c->read_copy == REPLAY_NONE)
         return fail(REPLAY_ERR_ARG, "REPLAY_FLAG_QUANTIZED_CKPT needs a read_copy format");
     if ((c->flags & REPLAY_FLAG_QUANTIZED_CKPT) && c->ckpt_dtype != REPLAY_F32)
@@ -247,6 +250,7 @@ rs::StepArgs step_args(const replay_state* st, const replay_inputs* in, void* y,
     a.nsplit = strips / wpg;
     a.ht = mamba2_heads_per_wg(c, wpg);
     a.qckpt = (c->flags & REPLAY_FLAG_QUANTIZED_CKPT) ? 1 : 0;
+    a.mxceil = (c->flags & REPLAY_FLAG_MX_SCALE_CEIL) ? 1 : 0;
     const replay_layout& L = st->lay;
     a.ckpt = at<void>(st, L.ckpt_off);
     a.rcopy = L.rcopy_bytes ? at<uint8_t>(st, L.rcopy_off) : nullptr;
@@ -428,7 +432,8 @@ static replay_status load_tiles(replay_state* st, const void* S, bool src_f32, i
     return LAUNCH(rs::launch_quantize_read_copy(at<void>(st, st->lay.ckpt_off), at<uint8_t>(st, st->lay.rcopy_off),
                                                 st->lay.rscale_bytes ? at<uint8_t>(st, st->lay.rscale_off) : nullptr,
                                                 ntiles, c->head_dim, c->state_dim, rc_kind(c), ck_kind(c),
-                                                (c->flags & REPLAY_FLAG_QUANTIZED_CKPT) != 0, m, hs),
+                                                (c->flags & REPLAY_FLAG_QUANTIZED_CKPT) != 0,
+                                                (c->flags & REPLAY_FLAG_MX_SCALE_CEIL) != 0, m, hs),
                   "read copy quantize");
 }
 

@@ -39,6 +39,7 @@ struct StepArgs {
     int vmax;                // LDS rows reserved for the virtual entry list
     int nsplit;              // workgroups per (b, h) tile, along the output axis
     int qckpt;               // nonzero: the checkpoint itself is kept at the copy's precision
+    int mxceil;              // nonzero: MXFP4 groups take the non-clipping shared exponent
     float scale;             // GDN output scale
     void* ckpt;              // fragment-ordered tiles (fp32 or fp16, ckpt.hpp)
     uint8_t* rcopy;          // read-copy codes (or null)
@@ -86,8 +87,12 @@ hipError_t launch_tiles_to_logical(const void* ckpt, void* out, int tiles, int C
 // tiles `m` names.
 hipError_t launch_logical_to_tiles(const void* in, void* ckpt, int tiles, int C, int R, int ck, bool src_f32,
                                    const SlotMap& m, hipStream_t s);
+// Mode bits of the read-copy quantizer.
+constexpr int QMODE_ROUND_CKPT = 0x1;   // round the checkpoint to the copy's grid too
+constexpr int QMODE_MX_CEIL = 0x2;      // MXFP4: non-clipping shared exponent
 hipError_t launch_quantize_read_copy(void* ckpt, uint8_t* codes, uint8_t* scales, int tiles,
-                                     int C, int R, int rc, int ck, bool round_ckpt, const SlotMap& m, hipStream_t s);
+                                     int C, int R, int rc, int ck, bool round_ckpt, bool mx_ceil, const SlotMap& m,
+                                     hipStream_t s);
 hipError_t launch_read_copy_to_logical(const uint8_t* codes, const uint8_t* scales, uint8_t* codes_out,
                                        uint8_t* scales_out, int tiles, int C, int R, int rc, hipStream_t s);
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t s);

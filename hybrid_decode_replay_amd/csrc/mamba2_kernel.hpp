@@ -201,7 +201,7 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
         if (f > 0) ckpt_round<NB, CK>(s);
         // a checkpoint kept at the copy's precision is rounded as soon as it is folded
         if constexpr (RC != RC_NONE) {
-            if (a.qckpt && f > 0) rc_roundtrip<NB, RC>(s);
+            if (a.qckpt && f > 0) rc_roundtrip<NB, RC>(s, a.mxceil);
         }
 
         // ---- 5. outputs of the new tokens
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
         // ---- 6. single checkpoint write on a folding step
         if (f > 0) {
             ckpt_store<NB, CK>(a.ckpt, strip_index, lane, s);
-            if constexpr (RC != RC_NONE) rc_store<NB, RC>(a.rcopy, a.rscale, strip_index, lane, s);
+            if constexpr (RC != RC_NONE) rc_store<NB, RC>(a.rcopy, a.rscale, strip_index, lane, s, a.mxceil);
         }
     }
 

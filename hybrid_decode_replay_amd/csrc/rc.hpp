@@ -46,12 +46,17 @@ __device__ __forceinline__ uint32_t pack_e4m3(f32x4 v)
 }
 
 // ---- FP4 E2M1 and the E8M0 shared exponent --------------------------------
-// Shared exponent X of a group with largest magnitude amax.
-__device__ __forceinline__ int mx_exponent(float amax)
+// Shared exponent X of a group with largest magnitude amax.  Default rule:
+// floor(log2 amax) minus E2M1's largest exponent (2), so amax / 2^X lies in
+// [4, 8) and the top of that range saturates at 6.  Non-clipping rule (ceil):
+// one step more when amax / 2^X > 6, i.e. when amax's significand exceeds 1.5,
+// which makes X the smallest exponent with amax <= 6 * 2^X.
+__device__ __forceinline__ int mx_exponent(float amax, bool ceil)
 {
-    const uint32_t ebits = (__builtin_bit_cast(uint32_t, amax) >> 23) & 0xffu;
+    const uint32_t bits = __builtin_bit_cast(uint32_t, amax);
+    const uint32_t ebits = (bits >> 23) & 0xffu;
     if (ebits == 0) return -127;                                 // zero or subnormal amax
-    const int X = (int)ebits - 127 - 2;
+    const int X = (int)ebits - 127 - 2 + ((ceil && (bits & 0x7fffffu) > 0x400000u) ? 1 : 0);
     return X < -127 ? -127 : (X > 127 ? 127 : X);
 }
 
@@ -181,7 +186,7 @@ __device__ __forceinline__ void rc_fp4_decode(const uint32_t (&w)[NB / 2], const
 
 template <int NB>
 __device__ __forceinline__ void rc_fp4_store(uint8_t* codes, uint8_t* scales, size_t strip_index, int lane,
-                                             const f32x4 (&s)[NB])
+                                             const f32x4 (&s)[NB], bool ceil)
 {
     static_assert(NB % 2 == 0, "MXFP4 groups need block pairs");
     constexpr int BPL = 2 * NB;
@@ -195,7 +200,7 @@ __device__ __forceinline__ void rc_fp4_store(uint8_t* codes, uint8_t* scales, si
                          fmaxf(fmaxf(__builtin_fabsf(b.x), __builtin_fabsf(b.y)), fmaxf(__builtin_fabsf(b.z), __builtin_fabsf(b.w))));
         am = fmaxf(am, __shfl_xor(am, 16, 64));      // the group spans lanes l%16 + 16*q
         am = fmaxf(am, __shfl_xor(am, 32, 64));
-        const int X = mx_exponent(am);
+        const int X = mx_exponent(am, ceil);
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
         w[p] = pack_e2m1(v, X);
         scw[p] = (uint32_t)(X + 127);
@@ -233,7 +238,7 @@ __device__ __forceinline__ void rc_fp8_roundtrip(f32x4 (&s)[NB])
 }
 
 template <int NB>
-__device__ __forceinline__ void rc_fp4_roundtrip(f32x4 (&s)[NB])
+__device__ __forceinline__ void rc_fp4_roundtrip(f32x4 (&s)[NB], bool ceil)
 {
     static_assert(NB % 2 == 0, "MXFP4 groups need block pairs");
 #pragma unroll
@@ -243,7 +248,7 @@ __device__ __forceinline__ void rc_fp4_roundtrip(f32x4 (&s)[NB])
                          fmaxf(fmaxf(__builtin_fabsf(b.x), __builtin_fabsf(b.y)), fmaxf(__builtin_fabsf(b.z), __builtin_fabsf(b.w))));
         am = fmaxf(am, __shfl_xor(am, 16, 64));
         am = fmaxf(am, __shfl_xor(am, 32, 64));
-        const int X = mx_exponent(am);
+        const int X = mx_exponent(am, ceil);
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
         const uint32_t word = pack_e2m1(v, X);
         const float scale = e8m0_to_f32((uint32_t)(X + 127));
@@ -257,18 +262,19 @@ __device__ __forceinline__ void rc_fp4_roundtrip(f32x4 (&s)[NB])
 }
 
 template <int NB, int RC>
-__device__ __forceinline__ void rc_roundtrip(f32x4 (&s)[NB])
+__device__ __forceinline__ void rc_roundtrip(f32x4 (&s)[NB], bool mx_ceil)
 {
     if constexpr (RC == RC_FP8) rc_fp8_roundtrip<NB>(s);
-    else if constexpr (RC == RC_MXFP4) rc_fp4_roundtrip<NB>(s);
+    else if constexpr (RC == RC_MXFP4) rc_fp4_roundtrip<NB>(s, mx_ceil);
 }
 
 // Refresh the read copy of one strip from its fp32 registers.
 template <int NB, int RC>
-__device__ __forceinline__ void rc_store(uint8_t* codes, uint8_t* scales, size_t strip_index, int lane, const f32x4 (&s)[NB])
+__device__ __forceinline__ void rc_store(uint8_t* codes, uint8_t* scales, size_t strip_index, int lane, const f32x4 (&s)[NB],
+                                         bool mx_ceil)
 {
     if constexpr (RC == RC_FP8) rc_fp8_store<NB>(codes, strip_index, lane, s);
-    else if constexpr (RC == RC_MXFP4) rc_fp4_store<NB>(codes, scales, strip_index, lane, s);
+    else if constexpr (RC == RC_MXFP4) rc_fp4_store<NB>(codes, scales, strip_index, lane, s, mx_ceil);
 }
 
 // Read-copy words of a strip, issued into the state registers (fp8: the word

@@ -118,6 +118,14 @@ typedef enum {
  * replay_flush ends the stagger for the sequences it folds.  Values do not
  * depend on when folds happen (up to rounding); only the flush schedule does. */
 #define REPLAY_FLAG_STAGGER_FLUSH 0x4
+/* MXFP4 read copy only (else REPLAY_ERR_ARG): give each 32-element group the
+ * smallest shared exponent X with amax <= 6 * 2^X, so that no element saturates
+ * (the default rule's X = floor(log2 amax) - 2, plus one when amax's
+ * significand exceeds 1.5).  The default rule is the conversion of the OCP
+ * Microscaling Formats specification; it clips amax / 2^X in (6, 8) to 6.
+ * Same layout and cost; only the E8M0 values and the codes of such groups
+ * differ. */
+#define REPLAY_FLAG_MX_SCALE_CEIL 0x8
 
 typedef struct {
     int32_t abi_version;  /* REPLAY_ABI_VERSION                                  */

@@ -224,6 +224,23 @@ int oracle_mxfp4_quantize_block(const double *v, int n, unsigned char *codes)
     return X + 127;
 }
 
+/* The same block quantization with the non-clipping scale rule: X is the   */
+/* smallest integer in [-127, 127] with amax <= 6 * 2^X (6 is E2M1's largest */
+/* magnitude), so no element saturates; 127 if there is none.  Found by a    */
+/* plain upward search; an all-zero block gets -127.                         */
+int oracle_mxfp4_quantize_block_ceil(const double *v, int n, unsigned char *codes)
+{
+    double amax = 0.0;
+    for (int i = 0; i < n; ++i) {
+        const double a = fabs(v[i]);
+        if (a > amax) amax = a;
+    }
+    int X = -127;
+    while (X < 127 && !(amax <= ldexp(6.0, X))) ++X;
+    for (int i = 0; i < n; ++i) codes[i] = (unsigned char)oracle_e2m1_encode(ldexp(v[i], -X));
+    return X + 127;
+}
+
 /* Bulk helpers over arrays (plain loops over the scalar definitions).      */
 void oracle_e4m3_encode_array(const double *v, long n, unsigned char *out)
 {
@@ -244,6 +261,14 @@ void oracle_mxfp4_quantize_array(const double *v, long nblocks,
 #pragma omp parallel for schedule(static)
     for (long b = 0; b < nblocks; ++b)
         scales[b] = (unsigned char)oracle_mxfp4_quantize_block(v + b * 32, 32, codes + b * 32);
+}
+
+void oracle_mxfp4_quantize_array_ceil(const double *v, long nblocks,
+                                      unsigned char *codes, unsigned char *scales)
+{
+#pragma omp parallel for schedule(static)
+    for (long b = 0; b < nblocks; ++b)
+        scales[b] = (unsigned char)oracle_mxfp4_quantize_block_ceil(v + b * 32, 32, codes + b * 32);
 }
 
 void oracle_mxfp4_dequantize_array(const unsigned char *codes, const unsigned char *scales,

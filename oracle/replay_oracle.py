@@ -125,6 +125,10 @@ def configure(L):
     L.oracle_e4m3_decode_array.restype = None
     L.oracle_mxfp4_quantize_array.argtypes = [_dp, ctypes.c_long, _ubp, _ubp]
     L.oracle_mxfp4_quantize_array.restype = None
+    L.oracle_mxfp4_quantize_array_ceil.argtypes = [_dp, ctypes.c_long, _ubp, _ubp]
+    L.oracle_mxfp4_quantize_array_ceil.restype = None
+    L.oracle_mxfp4_quantize_block_ceil.argtypes = [_dp, i, _ubp]
+    L.oracle_mxfp4_quantize_block_ceil.restype = i
     L.oracle_mxfp4_dequantize_array.argtypes = [_ubp, _ubp, ctypes.c_long, _dp]
     L.oracle_mxfp4_dequantize_array.restype = None
     L.oracle_threads.argtypes = []
@@ -237,8 +241,10 @@ def e4m3_decode(codes):
     return out
 
 
-def mxfp4_quantize(v):
-    """v [..., 32k]: blocks of 32 along the last axis.
+def mxfp4_quantize(v, rule="floor"):
+    """v [..., 32k]: blocks of 32 along the last axis.  rule "floor": the OCP shared
+    exponent floor(log2(amax)) - 2 (a block maximum may clip to 6); "ceil": the smallest
+    exponent with amax <= 6 * 2^X (nothing clips).
 
     Returns (codes uint8 [..., 32k] one 4-bit code per byte, scales uint8 [..., k])."""
     v = np.asarray(v, np.float64)
@@ -248,7 +254,8 @@ def mxfp4_quantize(v):
     flat, fp = _f64(v.reshape(nb, 32))
     codes = np.empty((nb, 32), np.uint8)
     scales = np.empty(nb, np.uint8)
-    lib().oracle_mxfp4_quantize_array(fp, nb, codes.ctypes.data_as(_ubp), scales.ctypes.data_as(_ubp))
+    fn = {"floor": lib().oracle_mxfp4_quantize_array, "ceil": lib().oracle_mxfp4_quantize_array_ceil}[rule]
+    fn(fp, nb, codes.ctypes.data_as(_ubp), scales.ctypes.data_as(_ubp))
     return codes.reshape(*lead, v.shape[-1]), scales.reshape(*lead, v.shape[-1] // 32)
 
 
@@ -265,14 +272,15 @@ def mxfp4_dequantize(codes, scales):
 def read_copy_values(S_fp64, fmt):
     """Dequantized read copy of a checkpoint image: round to fp32, quantize, dequantize.
 
-    Blocks (MXFP4) run along the last axis (N for Mamba-2, d_k for GDN)."""
+    Blocks (MXFP4) run along the last axis (N for Mamba-2, d_k for GDN); "mxfp4_ceil" is
+    MXFP4 with the non-clipping scale rule."""
     s32 = np.asarray(S_fp64, np.float64).astype(np.float32).astype(np.float64)
     if fmt is None:
         return s32
     if fmt == "fp8":
         return e4m3_decode(e4m3_encode(s32)).reshape(s32.shape)
-    if fmt == "mxfp4":
-        c, s = mxfp4_quantize(s32)
+    if fmt in ("mxfp4", "mxfp4_ceil"):
+        c, s = mxfp4_quantize(s32, "ceil" if fmt == "mxfp4_ceil" else "floor")
         return mxfp4_dequantize(c, s)
     raise ValueError(fmt)
 
@@ -294,6 +302,8 @@ class _Session:
                  seq_ids=None):
         if not 1 <= cap <= 16:
             raise ValueError("buffer capacity must be in [1, 16]")
+        if read_copy not in (None, "fp8", "mxfp4", "mxfp4_ceil"):
+            raise ValueError("read copy must be None, 'fp8', 'mxfp4' or 'mxfp4_ceil'")
         if quantized_ckpt and read_copy is None:
             raise ValueError("a quantized checkpoint needs a format")
         if ckpt_dtype not in ("f32", "f16", "fp8"):

@@ -165,6 +165,8 @@ class Pair:
         self.st = rb.ReplayState(self.cfg)
         self.st.load_checkpoint(torch.from_numpy(S0).cuda())
         rc = {rb.NONE: None, rb.FP8_E4M3: "fp8", rb.MXFP4: "mxfp4"}[read_copy]
+        if rc == "mxfp4" and flags & rb.FLAG_MX_SCALE_CEIL:
+            rc = "mxfp4_ceil"                       # the non-clipping shared exponent
         self.rc = rc
         cd = {rb.F16: "f16", rb.FP8_E4M3: "fp8"}.get(ckpt, "f32")
         self.fp8b = Fp8Bound(self.kname, (B, H, C, R), exact=(self.tol == 0.0)) if self.fp8 else None

@@ -49,11 +49,14 @@ def test_config_validation_codes():
         (dict(head_dim=272), rb.ERR_SHAPE), (dict(state_dim=96), rb.ERR_SHAPE), (dict(buf_cap=0), rb.ERR_SHAPE),
         (dict(buf_cap=17), rb.ERR_SHAPE), (dict(io_dtype=rb.F16), rb.ERR_DTYPE), (dict(kind=7), rb.ERR_ARG),
         (dict(flags=0x80), rb.ERR_ARG), (dict(read_copy=rb.BF16), rb.ERR_DTYPE),
+        (dict(flags=rb.FLAG_MX_SCALE_CEIL), rb.ERR_ARG),
+        (dict(flags=rb.FLAG_MX_SCALE_CEIL, read_copy=rb.FP8_E4M3), rb.ERR_ARG),
     ]
     for kw, want in cases:
         assert rb.config_check(_cfg(**kw)) == want, kw
         assert rb.state_bytes(_cfg(**kw)) == 0
         assert rb.lib().replay_last_error()
+    assert rb.config_check(_cfg(flags=rb.FLAG_MX_SCALE_CEIL, read_copy=rb.MXFP4)) == rb.OK
     bad = _cfg()
     bad.abi_version = 2
     assert rb.config_check(bad) == rb.ERR_ARG

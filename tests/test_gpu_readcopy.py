@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 
 from hybrid_decode_replay_amd import synth  # noqa: E402
 
-FORMATS = ["fp8", "mxfp4"]
+FORMATS = ["fp8", "mxfp4", "mxfp4_ceil"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -40,7 +40,15 @@ def rb():
 
 def rc_code(fmt):
     b = rb()
-    return {"fp8": b.FP8_E4M3, "mxfp4": b.MXFP4}[fmt]
+    return {"fp8": b.FP8_E4M3, "mxfp4": b.MXFP4, "mxfp4_ceil": b.MXFP4}[fmt]
+
+
+def rc_flags(fmt):
+    return rb().FLAG_MX_SCALE_CEIL if fmt == "mxfp4_ceil" else 0
+
+
+def mx_rule(fmt):
+    return "ceil" if fmt == "mxfp4_ceil" else "floor"
 
 
 def planted_checkpoint(seed, shape):
@@ -66,7 +74,8 @@ def test_quantizer_bit_exact_at_load(fmt, kind, C, R):
     from oracle import replay_oracle as ro
     b = rb()
     B, H = 3, 2
-    cfg = b.make_config(b.MAMBA2 if kind == "mamba2" else b.GDN, B, H, H, C, R, 16, b.F32, read_copy=rc_code(fmt))
+    cfg = b.make_config(b.MAMBA2 if kind == "mamba2" else b.GDN, B, H, H, C, R, 16, b.F32, read_copy=rc_code(fmt),
+                        flags=rc_flags(fmt))
     st = b.ReplayState(cfg)
     S0 = planted_checkpoint(40 + C + R, (B, H, C, R))
     st.load_checkpoint(torch.from_numpy(S0).cuda())
@@ -77,7 +86,7 @@ def test_quantizer_bit_exact_at_load(fmt, kind, C, R):
         want = ro.e4m3_encode(S0.astype(np.float64)).reshape(S0.shape)
         np.testing.assert_array_equal(codes, want)
     else:
-        wc, ws = ro.mxfp4_quantize(S0.astype(np.float64))
+        wc, ws = ro.mxfp4_quantize(S0.astype(np.float64), mx_rule(fmt))
         np.testing.assert_array_equal(codes, wc)
         np.testing.assert_array_equal(scales.cpu().numpy(), ws)
 
@@ -127,8 +136,9 @@ def mxfp4_sweep_groups(seed):
     """32-element groups whose largest magnitude is 7.9 * 2^X (shared exponent X), the
     other elements walking -7 .. 7 times 2^X in steps of 1/8 (every E2M1 value, every tie
     between neighbours, values past saturation), each group also with every element one
-    fp32 ulp up and one down; X from -126 to 100; a group with a subnormal maximum, an
-    all-zero group and scaled N(0, 1) groups."""
+    fp32 ulp up and one down; X from -126 to 100; groups whose maximum is exactly 6 * 2^X
+    or one fp32 ulp either side of it (the boundary of the non-clipping rule); a group
+    with a subnormal maximum, an all-zero group and scaled N(0, 1) groups."""
     rng = np.random.default_rng(seed)
     grid = np.arange(-56, 57) / 8.0
     groups = []
@@ -143,6 +153,13 @@ def mxfp4_sweep_groups(seed):
                 h = g.copy() if d is None else np.nextafter(g, np.float32(d))
                 h[31] = g[31]
                 groups.append(h)
+    for X in (-125, -1, 0, 5, 120):
+        base = (rng.uniform(-5.5, 5.5, 32) * 2.0 ** X).astype(np.float32)
+        top = np.float32(6.0 * 2.0 ** X)
+        for m in (top, np.nextafter(top, np.float32(np.inf)), np.nextafter(top, np.float32(0))):
+            h = base.copy()
+            h[rng.integers(32)] = -m if X % 2 else m
+            groups.append(h)
     groups.append((np.arange(32) * 2.0 ** -140).astype(np.float32))      # subnormal maximum
     groups.append(np.zeros(32, np.float32))
     for _ in range(64):
@@ -150,15 +167,17 @@ def mxfp4_sweep_groups(seed):
     return np.stack(groups)
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp4_ceil"])
 @pytest.mark.parametrize("kind,C,R", [("mamba2", 64, 128), ("gdn", 128, 128)])
-def test_mxfp4_encoder_every_tie(kind, C, R):
+def test_mxfp4_encoder_every_tie(kind, C, R, fmt):
     """The kernels' MXFP4 encoder (shared exponent and element codes) against the
     oracle's on the groups above, placed along the reduction axis of an N(0, 0.1)
-    checkpoint (codes and scales compared bit for bit)."""
+    checkpoint (codes and scales compared bit for bit), under both scale rules."""
     from oracle import replay_oracle as ro
     b = rb()
     B, H = 2, 2
-    cfg = b.make_config(b.MAMBA2 if kind == "mamba2" else b.GDN, B, H, H, C, R, 16, b.F32, read_copy=b.MXFP4)
+    cfg = b.make_config(b.MAMBA2 if kind == "mamba2" else b.GDN, B, H, H, C, R, 16, b.F32, read_copy=b.MXFP4,
+                        flags=rc_flags(fmt))
     st = b.ReplayState(cfg)
     S0 = synth.checkpoint(80 + C, (B, H, C, R)).astype(np.float32)
     groups = mxfp4_sweep_groups(81)
@@ -168,7 +187,7 @@ def test_mxfp4_encoder_every_tie(kind, C, R):
     st.load_checkpoint(torch.from_numpy(S0).cuda())
     codes, scales = st.read_copy()
     torch.cuda.synchronize()
-    wc, ws = ro.mxfp4_quantize(S0.astype(np.float64))
+    wc, ws = ro.mxfp4_quantize(S0.astype(np.float64), mx_rule(fmt))
     np.testing.assert_array_equal(scales.cpu().numpy(), ws)
     np.testing.assert_array_equal(codes.cpu().numpy(), wc)
 
@@ -178,7 +197,7 @@ def _pair(kind, fmt, B, H, C, R, cap, seed, io=None):
     b = rb()
     S0 = synth.checkpoint(seed, (B, H, C, R))
     return Pair(b.MAMBA2 if kind == "mamba2" else b.GDN, B, H, H, C, R, cap=cap, io=io or b.F32, seed=seed, S0=S0,
-                read_copy=rc_code(fmt))
+                read_copy=rc_code(fmt), flags=rc_flags(fmt))
 
 
 def _tokens(kind, seed, T, B, H, C, R, io="f32"):
@@ -212,8 +231,8 @@ def test_copy_tracks_checkpoint_and_never_feeds_the_recurrence(fmt, kind):
     kk = b.MAMBA2 if kind == "mamba2" else b.GDN
     S0 = synth.checkpoint(70, (B, H, C, R))
     states = {}
-    for name, rc in (("plain", b.NONE), ("copy", rc_code(fmt))):
-        st = b.ReplayState(b.make_config(kk, B, H, H, C, R, cap, b.F32, read_copy=rc))
+    for name, rc, fl in (("plain", b.NONE, 0), ("copy", rc_code(fmt), rc_flags(fmt))):
+        st = b.ReplayState(b.make_config(kk, B, H, H, C, R, cap, b.F32, read_copy=rc, flags=fl))
         st.load_checkpoint(torch.from_numpy(S0).cuda())
         states[name] = st
     toks = _tokens(kind, 70, T, B, H, C, R)
@@ -235,7 +254,7 @@ def test_copy_tracks_checkpoint_and_never_feeds_the_recurrence(fmt, kind):
         if fmt == "fp8":
             np.testing.assert_array_equal(codes.cpu().numpy(), ro.e4m3_encode(ck).reshape(ck.shape))
         else:
-            wc, ws = ro.mxfp4_quantize(ck)
+            wc, ws = ro.mxfp4_quantize(ck, mx_rule(fmt))
             np.testing.assert_array_equal(codes.cpu().numpy(), wc)
             np.testing.assert_array_equal(scales.cpu().numpy(), ws)
 
@@ -255,34 +274,56 @@ def test_spec_with_read_copy(fmt, kind):
 
 @pytest.mark.parametrize("fmt", FORMATS)
 def test_bf16_io_read_copy_full_size_sample(fmt):
-    """The batch-128 GDN layer (32 heads, d = 128, bf16 io) with an FP8 or MXFP4 copy, 48
-    steps (three folds, each re-making the copy from the stored checkpoint): outputs of
-    sampled sequences against the oracle's read-copy semantics (non-flush steps read the
+    """The batch-128 GDN layer (32 heads, d = 128, bf16 io) with a read copy, 48 steps
+    (three folds, each re-making the copy from the stored checkpoint): outputs of sampled
+    sequences against the oracle's read-copy semantics (non-flush steps read the
     dequantized copy, folding steps the fp32 checkpoint), the fp32 checkpoint within 1e-4,
-    bookkeeping bit-exact."""
+    bookkeeping bit-exact.  The fp32 and fp64 fold results differ by rounding, so a value
+    or a group maximum next to a quantization boundary can land on different codes; the
+    outputs after a fold are held to the bf16 tolerance plus the read-out of the measured
+    difference between the two sides' dequantized copies (tests/harness.py)."""
+    from harness import readout_bound
     from oracle import replay_oracle as ro
     b = rb()
-    B, H, D, T = 128, 32, 128, 48
-    cfg = b.make_config(b.GDN, B, H, H, D, D, 16, b.BF16, read_copy=rc_code(fmt))
+    B, H, D, T, cap = 128, 32, 128, 48, 16
+    cfg = b.make_config(b.GDN, B, H, H, D, D, cap, b.BF16, read_copy=rc_code(fmt), flags=rc_flags(fmt))
     st = b.ReplayState(cfg)
     S0 = synth.checkpoint_device(4, (B, H, D, D), "cuda")
     st.load_checkpoint(S0)
     toks = synth.gdn_tokens_device(4, T, B, H, H, D, D, "cuda")
     ys = torch.empty((T, B, H, D), dtype=torch.bfloat16, device="cuda")
+    sample = [0, 77, 127]
+    copies = {}
     print(f"[full-size gdn {fmt} copy] launching", flush=True)
     for t in range(T):
         st.decode({k: v[t:t + 1] for k, v in toks.items()}, y=ys[t:t + 1])
+        if (t + 1) % cap == 0:
+            codes, scales = st.read_copy()
+            codes = codes[sample].cpu().numpy()
+            if fmt == "fp8":
+                copies[t] = ro.e4m3_decode(codes).reshape(codes.shape)
+            else:
+                copies[t] = ro.mxfp4_dequantize(codes, scales[sample].cpu().numpy()).reshape(codes.shape)
     ck = st.read_checkpoint()
     L, Pd, F, E = st.read_book()
     torch.cuda.synchronize()
     assert torch.all(L == 0) and torch.all(F == 3) and torch.all(Pd == 0) and int(E[0]) == 0
-    sample = [0, 77, 127]
     sess = ro.GDNSession(S0[sample].cpu().numpy(), read_copy=fmt)
     host = {k: v[:, sample].float().cpu().numpy() for k, v in toks.items()}
-    yg = ys[:, sample].float().cpu().numpy()
+    yg = ys[:, sample].float().cpu().numpy().astype(np.float64)
+    dS = np.zeros((len(sample), H, D, D))
+    worst = 0.0
     for t in range(T):
-        err = ro.normwise_error(yg[t], sess.decode(synth.token(host, t)))
-        assert err <= 2e-2, (t, err)
+        tok = synth.token(host, t)
+        yo = sess.decode(tok)
+        allow = 2e-2 * np.max(np.abs(yo), axis=-1, keepdims=True) + readout_bound("gdn", dS, [tok])[0]
+        assert not np.any(np.abs(yg[t] - yo) > allow), t
+        worst = max(worst, ro.normwise_error(yg[t], yo))
+        if (t + 1) % cap == 0:
+            mine = ro.read_copy_values(sess.ckpt, fmt).reshape(sess.ckpt.shape)
+            dS = np.abs(copies[t] - mine)
+            print(f"  fold at step {t}: copy elements that differ {np.count_nonzero(dS)} of {dS.size}", flush=True)
+    print(f"  worst normwise output error {worst:.3e}", flush=True)
     err_ck = ro.normwise_error(ck[sample].cpu().numpy(), sess.ckpt, axis=(2, 3))
     assert err_ck <= 1e-4, err_ck
 
@@ -299,7 +340,7 @@ def test_quantized_checkpoint_variant(fmt, kind):
     B, H, C, R, cap = 2, 2, 32, 64, 6
     S0 = synth.checkpoint(90, (B, H, C, R))
     pair = Pair(b.MAMBA2 if kind == "mamba2" else b.GDN, B, H, H, C, R, cap=cap, io=b.F32, seed=90, S0=S0,
-                read_copy=rc_code(fmt), flags=b.FLAG_QUANTIZED_CKPT)
+                read_copy=rc_code(fmt), flags=b.FLAG_QUANTIZED_CKPT | rc_flags(fmt))
     # the oracle session of the harness keeps a full-precision checkpoint; use the variant's
     pair.orc = (ro.Mamba2Session(pair.orc.A, pair.orc.D, S0, cap=cap, read_copy=fmt, quantized_ckpt=True)
                 if kind == "mamba2" else ro.GDNSession(S0, cap=cap, read_copy=fmt, quantized_ckpt=True))

@@ -34,8 +34,10 @@ MUTANTS = {
     "e4m3_bias8": ("ldexp(1.0 + (double)m / 8.0, e - 7)", "ldexp(1.0 + (double)m / 8.0, e - 8)"),
     "e2m1_ties_odd": ("(err == best_err && (c & 1) == 0)) {\n            best = c;\n            best_err = err;\n        }\n    }\n    return sign | best;        /*",
                       "(err == best_err && (c & 1) == 1)) {\n            best = c;\n            best_err = err;\n        }\n    }\n    return sign | best;        /*"),
-    "mx_scale_off_by_one": ("X = (e2 - 1) - 2;", "X = (e2 - 1) - 1;"),
-    "mx_no_saturation_floor": ("X = (e2 - 1) - 2;", "X = e2 - 2;"),
+    "mx_scale_off_by_one": ("X = (e2 - 1) - 2;          /*", "X = (e2 - 1) - 1;          /*"),
+    "mx_no_saturation_floor": ("X = (e2 - 1) - 2;          /*", "X = e2 - 2;          /*"),
+    "mx_ceil_strict": ("!(amax <= ldexp(6.0, X))", "!(amax < ldexp(6.0, X))"),
+    "mx_ceil_is_floor_plus_one": ("!(amax <= ldexp(6.0, X))", "!(amax < ldexp(4.0, X))"),
 }
 
 PIN_TESTS = [
@@ -55,6 +57,7 @@ PIN_TESTS = [
     pins.test_e4m3_encode_matches_torch_cast_in_range,
     pins.test_e2m1_table_and_ties,
     pins.test_mxfp4_block_scale_rule,
+    pins.test_mxfp4_ceil_scale_rule,
 ]
 
 

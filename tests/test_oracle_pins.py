@@ -336,6 +336,51 @@ def test_mxfp4_error_bound():
         np.testing.assert_allclose(np.abs(np.abs(deq[i]) / scale[i] - np.minimum(r, 6.0)), best, atol=1e-12)
 
 
+def test_mxfp4_ceil_scale_rule():
+    """Non-clipping rule: X is the smallest exponent with amax <= 6 * 2^X.  Hand cases
+    (6 fits X = 0 exactly; 7 and 6(1 + 2^-20) need X = 1 where the default rule clips at
+    X = 0; 3 fits X = -1; 12 fits X = 1 like the default rule), the relation to the
+    default rule (the same X or one more, one more exactly when the default rule's
+    amax / 2^X exceeds 6), and that no element saturates."""
+    cases = [(6.0, 127), (7.0, 128), (6.0 * (1 + 2.0 ** -20), 128), (4.0, 127), (8.0, 128), (12.0, 128),
+             (12.5, 129), (3.0, 126), (3.1, 127), (0.3, 123), (0.38, 124), (2.0 ** -140, 0)]
+    for amax, scale_code in cases:
+        v = np.zeros(32)
+        v[7] = -amax
+        v[20] = amax / 5
+        _, scales = ro.mxfp4_quantize(v, "ceil")
+        assert scales[0] == scale_code, (amax, scales[0])
+    codes, scales = ro.mxfp4_quantize(np.zeros(32), "ceil")
+    assert scales[0] == 0 and not codes.any()
+    # hand example: amax 7 -> X = 1; 7/2 = 3.5 ties between 3 and 4 -> 4 (even code 6) -> 8;
+    # under the default rule (X = 0) the same 7 saturates to 6
+    v = np.zeros(32)
+    v[:3] = [7.0, -1.3, 0.2]
+    codes, scales = ro.mxfp4_quantize(v, "ceil")
+    assert scales[0] == 128 and list(codes[:3]) == [6, 8 | 1, 0]
+    assert list(ro.mxfp4_dequantize(codes, scales)[:3]) == [8.0, -1.0, 0.0]
+    cf, sf = ro.mxfp4_quantize(v)
+    assert sf[0] == 127 and ro.mxfp4_dequantize(cf, sf)[0] == 6.0
+    rng = np.random.default_rng(12)
+    v = rng.standard_normal((400, 32)) * 2.0 ** rng.integers(-30, 30, (400, 1))
+    v[:50, 3] = 6.0 * 2.0 ** rng.integers(-20, 20, 50)           # exactly on the boundary
+    codes, scales = ro.mxfp4_quantize(v, "ceil")
+    _, sfloor = ro.mxfp4_quantize(v)
+    amax = np.max(np.abs(v), axis=1)
+    X = scales.reshape(-1).astype(np.int64) - 127
+    for i in range(v.shape[0]):                                   # brute-force minimality
+        fits = [x for x in range(-127, 128) if amax[i] <= 6.0 * 2.0 ** x]
+        assert X[i] == fits[0], i
+    Xf = sfloor.reshape(-1).astype(np.int64) - 127
+    assert np.array_equal(X - Xf, (amax / 2.0 ** Xf > 6.0).astype(np.int64))
+    deq = ro.mxfp4_dequantize(codes, scales)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    r = np.abs(v) / 2.0 ** X[:, None]
+    assert np.all(r <= 6.0)
+    best = np.min(np.abs(grid[None, None, :] - r[:, :, None]), axis=2)
+    np.testing.assert_allclose(np.abs(np.abs(deq) / 2.0 ** X[:, None] - r), best, atol=1e-12)
+
+
 # --------------------------------------------------------------------------
 # Bookkeeping: hand-derived golden trace
 # --------------------------------------------------------------------------
