@@ -4,9 +4,11 @@
 // it, read out the output, store the state ([DE] "ReplaySSM beschleunigt das
 // Decoding ...", section "Wie es funktioniert" describes this step and why
 // it is memory-bound).  The state is the plain logical tile [C][R] (Mamba-2
-// [P][N], GDN [DV][DK]) in fp32, fp16 or FP8 E4M3; a low-precision state is updated in fp32, the
-// output is read from the fp32 update, and the state is rounded (RNE) after
-// every token, as storing and reloading it would.  Every row evolves
+// [P][N], GDN [DV][DK]) in fp32, fp16 or FP8 E4M3; a low-precision state is
+// updated in fp32 and rounded (RNE) after every token, and the token's output
+// is read from the rounded values, the ones stored: the same order as a
+// replayed step that folds (a conventional step is a replayed step with a
+// one-entry buffer).  Every row evolves
 // independently given the token, so a thread owns one 16-byte word of a row
 // (4 fp32, 8 fp16 or 16 FP8 values): the lanes of a row are adjacent, loads and stores
 // are 128-bit and contiguous across the row, and row dot products reduce with
@@ -139,14 +141,13 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_step_kernel(ConvArgs a)
                     if (p0 + u < passes) {           // uniform across the workgroup
                         const bool live = row < C;
                         const float x = live ? ld_io<IO>(a.in_c, (tb * a.H + h) * C + row) : 0.f;
+#pragma unroll
+                        for (int i = 0; i < VW; ++i) s[u][i] = decay * s[u][i] + (dt * x) * v1[i];
+                        SW::round(s[u]);
                         float dot = 0.f;
 #pragma unroll
-                        for (int i = 0; i < VW; ++i) {
-                            s[u][i] = decay * s[u][i] + (dt * x) * v1[i];
-                            dot += dot4(s[u][i], v2[i]);
-                        }
+                        for (int i = 0; i < VW; ++i) dot += dot4(s[u][i], v2[i]);
                         const float yv = group_sum<NL>(dot) + Dh * x;
-                        SW::round(s[u]);
                         if (live && q == 0) st_io<IO>(a.y, (tb * a.H + h) * C + row, yv);
                         if (SPEC && live)
                             SW::store(a.snaps, ((size_t)t * sB * a.H + tile) * tile_elems + (size_t)row * R + EPT * q, s[u]);
@@ -166,14 +167,13 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_step_kernel(ConvArgs a)
                         for (int i = 0; i < VW; ++i) sk += dot4(s[u][i], v1[i]);
                         sk = group_sum<NL>(sk);
                         const float w = be * (v - al * sk);
+#pragma unroll
+                        for (int i = 0; i < VW; ++i) s[u][i] = al * s[u][i] + w * v1[i];
+                        SW::round(s[u]);
                         float ov = 0.f;
 #pragma unroll
-                        for (int i = 0; i < VW; ++i) {
-                            s[u][i] = al * s[u][i] + w * v1[i];
-                            ov += dot4(s[u][i], v2[i]);
-                        }
+                        for (int i = 0; i < VW; ++i) ov += dot4(s[u][i], v2[i]);
                         ov = a.scale * group_sum<NL>(ov);
-                        SW::round(s[u]);
                         if (live && q == 0) st_io<IO>(a.y, (tb * a.H + h) * C + row, ov);
                         if (SPEC && live)
                             SW::store(a.snaps, ((size_t)t * sB * a.H + tile) * tile_elems + (size_t)row * R + EPT * q, s[u]);

@@ -150,9 +150,9 @@ def test_fp16_flags_rejected():
 @pytest.mark.parametrize("kind", ["mamba2", "gdn"])
 @pytest.mark.parametrize("C,R", [(32, 64), (160, 64), (160, 128)])   # 1 row pass; 3-5 with a ragged last
 def test_conventional_fp16_state(kind, C, R):
-    """Conventional decoding on an fp16 state vs the oracle's per-token step on an fp64 state
-    that is rounded to binary16 after every token (outputs from the unrounded update on both
-    sides; the state rounded after every token on both sides)."""
+    """Conventional decoding on an fp16 state vs the oracle's replay session with a one-entry
+    buffer (every token folds: the fp64 state is updated, rounded to binary16 and the output
+    read from the rounded values, the order the conventional kernel uses)."""
     from harness import TOL_F16
     from oracle import replay_oracle as ro
     b = rb()
@@ -161,22 +161,20 @@ def test_conventional_fp16_state(kind, C, R):
     S0 = synth.checkpoint(41, (B, H, C, R)).astype(np.float16)
     S = torch.from_numpy(S0).cuda()
     toks = _tokens(kind, 41, T, B, H, H, C, R)
-    Sref = S0.astype(np.float64)
-    params, A, D = {}, None, None
+    params = {}
     if kind == "mamba2":
         A, D = synth.mamba2_params(41, H)
         params = {"A": torch.from_numpy(A).cuda(), "D": torch.from_numpy(D).cuda()}
+        sess = ro.Mamba2Session(A, D, S0.astype(np.float64), cap=1, ckpt_dtype="f16")
+    else:
+        sess = ro.GDNSession(S0.astype(np.float64), cap=1, ckpt_dtype="f16")
     for t in range(T):
         tok = synth.token(toks, t)
         y = b.conv_decode_step(cfg, S, {k: torch.from_numpy(v).cuda() for k, v in tok.items()}, params)
-        if kind == "mamba2":
-            yr = ro.mamba2_token(Sref, tok["x"], tok["Bm"], tok["Cm"], tok["dt"], A, D)
-        else:
-            yr = ro.gdn_token(Sref, tok["q"], tok["k"], tok["v"], tok["alpha"], tok["beta"])
-        Sref[...] = Sref.astype(np.float16).astype(np.float64)
+        yr = sess.decode(tok)
         torch.cuda.synchronize()
         err = ro.normwise_error(y[0].float().cpu().numpy(), yr)
         assert err <= TOL_F16, (t, err)
         Sg = S.float().cpu().numpy().astype(np.float64)
-        cerr = float(np.max(np.abs(Sg - Sref)) / np.max(np.abs(Sref)))
+        cerr = float(np.max(np.abs(Sg - sess.S)) / np.max(np.abs(sess.S)))
         assert cerr <= TOL_F16, (t, cerr)

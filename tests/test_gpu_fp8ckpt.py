@@ -198,48 +198,45 @@ def test_fp8_flags_rejected():
 @pytest.mark.parametrize("kind", ["mamba2", "gdn"])
 @pytest.mark.parametrize("C,R", [(32, 64), (160, 64), (160, 128)])   # 1 row pass; 3-5 with a ragged last
 def test_conventional_fp8_state(kind, C, R):
-    """Conventional decoding on an FP8 state vs the oracle's per-token step on an fp64 state
-    rounded to E4M3 after every token (outputs from the unrounded update on both sides).
-    Both start from the same E4M3 values.  Every token rounds the state on both sides, so the
-    element-wise bound of tests/harness.py (Fp8Bound) is advanced once per token: a
-    difference is carried by the update (Mamba-2 decay <= 1 per element; GDN a product of
-    factors of 2-norm <= 1 per row) and each rounding may add about one E4M3 step.  The
-    outputs, read from the unrounded update, may differ by the read-out of the previous
-    state difference (readout_bound) beyond 1e-4 of the vector's norm; at most 1e-3 of the
-    codes may differ."""
+    """Conventional decoding on an FP8 state vs the oracle's replay session with a one-entry
+    buffer (every token folds: the fp64 state is updated, rounded to E4M3 and the output read
+    from the rounded values, the order the conventional kernel uses).  Both start from the
+    same E4M3 values.  Every token rounds the state on both sides, so the element-wise bound
+    of tests/harness.py (Fp8Bound) is advanced once per token: a difference is carried by
+    the update (Mamba-2 decay <= 1 per element; GDN a product of factors of 2-norm <= 1 per
+    row) and each rounding may add about one E4M3 step.  The outputs may differ by the
+    read-out of the measured state difference (readout_bound) beyond 1e-4 of the vector's
+    norm; at most 1e-3 of the codes may differ."""
     from harness import Fp8Bound, readout_bound
     from oracle import replay_oracle as ro
     b = rb()
     B, H, T = 3, 2, 6
     cfg = b.make_config(_kind(kind), B, H, H, C, R, 16, b.F32, ckpt_dtype=b.FP8_E4M3)
     S0 = synth.checkpoint(42, (B, H, C, R), std=0.5)
-    Sref = ro.e4m3_decode(ro.e4m3_encode(S0)).reshape(S0.shape)
     # the conventional state in the checkpoint dtype, made by the library's own load rounding
     st = b.ReplayState(b.make_config(_kind(kind), B, H, H, C, R, 16, b.F32, ckpt_dtype=b.FP8_E4M3))
     st.load_checkpoint(torch.from_numpy(S0).cuda())
     S = st.read_checkpoint()
     torch.cuda.synchronize()
-    assert np.array_equal(ro.e4m3_decode(S.view(torch.uint8).cpu().numpy()).reshape(S0.shape), Sref)
     toks = _tokens(kind, 42, T, B, H, H, C, R)
-    params, A, D = {}, None, None
+    params = {}
     if kind == "mamba2":
         A, D = synth.mamba2_params(42, H)
         params = {"A": torch.from_numpy(A).cuda(), "D": torch.from_numpy(D).cuda()}
+        sess = ro.Mamba2Session(A, D, S0, cap=1, ckpt_dtype="fp8")
+    else:
+        sess = ro.GDNSession(S0, cap=1, ckpt_dtype="fp8")
+    assert np.array_equal(ro.e4m3_decode(S.view(torch.uint8).cpu().numpy()).reshape(S0.shape), sess.S)
     bound = Fp8Bound(kind, (B, H, C, R))
-    dS = np.zeros((B, H, C, R))
     for t in range(T):
         tok = synth.token(toks, t)
         y = b.conv_decode_step(cfg, S, {k: torch.from_numpy(v).cuda() for k, v in tok.items()}, params)
-        if kind == "mamba2":
-            yr = ro.mamba2_token(Sref, tok["x"], tok["Bm"], tok["Cm"], tok["dt"], A, D)
-        else:
-            yr = ro.gdn_token(Sref, tok["q"], tok["k"], tok["v"], tok["alpha"], tok["beta"])
-        Sref[...] = ro.e4m3_decode(ro.e4m3_encode(Sref)).reshape(Sref.shape)
+        yr = sess.decode(tok)
         torch.cuda.synchronize()
+        bound.advance(np.ones(B, bool), sess.S)
+        Sg = ro.e4m3_decode(S.view(torch.uint8).cpu().numpy()).reshape(S0.shape)
+        dS, _ = bound.check(Sg, sess.S, f"token {t}")
         yg = y[0].float().cpu().numpy().astype(np.float64)
         allow = 1e-4 * np.max(np.abs(yr), axis=-1, keepdims=True) + readout_bound(kind, dS, [tok])[0]
         over = np.abs(yg - yr) > allow
         assert not over.any(), (t, int(over.sum()))
-        bound.advance(np.ones(B, bool), Sref)
-        Sg = ro.e4m3_decode(S.view(torch.uint8).cpu().numpy()).reshape(Sref.shape)
-        dS, _ = bound.check(Sg, Sref, f"token {t}")

@@ -3,12 +3,12 @@
 Stand-in for the pages' quantization study (Qwen3.5-4B at 128K tokens, GPQA-Diamond;
 [TR] "NVIDIA ve Dao AI Lab ...", section "Kuantizasyon hatasinin sinirlandirilmasi"):
 the batch-128 Gated DeltaNet layer (32 heads, d_k = d_v = 128, bf16 q/k/v, fp32
-gates) decodes 8192 steps from an N(0, 0.1) checkpoint in eleven variants:
+gates) decodes 8192 steps from an N(0, 0.1) checkpoint in thirteen variants:
   R0 fp32 checkpoint only          R1 fp32 checkpoint + FP8 read copy
   R2 fp32 checkpoint + MXFP4 copy  Q1 FP8 checkpoint only    Q2 MXFP4 checkpoint only
   H0 fp16 checkpoint only          H2 fp16 checkpoint + MXFP4 copy
   F0 FP8 checkpoint stored as E4M3 F2 FP8 checkpoint + MXFP4 copy
-  R2c, Q2c: R2 and Q2 with the non-clipping MXFP4 shared exponent
+  R2c, Q2c, H2c, F2c: R2, Q2, H2 and F2 with the non-clipping MXFP4 shared exponent
 Q1 keeps an fp32 array that mirrors its FP8 copy; F0 stores the E4M3 codes
 themselves, so the two take the same values (one fold result in ~1e5 may land
 one E4M3 step apart) and their errors agree.
@@ -46,7 +46,9 @@ def test_low_precision_error_over_8192_steps():
                 "H0": (b.NONE, 0, b.F16), "H2": (b.MXFP4, 0, b.F16),
                 "F0": (b.NONE, 0, b.FP8_E4M3), "F2": (b.MXFP4, 0, b.FP8_E4M3),
                 "R2c": (b.MXFP4, b.FLAG_MX_SCALE_CEIL, b.F32),
-                "Q2c": (b.MXFP4, b.FLAG_QUANTIZED_CKPT | b.FLAG_MX_SCALE_CEIL, b.F32)}
+                "Q2c": (b.MXFP4, b.FLAG_QUANTIZED_CKPT | b.FLAG_MX_SCALE_CEIL, b.F32),
+                "H2c": (b.MXFP4, b.FLAG_MX_SCALE_CEIL, b.F16),
+                "F2c": (b.MXFP4, b.FLAG_MX_SCALE_CEIL, b.FP8_E4M3)}
     # one starting checkpoint for every variant: N(0, 0.1) rounded to binary16, so the fp16
     # variants start from the same values as the others
     S0 = synth.checkpoint_device(4, (B, H, D, D), "cuda").half().float()
@@ -81,10 +83,10 @@ def test_low_precision_error_over_8192_steps():
     e = {r[0]: r for r in rows}
     assert e["R0"][5] <= 2e-2                                   # bf16 output rounding only
     assert e["H0"][5] <= 2e-2 and e["H0"][6] <= e["R0"][6] + 8 * 2.0 ** -11
-    for r in ("R1", "R2", "H2", "R2c"):
+    for r in ("R1", "R2", "H2", "R2c", "H2c"):
         assert e[r][4] <= 2.0 * e[r][1] + 1e-3, r               # read error does not accumulate
     assert e["Q1"][6] > e["R1"][6]
     assert e["Q2"][6] > e["R2"][6]
     assert e["Q2c"][6] > e["R2c"][6]
     assert abs(e["F0"][6] - e["Q1"][6]) <= 0.05 * e["Q1"][6]    # same values, stored differently
-    assert e["F0"][6] > e["H0"][6] and e["F2"][6] >= 0.9 * e["F0"][6]
+    assert e["F0"][6] > e["H0"][6] and e["F2"][6] >= 0.9 * e["F0"][6] and e["F2c"][6] >= 0.9 * e["F0"][6]
