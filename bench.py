@@ -790,7 +790,7 @@ def ceilings(rb, torch, dev, stream):
     e1.record(stream)
     torch.cuda.synchronize()
     copy = 10 * 2 * nb / (e0.elapsed_time(e1) / 1e3) / 1e9
-    acc = torch.zeros(1, dtype=torch.float32, device=dev)
+    acc = torch.empty(rb.stream_read_partials(nb), dtype=torch.float32, device=dev)
     for _ in range(3):
         rb.stream_read(src, nb, acc)
     e0.record(stream)

@@ -542,5 +542,20 @@ def stream_copy(dst, src, nbytes: int):
     _check(_lib.replay_stream_copy(_ptr(dst), _ptr(src), int(nbytes), _stream()), "replay_stream_copy")
 
 
-def stream_read(src, nbytes: int, sum_out):
-    _check(_lib.replay_stream_read(_ptr(src), int(nbytes), _ptr(sum_out), _stream()), "replay_stream_read")
+STREAM_TILE_BYTES = 32768
+
+
+def stream_read_partials(nbytes: int) -> int:
+    """Number of per-tile sums replay_stream_read writes for nbytes."""
+    return max(1, -(-int(nbytes) // STREAM_TILE_BYTES))
+
+
+def stream_read(src, nbytes: int, partials=None):
+    """Read nbytes of src as fp32; returns the device tensor of per-32-KiB-tile sums."""
+    import torch
+    if partials is None:
+        partials = torch.empty(stream_read_partials(nbytes), dtype=torch.float32, device=src.device)
+    if partials.dtype != torch.float32 or partials.numel() < stream_read_partials(nbytes) or not partials.is_cuda:
+        raise ValueError("partials: a device fp32 tensor of stream_read_partials(nbytes) entries")
+    _check(_lib.replay_stream_read(_ptr(src), int(nbytes), _ptr(partials), _stream()), "replay_stream_read")
+    return partials

@@ -367,47 +367,39 @@ hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStrea
 }
 
 // Read-only stream: the ceiling for checkpoint reads that write nothing back.
-// A fixed grid of 8 workgroups per CU walks the 32 KiB tiles (two per
-// iteration: sixteen 128-bit loads in flight per lane); the loaded values are
-// summed, so no load is dead, and one atomic per workgroup adds its sum.
-constexpr int STREAM_READ_GRID = 2048;
-
-__global__ __launch_bounds__(256) void stream_read_kernel(const f32x4* src, size_t n4, float* sum_out)
+// The replay kernels' pattern: one 32 KiB tile per workgroup (eight 128-bit
+// nontemporal loads in flight per lane, XCD-aware tile order), every loaded
+// value summed so that no load is dead, and one plain store per workgroup of
+// its tile's sum (a single shared accumulator would serialise 32768 atomics).
+// The last workgroup takes the ragged tail.
+__global__ __launch_bounds__(256) void stream_read_kernel(const f32x4* src, size_t n4, float* partials)
 {
     __shared__ float part[4];
-    const size_t ntiles = n4 / STREAM_TILE_F4;
-    const size_t off = (threadIdx.x >> 6) * 512 + (threadIdx.x & 63);
+    const size_t t = (size_t)xcd_tile_index();
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    size_t t = (size_t)xcd_tile_index();
-    for (; t + gridDim.x < ntiles; t += 2 * (size_t)gridDim.x) {
-        const f32x4* p0 = src + t * STREAM_TILE_F4 + off;
-        const f32x4* p1 = src + (t + gridDim.x) * STREAM_TILE_F4 + off;
-        f32x4 v[16];
+    if ((t + 1) * STREAM_TILE_F4 <= n4) {
+        const f32x4* p = src + t * STREAM_TILE_F4 + (threadIdx.x >> 6) * 512 + (threadIdx.x & 63);
+        f32x4 v[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = __builtin_nontemporal_load(p0 + i * 64);
+        for (int i = 0; i < 8; ++i) v[i] = __builtin_nontemporal_load(p + i * 64);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[8 + i] = __builtin_nontemporal_load(p1 + i * 64);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc += v[i];
-    }
-    if (t < ntiles) {
-        const f32x4* p0 = src + t * STREAM_TILE_F4 + off;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc += __builtin_nontemporal_load(p0 + i * 64);
-    }
-    if (blockIdx.x == 0)                           // the ragged tail past the last whole tile
-        for (size_t i = ntiles * STREAM_TILE_F4 + threadIdx.x; i < n4; i += blockDim.x)
+        for (int i = 0; i < 8; ++i) acc += v[i];
+    } else {
+        for (size_t i = t * STREAM_TILE_F4 + threadIdx.x; i < n4; i += blockDim.x)
             acc += __builtin_nontemporal_load(src + i);
+    }
     const float v = wave_sum64(acc.x + acc.y + acc.z + acc.w);
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
     __syncthreads();
-    if (threadIdx.x == 0) atomicAdd(sum_out, part[0] + part[1] + part[2] + part[3]);
+    if (threadIdx.x == 0) partials[t] = part[0] + part[1] + part[2] + part[3];
 }
 
-hipError_t launch_stream_read(const void* src, size_t bytes, float* sum_out, hipStream_t s)
+hipError_t launch_stream_read(const void* src, size_t bytes, float* partials, hipStream_t s)
 {
-    hipLaunchKernelGGL(stream_read_kernel, dim3(STREAM_READ_GRID), dim3(256), 0, s, (const f32x4*)src, bytes / 16,
-                       sum_out);
+    const size_t n4 = bytes / 16;
+    size_t blocks = (n4 + STREAM_TILE_F4 - 1) / STREAM_TILE_F4;
+    if (blocks == 0) blocks = 1;
+    hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const f32x4*)src, n4, partials);
     return hipGetLastError();
 }
 

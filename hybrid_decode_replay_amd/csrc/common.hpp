@@ -165,11 +165,22 @@ struct TileIdx {
     int b, h, sp;
 };
 
-__device__ __forceinline__ TileIdx tile_of(int item, int H, int nsplit) {
+// Division by a divisor d that is the same for the whole launch, through a
+// multiplier the host computes once (magic_div): q = floor(n m / 2^32) with
+// m = floor(2^32 / d) + 1, exact whenever n d < 2^32; m = 0 stands for d = 1.
+// (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994.)  One scalar multiply instead of a division sequence.
+__device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t m) { return m ? __umulhi(n, m) : n; }
+
+// Small per-lane quotients: q = (n m) >> 20 with m = ceil(2^20 / d) (magic_div20),
+// exact for n < 2^20 / d; with n < 4096 the 24-bit product fits 32 bits.
+__device__ __forceinline__ int div_small(int n, int m20) { return (int)(__umul24((uint32_t)n, (uint32_t)m20) >> 20); }
+
+__device__ __forceinline__ TileIdx tile_of(int item, int H, uint32_t mg_h, int nsplit, uint32_t mg_nsplit) {
     TileIdx t;
-    t.sp = item % nsplit;
-    const int bh = item / nsplit;
-    t.b = bh / H;
+    const int bh = (int)div_magic((uint32_t)item, mg_nsplit);
+    t.sp = item - bh * nsplit;
+    t.b = (int)div_magic((uint32_t)bh, mg_h);
     t.h = bh - t.b * H;
     return t;
 }

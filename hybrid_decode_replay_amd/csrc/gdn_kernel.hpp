@@ -54,8 +54,8 @@ __device__ __forceinline__ int lane_id_here()
     return l;
 }
 
-template <int NB, int IO, int TMAX, int RC, int CK>
-__global__ __launch_bounds__(256, NB <= 8 ? 6 : 4) void gdn_step_kernel(StepArgs a)
+template <int NB, int IO, int TMAX, int RC, int CK, int SPW>
+__global__ __launch_bounds__(256, SPW == 1 ? (NB <= 8 ? 6 : 4) : 4) void gdn_step_kernel(StepArgs a)
 {
     extern __shared__ float lds[];
     constexpr int R = NB * 16;                  // d_k
@@ -63,17 +63,17 @@ __global__ __launch_bounds__(256, NB <= 8 ? 6 : 4) void gdn_step_kernel(StepArgs
     constexpr int PRE = 4;
     constexpr int EL = R / 16;                  // chain elements per lane (one row of 16 lanes per chain)
     const int C = a.C;                          // d_v
-    const TileIdx tix = tile_of(xcd_tile_index(), a.H, a.nsplit);
+    const TileIdx tix = tile_of(xcd_tile_index(), a.H, a.mg_tiles, a.nsplit, a.mg_nsplit);
     const int b = tix.b, h = tix.h, tile = b * a.H + h;
-    const int g = h / a.hpg;
-    const int cw = C / a.nsplit, c0 = tix.sp * cw;   // this workgroup's output columns
+    const int g = (int)div_magic((uint32_t)h, a.mg_hpg);
+    const int cw = a.cw, c0 = tix.sp * cw;           // this workgroup's output columns
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, waves = nthr >> 6;
-    const int lc = 16 * w + (lane & 15);             // local output column
-    const int col = c0 + lc;                          // global output column
     const int rq = 4 * (lane >> 4);
     const int l16 = lane & 15, lq = lane >> 4;
     const size_t sB = (size_t)a.B;
+    // wave w owns the SPW strips w*SPW .. w*SPW+SPW-1 of the workgroup's columns
+    const int lc0 = 16 * SPW * w + l16;              // local output column of strip 0
 
     const StepPlan p = plan_step(a, b, h == 0 && tix.sp == 0 && tid == 0);
     if (p.skip || (a.mode == MODE_FLUSH && p.f == 0)) return;
@@ -97,53 +97,60 @@ __global__ __launch_bounds__(256, NB <= 8 ? 6 : 4) void gdn_step_kernel(StepArgs
     G.bank_c = a.bank_c; G.bank_r = a.bank_r; G.bank_s = a.bank_s;
     G.hc = (size_t)b * a.H + h; G.gr = (size_t)b * a.G + g;
     G.b = b; G.h = h; G.g = g; G.B = a.B; G.H = a.H; G.G = a.G; G.cap = a.cap; G.C = C;
-    G.c0 = c0; G.cw = cw;
+    G.c0 = c0; G.cw = cw; G.m20_cx = a.m20_cx;
     G.ht = 1; G.xc_stride = 0; G.sc_stride = 0;
     G.len = len; G.bank = p.bank; G.V = V; G.T = T;
     G.xc = vs; G.xr = ks; G.xq = qs; G.s0 = al; G.s1 = be; G.p0 = nullptr;
 
-    // ---- 1. entry chunks ahead of the checkpoint stream, 2. checkpoint tile
+    // ---- 1. entry chunks ahead of the checkpoint stream, 2. checkpoint strips
     const Stager<IO, R> stg(G);
     uint4 pre[PRE];
     ScalarRaw sr;
     stage_issue<IO, R, PRE, false>(stg, tid, nthr, pre, sr);
     // a step that folds nothing reads the low-precision copy when there is one
     // (loads issued now, decoded where the values are first used)
-    const size_t strip_index = (size_t)tile * (C >> 4) + (c0 >> 4) + w;
-    f32x4 s[NB];
+    const size_t strip0 = (size_t)tile * (C >> 4) + (c0 >> 4) + SPW * w;
+    f32x4 s[SPW][NB];
     bool from_copy = false;
     if constexpr (RC != RC_NONE) from_copy = (f == 0);
-    if (from_copy) {
-        if constexpr (RC != RC_NONE) rc_issue<NB, RC>(a.rcopy, a.rscale, strip_index, lane, s);
-    } else {
-        ckpt_issue<NB, CK>(a.ckpt, strip_index, lane, s);
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+        if (from_copy) {
+            if constexpr (RC != RC_NONE) rc_issue<NB, RC>(a.rcopy, a.rscale, strip0 + j, lane, s[j]);
+        } else {
+            ckpt_issue<NB, CK>(a.ckpt, strip0 + j, lane, s[j]);
+        }
     }
     stage_publish<IO, R, PRE>(stg, tid, nthr, pre, sr);
     __syncthreads();
 
     // ---- 3. fold the first f entries (WY form on MFMA)
     if (f > 0) {
-        ckpt_decode<NB, CK>(s);
-        // W[i][v] = (S0 k_i)[v]; lane result rows i = lq*4 + r, column col
-        f32x4 W = {0.f, 0.f, 0.f, 0.f};
         const bool arow = l16 < f;
+        f32x4 W[SPW];
 #pragma unroll
-        for (int jb = 0; jb < NB; ++jb) {
-            const f32x4 kv = arow ? ld4(ks + l16 * RS + jb * 16 + rq) : f32x4{0.f, 0.f, 0.f, 0.f};
-            W = mfma16x16x4(kv.x, s[jb].x, W);
-            W = mfma16x16x4(kv.y, s[jb].y, W);
-            W = mfma16x16x4(kv.z, s[jb].z, W);
-            W = mfma16x16x4(kv.w, s[jb].w, W);
+        for (int j = 0; j < SPW; ++j) {
+            ckpt_decode<NB, CK>(s[j]);
+            // W[i][v] = (S0 k_i)[v]; lane result rows i = lq*4 + r, column lc0 + 16 j
+            W[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb) {
+                const f32x4 kv = arow ? ld4(ks + l16 * RS + jb * 16 + rq) : f32x4{0.f, 0.f, 0.f, 0.f};
+                W[j] = mfma16x16x4(kv.x, s[j][jb].x, W[j]);
+                W[j] = mfma16x16x4(kv.y, s[j][jb].y, W[j]);
+                W[j] = mfma16x16x4(kv.z, s[j][jb].z, W[j]);
+                W[j] = mfma16x16x4(kv.w, s[j][jb].w, W[j]);
+            }
         }
         if (w == 0) {
             // gate products tt[j][i] = alpha_{j+1} ... alpha_i (1 for i <= j), i, j < f:
             // lane j multiplies along i, every product formed as a product
             if (lane < 16) {
-                float p = 1.f;
+                float pr = 1.f;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    if (i > lane && i < f) p *= al[i];
-                    tt[lane * 17 + i] = p;
+                    if (i > lane && i < f) pr *= al[i];
+                    tt[lane * 17 + i] = pr;
                 }
             }
             // Gram k_i . k_j on MFMA (lane result rows i = lq*4 + r, column j = l16)
@@ -157,9 +164,9 @@ __global__ __launch_bounds__(256, NB <= 8 ? 6 : 4) void gdn_step_kernel(StepArgs
             // strictly lower triangle of A, written to ti as a scratch matrix
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int i = lq * 4 + r, j = l16;
-                const float v = (j < i && i < f) ? be[i] * tt[j * 17 + i] * gm[r] : 0.f;
-                ti[i * 17 + j] = v;
+                const int i = lq * 4 + r, jj = l16;
+                const float v = (jj < i && i < f) ? be[i] * tt[jj * 17 + i] * gm[r] : 0.f;
+                ti[i * 17 + jj] = v;
             }
             wave_lds_sync();
             // column c of (I + A)^{-1} by forward substitution (lanes 0..15)
@@ -169,7 +176,7 @@ __global__ __launch_bounds__(256, NB <= 8 ? 6 : 4) void gdn_step_kernel(StepArgs
                 for (int i = 0; i < 16; ++i) {
                     float acc = (i == lane) ? 1.f : 0.f;
 #pragma unroll
-                    for (int j = 0; j < i; ++j) acc -= ti[i * 17 + j] * tc[j];
+                    for (int jj = 0; jj < i; ++jj) acc -= ti[i * 17 + jj] * tc[jj];
                     tc[i] = acc;
                 }
             }
@@ -182,45 +189,47 @@ __global__ __launch_bounds__(256, NB <= 8 ? 6 : 4) void gdn_step_kernel(StepArgs
         }
         __syncthreads();
 
-        // rhs[i][v] = beta_i (v_i[v] - P_i W[i][v]) for i < f
-        f32x4 rhs;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = lq * 4 + r;
-            float v = 0.f;
-            if (i < f) v = be[i] * (vs[i * cw + 16 * w + (lane_id_here() & 15)] - (al[0] * tt[i]) * W[r]);   // P_i = alpha_0 tt[0][i]
-            rhs[r] = v;
-        }
-        // U = (I + A)^{-1} rhs, then scaled by the decay from entry i to the end of the fold
-        f32x4 U = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) U = mfma16x16x4(ti[l16 * 17 + lq * 4 + r], rhs[r], U);
         const float decay = al[0] * tt[f - 1];                       // P_{f-1}
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = lq * 4 + r;
-            U[r] = (i < f) ? tt[i * 17 + f - 1] * U[r] : 0.f;         // alpha_{i+1} ... alpha_{f-1}
-        }
-        // S'^T[j][v] = decay S0^T[j][v] + sum_i K[i][j] U~[i][v]
-#pragma unroll
-        for (int jb = 0; jb < NB; ++jb) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < SPW; ++j) {
+            // rhs[i][v] = beta_i (v_i[v] - P_i W[i][v]) for i < f
+            f32x4 rhs;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = lq * 4 + r;
-                const float kv = (i < f) ? ks[i * RS + jb * 16 + l16] : 0.f;
-                acc = mfma16x16x4(kv, U[r], acc);
+                float v = 0.f;
+                if (i < f) v = be[i] * (vs[i * cw + 16 * (SPW * w + j) + (lane_id_here() & 15)] - (al[0] * tt[i]) * W[j][r]);
+                rhs[r] = v;
             }
-            s[jb] = decay * s[jb] + acc;
+            // U = (I + A)^{-1} rhs, then scaled by the decay from entry i to the end of the fold
+            f32x4 U = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) U = mfma16x16x4(ti[l16 * 17 + lq * 4 + r], rhs[r], U);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = lq * 4 + r;
+                U[r] = (i < f) ? tt[i * 17 + f - 1] * U[r] : 0.f;         // alpha_{i+1} ... alpha_{f-1}
+            }
+            // S'^T[jk][v] = decay S0^T[jk][v] + sum_i K[i][jk] U~[i][v]
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = lq * 4 + r;
+                    const float kv = (i < f) ? ks[i * RS + jb * 16 + l16] : 0.f;
+                    acc = mfma16x16x4(kv, U[r], acc);
+                }
+                s[j][jb] = decay * s[j][jb] + acc;
+            }
+            // the folded state takes the checkpoint's storage precision at once (fp16:
+            // RNE), so this step's outputs and the read copy see the stored values
+            ckpt_round<NB, CK>(s[j]);
+            // a checkpoint kept at the copy's precision is rounded as soon as it is folded
+            if constexpr (RC != RC_NONE) {
+                if (a.qckpt) rc_roundtrip<NB, RC>(s[j], a.mxceil);
+            }
         }
-    }
-
-    // the folded state takes the checkpoint's storage precision at once (fp16:
-    // RNE), so this step's outputs and the read copy see the stored values
-    if (f > 0) ckpt_round<NB, CK>(s);
-    // a checkpoint kept at the copy's precision is rounded as soon as it is folded
-    if constexpr (RC != RC_NONE) {
-        if (a.qckpt && f > 0) rc_roundtrip<NB, RC>(s, a.mxceil);
     }
 
     // ---- 4./5. adjoint chains and outputs.  A chain runs on one row of 16 lanes:
@@ -233,10 +242,13 @@ __global__ __launch_bounds__(256, NB <= 8 ? 6 : 4) void gdn_step_kernel(StepArgs
         const int rho = lane >> 4, j16 = lane & 15;
         if constexpr (TMAX == 1) {
             // one token: every row of every wave runs the chain itself (no workgroup
-            // barrier) and keeps the replay sum sum_i c_i v_i of its lane's column
+            // barrier) and keeps the replay sums sum_i c_i v_i of its lanes' columns
             float r[EL];
             lds_row_load<EL>(qs + EL * j16, r);
-            float rep = 0.f, sig = 1.f;
+            float rep[SPW], sig = 1.f;
+#pragma unroll
+            for (int j = 0; j < SPW; ++j) rep[j] = 0.f;
+            const float* vcol = vs + lc0;
             for (int i = len; i >= f; --i) {
                 float kv[EL];
                 lds_row_load<EL>(ks + i * RS + EL * j16, kv);
@@ -244,7 +256,9 @@ __global__ __launch_bounds__(256, NB <= 8 ? 6 : 4) void gdn_step_kernel(StepArgs
 #pragma unroll
                 for (int m = 0; m < EL; ++m) part += kv[m] * r[m];
                 const float bd = be[i] * group_sum<16>(part);
-                rep += (sig * bd) * vs[i * cw + 16 * w + (lane_id_here() & 15)];
+                const float cf = sig * bd;
+#pragma unroll
+                for (int j = 0; j < SPW; ++j) rep[j] += cf * vcol[i * cw + 16 * j];
 #pragma unroll
                 for (int m = 0; m < EL; ++m) r[m] -= bd * kv[m];
                 sig *= al[i];
@@ -255,15 +269,18 @@ __global__ __launch_bounds__(256, NB <= 8 ? 6 : 4) void gdn_step_kernel(StepArgs
             float* rw = rz + (size_t)w * R;
             if (rho == 0) lds_row_store<EL>(rw + EL * j16, r);
             wave_lds_sync();
-            if (f == 0) {
-                if (from_copy) rc_decode<NB, RC>(s);
-                else ckpt_decode<NB, CK>(s);
-            }
-            float gacc = 0.f;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) gacc += dot4(s[nb], ld4(rw + nb * 16 + rq));
-            gacc = sum_over_row_groups(gacc);
-            if (lane < 16) st_io<IO>(a.y, ((size_t)b * a.H + h) * C + col, a.scale * (gacc + rep));
+            for (int j = 0; j < SPW; ++j) {
+                if (f == 0) {
+                    if (from_copy) rc_decode<NB, RC>(s[j]);
+                    else ckpt_decode<NB, CK>(s[j]);
+                }
+                float gacc = 0.f;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) gacc += dot4(s[j][nb], ld4(rw + nb * 16 + rq));
+                gacc = sum_over_row_groups(gacc);
+                if (lane < 16) st_io<IO>(a.y, ((size_t)b * a.H + h) * C + c0 + lc0 + 16 * j, a.scale * (gacc + rep[j]));
+            }
         } else {
             // several tokens: one chain per (wave, row) pair; coefficients and r_0 go
             // through LDS to the output lanes
@@ -289,24 +306,28 @@ __global__ __launch_bounds__(256, NB <= 8 ? 6 : 4) void gdn_step_kernel(StepArgs
                 lds_row_store<EL>(rz + t * R + EL * j16, r);
             }
             __syncthreads();
-            if (f == 0) {
-                if (from_copy) rc_decode<NB, RC>(s);
-                else ckpt_decode<NB, CK>(s);
-            }
 
             // o_t = scale (S' r_0 + sum_i c_i v_i)
 #pragma unroll
-            for (int t = 0; t < TMAX; ++t) {
-                if (t < T) {
-                    float gacc = 0.f;
+            for (int j = 0; j < SPW; ++j) {
+                if (f == 0) {
+                    if (from_copy) rc_decode<NB, RC>(s[j]);
+                    else ckpt_decode<NB, CK>(s[j]);
+                }
+                const int lcj = lc0 + 16 * j;
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) gacc += dot4(s[nb], ld4(rz + t * R + nb * 16 + rq));
-                    gacc = sum_over_row_groups(gacc);
-                    const int pos = len + t;
-                    float rep = 0.f;
-                    for (int i = f; i <= pos; ++i) rep += cc[t * vmax + i] * vs[i * cw + 16 * w + (lane_id_here() & 15)];
-                    if (lane < 16)
-                        st_io<IO>(a.y, (((size_t)t * sB + b) * a.H + h) * C + col, a.scale * (gacc + rep));
+                for (int t = 0; t < TMAX; ++t) {
+                    if (t < T) {
+                        float gacc = 0.f;
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) gacc += dot4(s[j][nb], ld4(rz + t * R + nb * 16 + rq));
+                        gacc = sum_over_row_groups(gacc);
+                        const int pos = len + t;
+                        float rep = 0.f;
+                        for (int i = f; i <= pos; ++i) rep += cc[t * vmax + i] * vs[i * cw + lcj];
+                        if (lane < 16)
+                            st_io<IO>(a.y, (((size_t)t * sB + b) * a.H + h) * C + c0 + lcj, a.scale * (gacc + rep));
+                    }
                 }
             }
         }
@@ -314,29 +335,42 @@ __global__ __launch_bounds__(256, NB <= 8 ? 6 : 4) void gdn_step_kernel(StepArgs
 
     // ---- 6. single checkpoint write on a folding step
     if (f > 0) {
-        ckpt_store<NB, CK>(a.ckpt, strip_index, lane, s);
-        if constexpr (RC != RC_NONE) rc_store<NB, RC>(a.rcopy, a.rscale, strip_index, lane, s, a.mxceil);
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) {
+            ckpt_store<NB, CK>(a.ckpt, strip0 + j, lane, s[j]);
+            if constexpr (RC != RC_NONE) rc_store<NB, RC>(a.rcopy, a.rscale, strip0 + j, lane, s[j], a.mxceil);
+        }
     }
 
     // ---- 7. append the unfolded new tokens
     stage_append<IO, R>(G, a.bufc, a.bufr, a.bufs0, a.bufs1, p.bank_new, f, tid, nthr, tix.sp == 0,
-                        tix.sp == 0 && h % a.hpg == 0);
+                        tix.sp == 0 && h == g * a.hpg);
 }
 
-template <int NB, int IO, int TMAX, int RC, int CK>
-static hipError_t gdn_launch_nb(const StepArgs& a, hipStream_t s)
+template <int NB, int IO, int TMAX, int RC, int CK, int SPW>
+static hipError_t gdn_launch_spw(const StepArgs& a, hipStream_t s)
 {
     const size_t Tr = a.T > 0 ? a.T : 1;
     const size_t R = NB * 16, vmax = a.vmax;
     const size_t lds = sizeof(float) * (vmax * (a.C / a.nsplit + R + 4) + Tr * R + (Tr > 4 ? Tr : 4) * R + 2 * vmax +
                                         Tr * vmax + 2 * 16 * 17);
-    auto k = gdn_step_kernel<NB, IO, TMAX, RC, CK>;
+    auto k = gdn_step_kernel<NB, IO, TMAX, RC, CK, SPW>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k, dim3(a.B * a.H * a.nsplit), dim3(a.C / a.nsplit * 4), lds, s, a);
+    hipLaunchKernelGGL(k, dim3(a.B * a.H * a.nsplit), dim3(a.C / a.nsplit / SPW * 4), lds, s, a);
     return hipGetLastError();
+}
+
+template <int NB, int IO, int TMAX, int RC, int CK>
+static hipError_t gdn_launch_nb(const StepArgs& a, hipStream_t s)
+{
+    if constexpr (NB == 8) {
+        if (a.spw == 2) return gdn_launch_spw<NB, IO, TMAX, RC, CK, 2>(a, s);
+    }
+    if (a.spw != 1) return hipErrorInvalidValue;
+    return gdn_launch_spw<NB, IO, TMAX, RC, CK, 1>(a, s);
 }
 
 template <int IO, int TMAX, int RC, int CK>

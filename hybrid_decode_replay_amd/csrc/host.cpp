@@ -111,7 +111,9 @@ replay_status check_config(const replay_config* c)
         return fail(REPLAY_ERR_SHAPE, "state_dim %d must be 16, 32, 64, 128 or 256", R);
     if (c->buf_cap < 1 || c->buf_cap > REPLAY_MAX_BUF)
         return fail(REPLAY_ERR_SHAPE, "buf_cap %d must be in [1, %d]", c->buf_cap, REPLAY_MAX_BUF);
-    if ((long long)c->batch * c->nheads > (1LL << 30)) return fail(REPLAY_ERR_SHAPE, "batch * nheads too large");
+    // the kernels split work item indices by multiplication (exact while index * divisor < 2^32)
+    if ((long long)c->batch * c->nheads * (c->nheads > 256 ? c->nheads : 256) >= (1LL << 32))
+        return fail(REPLAY_ERR_SHAPE, "batch * nheads * max(nheads, 256) must be below 2^32");
     if (c->io_dtype != REPLAY_F32 && c->io_dtype != REPLAY_BF16)
         return fail(REPLAY_ERR_DTYPE, "io_dtype must be REPLAY_F32 or REPLAY_BF16");
     if (c->ckpt_dtype != REPLAY_F32 && c->ckpt_dtype != REPLAY_F16 && c->ckpt_dtype != REPLAY_FP8_E4M3)
@@ -223,6 +225,34 @@ int mamba2_heads_per_wg(const replay_config* c, int wpg)
     return (c->nheads / c->ngroups) % 4 == 0 ? 4 : 1;
 }
 
+// Multipliers for div_magic / div_small (the kernels' divisions by launch-invariant
+// divisors): floor(2^32 / d) + 1, exact for quotients of n with n d < 2^32 (0 for
+// d = 1); and ceil(2^20 / d), exact for n < 2^20 / d.
+uint32_t magic_div(uint32_t d)
+{
+    return d <= 1 ? 0u : (uint32_t)((1ull << 32) / d + 1);
+}
+
+int magic_div20(int d)
+{
+    return (int)(((1u << 20) + (uint32_t)d - 1) / (uint32_t)d);
+}
+
+// GDN strips per wave.  Every wave of a head runs the head's adjoint chain and
+// stages its entries, so a wave that owns two strips halves that work per head.
+// Used where the value rows of a head fill whole workgroups of four waves with
+// two strips each (d_v a multiple of 128), d_k = 128, and the step streams
+// fewer bytes than an fp32 checkpoint (an fp16 or FP8 checkpoint or a read
+// copy): there the fixed work per head bounds the step.  An fp32 stream keeps
+// one strip per wave: six waves per SIMD keep more loads in flight than four
+// (measured on the batch-256, 32-head layer: FP8 checkpoint 0.063 -> 0.054 ms
+// per step with two strips; fp32 0.100 -> 0.119 ms).
+int gdn_strips_per_wave(const replay_config* c)
+{
+    if (c->kind != REPLAY_GDN || c->state_dim != 128 || c->head_dim % 128 != 0) return 1;
+    return c->ckpt_dtype == REPLAY_F32 && c->read_copy == REPLAY_NONE ? 1 : 2;
+}
+
 rs::StepArgs step_args(const replay_state* st, const replay_inputs* in, void* y, int mode, int T,
                        const uint8_t* active)
 {
@@ -241,14 +271,20 @@ rs::StepArgs step_args(const replay_state* st, const replay_inputs* in, void* y,
     a.T = T;
     a.vmax = mode == rs::MODE_DECODE ? c->buf_cap + 1 : (mode == rs::MODE_FLUSH ? c->buf_cap : c->buf_cap + T);
     a.scale = c->scale;
-    // workgroups of at most 4 waves (one 16-column strip each): the largest
-    // divisor of the strip count that is <= 4 sets the waves per workgroup
+    // workgroups of at most 4 waves, each wave owning spw 16-column strips: the
+    // largest divisor of the wave count that is <= 4 sets the waves per workgroup
     const int strips = c->head_dim / 16;
+    a.spw = gdn_strips_per_wave(c);
     int wpg = 1;
     for (int d = 4; d >= 1; --d)
-        if (strips % d == 0) { wpg = d; break; }
-    a.nsplit = strips / wpg;
+        if ((strips / a.spw) % d == 0) { wpg = d; break; }
+    a.nsplit = strips / a.spw / wpg;
     a.ht = mamba2_heads_per_wg(c, wpg);
+    a.cw = c->head_dim / a.nsplit;
+    a.mg_nsplit = magic_div((uint32_t)a.nsplit);
+    a.mg_tiles = magic_div((uint32_t)(c->nheads / a.ht));
+    a.mg_hpg = magic_div((uint32_t)a.hpg);
+    a.m20_cx = magic_div20(a.cw / (c->io_dtype == REPLAY_BF16 ? 8 : 4));
     a.qckpt = (c->flags & REPLAY_FLAG_QUANTIZED_CKPT) ? 1 : 0;
     a.mxceil = (c->flags & REPLAY_FLAG_MX_SCALE_CEIL) ? 1 : 0;
     const replay_layout& L = st->lay;
@@ -1037,13 +1073,13 @@ replay_status replay_stream_copy(void* dst, const void* src, size_t bytes, void*
     return LAUNCH(rs::launch_stream_copy(dst, src, bytes, (hipStream_t)stream), "stream copy");
 }
 
-replay_status replay_stream_read(const void* src, size_t bytes, float* sum_out, void* stream)
+replay_status replay_stream_read(const void* src, size_t bytes, float* partials, void* stream)
 {
     replay_status s;
     if ((s = check_ptr(src, "src")) != REPLAY_OK) return s;
-    if (!sum_out) return fail(REPLAY_ERR_ARG, "sum_out is NULL");
+    if ((s = check_ptr(partials, "partials")) != REPLAY_OK) return s;
     if (bytes % 16) return fail(REPLAY_ERR_ALIGN, "bytes must be a multiple of 16");
-    return LAUNCH(rs::launch_stream_read(src, bytes, sum_out, (hipStream_t)stream), "stream read");
+    return LAUNCH(rs::launch_stream_read(src, bytes, partials, (hipStream_t)stream), "stream read");
 }
 
 }  // extern "C"

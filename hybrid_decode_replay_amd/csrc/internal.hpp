@@ -40,6 +40,13 @@ struct StepArgs {
     int nsplit;              // workgroups per (b, h) tile, along the output axis
     int qckpt;               // nonzero: the checkpoint itself is kept at the copy's precision
     int mxceil;              // nonzero: MXFP4 groups take the non-clipping shared exponent
+    int spw;                 // GDN: 16-column strips per wave (1 or 2)
+    // launch-invariant divisions by multiplication (div_magic / div_small)
+    int cw;                  // columns per workgroup, C / nsplit
+    uint32_t mg_nsplit;      // magic_div(nsplit)
+    uint32_t mg_tiles;       // magic_div(H / ht): heads served per sequence by the grid
+    uint32_t mg_hpg;         // magic_div(hpg)
+    int m20_cx;              // magic_div20(cw / elements per 16-byte chunk)
     float scale;             // GDN output scale
     void* ckpt;              // fragment-ordered tiles (fp32 or fp16, ckpt.hpp)
     uint8_t* rcopy;          // read-copy codes (or null)
@@ -96,7 +103,7 @@ hipError_t launch_quantize_read_copy(void* ckpt, uint8_t* codes, uint8_t* scales
 hipError_t launch_read_copy_to_logical(const uint8_t* codes, const uint8_t* scales, uint8_t* codes_out,
                                        uint8_t* scales_out, int tiles, int C, int R, int rc, hipStream_t s);
 hipError_t launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
-hipError_t launch_stream_read(const void* src, size_t bytes, float* sum_out, hipStream_t s);
+hipError_t launch_stream_read(const void* src, size_t bytes, float* partials, hipStream_t s);
 
 // Conventional baselines (conv.hip).
 struct ConvArgs {

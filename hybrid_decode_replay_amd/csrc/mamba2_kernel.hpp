@@ -54,10 +54,10 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
     constexpr int PRE = 4;                      // chunks per thread fetched ahead of the checkpoint
     constexpr int VM = (16 + TMAX + 3) & ~3;    // bound on the entry count cap + T, padded to 4
     const int C = a.C;
-    const TileIdx tix = tile_of(xcd_tile_index(), a.H / HT, a.nsplit);
+    const TileIdx tix = tile_of(xcd_tile_index(), a.H / HT, a.mg_tiles, a.nsplit, a.mg_nsplit);
     const int b = tix.b, h0 = tix.h * HT;
-    const int g = h0 / a.hpg;
-    const int cw = C / a.nsplit, c0 = tix.sp * cw;   // this workgroup's output columns
+    const int g = (int)div_magic((uint32_t)h0, a.mg_hpg);
+    const int cw = a.cw, c0 = tix.sp * cw;           // this workgroup's output columns
     const int tid = threadIdx.x, nthr = blockDim.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lc = 16 * w + (lane & 15);             // local output column
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
     G.bank_c = a.bank_c; G.bank_r = a.bank_r; G.bank_s = a.bank_s;
     G.hc = (size_t)b * a.H + h0; G.gr = (size_t)b * a.G + g;
     G.b = b; G.h = h0; G.g = g; G.B = a.B; G.H = a.H; G.G = a.G; G.cap = a.cap; G.C = C;
-    G.c0 = c0; G.cw = cw;
+    G.c0 = c0; G.cw = cw; G.m20_cx = a.m20_cx;
     G.ht = HT; G.xc_stride = a.vmax * cw; G.sc_stride = VM;
     G.len = len; G.bank = p.bank; G.V = p.V; G.T = T;
     G.xc = xs; G.xr = bs; G.xq = cs; G.s0 = ds; G.s1 = nullptr; G.p0 = ps;
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
 
     // ---- 7. append the unfolded new tokens to the buffer (slot = position - f)
     stage_append<IO, R>(G, a.bufc, a.bufr, a.bufs0, nullptr, p.bank_new, f, tid, nthr, tix.sp == 0,
-                        tix.sp == 0 && h0 % a.hpg == 0);
+                        tix.sp == 0 && h0 == g * a.hpg);
 }
 
 template <int NB, int IO, int TMAX, bool MF, int RC, int CK, int HT>

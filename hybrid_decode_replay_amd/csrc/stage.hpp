@@ -32,6 +32,7 @@ struct StageGeom {
     size_t hc, gr;       // b*H + h (first head), b*G + g
     int b, h, g, B, H, G, cap, C, len, bank, V, T;
     int c0, cw;          // column slice [c0, c0 + cw) of the per-head vectors this workgroup owns
+    int m20_cx;          // magic_div20 of the chunks per per-head row slice (cw / EPC)
     int ht;              // heads staged (h .. h + ht - 1, one group)
     int xc_stride;       // floats between consecutive heads' xc rows
     int sc_stride;       // floats between consecutive heads' scalars (s0, s1, p0)
@@ -88,13 +89,18 @@ struct Stager {
         nch = nx + nr + G.T * RX;
     }
 
+    // head of a per-head chunk: ht is 1 or at most 4, so compares replace a division
+    __device__ int head_of(int ch) const {
+        return G.ht == 1 ? 0 : (ch >= nxh) + (ch >= 2 * nxh) + (ch >= 3 * nxh);
+    }
+
     __device__ const uint4* src(int ch) const {
         size_t e;
         const void* base;
         if (ch < nx) {
-            const int hh = G.ht == 1 ? 0 : ch / nxh;
+            const int hh = head_of(ch);
             const int r = ch - hh * nxh;
-            const int j = r / CX, o = r - j * CX;
+            const int j = div_small(r, G.m20_cx), o = r - j * CX;
             if (j < G.len) { base = G.bufc; e = (size_t)G.bank * G.bank_c + ((G.hc + hh) * G.cap + j) * G.C + G.c0; }
             else { base = G.in_c; e = (((size_t)(j - G.len) * G.B + G.b) * G.H + G.h + hh) * G.C + G.c0; }
             return reinterpret_cast<const uint4*>(static_cast<const char*>(base) + e * ES) + o;
@@ -114,9 +120,9 @@ struct Stager {
 
     __device__ float* dst(int ch) const {
         if (ch < nx) {
-            const int hh = G.ht == 1 ? 0 : ch / nxh;
+            const int hh = head_of(ch);
             const int r = ch - hh * nxh;
-            const int j = r / CX;
+            const int j = div_small(r, G.m20_cx);
             return G.xc + hh * G.xc_stride + j * G.cw + (r - j * CX) * EPC;
         }
         ch -= nx;
@@ -213,19 +219,21 @@ __device__ __forceinline__ void stage_append(const StageGeom& G, void* bufc, voi
     const int nnew = G.V - j0;
     if (nnew <= 0) return;
     const int CX = G.cw / S::EPC;
-    for (int i = tid; i < G.ht * nnew * CX; i += nthr) {
-        const int hh = i / (nnew * CX), r = i - hh * nnew * CX;
-        const int jj = r / CX, o = r - jj * CX, j = j0 + jj;
+    for (int hh = 0; hh < G.ht; ++hh) {
         char* bx = static_cast<char*>(bufc) + ((size_t)bank_new * G.bank_c + (G.hc + hh) * G.cap * G.C + G.c0) * S::ES;
-        reinterpret_cast<uint4*>(bx + (size_t)(j - f) * G.C * S::ES)[o] =
-            lds_to_chunk<IO>(G.xc + hh * G.xc_stride + j * G.cw + o * S::EPC);
+        for (int r = tid; r < nnew * CX; r += nthr) {
+            const int jj = div_small(r, G.m20_cx), o = r - jj * CX, j = j0 + jj;
+            reinterpret_cast<uint4*>(bx + (size_t)(j - f) * G.C * S::ES)[o] =
+                lds_to_chunk<IO>(G.xc + hh * G.xc_stride + j * G.cw + o * S::EPC);
+        }
     }
     if (head_writer) {
-        for (int i = tid; i < G.ht * nnew; i += nthr) {
-            const int hh = i / nnew, jj = i - hh * nnew;
-            const size_t slot = (size_t)bank_new * G.bank_s + (G.hc + hh) * G.cap + (j0 + jj - f);
-            bufs0[slot] = G.s0[hh * G.sc_stride + j0 + jj];
-            if (bufs1) bufs1[slot] = G.s1[hh * G.sc_stride + j0 + jj];
+        for (int hh = 0; hh < G.ht; ++hh) {
+            for (int jj = tid; jj < nnew; jj += nthr) {
+                const size_t slot = (size_t)bank_new * G.bank_s + (G.hc + hh) * G.cap + (j0 + jj - f);
+                bufs0[slot] = G.s0[hh * G.sc_stride + j0 + jj];
+                if (bufs1) bufs1[slot] = G.s1[hh * G.sc_stride + j0 + jj];
+            }
         }
     }
     if (group_writer) {

@@ -130,7 +130,7 @@ typedef enum {
 typedef struct {
     int32_t abi_version;  /* REPLAY_ABI_VERSION                                  */
     int32_t kind;         /* replay_kind                                         */
-    int32_t batch;        /* B >= 1                                              */
+    int32_t batch;        /* B >= 1; B * H * max(H, 256) < 2^32 (REPLAY_ERR_SHAPE) */
     int32_t nheads;       /* H >= 1                                              */
     int32_t ngroups;      /* G >= 1, divides H (Mamba-2 B/C groups; GDN q/k heads)*/
     int32_t head_dim;     /* Mamba-2 P; GDN DV.  Multiple of 16, <= 256          */
@@ -398,10 +398,13 @@ replay_status replay_standin_attention(const void *q, int64_t q_stride, const vo
 /* Streaming copy of `bytes` (multiple of 16) from src to dst: the in-run
  * bandwidth ceiling and the reference for hardware byte counters. */
 replay_status replay_stream_copy(void *dst, const void *src, size_t bytes, void *stream);
-/* Streaming read of `bytes` (multiple of 16) fp32 values from src, adding
- * their sum to *sum_out (device float, caller-initialised): the read-only
- * bandwidth ceiling that non-flush steps are measured against. */
-replay_status replay_stream_read(const void *src, size_t bytes, float *sum_out, void *stream);
+/* Streaming read of `bytes` (multiple of 16, else REPLAY_ERR_ALIGN) of fp32
+ * values from src, in the replay kernels' access pattern (one 32 KiB tile per
+ * workgroup, 128-bit nontemporal loads): the read-only bandwidth ceiling that
+ * non-flush steps are measured against.  partials (device, caller-owned,
+ * max(1, ceil(bytes / 32768)) floats) receives the sum of each 32 KiB tile's
+ * values, the last tile ragged; every entry is overwritten. */
+replay_status replay_stream_read(const void *src, size_t bytes, float *partials, void *stream);
 
 #ifdef __cplusplus
 }

@@ -35,7 +35,10 @@ difference may also appear only rarely: at most FP8_FLIP_FRAC of the codes
 (the fp32 fold is within ~1e-6 relative of the fp64 one and E4M3 steps are at
 least 2^-4 relative, so about 3e-5 of the elements per fold straddle a midpoint).
 Outputs are then held element-wise to tol * |y|_inf plus the read-out of the
-checkpoint difference measured at that step (itself inside the derived bound):
+checkpoint difference measured at that step (itself inside the derived bound;
+the same form holds the outputs that read a read copy of an fp32 or fp16
+checkpoint, with the difference of the two sides' copies of their own
+checkpoints as dS, nonzero only where a value straddles a quantization boundary):
 Mamba-2 sum_n |dS[p, n]| |C_n| (decays <= 1); GDN scale |dS[i, :]|_2 |q|_2 (the
 adjoint chain's r_0 has 2-norm <= |q|_2).  With an MXFP4 copy of the FP8
 checkpoint the copy difference |Q(S_gpu) - Q(S_ref)| (both quantized by the
@@ -211,7 +214,7 @@ class Pair:
         checkpoint, whose measured difference is read out through them)."""
         got = y_gpu.float().cpu().numpy().reshape(np.shape(y_orc))
         assert np.all(np.isfinite(got)), f"{what}: non-finite GPU outputs"
-        if self.fp8 and self.dS is not None and self.dS.any():
+        if self.dS is not None and self.dS.any():
             g = np.asarray(got, np.float64).reshape(-1, self.B, self.H, self.C)
             r = np.asarray(y_orc, np.float64).reshape(g.shape)
             allow = self.tol * np.max(np.abs(r), axis=-1, keepdims=True) + readout_bound(
@@ -266,6 +269,13 @@ class Pair:
         err = float(np.max(np.where(zero, 0.0, num / den)))
         self.max_err["ckpt"] = max(self.max_err["ckpt"], err)
         assert err <= self.ckpt_tol, f"{what}: checkpoint error {err:.3e} > {self.ckpt_tol:.1e}"
+        if self.rc is not None:
+            # both sides quantize their own checkpoint: values next to a quantization
+            # boundary may land on different codes; the difference of the two copies
+            # (each quantized by the oracle) is read out by the next non-folding steps
+            d = np.abs(ro.read_copy_values(ck, self.rc).reshape(ck.shape)
+                       - ro.read_copy_values(ref, self.rc).reshape(ref.shape))
+            self.dS = d if d.any() else None
 
     def _check_book(self, what):
         check_book(self.st.read_book(), self.orc, what)
@@ -294,7 +304,7 @@ class Pair:
         """Outputs of the sequences `sel` only (masked steps leave the others' rows alone)."""
         if sel.size == 0:
             return
-        if self.fp8 and self.dS is not None and self.dS.any():
+        if self.dS is not None and self.dS.any():
             full = np.zeros_like(self.dS)
             full[sel] = self.dS[sel]
             saved, self.dS = self.dS, full
