@@ -132,6 +132,31 @@ __device__ __forceinline__ void ckpt_store(void* ck, size_t strip, int lane, con
     }
 }
 
+// Dot product of a strip's checkpoint values with per-block read-out vectors
+// (sum over nb of s[nb] . c[nb]), decoding the words ckpt_issue left in the
+// registers on the fly (no decoded strip is formed; fp32 is used as loaded).
+template <int NB, int CK>
+__device__ __forceinline__ float ckpt_dot(const f32x4 (&s)[NB], const f32x4 (&c)[NB])
+{
+    float acc = 0.f;
+    if constexpr (CK == CK_FP8) {
+        acc = rc_dot<NB, RC_FP8>(s, c);
+    } else if constexpr (CK == CK_F32) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc += dot4(s[nb], c[nb]);
+    } else if constexpr (NB == 1) {
+        const u32x4 w = __builtin_bit_cast(u32x4, s[0]);
+        acc = dot4(h4_to_f32(u32x2{w.x, w.y}), c[0]);
+    } else {
+#pragma unroll
+        for (int q = 0; q < NB / 2; ++q) {
+            const u32x4 w = __builtin_bit_cast(u32x4, s[2 * q]);
+            acc += dot4(h4_to_f32(u32x2{w.x, w.y}), c[2 * q]) + dot4(h4_to_f32(u32x2{w.z, w.w}), c[2 * q + 1]);
+        }
+    }
+    return acc;
+}
+
 // Registers -> the values the store will keep (identity for fp32).
 template <int NB, int CK>
 __device__ __forceinline__ void ckpt_round(f32x4 (&s)[NB])

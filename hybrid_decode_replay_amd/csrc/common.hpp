@@ -135,11 +135,40 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// Across the four 16-lane rows of a wave, on gfx950's row-swap permutes (VALU,
+// no LDS round trip): v_permlane16_swap with both operands v leaves rows
+// (r0, r0, r2, r2) in one register and (r1, r1, r3, r3) in the other, so their
+// sum holds r0 + r1 in rows 0-1 and r2 + r3 in rows 2-3; v_permlane32_swap does
+// the same for the two halves.  Every lane ends with (r0 + r1) + (r2 + r3).
+__device__ __forceinline__ float row_pair_swap16(float v, float& other) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v),
+                                                     false, false);
+    other = __builtin_bit_cast(float, (uint32_t)r[1]);
+    return __builtin_bit_cast(float, (uint32_t)r[0]);
+}
+__device__ __forceinline__ float half_swap32(float v, float& other) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v),
+                                                     false, false);
+    other = __builtin_bit_cast(float, (uint32_t)r[1]);
+    return __builtin_bit_cast(float, (uint32_t)r[0]);
+}
+
 // Sum over the four lanes that share (lane % 16): lanes l, l^16, l^32, l^48.
 __device__ __forceinline__ float sum_over_row_groups(float v) {
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
+    float o;
+    const float a = row_pair_swap16(v, o);
+    v = a + o;
+    const float c = half_swap32(v, o);
+    return c + o;
+}
+
+// Maximum over the same four lanes.
+__device__ __forceinline__ float max_over_row_groups(float v) {
+    float o;
+    const float a = row_pair_swap16(v, o);
+    v = fmaxf(a, o);
+    const float c = half_swap32(v, o);
+    return fmaxf(c, o);
 }
 
 // Order LDS accesses made by different lanes of the same wave (no workgroup barrier).

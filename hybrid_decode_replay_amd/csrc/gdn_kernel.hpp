@@ -271,13 +271,28 @@ __global__ __launch_bounds__(256, SPW == 1 ? (NB <= 8 ? 6 : 4) : 4) void gdn_ste
             wave_lds_sync();
 #pragma unroll
             for (int j = 0; j < SPW; ++j) {
-                if (f == 0) {
-                    if (from_copy) rc_decode<NB, RC>(s[j]);
-                    else ckpt_decode<NB, CK>(s[j]);
-                }
                 float gacc = 0.f;
+                if constexpr (SPW == 1) {
+                    f32x4 rv[NB];                 // r_0 as the lanes' checkpoint rows need it
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) gacc += dot4(s[j][nb], ld4(rw + nb * 16 + rq));
+                    for (int nb = 0; nb < NB; ++nb) rv[nb] = ld4(rw + nb * 16 + rq);
+                    // raw words that were not folded go straight into the dot product
+                    if (f == 0) {
+                        gacc = from_copy ? rc_dot<NB, RC>(s[j], rv) : ckpt_dot<NB, CK>(s[j], rv);
+                    } else {
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) gacc += dot4(s[j][nb], rv[nb]);
+                    }
+                } else {
+                    // two strips: decoding in place keeps the register count within four
+                    // waves per SIMD
+                    if (f == 0) {
+                        if (from_copy) rc_decode<NB, RC>(s[j]);
+                        else ckpt_decode<NB, CK>(s[j]);
+                    }
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) gacc += dot4(s[j][nb], ld4(rw + nb * 16 + rq));
+                }
                 gacc = sum_over_row_groups(gacc);
                 if (lane < 16) st_io<IO>(a.y, ((size_t)b * a.H + h) * C + c0 + lc0 + 16 * j, a.scale * (gacc + rep[j]));
             }

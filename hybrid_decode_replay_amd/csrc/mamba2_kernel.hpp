@@ -248,15 +248,29 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
                         }
                         gdec = fexp((psh[pos] - (f > 0 ? psh[f - 1] : 0.f)) * Ah);
                     }
-                    // the checkpoint values are needed from here on
-                    if (!EARLY_DECODE && t == 0 && f == 0) {
-                        if (from_copy) rc_decode<NB, RC>(s);
-                        else ckpt_decode<NB, CK>(s);
-                    }
-                    // checkpoint read-out (S' C_t)[col], reduced over the four row groups
+                    // checkpoint read-out (S' C_t)[col], reduced over the four row groups; one
+                    // token reads raw words that were not folded straight into the dot product
                     float gacc = 0.f;
+                    if constexpr (TMAX == 1 && !EARLY_DECODE) {
+                        // C as the lanes' checkpoint rows need it (rows 4(l/16)..+3 of every block)
+                        f32x4 cvec[NB];
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) gacc += dot4(s[nb], ld4(cs + t * R + nb * 16 + rq));
+                        for (int nb = 0; nb < NB; ++nb) cvec[nb] = ld4(cs + nb * 16 + rq);
+                        if (f == 0) {
+                            gacc = from_copy ? rc_dot<NB, RC>(s, cvec) : ckpt_dot<NB, CK>(s, cvec);
+                        } else {
+#pragma unroll
+                            for (int nb = 0; nb < NB; ++nb) gacc += dot4(s[nb], cvec[nb]);
+                        }
+                    } else {
+                        // the checkpoint values are needed from here on
+                        if (!EARLY_DECODE && t == 0 && f == 0) {
+                            if (from_copy) rc_decode<NB, RC>(s);
+                            else ckpt_decode<NB, CK>(s);
+                        }
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) gacc += dot4(s[nb], ld4(cs + t * R + nb * 16 + rq));
+                    }
                     gacc = sum_over_row_groups(gacc);
                     const float yv = (pos >= f) ? gdec * gacc + rep + Dh * xt : gacc + Dh * xt;
                     if (lane < 16) st_io<IO>(a.y, (((size_t)t * sB + b) * a.H + h) * C + col, yv);

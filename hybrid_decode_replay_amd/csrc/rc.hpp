@@ -198,8 +198,7 @@ __device__ __forceinline__ void rc_fp4_store(uint8_t* codes, uint8_t* scales, si
         const f32x4 a = s[2 * p], b = s[2 * p + 1];
         float am = fmaxf(fmaxf(fmaxf(__builtin_fabsf(a.x), __builtin_fabsf(a.y)), fmaxf(__builtin_fabsf(a.z), __builtin_fabsf(a.w))),
                          fmaxf(fmaxf(__builtin_fabsf(b.x), __builtin_fabsf(b.y)), fmaxf(__builtin_fabsf(b.z), __builtin_fabsf(b.w))));
-        am = fmaxf(am, __shfl_xor(am, 16, 64));      // the group spans lanes l%16 + 16*q
-        am = fmaxf(am, __shfl_xor(am, 32, 64));
+        am = max_over_row_groups(am);                // the group spans lanes l%16 + 16*q
         const int X = mx_exponent(am, ceil);
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
         w[p] = pack_e2m1(v, X);
@@ -246,8 +245,7 @@ __device__ __forceinline__ void rc_fp4_roundtrip(f32x4 (&s)[NB], bool ceil)
         const f32x4 a = s[2 * p], b = s[2 * p + 1];
         float am = fmaxf(fmaxf(fmaxf(__builtin_fabsf(a.x), __builtin_fabsf(a.y)), fmaxf(__builtin_fabsf(a.z), __builtin_fabsf(a.w))),
                          fmaxf(fmaxf(__builtin_fabsf(b.x), __builtin_fabsf(b.y)), fmaxf(__builtin_fabsf(b.z), __builtin_fabsf(b.w))));
-        am = fmaxf(am, __shfl_xor(am, 16, 64));
-        am = fmaxf(am, __shfl_xor(am, 32, 64));
+        am = max_over_row_groups(am);
         const int X = mx_exponent(am, ceil);
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
         const uint32_t word = pack_e2m1(v, X);
@@ -321,6 +319,42 @@ __device__ __forceinline__ void rc_decode(f32x4 (&s)[NB])
         }
         rc_fp4_decode<NB>(w, sc, s);
     }
+}
+
+// Dot product of a strip's read-copy values with per-block read-out vectors:
+// sum over nb of s[nb] . c[nb], the words decoded on the fly from the registers
+// rc_issue filled (no decoded strip is formed).  MXFP4: the group scale, a power
+// of two, multiplies the group's partial dot once.
+template <int NB, int RC>
+__device__ __forceinline__ float rc_dot(const f32x4 (&s)[NB], const f32x4 (&c)[NB])
+{
+    float acc = 0.f;
+    if constexpr (RC == RC_FP8) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const float x = s[nb].x;
+            const uint32_t w = __builtin_bit_cast(uint32_t, x);
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+            acc += lo[0] * c[nb].x + lo[1] * c[nb].y + hi[0] * c[nb].z + hi[1] * c[nb].w;
+        }
+    } else if constexpr (RC == RC_MXFP4) {
+#pragma unroll
+        for (int p = 0; p < NB / 2; ++p) {
+            const float x = s[2 * p].x, y = s[2 * p].y;
+            const uint32_t w = __builtin_bit_cast(uint32_t, x);
+            const float scale = e8m0_to_f32(__builtin_bit_cast(uint32_t, y));
+            const auto b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.f, 0);
+            const auto b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.f, 1);
+            const auto b2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.f, 2);
+            const auto b3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.f, 3);
+            const float g = b0[0] * c[2 * p].x + b0[1] * c[2 * p].y + b1[0] * c[2 * p].z + b1[1] * c[2 * p].w +
+                            b2[0] * c[2 * p + 1].x + b2[1] * c[2 * p + 1].y + b3[0] * c[2 * p + 1].z +
+                            b3[1] * c[2 * p + 1].w;
+            acc += scale * g;
+        }
+    }
+    return acc;
 }
 
 }  // namespace rs
