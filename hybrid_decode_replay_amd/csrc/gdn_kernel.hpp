@@ -98,8 +98,9 @@ __global__ __launch_bounds__(256, SPW == 1 ? (NB <= 8 ? 6 : 4) : 4) void gdn_ste
     G.hc = (size_t)b * a.H + h; G.gr = (size_t)b * a.G + g;
     G.b = b; G.h = h; G.g = g; G.B = a.B; G.H = a.H; G.G = a.G; G.cap = a.cap; G.C = C;
     G.c0 = c0; G.cw = cw; G.m20_cx = a.m20_cx;
-    G.ht = 1; G.xc_stride = 0; G.sc_stride = 0;
+    G.ht = 1; G.xc_stride = 0; G.xc_row = cw; G.sc_stride = 0;
     G.len = len; G.bank = p.bank; G.V = V; G.T = T;
+    G.f = p.f; G.bank_new = p.bank_new; G.head_writer = tix.sp == 0; G.group_writer = tix.sp == 0 && h == g * a.hpg;
     G.xc = vs; G.xr = ks; G.xq = qs; G.s0 = al; G.s1 = be; G.p0 = nullptr;
 
     // ---- 1. entry chunks ahead of the checkpoint stream, 2. checkpoint strips
@@ -356,10 +357,6 @@ __global__ __launch_bounds__(256, SPW == 1 ? (NB <= 8 ? 6 : 4) : 4) void gdn_ste
             if constexpr (RC != RC_NONE) rc_store<NB, RC>(a.rcopy, a.rscale, strip0 + j, lane, s[j], a.mxceil);
         }
     }
-
-    // ---- 7. append the unfolded new tokens
-    stage_append<IO, R>(G, a.bufc, a.bufr, a.bufs0, a.bufs1, p.bank_new, f, tid, nthr, tix.sp == 0,
-                        tix.sp == 0 && h == g * a.hpg);
 }
 
 template <int NB, int IO, int TMAX, int RC, int CK, int SPW>

@@ -53,6 +53,8 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
     constexpr int RS = R + 4;                   // padded LDS stride of B rows
     constexpr int PRE = 4;                      // chunks per thread fetched ahead of the checkpoint
     constexpr int VM = (16 + TMAX + 3) & ~3;    // bound on the entry count cap + T, padded to 4
+    constexpr int XS = 64;                      // LDS row stride of x rows (cw <= 64: four waves of 16)
+    const int vx = a.vmax + 3;                  // x rows per head: entries, then three zero rows
     const int C = a.C;
     const TileIdx tix = tile_of(xcd_tile_index(), a.H / HT, a.mg_tiles, a.nsplit, a.mg_nsplit);
     const int b = tix.b, h0 = tix.h * HT;
@@ -73,9 +75,10 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
     // ---- LDS partition (floats; the launch sizes cs for max(T, 1) rows)
     float* ds = lds;                              // [HT][VM]       entry dt (vmax <= VM)
     float* ps = ds + HT * VM;                     // [HT][VM]       inclusive prefix sums of dt
-    float* xs = ps + HT * VM;                     // [HT][vmax][cw] entry x rows (own columns)
-    float* bs = xs + (size_t)HT * a.vmax * cw;    // [vmax][RS]     entry B rows
+    float* xs = ps + HT * VM;                     // [HT][vx][XS]   entry x rows (own columns)
+    float* bs = xs + (size_t)HT * vx * XS;        // [vmax][RS]     entry B rows
     float* cs = bs + (size_t)a.vmax * RS;         // [Tr][R]        read-out rows C_t
+    float* cf = cs + (size_t)(T > 0 ? T : 1) * R; // [4][16]        per-wave replay coefficients
 
     StageGeom G;
     G.bufc = a.bufc; G.bufr = a.bufr; G.bufs0 = a.bufs0; G.bufs1 = nullptr;
@@ -84,8 +87,9 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
     G.hc = (size_t)b * a.H + h0; G.gr = (size_t)b * a.G + g;
     G.b = b; G.h = h0; G.g = g; G.B = a.B; G.H = a.H; G.G = a.G; G.cap = a.cap; G.C = C;
     G.c0 = c0; G.cw = cw; G.m20_cx = a.m20_cx;
-    G.ht = HT; G.xc_stride = a.vmax * cw; G.sc_stride = VM;
+    G.ht = HT; G.xc_stride = vx * XS; G.xc_row = XS; G.sc_stride = VM;
     G.len = len; G.bank = p.bank; G.V = p.V; G.T = T;
+    G.f = p.f; G.bank_new = p.bank_new; G.head_writer = tix.sp == 0; G.group_writer = tix.sp == 0 && h0 == g * a.hpg;
     G.xc = xs; G.xr = bs; G.xq = cs; G.s0 = ds; G.s1 = nullptr; G.p0 = ps;
 
     // ---- 1. entry and read-out chunks, issued ahead of the checkpoint stream
@@ -109,8 +113,14 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
     f32x4 sbuf[HT > 1 ? 2 : 1][NB];
     issue(0, sbuf[0]);
 
-    // ---- 3. publish the staged rows
+    // ---- 3. publish the staged rows; the three x rows after the last entry are
+    // zeroed, so a replay pass of four entries may read past the last one (with a
+    // zero coefficient) without touching stale values
     stage_publish<IO, R, PRE>(stg, tid, nthr, pre, sr);
+    for (int i = tid; i < HT * 3 * (XS / 4); i += nthr) {
+        const int hh = i / (3 * (XS / 4)), r = i - hh * (3 * (XS / 4));
+        st4(xs + (size_t)hh * vx * XS + (size_t)(p.V + r / (XS / 4)) * XS + 4 * (r % (XS / 4)), f32x4{0.f, 0.f, 0.f, 0.f});
+    }
     __syncthreads();
     // An fp16 checkpoint without a copy is decoded as soon as it is needed at all:
     // the shorter register life of the raw words keeps the kernel at more waves per
@@ -144,7 +154,7 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
         const size_t strip_index = (size_t)(b * a.H + h) * (C >> 4) + (c0 >> 4) + w;
         const float* dsh = ds + hh * VM;
         const float* psh = ps + hh * VM;
-        const float* xsh = xs + (size_t)hh * a.vmax * cw;
+        const float* xsh = xs + (size_t)hh * vx * XS;
         if constexpr (EARLY_DECODE) ckpt_decode<NB, CK>(s);
 
         const float Ah = a.A[h];
@@ -164,7 +174,7 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
                     const int i = kb * 4 + iq;
-                    bop[kb] = (i < f) ? fexp((pf - psh[i]) * Ah) * dsh[i] * xsh[i * cw + lc] : 0.f;
+                    bop[kb] = (i < f) ? fexp((pf - psh[i]) * Ah) * dsh[i] * xsh[i * XS + lc] : 0.f;
                 }
                 const int nkb = (f + 3) >> 2;
 #pragma unroll
@@ -184,7 +194,7 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
                 float wx[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    wx[i] = (i < f) ? fexp((pf - psh[i]) * Ah) * dsh[i] * xsh[i * cw + lc] : 0.f;
+                    wx[i] = (i < f) ? fexp((pf - psh[i]) * Ah) * dsh[i] * xsh[i * XS + lc] : 0.f;
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -211,16 +221,42 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
             for (int t = 0; t < TMAX; ++t) {
                 if (t < T) {
                     const int pos = len + t;
-                    const float xt = xsh[pos * cw + lc];
+                    const float xt = xsh[pos * XS + lc];
                     // replay of entries f..pos (formed first: it needs only LDS, so it runs while
                     // the checkpoint loads are in flight).  Lane quad jj = l/4 forms B_j . C_t and
                     // the decayed coefficient; output lanes gather the coefficients by readlane.
                     float rep = 0.f, gdec = 1.f;
-                    if (pos >= f) {
+                    if (TMAX == 1 && pos >= f) {
+                        // one token: at most 16 unfolded entries.  Lane quad jj forms entry
+                        // f + jj's decayed coefficient into this wave's LDS row; every lane
+                        // then reads them four at a time (broadcast) against its column of
+                        // the x rows (fixed row stride: immediate offsets, no index math).
+                        const int nr = pos - f + 1;
+                        const int jj = lane >> 2;
+                        float* cfw = cf + 16 * w;
+                        if ((lane & 3) == 0) {
+                            float c = 0.f;
+                            if (jj < nr) c = fexp((psh[pos] - psh[f + jj]) * Ah) * dsh[f + jj] * dot1;
+                            cfw[jj] = c;
+                        }
+                        wave_lds_sync();
+                        const float* xb = xsh + (size_t)f * XS + lc;
+#pragma unroll
+                        for (int e4 = 0; e4 < 16; e4 += 4) {
+                            if (e4 < nr) {
+                                const f32x4 c4 = ld4(cfw + e4);
+                                rep += c4.x * xb[(e4 + 0) * XS] + c4.y * xb[(e4 + 1) * XS] +
+                                       c4.z * xb[(e4 + 2) * XS] + c4.w * xb[(e4 + 3) * XS];
+                            }
+                        }
+                        // the row is read again by the next head's pass
+                        wave_lds_sync();
+                        gdec = fexp((psh[pos] - (f > 0 ? psh[f - 1] : 0.f)) * Ah);
+                    } else if (pos >= f) {
                         const int nr = pos - f + 1;
                         const int q = lane & 3;
                         const float* xcol = xsh + lc;
-                        const int pos_u = uni(pos), cw_u = uni(cw), f_u = uni(f);
+                        const int pos_u = uni(pos), f_u = uni(f);
                         for (int jj0 = 0; jj0 < nr; jj0 += 16) {
                             const int jj = jj0 + (lane >> 2), j = f + jj;
                             float dot = dot1;
@@ -242,7 +278,7 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
                                 if (e4 < ne) {
 #pragma unroll
                                     for (int e = e4; e < e4 + 4; ++e)
-                                        rep += readlane(coef, 4 * e) * xcol[uni(min(f_u + jj0 + e, pos_u) * cw_u)];
+                                        rep += readlane(coef, 4 * e) * xcol[uni(min(f_u + jj0 + e, pos_u) * XS)];
                                 }
                             }
                         }
@@ -284,10 +320,6 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
             if constexpr (RC != RC_NONE) rc_store<NB, RC>(a.rcopy, a.rscale, strip_index, lane, s, a.mxceil);
         }
     }
-
-    // ---- 7. append the unfolded new tokens to the buffer (slot = position - f)
-    stage_append<IO, R>(G, a.bufc, a.bufr, a.bufs0, nullptr, p.bank_new, f, tid, nthr, tix.sp == 0,
-                        tix.sp == 0 && h0 == g * a.hpg);
 }
 
 template <int NB, int IO, int TMAX, bool MF, int RC, int CK, int HT>
@@ -296,7 +328,7 @@ static hipError_t mamba2_launch_ht(const StepArgs& a, hipStream_t s)
     const size_t Tr = a.T > 0 ? a.T : 1;
     const size_t R = NB * 16;
     const size_t VM = (16 + TMAX + 3) & ~3;
-    const size_t lds = sizeof(float) * (HT * (size_t)a.vmax * (a.C / a.nsplit) + (size_t)a.vmax * (R + 4) + Tr * R +
+    const size_t lds = sizeof(float) * (HT * ((size_t)a.vmax + 3) * 64 + (size_t)a.vmax * (R + 4) + Tr * R + 64 +
                                         2 * HT * VM);
     auto k = mamba2_step_kernel<NB, IO, TMAX, MF, RC, CK, HT>;
     if (lds > 64 * 1024) {

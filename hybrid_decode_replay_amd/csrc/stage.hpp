@@ -8,7 +8,11 @@
 // are fetched as 16-byte chunks.  stage_issue() puts the first PRE chunks of
 // every thread in flight (call it before the checkpoint loads, so that
 // consuming the chunks later waits only for them); stage_publish() converts
-// them to fp32 in LDS.  The caller then needs one workgroup barrier.
+// them to fp32 in LDS and appends the new entries that stay unfolded to the
+// buffer straight from the chunk registers (raw io bits; scalars as fp32).  The
+// caller then needs one workgroup barrier.  The append writes slots the launch
+// reads from no workgroup: slots >= len of the bank being read, or the other
+// bank after a fold.
 //
 // A workgroup may serve ht consecutive heads h..h+ht-1 of one group: their
 // per-head rows and scalars are staged side by side (xc_stride, sc_stride
@@ -35,8 +39,14 @@ struct StageGeom {
     int m20_cx;          // magic_div20 of the chunks per per-head row slice (cw / EPC)
     int ht;              // heads staged (h .. h + ht - 1, one group)
     int xc_stride;       // floats between consecutive heads' xc rows
+    int xc_row;          // floats between consecutive entries' xc rows (>= cw)
     int sc_stride;       // floats between consecutive heads' scalars (s0, s1, p0)
-    float* xc;           // LDS [ht][vmax][cw]
+    // append of the unfolded new entries j >= max(f, len) to bank bank_new at slot
+    // j - f, made from the chunk registers as they are published
+    int f, bank_new;
+    bool head_writer;    // writes the per-head rows' own column slice and the scalars
+    bool group_writer;   // writes the per-group rows
+    float* xc;           // LDS [ht][vmax][xc_row]
     float* xr;           // LDS [vmax][R + 4]
     float* xq;           // LDS [T][R]
     float* s0;           // LDS [ht][sc_stride]
@@ -94,42 +104,69 @@ struct Stager {
         return G.ht == 1 ? 0 : (ch >= nxh) + (ch >= 2 * nxh) + (ch >= 3 * nxh);
     }
 
-    __device__ const uint4* src(int ch) const {
-        size_t e;
-        const void* base;
+    // A chunk's place: kind 0 per-head row (head hh), 1 per-group row, 2 read-out
+    // row; entry (or token) j, 16-byte offset o within the row slice.
+    struct Ref {
+        int kind, hh, j, o;
+    };
+
+    __device__ Ref ref(int ch) const {
+        Ref c;
         if (ch < nx) {
-            const int hh = head_of(ch);
-            const int r = ch - hh * nxh;
-            const int j = div_small(r, G.m20_cx), o = r - j * CX;
-            if (j < G.len) { base = G.bufc; e = (size_t)G.bank * G.bank_c + ((G.hc + hh) * G.cap + j) * G.C + G.c0; }
-            else { base = G.in_c; e = (((size_t)(j - G.len) * G.B + G.b) * G.H + G.h + hh) * G.C + G.c0; }
-            return reinterpret_cast<const uint4*>(static_cast<const char*>(base) + e * ES) + o;
+            c.kind = 0;
+            c.hh = head_of(ch);
+            const int r = ch - c.hh * nxh;
+            c.j = div_small(r, G.m20_cx);
+            c.o = r - c.j * CX;
+            return c;
         }
         ch -= nx;
-        if (ch < nr) {
-            const int j = ch / RX, o = ch - j * RX;
-            if (j < G.len) { base = G.bufr; e = (size_t)G.bank * G.bank_r + (G.gr * G.cap + j) * R; }
-            else { base = G.in_r; e = (((size_t)(j - G.len) * G.B + G.b) * G.G + G.g) * R; }
-            return reinterpret_cast<const uint4*>(static_cast<const char*>(base) + e * ES) + o;
-        }
-        ch -= nr;
-        const int t = ch / RX, o = ch - t * RX;
-        e = (((size_t)t * G.B + G.b) * G.G + G.g) * R;
-        return reinterpret_cast<const uint4*>(static_cast<const char*>(G.in_q) + e * ES) + o;
+        c.hh = 0;
+        c.kind = ch < nr ? 1 : 2;
+        if (ch >= nr) ch -= nr;
+        c.j = ch / RX;
+        c.o = ch - c.j * RX;
+        return c;
     }
 
-    __device__ float* dst(int ch) const {
-        if (ch < nx) {
-            const int hh = head_of(ch);
-            const int r = ch - hh * nxh;
-            const int j = div_small(r, G.m20_cx);
-            return G.xc + hh * G.xc_stride + j * G.cw + (r - j * CX) * EPC;
+    __device__ const uint4* src(const Ref& c) const {
+        size_t e;
+        const void* base;
+        if (c.kind == 0) {
+            if (c.j < G.len) { base = G.bufc; e = (size_t)G.bank * G.bank_c + ((G.hc + c.hh) * G.cap + c.j) * G.C + G.c0; }
+            else { base = G.in_c; e = (((size_t)(c.j - G.len) * G.B + G.b) * G.H + G.h + c.hh) * G.C + G.c0; }
+        } else if (c.kind == 1) {
+            if (c.j < G.len) { base = G.bufr; e = (size_t)G.bank * G.bank_r + (G.gr * G.cap + c.j) * R; }
+            else { base = G.in_r; e = (((size_t)(c.j - G.len) * G.B + G.b) * G.G + G.g) * R; }
+        } else {
+            base = G.in_q;
+            e = (((size_t)c.j * G.B + G.b) * G.G + G.g) * R;
         }
-        ch -= nx;
-        if (ch < nr) { const int j = ch / RX; return G.xr + j * RS + (ch - j * RX) * EPC; }
-        ch -= nr;
-        const int t = ch / RX;
-        return G.xq + t * R + (ch - t * RX) * EPC;
+        return reinterpret_cast<const uint4*>(static_cast<const char*>(base) + e * ES) + c.o;
+    }
+
+    __device__ float* dst(const Ref& c) const {
+        if (c.kind == 0) return G.xc + c.hh * G.xc_stride + c.j * G.xc_row + c.o * EPC;
+        if (c.kind == 1) return G.xr + c.j * RS + c.o * EPC;
+        return G.xq + c.j * R + c.o * EPC;
+    }
+
+    // Buffer slot a new entry's chunk is appended to, or null (an entry already in
+    // the buffer, a folded one, a read-out row, or a row another workgroup writes).
+    __device__ uint4* append_dst(const Ref& c) const {
+        const int j0 = max(G.f, G.len);
+        if (c.kind == 2 || c.j < j0) return nullptr;
+        size_t e;
+        void* base;
+        if (c.kind == 0) {                  // every workgroup writes its own column slice
+            base = const_cast<void*>(G.bufc);
+            e = (size_t)G.bank_new * G.bank_c + ((G.hc + c.hh) * G.cap + (c.j - G.f)) * G.C + G.c0;
+        } else {
+            if (!G.group_writer) return nullptr;
+            base = const_cast<void*>(G.bufr);
+            e = (size_t)G.bank_new * G.bank_r + (G.gr * G.cap + (c.j - G.f)) * R;
+        }
+        return reinterpret_cast<uint4*>(static_cast<char*>(base) + e * ES) + c.o;
     }
 };
 
@@ -147,7 +184,7 @@ __device__ __forceinline__ void stage_issue(const Stager<IO, R>& st, int tid, in
 #pragma unroll
     for (int u = 0; u < PRE; ++u) {
         const int ch = tid + u * nthr;
-        if (ch < st.nch) pre[u] = *st.src(ch);
+        if (ch < st.nch) pre[u] = *st.src(st.ref(ch));
     }
     // Entry scalars: lanes below len read the buffer, the rest the current inputs
     // (present whenever tokens are appended; with none, V == len).  One load per
@@ -187,14 +224,29 @@ __device__ __forceinline__ void stage_publish(const Stager<IO, R>& st, int tid, 
 #pragma unroll
     for (int u = 0; u < PRE; ++u) {
         const int ch = tid + u * nthr;
-        if (ch < st.nch) chunk_to_lds<IO>(st.dst(ch), pre[u]);
+        if (ch < st.nch) {
+            const auto c = st.ref(ch);
+            chunk_to_lds<IO>(st.dst(c), pre[u]);
+            if (uint4* ap = st.append_dst(c)) *ap = pre[u];
+        }
     }
-    for (int ch = tid + PRE * nthr; ch < st.nch; ch += nthr) chunk_to_lds<IO>(st.dst(ch), *st.src(ch));
+    for (int ch = tid + PRE * nthr; ch < st.nch; ch += nthr) {
+        const auto c = st.ref(ch);
+        const uint4 v = *st.src(c);
+        chunk_to_lds<IO>(st.dst(c), v);
+        if (uint4* ap = st.append_dst(c)) *ap = v;
+    }
     const int sh = tid >> 5, sj = tid & 31;
     const bool mine = sh < G.ht && sj < G.V;
     if (mine) {
-        G.s0[sh * G.sc_stride + sj] = __builtin_bit_cast(float, sr.s0 << sr.s0shift);
-        if (G.s1) G.s1[sh * G.sc_stride + sj] = __builtin_bit_cast(float, sr.s1);
+        const float v0 = __builtin_bit_cast(float, sr.s0 << sr.s0shift), v1 = __builtin_bit_cast(float, sr.s1);
+        G.s0[sh * G.sc_stride + sj] = v0;
+        if (G.s1) G.s1[sh * G.sc_stride + sj] = v1;
+        if (G.head_writer && sj >= max(G.f, G.len)) {      // append (buffered scalars are fp32)
+            const size_t slot = (size_t)G.bank_new * G.bank_s + (G.hc + sh) * G.cap + (sj - G.f);
+            const_cast<float*>(G.bufs0)[slot] = v0;
+            if (G.bufs1) const_cast<float*>(G.bufs1)[slot] = v1;
+        }
     }
     // entries are at most 32 (cap + T): one head's prefix sums per half wave (a
     // 32-lane scan runs in lanes 0..31 and, independently, in lanes 32..63)
@@ -202,46 +254,6 @@ __device__ __forceinline__ void stage_publish(const Stager<IO, R>& st, int tid, 
         const float v = mine ? __builtin_bit_cast(float, sr.s0 << sr.s0shift) : 0.f;
         const float ps = scan32_inclusive(v);
         if (mine) G.p0[sh * G.sc_stride + sj] = ps;
-    }
-}
-
-// Append the unfolded new entries [j0, V) to the buffer bank `bank_new` at
-// slot (position - f): each workgroup writes its own column slice of the
-// per-head vectors; scalars come from the first slice, per-group vectors from
-// the first slice of the first head of the group.
-template <int IO, int R>
-__device__ __forceinline__ void stage_append(const StageGeom& G, void* bufc, void* bufr, float* bufs0, float* bufs1,
-                                             int bank_new, int f, int tid, int nthr, bool head_writer,
-                                             bool group_writer)
-{
-    using S = Stager<IO, R>;
-    const int j0 = max(f, G.len);
-    const int nnew = G.V - j0;
-    if (nnew <= 0) return;
-    const int CX = G.cw / S::EPC;
-    for (int hh = 0; hh < G.ht; ++hh) {
-        char* bx = static_cast<char*>(bufc) + ((size_t)bank_new * G.bank_c + (G.hc + hh) * G.cap * G.C + G.c0) * S::ES;
-        for (int r = tid; r < nnew * CX; r += nthr) {
-            const int jj = div_small(r, G.m20_cx), o = r - jj * CX, j = j0 + jj;
-            reinterpret_cast<uint4*>(bx + (size_t)(j - f) * G.C * S::ES)[o] =
-                lds_to_chunk<IO>(G.xc + hh * G.xc_stride + j * G.cw + o * S::EPC);
-        }
-    }
-    if (head_writer) {
-        for (int hh = 0; hh < G.ht; ++hh) {
-            for (int jj = tid; jj < nnew; jj += nthr) {
-                const size_t slot = (size_t)bank_new * G.bank_s + (G.hc + hh) * G.cap + (j0 + jj - f);
-                bufs0[slot] = G.s0[hh * G.sc_stride + j0 + jj];
-                if (bufs1) bufs1[slot] = G.s1[hh * G.sc_stride + j0 + jj];
-            }
-        }
-    }
-    if (group_writer) {
-        char* bb = static_cast<char*>(bufr) + ((size_t)bank_new * G.bank_r + G.gr * G.cap * R) * S::ES;
-        for (int i = tid; i < nnew * S::RX; i += nthr) {
-            const int jj = i / S::RX, o = i - jj * S::RX, j = j0 + jj;
-            reinterpret_cast<uint4*>(bb + (size_t)(j - f) * R * S::ES)[o] = lds_to_chunk<IO>(G.xr + j * S::RS + o * S::EPC);
-        }
     }
 }
 
