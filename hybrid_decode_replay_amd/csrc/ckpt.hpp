@@ -20,7 +20,6 @@
 namespace rs {
 
 typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4 h4_to_f32(u32x2 u) {
     return __builtin_convertvector(__builtin_bit_cast(h16x4, u), f32x4);

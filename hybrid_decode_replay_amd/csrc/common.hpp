@@ -21,6 +21,7 @@ namespace rs {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---- scalar conversions -------------------------------------------------
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t v) {

@@ -98,6 +98,106 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
     ScalarRaw sr;
     stage_issue<IO, R, PRE, true>(stg, tid, nthr, pre, sr);
 
+    // ---- 3. publish the staged rows; the three x rows after the last entry are
+    // zeroed, so a replay pass of four entries may read past the last one (with a
+    // zero coefficient) without touching stale values
+    auto publish = [&]() {
+        stage_publish<IO, R, PRE>(stg, tid, nthr, pre, sr);
+        for (int i = tid; i < HT * 3 * (XS / 4); i += nthr) {
+            const int hh = i / (3 * (XS / 4)), r = i - hh * (3 * (XS / 4));
+            st4(xs + (size_t)hh * vx * XS + (size_t)(p.V + r / (XS / 4)) * XS + 4 * (r % (XS / 4)), f32x4{0.f, 0.f, 0.f, 0.f});
+        }
+        __syncthreads();
+    };
+
+    // B_j . C for the decode token: per group, so formed once for every head of the
+    // workgroup (lane quad jj holds entry f + jj; one token has at most 16 unfolded
+    // entries).  Several tokens form theirs per head below.
+    auto token_dots = [&]() {
+        float d = 0.f;
+        const int nr = len - f + 1;
+        if (a.mode != MODE_FLUSH && nr > 0) {
+            const int jj = lane >> 2, j = f + jj, q = lane & 3;
+            if (jj < nr) {
+#pragma unroll
+                for (int i = 0; i < R / 16; ++i)
+                    d += dot4(ld4(bs + j * RS + 16 * i + 4 * q), ld4(cs + 16 * i + 4 * q));
+            }
+            d = quad_sum(d);
+        }
+        return d;
+    };
+
+    // Replay of the unfolded entries f..pos for one token (TMAX == 1): lane quad jj
+    // forms entry f + jj's decayed coefficient into this wave's LDS row; every lane
+    // then reads them four at a time (broadcast) against its column of the x rows
+    // (fixed row stride: immediate offsets, no index math).  Returns the replay sum;
+    // gdec receives the decay of the checkpoint term.
+    auto replay1 = [&](const float* psh, const float* dsh, const float* xsh, float Ah, int pos, float dot1,
+                       float& gdec) {
+        float rep = 0.f;
+        const int nr = pos - f + 1;
+        const int jj = lane >> 2;
+        float* cfw = cf + 16 * w;
+        if ((lane & 3) == 0) {
+            float c = 0.f;
+            if (jj < nr) c = fexp((psh[pos] - psh[f + jj]) * Ah) * dsh[f + jj] * dot1;
+            cfw[jj] = c;
+        }
+        wave_lds_sync();
+        const float* xb = xsh + (size_t)f * XS + lc;
+#pragma unroll
+        for (int e4 = 0; e4 < 16; e4 += 4) {
+            if (e4 < nr) {
+                const f32x4 c4 = ld4(cfw + e4);
+                rep += c4.x * xb[(e4 + 0) * XS] + c4.y * xb[(e4 + 1) * XS] + c4.z * xb[(e4 + 2) * XS] +
+                       c4.w * xb[(e4 + 3) * XS];
+            }
+        }
+        // the row is written again for the next head
+        wave_lds_sync();
+        gdec = fexp((psh[pos] - (f > 0 ? psh[f - 1] : 0.f)) * Ah);
+        return rep;
+    };
+
+    // ---- 2'. a decode step that folds nothing and reads a read copy (FP8 or MXFP4
+    // words) keeps every head's strip in flight at once: the words stay compact
+    // until they are consumed by the read-out, so the loads of all HT heads fit the
+    // register budget (2 KiB or less per head and wave would otherwise leave too few
+    // bytes in flight to cover the memory latency).  Measured on the batch-256
+    // layer: fp32 checkpoint with an FP8 copy 0.114 -> 0.100 ms per step, FP8
+    // checkpoint with an MXFP4 copy 0.098 -> 0.082 ms; an FP8 checkpoint without a
+    // copy gains nothing over the prefetching path below and keeps it.
+    constexpr bool COMPACT = TMAX == 1 && HT > 1 && RC != RC_NONE;
+    if constexpr (COMPACT) {
+        if (a.mode == MODE_DECODE && f == 0) {
+            constexpr int FMT = RC == RC_MXFP4 ? 1 : 0;
+            const uint8_t* words = a.rcopy;
+            uint32_t raw[HT][NB];
+#pragma unroll
+            for (int hh = 0; hh < HT; ++hh)
+                raw_issue<NB, FMT>(words, a.rscale, (size_t)(b * a.H + h0 + hh) * (C >> 4) + (c0 >> 4) + w, lane,
+                                   raw[hh]);
+            publish();
+            const float dot1 = token_dots();
+#pragma unroll
+            for (int hh = 0; hh < HT; ++hh) {
+                const int h = h0 + hh;
+                const float* xsh = xs + (size_t)hh * vx * XS;
+                const float Ah = a.A[h];
+                float gdec;
+                const float rep = replay1(ps + hh * VM, ds + hh * VM, xsh, Ah, len, dot1, gdec);
+                f32x4 cvec[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) cvec[nb] = ld4(cs + nb * 16 + rq);
+                const float gacc = sum_over_row_groups(raw_dot<NB, FMT>(raw[hh], cvec));
+                const float yv = gdec * gacc + rep + a.D[h] * xsh[len * XS + lc];
+                if (lane < 16) st_io<IO>(a.y, ((size_t)b * a.H + h) * C + col, yv);
+            }
+            return;
+        }
+    }
+
     // ---- 2. checkpoint strip loads (128-bit, ckpt.hpp), decoded where first used;
     // a step that folds nothing reads the low-precision copy when there is one
     bool from_copy = false;
@@ -110,45 +210,29 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
             ckpt_issue<NB, CK>(a.ckpt, strip, lane, dst);
         }
     };
-    f32x4 sbuf[HT > 1 ? 2 : 1][NB];
+    // next head's strip in flight during the current head's arithmetic, except in
+    // the kernels with the compact path: there this path only serves folding and
+    // flush steps, and a single buffer keeps it within the register budget
+    constexpr bool PREFETCH = HT > 1 && !COMPACT;
+    f32x4 sbuf[PREFETCH ? 2 : 1][NB];
     issue(0, sbuf[0]);
 
-    // ---- 3. publish the staged rows; the three x rows after the last entry are
-    // zeroed, so a replay pass of four entries may read past the last one (with a
-    // zero coefficient) without touching stale values
-    stage_publish<IO, R, PRE>(stg, tid, nthr, pre, sr);
-    for (int i = tid; i < HT * 3 * (XS / 4); i += nthr) {
-        const int hh = i / (3 * (XS / 4)), r = i - hh * (3 * (XS / 4));
-        st4(xs + (size_t)hh * vx * XS + (size_t)(p.V + r / (XS / 4)) * XS + 4 * (r % (XS / 4)), f32x4{0.f, 0.f, 0.f, 0.f});
-    }
-    __syncthreads();
+    publish();
     // An fp16 checkpoint without a copy is decoded as soon as it is needed at all:
     // the shorter register life of the raw words keeps the kernel at more waves per
     // SIMD, which beats overlapping the replay terms with the loads.
     constexpr bool EARLY_DECODE = CK == CK_F16 && RC == RC_NONE;
 
-    // B_j . C for the decode token: per group, so formed once for every head of the
-    // workgroup (lane quad jj holds entry f + jj; one token has at most 16 unfolded
-    // entries).  Several tokens form theirs per head below.
     float dot1 = 0.f;
-    if constexpr (TMAX == 1) {
-        const int nr = len - f + 1;
-        if (a.mode != MODE_FLUSH && nr > 0) {
-            const int jj = lane >> 2, j = f + jj, q = lane & 3;
-            if (jj < nr) {
-#pragma unroll
-                for (int i = 0; i < R / 16; ++i)
-                    dot1 += dot4(ld4(bs + j * RS + 16 * i + 4 * q), ld4(cs + 16 * i + 4 * q));
-            }
-            dot1 = quad_sum(dot1);
-        }
-    }
+    if constexpr (TMAX == 1) dot1 = token_dots();
 
 #pragma unroll
     for (int hh = 0; hh < HT; ++hh) {
-        f32x4 (&s)[NB] = sbuf[hh & (HT > 1 ? 1 : 0)];
-        if constexpr (HT > 1) {
+        f32x4 (&s)[NB] = sbuf[hh & (PREFETCH ? 1 : 0)];
+        if constexpr (PREFETCH) {
             if (hh + 1 < HT) issue(hh + 1, sbuf[(hh + 1) & 1]);
+        } else if constexpr (HT > 1) {
+            if (hh > 0) issue(hh, s);
         }
         const int h = h0 + hh;
         const size_t strip_index = (size_t)(b * a.H + h) * (C >> 4) + (c0 >> 4) + w;
@@ -227,31 +311,7 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
                     // the decayed coefficient; output lanes gather the coefficients by readlane.
                     float rep = 0.f, gdec = 1.f;
                     if (TMAX == 1 && pos >= f) {
-                        // one token: at most 16 unfolded entries.  Lane quad jj forms entry
-                        // f + jj's decayed coefficient into this wave's LDS row; every lane
-                        // then reads them four at a time (broadcast) against its column of
-                        // the x rows (fixed row stride: immediate offsets, no index math).
-                        const int nr = pos - f + 1;
-                        const int jj = lane >> 2;
-                        float* cfw = cf + 16 * w;
-                        if ((lane & 3) == 0) {
-                            float c = 0.f;
-                            if (jj < nr) c = fexp((psh[pos] - psh[f + jj]) * Ah) * dsh[f + jj] * dot1;
-                            cfw[jj] = c;
-                        }
-                        wave_lds_sync();
-                        const float* xb = xsh + (size_t)f * XS + lc;
-#pragma unroll
-                        for (int e4 = 0; e4 < 16; e4 += 4) {
-                            if (e4 < nr) {
-                                const f32x4 c4 = ld4(cfw + e4);
-                                rep += c4.x * xb[(e4 + 0) * XS] + c4.y * xb[(e4 + 1) * XS] +
-                                       c4.z * xb[(e4 + 2) * XS] + c4.w * xb[(e4 + 3) * XS];
-                            }
-                        }
-                        // the row is read again by the next head's pass
-                        wave_lds_sync();
-                        gdec = fexp((psh[pos] - (f > 0 ? psh[f - 1] : 0.f)) * Ah);
+                        rep = replay1(psh, dsh, xsh, Ah, pos, dot1, gdec);
                     } else if (pos >= f) {
                         const int nr = pos - f + 1;
                         const int q = lane & 3;

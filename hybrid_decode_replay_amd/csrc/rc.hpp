@@ -164,9 +164,20 @@ __device__ __forceinline__ void rc_fp4_issue(const uint8_t* codes, const uint8_t
         for (int p = 0; p < NP; ++p)
             w[p] = *reinterpret_cast<const uint32_t*>(codes + rc_offset<BPL>(strip_index, 0, lane) + 4 * p);
     }
+    // the NP scale bytes of the lane's column are contiguous: one load
     const uint8_t* scp = scales + (strip_index * 16 + (lane & 15)) * NP;
+    if constexpr (NP == 4) {
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(scp);
 #pragma unroll
-    for (int p = 0; p < NP; ++p) sc[p] = scp[p];
+        for (int p = 0; p < NP; ++p) sc[p] = (v >> (8 * p)) & 0xffu;
+    } else if constexpr (NP == 8) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(scp);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) sc[p] = ((p < 4 ? v.x : v.y) >> (8 * (p & 3))) & 0xffu;
+    } else {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) sc[p] = scp[p];
+    }
 }
 
 template <int NB>
@@ -348,6 +359,55 @@ __device__ __forceinline__ float rc_dot(const f32x4 (&s)[NB], const f32x4 (&c)[N
             const auto b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.f, 1);
             const auto b2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.f, 2);
             const auto b3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.f, 3);
+            const float g = b0[0] * c[2 * p].x + b0[1] * c[2 * p].y + b1[0] * c[2 * p].z + b1[1] * c[2 * p].w +
+                            b2[0] * c[2 * p + 1].x + b2[1] * c[2 * p + 1].y + b3[0] * c[2 * p + 1].z +
+                            b3[1] * c[2 * p + 1].w;
+            acc += scale * g;
+        }
+    }
+    return acc;
+}
+
+// A strip's low-precision words as loaded, kept compact (no decoded registers):
+// FMT 0 the NB FP8 words (an FP8 read copy, or an FP8 checkpoint, which uses the
+// same layout); FMT 1 the NB/2 MXFP4 code words followed by their NB/2 scales.
+template <int NB, int FMT>
+__device__ __forceinline__ void raw_issue(const uint8_t* codes, const uint8_t* scales, size_t strip_index, int lane,
+                                          uint32_t (&w)[NB])
+{
+    if constexpr (FMT == 0) {
+        rc_fp8_issue<NB>(codes, strip_index, lane, w);
+    } else {
+        uint32_t c[NB / 2], sc[NB / 2];
+        rc_fp4_issue<NB>(codes, scales, strip_index, lane, c, sc);
+#pragma unroll
+        for (int p = 0; p < NB / 2; ++p) {
+            w[p] = c[p];
+            w[NB / 2 + p] = sc[p];
+        }
+    }
+}
+
+// sum over nb of (strip block nb) . c[nb] from compact words (rc_dot's arithmetic)
+template <int NB, int FMT>
+__device__ __forceinline__ float raw_dot(const uint32_t (&w)[NB], const f32x4 (&c)[NB])
+{
+    float acc = 0.f;
+    if constexpr (FMT == 0) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[nb], false);
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[nb], true);
+            acc += lo[0] * c[nb].x + lo[1] * c[nb].y + hi[0] * c[nb].z + hi[1] * c[nb].w;
+        }
+    } else {
+#pragma unroll
+        for (int p = 0; p < NB / 2; ++p) {
+            const float scale = e8m0_to_f32(w[NB / 2 + p]);
+            const auto b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[p], 1.f, 0);
+            const auto b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[p], 1.f, 1);
+            const auto b2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[p], 1.f, 2);
+            const auto b3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[p], 1.f, 3);
             const float g = b0[0] * c[2 * p].x + b0[1] * c[2 * p].y + b1[0] * c[2 * p].z + b1[1] * c[2 * p].w +
                             b2[0] * c[2 * p + 1].x + b2[1] * c[2 * p + 1].y + b3[0] * c[2 * p + 1].z +
                             b3[1] * c[2 * p + 1].w;
