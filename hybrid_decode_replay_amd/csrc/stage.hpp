@@ -275,14 +275,25 @@ struct StepPlan {
     bool skip;
 };
 
-__device__ __forceinline__ StepPlan plan_step(const StepArgs& a, int b, bool writer)
+// The current bookkeeping words of sequence b (len, fc, lim).
+struct BookWords {
+    int len, fc, lim;
+};
+
+__device__ __forceinline__ BookWords book_words(const StepArgs& a, int b)
 {
     const size_t sB = (size_t)a.B;
     const int32_t* bk = a.book + (size_t)a.parity * 4 * sB;
+    return BookWords{bk[b], bk[2 * sB + b], bk[3 * sB + b]};
+}
+
+__device__ __forceinline__ StepPlan plan_from(const StepArgs& a, int b, BookWords bw, bool writer)
+{
+    const size_t sB = (size_t)a.B;
     StepPlan p;
-    p.len = min(max(bk[b], 0), a.cap);   // invariant 0 <= len <= cap; clamped so that a
-    p.fc = bk[2 * sB + b];               // corrupted word cannot index out of bounds
-    const int lim = min(max(bk[3 * sB + b], 1), a.cap);
+    p.len = min(max(bw.len, 0), a.cap);  // invariant 0 <= len <= cap; clamped so that a
+    p.fc = bw.fc;                        // corrupted word cannot index out of bounds
+    const int lim = min(max(bw.lim, 1), a.cap);
     p.skip = a.active != nullptr && a.mode != MODE_FLUSH && a.active[b] == 0;
     if (p.skip) {
         if (writer) {
@@ -324,6 +335,11 @@ __device__ __forceinline__ StepPlan plan_step(const StepArgs& a, int b, bool wri
         nbk[3 * sB + b] = folds ? a.cap : lim;
     }
     return p;
+}
+
+__device__ __forceinline__ StepPlan plan_step(const StepArgs& a, int b, bool writer)
+{
+    return plan_from(a, b, book_words(a, b), writer);
 }
 
 }  // namespace rs

@@ -357,9 +357,13 @@ class _Session:
             return S
         return read_copy_values(S, self.read_copy).reshape(S.shape)
 
-    def _flush_rows(self, rows):
+    def _flush_rows(self, rows, rounded=True):
+        """Fold the buffered entries of the sequences `rows` into their checkpoints.
+        rounded=False leaves the state unrounded: the caller folds more entries in the
+        same pass and rounds once at its end."""
         for b in np.flatnonzero(rows):
-            self.S[b] = self._round(self.S[b:b + 1])[0]
+            if rounded:
+                self.S[b] = self._round(self.S[b:b + 1])[0]
             self.ckpt[b] = self.S[b]
             self.fc[b] += 1
             self.len[b] = 0
@@ -406,7 +410,12 @@ class _Session:
             raise PhaseError("decode while drafts are pending")
         act = self._mask(active)
         forced = act & (self.len + 1 > self.cap)
-        self._flush_rows(forced)
+        # A full buffer is folded before the token is appended.  With a one-entry
+        # buffer the token then fills the buffer again and is folded in the same step:
+        # the two folds are one pass over both entries, so a low-precision checkpoint
+        # is rounded once, after both (reading of the library's one-entry buffer; the
+        # pages fix the buffer at 16 entries).
+        self._flush_rows(forced, rounded=self.cap > 1)
         y = self._token(self.S, inp, act.astype(np.uint8))
         self.len += act.astype(np.int32)
         full = act & (self.len >= self.lim)

@@ -689,6 +689,22 @@ def test_full_buffer_decode_at_capacity_one():
     np.testing.assert_array_equal(sess.fc - fc0, [2, 1])
 
 
+def test_capacity_one_double_fold_rounds_once():
+    """cap = 1 with a committed draft: the decode folds the draft and the token in one pass,
+    so an FP8 checkpoint is rounded once.  A = 0, dt = x = 1 (each fold adds B): from 1 the
+    two entries add 1/16 each; one rounding gives 1 + 1/8 = 1.125 (on the grid), where
+    rounding after each fold would give round(1.0625) = 1 (tie to even), then again 1."""
+    S0 = np.ones((1, 1, 1, 1))
+    sess = ro.Mamba2Session(np.zeros(1), np.zeros(1), S0, cap=1, ckpt_dtype="fp8")
+    tok = {"x": np.ones((1, 1, 1)), "Bm": np.full((1, 1, 1), 1 / 16), "Cm": np.ones((1, 1, 1)),
+           "dt": np.ones((1, 1))}
+    sess.spec_append([tok])
+    sess.commit([1])
+    y = sess.decode(tok)
+    assert sess.ckpt.ravel()[0] == 1.125
+    assert y.ravel()[0] == 1.125 and sess.fc[0] == 2
+
+
 # --------------------------------------------------------------------------
 # FP8 (E4M3) recurrence checkpoint
 # --------------------------------------------------------------------------
