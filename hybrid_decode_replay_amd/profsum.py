@@ -5,7 +5,7 @@ Usage (after the rocprofv3 runs whose commands are passed in, for the record):
     python -m hybrid_decode_replay_amd.profsum traffic FETCH_DIR WRITE_DIR OUT.txt KERNEL GRID \\
         "FETCH_SIZE COMMAND" "WRITE_SIZE COMMAND"
 KERNEL is a name with template arguments as rocprofv3 prints them (one instantiation,
-e.g. "mamba2_step_kernel<8, 1, 1, true, 0, 0>") or a bare name (all instantiations).
+e.g. "mamba2_step_kernel<8, 1, 1, true, 0, 0, 1>") or a bare name (all instantiations).
 
 trace    per (kernel, grid size) call counts and durations from *_kernel_trace.csv of a
          `rocprofv3 --kernel-trace` run (one row per workload of the program).
@@ -282,15 +282,19 @@ def sweep(jsonl, out, command):
              "* **graph** -- 64 back-to-back steps captured in one HIP graph, replayed 8 times (GPU time per step,",
              "  no host launch overhead); the same for the conventional kernel.",
              "* **eager** -- 64 steps launched one by one from Python, back to back between two events (both",
-             "  kernels); the non-flush and flush columns come from a second pass with an event pair per launch.", "",
+             "  kernels); the non-flush and flush columns come from a second pass with an event pair per launch.",
+             "  Consecutive launches cycle through `rotate` copies of the layer state, so that they stream at",
+             "  least 512 MiB of distinct state (more than the 256 MiB Infinity Cache holds); the GB/s column is",
+             "  from these.  The graph timings use one state: at small batch it can stay in the Infinity Cache.", "",
              "| layer | batch | graph replay ms | graph conv ms | graph speedup | eager replay ms | eager conv ms "
-             "| replay non-flush ms | replay flush ms | replay GB/s (algorithmic, per launch) |",
-             "|---|---|---|---|---|---|---|---|---|---|"]
+             "| replay non-flush ms | replay flush ms | rotate | replay GB/s (algorithmic, whole windows) |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
         g = r["graph"]
         lines.append(f"| {r['kind']} | {r['batch']} | {g['replay_ms_per_step']:.4f} | {g['conventional_ms_per_step']:.4f} "
                      f"| {g['speedup_vs_conventional']:.3f} | {r['ms_per_step']:.4f} | {r['conventional']['ms_per_step']:.4f} "
-                     f"| {r['nonflush_step_ms']:.4f} | {r['flush_step_ms']:.4f} | {r['achieved_gbs']:.0f} |")
+                     f"| {r['nonflush_step_ms']:.4f} | {r['flush_step_ms']:.4f} | {r.get('rotate', 1)} "
+                     f"| {r['achieved_gbs']:.0f} |")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(out, len(rows), "points")
