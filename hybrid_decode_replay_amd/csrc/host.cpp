@@ -1034,8 +1034,8 @@ replay_status replay_standin_linear(const void* X, const void* W, void* Y, int32
     if ((s = check_ptr(X, "X")) != REPLAY_OK) return s;
     if ((s = check_ptr(W, "W")) != REPLAY_OK) return s;
     if ((s = check_ptr(Y, "Y")) != REPLAY_OK) return s;
-    if (M < 1 || K < 128 || K % 128 != 0 || N < 32 || N % 32 != 0)
-        return fail(REPLAY_ERR_SHAPE, "linear needs M >= 1, K a multiple of 128 and N a multiple of 32 (M %d, K %d, N %d)",
+    if (M < 1 || K < 64 || K % 64 != 0 || N < 1)
+        return fail(REPLAY_ERR_SHAPE, "linear needs M >= 1, K a positive multiple of 64 and N >= 1 (M %d, K %d, N %d)",
                     M, K, N);
     if ((long long)(M + 63) / 64 > 65535) return fail(REPLAY_ERR_SHAPE, "M %d too large", M);
     return LAUNCH(rs::launch_standin_linear(X, W, Y, M, K, N, (hipStream_t)stream), "stand-in linear");

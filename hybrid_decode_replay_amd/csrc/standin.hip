@@ -28,101 +28,136 @@ __device__ __forceinline__ f32x4 mfma16x16x32bf16(bf16x8 a, bf16x8 b, f32x4 c)
 }
 
 // ---- linear ------------------------------------------------------------------
-// Workgroup: four waves and an output tile of 64 rows x 32 columns (four 16-row
-// by two 16-column MFMA blocks).  The waves split K: wave w takes the 128-wide
-// k chunks w, w+4, w+8, ..., so every weight is read by one wave only, and the
-// four partial tiles are summed through LDS at the end.  Operand layout of the
-// 16x16x32 MFMA: A lane l holds row l%16, k = 8(l/16)..+7; B lane l holds column
-// l%16, the same k; the 16x16 result has rows 4(l/16)..+3 of column l%16.  A
-// chunk takes four 16-byte loads per operand block per lane; the next chunk's
-// loads are issued before the current one is multiplied (two register sets).
-// Rows past M read row M-1 and are not stored.
-struct LinChunk {
-    bf16x8 a[4][4], b[4][2];
-};
+// Workgroup: four waves in a 2 x 2 arrangement and an output tile of TM rows x 64
+// columns (TM = 128 or 64); wave (wr, wc) owns TM/2 rows and 32 columns, i.e. BI x 2
+// MFMA blocks of 16 x 16 (BI = TM / 32).  K advances in chunks of 64: the chunk's X
+// rows (TM x 64) and W rows (64 x 64) are copied to LDS once (coalesced 16-byte
+// loads) and every wave reads its operands from there, so each X value is fetched
+// from L2 once per workgroup and each weight once.  Two chunks are in flight
+// while one is multiplied: chunk c+2's global loads are issued into the register
+// set chunk c came through, and chunk c+1 (already in registers) is written to the
+// other LDS buffer after chunk c's products; one barrier per chunk.  TM = 64 is
+// taken when 128-row tiles would leave fewer than 512 workgroups (few output
+// columns or a long K per workgroup).  Operand layout of the 16x16x32 MFMA: A lane
+// l holds row l%16, k = 8(l/16)..+7; B lane l holds column l%16, the same k; the
+// 16x16 result has rows 4(l/16)..+3 of column l%16.  LDS rows are 72 bf16 long
+// (64 + 8 of padding), so the 16 rows a fragment read touches start 36 banks
+// apart.  Rows past M and columns past N read row M-1 / column N-1 and are not
+// stored.
+constexpr int LIN_TN = 64, LIN_KC = 64, LIN_PITCH = 72;
 
-__device__ __forceinline__ void lin_load(LinChunk& c, const uint16_t* const (&xrow)[4], const uint16_t* const (&wrow)[2],
-                                         int k0)
-{
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            c.b[u][j] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(
-                                                       reinterpret_cast<const u32x4*>(wrow[j] + k0 + 32 * u)));
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            c.a[u][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xrow[i] + k0 + 32 * u));
-    }
-}
-
-__device__ __forceinline__ void lin_mma(const LinChunk& c, f32x4 (&acc)[4][2])
-{
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = mfma16x16x32bf16(c.a[u][i], c.b[u][j], acc[i][j]);
-}
-
+template <int TM>
 __global__ __launch_bounds__(256) void standin_linear_kernel(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M,
                                                              int K, int N)
 {
-    __shared__ f32x4 red[3][4][2][64];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int n0 = blockIdx.x * 32, m0 = blockIdx.y * 64;
+    constexpr int BI = TM / 32;                 // row blocks per wave
+    constexpr int XU = TM * 8 / 256;            // 16-byte X pieces per thread and chunk
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][TM * LIN_PITCH];
+    __shared__ __attribute__((aligned(16))) uint16_t wsh[2][LIN_TN * LIN_PITCH];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wr = w >> 1, wc = w & 1;
+    const int n0 = blockIdx.x * LIN_TN, m0 = blockIdx.y * TM;
     const int lr = lane & 15, kq = 8 * (lane >> 4);
-    const uint16_t* xrow[4];
+
+    // X piece c = tid + 256 u: row c / 8, 16-byte piece c % 8; W piece likewise by column
+    const uint16_t* xsrc[XU];
+    int xdst[XU];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xrow[i] = X + (size_t)min(m0 + 16 * i + lr, M - 1) * K + kq;
-    const uint16_t* wrow[2];
+    for (int u = 0; u < XU; ++u) {
+        const int c = tid + 256 * u, row = c >> 3, pc = c & 7;
+        xsrc[u] = X + (size_t)min(m0 + row, M - 1) * K + 8 * pc;
+        xdst[u] = row * LIN_PITCH + 8 * pc;
+    }
+    const uint16_t* wsrc[2];
+    int wdst[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) wrow[j] = W + (size_t)(n0 + 16 * j + lr) * K + kq;
-    f32x4 acc[4][2];
+    for (int u = 0; u < 2; ++u) {
+        const int c = tid + 256 * u, col = c >> 3, pc = c & 7;
+        wsrc[u] = W + (size_t)min(n0 + col, N - 1) * K + 8 * pc;
+        wdst[u] = col * LIN_PITCH + 8 * pc;
+    }
+    struct Regs {
+        u32x4 x[XU], w[2];
+    };
+    Regs r0, r1;
+    auto load_chunk = [&](Regs& r, int kc) {
+        const int k0 = kc * LIN_KC;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int u = 0; u < XU; ++u) r.x[u] = *reinterpret_cast<const u32x4*>(xsrc[u] + k0);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) r.w[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[u] + k0));
+    };
+    auto store_chunk = [&](const Regs& r, int buf) {
+#pragma unroll
+        for (int u = 0; u < XU; ++u) *reinterpret_cast<u32x4*>(&xs[buf][xdst[u]]) = r.x[u];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) *reinterpret_cast<u32x4*>(&wsh[buf][wdst[u]]) = r.w[u];
+    };
+
+    f32x4 acc[BI][2];
+#pragma unroll
+    for (int i = 0; i < BI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int nch = K / 128;
-    LinChunk c0, c1;
-    int c = w;
-    if (c < nch) lin_load(c0, xrow, wrow, 128 * c);
-    while (c < nch) {
-        if (c + 4 < nch) lin_load(c1, xrow, wrow, 128 * (c + 4));
-        lin_mma(c0, acc);
-        c += 4;
-        if (c >= nch) break;
-        if (c + 4 < nch) lin_load(c0, xrow, wrow, 128 * (c + 4));
-        lin_mma(c1, acc);
-        c += 4;
-    }
-    if (w > 0) {
+    auto multiply = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int ks = 0; ks < LIN_KC / 32; ++ks) {
+            bf16x8 a[BI], bb[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) red[w - 1][i][j][lane] = acc[i][j];
-    }
+            for (int i = 0; i < BI; ++i)
+                a[i] = *reinterpret_cast<const bf16x8*>(
+                    &xs[buf][((TM / 2) * wr + 16 * i + lr) * LIN_PITCH + 32 * ks + kq]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                bb[j] = *reinterpret_cast<const bf16x8*>(&wsh[buf][(32 * wc + 16 * j + lr) * LIN_PITCH + 32 * ks + kq]);
+#pragma unroll
+            for (int i = 0; i < BI; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j] = mfma16x16x32bf16(a[i], bb[j], acc[i][j]);
+        }
+    };
+
+    // chunk c comes through register set c % 2 and LDS buffer c % 2
+    const int nk = K / LIN_KC;
+    load_chunk(r0, 0);
+    if (nk > 1) load_chunk(r1, 1);
+    store_chunk(r0, 0);
     __syncthreads();
-    if (w != 0) return;
+    for (int kc = 0; kc < nk; kc += 2) {
+        if (kc + 2 < nk) load_chunk(r0, kc + 2);
+        multiply(0);
+        if (kc + 1 < nk) store_chunk(r1, 1);
+        __syncthreads();
+        if (kc + 1 >= nk) break;
+        if (kc + 3 < nk) load_chunk(r1, kc + 3);
+        multiply(1);
+        if (kc + 2 < nk) store_chunk(r0, 0);
+        __syncthreads();
+    }
+
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < BI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const f32x4 v = acc[i][j] + red[0][i][j][lane] + red[1][i][j][lane] + red[2][i][j][lane];
+            const int col = n0 + 32 * wc + 16 * j + lr;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = m0 + 16 * i + 4 * (lane >> 4) + r;
-                if (row < M) Y[(size_t)row * N + n0 + 16 * j + lr] = f32_to_bf16_bits(v[r]);
+                const int row = m0 + (TM / 2) * wr + 16 * i + 4 * (lane >> 4) + r;
+                if (row < M && col < N) Y[(size_t)row * N + col] = f32_to_bf16_bits(acc[i][j][r]);
             }
         }
 }
 
 hipError_t launch_standin_linear(const void* X, const void* W, void* Y, int M, int K, int N, hipStream_t s)
 {
-    hipLaunchKernelGGL(standin_linear_kernel, dim3(N / 32, (M + 63) / 64), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(W), static_cast<uint16_t*>(Y), M,
-                       K, N);
+    const auto x = static_cast<const uint16_t*>(X);
+    const auto w = static_cast<const uint16_t*>(W);
+    const auto y = static_cast<uint16_t*>(Y);
+    const int cols = (N + LIN_TN - 1) / LIN_TN;
+    if ((long long)cols * ((M + 127) / 128) >= 512)
+        hipLaunchKernelGGL(standin_linear_kernel<128>, dim3(cols, (M + 127) / 128), dim3(256), 0, s, x, w, y, M, K, N);
+    else
+        hipLaunchKernelGGL(standin_linear_kernel<64>, dim3(cols, (M + 63) / 64), dim3(256), 0, s, x, w, y, M, K, N);
     return hipGetLastError();
 }
 

@@ -379,7 +379,7 @@ replay_status replay_conv_spec_restore(const replay_config *cfg, void *S, const 
  * Both are plain definitions (no buffer or checkpoint): */
 /* Y[m][n] = sum_k X[m][k] W[n][k]: X [M][K], W [N][K] (one output feature's
  * weights contiguous), Y [M][N]; all bf16, row-major, fp32 accumulation, Y
- * rounded to nearest even.  Needs K a multiple of 128 and N a multiple of 32
+ * rounded to nearest even.  Needs K a positive multiple of 64 and M, N >= 1
  * (else REPLAY_ERR_SHAPE). */
 replay_status replay_standin_linear(const void *X, const void *W, void *Y, int32_t M, int32_t K, int32_t N,
                                     void *stream);

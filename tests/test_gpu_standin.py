@@ -38,7 +38,8 @@ def _err(got, ref):
     return ro.normwise_error(got, ref)
 
 
-@pytest.mark.parametrize("M,K,N", [(1, 128, 32), (37, 384, 96), (256, 1024, 256), (300, 512, 64), (256, 4096, 160)])
+@pytest.mark.parametrize("M,K,N", [(1, 128, 32), (37, 384, 96), (256, 1024, 256), (300, 512, 64), (256, 4096, 160),
+                                   (129, 64, 40), (5, 192, 1), (256, 8192, 200)])
 def test_linear(M, K, N):
     from hybrid_decode_replay_amd import binding as b
     from oracle import standin_oracle as so
@@ -57,7 +58,7 @@ def test_linear_rejects_bad_shapes():
     with pytest.raises(b.ReplayError) as e:
         b.standin_linear(X, W)
     assert e.value.status == b.ERR_SHAPE
-    X, W = _bf16((4, 128), 1).cuda(), _bf16((40, 128), 2).cuda()
+    X, W = _bf16((4, 96), 1).cuda(), _bf16((40, 96), 2).cuda()
     with pytest.raises(b.ReplayError) as e:
         b.standin_linear(X, W)
     assert e.value.status == b.ERR_SHAPE
