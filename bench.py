@@ -36,6 +36,16 @@ The JSON line also carries:
                 at the shapes above, batch 256) through one layer stack, with
                 lockstep and staggered flush phases, against the conventional
                 kernel per layer
+  standin_kernels_b256
+                per-launch time and algorithmic bandwidth of the stand-in
+                non-SSM kernels (bf16 projections on MFMA, decode attention over
+                a bf16 KV cache) at a model step's shapes
+  hybrid_model_step_b256
+                a synthetic hybrid decode step: the four SSM layers above
+                interleaved with stand-in projections and attention (and
+                optionally MLP projections), attention context 1024 or 4096;
+                replay vs conventional SSM layers with identical stand-ins, the
+                stand-ins' share of the step and the SSM speedup it implies
   flush_mfma    (in each layer report) the fold's MFMA flops per flush step and
                 their rate over the measured flush-step time, against the
                 fp32 MFMA peak (157.3 TFLOP/s)
@@ -568,7 +578,9 @@ def time_model_step(rb, synth, torch, dev, stream, B, context, mlp, K=32, W=8, d
     att_o = torch.empty((B, a["Hq"], a["D"]), dtype=torch.bfloat16, device=dev)
     X2 = torch.empty_like(X)
     up = torch.empty((B, 2 * d_ff), dtype=torch.bfloat16, device=dev) if mlp else None
-    act = torch.empty((B, d_ff), dtype=torch.bfloat16, device=dev) if mlp else None   # gated activation
+    # the down projection's input stands for the gated activation of `up`; the elementwise
+    # gate itself (B x d_ff bf16, ~1 % of an MLP's bytes) is not computed in either run
+    act = torch.randn((B, d_ff), generator=g, device=dev).to(torch.bfloat16) if mlp else None
     ys = [torch.empty((1, L.B, L.H, L.C), dtype=torch.bfloat16, device=dev) for L in ssm]
     lib, sp = rb.lib(), rb.ctypes.c_void_p(stream.cuda_stream)
     states = [rb.ReplayState(L.cfg, device=dev) for L in ssm]
