@@ -214,14 +214,15 @@ replay_status check_inputs(const replay_config* c, const replay_inputs* in, bool
 // and the sequence's bookkeeping, and a workgroup that serves several of them
 // streams one head's checkpoint while it computes the previous head's outputs.
 // Used with four waves per workgroup when the group size allows it.
-// An fp32 checkpoint without a read copy streams enough bytes per head that six
-// single-head workgroups per SIMD hide the fixed work better (measured: 0.182 vs
-// 0.192 ms per step on the batch-256 layer); the lighter streams gain from the
-// shared staging (FP8 checkpoint 0.115 -> 0.097 ms).
+// An fp32 or fp16 checkpoint without a read copy streams enough bytes per head
+// that six single-head workgroups per SIMD hide the fixed work better (measured
+// on the batch-256 layer: fp32 0.182 vs 0.192 ms per step, fp16 0.108 vs
+// 0.110 ms); the lighter streams gain from the shared staging (FP8 checkpoint
+// 0.091 -> 0.077 ms, read copies 0.10-0.29 -> 0.07-0.11 ms).
 int mamba2_heads_per_wg(const replay_config* c, int wpg)
 {
     if (c->kind != REPLAY_MAMBA2 || wpg != 4) return 1;
-    if (c->ckpt_dtype == REPLAY_F32 && c->read_copy == REPLAY_NONE) return 1;
+    if (c->ckpt_dtype != REPLAY_FP8_E4M3 && c->read_copy == REPLAY_NONE) return 1;
     return (c->nheads / c->ngroups) % 4 == 0 ? 4 : 1;
 }
 

@@ -97,6 +97,15 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
     uint4 pre[PRE];
     ScalarRaw sr;
     stage_issue<IO, R, PRE, true>(stg, tid, nthr, pre, sr);
+    // the heads' A and D, fetched before the checkpoint loads: vector loads complete
+    // in issue order, so a value fetched after them could only be used once every
+    // one of them had landed
+    float Av[HT], Dv[HT];
+#pragma unroll
+    for (int hh = 0; hh < HT; ++hh) {
+        Av[hh] = a.A[h0 + hh];
+        Dv[hh] = a.D[h0 + hh];
+    }
 
     // ---- 3. publish the staged rows; the three x rows after the last entry are
     // zeroed, so a replay pass of four entries may read past the last one (with a
@@ -170,7 +179,7 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
     // copy gains nothing over the prefetching path below and keeps it.
     constexpr bool COMPACT = TMAX == 1 && HT > 1 && RC != RC_NONE;
     if constexpr (COMPACT) {
-        if (a.mode == MODE_DECODE && f == 0) {
+        if (a.mode != MODE_FLUSH && f == 0) {
             constexpr int FMT = RC == RC_MXFP4 ? 1 : 0;
             const uint8_t* words = a.rcopy;
             uint32_t raw[HT][NB];
@@ -184,14 +193,14 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
             for (int hh = 0; hh < HT; ++hh) {
                 const int h = h0 + hh;
                 const float* xsh = xs + (size_t)hh * vx * XS;
-                const float Ah = a.A[h];
+                const float Ah = Av[hh];
                 float gdec;
                 const float rep = replay1(ps + hh * VM, ds + hh * VM, xsh, Ah, len, dot1, gdec);
                 f32x4 cvec[NB];
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) cvec[nb] = ld4(cs + nb * 16 + rq);
                 const float gacc = sum_over_row_groups(raw_dot<NB, FMT>(raw[hh], cvec));
-                const float yv = gdec * gacc + rep + a.D[h] * xsh[len * XS + lc];
+                const float yv = gdec * gacc + rep + Dv[hh] * xsh[len * XS + lc];
                 if (lane < 16) st_io<IO>(a.y, ((size_t)b * a.H + h) * C + col, yv);
             }
             return;
@@ -199,9 +208,11 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
     }
 
     // ---- 2. checkpoint strip loads (128-bit, ckpt.hpp), decoded where first used;
-    // a step that folds nothing reads the low-precision copy when there is one
+    // a step that folds nothing reads the low-precision copy when there is one (in
+    // the kernels with the compact path every such step took that path, and a flush
+    // that folds nothing has returned: here f > 0)
     bool from_copy = false;
-    if constexpr (RC != RC_NONE) from_copy = (f == 0);
+    if constexpr (RC != RC_NONE && !COMPACT) from_copy = (f == 0);
     auto issue = [&](int hh, f32x4 (&dst)[NB]) {
         const size_t strip = (size_t)(b * a.H + h0 + hh) * (C >> 4) + (c0 >> 4) + w;
         if (from_copy) {
@@ -241,7 +252,7 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
         const float* xsh = xs + (size_t)hh * vx * XS;
         if constexpr (EARLY_DECODE) ckpt_decode<NB, CK>(s);
 
-        const float Ah = a.A[h];
+        const float Ah = Av[hh];
 
         // ---- 4. fold the first f entries into the checkpoint registers
         // sums of dt over an entry range come from the prefix sums: sum_{lo<=i<hi} = ps[hi-1] - ps[lo-1]
@@ -298,9 +309,17 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
             if (a.qckpt && f > 0) rc_roundtrip<NB, RC>(s, a.mxceil);
         }
 
-        // ---- 5. outputs of the new tokens
+        // ---- 5. single checkpoint write on a folding step (before the outputs, which
+        // only read the folded values: the encoders' temporaries are dead by the time
+        // the read-out rows are loaded)
+        if (f > 0) {
+            ckpt_store<NB, CK>(a.ckpt, strip_index, lane, s);
+            if constexpr (RC != RC_NONE) rc_store<NB, RC>(a.rcopy, a.rscale, strip_index, lane, s, a.mxceil);
+        }
+
+        // ---- 6. outputs of the new tokens
         if (a.mode != MODE_FLUSH) {
-            const float Dh = a.D[h];
+            const float Dh = Dv[hh];
 #pragma unroll
             for (int t = 0; t < TMAX; ++t) {
                 if (t < T) {
@@ -374,11 +393,6 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
             }
         }
 
-        // ---- 6. single checkpoint write on a folding step
-        if (f > 0) {
-            ckpt_store<NB, CK>(a.ckpt, strip_index, lane, s);
-            if constexpr (RC != RC_NONE) rc_store<NB, RC>(a.rcopy, a.rscale, strip_index, lane, s, a.mxceil);
-        }
     }
 }
 
