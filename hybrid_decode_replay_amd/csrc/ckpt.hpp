@@ -156,6 +156,25 @@ __device__ __forceinline__ float ckpt_dot(const f32x4 (&s)[NB], const f32x4 (&c)
     return acc;
 }
 
+// Block jb of a strip as fp32, from the words ckpt_issue left in the registers
+// (fp32 as loaded): lets a fold read the checkpoint twice without keeping a
+// decoded copy of the strip.
+template <int NB, int CK>
+__device__ __forceinline__ f32x4 ckpt_block(const f32x4 (&s)[NB], int jb)
+{
+    if constexpr (CK == CK_FP8) {
+        const uint32_t w = __builtin_bit_cast(uint32_t, s[jb].x);
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+        return f32x4{lo[0], lo[1], hi[0], hi[1]};
+    } else if constexpr (CK == CK_F16) {
+        const u32x4 w = __builtin_bit_cast(u32x4, s[NB == 1 ? 0 : jb & ~1]);
+        return (jb & 1) ? h4_to_f32(u32x2{w.z, w.w}) : h4_to_f32(u32x2{w.x, w.y});
+    } else {
+        return s[jb];
+    }
+}
+
 // Registers -> the values the store will keep (identity for fp32).
 template <int NB, int CK>
 __device__ __forceinline__ void ckpt_round(f32x4 (&s)[NB])

@@ -54,6 +54,12 @@ __device__ __forceinline__ int lane_id_here()
     return l;
 }
 
+// Compile-time flag passed to the kernel's generic lambdas.
+template <bool B>
+struct BoolTag {
+    static constexpr bool value = B;
+};
+
 template <int NB, int IO, int TMAX, int RC, int CK, int SPW>
 __global__ __launch_bounds__(256, SPW == 1 ? (NB <= 8 ? 6 : 4) : 4) void gdn_step_kernel(StepArgs a)
 {
@@ -125,24 +131,18 @@ __global__ __launch_bounds__(256, SPW == 1 ? (NB <= 8 ? 6 : 4) : 4) void gdn_ste
     stage_publish<IO, R, PRE>(stg, tid, nthr, pre, sr);
     __syncthreads();
 
-    // ---- 3. fold the first f entries (WY form on MFMA)
-    if (f > 0) {
+    // ---- 3. fold of the first f entries (WY form on MFMA), in two parts.
+    // fold_front: wave 0 forms the gate products and (I + A)^{-1}; every wave forms
+    // W = K S0^T for its strips; one workgroup barrier.  fold_strip: strip j's
+    // S' = P S0 + K^T U~ into `out`.  S0 is read as the registers hold it: decoded
+    // fp32 (DEC), or the loaded words decoded block by block (fp16/FP8), so a fold
+    // needs no decoded copy of the strips besides its result.
+    auto s0_block = [&](auto dec, int j, int jb) -> f32x4 {
+        if constexpr (decltype(dec)::value) return s[j][jb];
+        else return ckpt_block<NB, CK>(s[j], jb);
+    };
+    auto fold_front = [&](auto dec, f32x4 (&W)[SPW]) {
         const bool arow = l16 < f;
-        f32x4 W[SPW];
-#pragma unroll
-        for (int j = 0; j < SPW; ++j) {
-            ckpt_decode<NB, CK>(s[j]);
-            // W[i][v] = (S0 k_i)[v]; lane result rows i = lq*4 + r, column lc0 + 16 j
-            W[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int jb = 0; jb < NB; ++jb) {
-                const f32x4 kv = arow ? ld4(ks + l16 * RS + jb * 16 + rq) : f32x4{0.f, 0.f, 0.f, 0.f};
-                W[j] = mfma16x16x4(kv.x, s[j][jb].x, W[j]);
-                W[j] = mfma16x16x4(kv.y, s[j][jb].y, W[j]);
-                W[j] = mfma16x16x4(kv.z, s[j][jb].z, W[j]);
-                W[j] = mfma16x16x4(kv.w, s[j][jb].w, W[j]);
-            }
-        }
         if (w == 0) {
             // gate products tt[j][i] = alpha_{j+1} ... alpha_i (1 for i <= j), i, j < f:
             // lane j multiplies along i, every product formed as a product
@@ -188,50 +188,62 @@ __global__ __launch_bounds__(256, SPW == 1 ? (NB <= 8 ? 6 : 4) : 4) void gdn_ste
                 for (int i = 0; i < 16; ++i) ti[i * 17 + lane] = tc[i];
             }
         }
-        __syncthreads();
-
-        const float decay = al[0] * tt[f - 1];                       // P_{f-1}
 #pragma unroll
         for (int j = 0; j < SPW; ++j) {
-            // rhs[i][v] = beta_i (v_i[v] - P_i W[i][v]) for i < f
-            f32x4 rhs;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = lq * 4 + r;
-                float v = 0.f;
-                if (i < f) v = be[i] * (vs[i * cw + 16 * (SPW * w + j) + (lane_id_here() & 15)] - (al[0] * tt[i]) * W[j][r]);
-                rhs[r] = v;
-            }
-            // U = (I + A)^{-1} rhs, then scaled by the decay from entry i to the end of the fold
-            f32x4 U = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) U = mfma16x16x4(ti[l16 * 17 + lq * 4 + r], rhs[r], U);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = lq * 4 + r;
-                U[r] = (i < f) ? tt[i * 17 + f - 1] * U[r] : 0.f;         // alpha_{i+1} ... alpha_{f-1}
-            }
-            // S'^T[jk][v] = decay S0^T[jk][v] + sum_i K[i][jk] U~[i][v]
+            // W[i][v] = (S0 k_i)[v]; lane result rows i = lq*4 + r, column lc0 + 16 j
+            W[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int jb = 0; jb < NB; ++jb) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = lq * 4 + r;
-                    const float kv = (i < f) ? ks[i * RS + jb * 16 + l16] : 0.f;
-                    acc = mfma16x16x4(kv, U[r], acc);
-                }
-                s[j][jb] = decay * s[j][jb] + acc;
-            }
-            // the folded state takes the checkpoint's storage precision at once (fp16:
-            // RNE), so this step's outputs and the read copy see the stored values
-            ckpt_round<NB, CK>(s[j]);
-            // a checkpoint kept at the copy's precision is rounded as soon as it is folded
-            if constexpr (RC != RC_NONE) {
-                if (a.qckpt) rc_roundtrip<NB, RC>(s[j], a.mxceil);
+                const f32x4 kv = arow ? ld4(ks + l16 * RS + jb * 16 + rq) : f32x4{0.f, 0.f, 0.f, 0.f};
+                const f32x4 sv = s0_block(dec, j, jb);
+                W[j] = mfma16x16x4(kv.x, sv.x, W[j]);
+                W[j] = mfma16x16x4(kv.y, sv.y, W[j]);
+                W[j] = mfma16x16x4(kv.z, sv.z, W[j]);
+                W[j] = mfma16x16x4(kv.w, sv.w, W[j]);
             }
         }
-    }
+        __syncthreads();
+    };
+    auto fold_strip = [&](auto dec, int j, const f32x4& Wj, f32x4 (&out)[NB]) {
+        const float decay = al[0] * tt[f - 1];                       // P_{f-1}
+        // rhs[i][v] = beta_i (v_i[v] - P_i W[i][v]) for i < f
+        f32x4 rhs;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = lq * 4 + r;
+            float v = 0.f;
+            if (i < f) v = be[i] * (vs[i * cw + 16 * (SPW * w + j) + (lane_id_here() & 15)] - (al[0] * tt[i]) * Wj[r]);
+            rhs[r] = v;
+        }
+        // U = (I + A)^{-1} rhs, then scaled by the decay from entry i to the end of the fold
+        f32x4 U = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) U = mfma16x16x4(ti[l16 * 17 + lq * 4 + r], rhs[r], U);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = lq * 4 + r;
+            U[r] = (i < f) ? tt[i * 17 + f - 1] * U[r] : 0.f;         // alpha_{i+1} ... alpha_{f-1}
+        }
+        // S'^T[jk][v] = decay S0^T[jk][v] + sum_i K[i][jk] U~[i][v]
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = lq * 4 + r;
+                const float kv = (i < f) ? ks[i * RS + jb * 16 + l16] : 0.f;
+                acc = mfma16x16x4(kv, U[r], acc);
+            }
+            out[jb] = decay * s0_block(dec, j, jb) + acc;
+        }
+        // the folded state takes the checkpoint's storage precision at once (fp16:
+        // RNE), so this step's outputs and the read copy see the stored values
+        ckpt_round<NB, CK>(out);
+        // a checkpoint kept at the copy's precision is rounded as soon as it is folded
+        if constexpr (RC != RC_NONE) {
+            if (a.qckpt) rc_roundtrip<NB, RC>(out, a.mxceil);
+        }
+    };
 
     // ---- 4./5. adjoint chains and outputs.  A chain runs on one row of 16 lanes:
     // lane j of the row holds elements EL*j .. EL*j+EL-1 of r (EL = d_k / 16), so
@@ -239,16 +251,21 @@ __global__ __launch_bounds__(256, SPW == 1 ? (NB <= 8 ? 6 : 4) : 4) void gdn_ste
     // The gates are kept out of the vector update: with r = sig * rr and sig the
     // product of the gates of the entries already passed, c_i = sig beta_i (k_i . rr)
     // and rr <- rr - beta_i (k_i . rr) k_i, then sig <- alpha_i sig; r_0 = sig rr.
-    if (a.mode != MODE_FLUSH) {
-        const int rho = lane >> 4, j16 = lane & 15;
-        if constexpr (TMAX == 1) {
-            // one token: every row of every wave runs the chain itself (no workgroup
-            // barrier) and keeps the replay sums sum_i c_i v_i of its lanes' columns
+    const int rho = lane >> 4, j16 = lane & 15;
+    if constexpr (TMAX == 1) {
+        // One token.  Its chain needs only the published entries, so it runs first,
+        // while the checkpoint loads land: every row of every wave runs it (no
+        // workgroup barrier) and keeps the replay sums sum_i c_i v_i of its lanes'
+        // columns; r_0 goes to a wave-private LDS row.  Then each strip is folded
+        // (if this step folds), stored and read out in turn.
+        float rep[SPW];
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) rep[j] = 0.f;
+        float* rw = rz + (size_t)w * R;
+        if (a.mode != MODE_FLUSH) {
             float r[EL];
             lds_row_load<EL>(qs + EL * j16, r);
-            float rep[SPW], sig = 1.f;
-#pragma unroll
-            for (int j = 0; j < SPW; ++j) rep[j] = 0.f;
+            float sig = 1.f;
             const float* vcol = vs + lc0;
             for (int i = len; i >= f; --i) {
                 float kv[EL];
@@ -267,39 +284,62 @@ __global__ __launch_bounds__(256, SPW == 1 ? (NB <= 8 ? 6 : 4) : 4) void gdn_ste
 #pragma unroll
             for (int m = 0; m < EL; ++m) r[m] *= sig;
             // r_0 of this wave (every row holds the same values) -> wave-private LDS row
-            float* rw = rz + (size_t)w * R;
             if (rho == 0) lds_row_store<EL>(rw + EL * j16, r);
             wave_lds_sync();
+        }
+        auto emit = [&](int j, float gacc) {
+            gacc = sum_over_row_groups(gacc);
+            if (lane < 16) st_io<IO>(a.y, ((size_t)b * a.H + h) * C + c0 + lc0 + 16 * j, a.scale * (gacc + rep[j]));
+        };
+        if (f > 0) {
+            f32x4 W[SPW];
+            fold_front(BoolTag<false>{}, W);
 #pragma unroll
             for (int j = 0; j < SPW; ++j) {
-                float gacc = 0.f;
-                if constexpr (SPW == 1) {
-                    f32x4 rv[NB];                 // r_0 as the lanes' checkpoint rows need it
+                auto finish = [&](f32x4 (&sn)[NB]) {
+                    // single checkpoint write, then the read-out of the stored values
+                    ckpt_store<NB, CK>(a.ckpt, strip0 + j, lane, sn);
+                    if constexpr (RC != RC_NONE) rc_store<NB, RC>(a.rcopy, a.rscale, strip0 + j, lane, sn, a.mxceil);
+                    if (a.mode != MODE_FLUSH) {
+                        float gacc = 0.f;
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) rv[nb] = ld4(rw + nb * 16 + rq);
-                    // raw words that were not folded go straight into the dot product
-                    if (f == 0) {
-                        gacc = from_copy ? rc_dot<NB, RC>(s[j], rv) : ckpt_dot<NB, CK>(s[j], rv);
-                    } else {
-#pragma unroll
-                        for (int nb = 0; nb < NB; ++nb) gacc += dot4(s[j][nb], rv[nb]);
+                        for (int nb = 0; nb < NB; ++nb) gacc += dot4(sn[nb], ld4(rw + nb * 16 + rq));
+                        emit(j, gacc);
                     }
+                };
+                if constexpr (CK == CK_F32) {
+                    fold_strip(BoolTag<true>{}, j, W[j], s[j]);      // in place: block jb is read before written
+                    finish(s[j]);
                 } else {
-                    // two strips: decoding in place keeps the register count within four
-                    // waves per SIMD
-                    if (f == 0) {
-                        if (from_copy) rc_decode<NB, RC>(s[j]);
-                        else ckpt_decode<NB, CK>(s[j]);
-                    }
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) gacc += dot4(s[j][nb], ld4(rw + nb * 16 + rq));
+                    f32x4 sn[NB];
+                    fold_strip(BoolTag<false>{}, j, W[j], sn);
+                    finish(sn);
                 }
-                gacc = sum_over_row_groups(gacc);
-                if (lane < 16) st_io<IO>(a.y, ((size_t)b * a.H + h) * C + c0 + lc0 + 16 * j, a.scale * (gacc + rep[j]));
             }
-        } else {
-            // several tokens: one chain per (wave, row) pair; coefficients and r_0 go
-            // through LDS to the output lanes
+        } else if (a.mode != MODE_FLUSH) {
+            // raw words that were not folded go straight into the dot product
+#pragma unroll
+            for (int j = 0; j < SPW; ++j) {
+                f32x4 rv[NB];                 // r_0 as the lanes' checkpoint rows need it
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) rv[nb] = ld4(rw + nb * 16 + rq);
+                emit(j, from_copy ? rc_dot<NB, RC>(s[j], rv) : ckpt_dot<NB, CK>(s[j], rv));
+            }
+        }
+    } else {
+        // Several tokens: the strips are decoded once, folded in place, read out by
+        // every token, then stored.
+        if (f > 0) {
+#pragma unroll
+            for (int j = 0; j < SPW; ++j) ckpt_decode<NB, CK>(s[j]);
+            f32x4 W[SPW];
+            fold_front(BoolTag<true>{}, W);
+#pragma unroll
+            for (int j = 0; j < SPW; ++j) fold_strip(BoolTag<true>{}, j, W[j], s[j]);
+        }
+        if (a.mode != MODE_FLUSH) {
+            // one chain per (wave, row) pair; coefficients and r_0 go through LDS to
+            // the output lanes
             for (int t = w * 4 + rho; t < T; t += waves * 4) {
                 const int pos = len + t;
                 float r[EL];
@@ -347,14 +387,14 @@ __global__ __launch_bounds__(256, SPW == 1 ? (NB <= 8 ? 6 : 4) : 4) void gdn_ste
                 }
             }
         }
-    }
 
-    // ---- 6. single checkpoint write on a folding step
-    if (f > 0) {
+        // ---- 6. single checkpoint write on a folding step
+        if (f > 0) {
 #pragma unroll
-        for (int j = 0; j < SPW; ++j) {
-            ckpt_store<NB, CK>(a.ckpt, strip0 + j, lane, s[j]);
-            if constexpr (RC != RC_NONE) rc_store<NB, RC>(a.rcopy, a.rscale, strip0 + j, lane, s[j], a.mxceil);
+            for (int j = 0; j < SPW; ++j) {
+                ckpt_store<NB, CK>(a.ckpt, strip0 + j, lane, s[j]);
+                if constexpr (RC != RC_NONE) rc_store<NB, RC>(a.rcopy, a.rscale, strip0 + j, lane, s[j], a.mxceil);
+            }
         }
     }
 }
