@@ -44,6 +44,18 @@ __device__ __forceinline__ float fexp(float x) {
 // register (index arithmetic on it then runs on the scalar unit).
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Read of a value no workgroup of the launch writes, at a wave-uniform address,
+// through the constant address space: the compiler emits a scalar load, whose
+// completion is counted apart from the vector loads, so waiting for it never
+// waits for checkpoint loads issued before or after it.  (Reads only; data
+// written by an earlier launch is visible, the scalar cache being invalidated
+// at every dispatch.)
+template <typename T>
+__device__ __forceinline__ T uload(const T* p)
+{
+    return *(const __attribute__((address_space(4))) T*)p;
+}
+
 template <int IO>
 __device__ __forceinline__ float ld_io(const void* p, size_t i) {
     if constexpr (IO == IO_F32) return static_cast<const float*>(p)[i];

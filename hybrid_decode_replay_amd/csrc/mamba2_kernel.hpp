@@ -67,6 +67,15 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
     const int rq = 4 * (lane >> 4);
     const size_t sB = (size_t)a.B;
 
+    // ---- the heads' A and D by scalar loads (a vector load issued after the
+    // checkpoint loads could only be used once every one of them had landed)
+    float Av[HT], Dv[HT];
+#pragma unroll
+    for (int hh = 0; hh < HT; ++hh) {
+        Av[hh] = uload(a.A + h0 + hh);
+        Dv[hh] = uload(a.D + h0 + hh);
+    }
+
     // ---- bookkeeping: identical decision in every workgroup of sequence b
     const StepPlan p = plan_step(a, b, h0 == 0 && tix.sp == 0 && tid == 0);
     if (p.skip || (a.mode == MODE_FLUSH && p.f == 0)) return;
@@ -97,15 +106,6 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
     uint4 pre[PRE];
     ScalarRaw sr;
     stage_issue<IO, R, PRE, true>(stg, tid, nthr, pre, sr);
-    // the heads' A and D, fetched before the checkpoint loads: vector loads complete
-    // in issue order, so a value fetched after them could only be used once every
-    // one of them had landed
-    float Av[HT], Dv[HT];
-#pragma unroll
-    for (int hh = 0; hh < HT; ++hh) {
-        Av[hh] = a.A[h0 + hh];
-        Dv[hh] = a.D[h0 + hh];
-    }
 
     // ---- 3. publish the staged rows; the three x rows after the last entry are
     // zeroed, so a replay pass of four entries may read past the last one (with a

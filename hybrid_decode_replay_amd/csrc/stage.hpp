@@ -280,21 +280,46 @@ struct BookWords {
     int len, fc, lim;
 };
 
+// The words a step's plan depends on: the sequence's bookkeeping (the copy this
+// launch reads; the launch writes only the other) and its active flag.  Scalar
+// loads (uload): a kernel may issue its checkpoint loads before it waits for them.
+struct PlanInputs {
+    BookWords bw;
+    bool active;
+};
+
 __device__ __forceinline__ BookWords book_words(const StepArgs& a, int b)
 {
     const size_t sB = (size_t)a.B;
     const int32_t* bk = a.book + (size_t)a.parity * 4 * sB;
-    return BookWords{bk[b], bk[2 * sB + b], bk[3 * sB + b]};
+    return BookWords{uload(bk + b), uload(bk + 2 * sB + b), uload(bk + 3 * sB + b)};
 }
 
-__device__ __forceinline__ StepPlan plan_from(const StepArgs& a, int b, BookWords bw, bool writer)
+__device__ __forceinline__ PlanInputs plan_inputs(const StepArgs& a, int b)
+{
+    PlanInputs q;
+    q.bw = book_words(a, b);
+    q.active = true;
+    if (a.active != nullptr && a.mode != MODE_FLUSH) {
+        // the aligned 32-bit word holding the flag byte: a scalar load reads whole
+        // words, and an aligned word never spans two pages, so the bytes of it past
+        // the end of the mask cannot fault (they are not used)
+        const uintptr_t at = reinterpret_cast<uintptr_t>(a.active) + (uintptr_t)b;
+        const uint32_t word = uload(reinterpret_cast<const uint32_t*>(at & ~(uintptr_t)3));
+        q.active = ((word >> (8 * (at & 3))) & 0xffu) != 0;
+    }
+    return q;
+}
+
+__device__ __forceinline__ StepPlan plan_from(const StepArgs& a, int b, PlanInputs in, bool writer)
 {
     const size_t sB = (size_t)a.B;
+    const BookWords bw = in.bw;
     StepPlan p;
     p.len = min(max(bw.len, 0), a.cap);  // invariant 0 <= len <= cap; clamped so that a
     p.fc = bw.fc;                        // corrupted word cannot index out of bounds
     const int lim = min(max(bw.lim, 1), a.cap);
-    p.skip = a.active != nullptr && a.mode != MODE_FLUSH && a.active[b] == 0;
+    p.skip = !in.active;
     if (p.skip) {
         if (writer) {
             int32_t* nbk = a.book + (size_t)(a.parity ^ 1) * 4 * sB;
@@ -339,7 +364,7 @@ __device__ __forceinline__ StepPlan plan_from(const StepArgs& a, int b, BookWord
 
 __device__ __forceinline__ StepPlan plan_step(const StepArgs& a, int b, bool writer)
 {
-    return plan_from(a, b, book_words(a, b), writer);
+    return plan_from(a, b, plan_inputs(a, b), writer);
 }
 
 }  // namespace rs
