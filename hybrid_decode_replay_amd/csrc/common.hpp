@@ -22,6 +22,7 @@ namespace rs {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // ---- scalar conversions -------------------------------------------------
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t v) {
@@ -257,6 +258,25 @@ __device__ __forceinline__ T* strip_block(T* ck, size_t first, int blk, int lane
 
 __device__ __forceinline__ f32x4 mfma16x16x4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// 16x16x32 bf16 product, fp32 accumulation.  Operands: lane l holds row (A) or
+// column (B) l%16 and eight k values; A and B lanes of one lane group must hold
+// the same k values in the same order (which eight is the caller's choice: the
+// sum over k does not depend on it).  Result: rows 4(l/16)..+3 of column l%16.
+__device__ __forceinline__ f32x4 mfma16x16x32bf16(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Eight fp32 values that are bf16 numbers (bf16 inputs widened, E4M3 values) as
+// bf16: the upper half of each is its bf16 code, so the conversion is exact.
+__device__ __forceinline__ bf16x8 bf16x8_exact(f32x4 lo, f32x4 hi)
+{
+    const u32x4 l = __builtin_bit_cast(u32x4, lo), h = __builtin_bit_cast(u32x4, hi);
+    const u32x4 w = {(l.x >> 16) | (l.y & 0xffff0000u), (l.z >> 16) | (l.w & 0xffff0000u),
+                     (h.x >> 16) | (h.y & 0xffff0000u), (h.z >> 16) | (h.w & 0xffff0000u)};
+    return __builtin_bit_cast(bf16x8, w);
 }
 
 __device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }

@@ -141,8 +141,21 @@ __global__ __launch_bounds__(256, SPW == 1 ? (NB <= 8 ? 6 : 4) : 4) void gdn_ste
         if constexpr (decltype(dec)::value) return s[j][jb];
         else return ckpt_block<NB, CK>(s[j], jb);
     };
+    // With bf16 io the entry keys are bf16 numbers, and so are the values of an FP8
+    // checkpoint: the Gram matrix (and then W) take the 16x16x32 bf16 product,
+    // exact products summed in fp32 like the fp32 product's.  For key chunk m (32
+    // keys) lane group q holds keys 32m + 4q + 0..3 and 32m + 16 + 4q + 0..3, the
+    // rows of checkpoint blocks 2m and 2m+1 it holds.
+    constexpr bool BFK = IO == IO_BF16 && R % 32 == 0;
+    constexpr bool BFW = BFK && CK == CK_FP8;
     auto fold_front = [&](auto dec, f32x4 (&W)[SPW]) {
         const bool arow = l16 < f;
+        // key chunk m of entry row l16 (zero past the folded entries)
+        auto key_chunk = [&](int m) {
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            return bf16x8_exact(arow ? ld4(ks + l16 * RS + 32 * m + rq) : z,
+                                arow ? ld4(ks + l16 * RS + 32 * m + 16 + rq) : z);
+        };
         if (w == 0) {
             // gate products tt[j][i] = alpha_{j+1} ... alpha_i (1 for i <= j), i, j < f:
             // lane j multiplies along i, every product formed as a product
@@ -156,10 +169,18 @@ __global__ __launch_bounds__(256, SPW == 1 ? (NB <= 8 ? 6 : 4) : 4) void gdn_ste
             }
             // Gram k_i . k_j on MFMA (lane result rows i = lq*4 + r, column j = l16)
             f32x4 gm = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (BFK) {
 #pragma unroll
-            for (int d = 0; d < R / 4; ++d) {
-                const float kv = arow ? ks[l16 * RS + 4 * d + lq] : 0.f;
-                gm = mfma16x16x4(kv, kv, gm);
+                for (int m = 0; m < R / 32; ++m) {
+                    const bf16x8 km = key_chunk(m);
+                    gm = mfma16x16x32bf16(km, km, gm);
+                }
+            } else {
+#pragma unroll
+                for (int d = 0; d < R / 4; ++d) {
+                    const float kv = arow ? ks[l16 * RS + 4 * d + lq] : 0.f;
+                    gm = mfma16x16x4(kv, kv, gm);
+                }
             }
             wave_lds_sync();
             // strictly lower triangle of A, written to ti as a scratch matrix
@@ -188,18 +209,30 @@ __global__ __launch_bounds__(256, SPW == 1 ? (NB <= 8 ? 6 : 4) : 4) void gdn_ste
                 for (int i = 0; i < 16; ++i) ti[i * 17 + lane] = tc[i];
             }
         }
+        // W[i][v] = (S0 k_i)[v]; lane result rows i = lq*4 + r, column lc0 + 16 j
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) W[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (BFW) {
+#pragma unroll
+            for (int m = 0; m < R / 32; ++m) {
+                const bf16x8 km = key_chunk(m);
+#pragma unroll
+                for (int j = 0; j < SPW; ++j)
+                    W[j] = mfma16x16x32bf16(km, bf16x8_exact(s0_block(dec, j, 2 * m), s0_block(dec, j, 2 * m + 1)), W[j]);
+            }
+        }
 #pragma unroll
         for (int j = 0; j < SPW; ++j) {
-            // W[i][v] = (S0 k_i)[v]; lane result rows i = lq*4 + r, column lc0 + 16 j
-            W[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (!BFW) {
 #pragma unroll
-            for (int jb = 0; jb < NB; ++jb) {
-                const f32x4 kv = arow ? ld4(ks + l16 * RS + jb * 16 + rq) : f32x4{0.f, 0.f, 0.f, 0.f};
-                const f32x4 sv = s0_block(dec, j, jb);
-                W[j] = mfma16x16x4(kv.x, sv.x, W[j]);
-                W[j] = mfma16x16x4(kv.y, sv.y, W[j]);
-                W[j] = mfma16x16x4(kv.z, sv.z, W[j]);
-                W[j] = mfma16x16x4(kv.w, sv.w, W[j]);
+                for (int jb = 0; jb < NB; ++jb) {
+                    const f32x4 kv = arow ? ld4(ks + l16 * RS + jb * 16 + rq) : f32x4{0.f, 0.f, 0.f, 0.f};
+                    const f32x4 sv = s0_block(dec, j, jb);
+                    W[j] = mfma16x16x4(kv.x, sv.x, W[j]);
+                    W[j] = mfma16x16x4(kv.y, sv.y, W[j]);
+                    W[j] = mfma16x16x4(kv.z, sv.z, W[j]);
+                    W[j] = mfma16x16x4(kv.w, sv.w, W[j]);
+                }
             }
         }
         __syncthreads();

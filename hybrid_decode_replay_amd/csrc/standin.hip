@@ -20,13 +20,6 @@
 
 namespace rs {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ f32x4 mfma16x16x32bf16(bf16x8 a, bf16x8 b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
 // ---- linear ------------------------------------------------------------------
 // Workgroup: four waves in a 2 x 2 arrangement and an output tile of TM rows x 64
 // columns (TM = 128 or 64); wave (wr, wc) owns TM/2 rows and 32 columns, i.e. BI x 2
