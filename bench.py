@@ -94,6 +94,40 @@ GDN = dict(H=32, G=32, C=128, R=128)       # heads, q/k heads, d_v, d_k
 ROTATE_MIN_BYTES = 512 << 20
 
 
+def token_sizes(kind, H, G, C, R, io_bytes=2):
+    """Bytes per sequence and token: (buffer entry, inputs read, output written).  Entries:
+    Mamba-2 x, B, dt; GDN k, v and the fp32 gates; inputs add C (q)."""
+    if kind == "mamba2":
+        entry = (H * C + G * R + H) * io_bytes
+        inp = (H * C + 2 * G * R + H) * io_bytes
+    else:
+        entry = (H * C + G * R) * io_bytes + 2 * H * 4
+        inp = (H * C + 2 * G * R) * io_bytes + 2 * H * 4
+    return entry, inp, H * C * io_bytes
+
+
+def spec_bytes(kind, H, G, C, R, cap, k, acc, io_bytes=2, ckpt_bytes=4):
+    """Algorithmic bytes of `len(acc)` speculative rounds of k drafts at accepted counts acc
+    [rounds][B], and the per-sequence (len, folds) the bookkeeping must end with.  A round
+    reads the checkpoint once, the committed entries once (staged for the outputs, or for
+    the fold of the committed prefix when len + k > cap, which also writes the checkpoint),
+    the k drafts' inputs, and writes their entries and outputs."""
+    import numpy as np
+    entry, inp, out = token_sizes(kind, H, G, C, R, io_bytes)
+    S = H * C * R * ckpt_bytes
+    rounds, B = acc.shape
+    lens = np.zeros(B, np.int64)
+    folds = np.zeros(B, np.int64)
+    hist = 0
+    for r in range(rounds):
+        hist += int(lens.sum())
+        f = lens + k > cap
+        folds += f
+        lens = np.where(f, 0, lens) + np.clip(acc[r], 0, k)
+    total = rounds * B * (S + k * (inp + entry + out)) + hist * entry + int(folds.sum()) * S
+    return total, lens, folds
+
+
 def traffic_model(kind, H, G, C, R, cap=16, io_bytes=2, read_copy=None, ckpt_bytes=4):
     """Algorithmic bytes per sequence-token, by part: (replay, conventional) dicts.
 
@@ -107,13 +141,7 @@ def traffic_model(kind, H, G, C, R, cap=16, io_bytes=2, read_copy=None, ckpt_byt
     ckpt_bytes per element."""
     n = H * C * R
     S = n * ckpt_bytes
-    if kind == "mamba2":
-        entry = (H * C + G * R + H) * io_bytes
-        inp = (H * C + 2 * G * R + H) * io_bytes
-    else:
-        entry = (H * C + G * R) * io_bytes + 2 * H * 4
-        inp = (H * C + 2 * G * R) * io_bytes + 2 * H * 4
-    out = H * C * io_bytes
+    entry, inp, out = token_sizes(kind, H, G, C, R, io_bytes)
     ckpt = S + S / cap
     if read_copy is not None:
         copy = n if read_copy == "fp8" else n / 2 + n / 32
@@ -750,6 +778,24 @@ def time_spec(L, rounds, k, stream, seed=3):
     ins = [L.inputs(r * k, k) for r in range(rounds)]
     y = torch.empty((k, L.B, L.H, L.C), dtype=torch.bfloat16, device=L.dev)
     yp = rb.ctypes.c_void_p(y.data_ptr())
+    # untimed warm-up rounds of both schemes on throwaway states, so the timed rounds start
+    # warm; the timed replay rounds then start from a fresh load
+    warm = min(16, rounds)
+    st = rb.ReplayState(L.cfg, device=L.dev)
+    st.load_checkpoint(L.S0)
+    Sw = L.S0.clone()
+    snw = torch.empty((k,) + tuple(Sw.shape), dtype=torch.float32, device=L.dev)
+    for r in range(warm):
+        s = lib.replay_spec_append(st.h, k, rb.ctypes.byref(ins[r]), yp, sp)
+        s |= lib.replay_spec_commit(st.h, rb.ctypes.c_void_p(acc[r].data_ptr()), sp)
+        s |= lib.replay_conv_spec_step(rb.ctypes.byref(L.cfg), rb.ctypes.c_void_p(Sw.data_ptr()),
+                                       rb.ctypes.c_void_p(snw.data_ptr()), k, rb.ctypes.byref(ins[r]), yp, sp)
+        s |= lib.replay_conv_spec_restore(rb.ctypes.byref(L.cfg), rb.ctypes.c_void_p(Sw.data_ptr()),
+                                          rb.ctypes.c_void_p(snw.data_ptr()), k, rb.ctypes.c_void_p(acc[r].data_ptr()), sp)
+        if s != rb.OK:
+            raise rb.ReplayError(s, "spec warm-up round")
+    torch.cuda.synchronize()
+    del st, Sw, snw
     st = rb.ReplayState(L.cfg, device=L.dev)
     st.load_checkpoint(L.S0)
     torch.cuda.synchronize()
@@ -763,6 +809,13 @@ def time_spec(L, rounds, k, stream, seed=3):
     e1.record(stream)
     torch.cuda.synchronize()
     replay_ms = e0.elapsed_time(e1) / rounds
+    # the bytes these rounds move, from the same accepted counts; the bookkeeping the
+    # library ends with must be the one the count assumed
+    nbytes, lens, folds = spec_bytes(L.kind, L.H, L.G, L.C, L.R, L.cap, k, acc_np)
+    ln, _, fc, _ = st.read_book()
+    torch.cuda.synchronize()
+    if not (np.array_equal(ln.cpu().numpy(), lens) and np.array_equal(fc.cpu().numpy(), folds)):
+        raise RuntimeError("spec rounds: bookkeeping differs from the byte count's")
     del st
     S = L.S0.clone()
     snaps = torch.empty((k,) + tuple(S.shape), dtype=torch.float32, device=L.dev)
@@ -781,6 +834,10 @@ def time_spec(L, rounds, k, stream, seed=3):
     accepted = float(acc_np.sum()) / rounds
     return {"batch": L.B, "drafts": k, "rounds": rounds, "mean_accepted": round(accepted / L.B, 4),
             "replay_ms_per_round": round(replay_ms, 5), "conventional_ms_per_round": round(conv_ms, 5),
+            "replay_bytes_per_round_algorithmic": int(nbytes // rounds),
+            "replay_achieved_gbs": round(nbytes / rounds / (replay_ms / 1e3) / 1e9, 1),
+            "replay_frac_of_peak": round(nbytes / rounds / (replay_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "folded_prefixes_per_round": round(float(folds.sum()) / rounds, 2), "untimed_warmup_rounds": warm,
             "replay_accepted_tokens_per_s": round(accepted / (replay_ms / 1e3), 1),
             "conventional_accepted_tokens_per_s": round(accepted / (conv_ms / 1e3), 1),
             "speedup": round(conv_ms / replay_ms, 3)}

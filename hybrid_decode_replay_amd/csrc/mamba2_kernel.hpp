@@ -88,6 +88,7 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
     float* bs = xs + (size_t)HT * vx * XS;        // [vmax][RS]     entry B rows
     float* cs = bs + (size_t)a.vmax * RS;         // [Tr][R]        read-out rows C_t
     float* cf = cs + (size_t)(T > 0 ? T : 1) * R; // [4][16]        per-wave replay coefficients
+    float* gs = cf + 64;                          // [Tr][VM]       B_j . C_t (several tokens)
 
     StageGeom G;
     G.bufc = a.bufc; G.bufr = a.bufr; G.bufs0 = a.bufs0; G.bufs1 = nullptr;
@@ -236,6 +237,29 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
 
     float dot1 = 0.f;
     if constexpr (TMAX == 1) dot1 = token_dots();
+    // Several tokens: the dots B_j . C_t of the unfolded entries j = f .. len + t are
+    // per group, so they are formed once for the workgroup (wave w: tokens w, w +
+    // waves, ...; lane quad jj: entry f + jj) into an LDS table.
+    if constexpr (TMAX > 1) {
+        if (a.mode != MODE_FLUSH) {
+            const int waves = nthr >> 6, q = lane & 3;
+            for (int t = w; t < T; t += waves) {
+                const int nr = len + t - f + 1;
+                for (int jj0 = 0; jj0 < nr; jj0 += 16) {
+                    const int jj = jj0 + (lane >> 2), j = f + jj;
+                    float dot = 0.f;
+                    if (jj < nr) {
+#pragma unroll
+                        for (int i = 0; i < R / 16; ++i)
+                            dot += dot4(ld4(bs + j * RS + 16 * i + 4 * q), ld4(cs + t * R + 16 * i + 4 * q));
+                    }
+                    dot = quad_sum(dot);
+                    if (q == 0 && jj < nr) gs[t * VM + j] = dot;
+                }
+            }
+            __syncthreads();
+        }
+    }
 
 #pragma unroll
     for (int hh = 0; hh < HT; ++hh) {
@@ -317,37 +341,30 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
             if constexpr (RC != RC_NONE) rc_store<NB, RC>(a.rcopy, a.rscale, strip_index, lane, s, a.mxceil);
         }
 
-        // ---- 6. outputs of the new tokens
+        // ---- 6. outputs of the new tokens.  The replay terms of every token come
+        // first: they need only LDS, so they run while the checkpoint loads are in
+        // flight; then the checkpoint read-outs.
         if (a.mode != MODE_FLUSH) {
             const float Dh = Dv[hh];
+            float rep[TMAX], gdec[TMAX];
 #pragma unroll
             for (int t = 0; t < TMAX; ++t) {
-                if (t < T) {
-                    const int pos = len + t;
-                    const float xt = xsh[pos * XS + lc];
-                    // replay of entries f..pos (formed first: it needs only LDS, so it runs while
-                    // the checkpoint loads are in flight).  Lane quad jj = l/4 forms B_j . C_t and
-                    // the decayed coefficient; output lanes gather the coefficients by readlane.
-                    float rep = 0.f, gdec = 1.f;
-                    if (TMAX == 1 && pos >= f) {
-                        rep = replay1(psh, dsh, xsh, Ah, pos, dot1, gdec);
-                    } else if (pos >= f) {
+                rep[t] = 0.f;
+                gdec[t] = 1.f;
+                const int pos = len + t;
+                if (t < T && pos >= f) {
+                    if constexpr (TMAX == 1) {
+                        rep[t] = replay1(psh, dsh, xsh, Ah, pos, dot1, gdec[t]);
+                    } else {
+                        // replay of entries f..pos: lane quad jj = l/4 forms B_j . C_t and the
+                        // decayed coefficient; output lanes gather the coefficients by readlane
                         const int nr = pos - f + 1;
-                        const int q = lane & 3;
                         const float* xcol = xsh + lc;
                         const int pos_u = uni(pos), f_u = uni(f);
+                        float r = 0.f;
                         for (int jj0 = 0; jj0 < nr; jj0 += 16) {
                             const int jj = jj0 + (lane >> 2), j = f + jj;
-                            float dot = dot1;
-                            if constexpr (TMAX > 1) {
-                                if (jj < nr) {
-#pragma unroll
-                                    for (int i = 0; i < R / 16; ++i)
-                                        dot += dot4(ld4(bs + j * RS + 16 * i + 4 * q), ld4(cs + t * R + 16 * i + 4 * q));
-                                }
-                                dot = quad_sum(dot);
-                            }
-                            const float coef = (jj < nr) ? fexp((psh[pos] - psh[j]) * Ah) * dsh[j] * dot : 0.f;
+                            const float coef = (jj < nr) ? fexp((psh[pos] - psh[j]) * Ah) * dsh[j] * gs[t * VM + j] : 0.f;
                             // entries past pos carry a zero coefficient; their row is clamped to a
                             // staged one so the product stays finite (row offsets are scalar)
                             // four entries per pass, passes while entries remain (nr is uniform)
@@ -357,12 +374,20 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
                                 if (e4 < ne) {
 #pragma unroll
                                     for (int e = e4; e < e4 + 4; ++e)
-                                        rep += readlane(coef, 4 * e) * xcol[uni(min(f_u + jj0 + e, pos_u) * XS)];
+                                        r += readlane(coef, 4 * e) * xcol[uni(min(f_u + jj0 + e, pos_u) * XS)];
                                 }
                             }
                         }
-                        gdec = fexp((psh[pos] - (f > 0 ? psh[f - 1] : 0.f)) * Ah);
+                        rep[t] = r;
+                        gdec[t] = fexp((psh[pos] - (f > 0 ? psh[f - 1] : 0.f)) * Ah);
                     }
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < TMAX; ++t) {
+                if (t < T) {
+                    const int pos = len + t;
+                    const float xt = xsh[pos * XS + lc];
                     // checkpoint read-out (S' C_t)[col], reduced over the four row groups; one
                     // token reads raw words that were not folded straight into the dot product
                     float gacc = 0.f;
@@ -387,12 +412,11 @@ __global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2
                         for (int nb = 0; nb < NB; ++nb) gacc += dot4(s[nb], ld4(cs + t * R + nb * 16 + rq));
                     }
                     gacc = sum_over_row_groups(gacc);
-                    const float yv = (pos >= f) ? gdec * gacc + rep + Dh * xt : gacc + Dh * xt;
+                    const float yv = (pos >= f) ? gdec[t] * gacc + rep[t] + Dh * xt : gacc + Dh * xt;
                     if (lane < 16) st_io<IO>(a.y, (((size_t)t * sB + b) * a.H + h) * C + col, yv);
                 }
             }
         }
-
     }
 }
 
@@ -403,7 +427,7 @@ static hipError_t mamba2_launch_ht(const StepArgs& a, hipStream_t s)
     const size_t R = NB * 16;
     const size_t VM = (16 + TMAX + 3) & ~3;
     const size_t lds = sizeof(float) * (HT * ((size_t)a.vmax + 3) * 64 + (size_t)a.vmax * (R + 4) + Tr * R + 64 +
-                                        2 * HT * VM);
+                                        (TMAX > 1 ? Tr * VM : 0) + 2 * HT * VM);
     auto k = mamba2_step_kernel<NB, IO, TMAX, MF, RC, CK, HT>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
