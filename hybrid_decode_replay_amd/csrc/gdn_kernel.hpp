@@ -90,8 +90,9 @@ __global__ __launch_bounds__(256, SPW == 1 ? (NB <= 8 ? 6 : 4) : 4) void gdn_ste
     float* vs = lds;                          // [vmax][cw]  entry v rows (own columns)
     float* ks = vs + (size_t)vmax * cw;       // [vmax][RS]  entry k rows
     float* qs = ks + (size_t)vmax * RS;       // [Tr][R]     query rows
-    float* rz = qs + (size_t)Tr * R;          // [max(Tr,4)][R] chain results r_0 (per token, or per wave)
-    float* al = rz + (size_t)(Tr > 4 ? Tr : 4) * R;   // [vmax] alpha
+    float* rz = qs + (size_t)Tr * R;          // chain results r_0: [4][R] per wave (one token), [4][4][R]
+                                              // per wave and token (up to four), or [Tr][R] per token
+    float* al = rz + (size_t)(TMAX == 1 ? 4 : TMAX <= 4 ? 16 : Tr) * R;   // [vmax] alpha
     float* be = al + vmax;                    // [vmax]      beta
     float* cc = be + vmax;                    // [Tr][vmax]  chain coefficients c_i
     float* ti = cc + (size_t)Tr * vmax;       // [16][17]    (I + A)^{-1}
@@ -359,6 +360,79 @@ __global__ __launch_bounds__(256, SPW == 1 ? (NB <= 8 ? 6 : 4) : 4) void gdn_ste
                 emit(j, from_copy ? rc_dot<NB, RC>(s[j], rv) : ckpt_dot<NB, CK>(s[j], rv));
             }
         }
+    } else if constexpr (TMAX <= 4) {
+        // Up to four tokens: row rho of every wave runs token rho's chain itself (no
+        // workgroup barrier), keeping that token's replay sums for the row's columns;
+        // r_0 of each token goes to the wave's own LDS rows.  A lane (row rho, column
+        // c) then owns the output of token rho at column c.  The chains need only the
+        // published entries, so they run while the checkpoint loads land.
+        float rep[SPW];
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) rep[j] = 0.f;
+        float* rzw = rz + (size_t)w * 4 * R;
+        if (a.mode != MODE_FLUSH) {
+            if (rho < T) {
+                float r[EL];
+                lds_row_load<EL>(qs + rho * R + EL * j16, r);
+                float sig = 1.f;
+                const float* vcol = vs + lc0;
+                for (int i = len + rho; i >= f; --i) {
+                    float kv[EL];
+                    lds_row_load<EL>(ks + i * RS + EL * j16, kv);
+                    float part = 0.f;
+#pragma unroll
+                    for (int m = 0; m < EL; ++m) part += kv[m] * r[m];
+                    const float bd = be[i] * group_sum<16>(part);
+                    const float cf = sig * bd;
+#pragma unroll
+                    for (int j = 0; j < SPW; ++j) rep[j] += cf * vcol[i * cw + 16 * j];
+#pragma unroll
+                    for (int m = 0; m < EL; ++m) r[m] -= bd * kv[m];
+                    sig *= al[i];
+                }
+#pragma unroll
+                for (int m = 0; m < EL; ++m) r[m] *= sig;
+                lds_row_store<EL>(rzw + rho * R + EL * j16, r);
+            }
+            wave_lds_sync();
+        }
+        if (f > 0) {
+#pragma unroll
+            for (int j = 0; j < SPW; ++j) ckpt_decode<NB, CK>(s[j]);
+            f32x4 W[SPW];
+            fold_front(BoolTag<true>{}, W);
+#pragma unroll
+            for (int j = 0; j < SPW; ++j) fold_strip(BoolTag<true>{}, j, W[j], s[j]);
+        }
+        if (a.mode != MODE_FLUSH) {
+#pragma unroll
+            for (int j = 0; j < SPW; ++j) {
+                if (f == 0) {
+                    if (from_copy) rc_decode<NB, RC>(s[j]);
+                    else ckpt_decode<NB, CK>(s[j]);
+                }
+                float mine = 0.f;
+#pragma unroll
+                for (int t = 0; t < TMAX; ++t) {
+                    if (t < T) {
+                        float gacc = 0.f;
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) gacc += dot4(s[j][nb], ld4(rzw + t * R + nb * 16 + rq));
+                        gacc = sum_over_row_groups(gacc);
+                        if (rho == t) mine = gacc;
+                    }
+                }
+                if (rho < T)
+                    st_io<IO>(a.y, (((size_t)rho * sB + b) * a.H + h) * C + c0 + lc0 + 16 * j, a.scale * (mine + rep[j]));
+            }
+        }
+        if (f > 0) {
+#pragma unroll
+            for (int j = 0; j < SPW; ++j) {
+                ckpt_store<NB, CK>(a.ckpt, strip0 + j, lane, s[j]);
+                if constexpr (RC != RC_NONE) rc_store<NB, RC>(a.rcopy, a.rscale, strip0 + j, lane, s[j], a.mxceil);
+            }
+        }
     } else {
         // Several tokens: the strips are decoded once, folded in place, read out by
         // every token, then stored.
@@ -437,7 +511,8 @@ static hipError_t gdn_launch_spw(const StepArgs& a, hipStream_t s)
 {
     const size_t Tr = a.T > 0 ? a.T : 1;
     const size_t R = NB * 16, vmax = a.vmax;
-    const size_t lds = sizeof(float) * (vmax * (a.C / a.nsplit + R + 4) + Tr * R + (Tr > 4 ? Tr : 4) * R + 2 * vmax +
+    const size_t rzr = TMAX == 1 ? 4 : TMAX <= 4 ? 16 : Tr;
+    const size_t lds = sizeof(float) * (vmax * (a.C / a.nsplit + R + 4) + Tr * R + rzr * R + 2 * vmax +
                                         Tr * vmax + 2 * 16 * 17);
     auto k = gdn_step_kernel<NB, IO, TMAX, RC, CK, SPW>;
     if (lds > 64 * 1024) {
