@@ -23,28 +23,32 @@ namespace rs {
 // ---- linear ------------------------------------------------------------------
 // Workgroup: four waves in a 2 x 2 arrangement and an output tile of TM rows x 64
 // columns (TM = 128 or 64); wave (wr, wc) owns TM/2 rows and 32 columns, i.e. BI x 2
-// MFMA blocks of 16 x 16 (BI = TM / 32).  K advances in chunks of 64: the chunk's X
-// rows (TM x 64) and W rows (64 x 64) are copied to LDS once (coalesced 16-byte
-// loads) and every wave reads its operands from there, so each X value is fetched
-// from L2 once per workgroup and each weight once.  Two chunks are in flight
+// MFMA blocks of 16 x 16 (BI = TM / 32).  K advances in chunks of KC (64, 128 or
+// 256: at decode batch sizes the launch is bound by the loads in flight, so the
+// chunk is as deep as the registers allow): the chunk's X rows (TM x KC) and W rows
+// (64 x KC) are copied to LDS once (coalesced 16-byte loads) and every wave reads
+// its operands from there, so each X value is fetched from L2 once per workgroup
+// and each weight once.  Two chunks are in flight
 // while one is multiplied: chunk c+2's global loads are issued into the register
 // set chunk c came through, and chunk c+1 (already in registers) is written to the
 // other LDS buffer after chunk c's products; one barrier per chunk.  TM = 64 is
 // taken when 128-row tiles would leave fewer than 512 workgroups (few output
 // columns or a long K per workgroup).  Operand layout of the 16x16x32 MFMA: A lane
 // l holds row l%16, k = 8(l/16)..+7; B lane l holds column l%16, the same k; the
-// 16x16 result has rows 4(l/16)..+3 of column l%16.  LDS rows are 72 bf16 long
-// (64 + 8 of padding), so the 16 rows a fragment read touches start 36 banks
-// apart.  Rows past M and columns past N read row M-1 / column N-1 and are not
-// stored.
-constexpr int LIN_TN = 64, LIN_KC = 64, LIN_PITCH = 72;
+// 16x16 result has rows 4(l/16)..+3 of column l%16.  LDS rows are KC + 8 bf16
+// long (8 of padding), so consecutive rows of a fragment read start 4 banks apart.
+// Rows past M and columns past N read row M-1 / column N-1 and are not stored.
+constexpr int LIN_TN = 64;
 
-template <int TM>
+template <int TM, int LIN_KC>
 __global__ __launch_bounds__(256) void standin_linear_kernel(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M,
                                                              int K, int N)
 {
+    constexpr int LIN_PITCH = LIN_KC + 8;       // padded LDS row (bf16)
+    constexpr int PR = LIN_KC / 8;              // 16-byte pieces per row and chunk
     constexpr int BI = TM / 32;                 // row blocks per wave
-    constexpr int XU = TM * 8 / 256;            // 16-byte X pieces per thread and chunk
+    constexpr int XU = TM * PR / 256;           // 16-byte X pieces per thread and chunk
+    constexpr int WU = LIN_TN * PR / 256;       // 16-byte W pieces per thread and chunk
     __shared__ __attribute__((aligned(16))) uint16_t xs[2][TM * LIN_PITCH];
     __shared__ __attribute__((aligned(16))) uint16_t wsh[2][LIN_TN * LIN_PITCH];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -57,20 +61,20 @@ __global__ __launch_bounds__(256) void standin_linear_kernel(const uint16_t* X, 
     int xdst[XU];
 #pragma unroll
     for (int u = 0; u < XU; ++u) {
-        const int c = tid + 256 * u, row = c >> 3, pc = c & 7;
+        const int c = tid + 256 * u, row = c / PR, pc = c % PR;
         xsrc[u] = X + (size_t)min(m0 + row, M - 1) * K + 8 * pc;
         xdst[u] = row * LIN_PITCH + 8 * pc;
     }
-    const uint16_t* wsrc[2];
-    int wdst[2];
+    const uint16_t* wsrc[WU];
+    int wdst[WU];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int c = tid + 256 * u, col = c >> 3, pc = c & 7;
+    for (int u = 0; u < WU; ++u) {
+        const int c = tid + 256 * u, col = c / PR, pc = c % PR;
         wsrc[u] = W + (size_t)min(n0 + col, N - 1) * K + 8 * pc;
         wdst[u] = col * LIN_PITCH + 8 * pc;
     }
     struct Regs {
-        u32x4 x[XU], w[2];
+        u32x4 x[XU], w[WU];
     };
     Regs r0, r1;
     auto load_chunk = [&](Regs& r, int kc) {
@@ -78,13 +82,13 @@ __global__ __launch_bounds__(256) void standin_linear_kernel(const uint16_t* X, 
 #pragma unroll
         for (int u = 0; u < XU; ++u) r.x[u] = *reinterpret_cast<const u32x4*>(xsrc[u] + k0);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) r.w[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[u] + k0));
+        for (int u = 0; u < WU; ++u) r.w[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[u] + k0));
     };
     auto store_chunk = [&](const Regs& r, int buf) {
 #pragma unroll
         for (int u = 0; u < XU; ++u) *reinterpret_cast<u32x4*>(&xs[buf][xdst[u]]) = r.x[u];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) *reinterpret_cast<u32x4*>(&wsh[buf][wdst[u]]) = r.w[u];
+        for (int u = 0; u < WU; ++u) *reinterpret_cast<u32x4*>(&wsh[buf][wdst[u]]) = r.w[u];
     };
 
     f32x4 acc[BI][2];
@@ -147,10 +151,19 @@ hipError_t launch_standin_linear(const void* X, const void* W, void* Y, int M, i
     const auto w = static_cast<const uint16_t*>(W);
     const auto y = static_cast<uint16_t*>(Y);
     const int cols = (N + LIN_TN - 1) / LIN_TN;
-    if ((long long)cols * ((M + 127) / 128) >= 512)
-        hipLaunchKernelGGL(standin_linear_kernel<128>, dim3(cols, (M + 127) / 128), dim3(256), 0, s, x, w, y, M, K, N);
-    else
-        hipLaunchKernelGGL(standin_linear_kernel<64>, dim3(cols, (M + 63) / 64), dim3(256), 0, s, x, w, y, M, K, N);
+    // Chunk depth: the deepest the register budget allows for the tile, as K permits.
+    // Measured at batch 256: 8192 -> 4096 projection 0.095 ms (64-deep chunks) ->
+    // 0.059 (128) -> 0.049 ms (256); 4096 -> 18560 0.131 -> 0.123 ms (128).
+    if ((long long)cols * ((M + 127) / 128) >= 512) {
+        const dim3 grid(cols, (M + 127) / 128);
+        if (K % 128 == 0) hipLaunchKernelGGL((standin_linear_kernel<128, 128>), grid, dim3(256), 0, s, x, w, y, M, K, N);
+        else hipLaunchKernelGGL((standin_linear_kernel<128, 64>), grid, dim3(256), 0, s, x, w, y, M, K, N);
+    } else {
+        const dim3 grid(cols, (M + 63) / 64);
+        if (K % 256 == 0) hipLaunchKernelGGL((standin_linear_kernel<64, 256>), grid, dim3(256), 0, s, x, w, y, M, K, N);
+        else if (K % 128 == 0) hipLaunchKernelGGL((standin_linear_kernel<64, 128>), grid, dim3(256), 0, s, x, w, y, M, K, N);
+        else hipLaunchKernelGGL((standin_linear_kernel<64, 64>), grid, dim3(256), 0, s, x, w, y, M, K, N);
+    }
     return hipGetLastError();
 }
 

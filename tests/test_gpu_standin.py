@@ -39,7 +39,7 @@ def _err(got, ref):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 128, 32), (37, 384, 96), (256, 1024, 256), (300, 512, 64), (256, 4096, 160),
-                                   (129, 64, 40), (5, 192, 1), (256, 8192, 200)])
+                                   (129, 64, 40), (5, 192, 1), (256, 8192, 200), (200, 192, 16384)])
 def test_linear(M, K, N):
     from hybrid_decode_replay_amd import binding as b
     from oracle import standin_oracle as so
