@@ -45,8 +45,21 @@ namespace rs {
 // staging are done once for the HT heads; the heads are then processed in turn,
 // and head hh+1's checkpoint (or read-copy) loads are issued before head hh's
 // arithmetic, so one head's stream overlaps the previous head's work.
+// Workgroups per CU the register budget is set for: six single-head workgroups; four
+// four-head ones, except with an FP8 checkpoint and an MXFP4 copy, where the fold's two
+// encoders need more registers than four allow (at four the compiler spills the staged
+// entry chunks of every step, and the step's scratch traffic depends on what ran before
+// it; measured at batch 256: 29-40 % of peak spilling, 34 % at three without spills).
+template <int HT, int NB, int RC, int CK>
+constexpr int mamba2_wg_per_cu()
+{
+    if constexpr (HT == 1) return NB <= 8 ? 6 : 4;
+    else if constexpr (NB > 8) return 2;
+    else return CK == CK_FP8 && RC == RC_MXFP4 ? 3 : 4;
+}
+
 template <int NB, int IO, int TMAX, bool MFMA_FOLD, int RC, int CK, int HT>
-__global__ __launch_bounds__(256, HT == 1 ? (NB <= 8 ? 6 : 4) : (NB <= 8 ? 4 : 2)) void mamba2_step_kernel(StepArgs a)
+__global__ __launch_bounds__(256, (mamba2_wg_per_cu<HT, NB, RC, CK>())) void mamba2_step_kernel(StepArgs a)
 {
     extern __shared__ float lds[];
     constexpr int R = NB * 16;
