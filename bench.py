@@ -31,6 +31,9 @@ The JSON line also carries:
   flush_schedule_mamba2_b256
                 per-step launch time (p50, p99, max) with lockstep folds and
                 with staggered flush phases
+  ragged_b256   both batch-256 layers with a seeded 75 % of the slots active per
+                step (masked steps), and with 8 slots taking a fresh checkpoint
+                every 16 steps; throughput over active tokens
   hybrid_stack_b256
                 a model step over four SSM layers (Mamba-2, GDN, Mamba-2, GDN
                 at the shapes above, batch 256) through one layer stack, with
@@ -675,6 +678,66 @@ def time_model_step(rb, synth, torch, dev, stream, B, context, mlp, K=32, W=8, d
             "replay_tokens_per_s": round(B / (rep / 1e3), 1)}
 
 
+def time_ragged(L, K, W, stream, p_active=0.75, arrive_every=16, n_arrive=8, seed=11):
+    """A serving batch whose slots come and go: every step a seeded mask marks each slot
+    active with probability p_active (masked decode); in a second run, n_arrive slots also
+    take a fresh fp32 checkpoint (a prefill hand-over) every arrive_every steps.  K steps
+    back to back after W untimed ones; throughput counts active tokens only, and the
+    algorithmic bytes are the layer's per-token window bytes times the active tokens (a
+    sequence folds once per window of its own steps)."""
+    import numpy as np
+    rb, torch = L.rb, L.torch
+    rng = np.random.default_rng(seed)
+    masks_np = (rng.random((K + W, L.B)) < p_active).astype(np.uint8)
+    masks = torch.from_numpy(masks_np).to(L.dev)
+    lib, sp = rb.lib(), rb.ctypes.c_void_p(stream.cuda_stream)
+    ins = [L.inputs(t % L.ntok) for t in range(K + W)]
+    y = torch.empty((1, L.B, L.H, L.C), dtype=torch.bfloat16, device=L.dev)
+    yp = rb.ctypes.c_void_p(y.data_ptr())
+    arrivals = [np.sort(rng.choice(L.B, n_arrive, replace=False)).astype(np.int32) for _ in range((K + W) // arrive_every + 1)]
+    fresh = L.S0[:n_arrive].clone()
+    out = {"batch": L.B, "p_active": p_active}
+    for label, arrive in (("masked", False), ("masked_with_arrivals", True)):
+        st = rb.ReplayState(L.cfg, device=L.dev)
+        st.load_checkpoint(L.S0)
+        torch.cuda.synchronize()
+
+        def step(t):
+            if arrive and t % arrive_every == 0:
+                arr = arrivals[t // arrive_every]
+                s = lib.replay_load_slots(st.h, n_arrive, arr.ctypes.data_as(rb.ctypes.POINTER(rb.ctypes.c_int32)),
+                                          rb.ctypes.c_void_p(fresh.data_ptr()), sp)
+                if s != rb.OK:
+                    raise rb.ReplayError(s, "replay_load_slots")
+            s = lib.replay_decode_step_masked(st.h, rb.ctypes.byref(ins[t]), rb.ctypes.c_void_p(masks[t].data_ptr()),
+                                              yp, sp)
+            if s != rb.OK:
+                raise rb.ReplayError(s, "replay_decode_step_masked")
+
+        for t in range(W):
+            step(t)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for t in range(W, W + K):
+            step(t)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / K
+        act = int(masks_np[W:].sum())
+        per_tok = algorithmic_bytes(L.kind, L.H, L.G, L.C, L.R, L.cap)[0]
+        r = {"ms_per_step": round(ms, 5), "active_tokens_per_step": round(act / K, 1),
+             "active_tokens_per_s": round(act / (ms * K / 1e3), 1)}
+        if not arrive:
+            gbs = act * per_tok / (ms * K / 1e3) / 1e9
+            r.update({"achieved_gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)})
+        else:
+            r["arrivals"] = f"{n_arrive} slots every {arrive_every} steps"
+        out[label] = r
+        del st
+    return out
+
+
 def time_standins(rb, torch, dev, stream, B=256, reps=20):
     """Per-launch time and algorithmic bandwidth of the stand-in kernels at the model step's
     shapes: weights (and activations) for the projections, the cache for attention."""
@@ -1011,6 +1074,15 @@ def main():
             del Lg
             torch.cuda.empty_cache()
         out["flush_schedule_mamba2_b256"] = sched
+        # a serving batch whose slots come and go: masked steps, per-slot arrivals
+        log("ragged occupancy")
+        rag = {}
+        for kind, seed in (("mamba2", 13), ("gdn", 14)):
+            Lr = Layer(rb, synth, torch, dev, kind, B, 160, seed=seed)
+            rag[kind] = time_ragged(Lr, 256, 32, stream)
+            del Lr
+            torch.cuda.empty_cache()
+        out["ragged_b256"] = rag
         # a hybrid model's SSM layers decoded as one stack (one bookkeeping set), lockstep
         # and staggered flush phases, against the conventional kernel per layer
         log("hybrid stack")
