@@ -297,28 +297,37 @@ __global__ __launch_bounds__(256, SPW == 1 ? (NB <= 8 ? 6 : 4) : 4) void gdn_ste
         for (int j = 0; j < SPW; ++j) rep[j] = 0.f;
         float* rw = rz + (size_t)w * R;
         if (a.mode != MODE_FLUSH) {
-            float r[EL];
-            lds_row_load<EL>(qs + EL * j16, r);
+            // With d_k >= 64 the chain is spread over the whole wave (lane l holds
+            // elements EW*l .. EW*l+EW-1 of r, the dot reduced over the row and then the
+            // four rows): a quarter of the per-entry multiply-adds of a 16-lane row,
+            // for two more reduction steps.
+            constexpr int EW = R >= 64 ? R / 64 : EL;
+            constexpr int NL = R >= 64 ? 64 : 16;
+            const int li = R >= 64 ? lane : j16;
+            float r[EW];
+            lds_row_load<EW>(qs + EW * li, r);
             float sig = 1.f;
             const float* vcol = vs + lc0;
             for (int i = len; i >= f; --i) {
-                float kv[EL];
-                lds_row_load<EL>(ks + i * RS + EL * j16, kv);
+                float kv[EW];
+                lds_row_load<EW>(ks + i * RS + EW * li, kv);
                 float part = 0.f;
 #pragma unroll
-                for (int m = 0; m < EL; ++m) part += kv[m] * r[m];
-                const float bd = be[i] * group_sum<16>(part);
+                for (int m = 0; m < EW; ++m) part += kv[m] * r[m];
+                part = group_sum<16>(part);
+                if constexpr (NL == 64) part = sum_over_row_groups(part);
+                const float bd = be[i] * part;
                 const float cf = sig * bd;
 #pragma unroll
                 for (int j = 0; j < SPW; ++j) rep[j] += cf * vcol[i * cw + 16 * j];
 #pragma unroll
-                for (int m = 0; m < EL; ++m) r[m] -= bd * kv[m];
+                for (int m = 0; m < EW; ++m) r[m] -= bd * kv[m];
                 sig *= al[i];
             }
 #pragma unroll
-            for (int m = 0; m < EL; ++m) r[m] *= sig;
-            // r_0 of this wave (every row holds the same values) -> wave-private LDS row
-            if (rho == 0) lds_row_store<EL>(rw + EL * j16, r);
+            for (int m = 0; m < EW; ++m) r[m] *= sig;
+            // r_0 of this wave -> wave-private LDS row
+            if (NL == 64 || rho == 0) lds_row_store<EW>(rw + EW * li, r);
             wave_lds_sync();
         }
         auto emit = [&](int j, float gacc) {
