@@ -949,6 +949,9 @@ def main():
     ap.add_argument("--spec-rounds", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="headline layer only (no GDN, spec, conventional)")
+    ap.add_argument("--no-ragged", action="store_true",
+                    help="skip the ragged-occupancy section (its masked launches share the step kernels and grids of "
+                         "the other sections, so per-kernel profiles are taken without it)")
     ap.add_argument("--sweep", metavar="FILE", help="also sweep batch 1..512 for both layers, JSON lines to FILE")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -1075,14 +1078,15 @@ def main():
             torch.cuda.empty_cache()
         out["flush_schedule_mamba2_b256"] = sched
         # a serving batch whose slots come and go: masked steps, per-slot arrivals
-        log("ragged occupancy")
-        rag = {}
-        for kind, seed in (("mamba2", 13), ("gdn", 14)):
-            Lr = Layer(rb, synth, torch, dev, kind, B, 160, seed=seed)
-            rag[kind] = time_ragged(Lr, 256, 32, stream)
-            del Lr
-            torch.cuda.empty_cache()
-        out["ragged_b256"] = rag
+        if not args.no_ragged:
+            log("ragged occupancy")
+            rag = {}
+            for kind, seed in (("mamba2", 13), ("gdn", 14)):
+                Lr = Layer(rb, synth, torch, dev, kind, B, 160, seed=seed)
+                rag[kind] = time_ragged(Lr, 256, 32, stream)
+                del Lr
+                torch.cuda.empty_cache()
+            out["ragged_b256"] = rag
         # a hybrid model's SSM layers decoded as one stack (one bookkeeping set), lockstep
         # and staggered flush phases, against the conventional kernel per layer
         log("hybrid stack")
