@@ -269,6 +269,26 @@ __device__ __forceinline__ f32x4 mfma16x16x32bf16(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// x as hi + mid + lo, each a bf16 number rounded to nearest even from what the
+// terms before it leave: 24 significant bits in all, so the three terms carry x
+// up to a relative 2^-24 or so (each difference is exact in fp32).
+__device__ __forceinline__ void split3_bf16(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo)
+{
+    hi = f32_to_bf16_bits(x);
+    const float r1 = x - bf16_bits_to_f32((uint16_t)hi);
+    mid = f32_to_bf16_bits(r1);
+    const float r2 = r1 - bf16_bits_to_f32((uint16_t)mid);
+    lo = f32_to_bf16_bits(r2);
+}
+
+// Eight bf16 codes (low halves of w0..w7) as one MFMA operand, w0 first.
+__device__ __forceinline__ bf16x8 bf16x8_pack(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, uint32_t w4,
+                                              uint32_t w5, uint32_t w6, uint32_t w7)
+{
+    const u32x4 w = {w0 | (w1 << 16), w2 | (w3 << 16), w4 | (w5 << 16), w6 | (w7 << 16)};
+    return __builtin_bit_cast(bf16x8, w);
+}
+
 // Eight fp32 values that are bf16 numbers (bf16 inputs widened, E4M3 values) as
 // bf16: the upper half of each is its bf16 code, so the conversion is exact.
 __device__ __forceinline__ bf16x8 bf16x8_exact(f32x4 lo, f32x4 hi)

@@ -308,19 +308,47 @@ __global__ __launch_bounds__(256, (mamba2_wg_per_cu<HT, NB, RC, CK>())) void mam
                     const int i = kb * 4 + iq;
                     bop[kb] = (i < f) ? fexp((pf - psh[i]) * Ah) * dsh[i] * xsh[i * XS + lc] : 0.f;
                 }
-                const int nkb = (f + 3) >> 2;
+                if constexpr (IO == IO_BF16 && HT > 1) {
+                    // bf16 io (four-head kernels; the one-head kernels keep the fp32 product
+                    // within their register budget, and their folds are bound by the
+                    // checkpoint stream): the B entries are bf16 numbers, and each weight splits into
+                    // three bf16 terms (hi + mid + lo, 24 bits), so two 16x16x32 bf16
+                    // products per block replace four fp32 ones: exact products, fp32
+                    // sums.  Lane group q holds entries 4 kb + q, in the k slots
+                    // (hi of the four, mid of the four) and (lo of the four, zeros).
+                    uint32_t wh[4], wm[4], wl[4];
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    for (int kb = 0; kb < 4; ++kb) split3_bf16(bop[kb], wh[kb], wm[kb], wl[kb]);
+                    const bf16x8 b1 = bf16x8_pack(wh[0], wh[1], wh[2], wh[3], wm[0], wm[1], wm[2], wm[3]);
+                    const bf16x8 b2 = bf16x8_pack(wl[0], wl[1], wl[2], wl[3], 0u, 0u, 0u, 0u);
 #pragma unroll
-                    for (int kb = 0; kb < 4; ++kb) {
-                        if (kb < nkb) {
+                    for (int nb = 0; nb < NB; ++nb) {
+                        uint32_t av[4];
+#pragma unroll
+                        for (int kb = 0; kb < 4; ++kb) {
                             const int i = kb * 4 + iq;
-                            const float av = (i < f) ? bs[i * RS + nb * 16 + (lane & 15)] : 0.f;
-                            acc = mfma16x16x4(av, bop[kb], acc);
+                            av[kb] = (i < f) ? (__builtin_bit_cast(uint32_t, bs[i * RS + nb * 16 + (lane & 15)]) >> 16) : 0u;
                         }
+                        f32x4 acc = mfma16x16x32bf16(bf16x8_pack(av[0], av[1], av[2], av[3], av[0], av[1], av[2], av[3]),
+                                                     b1, f32x4{0.f, 0.f, 0.f, 0.f});
+                        acc = mfma16x16x32bf16(bf16x8_pack(av[0], av[1], av[2], av[3], 0u, 0u, 0u, 0u), b2, acc);
+                        s[nb] = decay * s[nb] + acc;
                     }
-                    s[nb] = decay * s[nb] + acc;
+                } else {
+                    const int nkb = (f + 3) >> 2;
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int kb = 0; kb < 4; ++kb) {
+                            if (kb < nkb) {
+                                const int i = kb * 4 + iq;
+                                const float av = (i < f) ? bs[i * RS + nb * 16 + (lane & 15)] : 0.f;
+                                acc = mfma16x16x4(av, bop[kb], acc);
+                            }
+                        }
+                        s[nb] = decay * s[nb] + acc;
+                    }
                 }
             } else {
                 float wx[16];
