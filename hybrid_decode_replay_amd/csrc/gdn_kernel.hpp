@@ -142,13 +142,13 @@ __global__ __launch_bounds__(256, SPW == 1 ? (NB <= 8 ? 6 : 4) : 4) void gdn_ste
         if constexpr (decltype(dec)::value) return s[j][jb];
         else return ckpt_block<NB, CK>(s[j], jb);
     };
-    // With bf16 io the entry keys are bf16 numbers, and so are the values of an FP8
-    // checkpoint: the Gram matrix (and then W) take the 16x16x32 bf16 product,
-    // exact products summed in fp32 like the fp32 product's.  For key chunk m (32
-    // keys) lane group q holds keys 32m + 4q + 0..3 and 32m + 16 + 4q + 0..3, the
-    // rows of checkpoint blocks 2m and 2m+1 it holds.
+    // With bf16 io the entry keys are bf16 numbers, so the Gram matrix, W and the
+    // update take the 16x16x32 bf16 product: exact products summed in fp32 like the
+    // fp32 product's.  The other operand is a bf16 number (an FP8 checkpoint's
+    // values) or split into two (fp16) or three (fp32) bf16 terms.  For key chunk m
+    // (32 keys) lane group q holds keys 32m + 4q + 0..3 and 32m + 16 + 4q + 0..3,
+    // the rows of checkpoint blocks 2m and 2m+1 it holds.
     constexpr bool BFK = IO == IO_BF16 && R % 32 == 0;
-    constexpr bool BFW = BFK && CK == CK_FP8;
     auto fold_front = [&](auto dec, f32x4 (&W)[SPW]) {
         const bool arow = l16 < f;
         // key chunk m of entry row l16 (zero past the folded entries)
@@ -213,18 +213,36 @@ __global__ __launch_bounds__(256, SPW == 1 ? (NB <= 8 ? 6 : 4) : 4) void gdn_ste
         // W[i][v] = (S0 k_i)[v]; lane result rows i = lq*4 + r, column lc0 + 16 j
 #pragma unroll
         for (int j = 0; j < SPW; ++j) W[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (BFW) {
+        if constexpr (BFK) {
 #pragma unroll
             for (int m = 0; m < R / 32; ++m) {
                 const bf16x8 km = key_chunk(m);
 #pragma unroll
-                for (int j = 0; j < SPW; ++j)
-                    W[j] = mfma16x16x32bf16(km, bf16x8_exact(s0_block(dec, j, 2 * m), s0_block(dec, j, 2 * m + 1)), W[j]);
+                for (int j = 0; j < SPW; ++j) {
+                    const f32x4 sa = s0_block(dec, j, 2 * m), sb = s0_block(dec, j, 2 * m + 1);
+                    if constexpr (CK == CK_FP8) {
+                        W[j] = mfma16x16x32bf16(km, bf16x8_exact(sa, sb), W[j]);
+                    } else {
+                        // fp16 values are hi + mid exactly (11 bits); fp32 values take lo too
+                        uint32_t h[8], md[8], lo[8];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            split3_bf16(sa[e], h[e], md[e], lo[e]);
+                            split3_bf16(sb[e], h[4 + e], md[4 + e], lo[4 + e]);
+                        }
+                        W[j] = mfma16x16x32bf16(km, bf16x8_pack(h[0], h[1], h[2], h[3], h[4], h[5], h[6], h[7]), W[j]);
+                        W[j] = mfma16x16x32bf16(km, bf16x8_pack(md[0], md[1], md[2], md[3], md[4], md[5], md[6], md[7]),
+                                                W[j]);
+                        if constexpr (CK == CK_F32)
+                            W[j] = mfma16x16x32bf16(km, bf16x8_pack(lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]),
+                                                    W[j]);
+                    }
+                }
             }
         }
 #pragma unroll
         for (int j = 0; j < SPW; ++j) {
-            if constexpr (!BFW) {
+            if constexpr (!BFK) {
 #pragma unroll
                 for (int jb = 0; jb < NB; ++jb) {
                     const f32x4 kv = arow ? ld4(ks + l16 * RS + jb * 16 + rq) : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -259,16 +277,41 @@ __global__ __launch_bounds__(256, SPW == 1 ? (NB <= 8 ? 6 : 4) : 4) void gdn_ste
             U[r] = (i < f) ? tt[i * 17 + f - 1] * U[r] : 0.f;         // alpha_{i+1} ... alpha_{f-1}
         }
         // S'^T[jk][v] = decay S0^T[jk][v] + sum_i K[i][jk] U~[i][v]
+        if constexpr (BFK) {
+            // the keys are bf16 numbers and U~ splits into three bf16 terms (hi + mid
+            // + lo), so two 16x16x32 bf16 products per block replace four fp32 ones:
+            // lane group q holds entries 4q..4q+3 twice, against (hi, mid) and (lo, 0)
+            uint32_t uh[4], um[4], ul[4];
 #pragma unroll
-        for (int jb = 0; jb < NB; ++jb) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int r = 0; r < 4; ++r) split3_bf16(U[r], uh[r], um[r], ul[r]);
+            const bf16x8 b1 = bf16x8_pack(uh[0], uh[1], uh[2], uh[3], um[0], um[1], um[2], um[3]);
+            const bf16x8 b2 = bf16x8_pack(ul[0], ul[1], ul[2], ul[3], 0u, 0u, 0u, 0u);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = lq * 4 + r;
-                const float kv = (i < f) ? ks[i * RS + jb * 16 + l16] : 0.f;
-                acc = mfma16x16x4(kv, U[r], acc);
+            for (int jb = 0; jb < NB; ++jb) {
+                uint32_t kv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = lq * 4 + r;                        // rows past f are inside ks
+                    const uint32_t raw = __builtin_bit_cast(uint32_t, ks[i * RS + jb * 16 + l16]);
+                    kv[r] = (i < f) ? (raw >> 16) : 0u;
+                }
+                const bf16x8 ka = bf16x8_pack(kv[0], kv[1], kv[2], kv[3], kv[0], kv[1], kv[2], kv[3]);
+                f32x4 acc = mfma16x16x32bf16(ka, b1, f32x4{0.f, 0.f, 0.f, 0.f});
+                acc = mfma16x16x32bf16(ka, b2, acc);
+                out[jb] = decay * s0_block(dec, j, jb) + acc;
             }
-            out[jb] = decay * s0_block(dec, j, jb) + acc;
+        } else {
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = lq * 4 + r;
+                    const float kv = (i < f) ? ks[i * RS + jb * 16 + l16] : 0.f;
+                    acc = mfma16x16x4(kv, U[r], acc);
+                }
+                out[jb] = decay * s0_block(dec, j, jb) + acc;
+            }
         }
         // the folded state takes the checkpoint's storage precision at once (fp16:
         // RNE), so this step's outputs and the read copy see the stored values
