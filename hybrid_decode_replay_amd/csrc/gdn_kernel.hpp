@@ -60,8 +60,20 @@ struct BoolTag {
     static constexpr bool value = B;
 };
 
+// Workgroups per CU the register budget is cut for (256 threads each).  The
+// one-token two-strip kernels on fp16 and FP8 (no copy) checkpoints take five:
+// their steps that fold nothing gain more from the fifth wave per SIMD than their
+// fold steps lose to the few values the fold then keeps in scratch.
+template <int NB, int TMAX, int RC, int CK, int SPW>
+constexpr int gdn_wg_per_cu()
+{
+    if constexpr (SPW == 1) return NB <= 8 ? 6 : 4;
+    const bool five = TMAX == 1 && NB <= 8 && (CK == CK_F16 || (CK == CK_FP8 && RC == RC_NONE));
+    return five ? 5 : 4;
+}
+
 template <int NB, int IO, int TMAX, int RC, int CK, int SPW>
-__global__ __launch_bounds__(256, SPW == 1 ? (NB <= 8 ? 6 : 4) : 4) void gdn_step_kernel(StepArgs a)
+__global__ __launch_bounds__(256, (gdn_wg_per_cu<NB, TMAX, RC, CK, SPW>())) void gdn_step_kernel(StepArgs a)
 {
     extern __shared__ float lds[];
     constexpr int R = NB * 16;                  // d_k
