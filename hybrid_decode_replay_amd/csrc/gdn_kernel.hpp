@@ -61,19 +61,19 @@ struct BoolTag {
 };
 
 // Workgroups per CU the register budget is cut for (256 threads each).  The
-// one-token two-strip kernels on fp16 and FP8 (no copy) checkpoints take five:
-// their steps that fold nothing gain more from the fifth wave per SIMD than their
-// fold steps lose to the few values the fold then keeps in scratch.
-template <int NB, int TMAX, int RC, int CK, int SPW>
+// one-token two-strip kernels with bf16 io on fp16 and FP8 (no copy) checkpoints
+// take five: a fifth wave per SIMD for the steps that fold nothing, with no
+// scratch (their folds form each strip's W when they fold it).
+template <int NB, int IO, int TMAX, int RC, int CK, int SPW>
 constexpr int gdn_wg_per_cu()
 {
     if constexpr (SPW == 1) return NB <= 8 ? 6 : 4;
-    const bool five = TMAX == 1 && NB <= 8 && (CK == CK_F16 || (CK == CK_FP8 && RC == RC_NONE));
+    const bool five = IO == IO_BF16 && TMAX == 1 && NB <= 8 && (CK == CK_F16 || (CK == CK_FP8 && RC == RC_NONE));
     return five ? 5 : 4;
 }
 
 template <int NB, int IO, int TMAX, int RC, int CK, int SPW>
-__global__ __launch_bounds__(256, (gdn_wg_per_cu<NB, TMAX, RC, CK, SPW>())) void gdn_step_kernel(StepArgs a)
+__global__ __launch_bounds__(256, (gdn_wg_per_cu<NB, IO, TMAX, RC, CK, SPW>())) void gdn_step_kernel(StepArgs a)
 {
     extern __shared__ float lds[];
     constexpr int R = NB * 16;                  // d_k
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256, (gdn_wg_per_cu<NB, TMAX, RC, CK, SPW>())) void
 
     // ---- 3. fold of the first f entries (WY form on MFMA), in two parts.
     // fold_front: wave 0 forms the gate products and (I + A)^{-1}; every wave forms
-    // W = K S0^T for its strips; one workgroup barrier.  fold_strip: strip j's
+    // W = K S0^T for its first strip; one workgroup barrier.  fold_strip: strip j's
     // S' = P S0 + K^T U~ into `out`.  S0 is read as the registers hold it: decoded
     // fp32 (DEC), or the loaded words decoded block by block (fp16/FP8), so a fold
     // needs no decoded copy of the strips besides its result.
@@ -161,14 +161,57 @@ __global__ __launch_bounds__(256, (gdn_wg_per_cu<NB, TMAX, RC, CK, SPW>())) void
     // (32 keys) lane group q holds keys 32m + 4q + 0..3 and 32m + 16 + 4q + 0..3,
     // the rows of checkpoint blocks 2m and 2m+1 it holds.
     constexpr bool BFK = IO == IO_BF16 && R % 32 == 0;
-    auto fold_front = [&](auto dec, f32x4 (&W)[SPW]) {
+    // key chunk m of entry row l16 (zero past the folded entries)
+    auto key_chunk = [&](int m) {
         const bool arow = l16 < f;
-        // key chunk m of entry row l16 (zero past the folded entries)
-        auto key_chunk = [&](int m) {
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            return bf16x8_exact(arow ? ld4(ks + l16 * RS + 32 * m + rq) : z,
-                                arow ? ld4(ks + l16 * RS + 32 * m + 16 + rq) : z);
-        };
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        return bf16x8_exact(arow ? ld4(ks + l16 * RS + 32 * m + rq) : z,
+                            arow ? ld4(ks + l16 * RS + 32 * m + 16 + rq) : z);
+    };
+    // W[i][v] = (S0 k_i)[v] of strip j; lane result rows i = lq*4 + r, column lc0 + 16 j
+    auto w_of = [&](auto dec, int j) __attribute__((always_inline)) -> f32x4 {
+        f32x4 Wj = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (BFK) {
+#pragma unroll
+            for (int m = 0; m < R / 32; ++m) {
+                const bf16x8 km = key_chunk(m);
+                const f32x4 sa = s0_block(dec, j, 2 * m), sb = s0_block(dec, j, 2 * m + 1);
+                if constexpr (CK == CK_FP8) {
+                    Wj = mfma16x16x32bf16(km, bf16x8_exact(sa, sb), Wj);
+                } else {
+                    // fp16 values are hi + mid exactly (11 bits); fp32 values take lo too
+                    uint32_t h[8], md[8], lo[8];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        split3_bf16(sa[e], h[e], md[e], lo[e]);
+                        split3_bf16(sb[e], h[4 + e], md[4 + e], lo[4 + e]);
+                    }
+                    Wj = mfma16x16x32bf16(km, bf16x8_pack(h[0], h[1], h[2], h[3], h[4], h[5], h[6], h[7]), Wj);
+                    Wj = mfma16x16x32bf16(km, bf16x8_pack(md[0], md[1], md[2], md[3], md[4], md[5], md[6], md[7]), Wj);
+                    if constexpr (CK == CK_F32)
+                        Wj = mfma16x16x32bf16(km, bf16x8_pack(lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]),
+                                              Wj);
+                }
+            }
+        } else {
+            const bool arow = l16 < f;
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb) {
+                const f32x4 kv = arow ? ld4(ks + l16 * RS + jb * 16 + rq) : f32x4{0.f, 0.f, 0.f, 0.f};
+                const f32x4 sv = s0_block(dec, j, jb);
+                Wj = mfma16x16x4(kv.x, sv.x, Wj);
+                Wj = mfma16x16x4(kv.y, sv.y, Wj);
+                Wj = mfma16x16x4(kv.z, sv.z, Wj);
+                Wj = mfma16x16x4(kv.w, sv.w, Wj);
+            }
+        }
+        return Wj;
+    };
+    // fold_front forms W of every strip (all) or of strip 0 only while wave 0 works;
+    // one-token steps form the other strips' W when they fold them, so no W is held
+    // across another strip's fold.
+    auto fold_front = [&](auto dec, auto all, f32x4 (&W)[SPW]) {
+        const bool arow = l16 < f;
         if (w == 0) {
             // gate products tt[j][i] = alpha_{j+1} ... alpha_i (1 for i <= j), i, j < f:
             // lane j multiplies along i, every product formed as a product
@@ -222,50 +265,8 @@ __global__ __launch_bounds__(256, (gdn_wg_per_cu<NB, TMAX, RC, CK, SPW>())) void
                 for (int i = 0; i < 16; ++i) ti[i * 17 + lane] = tc[i];
             }
         }
-        // W[i][v] = (S0 k_i)[v]; lane result rows i = lq*4 + r, column lc0 + 16 j
 #pragma unroll
-        for (int j = 0; j < SPW; ++j) W[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (BFK) {
-#pragma unroll
-            for (int m = 0; m < R / 32; ++m) {
-                const bf16x8 km = key_chunk(m);
-#pragma unroll
-                for (int j = 0; j < SPW; ++j) {
-                    const f32x4 sa = s0_block(dec, j, 2 * m), sb = s0_block(dec, j, 2 * m + 1);
-                    if constexpr (CK == CK_FP8) {
-                        W[j] = mfma16x16x32bf16(km, bf16x8_exact(sa, sb), W[j]);
-                    } else {
-                        // fp16 values are hi + mid exactly (11 bits); fp32 values take lo too
-                        uint32_t h[8], md[8], lo[8];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            split3_bf16(sa[e], h[e], md[e], lo[e]);
-                            split3_bf16(sb[e], h[4 + e], md[4 + e], lo[4 + e]);
-                        }
-                        W[j] = mfma16x16x32bf16(km, bf16x8_pack(h[0], h[1], h[2], h[3], h[4], h[5], h[6], h[7]), W[j]);
-                        W[j] = mfma16x16x32bf16(km, bf16x8_pack(md[0], md[1], md[2], md[3], md[4], md[5], md[6], md[7]),
-                                                W[j]);
-                        if constexpr (CK == CK_F32)
-                            W[j] = mfma16x16x32bf16(km, bf16x8_pack(lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]),
-                                                    W[j]);
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < SPW; ++j) {
-            if constexpr (!BFK) {
-#pragma unroll
-                for (int jb = 0; jb < NB; ++jb) {
-                    const f32x4 kv = arow ? ld4(ks + l16 * RS + jb * 16 + rq) : f32x4{0.f, 0.f, 0.f, 0.f};
-                    const f32x4 sv = s0_block(dec, j, jb);
-                    W[j] = mfma16x16x4(kv.x, sv.x, W[j]);
-                    W[j] = mfma16x16x4(kv.y, sv.y, W[j]);
-                    W[j] = mfma16x16x4(kv.z, sv.z, W[j]);
-                    W[j] = mfma16x16x4(kv.w, sv.w, W[j]);
-                }
-            }
-        }
+        for (int j = 0; j < (decltype(all)::value ? SPW : 1); ++j) W[j] = w_of(dec, j);
         __syncthreads();
     };
     auto fold_strip = [&](auto dec, int j, const f32x4& Wj, f32x4 (&out)[NB]) {
@@ -391,9 +392,10 @@ __global__ __launch_bounds__(256, (gdn_wg_per_cu<NB, TMAX, RC, CK, SPW>())) void
         };
         if (f > 0) {
             f32x4 W[SPW];
-            fold_front(BoolTag<false>{}, W);
+            fold_front(BoolTag<false>{}, BoolTag<false>{}, W);
 #pragma unroll
             for (int j = 0; j < SPW; ++j) {
+                const f32x4 Wj = j == 0 ? W[0] : w_of(BoolTag<false>{}, j);
                 auto finish = [&](f32x4 (&sn)[NB]) {
                     // single checkpoint write, then the read-out of the stored values
                     ckpt_store<NB, CK>(a.ckpt, strip0 + j, lane, sn);
@@ -406,11 +408,11 @@ __global__ __launch_bounds__(256, (gdn_wg_per_cu<NB, TMAX, RC, CK, SPW>())) void
                     }
                 };
                 if constexpr (CK == CK_F32) {
-                    fold_strip(BoolTag<true>{}, j, W[j], s[j]);      // in place: block jb is read before written
+                    fold_strip(BoolTag<true>{}, j, Wj, s[j]);        // in place: block jb is read before written
                     finish(s[j]);
                 } else {
                     f32x4 sn[NB];
-                    fold_strip(BoolTag<false>{}, j, W[j], sn);
+                    fold_strip(BoolTag<false>{}, j, Wj, sn);
                     finish(sn);
                 }
             }
@@ -464,7 +466,7 @@ __global__ __launch_bounds__(256, (gdn_wg_per_cu<NB, TMAX, RC, CK, SPW>())) void
 #pragma unroll
             for (int j = 0; j < SPW; ++j) ckpt_decode<NB, CK>(s[j]);
             f32x4 W[SPW];
-            fold_front(BoolTag<true>{}, W);
+            fold_front(BoolTag<true>{}, BoolTag<true>{}, W);
 #pragma unroll
             for (int j = 0; j < SPW; ++j) fold_strip(BoolTag<true>{}, j, W[j], s[j]);
         }
@@ -504,7 +506,7 @@ __global__ __launch_bounds__(256, (gdn_wg_per_cu<NB, TMAX, RC, CK, SPW>())) void
 #pragma unroll
             for (int j = 0; j < SPW; ++j) ckpt_decode<NB, CK>(s[j]);
             f32x4 W[SPW];
-            fold_front(BoolTag<true>{}, W);
+            fold_front(BoolTag<true>{}, BoolTag<true>{}, W);
 #pragma unroll
             for (int j = 0; j < SPW; ++j) fold_strip(BoolTag<true>{}, j, W[j], s[j]);
         }
