@@ -61,14 +61,16 @@ struct BoolTag {
 };
 
 // Workgroups per CU the register budget is cut for (256 threads each).  The
-// one-token two-strip kernels with bf16 io on fp16 and FP8 (no copy) checkpoints
-// take five: a fifth wave per SIMD for the steps that fold nothing, with no
-// scratch (their folds form each strip's W when they fold it).
+// one-token two-strip kernels with bf16 io on fp16 and FP8 (no copy) checkpoints,
+// and on fp32 checkpoints with a copy, take five: a fifth wave per SIMD for the
+// steps that fold nothing, with no scratch (their folds form each strip's W, and
+// load each fp32 strip, when they fold it).
 template <int NB, int IO, int TMAX, int RC, int CK, int SPW>
 constexpr int gdn_wg_per_cu()
 {
     if constexpr (SPW == 1) return NB <= 8 ? 6 : 4;
-    const bool five = IO == IO_BF16 && TMAX == 1 && NB <= 8 && (CK == CK_F16 || (CK == CK_FP8 && RC == RC_NONE));
+    const bool five = IO == IO_BF16 && TMAX == 1 && NB <= 8 &&
+                      (CK == CK_F16 || (CK == CK_FP8 && RC == RC_NONE) || (CK == CK_F32 && RC != RC_NONE));
     return five ? 5 : 4;
 }
 
@@ -133,11 +135,15 @@ __global__ __launch_bounds__(256, (gdn_wg_per_cu<NB, IO, TMAX, RC, CK, SPW>())) 
     f32x4 s[SPW][NB];
     bool from_copy = false;
     if constexpr (RC != RC_NONE) from_copy = (f == 0);
+    // One-token fold steps on an fp32 checkpoint with a copy load strip j > 0 when
+    // they fold it, so one fp32 strip is held at a time (the steps that fold nothing
+    // read only the copy's words).
+    constexpr bool LATE = TMAX == 1 && SPW > 1 && CK == CK_F32 && RC != RC_NONE;
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
         if (from_copy) {
             if constexpr (RC != RC_NONE) rc_issue<NB, RC>(a.rcopy, a.rscale, strip0 + j, lane, s[j]);
-        } else {
+        } else if (!LATE || j == 0) {
             ckpt_issue<NB, CK>(a.ckpt, strip0 + j, lane, s[j]);
         }
     }
@@ -395,6 +401,7 @@ __global__ __launch_bounds__(256, (gdn_wg_per_cu<NB, IO, TMAX, RC, CK, SPW>())) 
             fold_front(BoolTag<false>{}, BoolTag<false>{}, W);
 #pragma unroll
             for (int j = 0; j < SPW; ++j) {
+                if (LATE && j > 0) ckpt_issue<NB, CK>(a.ckpt, strip0 + j, lane, s[j]);
                 const f32x4 Wj = j == 0 ? W[0] : w_of(BoolTag<false>{}, j);
                 auto finish = [&](f32x4 (&sn)[NB]) {
                     // single checkpoint write, then the read-out of the stored values
