@@ -225,10 +225,11 @@ def dram(rd_dir, wr_dir, out, kernel, grid, rd_cmd, wr_cmd, algorithmic_bytes):
 
 
 def mfma(pmc_dir, out, command):
-    """Flush-step MFMA use per (kernel, grid) from a `--pmc MfmaUtil MfmaFlopsF32
-    GRBM_GUI_ACTIVE` run.  A replay step issues MFMA only when it folds, so the
-    dispatches with MfmaFlopsF32 > 0 are the flush steps.  MfmaUtil is rocprofv3's own
-    derived counter: MFMA busy cycles summed over SIMDs / (GUI-active cycles x SIMDs)."""
+    """Flush-step MFMA use per (kernel, grid) from a `--pmc MfmaUtil MfmaFlops
+    MfmaFlopsBF16 GRBM_GUI_ACTIVE` run.  A replay step issues MFMA only when it folds, so
+    the dispatches with MfmaFlops > 0 are the flush steps.  MfmaFlops is rocprofv3's
+    count over every MFMA type (512 per MOP); MfmaUtil its derived counter: MFMA busy
+    cycles summed over SIMDs / (GUI-active cycles x SIMDs)."""
     per = {}
     for r in csv.DictReader(open(_one(os.path.join(pmc_dir, "**", "*counter_collection.csv")))):
         d = per.setdefault(int(r["Dispatch_Id"]), {"name": short(r["Kernel_Name"]), "grid": int(r["Grid_Size"]),
@@ -236,34 +237,38 @@ def mfma(pmc_dir, out, command):
         d[r["Counter_Name"]] = float(r["Counter_Value"])
     groups = {}
     for d in per.values():
-        if d.get("MfmaFlopsF32", 0.0) > 0 and d["name"].startswith(("mamba2", "gdn")):
+        if d.get("MfmaFlops", 0.0) > 0 and d["name"].startswith(("mamba2", "gdn")):
             groups.setdefault((d["name"], d["grid"]), []).append(d)
     # full folds (every sequence of the batch folds: the most flops seen for the kernel and
     # grid) apart from partial ones (staggered flush phases, forced flushes of some sequences)
     split = {}
     for (name, grid), ds in groups.items():
-        top = max(d["MfmaFlopsF32"] for d in ds)
-        full = [d for d in ds if d["MfmaFlopsF32"] >= 0.999 * top]
-        part = [d for d in ds if d["MfmaFlopsF32"] < 0.999 * top]
+        top = max(d["MfmaFlops"] for d in ds)
+        full = [d for d in ds if d["MfmaFlops"] >= 0.999 * top]
+        part = [d for d in ds if d["MfmaFlops"] < 0.999 * top]
         split[(name, grid, "full")] = full
         if part:
             split[(name, grid, "partial")] = part
     lines = [f"# MFMA use on fold (flush) dispatches: {os.path.basename(out)[:-3]}", "",
              "Command (from the repository root; run under `cd /tmp && export TMPDIR=/tmp`):", "",
              f"    {command}", "",
-             "Dispatches with MfmaFlopsF32 > 0 (replay steps issue MFMA only when they fold).",
+             "Dispatches with MfmaFlops > 0 (replay steps issue MFMA only when they fold).",
+             "MfmaFlops: rocprofv3's count over all MFMA types, 512 per MOP, as the hardware counts them (a",
+             "16x16x32 bf16 product counts its whole k = 32, zero and repeated operands included).",
              "MfmaUtil: rocprofv3's derived counter, MFMA busy cycles summed over SIMDs / (GUI-active cycles x SIMDs).",
-             "TFLOP/s: MfmaFlopsF32 / the profiled dispatch duration (counter runs serialise dispatches).", "",
-             "Full: every sequence folds (the largest MfmaFlopsF32 of the kernel and grid); partial: some do.", "",
-             "| kernel | grid (threads) | folds | dispatches | MfmaFlopsF32 per dispatch | MfmaUtil % | profiled us "
-             "| TFLOP/s |",
-             "|---|---|---|---|---|---|---|---|"]
+             "TFLOP/s: MfmaFlops / the profiled dispatch duration (counter runs serialise dispatches).", "",
+             "Full: every sequence folds (the largest MfmaFlops of the kernel and grid); partial: some do.", "",
+             "| kernel | grid (threads) | folds | dispatches | MfmaFlops per dispatch | bf16 share | MfmaUtil % "
+             "| profiled us | TFLOP/s |",
+             "|---|---|---|---|---|---|---|---|---|"]
     for (name, grid, kind), ds in sorted(split.items(), key=lambda kv: (kv[0][2], -kv[0][1], kv[0][0])):
         n = len(ds)
-        fl = sum(d["MfmaFlopsF32"] for d in ds) / n
+        fl = sum(d["MfmaFlops"] for d in ds) / n
+        bf = sum(d.get("MfmaFlopsBF16", 0.0) for d in ds) / n
         ut = sum(d.get("MfmaUtil", 0.0) for d in ds) / n
         us = sum(d["ns"] for d in ds) / n / 1e3
-        lines.append(f"| `{name}` | {grid} | {kind} | {n} | {fl:.4g} | {ut:.2f} | {us:.1f} | {fl / us / 1e6:.2f} |")
+        lines.append(f"| `{name}` | {grid} | {kind} | {n} | {fl:.4g} | {bf / fl:.2f} | {ut:.2f} | {us:.1f} "
+                     f"| {fl / us / 1e6:.2f} |")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(out, len(split), "rows")

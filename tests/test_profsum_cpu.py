@@ -66,7 +66,8 @@ def test_mfma_splits_full_and_partial_folds(tmp_path):
     kern = "void rs::gdn_step_kernel<8, 1, 1, 0, 0>(rs::StepArgs)"
     rows = []
     for did, flops, util in ((1, 0.0, 0.0), (2, 1.0e10, 30.0), (3, 1.0e10, 32.0), (4, 6.0e8, 3.0)):
-        rows += [_row(did, kern, 4194304, "MfmaFlopsF32", flops, ns=200000),
+        rows += [_row(did, kern, 4194304, "MfmaFlops", flops, ns=200000),
+                 _row(did, kern, 4194304, "MfmaFlopsBF16", 0.75 * flops, ns=200000),
                  _row(did, kern, 4194304, "MfmaUtil", util, ns=200000)]
     _write_csv(str(tmp_path / "m" / "x_counter_collection.csv"), rows)
     out = str(tmp_path / "m.md")
@@ -76,9 +77,9 @@ def test_mfma_splits_full_and_partial_folds(tmp_path):
     part = [line for line in table if "| partial |" in line]
     assert len(full) == 1 and len(part) == 1
     cells = [c.strip() for c in full[0].split("|")]
-    # kernel, grid, kind, dispatches, flops, util, us, TFLOP/s
-    assert cells[4] == "2" and float(cells[5]) == 1.0e10 and float(cells[6]) == 31.0
-    assert float(cells[7]) == 200.0 and float(cells[8]) == 50.0      # 1e10 flop / 200 us
+    # kernel, grid, kind, dispatches, flops, bf16 share, util, us, TFLOP/s
+    assert cells[4] == "2" and float(cells[5]) == 1.0e10 and float(cells[6]) == 0.75 and float(cells[7]) == 31.0
+    assert float(cells[8]) == 200.0 and float(cells[9]) == 50.0      # 1e10 flop / 200 us
     assert [c.strip() for c in part[0].split("|")][4] == "1"
 
 
