@@ -61,16 +61,17 @@ struct BoolTag {
 };
 
 // Workgroups per CU the register budget is cut for (256 threads each).  The
-// one-token two-strip kernels with bf16 io on fp16 and FP8 (no copy) checkpoints,
-// and on fp32 checkpoints with a copy, take five: a fifth wave per SIMD for the
-// steps that fold nothing, with no scratch (their folds form each strip's W, and
-// load each fp32 strip, when they fold it).
+// one-token two-strip kernels with bf16 io on fp16 and FP8 checkpoints, and on
+// fp32 checkpoints with a copy, take five: a fifth wave per SIMD for the steps
+// that fold nothing, in 96 VGPRs (their folds form each strip's W, and load each
+// fp32 strip, when they fold it; with an MXFP4 copy the FP8 fold keeps one value
+// in scratch).
 template <int NB, int IO, int TMAX, int RC, int CK, int SPW>
 constexpr int gdn_wg_per_cu()
 {
     if constexpr (SPW == 1) return NB <= 8 ? 6 : 4;
     const bool five = IO == IO_BF16 && TMAX == 1 && NB <= 8 &&
-                      (CK == CK_F16 || (CK == CK_FP8 && RC == RC_NONE) || (CK == CK_F32 && RC != RC_NONE));
+                      (CK == CK_F16 || CK == CK_FP8 || (CK == CK_F32 && RC != RC_NONE));
     return five ? 5 : 4;
 }
 
