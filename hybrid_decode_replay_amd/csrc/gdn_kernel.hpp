@@ -153,7 +153,8 @@ __global__ __launch_bounds__(256, (gdn_wg_per_cu<NB, IO, TMAX, RC, CK, SPW>())) 
 
     // ---- 3. fold of the first f entries (WY form on MFMA), in two parts.
     // fold_front: wave 0 forms the gate products and (I + A)^{-1}; every wave forms
-    // W = K S0^T for its first strip; one workgroup barrier.  fold_strip: strip j's
+    // W = K S0^T for its first strip (one-token steps) or for all its strips; one
+    // workgroup barrier.  fold_strip: strip j's
     // S' = P S0 + K^T U~ into `out`.  S0 is read as the registers hold it: decoded
     // fp32 (DEC), or the loaded words decoded block by block (fp16/FP8), so a fold
     // needs no decoded copy of the strips besides its result.
