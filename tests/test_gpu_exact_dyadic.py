@@ -141,3 +141,44 @@ def test_bit_exact_on_dyadic_inputs(kind, ckpt, copy):
             wc, ws = ro.mxfp4_quantize(ref)
             np.testing.assert_array_equal(codes.cpu().numpy(), wc)
             np.testing.assert_array_equal(scales.cpu().numpy(), ws)
+
+
+BF16_CASES = [("f32", "none"), ("f32", "fp8"), ("f32", "mxfp4"), ("f16", "none"), ("fp8", "none"),
+              ("fp8", "mxfp4")]
+
+
+@pytest.mark.parametrize("ckpt,copy", BF16_CASES)
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_bit_exact_fold_with_bf16_io(kind, ckpt, copy):
+    """The same dyadic script with bf16 io, where the folds take the 16x16x32 bf16 product
+    (the four-head Mamba-2 kernels, every GDN kernel).  This pins those products' operand
+    layouts and the rounding after them bit for bit: checkpoints and bookkeeping must match
+    exactly.  The dyadic fold weights are bf16 numbers, so the split terms after the first
+    are zero here; the splits' precision is held by the other parity tests (fp32 checkpoints
+    to 1e-4).  Outputs are written in bf16, so they are held to its rounding (relative 2^-9
+    per element).  Mamba-2 runs with one B/C group, so that its four-head kernels fold."""
+    from harness import Pair
+    b = rb()
+    B, H, G, C, R, cap = 4, 4, 1, 64, 128, 4
+    if kind == "gdn":
+        G = H
+    rng = np.random.default_rng([H, C, R, 818])
+    S0 = _state(rng, (B, H, C, R))
+    toks = _inputs(kind, 19, 17, B, H, G, C, R)
+    for n, v in toks.items():
+        if n not in ("alpha", "beta"):
+            assert np.array_equal(torch.from_numpy(v).to(torch.bfloat16).float().numpy(), v), n
+    _host_exact(kind, S0, toks, H)
+    ck = {"f32": b.F32, "f16": b.F16, "fp8": b.FP8_E4M3}[ckpt]
+    rc = {"none": b.NONE, "fp8": b.FP8_E4M3, "mxfp4": b.MXFP4}[copy]
+    print(f"[exact bf16] {kind} ckpt={ckpt} copy={copy}", flush=True)
+    pair = Pair(b.MAMBA2 if kind == "mamba2" else b.GDN, B, H, G, C, R, cap=cap, io=b.BF16, seed=19, S0=S0,
+                ckpt=ck, read_copy=rc, tol=0.0)
+    pair.tol = 2.0 ** -8          # outputs only; checkpoints stay bit-exact (ckpt_tol = 0)
+    if kind == "mamba2":
+        pair.params = {"A": torch.zeros(H, device="cuda"), "D": torch.ones(H, device="cuda")}
+        pair.orc.A = np.zeros(H)
+        pair.orc.D = np.ones(H)
+    _script(kind, pair, toks)
+    assert pair.max_err["ckpt"] == 0.0
+    assert pair.max_err["y"] <= 2.0 ** -8
