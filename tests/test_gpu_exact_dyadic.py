@@ -153,10 +153,11 @@ def test_bit_exact_fold_with_bf16_io(kind, ckpt, copy):
     """The same dyadic script with bf16 io, where the folds take the 16x16x32 bf16 product
     (the four-head Mamba-2 kernels, every GDN kernel).  This pins those products' operand
     layouts and the rounding after them bit for bit: checkpoints and bookkeeping must match
-    exactly.  The dyadic fold weights are bf16 numbers, so the split terms after the first
-    are zero here; the splits' precision is held by the other parity tests (fp32 checkpoints
-    to 1e-4).  Outputs are written in bf16, so they are held to its rounding (relative 2^-9
-    per element).  Mamba-2 runs with one B/C group, so that its four-head kernels fold."""
+    exactly.  Mamba-2's dt takes 8-bit values in [1/2, 2), so a fold weight dt x carries up
+    to 10 bits and its second bf16 term is not zero (with A = 0 nothing needs the third,
+    which the other parity tests hold, fp32 checkpoints to 1e-4).  Outputs are written in
+    bf16, so they are held to its rounding (relative 2^-9 per element).  Mamba-2 runs with
+    one B/C group, so that its four-head kernels fold."""
     from harness import Pair
     b = rb()
     B, H, G, C, R, cap = 4, 4, 1, 64, 128, 4
@@ -165,6 +166,8 @@ def test_bit_exact_fold_with_bf16_io(kind, ckpt, copy):
     rng = np.random.default_rng([H, C, R, 818])
     S0 = _state(rng, (B, H, C, R))
     toks = _inputs(kind, 19, 17, B, H, G, C, R)
+    if kind == "mamba2":
+        toks["dt"] = (np.random.default_rng([19, 707]).integers(64, 256, toks["dt"].shape) / 128.0).astype(np.float32)
     for n, v in toks.items():
         if n not in ("alpha", "beta"):
             assert np.array_equal(torch.from_numpy(v).to(torch.bfloat16).float().numpy(), v), n
